@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Benchmark of the GDN hot path on one MI355X.
+
+One step = one pass of the hot path over one batch of synthetic input:
+  * decode step at batch 256 drawn from a 2048-slot cache (16 key heads,
+    32 value heads, d = 128, conv width 4 over 8192 channels, bf16 conv cache,
+    fp32 state): gdn_decode_step, the headline workload;
+  * decode step at batch 16 from a 256-slot cache (the small bucket);
+  * chunked prefill of 8 sequences with lengths uniform in [512, 8192]
+    (about 32k tokens), bf16 q/k/v, fp32 states (when the prefill is built).
+Inputs are resident in HBM before the timed region.  Successive steps rotate
+over disjoint slot sets so the 256 MB Infinity Cache (MALL) cannot serve a
+state written in a recent step.
+
+Prints ONE JSON line.  `value` is the decode step's algorithmic HBM bytes per
+second at batch 256 (GB/s); the batch-16 decode rate and the prefill tokens/s
+ride along in "extra".  "roofline" reports the dominant kernel (the decode
+recurrence) timed alone with HIP events over the timed region; "cpu_baseline"
+is the fp64 oracle on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, 8 TB/s
+BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
+
+H, HV, DK, DV, W = 16, 32, 128, 128, 4
+D = 2 * H * DK + HV * DV
+
+
+def decode_bytes_per_seq(x_bytes=2, cs_bytes=2, out_bytes=4):
+    """Algorithmic HBM bytes of one decode row: state read + write, conv state
+    read + write, the new token, g and beta, the slot index and the output."""
+    state = 2 * HV * DV * DK * 4
+    conv = 2 * D * (W - 1) * cs_bytes
+    return state + conv + D * x_bytes + 2 * HV * 4 + 4 + HV * DV * out_bytes
+
+
+def rec_bytes_per_seq(y_bytes=4, out_bytes=4):
+    """Algorithmic bytes of the recurrence kernel alone (post-conv activations in)."""
+    return 2 * HV * DV * DK * 4 + D * y_bytes + 2 * HV * 4 + 4 + HV * DV * out_bytes
+
+
+def conv_weight_bytes(w_bytes=2):
+    return D * W * w_bytes
+
+
+def prefill_flops(lengths, chunk=64):
+    """MFMA-shaped FLOPs of the chunked prefill: per chunk of length L,
+    HV (6 L^2 d + 6 L d^2) + H (4 L^2 d)."""
+    f = 0
+    for n in lengths:
+        for c0 in range(0, n, chunk):
+            L = min(chunk, n - c0)
+            f += HV * (6 * L * L * DK + 6 * L * DK * DV) + H * 4 * L * L * DK
+    return f
+
+
+def prefill_bytes(total_tokens, n_seqs, in_bytes=2, out_bytes=2):
+    per_tok = (2 * H * DK + HV * DV) * in_bytes + 2 * HV * 4 + HV * DV * out_bytes
+    return total_tokens * per_tok + n_seqs * 2 * HV * DV * DK * 4
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="wall-clock budget of the oracle sample")
+    ap.add_argument("--validate", action="store_true",
+                    help="time with device-side index validation on")
+    return ap.parse_args()
+
+
+class DecodeSetup:
+    """A decode workload with K disjoint slot sets rotated step to step."""
+
+    def __init__(self, batch, num_slots, seed, dev):
+        import torch
+        import gdn_inputs as gi
+        import gated_deltanet_recurrent_gdn_amd as gdn
+        self.torch, self.gdn = torch, gdn
+        self.batch = batch
+        d = gi.decode_inputs(batch, num_slots, seed=seed, gen_device=dev)
+        self.d = d
+        gen = torch.Generator(device="cpu")
+        gen.manual_seed(seed + 100)
+        perm = (torch.randperm(num_slots - 1, generator=gen) + 1).to(torch.int32)
+        nsets = max(1, (num_slots - 1) // batch)
+        self.slot_sets = [perm[i * batch:(i + 1) * batch].to(dev) for i in range(nsets)]
+        self.dims = gdn.make_dims(H, HV, DK, DV, W)
+        self.out = torch.empty(batch, HV, DV, device=dev)
+        self.ws = torch.empty(gdn.gdn_decode_workspace_size(self.dims, batch),
+                              dtype=torch.uint8, device=dev)
+        self.err = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.y = torch.empty(batch, D, device=dev)          # post-conv activations
+        self.scale = DK ** -0.5
+        self.i = 0
+
+    def step(self, validate=False):
+        gdn = self.gdn
+        d = self.d
+        slots = self.slot_sets[self.i % len(self.slot_sets)]
+        self.i += 1
+        flags = gdn.DEFAULT_DECODE_FLAGS | (gdn.FLAG_VALIDATE if validate else 0)
+        gdn.gdn_decode_step(d["mixed_qkv"], d["g"], d["beta"], slots, d["conv_state"],
+                            d["conv_weight"], d["rec_state"], self.out, self.dims, self.scale,
+                            flags=flags, workspace=self.ws,
+                            err_flag=self.err if validate else None)
+
+    def prepare_rec(self):
+        gdn = self.gdn
+        d = self.d
+        gdn.gdn_conv_update(d["mixed_qkv"], self.slot_sets[0], d["conv_state"].clone(),
+                            d["conv_weight"], self.y, flags=gdn.FLAG_SILU)
+
+    def rec_step(self):
+        gdn = self.gdn
+        d = self.d
+        slots = self.slot_sets[self.i % len(self.slot_sets)]
+        self.i += 1
+        gdn.gdn_decode_recurrent(self.y, d["g"], d["beta"], slots, d["rec_state"], self.out,
+                                 self.dims, self.scale)
+
+
+def time_loop(torch, fn, steps, warmup):
+    """Per-launch event timing on the current stream; returns a list of ms."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        starts[i].record()
+        fn()
+        ends[i].record()
+    torch.cuda.synchronize()
+    return [s.elapsed_time(e) for s, e in zip(starts, ends)]
+
+
+def cpu_baseline(budget_s):
+    """The fp64 oracle, as it stands, on decode rows of the batch-256 workload
+    (same shapes and distributions), repeated until the budget is spent."""
+    import numpy as np
+    import gdn_inputs as gi
+    import oracle
+    B = 64
+    d = gi.decode_inputs(B, B + 1, seed=2)
+    x = d["mixed_qkv"].double().numpy()
+    g = d["g"].double().numpy()
+    b = d["beta"].double().numpy()
+    slots = d["slot_idx"].numpy()
+    cs = d["conv_state"].double().numpy().copy()
+    rs = d["rec_state"].double().numpy().copy()
+    w = d["conv_weight"].double().numpy()
+    rows = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        oracle.decode_step(x, g, b, slots, cs, w, rs, H, HV, DK, DV, DK ** -0.5)
+        rows += B
+    dt = time.perf_counter() - t0
+    gbs = rows * decode_bytes_per_seq() / dt / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows} decode rows ({rows // B} steps of batch {B}, same shapes "
+                      f"and distributions as the batch-256 workload) in {dt:.1f} s, "
+                      "single-threaded fp64 C"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the GDN core has "
+              "no cross-GPU step in this build.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import gated_deltanet_recurrent_gdn_amd as gdn
+    gdn.load_library()                               # raises when not built
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    big = DecodeSetup(256, 2048, seed=2, dev="cuda")
+    small = DecodeSetup(16, 256, seed=1, dev="cuda")
+    torch.cuda.synchronize()
+
+    # headline: decode step, batch 256
+    ms_big = time_loop(torch, lambda: big.step(args.validate), args.steps, args.warmup)
+    ms_small = time_loop(torch, lambda: small.step(args.validate), args.steps, args.warmup)
+    # dominant kernel alone (the recurrence), same rotation
+    big.prepare_rec()
+    ms_rec = time_loop(torch, big.rec_step, args.steps, args.warmup)
+    torch.cuda.synchronize()
+
+    med = lambda xs: sorted(xs)[len(xs) // 2]  # noqa: E731
+    step_bytes_big = 256 * decode_bytes_per_seq() + conv_weight_bytes()
+    step_bytes_small = 16 * decode_bytes_per_seq() + conv_weight_bytes()
+    mean_big = sum(ms_big) / len(ms_big)
+    gbs_big = step_bytes_big / (mean_big * 1e-3) / 1e9
+    gbs_small = step_bytes_small / (sum(ms_small) / len(ms_small) * 1e-3) / 1e9
+    rec_ms = sum(ms_rec) / len(ms_rec)
+    rec_bytes = 256 * rec_bytes_per_seq()
+    rec_gbs = rec_bytes / (rec_ms * 1e-3) / 1e9
+
+    extra = {
+        "decode_b256_ms_mean": round(mean_big, 5), "decode_b256_ms_median": round(med(ms_big), 5),
+        "decode_b256_ms_min": round(min(ms_big), 5), "decode_b256_ms_max": round(max(ms_big), 5),
+        "decode_b256_bytes_per_step": step_bytes_big,
+        "decode_b256_pct_hbm_peak": round(100 * gbs_big / HBM_PEAK_GBS, 2),
+        "decode_b16_GBps": round(gbs_small, 2),
+        "decode_b16_ms_mean": round(sum(ms_small) / len(ms_small), 5),
+        "decode_b16_pct_hbm_peak": round(100 * gbs_small / HBM_PEAK_GBS, 2),
+        "validate": bool(args.validate),
+    }
+
+    total_ms = sum(ms_big) / len(ms_big) + sum(ms_small) / len(ms_small)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.cpu_seconds)
+
+    line = {
+        "metric": "GDN decode HBM GB/s (% peak) at batch 16/256; prefill tokens/s (% MFMA)",
+        "value": round(gbs_big, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "GDN decode step, batch 256 of a 2048-slot cache, H=16 HV=32 "
+                               "d=128, conv width 4 (D=8192), bf16 conv cache, fp32 state",
+                   "global_batch": 256, "seq_len": 1, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "kernel": "decode_rec_kernel",
+                     "achieved": round(rec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(rec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_launch_ms": round(rec_ms, 5),
+                     "algorithmic_bytes_per_launch": rec_bytes},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

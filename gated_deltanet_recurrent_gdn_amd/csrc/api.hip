@@ -1,0 +1,169 @@
+// api.hip -- the extern "C" entry points of libgdn.so (declared in gdn.h).
+//
+// Host-side only: validate what can be checked without reading device memory,
+// then enqueue the kernels on the caller's stream and return.  No allocation,
+// no synchronisation, no global mutable state.
+#include <hip/hip_runtime.h>
+
+#include "gdn.h"
+#include "gdn_internal.hpp"
+
+using namespace gdn;
+
+namespace {
+
+constexpr int32_t KNOWN_FLAGS = GDN_FLAG_SILU | GDN_FLAG_QK_L2NORM | GDN_FLAG_VALIDATE;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool dtype_ok(gdn_dtype t) { return t == GDN_F32 || t == GDN_BF16; }
+size_t round256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
+
+gdn_status check_dims(const gdn_dims* d) {
+    if (!d) return GDN_ERR_NULL;
+    const int32_t H = d->num_k_heads, HV = d->num_v_heads, dk = d->head_k_dim, dv = d->head_v_dim;
+    if (H <= 0 || HV <= 0 || HV % H != 0) return GDN_ERR_DIMS;
+    if (dk != 32 && dk != 64 && dk != 128 && dk != 256) return GDN_ERR_DIMS;
+    if (dv <= 0 || dv % 32 != 0 || dv > 256) return GDN_ERR_DIMS;
+    if (d->conv_width != 4) return GDN_ERR_DIMS;
+    const int64_t D = 2LL * H * dk + static_cast<int64_t>(HV) * dv;
+    if (D > (1 << 20)) return GDN_ERR_DIMS;
+    return GDN_OK;
+}
+
+int64_t conv_channels(const gdn_dims* d) {
+    return 2LL * d->num_k_heads * d->head_k_dim + static_cast<int64_t>(d->num_v_heads) * d->head_v_dim;
+}
+
+gdn_status check_flags(int32_t flags, int32_t allowed, const int32_t* err_flag) {
+    if (flags & ~allowed) return GDN_ERR_FLAGS;
+    if ((flags & GDN_FLAG_VALIDATE) && err_flag == nullptr) return GDN_ERR_FLAGS;
+    return GDN_OK;
+}
+
+#define GDN_TRY_LAUNCH(expr)                                  \
+    do {                                                      \
+        if ((expr) != hipSuccess) return GDN_ERR_LAUNCH;      \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn_strerror(gdn_status s) {
+    switch (s) {
+        case GDN_OK: return "success";
+        case GDN_ERR_NULL: return "a required pointer is NULL";
+        case GDN_ERR_DIMS: return "unsupported or inconsistent sizes";
+        case GDN_ERR_DTYPE: return "unsupported dtype";
+        case GDN_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+        case GDN_ERR_WORKSPACE: return "workspace missing or too small";
+        case GDN_ERR_LAUNCH: return "kernel launch failed";
+        case GDN_ERR_FLAGS: return "unknown flag bits, or VALIDATE without err_flag";
+    }
+    return "unknown status";
+}
+
+gdn_status gdn_conv_update(const void* x, gdn_dtype x_dt, const int32_t* cu_seqlens,
+                           int32_t n_seqs, int32_t total_tokens, const int32_t* slot_idx,
+                           void* conv_state, gdn_dtype cs_dt, int32_t num_slots,
+                           const void* weight, const void* bias, gdn_dtype w_dt, void* out,
+                           gdn_dtype out_dt, int32_t dim, int32_t width, int32_t flags,
+                           int32_t* err_flag, void* stream) {
+    if (gdn_status st = check_flags(flags, GDN_FLAG_SILU | GDN_FLAG_VALIDATE, err_flag)) return st;
+    if (n_seqs < 0 || total_tokens < 0 || num_slots < 1 || dim <= 0 || width != 4)
+        return GDN_ERR_DIMS;
+    if (!cu_seqlens && total_tokens != n_seqs) return GDN_ERR_DIMS;
+    if (n_seqs > 65535) return GDN_ERR_DIMS;
+    if (!dtype_ok(x_dt) || !dtype_ok(cs_dt) || !dtype_ok(w_dt) || !dtype_ok(out_dt))
+        return GDN_ERR_DTYPE;
+    if (n_seqs > 0 && (!slot_idx || !conv_state || !weight)) return GDN_ERR_NULL;
+    if (total_tokens > 0 && (!x || !out)) return GDN_ERR_NULL;
+    auto s = static_cast<hipStream_t>(stream);
+    if (flags & GDN_FLAG_VALIDATE)
+        GDN_TRY_LAUNCH(launch_validate(slot_idx, n_seqs, num_slots, cu_seqlens, total_tokens,
+                                       err_flag, s));
+    const int32_t* ef = (flags & GDN_FLAG_VALIDATE) ? err_flag : nullptr;
+    if (cu_seqlens)
+        GDN_TRY_LAUNCH(launch_conv_varlen(x, x_dt, cu_seqlens, n_seqs, slot_idx, conv_state, cs_dt,
+                                          weight, bias, w_dt, out, out_dt, dim, flags, ef, s));
+    else
+        GDN_TRY_LAUNCH(launch_conv_decode(x, x_dt, slot_idx, n_seqs, conv_state, cs_dt, weight,
+                                          bias, w_dt, out, out_dt, dim, flags, ef, s));
+    return GDN_OK;
+}
+
+size_t gdn_decode_workspace_size(const gdn_dims* dims, int32_t batch) {
+    if (check_dims(dims) != GDN_OK || batch < 0) return 0;
+    return round256(static_cast<size_t>(batch) * static_cast<size_t>(conv_channels(dims)) * sizeof(float));
+}
+
+gdn_status gdn_decode_step(const void* mixed_qkv, gdn_dtype x_dt, const float* g,
+                           const float* beta, const int32_t* slot_idx, int32_t batch,
+                           void* conv_state, gdn_dtype cs_dt, const void* conv_weight,
+                           const void* conv_bias, gdn_dtype w_dt, float* rec_state,
+                           int32_t num_slots, void* out, gdn_dtype out_dt, const gdn_dims* dims,
+                           float scale, int32_t flags, void* workspace, size_t workspace_bytes,
+                           int32_t* err_flag, void* stream) {
+    if (gdn_status st = check_flags(flags, KNOWN_FLAGS, err_flag)) return st;
+    if (gdn_status st = check_dims(dims)) return st;
+    if (batch < 0 || batch > 65535 || num_slots < 1) return GDN_ERR_DIMS;
+    if (!dtype_ok(x_dt) || !dtype_ok(cs_dt) || !dtype_ok(w_dt) || !dtype_ok(out_dt))
+        return GDN_ERR_DTYPE;
+    if (batch > 0) {
+        if (!mixed_qkv || !g || !beta || !slot_idx || !conv_state || !conv_weight ||
+            !rec_state || !out || !workspace)
+            return GDN_ERR_NULL;
+        if (!aligned16(rec_state) || !aligned16(workspace)) return GDN_ERR_ALIGN;
+        if (workspace_bytes < gdn_decode_workspace_size(dims, batch)) return GDN_ERR_WORKSPACE;
+    }
+    auto s = static_cast<hipStream_t>(stream);
+    if (flags & GDN_FLAG_VALIDATE)
+        GDN_TRY_LAUNCH(launch_validate(slot_idx, batch, num_slots, nullptr, 0, err_flag, s));
+    if (batch == 0) return GDN_OK;
+    const int32_t* ef = (flags & GDN_FLAG_VALIDATE) ? err_flag : nullptr;
+    const int32_t D = static_cast<int32_t>(conv_channels(dims));
+    float* y = static_cast<float*>(workspace);
+    GDN_TRY_LAUNCH(launch_conv_decode(mixed_qkv, x_dt, slot_idx, batch, conv_state, cs_dt,
+                                      conv_weight, conv_bias, w_dt, y, GDN_F32, D,
+                                      flags & GDN_FLAG_SILU, ef, s));
+    GDN_TRY_LAUNCH(launch_decode_rec(y, GDN_F32, g, beta, slot_idx, batch, rec_state, out,
+                                     out_dt, *dims, scale, flags, ef, s));
+    return GDN_OK;
+}
+
+gdn_status gdn_decode_recurrent(const void* qkv, gdn_dtype qkv_dt, const float* g,
+                                const float* beta, const int32_t* slot_idx, int32_t batch,
+                                float* rec_state, int32_t num_slots, void* out, gdn_dtype out_dt,
+                                const gdn_dims* dims, float scale, int32_t flags,
+                                int32_t* err_flag, void* stream) {
+    if (gdn_status st = check_flags(flags, GDN_FLAG_QK_L2NORM | GDN_FLAG_VALIDATE, err_flag))
+        return st;
+    if (gdn_status st = check_dims(dims)) return st;
+    if (batch < 0 || batch > 65535 || num_slots < 1) return GDN_ERR_DIMS;
+    if (!dtype_ok(qkv_dt) || !dtype_ok(out_dt)) return GDN_ERR_DTYPE;
+    if (batch > 0) {
+        if (!qkv || !g || !beta || !slot_idx || !rec_state || !out) return GDN_ERR_NULL;
+        if (!aligned16(rec_state) || !aligned16(qkv)) return GDN_ERR_ALIGN;
+    }
+    auto s = static_cast<hipStream_t>(stream);
+    if (flags & GDN_FLAG_VALIDATE)
+        GDN_TRY_LAUNCH(launch_validate(slot_idx, batch, num_slots, nullptr, 0, err_flag, s));
+    const int32_t* ef = (flags & GDN_FLAG_VALIDATE) ? err_flag : nullptr;
+    GDN_TRY_LAUNCH(launch_decode_rec(qkv, qkv_dt, g, beta, slot_idx, batch, rec_state, out,
+                                     out_dt, *dims, scale, flags, ef, s));
+    return GDN_OK;
+}
+
+size_t gdn_prefill_workspace_size(const gdn_dims* dims, int32_t n_seqs, int32_t total_tokens) {
+    (void)dims; (void)n_seqs; (void)total_tokens;
+    return 0;
+}
+
+gdn_status gdn_prefill_chunked(const void*, const void*, const void*, gdn_dtype, const float*,
+                               const float*, const int32_t*, int32_t, int32_t, const int32_t*,
+                               float*, int32_t, void*, gdn_dtype, const gdn_dims*, float, int32_t,
+                               void*, size_t, int32_t*, void*) {
+    return GDN_ERR_DIMS;
+}
+
+}  // extern "C"

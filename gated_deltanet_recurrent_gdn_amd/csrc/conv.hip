@@ -1,0 +1,214 @@
+// conv.hip -- causal depthwise conv1d update over a slot-indexed conv cache.
+//
+// RL-Kernel PR #469, "Summary" and "The conv half: coverage and the two
+// mismatch mechanisms": the conv state is [num_blocks, dim, W-1]; the window
+// is the state followed by the new token(s); the fp32 accumulator starts from
+// the bias and adds the taps in order; the state is rolled to the last W-1
+// raw inputs (compared bitwise there); SiLU is optional.  This build keeps the
+// exact bf16 x bf16 products (exact in fp32) instead of rounding each product
+// to bf16, and computes SiLU with IEEE division and the device expf.
+//
+// Ownership: each (sequence, channel) is read and rolled by exactly one
+// workgroup, and inside it by one thread, after every read of the old state
+// by that workgroup -- no cross-workgroup race on the in-place roll.
+#include "gdn_device.hpp"
+#include "gdn_internal.hpp"
+
+namespace gdn {
+
+constexpr int CONV_W = 4;
+
+// ---------------------------------------------------------------------------
+// Decode: one token per row.  grid = (ceil(D / 256), rows), one thread per
+// channel: reads W-1 state taps + 1 token + W weights, writes one output and
+// W-1 rolled taps.
+// ---------------------------------------------------------------------------
+template <typename XT, typename CT, typename WT, typename OT>
+__global__ __launch_bounds__(256) void conv_decode_kernel(
+    const XT* __restrict__ x, const int32_t* __restrict__ slot, CT* __restrict__ cs,
+    const WT* __restrict__ w, const WT* __restrict__ bias, OT* __restrict__ out, int32_t D,
+    int32_t flags, const int32_t* __restrict__ err_flag) {
+    if (call_rejected(err_flag)) return;
+    const int b = blockIdx.y;
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    if (c >= D) return;
+    const int32_t s = slot[b];
+    OT* o = out + static_cast<size_t>(b) * D + c;
+    if (s <= 0) {                       // inactive row: zeros, cache untouched
+        elem<OT>::st(o, 0.0f);
+        return;
+    }
+    CT* st = cs + (static_cast<size_t>(s) * D + c) * (CONV_W - 1);
+    CT raw[CONV_W - 1];
+#pragma unroll
+    for (int j = 0; j < CONV_W - 1; ++j) raw[j] = st[j];
+    const XT xin = x[static_cast<size_t>(b) * D + c];
+
+    float acc = bias ? elem<WT>::ld(bias + c) : 0.0f;
+#pragma unroll
+    for (int j = 0; j < CONV_W - 1; ++j)
+        acc = fmaf(elem<WT>::ld(w + c * CONV_W + j), elem<CT>::ld(&raw[j]), acc);
+    acc = fmaf(elem<WT>::ld(w + c * CONV_W + CONV_W - 1), elem<XT>::ld(&xin), acc);
+    if (flags & GDN_FLAG_SILU) acc = silu(acc);
+    elem<OT>::st(o, acc);
+
+    // roll: drop the oldest tap, append the token (raw bits when the cache has
+    // the token's dtype, otherwise rounded to the cache dtype)
+#pragma unroll
+    for (int j = 0; j < CONV_W - 2; ++j) st[j] = raw[j + 1];
+    CT tok;
+    elem<CT>::st(&tok, elem<XT>::ld(&xin));
+    st[CONV_W - 2] = tok;
+}
+
+// ---------------------------------------------------------------------------
+// Varlen: grid = (ceil(D / 64), n_seqs), 256 threads = 64 channels x 4 token
+// lanes; token lane tg handles tokens tg, tg+4, ...  The old state is read
+// into registers by every thread before a barrier; after it, token lane 0
+// alone writes the rolled state.
+// ---------------------------------------------------------------------------
+template <typename XT, typename CT, typename WT, typename OT>
+__global__ __launch_bounds__(256) void conv_varlen_kernel(
+    const XT* __restrict__ x, const int32_t* __restrict__ cu, const int32_t* __restrict__ slot,
+    CT* __restrict__ cs, const WT* __restrict__ w, const WT* __restrict__ bias,
+    OT* __restrict__ out, int32_t D, int32_t flags, const int32_t* __restrict__ err_flag) {
+    if (call_rejected(err_flag)) return;
+    const int n = blockIdx.y;
+    const int cl = threadIdx.x & 63;
+    const int tg = threadIdx.x >> 6;
+    const int c = blockIdx.x * 64 + cl;
+    const bool valid = c < D;
+    const int32_t start = cu[n];
+    const int32_t L = cu[n + 1] - start;
+    const int32_t s = slot[n];
+    if (s <= 0) {                       // block-uniform branch
+        if (valid)
+            for (int t = tg; t < L; t += 4)
+                elem<OT>::st(out + static_cast<size_t>(start + t) * D + c, 0.0f);
+        return;
+    }
+    CT* st = cs + (static_cast<size_t>(s) * D + (valid ? c : 0)) * (CONV_W - 1);
+    CT raw[CONV_W - 1];
+    float prev[CONV_W - 1];
+    float wt[CONV_W];
+#pragma unroll
+    for (int j = 0; j < CONV_W - 1; ++j) {
+        raw[j] = valid ? st[j] : CT(0);
+        prev[j] = elem<CT>::ld(&raw[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < CONV_W; ++j) wt[j] = valid ? elem<WT>::ld(w + c * CONV_W + j) : 0.0f;
+    const float b0 = (valid && bias) ? elem<WT>::ld(bias + c) : 0.0f;
+    __syncthreads();                    // all reads of the old state precede the roll
+
+    if (valid) {
+        for (int t = tg; t < L; t += 4) {
+            float acc = b0;
+#pragma unroll
+            for (int j = 0; j < CONV_W; ++j) {
+                const int idx = t + j;          // position in [state | tokens]
+                float v = 0.0f;
+                if (idx < CONV_W - 1) {
+#pragma unroll
+                    for (int m = 0; m < CONV_W - 1; ++m)
+                        if (idx == m) v = prev[m];
+                } else {
+                    v = elem<XT>::ld(x + static_cast<size_t>(start + idx - (CONV_W - 1)) * D + c);
+                }
+                acc = fmaf(wt[j], v, acc);
+            }
+            if (flags & GDN_FLAG_SILU) acc = silu(acc);
+            elem<OT>::st(out + static_cast<size_t>(start + t) * D + c, acc);
+        }
+        if (tg == 0 && L > 0) {
+#pragma unroll
+            for (int j = 0; j < CONV_W - 1; ++j) {
+                const int idx = L + j;          // new state = last W-1 of [state | tokens]
+                CT nv = CT(0);
+                if (idx < CONV_W - 1) {
+#pragma unroll
+                    for (int m = 0; m < CONV_W - 1; ++m)
+                        if (idx == m) nv = raw[m];
+                } else {
+                    elem<CT>::st(&nv, elem<XT>::ld(x + static_cast<size_t>(start + idx - (CONV_W - 1)) * D + c));
+                }
+                st[j] = nv;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dtype dispatch
+// ---------------------------------------------------------------------------
+namespace {
+template <typename XT, typename CT, typename WT, typename OT>
+struct DecodeK {
+    static hipError_t run(const void* x, const int32_t* slot, int32_t rows, void* cs,
+                          const void* w, const void* bias, void* out, int32_t D, int32_t flags,
+                          const int32_t* err, hipStream_t st) {
+        dim3 grid((D + 255) / 256, rows);
+        return launch(conv_decode_kernel<XT, CT, WT, OT>, grid, dim3(256), 0, st,
+                      static_cast<const XT*>(x), slot, static_cast<CT*>(cs),
+                      static_cast<const WT*>(w), static_cast<const WT*>(bias),
+                      static_cast<OT*>(out), D, flags, err);
+    }
+};
+template <typename XT, typename CT, typename WT, typename OT>
+struct VarlenK {
+    static hipError_t run(const void* x, const int32_t* cu, int32_t n_seqs, const int32_t* slot,
+                          void* cs, const void* w, const void* bias, void* out, int32_t D,
+                          int32_t flags, const int32_t* err, hipStream_t st) {
+        dim3 grid((D + 63) / 64, n_seqs);
+        return launch(conv_varlen_kernel<XT, CT, WT, OT>, grid, dim3(256), 0, st,
+                      static_cast<const XT*>(x), cu, slot, static_cast<CT*>(cs),
+                      static_cast<const WT*>(w), static_cast<const WT*>(bias),
+                      static_cast<OT*>(out), D, flags, err);
+    }
+};
+
+template <template <typename, typename, typename, typename> class K, typename OT, typename WT,
+          typename CT, typename... A>
+hipError_t pick_x(gdn_dtype x, A&&... a) {
+    return x == GDN_BF16 ? K<bf16_t, CT, WT, OT>::run(std::forward<A>(a)...)
+                         : K<float, CT, WT, OT>::run(std::forward<A>(a)...);
+}
+template <template <typename, typename, typename, typename> class K, typename OT, typename WT,
+          typename... A>
+hipError_t pick_c(gdn_dtype x, gdn_dtype c, A&&... a) {
+    return c == GDN_BF16 ? pick_x<K, OT, WT, bf16_t>(x, std::forward<A>(a)...)
+                         : pick_x<K, OT, WT, float>(x, std::forward<A>(a)...);
+}
+template <template <typename, typename, typename, typename> class K, typename OT, typename... A>
+hipError_t pick_w(gdn_dtype x, gdn_dtype c, gdn_dtype w, A&&... a) {
+    return w == GDN_BF16 ? pick_c<K, OT, bf16_t>(x, c, std::forward<A>(a)...)
+                         : pick_c<K, OT, float>(x, c, std::forward<A>(a)...);
+}
+template <template <typename, typename, typename, typename> class K, typename... A>
+hipError_t pick_all(gdn_dtype x, gdn_dtype c, gdn_dtype w, gdn_dtype o, A&&... a) {
+    return o == GDN_BF16 ? pick_w<K, bf16_t>(x, c, w, std::forward<A>(a)...)
+                         : pick_w<K, float>(x, c, w, std::forward<A>(a)...);
+}
+}  // namespace
+
+hipError_t launch_conv_decode(const void* x, gdn_dtype x_dt, const int32_t* slot_idx,
+                              int32_t rows, void* conv_state, gdn_dtype cs_dt,
+                              const void* weight, const void* bias, gdn_dtype w_dt,
+                              void* out, gdn_dtype out_dt, int32_t dim, int32_t flags,
+                              const int32_t* err_flag, hipStream_t stream) {
+    if (rows == 0) return hipSuccess;
+    return pick_all<DecodeK>(x_dt, cs_dt, w_dt, out_dt, x, slot_idx, rows, conv_state, weight,
+                             bias, out, dim, flags, err_flag, stream);
+}
+
+hipError_t launch_conv_varlen(const void* x, gdn_dtype x_dt, const int32_t* cu_seqlens,
+                              int32_t n_seqs, const int32_t* slot_idx, void* conv_state,
+                              gdn_dtype cs_dt, const void* weight, const void* bias,
+                              gdn_dtype w_dt, void* out, gdn_dtype out_dt, int32_t dim,
+                              int32_t flags, const int32_t* err_flag, hipStream_t stream) {
+    if (n_seqs == 0) return hipSuccess;
+    return pick_all<VarlenK>(x_dt, cs_dt, w_dt, out_dt, x, cu_seqlens, n_seqs, slot_idx,
+                             conv_state, weight, bias, out, dim, flags, err_flag, stream);
+}
+
+}  // namespace gdn

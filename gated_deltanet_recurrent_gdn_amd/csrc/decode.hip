@@ -1,0 +1,203 @@
+// decode.hip -- gated delta-rule decode update of a slot-indexed fp32 state.
+//
+// Per active row b and value head hv (key head h = hv / (HV / H), RL-Kernel
+// PR #469, "How the golden relates to the kernel", item 2):
+//   q, k  <- post-conv activations, L2-normalised x / sqrt(sum(x*x) + 1e-6),
+//            q multiplied by `scale` after the norm, k never scaled (item 3)
+//   alpha = exp(g);  S1 = alpha * S;  u = S1 k;  S' = S1 + beta (v - u) k^T;
+//   o = S' q;  S' stored back in fp32 (RL-Kernel PR #469, "Summary": the
+//   state is [num_blocks, HV, V, K], fp32 accumulator, the store rounds to the
+//   state dtype -- fp32 here).
+//
+// The kernel is a stream of the fp32 state (2 MiB read + 2 MiB written per
+// sequence at HV = 32, d = 128), so it is HBM-bound.  Layout in registers:
+// a state row S[v, :] (dk floats, contiguous) is spread over 8 lanes; lane
+// `sub` of the group holds the float4s at k = 32 i + 4 sub (i < dk / 32), so
+// each load instruction of a wave covers 8 full 128-byte lines.  A wave holds
+// 8 rows per step; a 256-thread workgroup holds 32 rows per step and RPL
+// steps, i.e. 32 * RPL rows of one (row, head).  Each lane issues every load
+// of its rows before any arithmetic, so 256 * 16 * RPL * dk / 32 bytes are in
+// flight per workgroup.  Both row reductions (S1 k and S' q) are an in-lane
+// fixed-order fma chain followed by the 8-lane DPP butterfly `sum8`: the order
+// depends on nothing but dk, so results are batch-invariant and replay
+// bitwise.  No LDS is used at all.
+#include "gdn_device.hpp"
+#include "gdn_internal.hpp"
+
+namespace gdn {
+
+// Four consecutive activations as fp32 (16-byte load for fp32, 8 for bf16).
+template <typename YT> __device__ __forceinline__ float4 load4(const YT* p);
+template <> __device__ __forceinline__ float4 load4<float>(const float* p) {
+    return *reinterpret_cast<const float4*>(p);
+}
+template <> __device__ __forceinline__ float4 load4<bf16_t>(const bf16_t* p) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+}
+
+template <int DK, int RPL, typename YT, typename OT>
+__global__ __launch_bounds__(256) void decode_rec_kernel(
+    const YT* __restrict__ y, const float* __restrict__ g, const float* __restrict__ beta,
+    const int32_t* __restrict__ slot, float* __restrict__ rec, OT* __restrict__ out, int32_t H,
+    int32_t HV, int32_t dv, int32_t tiles_per_head, float scale, int32_t flags,
+    const int32_t* __restrict__ err_flag) {
+    constexpr int NV = DK / 32;               // float4 per lane per row
+    if (call_rejected(err_flag)) return;
+    const int b = blockIdx.y;
+    const int hv = blockIdx.x / tiles_per_head;
+    const int tile = blockIdx.x - hv * tiles_per_head;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int sub = lane & 7;
+    const int row0 = tile * (32 * RPL) + wave * 8 + (lane >> 3);   // + 32 r
+    const int32_t s = slot[b];
+    OT* ob = out + (static_cast<size_t>(b) * HV + hv) * dv;
+
+    if (s <= 0) {                             // inactive row: zeros, state untouched
+        if (sub == 0) {
+#pragma unroll
+            for (int r = 0; r < RPL; ++r) {
+                const int row = row0 + 32 * r;
+                if (row < dv) elem<OT>::st(ob + row, 0.0f);
+            }
+        }
+        return;
+    }
+
+    const int D = 2 * H * DK + HV * dv;
+    const int h = hv / (HV / H);
+    const YT* yb = y + static_cast<size_t>(b) * D;
+    float* Sb = rec + (static_cast<size_t>(s) * HV + hv) * static_cast<size_t>(dv) * DK;
+
+    // 1. issue the state loads first (the long-latency HBM traffic)
+    float4 S[RPL][NV];
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+        const int row = row0 + 32 * r;
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            S[r][i] = (row < dv)
+                ? *reinterpret_cast<const float4*>(Sb + static_cast<size_t>(row) * DK + 32 * i + 4 * sub)
+                : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+
+    // 2. q, k fragments of key head h (L2-resident activations) and their norms
+    float4 qf[NV], kf[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        qf[i] = load4<YT>(yb + h * DK + 32 * i + 4 * sub);
+        kf[i] = load4<YT>(yb + H * DK + h * DK + 32 * i + 4 * sub);
+    }
+    float qmul = scale, kmul = 1.0f;
+    if (flags & GDN_FLAG_QK_L2NORM) {
+        float sq = 0.f, sk = 0.f;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            sq = fmaf(qf[i].x, qf[i].x, sq); sq = fmaf(qf[i].y, qf[i].y, sq);
+            sq = fmaf(qf[i].z, qf[i].z, sq); sq = fmaf(qf[i].w, qf[i].w, sq);
+            sk = fmaf(kf[i].x, kf[i].x, sk); sk = fmaf(kf[i].y, kf[i].y, sk);
+            sk = fmaf(kf[i].z, kf[i].z, sk); sk = fmaf(kf[i].w, kf[i].w, sk);
+        }
+        sq = sum8(sq);
+        sk = sum8(sk);
+        qmul = scale / sqrtf(sq + 1e-6f);
+        kmul = 1.0f / sqrtf(sk + 1e-6f);
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        qf[i].x *= qmul; qf[i].y *= qmul; qf[i].z *= qmul; qf[i].w *= qmul;
+        kf[i].x *= kmul; kf[i].y *= kmul; kf[i].z *= kmul; kf[i].w *= kmul;
+    }
+
+    const float alpha = expf(g[static_cast<size_t>(b) * HV + hv]);
+    const float bt = beta[static_cast<size_t>(b) * HV + hv];
+    const YT* vb = yb + 2 * H * DK + hv * dv;
+
+    // 3. per row: decay, predict, delta update, output
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+        const int row = row0 + 32 * r;
+        const float vv = (row < dv) ? elem<YT>::ld(vb + row) : 0.0f;
+        float u = 0.f;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            S[r][i].x *= alpha; S[r][i].y *= alpha; S[r][i].z *= alpha; S[r][i].w *= alpha;
+            u = fmaf(S[r][i].x, kf[i].x, u); u = fmaf(S[r][i].y, kf[i].y, u);
+            u = fmaf(S[r][i].z, kf[i].z, u); u = fmaf(S[r][i].w, kf[i].w, u);
+        }
+        u = sum8(u);
+        const float delta = bt * (vv - u);
+        float o = 0.f;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            S[r][i].x = fmaf(delta, kf[i].x, S[r][i].x); S[r][i].y = fmaf(delta, kf[i].y, S[r][i].y);
+            S[r][i].z = fmaf(delta, kf[i].z, S[r][i].z); S[r][i].w = fmaf(delta, kf[i].w, S[r][i].w);
+            o = fmaf(S[r][i].x, qf[i].x, o); o = fmaf(S[r][i].y, qf[i].y, o);
+            o = fmaf(S[r][i].z, qf[i].z, o); o = fmaf(S[r][i].w, qf[i].w, o);
+        }
+        o = sum8(o);
+        if (row < dv) {
+#pragma unroll
+            for (int i = 0; i < NV; ++i)
+                *reinterpret_cast<float4*>(Sb + static_cast<size_t>(row) * DK + 32 * i + 4 * sub) = S[r][i];
+            if (sub == 0) elem<OT>::st(ob + row, o);
+        }
+    }
+}
+
+namespace {
+struct RecArgs {
+    const void* y; const float* g; const float* beta; const int32_t* slot; int32_t batch;
+    float* rec; void* out; const gdn_dims* d; float scale; int32_t flags; const int32_t* err;
+    hipStream_t st;
+};
+
+template <int DK, int RPL, typename YT, typename OT>
+hipError_t run_rec(const RecArgs& a) {
+    const int rows_per_wg = 32 * RPL;
+    const int tiles = (a.d->head_v_dim + rows_per_wg - 1) / rows_per_wg;
+    dim3 grid(a.d->num_v_heads * tiles, a.batch);
+    return launch(decode_rec_kernel<DK, RPL, YT, OT>, grid, dim3(256), 0, a.st,
+                  static_cast<const YT*>(a.y), a.g, a.beta, a.slot, a.rec,
+                  static_cast<OT*>(a.out), a.d->num_k_heads, a.d->num_v_heads,
+                  a.d->head_v_dim, tiles, a.scale, a.flags, a.err);
+}
+
+// Rows per lane: as many 32-row steps as the head needs (up to 4), so one
+// workgroup streams a whole head of up to 128 rows; the per-row arithmetic is
+// identical for every choice.
+template <int DK, typename YT, typename OT>
+hipError_t pick_rpl(const RecArgs& a) {
+    const int dv = a.d->head_v_dim;
+    if (dv > 64) return run_rec<DK, 4, YT, OT>(a);
+    if (dv > 32) return run_rec<DK, 2, YT, OT>(a);
+    return run_rec<DK, 1, YT, OT>(a);
+}
+
+template <typename YT, typename OT>
+hipError_t pick_dk(const RecArgs& a) {
+    switch (a.d->head_k_dim) {
+        case 32: return pick_rpl<32, YT, OT>(a);
+        case 64: return pick_rpl<64, YT, OT>(a);
+        case 128: return pick_rpl<128, YT, OT>(a);
+        case 256: return pick_rpl<256, YT, OT>(a);
+        default: return hipErrorInvalidValue;
+    }
+}
+}  // namespace
+
+hipError_t launch_decode_rec(const void* y, gdn_dtype y_dt, const float* g, const float* beta,
+                             const int32_t* slot_idx, int32_t batch, float* rec_state,
+                             void* out, gdn_dtype out_dt, const gdn_dims& dims, float scale,
+                             int32_t flags, const int32_t* err_flag, hipStream_t stream) {
+    if (batch == 0) return hipSuccess;
+    const RecArgs a{y, g, beta, slot_idx, batch, rec_state, out, &dims, scale, flags, err_flag,
+                    stream};
+    if (y_dt == GDN_BF16)
+        return out_dt == GDN_BF16 ? pick_dk<bf16_t, bf16_t>(a) : pick_dk<bf16_t, float>(a);
+    return out_dt == GDN_BF16 ? pick_dk<float, bf16_t>(a) : pick_dk<float, float>(a);
+}
+
+}  // namespace gdn

@@ -1,0 +1,68 @@
+// gdn_device.hpp -- device helpers shared by the gfx950 GDN kernels.
+//
+// bf16 is carried as raw uint16_t bits: widening is exact (bits << 16) and
+// narrowing rounds to nearest, ties to even, quieting NaNs.  Reductions inside
+// a wavefront use DPP lane permutations in a fixed butterfly, so every lane of
+// a group ends with the bitwise-same sum and the order never depends on the
+// batch, the grid or the tile (the property the batch-invariance tests of
+// RL-Kernel PR #469, "L1, and the bf16 recurrent state", ask of a golden).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef uint16_t bf16_t;
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) {
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);  // NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<bf16_t>(u >> 16);
+}
+
+// Typed load/store of one element as fp32.
+template <typename T> struct elem;
+template <> struct elem<float> {
+    __device__ __forceinline__ static float ld(const float* p) { return *p; }
+    __device__ __forceinline__ static void st(float* p, float v) { *p = v; }
+};
+template <> struct elem<bf16_t> {
+    __device__ __forceinline__ static float ld(const bf16_t* p) { return bf16_to_f32(*p); }
+    __device__ __forceinline__ static void st(bf16_t* p, float v) { *p = f32_to_bf16(v); }
+};
+
+// DPP controls (GCN/CDNA encoding).
+constexpr int DPP_QUAD_XOR1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141; // lane i <- lane 7-i within each 8
+constexpr int DPP_ROW_MIRROR = 0x140;  // lane i <- lane 15-i within each 16
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over each aligned group of 8 lanes; every lane of the group receives the
+// bitwise-identical total (fp addition is commutative, and each step pairs
+// lanes symmetrically).
+__device__ __forceinline__ float sum8(float x) {
+    x = x + dpp<DPP_QUAD_XOR1>(x);
+    x = x + dpp<DPP_QUAD_XOR2>(x);
+    x = x + dpp<DPP_HALF_MIRROR>(x);
+    return x;
+}
+
+// Device-side validation result: nonzero means fail closed.
+__device__ __forceinline__ bool call_rejected(const int32_t* err_flag) {
+    return err_flag != nullptr && __builtin_nontemporal_load(err_flag) != 0;
+}
+
+__device__ __forceinline__ float silu(float y) { return y / (1.0f + expf(-y)); }
+
+}  // namespace gdn

@@ -1,0 +1,53 @@
+// gdn_internal.hpp -- host-side launchers shared between the translation
+// units of libgdn.so (not part of the public ABI; see include/gdn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <tuple>
+#include <utility>
+
+#include "gdn.h"
+
+namespace gdn {
+
+// Launch with the error of THIS launch returned (not a stale runtime error).
+template <typename... KArgs, typename... Args>
+hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem,
+                  hipStream_t stream, Args&&... args) {
+    static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
+    std::tuple<KArgs...> a(std::forward<Args>(args)...);
+    void* p[sizeof...(KArgs) > 0 ? sizeof...(KArgs) : 1];
+    std::apply([&](auto&... e) { int i = 0; ((p[i++] = static_cast<void*>(&e)), ...); }, a);
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, p, shmem, stream);
+}
+
+// Writes *err_flag (0 or GDN_EFLAG_* bits) for n slot indices and, when cu is
+// non-null, cu_seqlens[n + 1] against total.
+hipError_t launch_validate(const int32_t* slot_idx, int32_t n, int32_t num_slots,
+                           const int32_t* cu_seqlens, int32_t total, int32_t* err_flag,
+                           hipStream_t stream);
+
+// Conv update, one token per row (decode).  out_dt may be GDN_F32 / GDN_BF16.
+hipError_t launch_conv_decode(const void* x, gdn_dtype x_dt, const int32_t* slot_idx,
+                              int32_t rows, void* conv_state, gdn_dtype cs_dt,
+                              const void* weight, const void* bias, gdn_dtype w_dt,
+                              void* out, gdn_dtype out_dt, int32_t dim, int32_t flags,
+                              const int32_t* err_flag, hipStream_t stream);
+
+// Conv update over token runs described by cu_seqlens.
+hipError_t launch_conv_varlen(const void* x, gdn_dtype x_dt, const int32_t* cu_seqlens,
+                              int32_t n_seqs, const int32_t* slot_idx, void* conv_state,
+                              gdn_dtype cs_dt, const void* weight, const void* bias,
+                              gdn_dtype w_dt, void* out, gdn_dtype out_dt, int32_t dim,
+                              int32_t flags, const int32_t* err_flag, hipStream_t stream);
+
+// Gated delta-rule decode update from the post-conv activations y [B, D].
+hipError_t launch_decode_rec(const void* y, gdn_dtype y_dt, const float* g, const float* beta,
+                             const int32_t* slot_idx, int32_t batch, float* rec_state,
+                             void* out, gdn_dtype out_dt, const gdn_dims& dims, float scale,
+                             int32_t flags, const int32_t* err_flag, hipStream_t stream);
+
+}  // namespace gdn

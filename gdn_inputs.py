@@ -79,9 +79,7 @@ def decode_inputs(batch, num_slots, H=16, HV=32, dk=128, dv=128, W=4,
     if state_std == 0:
         rec = torch.zeros(num_slots, HV, dv, dk, device=dev)
     else:
-        rec = torch.empty(num_slots, HV, dv, dk, device=dev)
-        for s in range(num_slots):      # per slot keeps peak memory at one slab
-            rec[s].normal_(0.0, state_std, generator=gen)
+        rec = torch.randn(num_slots, HV, dv, dk, generator=gen, device=dev).mul_(state_std)
     return dict(mixed_qkv=x.to(act_dtype), g=g.float(), beta=beta.float(),
                 slot_idx=slots, conv_state=conv_state, conv_weight=weight,
                 conv_bias=bias, rec_state=rec,

@@ -1,0 +1,232 @@
+/*
+ * gdn.h -- C ABI of libgdn.so, the MI355X (gfx950) Gated DeltaNet core.
+ *
+ * Operations, each a thin host layer over hand-written HIP kernels:
+ *   gdn_conv_update      causal depthwise conv1d over a slot-indexed conv cache
+ *   gdn_decode_step      one decode token per row: conv -> SiLU -> q/k L2 norm
+ *                        -> gated delta-rule update of a slot-indexed fp32 state
+ *   gdn_decode_recurrent the recurrent half of the decode step alone
+ *   gdn_prefill_chunked  varlen chunked (64-token, WY/UT) prefill on post-conv
+ *                        q/k/v, reading and writing the same state cache
+ *
+ * Sources (pages, by title and section):
+ *   [P1] RL-Kernel PR #469 "C6: GDN decode-step goldens and recurrent/conv
+ *        state contract": "Summary" (gating, GQA map, QK norm, state layouts),
+ *        "State ABI: index validation and the two NULL_BLOCK_ID contracts",
+ *        "The conv half: coverage and the two mismatch mechanisms".
+ *   [P2] "A reduction barrier makes Qwen GDN graph replay bit exact" (replay
+ *        determinism; inactive rows and slot 0 left untouched).
+ *   [P4] vLLM PR #53864, "Numerical root cause and fix" (16x16 lower-
+ *        triangular KK^T diagonal-block inverses in the chunked prefill).
+ *   The recurrence is the gated delta rule
+ *        S_t = exp(g_t) S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *        o_t = S_t q_t,
+ *   computed as S1 = exp(g) S, u = S1 k, S' = S1 + beta (v - u) k^T, o = S' q.
+ *
+ * Conventions common to every call
+ *   - Every tensor is caller-owned DEVICE memory, dense, row-major (C order),
+ *     at least 16-byte aligned.  The library never allocates, frees or
+ *     synchronises; each call only enqueues kernels on `stream` (a
+ *     hipStream_t; NULL = the default stream) and returns.
+ *   - Caches are updated in place.  Outputs must not alias any input.  Within
+ *     one call each active slot may appear at most once ([P1] "State ABI").
+ *   - Slot indices: s <= 0 marks an inactive (padded) row: its outputs are
+ *     written as zeros and no cache entry is read or written.  Slot 0 is the
+ *     reserved null block and is never addressed ([P1] "State ABI"; [P2]).
+ *   - Synchronous status (gdn_status): what the host can check without reading
+ *     device memory -- null pointers, dims, dtypes, alignment, workspace size.
+ *     On any status other than GDN_OK nothing was enqueued.
+ *   - Device-side validation: with GDN_FLAG_VALIDATE set, a first kernel
+ *     checks the slot indices (and cu_seqlens) and WRITES *err_flag (0 when
+ *     clean, else GDN_EFLAG_* bits).  When any bit is set every later kernel
+ *     of the call returns before touching outputs or caches (fail closed).
+ *     err_flag is then a required int32 device pointer; read it after the
+ *     stream completes.  Without the flag, indices are trusted (as the
+ *     serving providers of [P1] do) and err_flag may be NULL.
+ *   - Results are bitwise reproducible run to run and batch-invariant: a row's
+ *     outputs and cache updates do not depend on which other rows share the
+ *     call, their order, or the batch size (fixed per-row reduction order, no
+ *     split reductions, no atomics on data).
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_NULL = 1,       /* a required pointer is NULL                        */
+    GDN_ERR_DIMS = 2,       /* unsupported or inconsistent sizes                 */
+    GDN_ERR_DTYPE = 3,      /* unsupported dtype (combination)                   */
+    GDN_ERR_ALIGN = 4,      /* a pointer is not 16-byte aligned                  */
+    GDN_ERR_WORKSPACE = 5,  /* workspace NULL or smaller than *_workspace_size   */
+    GDN_ERR_LAUNCH = 6,     /* the HIP runtime refused a kernel launch           */
+    GDN_ERR_FLAGS = 7       /* unknown flag bits, or VALIDATE without err_flag   */
+} gdn_status;
+
+enum {
+    GDN_FLAG_SILU = 1,      /* SiLU after the conv (decode step, conv update)    */
+    GDN_FLAG_QK_L2NORM = 2, /* q, k <- x / sqrt(sum(x*x) + 1e-6) before use      */
+    GDN_FLAG_VALIDATE = 4   /* device-side index validation, see above           */
+};
+
+enum {                      /* bits written to *err_flag under GDN_FLAG_VALIDATE */
+    GDN_EFLAG_SLOT_RANGE = 1,   /* an active slot >= num_slots                   */
+    GDN_EFLAG_SLOT_REPEAT = 2,  /* an active slot appears twice                  */
+    GDN_EFLAG_SEQLENS = 4       /* cu_seqlens[0] != 0, decreasing, or last != total */
+};
+
+/* Head geometry.  conv channel count D = 2*num_k_heads*head_k_dim +
+   num_v_heads*head_v_dim, channel order [q | k | v], each head-major with the
+   head dimension contiguous.  Value head hv reads key head hv / (HV / H)
+   ([P1] "How the golden relates to the kernel": no repeat_interleave).
+   Supported: head_k_dim in {32, 64, 128, 256}; head_v_dim a multiple of 32,
+   at most 256; HV a multiple of H; conv_width == 4. */
+typedef struct {
+    int32_t num_k_heads;   /* H  */
+    int32_t num_v_heads;   /* HV */
+    int32_t head_k_dim;    /* dk */
+    int32_t head_v_dim;    /* dv */
+    int32_t conv_width;    /* W  */
+} gdn_dims;
+
+/*
+ * gdn_conv_update -- causal depthwise conv1d with per-slot left context
+ * ([P1] "Summary": conv state [num_blocks, dim, W-1]; "The conv half").
+ *
+ *   x           [total_tokens, dim], x_dt
+ *   cu_seqlens  [n_seqs + 1] int32 token offsets, or NULL: one token per row
+ *               (n_seqs == total_tokens, decode)
+ *   slot_idx    [n_seqs] int32 (<= 0 inactive)
+ *   conv_state  [num_slots, dim, width-1], cs_dt, oldest tap first.  Rolled in
+ *               place to the last width-1 raw inputs of each active sequence
+ *               (an exact copy in cs_dt: bit-exact roll); a zero-length active
+ *               sequence leaves its state unchanged.
+ *   weight      [dim, width], bias [dim] or NULL, both w_dt.  Tap j multiplies
+ *               X[t + j] where X = [conv_state row, tokens]: tap width-1 is the
+ *               current token.
+ *   out         [total_tokens, dim], out_dt:
+ *               y = bias + sum_j weight[c, j] X[t + j] accumulated in fp32 in
+ *               tap order j = 0..W-1 starting from the bias, then SiLU when
+ *               GDN_FLAG_SILU; rows of inactive sequences are zeros.
+ *   dtypes      x, conv_state, weight: GDN_F32 or GDN_BF16 each; out likewise.
+ *   flags       GDN_FLAG_SILU | GDN_FLAG_VALIDATE.
+ */
+gdn_status gdn_conv_update(const void* x, gdn_dtype x_dt,
+                           const int32_t* cu_seqlens, int32_t n_seqs, int32_t total_tokens,
+                           const int32_t* slot_idx,
+                           void* conv_state, gdn_dtype cs_dt, int32_t num_slots,
+                           const void* weight, const void* bias, gdn_dtype w_dt,
+                           void* out, gdn_dtype out_dt,
+                           int32_t dim, int32_t width, int32_t flags,
+                           int32_t* err_flag, void* stream);
+
+/*
+ * gdn_decode_workspace_size -- bytes of device workspace gdn_decode_step needs
+ * for `batch` rows (the fp32 post-conv activations, batch * D * 4 bytes,
+ * rounded up to 256).  Returns 0 for unsupported dims.
+ */
+size_t gdn_decode_workspace_size(const gdn_dims* dims, int32_t batch);
+
+/*
+ * gdn_decode_step -- one decode token per row ([P1] "Summary"; the decode-only
+ * step: conv update, SiLU, split, QK norm with scale on q, recurrent update).
+ *
+ *   mixed_qkv    [batch, D], x_dt (GDN_F32 or GDN_BF16)
+ *   g, beta      [batch, HV] fp32: alpha = exp(g) decays the state, beta is
+ *                the write strength (already gated by the caller)
+ *   slot_idx     [batch] int32 (<= 0 inactive: zero output, caches untouched)
+ *   conv_state   [num_slots, D, W-1] cs_dt; conv_weight [D, W], conv_bias [D]
+ *                or NULL, w_dt
+ *   rec_state    [num_slots, HV, dv, dk] fp32 (S[v][k], k fastest), in place
+ *   out          [batch, HV, dv], out_dt (GDN_F32 or GDN_BF16)
+ *   scale        multiplies q after the norm (k is never scaled); usually
+ *                dk^-1/2
+ *   flags        GDN_FLAG_SILU | GDN_FLAG_QK_L2NORM | GDN_FLAG_VALIDATE
+ *   workspace    >= gdn_decode_workspace_size(dims, batch) bytes of device
+ *                memory, contents irrelevant; not retained after the call
+ */
+gdn_status gdn_decode_step(const void* mixed_qkv, gdn_dtype x_dt,
+                           const float* g, const float* beta,
+                           const int32_t* slot_idx, int32_t batch,
+                           void* conv_state, gdn_dtype cs_dt,
+                           const void* conv_weight, const void* conv_bias, gdn_dtype w_dt,
+                           float* rec_state, int32_t num_slots,
+                           void* out, gdn_dtype out_dt,
+                           const gdn_dims* dims, float scale, int32_t flags,
+                           void* workspace, size_t workspace_bytes,
+                           int32_t* err_flag, void* stream);
+
+/*
+ * gdn_decode_recurrent -- the recurrent half of the decode step alone, on
+ * post-conv activations (the split of [P1] "Which provider this aligns to":
+ * conv update, then the packed recurrent decode on mixed q|k|v):
+ * split [q | k | v] -> QK norm (flag) -> scale q -> gated delta rule on
+ * rec_state[slot] -> o.  gdn_decode_step == gdn_conv_update (one token per
+ * row, SiLU, fp32 output) followed by this call, bit for bit.
+ *
+ *   qkv          [batch, D], qkv_dt (GDN_F32 or GDN_BF16)
+ *   g, beta      [batch, HV] fp32; slot_idx [batch] int32 (<= 0 inactive)
+ *   rec_state    [num_slots, HV, dv, dk] fp32, in place
+ *   out          [batch, HV, dv], out_dt
+ *   flags        GDN_FLAG_QK_L2NORM | GDN_FLAG_VALIDATE
+ */
+gdn_status gdn_decode_recurrent(const void* qkv, gdn_dtype qkv_dt,
+                                const float* g, const float* beta,
+                                const int32_t* slot_idx, int32_t batch,
+                                float* rec_state, int32_t num_slots,
+                                void* out, gdn_dtype out_dt,
+                                const gdn_dims* dims, float scale, int32_t flags,
+                                int32_t* err_flag, void* stream);
+
+/*
+ * gdn_prefill_workspace_size -- bytes of device workspace gdn_prefill_chunked
+ * needs for n_seqs sequences and total_tokens tokens.  Returns 0 for
+ * unsupported dims.
+ */
+size_t gdn_prefill_workspace_size(const gdn_dims* dims, int32_t n_seqs, int32_t total_tokens);
+
+/*
+ * gdn_prefill_chunked -- varlen chunked prefill on post-conv q, k, v.
+ * Equal (to rounding) to running the decode recurrence token by token; the
+ * sequence is cut into 64-token chunks, each handled in WY/UT form with
+ * inverses of the 16x16 lower-triangular KK^T diagonal blocks by exact fp32
+ * forward substitution ([P4] "Numerical root cause and fix"), and the state is
+ * carried from chunk to chunk.
+ *
+ *   q, k         [total_tokens, H, dk]; v [total_tokens, HV, dv]; in_dt
+ *   g, beta      [total_tokens, HV] fp32
+ *   cu_seqlens   [n_seqs + 1] int32; slot_idx [n_seqs] int32 (<= 0 inactive:
+ *                zero outputs, state untouched)
+ *   rec_state    [num_slots, HV, dv, dk] fp32: each active sequence starts
+ *                from rec_state[slot] and its final state is written back
+ *                there (zero-fill a fresh slot first)
+ *   out          [total_tokens, HV, dv], out_dt
+ *   scale, flags as for gdn_decode_step (GDN_FLAG_QK_L2NORM, GDN_FLAG_VALIDATE)
+ *   workspace    >= gdn_prefill_workspace_size(...) bytes of device memory
+ */
+gdn_status gdn_prefill_chunked(const void* q, const void* k, const void* v, gdn_dtype in_dt,
+                               const float* g, const float* beta,
+                               const int32_t* cu_seqlens, int32_t n_seqs, int32_t total_tokens,
+                               const int32_t* slot_idx,
+                               float* rec_state, int32_t num_slots,
+                               void* out, gdn_dtype out_dt,
+                               const gdn_dims* dims, float scale, int32_t flags,
+                               void* workspace, size_t workspace_bytes,
+                               int32_t* err_flag, void* stream);
+
+/* gdn_strerror -- static, NUL-terminated description of a status code. */
+const char* gdn_strerror(gdn_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

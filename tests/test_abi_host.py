@@ -1,0 +1,130 @@
+"""CPU tests of the C ABI: the library loads, exports every function that
+include/gdn.h declares, and rejects bad arguments synchronously (before any
+kernel launch, so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_deltanet_recurrent_gdn_amd as gdn
+from gated_deltanet_recurrent_gdn_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+OK, ERR_NULL, ERR_DIMS, ERR_DTYPE, ERR_ALIGN, ERR_WS, ERR_LAUNCH, ERR_FLAGS = range(8)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return gdn.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(names) == set(_abi.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_strerror(lib):
+    for code in range(8):
+        assert gdn.gdn_strerror(code)
+    assert gdn.gdn_strerror(99) == "unknown status"
+
+
+def test_workspace_sizes(lib):
+    d = gdn.make_dims(16, 32, 128, 128, 4)
+    assert gdn.gdn_decode_workspace_size(d, 256) == 256 * 8192 * 4
+    assert gdn.gdn_decode_workspace_size(d, 0) == 0
+    assert gdn.gdn_decode_workspace_size(gdn.make_dims(16, 32, 100, 128, 4), 4) == 0
+    assert gdn.gdn_decode_workspace_size(gdn.make_dims(16, 30, 128, 128, 4), 4) == 0
+
+
+def _dims(H=16, HV=32, dk=128, dv=128, W=4):
+    return ctypes.byref(gdn.make_dims(H, HV, dk, dv, W))
+
+
+FAKE = ctypes.c_void_p(0x10000)          # aligned, never dereferenced (rejected first)
+MISALIGNED = ctypes.c_void_p(0x10004)
+
+
+def _decode(lib, dims=None, batch=4, flags=3, x=FAKE, rec=FAKE, ws=FAKE, ws_bytes=1 << 30,
+            err=None, x_dt=1, out_dt=0):
+    return lib.gdn_decode_step(x, x_dt, FAKE, FAKE, FAKE, batch, FAKE, 1, FAKE, None, 1, rec,
+                               8, FAKE, out_dt, dims or _dims(), 0.1, flags, ws, ws_bytes, err,
+                               None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dims=_dims(dk=100)), ERR_DIMS),
+    (dict(dims=_dims(HV=24, H=16)), ERR_DIMS),
+    (dict(dims=_dims(dv=48)), ERR_DIMS),
+    (dict(dims=_dims(W=3)), ERR_DIMS),
+    (dict(batch=-1), ERR_DIMS),
+    (dict(batch=70000), ERR_DIMS),
+    (dict(x_dt=5), ERR_DTYPE),
+    (dict(out_dt=2), ERR_DTYPE),
+    (dict(flags=64), ERR_FLAGS),
+    (dict(flags=7, err=None), ERR_FLAGS),          # VALIDATE without err_flag
+    (dict(x=None), ERR_NULL),
+    (dict(ws=None), ERR_NULL),
+    (dict(rec=MISALIGNED), ERR_ALIGN),
+    (dict(ws_bytes=16), ERR_WS),
+])
+def test_decode_step_rejects(lib, kw, code):
+    assert _decode(lib, **kw) == code
+
+
+def test_decode_step_empty_batch_is_ok(lib):
+    # batch 0 without validation enqueues nothing at all
+    assert _decode(lib, batch=0, x=None, rec=None, ws=None) == OK
+
+
+def test_conv_update_rejects(lib):
+    f = lib.gdn_conv_update
+    # width other than 4
+    assert f(FAKE, 1, None, 4, 4, FAKE, FAKE, 1, 8, FAKE, None, 1, FAKE, 0, 64, 3, 1, None,
+             None) == ERR_DIMS
+    # decode form needs total_tokens == n_seqs
+    assert f(FAKE, 1, None, 4, 5, FAKE, FAKE, 1, 8, FAKE, None, 1, FAKE, 0, 64, 4, 1, None,
+             None) == ERR_DIMS
+    # unknown flag (QK norm does not apply to the conv)
+    assert f(FAKE, 1, None, 4, 4, FAKE, FAKE, 1, 8, FAKE, None, 1, FAKE, 0, 64, 4, 2, None,
+             None) == ERR_FLAGS
+    assert f(FAKE, 1, None, 4, 4, None, FAKE, 1, 8, FAKE, None, 1, FAKE, 0, 64, 4, 1, None,
+             None) == ERR_NULL
+    assert f(FAKE, 7, None, 4, 4, FAKE, FAKE, 1, 8, FAKE, None, 1, FAKE, 0, 64, 4, 1, None,
+             None) == ERR_DTYPE
+
+
+def test_decode_recurrent_rejects(lib):
+    f = lib.gdn_decode_recurrent
+    assert f(FAKE, 0, FAKE, FAKE, FAKE, 4, FAKE, 8, FAKE, 0, _dims(), 0.1, 1, None,
+             None) == ERR_FLAGS                      # SiLU is not part of this call
+    assert f(MISALIGNED, 0, FAKE, FAKE, FAKE, 4, FAKE, 8, FAKE, 0, _dims(), 0.1, 2, None,
+             None) == ERR_ALIGN
+    assert f(FAKE, 0, FAKE, FAKE, FAKE, 4, FAKE, 8, FAKE, 0, _dims(dk=48), 0.1, 2, None,
+             None) == ERR_DIMS
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    d = gdn.make_dims(2, 4, 32, 32, 4)
+    x = torch.zeros(1, 2 * 2 * 32 + 4 * 32)
+    with pytest.raises(TypeError):
+        gdn.gdn_decode_recurrent(x, torch.zeros(1, 4), torch.zeros(1, 4),
+                                 torch.ones(1, dtype=torch.int32), torch.zeros(2, 4, 32, 32),
+                                 torch.zeros(1, 4, 32), d, 0.1)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(ImportError):
+        _abi.load_library(str(tmp_path / "libgdn_missing.so"))
