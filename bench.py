@@ -117,6 +117,24 @@ class DecodeSetup:
                             flags=flags, workspace=self.ws,
                             err_flag=self.err if validate else None)
 
+    def capture(self, validate=False):
+        """One HIP graph holding one step per slot set (replayed as a unit)."""
+        torch = self.torch
+        self.i = 0
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):          # warm the capture path once
+            self.step(validate)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        self.i = 0
+        with torch.cuda.graph(graph):
+            for _ in range(len(self.slot_sets)):
+                self.step(validate)
+        torch.cuda.synchronize()
+        return graph, len(self.slot_sets)
+
     def prepare_rec(self):
         gdn = self.gdn
         d = self.d
@@ -130,6 +148,48 @@ class DecodeSetup:
         self.i += 1
         gdn.gdn_decode_recurrent(self.y, d["g"], d["beta"], slots, d["rec_state"], self.out,
                                  self.dims, self.scale)
+
+
+class PrefillSetup:
+    """The varlen prefill workload: 8 sequences, lengths uniform in [512, 8192]."""
+
+    def __init__(self, seed, dev):
+        import torch
+        import gdn_inputs as gi
+        import gated_deltanet_recurrent_gdn_amd as gdn
+        self.torch, self.gdn = torch, gdn
+        gen = torch.Generator().manual_seed(seed)
+        self.lengths = gi.seqlens_uniform(8, 512, 8192, gen)
+        p = gi.prefill_inputs(self.lengths, 16, seed=seed)
+        self.p = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in p.items()}
+        self.T = int(sum(self.lengths))
+        self.dims = gdn.make_dims(H, HV, DK, DV, W)
+        self.out = torch.empty(self.T, HV, DV, dtype=torch.bfloat16, device=dev)
+        self.err = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def step(self, validate=False):
+        gdn = self.gdn
+        p = self.p
+        flags = gdn.FLAG_QK_L2NORM | (gdn.FLAG_VALIDATE if validate else 0)
+        gdn.gdn_prefill_chunked(p["q"], p["k"], p["v"], p["g"], p["beta"], p["cu_seqlens"],
+                                p["slot_idx"], p["rec_state"], self.out, self.dims, DK ** -0.5,
+                                flags=flags, err_flag=self.err if validate else None)
+
+
+def time_graph(torch, graph, per_replay, steps, warmup):
+    """Replay a captured graph of `per_replay` steps; per-step ms for each replay."""
+    for _ in range(max(1, warmup // per_replay)):
+        graph.replay()
+    torch.cuda.synchronize()
+    n = max(1, -(-steps // per_replay))
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for i in range(n):
+        starts[i].record()
+        graph.replay()
+        ends[i].record()
+    torch.cuda.synchronize()
+    return [s.elapsed_time(e) / per_replay for s, e in zip(starts, ends)]
 
 
 def time_loop(torch, fn, steps, warmup):
@@ -175,6 +235,25 @@ def cpu_baseline(budget_s):
                       "single-threaded fp64 C"}
 
 
+def cpu_baseline_prefill(budget_s):
+    """The fp64 oracle prefill on the first 512 tokens of the prefill workload's
+    first sequence (all 32 value heads), repeated until the budget is spent."""
+    import gdn_inputs as gi
+    import oracle
+    p = gi.prefill_inputs([512], 2, seed=3)
+    args = [p[k].double().numpy() for k in ("q", "k", "v", "g", "beta")]
+    rec = p["rec_state"].double().numpy().copy()
+    toks = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        oracle.prefill(*args, p["cu_seqlens"].numpy(), p["slot_idx"].numpy(), rec, DK ** -0.5)
+        toks += 512
+    dt = time.perf_counter() - t0
+    return {"value": round(toks / dt, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{toks} prefill tokens (512-token sequence, H=16 HV=32 d=128) in "
+                      f"{dt:.1f} s, single-threaded fp64 C, token by token"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -189,42 +268,62 @@ def main():
 
     big = DecodeSetup(256, 2048, seed=2, dev="cuda")
     small = DecodeSetup(16, 256, seed=1, dev="cuda")
+    pre = PrefillSetup(seed=3, dev="cuda")
     torch.cuda.synchronize()
 
-    # headline: decode step, batch 256
-    ms_big = time_loop(torch, lambda: big.step(args.validate), args.steps, args.warmup)
-    ms_small = time_loop(torch, lambda: small.step(args.validate), args.steps, args.warmup)
-    # dominant kernel alone (the recurrence), same rotation
+    # decode buckets: graph replay of one step per disjoint slot set
+    g_big, r_big = big.capture(args.validate)
+    g_small, r_small = small.capture(args.validate)
+    ms_big = time_graph(torch, g_big, r_big, args.steps, args.warmup)
+    ms_small = time_graph(torch, g_small, r_small, args.steps, args.warmup)
+    # prefill, eager (one call is milliseconds)
+    ms_pre = time_loop(torch, lambda: pre.step(args.validate), args.steps, args.warmup)
+    # dominant kernel alone (the decode recurrence), eager launches with events
     big.prepare_rec()
     ms_rec = time_loop(torch, big.rec_step, args.steps, args.warmup)
     torch.cuda.synchronize()
 
+    mean = lambda xs: sum(xs) / len(xs)  # noqa: E731
     med = lambda xs: sorted(xs)[len(xs) // 2]  # noqa: E731
     step_bytes_big = 256 * decode_bytes_per_seq() + conv_weight_bytes()
     step_bytes_small = 16 * decode_bytes_per_seq() + conv_weight_bytes()
-    mean_big = sum(ms_big) / len(ms_big)
-    gbs_big = step_bytes_big / (mean_big * 1e-3) / 1e9
-    gbs_small = step_bytes_small / (sum(ms_small) / len(ms_small) * 1e-3) / 1e9
-    rec_ms = sum(ms_rec) / len(ms_rec)
+    gbs_big = step_bytes_big / (mean(ms_big) * 1e-3) / 1e9
+    gbs_small = step_bytes_small / (mean(ms_small) * 1e-3) / 1e9
+    rec_ms = mean(ms_rec)
     rec_bytes = 256 * rec_bytes_per_seq()
     rec_gbs = rec_bytes / (rec_ms * 1e-3) / 1e9
+    pre_ms = mean(ms_pre)
+    pre_flops = prefill_flops(pre.lengths)
+    pre_bytes = prefill_bytes(pre.T, len(pre.lengths))
+    pre_tps = pre.T / (pre_ms * 1e-3)
+    pre_tflops = pre_flops / (pre_ms * 1e-3) / 1e12
 
     extra = {
-        "decode_b256_ms_mean": round(mean_big, 5), "decode_b256_ms_median": round(med(ms_big), 5),
+        "decode_b256_ms_mean": round(mean(ms_big), 5), "decode_b256_ms_median": round(med(ms_big), 5),
         "decode_b256_ms_min": round(min(ms_big), 5), "decode_b256_ms_max": round(max(ms_big), 5),
         "decode_b256_bytes_per_step": step_bytes_big,
         "decode_b256_pct_hbm_peak": round(100 * gbs_big / HBM_PEAK_GBS, 2),
         "decode_b16_GBps": round(gbs_small, 2),
-        "decode_b16_ms_mean": round(sum(ms_small) / len(ms_small), 5),
+        "decode_b16_ms_mean": round(mean(ms_small), 5),
         "decode_b16_pct_hbm_peak": round(100 * gbs_small / HBM_PEAK_GBS, 2),
+        "decode_timing": "HIP graph replay, one step per disjoint slot set "
+                         f"({r_big} sets at batch 256, {r_small} at batch 16)",
+        "prefill_tokens": pre.T, "prefill_lengths": pre.lengths,
+        "prefill_ms_mean": round(pre_ms, 4), "prefill_ms_min": round(min(ms_pre), 4),
+        "prefill_tokens_per_s": round(pre_tps, 1),
+        "prefill_TFLOPs": round(pre_tflops, 2),
+        "prefill_pct_mfma_peak": round(100 * pre_tflops / BF16_PEAK_TFLOPS, 2),
+        "prefill_algorithmic_flops": pre_flops, "prefill_algorithmic_bytes": pre_bytes,
+        "prefill_pct_hbm_peak": round(100 * pre_bytes / (pre_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
         "validate": bool(args.validate),
     }
 
-    total_ms = sum(ms_big) / len(ms_big) + sum(ms_small) / len(ms_small)
+    total_ms = mean(ms_big) + mean(ms_small) + pre_ms
 
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args.cpu_seconds)
+        extra["cpu_baseline_prefill"] = cpu_baseline_prefill(max(4.0, args.cpu_seconds / 2))
 
     line = {
         "metric": "GDN decode HBM GB/s (% peak) at batch 16/256; prefill tokens/s (% MFMA)",
@@ -240,7 +339,9 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "GDN decode step, batch 256 of a 2048-slot cache, H=16 HV=32 "
-                               "d=128, conv width 4 (D=8192), bf16 conv cache, fp32 state",
+                               "d=128, conv width 4 (D=8192), bf16 conv cache, fp32 state; "
+                               "step also runs decode batch 16 and the 8-sequence varlen "
+                               "prefill (see extra)",
                    "global_batch": 256, "seq_len": 1, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "kernel": "decode_rec_kernel",
                      "achieved": round(rec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",

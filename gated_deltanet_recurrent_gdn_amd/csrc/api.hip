@@ -155,15 +155,39 @@ gdn_status gdn_decode_recurrent(const void* qkv, gdn_dtype qkv_dt, const float* 
 }
 
 size_t gdn_prefill_workspace_size(const gdn_dims* dims, int32_t n_seqs, int32_t total_tokens) {
+    // The fused prefill keeps every intermediate on chip: no workspace.
     (void)dims; (void)n_seqs; (void)total_tokens;
     return 0;
 }
 
-gdn_status gdn_prefill_chunked(const void*, const void*, const void*, gdn_dtype, const float*,
-                               const float*, const int32_t*, int32_t, int32_t, const int32_t*,
-                               float*, int32_t, void*, gdn_dtype, const gdn_dims*, float, int32_t,
-                               void*, size_t, int32_t*, void*) {
-    return GDN_ERR_DIMS;
+gdn_status gdn_prefill_chunked(const void* q, const void* k, const void* v, gdn_dtype in_dt,
+                               const float* g, const float* beta, const int32_t* cu_seqlens,
+                               int32_t n_seqs, int32_t total_tokens, const int32_t* slot_idx,
+                               float* rec_state, int32_t num_slots, void* out, gdn_dtype out_dt,
+                               const gdn_dims* dims, float scale, int32_t flags, void* workspace,
+                               size_t workspace_bytes, int32_t* err_flag, void* stream) {
+    (void)workspace; (void)workspace_bytes;
+    if (gdn_status st = check_flags(flags, GDN_FLAG_QK_L2NORM | GDN_FLAG_VALIDATE, err_flag))
+        return st;
+    if (gdn_status st = check_dims(dims)) return st;
+    if (n_seqs < 0 || n_seqs > 65535 || total_tokens < 0 || num_slots < 1) return GDN_ERR_DIMS;
+    if (!dtype_ok(in_dt) || !dtype_ok(out_dt)) return GDN_ERR_DTYPE;
+    if (dims->head_k_dim != dims->head_v_dim ||
+        (dims->head_k_dim != 64 && dims->head_k_dim != 128))
+        return GDN_ERR_DIMS;
+    if (!prefill_supported(*dims, in_dt)) return GDN_ERR_DTYPE;
+    if (n_seqs > 0 && (!cu_seqlens || !slot_idx || !rec_state)) return GDN_ERR_NULL;
+    if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !out)) return GDN_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(rec_state))
+        return GDN_ERR_ALIGN;
+    auto s = static_cast<hipStream_t>(stream);
+    if (flags & GDN_FLAG_VALIDATE)
+        GDN_TRY_LAUNCH(launch_validate(slot_idx, n_seqs, num_slots, cu_seqlens, total_tokens,
+                                       err_flag, s));
+    const int32_t* ef = (flags & GDN_FLAG_VALIDATE) ? err_flag : nullptr;
+    GDN_TRY_LAUNCH(launch_prefill(q, k, v, in_dt, g, beta, cu_seqlens, n_seqs, slot_idx,
+                                  rec_state, out, out_dt, *dims, scale, flags, ef, s));
+    return GDN_OK;
 }
 
 }  // extern "C"

@@ -50,4 +50,12 @@ hipError_t launch_decode_rec(const void* y, gdn_dtype y_dt, const float* g, cons
                              void* out, gdn_dtype out_dt, const gdn_dims& dims, float scale,
                              int32_t flags, const int32_t* err_flag, hipStream_t stream);
 
+// Chunked prefill: one workgroup per (sequence, value head).
+bool prefill_supported(const gdn_dims& d, gdn_dtype in_dt);
+hipError_t launch_prefill(const void* q, const void* k, const void* v, gdn_dtype in_dt,
+                          const float* g, const float* beta, const int32_t* cu, int32_t n_seqs,
+                          const int32_t* slot, float* rec, void* out, gdn_dtype out_dt,
+                          const gdn_dims& d, float scale, int32_t flags, const int32_t* err,
+                          hipStream_t st);
+
 }  // namespace gdn

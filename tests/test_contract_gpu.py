@@ -54,12 +54,20 @@ def test_null_slots_untouched():
 @pytest.mark.parametrize("bad,bit", [("range", gdn.EFLAG_SLOT_RANGE),
                                      ("repeat", gdn.EFLAG_SLOT_REPEAT)])
 def test_validation_fails_closed(bad, bit):
-    d = to_dev(gi.decode_inputs(9, 32, seed=10))
+    # 33 slots of memory, 32 exposed: slot 32 is out of range for the call but
+    # still allocated, so a missed check could not fault
+    d = gi.decode_inputs(9, 32, seed=10)
+    d["rec_state"] = torch.cat([d["rec_state"], torch.randn(1, *d["rec_state"].shape[1:])])
+    d["conv_state"] = torch.cat([d["conv_state"], d["conv_state"][:1]])
+    d = to_dev(d)
+    full = {k: d[k] for k in ("rec_state", "conv_state")}
+    for k in full:
+        d[k] = full[k][:32]
     if bad == "range":
         d["slot_idx"][4] = 32
     else:
         d["slot_idx"][6] = d["slot_idx"][2]
-    before = {k: d[k].clone() for k in ("rec_state", "conv_state")}
+    before = {k: v.clone() for k, v in full.items()}
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     out = run_decode_gpu(d, SCALE, flags=gdn.DEFAULT_DECODE_FLAGS | gdn.FLAG_VALIDATE,
                          err_flag=err)
@@ -67,7 +75,7 @@ def test_validation_fails_closed(bad, bit):
     assert int(err.item()) & bit
     assert torch.isnan(out).all(), "a rejected call must not write the output"
     for k, v in before.items():
-        assert torch.equal(v, d[k]), f"{k} mutated by a rejected call"
+        assert torch.equal(v, full[k]), f"{k} mutated by a rejected call"
 
 
 def test_validation_clean_call_writes_zero():
@@ -168,3 +176,41 @@ def test_replay_under_concurrent_load():
         h = (fnv64(o), fnv64(d["conv_state"]), fnv64(d["rec_state"]))
         ref = ref or h
         assert h == ref, i
+
+
+def test_graph_replay_matches_eager():
+    """A captured HIP graph of the decode step reproduces the eager results on
+    every replay, with eager work and synchronisations between replays (the
+    step enqueues kernels only: no allocation, no memset)."""
+    base = to_dev(gi.decode_inputs(32, 48, seed=14))
+    dims = gdn.make_dims(16, 32, 128, 128, 4)
+    ws = torch.empty(gdn.gdn_decode_workspace_size(dims, 32), dtype=torch.uint8, device="cuda")
+    # eager reference: three consecutive steps from the base caches
+    ref = _clone(base)
+    ref_out = []
+    for _ in range(3):
+        o = torch.empty(32, 32, 128, device="cuda")
+        gdn.gdn_decode_step(ref["mixed_qkv"], ref["g"], ref["beta"], ref["slot_idx"],
+                            ref["conv_state"], ref["conv_weight"], ref["rec_state"], o, dims,
+                            SCALE, workspace=ws)
+        ref_out.append(o)
+    torch.cuda.synchronize()
+    # graph of one step over live buffers, replayed three times
+    live = _clone(base)
+    out = torch.empty(32, 32, 128, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gdn.gdn_decode_step(live["mixed_qkv"], live["g"], live["beta"], live["slot_idx"],
+                            live["conv_state"], live["conv_weight"], live["rec_state"], out,
+                            dims, SCALE, workspace=ws)
+    torch.cuda.synchronize()
+    for i in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out[i]), f"replay {i} output"
+        _ = torch.randn(1024, 1024, device="cuda").sum().item()   # eager work between
+    assert torch.equal(live["rec_state"], ref["rec_state"])
+    assert torch.equal(live["conv_state"], ref["conv_state"])

@@ -1,0 +1,201 @@
+"""GPU parity of the chunked prefill against the fp64 token-by-token oracle.
+
+Bar: output and final state at max|err| / max|ref| <= 5e-3.  Cases: ragged
+lengths around the 16- and 64-token boundaries with random initial states;
+the 8-sequence varlen workload (lengths uniform in [512, 8192], H=16, HV=32,
+d=128) and the correlated-key stress case (k_t = normalise(base + 0.05 N),
+beta = 0.9, g = 0, zero state; vLLM PR #53864, "Test Plan") at 64 and 16384
+tokens, both checked against the oracle on sampled value heads (each head's
+recurrence is independent) with every output checked finite; inactive and
+empty sequences; fail-closed validation; bitwise run-to-run reproducibility.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gdn_inputs as gi
+import gated_deltanet_recurrent_gdn_amd as gdn
+import oracle
+from gpu_helpers import PREFILL_TOL, f64, fnv64, rel_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run_prefill_gpu(p, scale, out_dtype=torch.bfloat16, flags=gdn.FLAG_QK_L2NORM,
+                    err_flag=None):
+    dm = p["dims"]
+    dims = gdn.make_dims(dm["H"], dm["HV"], dm["dk"], dm["dv"], 4)
+    T = p["q"].shape[0]
+    out = torch.full((T, dm["HV"], dm["dv"]), float("nan"), dtype=out_dtype, device="cuda")
+    gdn.gdn_prefill_chunked(p["q"], p["k"], p["v"], p["g"], p["beta"], p["cu_seqlens"],
+                            p["slot_idx"], p["rec_state"], out, dims, scale, flags=flags,
+                            err_flag=err_flag)
+    return out
+
+
+def oracle_heads(p_cpu, heads, scale, flags=oracle.FLAG_QK_L2NORM):
+    """Oracle on a subset of value heads, each as a one-head problem with its key
+    head (hv // (HV / H)); returns o [T, len(heads), dv] and final states
+    [n_seqs, len(heads), dv, dk] in the order of slot_idx."""
+    dm = p_cpu["dims"]
+    grp = dm["HV"] // dm["H"]
+    slots = p_cpu["slot_idx"].numpy()
+    n = len(slots)
+    outs, states = [], []
+    for hv in heads:
+        h = hv // grp
+        rec = np.zeros((n + 1, 1, dm["dv"], dm["dk"]))
+        comp = np.where(slots > 0, np.arange(1, n + 1), slots).astype(np.int32)
+        for i, s in enumerate(slots):
+            if s > 0:
+                rec[i + 1, 0] = f64(p_cpu["rec_state"][s, hv])
+        o = oracle.prefill(f64(p_cpu["q"][:, h:h + 1]), f64(p_cpu["k"][:, h:h + 1]),
+                           f64(p_cpu["v"][:, hv:hv + 1]), f64(p_cpu["g"][:, hv:hv + 1]),
+                           f64(p_cpu["beta"][:, hv:hv + 1]), p_cpu["cu_seqlens"].numpy(), comp,
+                           rec, scale, flags=flags)
+        outs.append(o[:, 0])
+        states.append(rec[1:, 0])
+    return np.stack(outs, 1), np.stack(states, 1)
+
+
+def check_heads(p_cpu, p_gpu, out, heads, scale, tol=PREFILL_TOL, flags=oracle.FLAG_QK_L2NORM):
+    o_ref, s_ref = oracle_heads(p_cpu, heads, scale, flags=flags)
+    o = f64(out[:, heads])
+    eo = rel_err(o, o_ref)
+    slots = p_cpu["slot_idx"].tolist()
+    act = [i for i, s in enumerate(slots) if s > 0]
+    sg = np.stack([f64(p_gpu["rec_state"][slots[i]][heads]) for i in act]) if act else None
+    es = rel_err(sg, s_ref[act]) if act else 0.0
+    assert eo <= tol, f"output rel err {eo:.3e}"
+    assert es <= tol, f"state rel err {es:.3e}"
+    return eo, es
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_prefill_ragged(d, out_dtype):
+    lengths = [1, 15, 16, 17, 63, 64, 65, 130, 200]
+    p = gi.prefill_inputs(lengths, 12, H=2, HV=4, dk=d, dv=d, seed=5, state_std=0.1)
+    g = to_dev(p)
+    out = run_prefill_gpu(g, d ** -0.5, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    eo, es = check_heads(p, g, out, list(range(4)), d ** -0.5)
+    print(f"ragged d={d} {out_dtype}: out {eo:.2e} state {es:.2e}")
+
+
+def test_prefill_norm_flag_off():
+    p = gi.prefill_inputs([70, 64, 5], 6, H=2, HV=4, dk=128, dv=128, seed=6,
+                          qk_normalised=True)
+    g = to_dev(p)
+    out = run_prefill_gpu(g, 128 ** -0.5, out_dtype=torch.float32, flags=0)
+    torch.cuda.synchronize()
+    check_heads(p, g, out, list(range(4)), 128 ** -0.5, flags=0)
+
+
+@pytest.fixture(scope="module")
+def varlen_workload():
+    gen = torch.Generator().manual_seed(3)
+    lengths = gi.seqlens_uniform(8, 512, 8192, gen)
+    return gi.prefill_inputs(lengths, 16, seed=3)
+
+
+def test_prefill_varlen_full_size(varlen_workload):
+    p = varlen_workload
+    g = to_dev(p)
+    out = run_prefill_gpu(g, 128 ** -0.5)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    eo, es = check_heads(p, g, out, [0, 13, 31], 128 ** -0.5)
+    print(f"varlen T={p['q'].shape[0]}: out {eo:.2e} state {es:.2e}")
+
+
+@pytest.mark.parametrize("T,heads", [(64, list(range(32))), (16384, [0, 17, 30])])
+def test_prefill_correlated_keys(T, heads):
+    p = gi.stress_prefill_inputs(T)
+    g = to_dev(p)
+    out = run_prefill_gpu(g, 128 ** -0.5)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    assert torch.isfinite(g["rec_state"]).all()
+    eo, es = check_heads(p, g, out, heads, 128 ** -0.5)
+    print(f"stress T={T}: out {eo:.2e} state {es:.2e}")
+
+
+def test_prefill_inactive_and_empty():
+    p = gi.prefill_inputs([40, 0, 70, 33], 8, H=2, HV=4, dk=64, dv=64, seed=8)
+    p["slot_idx"][2] = 0                    # inactive sequence of 70 tokens
+    g = to_dev(p)
+    before = g["rec_state"].clone()
+    out = run_prefill_gpu(g, 0.125)
+    torch.cuda.synchronize()
+    cu = p["cu_seqlens"].tolist()
+    assert torch.all(out[cu[2]:cu[3]] == 0)
+    untouched = [s for s in range(8) if s not in (int(p["slot_idx"][0]), int(p["slot_idx"][3]))]
+    assert torch.equal(before[untouched], g["rec_state"][untouched])
+    check_heads(p, g, out, list(range(4)), 0.125)
+
+
+@pytest.mark.parametrize("bad", ["range", "repeat", "seqlens"])
+def test_prefill_validation_fails_closed(bad):
+    # 9 slots of memory, 8 exposed: an index of 8 is out of range for the call
+    # but still lands in allocated memory, so a missed check cannot fault
+    p = gi.prefill_inputs([40, 50, 60], 8, H=2, HV=4, dk=64, dv=64, seed=9)
+    p["rec_state"] = torch.cat([p["rec_state"], torch.randn(1, 4, 64, 64)])
+    if bad == "range":
+        p["slot_idx"][1] = 8
+    elif bad == "repeat":
+        p["slot_idx"][2] = p["slot_idx"][0]
+    else:
+        p["cu_seqlens"][1] = 95             # offsets 0, 95, 90, 150: decreasing
+    g = to_dev(p)
+    full = g["rec_state"]
+    g["rec_state"] = full[:8]
+    before = full.clone()
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = run_prefill_gpu(g, 0.125, flags=gdn.FLAG_QK_L2NORM | gdn.FLAG_VALIDATE, err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) != 0
+    assert torch.isnan(out.float()).all()
+    assert torch.equal(before, full)
+
+
+def test_prefill_reproducible(varlen_workload):
+    p = varlen_workload
+    hashes = set()
+    for _ in range(2):
+        g = to_dev(p)
+        out = run_prefill_gpu(g, 128 ** -0.5)
+        torch.cuda.synchronize()
+        hashes.add((fnv64(out), fnv64(g["rec_state"])))
+    assert len(hashes) == 1
+
+
+def test_prefill_then_decode_continues_state():
+    """Prefill of T tokens followed by a decode token equals the oracle run of
+    T + 1 tokens (the caches are the resume mechanism)."""
+    d = 128
+    p = gi.prefill_inputs([97, 130], 6, H=2, HV=4, dk=d, dv=d, seed=10)
+    g = to_dev(p)
+    run_prefill_gpu(g, d ** -0.5, out_dtype=torch.float32)
+    # one more token per sequence through the recurrent half of the decode step
+    gen = torch.Generator().manual_seed(11)
+    D = 2 * 2 * d + 4 * d
+    qkv = torch.randn(2, D, generator=gen)
+    gg = -torch.rand(2, 4, generator=gen)
+    bb = torch.sigmoid(torch.randn(2, 4, generator=gen))
+    dims = gdn.make_dims(2, 4, d, d, 4)
+    o = torch.empty(2, 4, d, device="cuda")
+    gdn.gdn_decode_recurrent(qkv.cuda(), gg.cuda(), bb.cuda(), g["slot_idx"], g["rec_state"], o,
+                             dims, d ** -0.5)
+    torch.cuda.synchronize()
+    # oracle: prefill, then one decode-recurrent token via a one-token prefill
+    rec = f64(p["rec_state"]).copy()
+    oracle.prefill(f64(p["q"]), f64(p["k"]), f64(p["v"]), f64(p["g"]), f64(p["beta"]),
+                   p["cu_seqlens"].numpy(), p["slot_idx"].numpy(), rec, d ** -0.5)
+    x = qkv.double().numpy()
+    o_ref = oracle.prefill(x[:, :2 * d].reshape(2, 2, d), x[:, 2 * d:4 * d].reshape(2, 2, d),
+                           x[:, 4 * d:].reshape(2, 4, d), gg.double().numpy(),
+                           bb.double().numpy(), [0, 1, 2], p["slot_idx"].numpy(), rec, d ** -0.5)
+    assert rel_err(f64(o), o_ref) <= PREFILL_TOL
+    act = p["slot_idx"].tolist()
+    assert rel_err(f64(g["rec_state"][act]), rec[act]) <= PREFILL_TOL
