@@ -19,12 +19,22 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t h) {
     return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
+// Round to nearest even (the hardware v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);  // NaN
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<bf16_t>(u >> 16);
+    return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
 }
+
+// Two floats to two packed bf16 (element a in the low half), one instruction.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    typedef __attribute__((ext_vector_type(2))) float f2;
+    typedef __attribute__((ext_vector_type(2))) __bf16 b2;
+    const f2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2));
+}
+
+// Widen the low / high bf16 of a packed pair.
+__device__ __forceinline__ float bf16lo_to_f32(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16hi_to_f32(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
 // Typed load/store of one element as fp32.
 template <typename T> struct elem;

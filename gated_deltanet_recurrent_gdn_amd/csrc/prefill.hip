@@ -47,25 +47,22 @@ __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f3
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// fp32 16x16x4: lane l supplies A[l%16][l/16] and B[l/16][l%16].
+__device__ __forceinline__ f32x4 mfma4(float a, float b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
-
-__device__ __forceinline__ uint32_t pack2(bf16_t lo, bf16_t hi) {
-    return static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
-}
-
-// Split four floats into packed bf16 hi parts and packed bf16 lo parts.
-__device__ __forceinline__ void split4(const f32x4& x, uint2& hi, uint2& lo) {
-    bf16_t h[4], l[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        h[j] = f32_to_bf16(x[j]);
-        l[j] = f32_to_bf16(x[j] - bf16_to_f32(h[j]));
-    }
-    hi = make_uint2(pack2(h[0], h[1]), pack2(h[2], h[3]));
-    lo = make_uint2(pack2(l[0], l[1]), pack2(l[2], l[3]));
-}
-
 __device__ __forceinline__ uint4 cat(uint2 a, uint2 b) { return make_uint4(a.x, a.y, b.x, b.y); }
+
+// Split four floats into packed bf16 hi parts and packed bf16 lo parts
+// (x = hi + lo to ~16 significant bits; x - hi is exact in fp32).
+__device__ __forceinline__ void split4(const f32x4& x, uint2& hi, uint2& lo) {
+    const uint32_t h01 = pack_bf16x2(x[0], x[1]), h23 = pack_bf16x2(x[2], x[3]);
+    hi = make_uint2(h01, h23);
+    lo = make_uint2(pack_bf16x2(x[0] - bf16lo_to_f32(h01), x[1] - bf16hi_to_f32(h01)),
+                    pack_bf16x2(x[2] - bf16lo_to_f32(h23), x[3] - bf16hi_to_f32(h23)));
+}
 
 // Standard-slot fragment: 8 consecutive bf16 at row `row`, column c0 + 8q.
 __device__ __forceinline__ bf16x8 frag_std(const bf16_t* base, int stride, int row, int c0, int q) {
@@ -78,7 +75,7 @@ __device__ __forceinline__ bf16x8 frag_perm(const bf16_t* base, int stride, int 
     return as_bf16x8(cat(a, b));
 }
 
-template <int DK, int DV, typename IT, typename OT>
+template <int DK, int DV>
 struct PrefillSmem {
     static constexpr int SK = DK + PADB;        // row stride of K, Q, W (bf16)
     static constexpr int ST = CH + PADB;        // row stride of K^T, V^T, coefficient arrays
@@ -87,19 +84,19 @@ struct PrefillSmem {
     bf16_t q[CH * SK];                          // Q   [t][k]
     bf16_t kt[DK * ST];                         // K^T [k][t]
     bf16_t vt_w[(DV * ST > CH * SK) ? DV * ST : CH * SK];   // V^T [v][t], later -W [t][k]
-    float g[CH * SF];                           // K K^T -> A -> T (and merge scratch)
+    float g[CH * SF];                           // A, then T in place (lower, unit diag, zero upper)
     union {
-        float p[CH * SF];                       // Q K^T
         bf16_t c[4 * CH * ST];                  // cW hi, cW lo, cU hi, cU lo   [t][t']
+        float x[32 * 36];                       // merge scratch X
     } pc;
     bf16_t mp[2 * CH * ST];                     // (M o P) hi, lo   [t][t']
     float gam[CH], beta[CH], rk[CH], rq[CH], eg[CH], ck[CH], cwc[CH];
     float egl;
 };
 
-template <int DK, int DV, typename IT, typename OT>
+template <int DK, int DV, typename OT>
 __global__ __launch_bounds__(256) void prefill_kernel(
-    const IT* __restrict__ qg, const IT* __restrict__ kg, const IT* __restrict__ vg,
+    const bf16_t* __restrict__ qg, const bf16_t* __restrict__ kg, const bf16_t* __restrict__ vg,
     const float* __restrict__ gg, const float* __restrict__ bg, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ slot, float* __restrict__ rec, OT* __restrict__ out, int32_t H,
     int32_t HV, float scale, int32_t flags, const int32_t* __restrict__ err_flag) {
@@ -109,7 +106,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     constexpr int VB = DV / 16 / NW;             // value blocks (16 wide) per wave
     constexpr int KB = DK / 16;                  // key blocks (16 tall)
     constexpr int KS = DK / 32;                  // k-steps over DK
-    using Sm = PrefillSmem<DK, DV, IT, OT>;
+    using Sm = PrefillSmem<DK, DV>;
     constexpr int SK = Sm::SK, ST = Sm::ST, SF = Sm::SF;
     __shared__ Sm sm;
 
@@ -125,6 +122,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     const int32_t t0 = cu[n];
     const int32_t t1 = cu[n + 1];
     const int32_t s = slot[n];
+    const bool norm = (flags & GDN_FLAG_QK_L2NORM) != 0;
 
     if (s <= 0) {                                // inactive: zero outputs, state untouched
         for (int64_t i = tid; i < static_cast<int64_t>(t1 - t0) * DV; i += 256) {
@@ -149,44 +147,131 @@ __global__ __launch_bounds__(256) void prefill_kernel(
             st[kb][vb] = f32x4{x.x, x.y, x.z, x.w};
         }
 
+    // Chunk loads.  Thread (tp, cg) moves token rows 2tp, 2tp+1 at columns
+    // 8 (cg + 8 pass); K^T / V^T receive 32-bit (t, t+1) pairs, so the 64 lanes
+    // of a wave store to 64 distinct banks.  The next chunk's loads are issued
+    // during the current chunk's state update and staged at the loop top.
+    const int tp = tid & 31;
+    const int cg = tid >> 5;                     // 0..7
+    const int ta = 2 * tp, tb2 = 2 * tp + 1;
+    constexpr int KP = DK / 64, VP = DV / 64;    // column passes
+    uint4 pk[KP][2], pq[KP][2], pv[VP][2];
+    float pbeta = 0.0f, pg = 0.0f;
+    auto fetch = [&](int32_t c, int Lc) {
+#pragma unroll
+        for (int pass = 0; pass < KP; ++pass) {
+            const int k0 = 8 * (cg + 8 * pass);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int t = ta + e;
+                pk[pass][e] = make_uint4(0, 0, 0, 0);
+                pq[pass][e] = make_uint4(0, 0, 0, 0);
+                if (t < Lc) {
+                    const size_t off = (static_cast<size_t>(c + t) * H + h) * DK + k0;
+                    pk[pass][e] = *reinterpret_cast<const uint4*>(kg + off);
+                    pq[pass][e] = *reinterpret_cast<const uint4*>(qg + off);
+                }
+            }
+        }
+#pragma unroll
+        for (int pass = 0; pass < VP; ++pass) {
+            const int v0 = 8 * (cg + 8 * pass);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int t = ta + e;
+                pv[pass][e] = make_uint4(0, 0, 0, 0);
+                if (t < Lc)
+                    pv[pass][e] = *reinterpret_cast<const uint4*>(vg + (static_cast<size_t>(c + t) * HV + hv) * DV + v0);
+            }
+        }
+        pbeta = (tid < Lc) ? bg[static_cast<size_t>(c + tid) * HV + hv] : 0.0f;   // used by tid < 64
+        pg = (tid < Lc) ? gg[static_cast<size_t>(c + tid) * HV + hv] : 0.0f;      // used by wave 0
+    };
+    fetch(t0, min(CH, t1 - t0));
+
     for (int32_t c0 = t0; c0 < t1; c0 += CH) {
         const int L = min(CH, t1 - c0);
 
-        // ---------------- load the chunk: K, Q (row-major), K^T, V^T, g, beta
-        for (int i = tid; i < CH * DK / 8; i += 256) {
-            const int t = i / (DK / 8);
-            const int k0 = (i % (DK / 8)) * 8;
-            uint4 kv = make_uint4(0, 0, 0, 0), qv = make_uint4(0, 0, 0, 0);
-            if (t < L) {
-                const size_t off = (static_cast<size_t>(c0 + t) * H + h) * DK + k0;
-                kv = *reinterpret_cast<const uint4*>(kg + off);
-                qv = *reinterpret_cast<const uint4*>(qg + off);
+        // ---------------- stage the fetched chunk into LDS
+#pragma unroll
+        for (int pass = 0; pass < KP; ++pass) {
+            const int k0 = 8 * (cg + 8 * pass);
+            *reinterpret_cast<uint4*>(&sm.k[ta * SK + k0]) = pk[pass][0];
+            *reinterpret_cast<uint4*>(&sm.k[tb2 * SK + k0]) = pk[pass][1];
+            *reinterpret_cast<uint4*>(&sm.q[ta * SK + k0]) = pq[pass][0];
+            *reinterpret_cast<uint4*>(&sm.q[tb2 * SK + k0]) = pq[pass][1];
+            const uint32_t* a32 = reinterpret_cast<const uint32_t*>(&pk[pass][0]);
+            const uint32_t* b32 = reinterpret_cast<const uint32_t*>(&pk[pass][1]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                *reinterpret_cast<uint32_t*>(&sm.kt[(k0 + 2 * j) * ST + ta]) =
+                    (a32[j] & 0xffffu) | (b32[j] << 16);
+                *reinterpret_cast<uint32_t*>(&sm.kt[(k0 + 2 * j + 1) * ST + ta]) =
+                    (a32[j] >> 16) | (b32[j] & 0xffff0000u);
             }
-            *reinterpret_cast<uint4*>(&sm.k[t * SK + k0]) = kv;
-            *reinterpret_cast<uint4*>(&sm.q[t * SK + k0]) = qv;
-            const bf16_t* kb16 = reinterpret_cast<const bf16_t*>(&kv);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) sm.kt[(k0 + j) * ST + t] = kb16[j];
         }
-        for (int i = tid; i < CH * DV / 8; i += 256) {
-            const int t = i / (DV / 8);
-            const int v0 = (i % (DV / 8)) * 8;
-            uint4 vv = make_uint4(0, 0, 0, 0);
-            if (t < L) vv = *reinterpret_cast<const uint4*>(vg + (static_cast<size_t>(c0 + t) * HV + hv) * DV + v0);
-            const bf16_t* vb16 = reinterpret_cast<const bf16_t*>(&vv);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) sm.vt_w[(v0 + j) * ST + t] = vb16[j];
+        for (int pass = 0; pass < VP; ++pass) {
+            const int v0 = 8 * (cg + 8 * pass);
+            const uint32_t* a32 = reinterpret_cast<const uint32_t*>(&pv[pass][0]);
+            const uint32_t* b32 = reinterpret_cast<const uint32_t*>(&pv[pass][1]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                *reinterpret_cast<uint32_t*>(&sm.vt_w[(v0 + 2 * j) * ST + ta]) =
+                    (a32[j] & 0xffffu) | (b32[j] << 16);
+                *reinterpret_cast<uint32_t*>(&sm.vt_w[(v0 + 2 * j + 1) * ST + ta]) =
+                    (a32[j] >> 16) | (b32[j] & 0xffff0000u);
+            }
         }
-        if (tid < CH) {
-            const bool ok = tid < L;
-            sm.beta[tid] = ok ? bg[static_cast<size_t>(c0 + tid) * HV + hv] : 0.0f;
-            sm.gam[tid] = ok ? gg[static_cast<size_t>(c0 + tid) * HV + hv] : 0.0f;
+        if (tid < CH) sm.beta[tid] = pbeta;
+        float gt = pg;                           // wave 0: this lane's g, scanned below
+        __syncthreads();
+
+        // ---------------- row norms (8 lanes per row, the decode kernel's order)
+        // and the cumulative log-decay (wave 0, a fixed-order inclusive scan)
+        for (int pass = 0; pass < 4; ++pass) {
+            const int rowid = pass * 32 + (tid >> 3);
+            const int sub = tid & 7;
+            const bf16_t* rowp = (rowid < CH) ? &sm.k[rowid * SK] : &sm.q[(rowid - CH) * SK];
+            float acc = 0.f;
+#pragma unroll
+            for (int i = 0; i < DK / 32; ++i) {
+                const uint2 u = *reinterpret_cast<const uint2*>(rowp + 32 * i + 4 * sub);
+                const float x0 = bf16lo_to_f32(u.x), x1 = bf16hi_to_f32(u.x);
+                const float x2 = bf16lo_to_f32(u.y), x3 = bf16hi_to_f32(u.y);
+                acc = fmaf(x0, x0, acc); acc = fmaf(x1, x1, acc);
+                acc = fmaf(x2, x2, acc); acc = fmaf(x3, x3, acc);
+            }
+            acc = sum8(acc);
+            if (sub == 0) {
+                if (rowid < CH) sm.rk[rowid] = norm ? 1.0f / sqrtf(acc + 1e-6f) : 1.0f;
+                else sm.rq[rowid - CH] = norm ? scale / sqrtf(acc + 1e-6f) : scale;
+            }
+        }
+        if (wave == 0) {
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const float y = __shfl_up(gt, d, 64);
+                if (lane >= d) gt += y;
+            }
+            sm.gam[lane] = gt;
         }
         __syncthreads();
 
-        // ---------------- G = K K^T and P = Q K^T (raw bf16, exact products)
+        // ---------------- per-token coefficients (wave 0) and, in every wave,
+        // G = K K^T, P = Q K^T on MFMA with the epilogue forming A (fp32 into
+        // sm.g) and M o P (hi/lo bf16 into sm.mp) straight from the accumulators
+        if (tid < CH) {
+            const float gl = sm.gam[L - 1];
+            const float gv = sm.gam[tid];
+            const float et = expf(gv);
+            sm.eg[tid] = et * sm.rq[tid];
+            sm.ck[tid] = (tid < L) ? expf(gl - gv) * sm.rk[tid] : 0.0f;
+            sm.cwc[tid] = sm.beta[tid] * et * sm.rk[tid];
+            if (tid == 0) sm.egl = expf(gl);
+        }
         {
-            const int tb = wave;                 // wave computes row block tb of G and P
+            const int tb = wave;
             f32x4 accg[4], accp[4];
 #pragma unroll
             for (int jb = 0; jb < 4; ++jb) { accg[jb] = f32x4{0, 0, 0, 0}; accp[jb] = f32x4{0, 0, 0, 0}; }
@@ -201,145 +286,139 @@ __global__ __launch_bounds__(256) void prefill_kernel(
                     accp[jb] = mfma(aq, bk, accp[jb]);
                 }
             }
+            float gr[4], brk[4], rqr[4];
 #pragma unroll
-            for (int jb = 0; jb < 4; ++jb)
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * tb + 4 * q4 + r;
+                gr[r] = sm.gam[i];
+                brk[r] = sm.beta[i] * sm.rk[i];
+                rqr[r] = sm.rq[i];
+            }
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb) {
+                const int c = 16 * jb + l16;
+                const float gc = sm.gam[c];
+                const float rkc = sm.rk[c];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    sm.g[(16 * tb + 4 * q4 + r) * SF + 16 * jb + l16] = accg[jb][r];
-                    sm.pc.p[(16 * tb + 4 * q4 + r) * SF + 16 * jb + l16] = accp[jb][r];
+                    const int i = 16 * tb + 4 * q4 + r;
+                    const float dec = (c <= i) ? expf(gr[r] - gc) : 0.0f;
+                    sm.g[i * SF + c] = (c < i) ? (brk[r] * rkc) * (dec * accg[jb][r]) : 0.0f;
+                    const float mp = (rqr[r] * rkc) * (dec * accp[jb][r]);
+                    const bf16_t hi = f32_to_bf16(mp);
+                    sm.mp[i * ST + c] = hi;
+                    sm.mp[CH * ST + i * ST + c] = f32_to_bf16(mp - bf16_to_f32(hi));
                 }
-        }
-        // ---------------- row norms (8 lanes per row, the decode kernel's order) + gamma
-        {
-            // 64 K rows then 64 Q rows; 256 threads = 32 rows per pass
-            for (int pass = 0; pass < 4; ++pass) {
-                const int rowid = pass * 32 + (tid >> 3);
-                const int sub = tid & 7;
-                const bf16_t* rowp = (rowid < CH) ? &sm.k[rowid * SK] : &sm.q[(rowid - CH) * SK];
-                float acc = 0.f;
-#pragma unroll
-                for (int i = 0; i < DK / 32; ++i)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float x = bf16_to_f32(rowp[32 * i + 4 * sub + e]);
-                        acc = fmaf(x, x, acc);
-                    }
-                acc = sum8(acc);
-                if (sub == 0) {
-                    if (rowid < CH)
-                        sm.rk[rowid] = (flags & GDN_FLAG_QK_L2NORM) ? 1.0f / sqrtf(acc + 1e-6f) : 1.0f;
-                    else
-                        sm.rq[rowid - CH] = (flags & GDN_FLAG_QK_L2NORM) ? scale / sqrtf(acc + 1e-6f) : scale;
-                }
-            }
-            if (tid == 0) {                      // cumulative log-decay, sequential order
-                float a = 0.f;
-                for (int t = 0; t < CH; ++t) { a += sm.gam[t]; sm.gam[t] = a; }
             }
         }
         __syncthreads();
 
-        // ---------------- per-token coefficient vectors
-        if (tid < CH) {
-            const float gl = sm.gam[L - 1];
-            const float gt = sm.gam[tid];
-            const float et = expf(gt);
-            sm.eg[tid] = et * sm.rq[tid];
-            sm.ck[tid] = (tid < L) ? expf(gl - gt) * sm.rk[tid] : 0.0f;
-            sm.cwc[tid] = sm.beta[tid] * et * sm.rk[tid];
-            if (tid == 0) sm.egl = expf(gl);
-        }
-        // ---------------- A (in sm.g) and M o P (split into sm.mp)
-        for (int i = tid; i < CH * CH; i += 256) {
-            const int r = i / CH, c = i % CH;
-            const float dec = (c <= r) ? expf(sm.gam[r] - sm.gam[c]) : 0.0f;
-            const float a = (c < r) ? sm.beta[r] * dec * (sm.g[r * SF + c] * (sm.rk[r] * sm.rk[c])) : 0.0f;
-            sm.g[r * SF + c] = a;
-            const float mp = dec * (sm.pc.p[r * SF + c] * (sm.rq[r] * sm.rk[c]));
-            const bf16_t hi = f32_to_bf16(mp);
-            sm.mp[r * ST + c] = hi;
-            sm.mp[CH * ST + r * ST + c] = f32_to_bf16(mp - bf16_to_f32(hi));
-        }
-        __syncthreads();
-
-        // ---------------- T = (I + A)^-1: diagonal 16x16 blocks by forward substitution
+        // ---------------- T = (I + A)^-1.  Diagonal 16x16 blocks by forward
+        // substitution (wave 0: lane = 16 block + column); the upper triangle of
+        // sm.g is zero from the epilogue above and stays zero.
         if (wave == 0) {
-            const int b = lane >> 4;             // block
-            const int c = lane & 15;             // column within the block
+            const int b = lane >> 4;
+            const int c = lane & 15;
+            const float* blk = &sm.g[(16 * b) * SF + 16 * b];
             float tc[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) tc[r] = (r == c) ? 1.0f : 0.0f;
 #pragma unroll
             for (int r = 1; r < 16; ++r) {
+                float arow[16];
+#pragma unroll
+                for (int j4 = 0; j4 < (r + 3) / 4; ++j4) {
+                    const float4 a4 = *reinterpret_cast<const float4*>(blk + r * SF + 4 * j4);
+                    arow[4 * j4] = a4.x; arow[4 * j4 + 1] = a4.y;
+                    arow[4 * j4 + 2] = a4.z; arow[4 * j4 + 3] = a4.w;
+                }
                 float acc = 0.f;
 #pragma unroll
-                for (int j = 0; j < r; ++j)
-                    acc = fmaf(sm.g[(16 * b + r) * SF + 16 * b + j], tc[j], acc);
+                for (int j = 0; j < r; ++j) acc = fmaf(arow[j], tc[j], acc);
                 tc[r] = (r > c) ? -acc : tc[r];
             }
 #pragma unroll
             for (int r = 0; r < 16; ++r) sm.g[(16 * b + r) * SF + 16 * b + c] = tc[r];
         }
         __syncthreads();
-        // merge 16 -> 32 for block pairs (0,1) and (2,3):  T21 = -T22 (A21 T11).
-        // X = A21 T11 goes to the (unused) upper block T[16p .. 16p+15][16p+16 ..].
-        for (int i = tid; i < 2 * 256; i += 256) {
-            const int p = i >> 8, e = i & 255, r = e >> 4, c = e & 15;
-            const int b0 = 32 * p, b1 = b0 + 16;
-            float acc = 0.f;
+        // merge 16 -> 32 for block pairs p = (0,1), (2,3) on fp32 MFMA (waves 0, 1):
+        // X = A21 T11 into the scratch area, then T21 = -T22 X
+        if (wave < 2) {
+            const int b0 = 32 * wave, b1 = b0 + 16;
+            f32x4 x = f32x4{0, 0, 0, 0};
 #pragma unroll
-            for (int j = 0; j < 16; ++j)
-                acc = fmaf(sm.g[(b1 + r) * SF + b0 + j], sm.g[(b0 + j) * SF + b0 + c], acc);
-            sm.g[(b0 + r) * SF + b1 + c] = acc;
-        }
-        __syncthreads();
-        for (int i = tid; i < 2 * 256; i += 256) {
-            const int p = i >> 8, e = i & 255, r = e >> 4, c = e & 15;
-            const int b0 = 32 * p, b1 = b0 + 16;
-            float acc = 0.f;
+            for (int kk = 0; kk < 4; ++kk)
+                x = mfma4(sm.g[(b1 + l16) * SF + b0 + 4 * kk + q4],
+                          sm.g[(b0 + 4 * kk + q4) * SF + b0 + l16], x);
 #pragma unroll
-            for (int j = 0; j < 16; ++j)
-                acc = fmaf(sm.g[(b1 + r) * SF + b1 + j], sm.g[(b0 + j) * SF + b1 + c], acc);
-            sm.g[(b1 + r) * SF + b0 + c] = -acc;
+            for (int r = 0; r < 4; ++r) sm.pc.x[(16 * wave + 4 * q4 + r) * 36 + l16] = x[r];
         }
         __syncthreads();
-        // merge 32 -> 64: X = A[32:64][0:32] T[0:32][0:32] -> T[0:32][32:64]
-        for (int i = tid; i < 1024; i += 256) {
-            const int r = i >> 5, c = i & 31;
-            float acc = 0.f;
-#pragma unroll 8
-            for (int j = 0; j < 32; ++j) {
-                const float tv = (j >= c) ? sm.g[j * SF + c] : 0.0f;   // T11 lower part only
-                acc = fmaf(sm.g[(32 + r) * SF + j], tv, acc);
-            }
-            sm.g[r * SF + 32 + c] = acc;
+        if (wave < 2) {
+            const int b0 = 32 * wave, b1 = b0 + 16;
+            f32x4 t = f32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                t = mfma4(sm.g[(b1 + l16) * SF + b1 + 4 * kk + q4],
+                          sm.pc.x[(16 * wave + 4 * kk + q4) * 36 + l16], t);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sm.g[(b1 + 4 * q4 + r) * SF + b0 + l16] = -t[r];
         }
         __syncthreads();
-        for (int i = tid; i < 1024; i += 256) {
-            const int r = i >> 5, c = i & 31;
-            float acc = 0.f;
-#pragma unroll 8
-            for (int j = 0; j < 32; ++j) {
-                const float tv = (r >= j) ? sm.g[(32 + r) * SF + 32 + j] : 0.0f;   // T22 lower
-                acc = fmaf(tv, sm.g[j * SF + 32 + c], acc);
+        // merge 32 -> 64 (wave = 16x16 output tile (ti, tj)): X = A[32:64][0:32] T11,
+        // T21 = -T22 X.  T11's block (0, 1) and T22's block (0, 1) are zero: skipped.
+        {
+            const int ti = wave >> 1, tj = wave & 1;
+            f32x4 x = f32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+                if (tj == 1 && kk < 4) continue;
+                x = mfma4(sm.g[(32 + 16 * ti + l16) * SF + 4 * kk + q4],
+                          sm.g[(4 * kk + q4) * SF + 16 * tj + l16], x);
             }
-            sm.g[(32 + r) * SF + c] = -acc;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sm.pc.x[(16 * ti + 4 * q4 + r) * 36 + 16 * tj + l16] = x[r];
+        }
+        __syncthreads();
+        {
+            const int ti = wave >> 1, tj = wave & 1;
+            f32x4 t = f32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+                if (ti == 0 && kk >= 4) continue;
+                t = mfma4(sm.g[(32 + 16 * ti + l16) * SF + 32 + 4 * kk + q4],
+                          sm.pc.x[(4 * kk + q4) * 36 + 16 * tj + l16], t);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sm.g[(32 + 16 * ti + 4 * q4 + r) * SF + 16 * tj + l16] = -t[r];
         }
         __syncthreads();
 
         // ---------------- coefficients cW = T diag(cwc), cU = T diag(beta), split
-        for (int i = tid; i < CH * CH; i += 256) {
-            const int r = i / CH, c = i % CH;
-            // T is lower triangular with unit diagonal; the upper part of sm.g
-            // holds merge scratch and is masked here.
-            const float tv = (c < r) ? sm.g[r * SF + c] : ((c == r) ? 1.0f : 0.0f);
-            const float w = tv * sm.cwc[c];
-            const float u = tv * sm.beta[c];
-            const bf16_t wh = f32_to_bf16(w), uh = f32_to_bf16(u);
-            sm.pc.c[0 * CH * ST + r * ST + c] = wh;
-            sm.pc.c[1 * CH * ST + r * ST + c] = f32_to_bf16(w - bf16_to_f32(wh));
-            sm.pc.c[2 * CH * ST + r * ST + c] = uh;
-            sm.pc.c[3 * CH * ST + r * ST + c] = f32_to_bf16(u - bf16_to_f32(uh));
+        // (thread: row r, 16 columns; T's upper triangle is exactly zero)
+        {
+            const int r = tid >> 2, cb = 16 * (tid & 3);
+            uint32_t wh[8], wl[8], uh[8], ul[8];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float4 t = *reinterpret_cast<const float4*>(&sm.g[r * SF + cb + 4 * j]);
+                const float4 cw = *reinterpret_cast<const float4*>(&sm.cwc[cb + 4 * j]);
+                const float4 bt = *reinterpret_cast<const float4*>(&sm.beta[cb + 4 * j]);
+                const f32x4 w = {t.x * cw.x, t.y * cw.y, t.z * cw.z, t.w * cw.w};
+                const f32x4 u = {t.x * bt.x, t.y * bt.y, t.z * bt.z, t.w * bt.w};
+                uint2 h2, l2;
+                split4(w, h2, l2); wh[2 * j] = h2.x; wh[2 * j + 1] = h2.y; wl[2 * j] = l2.x; wl[2 * j + 1] = l2.y;
+                split4(u, h2, l2); uh[2 * j] = h2.x; uh[2 * j + 1] = h2.y; ul[2 * j] = l2.x; ul[2 * j + 1] = l2.y;
+            }
+            bf16_t* base = sm.pc.c + r * ST + cb;
+            *reinterpret_cast<uint4*>(base + 0 * CH * ST) = make_uint4(wh[0], wh[1], wh[2], wh[3]);
+            *reinterpret_cast<uint4*>(base + 0 * CH * ST + 8) = make_uint4(wh[4], wh[5], wh[6], wh[7]);
+            *reinterpret_cast<uint4*>(base + 1 * CH * ST) = make_uint4(wl[0], wl[1], wl[2], wl[3]);
+            *reinterpret_cast<uint4*>(base + 1 * CH * ST + 8) = make_uint4(wl[4], wl[5], wl[6], wl[7]);
+            *reinterpret_cast<uint4*>(base + 2 * CH * ST) = make_uint4(uh[0], uh[1], uh[2], uh[3]);
+            *reinterpret_cast<uint4*>(base + 2 * CH * ST + 8) = make_uint4(uh[4], uh[5], uh[6], uh[7]);
+            *reinterpret_cast<uint4*>(base + 3 * CH * ST) = make_uint4(ul[0], ul[1], ul[2], ul[3]);
+            *reinterpret_cast<uint4*>(base + 3 * CH * ST + 8) = make_uint4(ul[4], ul[5], ul[6], ul[7]);
         }
         __syncthreads();
 
@@ -389,41 +468,39 @@ __global__ __launch_bounds__(256) void prefill_kernel(
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     sm.vt_w[(16 * tb + 4 * q4 + r) * SK + 16 * (wave * WB + kb) + l16] = f32_to_bf16(-w[tb][kb][r]);
-
-        // ---------------- split the state into hi/lo B fragments (permuted k-slots)
-        bf16x8 sh[KS][VB], sl[KS][VB];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-            for (int vb = 0; vb < VB; ++vb) {
-                uint2 h0, l0, h1, l1;
-                split4(st[2 * ks][vb], h0, l0);
-                split4(st[2 * ks + 1][vb], h1, l1);
-                sh[ks][vb] = as_bf16x8(cat(h0, h1));
-                sl[ks][vb] = as_bf16x8(cat(l0, l1));
-            }
         __syncthreads();                         // -W visible to all waves
 
-        // ---------------- U = Ut - W S0^T ;  O1 = Q S0^T
+        // ---------------- U = Ut - W S0^T ;  O1 = Q S0^T  (state split per k-step
+        // into hi/lo B fragments with permuted k-slots)
         f32x4 o[4][VB];
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
             for (int vb = 0; vb < VB; ++vb) o[tb][vb] = f32x4{0, 0, 0, 0};
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
+        for (int ks = 0; ks < KS; ++ks) {
+            bf16x8 sh[VB], sl[VB];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
+            for (int vb = 0; vb < VB; ++vb) {
+                uint2 h0, l0, h1, l1;
+                split4(st[2 * ks][vb], h0, l0);
+                split4(st[2 * ks + 1][vb], h1, l1);
+                sh[vb] = as_bf16x8(cat(h0, h1));
+                sl[vb] = as_bf16x8(cat(l0, l1));
+            }
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
                 const bf16x8 aw = frag_perm(sm.vt_w, SK, 16 * tb + l16, 32 * ks, q4);
                 const bf16x8 aq = frag_perm(sm.q, SK, 16 * tb + l16, 32 * ks, q4);
 #pragma unroll
                 for (int vb = 0; vb < VB; ++vb) {
-                    u[tb][vb] = mfma(aw, sh[ks][vb], u[tb][vb]);
-                    u[tb][vb] = mfma(aw, sl[ks][vb], u[tb][vb]);
-                    o[tb][vb] = mfma(aq, sh[ks][vb], o[tb][vb]);
-                    o[tb][vb] = mfma(aq, sl[ks][vb], o[tb][vb]);
+                    u[tb][vb] = mfma(aw, sh[vb], u[tb][vb]);
+                    u[tb][vb] = mfma(aw, sl[vb], u[tb][vb]);
+                    o[tb][vb] = mfma(aq, sh[vb], o[tb][vb]);
+                    o[tb][vb] = mfma(aq, sl[vb], o[tb][vb]);
                 }
             }
+        }
         // O1 rows scaled by e^gamma_t rq_t
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb)
@@ -474,6 +551,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(
                 }
             }
 
+        if (c0 + CH < t1) fetch(c0 + CH, min(CH, t1 - c0 - CH));   // next chunk, in flight
+
         // ---------------- S0^T <- e^{gamma_L} S0^T + K^T (cK . U)
         bf16x8 ch[2][VB], cl[2][VB];
 #pragma unroll
@@ -494,19 +573,22 @@ __global__ __launch_bounds__(256) void prefill_kernel(
             }
         const float egl = sm.egl;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+        for (int kb = 0; kb < KB; ++kb) {
+            bf16x8 ak[2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) ak[ks] = frag_perm(sm.kt, ST, 16 * kb + l16, 32 * ks, q4);
 #pragma unroll
             for (int vb = 0; vb < VB; ++vb) {
                 f32x4 acc = st[kb][vb];
                 acc[0] *= egl; acc[1] *= egl; acc[2] *= egl; acc[3] *= egl;
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
-                    const bf16x8 ak = frag_perm(sm.kt, ST, 16 * kb + l16, 32 * ks, q4);
-                    acc = mfma(ak, ch[ks][vb], acc);
-                    acc = mfma(ak, cl[ks][vb], acc);
+                    acc = mfma(ak[ks], ch[ks][vb], acc);
+                    acc = mfma(ak[ks], cl[ks][vb], acc);
                 }
                 st[kb][vb] = acc;
             }
+        }
         __syncthreads();                         // LDS is rewritten by the next chunk
     }
 
@@ -528,7 +610,7 @@ hipError_t run_prefill(const void* q, const void* k, const void* v, const float*
                        float* rec, void* out, const gdn_dims& d, float scale, int32_t flags,
                        const int32_t* err, hipStream_t st) {
     dim3 grid(d.num_v_heads, n_seqs);
-    return launch(prefill_kernel<D, D, bf16_t, OT>, grid, dim3(256), 0, st,
+    return launch(prefill_kernel<D, D, OT>, grid, dim3(256), 0, st,
                   static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
                   static_cast<const bf16_t*>(v), g, beta, cu, slot, rec, static_cast<OT*>(out),
                   d.num_k_heads, d.num_v_heads, scale, flags, err);
