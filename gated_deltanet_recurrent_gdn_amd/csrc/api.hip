@@ -172,9 +172,7 @@ gdn_status gdn_prefill_chunked(const void* q, const void* k, const void* v, gdn_
     if (gdn_status st = check_dims(dims)) return st;
     if (n_seqs < 0 || n_seqs > 65535 || total_tokens < 0 || num_slots < 1) return GDN_ERR_DIMS;
     if (!dtype_ok(in_dt) || !dtype_ok(out_dt)) return GDN_ERR_DTYPE;
-    if (dims->head_k_dim != dims->head_v_dim ||
-        (dims->head_k_dim != 64 && dims->head_k_dim != 128))
-        return GDN_ERR_DIMS;
+    if (dims->head_k_dim != dims->head_v_dim || dims->head_k_dim > 128) return GDN_ERR_DIMS;
     if (!prefill_supported(*dims, in_dt)) return GDN_ERR_DTYPE;
     if (n_seqs > 0 && (!cu_seqlens || !slot_idx || !rec_state)) return GDN_ERR_NULL;
     if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !out)) return GDN_ERR_NULL;

@@ -75,15 +75,47 @@ __device__ __forceinline__ bf16x8 frag_perm(const bf16_t* base, int stride, int 
     return as_bf16x8(cat(a, b));
 }
 
-template <int DK, int DV>
+// Eight fp32 values (two uint4 of bits) into packed bf16 hi and lo words.
+__device__ __forceinline__ void split8(const uint4& a, const uint4& b, uint4& hi, uint4& lo) {
+    const float f[8] = {__uint_as_float(a.x), __uint_as_float(a.y), __uint_as_float(a.z),
+                        __uint_as_float(a.w), __uint_as_float(b.x), __uint_as_float(b.y),
+                        __uint_as_float(b.z), __uint_as_float(b.w)};
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        h[j] = pack_bf16x2(f[2 * j], f[2 * j + 1]);
+        l[j] = pack_bf16x2(f[2 * j] - bf16lo_to_f32(h[j]), f[2 * j + 1] - bf16hi_to_f32(h[j]));
+    }
+    hi = make_uint4(h[0], h[1], h[2], h[3]);
+    lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+// Store the 32-bit (t, t+1) pairs of two token rows' 8 columns into a
+// transposed [col][t] array at column c0, token t = ta (even).
+__device__ __forceinline__ void store_pairs_t(bf16_t* arr, int stride, int c0, int ta, const uint4& ra,
+                                              const uint4& rb) {
+    const uint32_t* a32 = reinterpret_cast<const uint32_t*>(&ra);
+    const uint32_t* b32 = reinterpret_cast<const uint32_t*>(&rb);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        *reinterpret_cast<uint32_t*>(&arr[(c0 + 2 * j) * stride + ta]) = (a32[j] & 0xffffu) | (b32[j] << 16);
+        *reinterpret_cast<uint32_t*>(&arr[(c0 + 2 * j + 1) * stride + ta]) = (a32[j] >> 16) | (b32[j] & 0xffff0000u);
+    }
+}
+
+// LDS of one workgroup.  NP planes hold a raw input as bf16 (NP = 1) or as
+// bf16 hi + lo parts of fp32 values (NP = 2).
+template <int D, bool SPL>
 struct PrefillSmem {
-    static constexpr int SK = DK + PADB;        // row stride of K, Q, W (bf16)
+    static constexpr int NP = SPL ? 2 : 1;
+    static constexpr int SK = D + PADB;         // row stride of K, Q, W (bf16)
     static constexpr int ST = CH + PADB;        // row stride of K^T, V^T, coefficient arrays
     static constexpr int SF = CH + PADF;        // row stride of fp32 64x64 arrays
-    bf16_t k[CH * SK];                          // K   [t][k]
-    bf16_t q[CH * SK];                          // Q   [t][k]
-    bf16_t kt[DK * ST];                         // K^T [k][t]
-    bf16_t vt_w[(DV * ST > CH * SK) ? DV * ST : CH * SK];   // V^T [v][t], later -W [t][k]
+    static constexpr int VW = (D * ST > CH * SK) ? D * ST : CH * SK;
+    bf16_t k[NP][CH * SK];                      // K   [t][k]
+    bf16_t q[NP][CH * SK];                      // Q   [t][k]
+    bf16_t kt[NP][D * ST];                      // K^T [k][t]
+    bf16_t vt_w[NP][VW];                        // V^T [v][t]; later -W [t][k] in plane 0
     float g[CH * SF];                           // A, then T in place (lower, unit diag, zero upper)
     union {
         bf16_t c[4 * CH * ST];                  // cW hi, cW lo, cU hi, cU lo   [t][t']
@@ -94,19 +126,25 @@ struct PrefillSmem {
     float egl;
 };
 
-template <int DK, int DV, typename OT>
+// D: head dim (d_k = d_v).  IT: input element type (bf16_t, or float read as
+// hi/lo bf16 planes).  OT: output element type.
+template <int D, typename IT, typename OT>
 __global__ __launch_bounds__(256) void prefill_kernel(
-    const bf16_t* __restrict__ qg, const bf16_t* __restrict__ kg, const bf16_t* __restrict__ vg,
+    const IT* __restrict__ qg, const IT* __restrict__ kg, const IT* __restrict__ vg,
     const float* __restrict__ gg, const float* __restrict__ bg, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ slot, float* __restrict__ rec, OT* __restrict__ out, int32_t H,
     int32_t HV, float scale, int32_t flags, const int32_t* __restrict__ err_flag) {
-    static_assert(DK == DV, "square heads");
-    static_assert(DV == 128 || DV == 64, "value head dim");
+    constexpr bool SPL = sizeof(IT) == 4;        // fp32 inputs: hi/lo planes
+    constexpr int NP = SPL ? 2 : 1;
+    static_assert(D == 32 || D == 64 || D == 128, "head dim");
     constexpr int NW = 4;                        // waves
-    constexpr int VB = DV / 16 / NW;             // value blocks (16 wide) per wave
-    constexpr int KB = DK / 16;                  // key blocks (16 tall)
-    constexpr int KS = DK / 32;                  // k-steps over DK
-    using Sm = PrefillSmem<DK, DV>;
+    constexpr int KB = D / 16;                   // 16-row key blocks of the state
+    constexpr int KS = D / 32;                   // 32-wide k-steps over the head dim
+    constexpr int VB = (D / 64 > 0) ? D / 64 : 1;    // 16-wide value blocks per wave
+    constexpr int WB = (KB / NW > 0) ? KB / NW : 1;  // 16-wide key blocks of W per wave
+    constexpr int CP = (D / 64 > 0) ? D / 64 : 1;    // load passes of 64 columns
+    constexpr int WPE = SPL ? 2 : 1;             // uint4 words per 8 input elements
+    using Sm = PrefillSmem<D, SPL>;
     constexpr int SK = Sm::SK, ST = Sm::ST, SF = Sm::SF;
     __shared__ Sm sm;
 
@@ -123,17 +161,19 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     const int32_t t1 = cu[n + 1];
     const int32_t s = slot[n];
     const bool norm = (flags & GDN_FLAG_QK_L2NORM) != 0;
+    const bool vact = wave * VB * 16 < D;        // this wave owns value columns
+    const bool wact = wave * WB < KB;            // this wave owns W columns
 
     if (s <= 0) {                                // inactive: zero outputs, state untouched
-        for (int64_t i = tid; i < static_cast<int64_t>(t1 - t0) * DV; i += 256) {
-            const int64_t t = t0 + i / DV;
-            elem<OT>::st(out + (t * HV + hv) * DV + i % DV, 0.0f);
+        for (int64_t i = tid; i < static_cast<int64_t>(t1 - t0) * D; i += 256) {
+            const int64_t t = t0 + i / D;
+            elem<OT>::st(out + (t * HV + hv) * D + i % D, 0.0f);
         }
         return;
     }
     if (t1 <= t0) return;                        // empty sequence: state untouched
 
-    float* S = rec + (static_cast<size_t>(s) * HV + hv) * static_cast<size_t>(DV) * DK;
+    float* S = rec + (static_cast<size_t>(s) * HV + hv) * static_cast<size_t>(D) * D;
 
     // ---- state S0^T [k][v] in accumulator layout: tile (kb, vb) lane holds
     //      S0^T[16 kb + 4 q4 + r][16 (wave VB + vb) + l16] = S[v][k..k+3]
@@ -142,9 +182,12 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int vb = 0; vb < VB; ++vb) {
-            const int v = 16 * (wave * VB + vb) + l16;
-            const float4 x = *reinterpret_cast<const float4*>(S + static_cast<size_t>(v) * DK + 16 * kb + 4 * q4);
-            st[kb][vb] = f32x4{x.x, x.y, x.z, x.w};
+            st[kb][vb] = f32x4{0, 0, 0, 0};
+            if (vact) {
+                const int v = 16 * (wave * VB + vb) + l16;
+                const float4 x = *reinterpret_cast<const float4*>(S + static_cast<size_t>(v) * D + 16 * kb + 4 * q4);
+                st[kb][vb] = f32x4{x.x, x.y, x.z, x.w};
+            }
         }
 
     // Chunk loads.  Thread (tp, cg) moves token rows 2tp, 2tp+1 at columns
@@ -153,35 +196,25 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     // during the current chunk's state update and staged at the loop top.
     const int tp = tid & 31;
     const int cg = tid >> 5;                     // 0..7
-    const int ta = 2 * tp, tb2 = 2 * tp + 1;
-    constexpr int KP = DK / 64, VP = DV / 64;    // column passes
-    uint4 pk[KP][2], pq[KP][2], pv[VP][2];
+    const int ta = 2 * tp;
+    uint4 pk[CP][2][WPE], pq[CP][2][WPE], pv[CP][2][WPE];
     float pbeta = 0.0f, pg = 0.0f;
     auto fetch = [&](int32_t c, int Lc) {
 #pragma unroll
-        for (int pass = 0; pass < KP; ++pass) {
+        for (int pass = 0; pass < CP; ++pass) {
             const int k0 = 8 * (cg + 8 * pass);
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const int t = ta + e;
-                pk[pass][e] = make_uint4(0, 0, 0, 0);
-                pq[pass][e] = make_uint4(0, 0, 0, 0);
-                if (t < Lc) {
-                    const size_t off = (static_cast<size_t>(c + t) * H + h) * DK + k0;
-                    pk[pass][e] = *reinterpret_cast<const uint4*>(kg + off);
-                    pq[pass][e] = *reinterpret_cast<const uint4*>(qg + off);
+                const bool ok = (t < Lc) && (k0 < D);
+                const size_t off = (static_cast<size_t>(c + t) * H + h) * D + k0;
+                const size_t offv = (static_cast<size_t>(c + t) * HV + hv) * D + k0;
+#pragma unroll
+                for (int w = 0; w < WPE; ++w) {
+                    pk[pass][e][w] = ok ? reinterpret_cast<const uint4*>(kg + off)[w] : make_uint4(0, 0, 0, 0);
+                    pq[pass][e][w] = ok ? reinterpret_cast<const uint4*>(qg + off)[w] : make_uint4(0, 0, 0, 0);
+                    pv[pass][e][w] = ok ? reinterpret_cast<const uint4*>(vg + offv)[w] : make_uint4(0, 0, 0, 0);
                 }
-            }
-        }
-#pragma unroll
-        for (int pass = 0; pass < VP; ++pass) {
-            const int v0 = 8 * (cg + 8 * pass);
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int t = ta + e;
-                pv[pass][e] = make_uint4(0, 0, 0, 0);
-                if (t < Lc)
-                    pv[pass][e] = *reinterpret_cast<const uint4*>(vg + (static_cast<size_t>(c + t) * HV + hv) * DV + v0);
             }
         }
         pbeta = (tid < Lc) ? bg[static_cast<size_t>(c + tid) * HV + hv] : 0.0f;   // used by tid < 64
@@ -192,60 +225,65 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     for (int32_t c0 = t0; c0 < t1; c0 += CH) {
         const int L = min(CH, t1 - c0);
 
-        // ---------------- stage the fetched chunk into LDS
+        // ---------------- stage the fetched chunk into LDS (planes hi [, lo])
 #pragma unroll
-        for (int pass = 0; pass < KP; ++pass) {
+        for (int pass = 0; pass < CP; ++pass) {
             const int k0 = 8 * (cg + 8 * pass);
-            *reinterpret_cast<uint4*>(&sm.k[ta * SK + k0]) = pk[pass][0];
-            *reinterpret_cast<uint4*>(&sm.k[tb2 * SK + k0]) = pk[pass][1];
-            *reinterpret_cast<uint4*>(&sm.q[ta * SK + k0]) = pq[pass][0];
-            *reinterpret_cast<uint4*>(&sm.q[tb2 * SK + k0]) = pq[pass][1];
-            const uint32_t* a32 = reinterpret_cast<const uint32_t*>(&pk[pass][0]);
-            const uint32_t* b32 = reinterpret_cast<const uint32_t*>(&pk[pass][1]);
+            if (k0 < D) {
+                uint4 kw[2][2], qw[2][2], vw[2][2];      // [row][plane]
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                *reinterpret_cast<uint32_t*>(&sm.kt[(k0 + 2 * j) * ST + ta]) =
-                    (a32[j] & 0xffffu) | (b32[j] << 16);
-                *reinterpret_cast<uint32_t*>(&sm.kt[(k0 + 2 * j + 1) * ST + ta]) =
-                    (a32[j] >> 16) | (b32[j] & 0xffff0000u);
-            }
-        }
+                for (int e = 0; e < 2; ++e) {
+                    if constexpr (SPL) {
+                        split8(pk[pass][e][0], pk[pass][e][WPE - 1], kw[e][0], kw[e][1]);
+                        split8(pq[pass][e][0], pq[pass][e][WPE - 1], qw[e][0], qw[e][1]);
+                        split8(pv[pass][e][0], pv[pass][e][WPE - 1], vw[e][0], vw[e][1]);
+                    } else {
+                        kw[e][0] = pk[pass][e][0]; qw[e][0] = pq[pass][e][0]; vw[e][0] = pv[pass][e][0];
+                        kw[e][1] = kw[e][0]; qw[e][1] = qw[e][0]; vw[e][1] = vw[e][0];
+                    }
+                }
 #pragma unroll
-        for (int pass = 0; pass < VP; ++pass) {
-            const int v0 = 8 * (cg + 8 * pass);
-            const uint32_t* a32 = reinterpret_cast<const uint32_t*>(&pv[pass][0]);
-            const uint32_t* b32 = reinterpret_cast<const uint32_t*>(&pv[pass][1]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                *reinterpret_cast<uint32_t*>(&sm.vt_w[(v0 + 2 * j) * ST + ta]) =
-                    (a32[j] & 0xffffu) | (b32[j] << 16);
-                *reinterpret_cast<uint32_t*>(&sm.vt_w[(v0 + 2 * j + 1) * ST + ta]) =
-                    (a32[j] >> 16) | (b32[j] & 0xffff0000u);
+                for (int pl = 0; pl < NP; ++pl) {
+                    *reinterpret_cast<uint4*>(&sm.k[pl][ta * SK + k0]) = kw[0][pl];
+                    *reinterpret_cast<uint4*>(&sm.k[pl][(ta + 1) * SK + k0]) = kw[1][pl];
+                    *reinterpret_cast<uint4*>(&sm.q[pl][ta * SK + k0]) = qw[0][pl];
+                    *reinterpret_cast<uint4*>(&sm.q[pl][(ta + 1) * SK + k0]) = qw[1][pl];
+                    store_pairs_t(sm.kt[pl], ST, k0, ta, kw[0][pl], kw[1][pl]);
+                    store_pairs_t(sm.vt_w[pl], ST, k0, ta, vw[0][pl], vw[1][pl]);
+                }
             }
         }
         if (tid < CH) sm.beta[tid] = pbeta;
         float gt = pg;                           // wave 0: this lane's g, scanned below
         __syncthreads();
 
-        // ---------------- row norms (8 lanes per row, the decode kernel's order)
-        // and the cumulative log-decay (wave 0, a fixed-order inclusive scan)
+        // ---------------- row norms (8 lanes per row, the decode kernel's order;
+        // fp32 inputs as hi + lo) and the cumulative log-decay (wave 0, a
+        // fixed-order inclusive scan)
         for (int pass = 0; pass < 4; ++pass) {
             const int rowid = pass * 32 + (tid >> 3);
             const int sub = tid & 7;
-            const bf16_t* rowp = (rowid < CH) ? &sm.k[rowid * SK] : &sm.q[(rowid - CH) * SK];
+            const int rr = (rowid < CH) ? rowid : rowid - CH;
+            const bf16_t* rh = (rowid < CH) ? &sm.k[0][rr * SK] : &sm.q[0][rr * SK];
+            const bf16_t* rl = (rowid < CH) ? &sm.k[NP - 1][rr * SK] : &sm.q[NP - 1][rr * SK];
             float acc = 0.f;
 #pragma unroll
-            for (int i = 0; i < DK / 32; ++i) {
-                const uint2 u = *reinterpret_cast<const uint2*>(rowp + 32 * i + 4 * sub);
-                const float x0 = bf16lo_to_f32(u.x), x1 = bf16hi_to_f32(u.x);
-                const float x2 = bf16lo_to_f32(u.y), x3 = bf16hi_to_f32(u.y);
+            for (int i = 0; i < D / 32; ++i) {
+                const uint2 u = *reinterpret_cast<const uint2*>(rh + 32 * i + 4 * sub);
+                float x0 = bf16lo_to_f32(u.x), x1 = bf16hi_to_f32(u.x);
+                float x2 = bf16lo_to_f32(u.y), x3 = bf16hi_to_f32(u.y);
+                if constexpr (SPL) {
+                    const uint2 w = *reinterpret_cast<const uint2*>(rl + 32 * i + 4 * sub);
+                    x0 += bf16lo_to_f32(w.x); x1 += bf16hi_to_f32(w.x);
+                    x2 += bf16lo_to_f32(w.y); x3 += bf16hi_to_f32(w.y);
+                }
                 acc = fmaf(x0, x0, acc); acc = fmaf(x1, x1, acc);
                 acc = fmaf(x2, x2, acc); acc = fmaf(x3, x3, acc);
             }
             acc = sum8(acc);
             if (sub == 0) {
-                if (rowid < CH) sm.rk[rowid] = norm ? 1.0f / sqrtf(acc + 1e-6f) : 1.0f;
-                else sm.rq[rowid - CH] = norm ? scale / sqrtf(acc + 1e-6f) : scale;
+                if (rowid < CH) sm.rk[rr] = norm ? 1.0f / sqrtf(acc + 1e-6f) : 1.0f;
+                else sm.rq[rr] = norm ? scale / sqrtf(acc + 1e-6f) : scale;
             }
         }
         if (wave == 0) {
@@ -277,13 +315,19 @@ __global__ __launch_bounds__(256) void prefill_kernel(
             for (int jb = 0; jb < 4; ++jb) { accg[jb] = f32x4{0, 0, 0, 0}; accp[jb] = f32x4{0, 0, 0, 0}; }
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 ak = frag_std(sm.k, SK, 16 * tb + l16, 32 * ks, q4);
-                const bf16x8 aq = frag_std(sm.q, SK, 16 * tb + l16, 32 * ks, q4);
 #pragma unroll
-                for (int jb = 0; jb < 4; ++jb) {
-                    const bf16x8 bk = frag_std(sm.k, SK, 16 * jb + l16, 32 * ks, q4);
-                    accg[jb] = mfma(ak, bk, accg[jb]);
-                    accp[jb] = mfma(aq, bk, accp[jb]);
+                for (int pa = 0; pa < NP; ++pa) {        // raw x raw: hh (+ hl + lh)
+                    const bf16x8 ak = frag_std(sm.k[pa], SK, 16 * tb + l16, 32 * ks, q4);
+                    const bf16x8 aq = frag_std(sm.q[pa], SK, 16 * tb + l16, 32 * ks, q4);
+#pragma unroll
+                    for (int pb = 0; pb < NP - pa; ++pb) {
+#pragma unroll
+                        for (int jb = 0; jb < 4; ++jb) {
+                            const bf16x8 bk = frag_std(sm.k[pb], SK, 16 * jb + l16, 32 * ks, q4);
+                            accg[jb] = mfma(ak, bk, accg[jb]);
+                            accp[jb] = mfma(aq, bk, accp[jb]);
+                        }
+                    }
                 }
             }
             float gr[4], brk[4], rqr[4];
@@ -423,203 +467,243 @@ __global__ __launch_bounds__(256) void prefill_kernel(
         __syncthreads();
 
         // ---------------- Ut = cU V (wave's value columns) and W = cW K
+        // (split coefficients x raw planes: hh + lh (+ hl for split inputs))
         f32x4 u[4][VB];                          // U tiles (t-block, v-block): rows t, cols v
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
             for (int vb = 0; vb < VB; ++vb) u[tb][vb] = f32x4{0, 0, 0, 0};
+        if (vact) {
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
+            for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const bf16x8 ah = frag_std(sm.pc.c + 2 * CH * ST, ST, 16 * tb + l16, 32 * ks, q4);
-                const bf16x8 al = frag_std(sm.pc.c + 3 * CH * ST, ST, 16 * tb + l16, 32 * ks, q4);
+                for (int ks = 0; ks < 2; ++ks) {
+                    const bf16x8 ah = frag_std(sm.pc.c + 2 * CH * ST, ST, 16 * tb + l16, 32 * ks, q4);
+                    const bf16x8 al = frag_std(sm.pc.c + 3 * CH * ST, ST, 16 * tb + l16, 32 * ks, q4);
 #pragma unroll
-                for (int vb = 0; vb < VB; ++vb) {
-                    const bf16x8 bv = frag_std(sm.vt_w, ST, 16 * (wave * VB + vb) + l16, 32 * ks, q4);
-                    u[tb][vb] = mfma(ah, bv, u[tb][vb]);
-                    u[tb][vb] = mfma(al, bv, u[tb][vb]);
+                    for (int vb = 0; vb < VB; ++vb) {
+                        const int vr = 16 * (wave * VB + vb) + l16;
+                        const bf16x8 bv = frag_std(sm.vt_w[0], ST, vr, 32 * ks, q4);
+                        u[tb][vb] = mfma(ah, bv, u[tb][vb]);
+                        u[tb][vb] = mfma(al, bv, u[tb][vb]);
+                        if constexpr (SPL)
+                            u[tb][vb] = mfma(ah, frag_std(sm.vt_w[NP - 1], ST, vr, 32 * ks, q4), u[tb][vb]);
+                    }
                 }
-            }
-        constexpr int WB = KB / NW;              // key blocks of W per wave
+        }
         f32x4 w[4][WB];
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
             for (int kb = 0; kb < WB; ++kb) w[tb][kb] = f32x4{0, 0, 0, 0};
+        if (wact) {
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
+            for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const bf16x8 ah = frag_std(sm.pc.c + 0 * CH * ST, ST, 16 * tb + l16, 32 * ks, q4);
-                const bf16x8 al = frag_std(sm.pc.c + 1 * CH * ST, ST, 16 * tb + l16, 32 * ks, q4);
+                for (int ks = 0; ks < 2; ++ks) {
+                    const bf16x8 ah = frag_std(sm.pc.c + 0 * CH * ST, ST, 16 * tb + l16, 32 * ks, q4);
+                    const bf16x8 al = frag_std(sm.pc.c + 1 * CH * ST, ST, 16 * tb + l16, 32 * ks, q4);
 #pragma unroll
-                for (int kb = 0; kb < WB; ++kb) {
-                    const bf16x8 bk = frag_std(sm.kt, ST, 16 * (wave * WB + kb) + l16, 32 * ks, q4);
-                    w[tb][kb] = mfma(ah, bk, w[tb][kb]);
-                    w[tb][kb] = mfma(al, bk, w[tb][kb]);
+                    for (int kb = 0; kb < WB; ++kb) {
+                        const int kr = 16 * (wave * WB + kb) + l16;
+                        const bf16x8 bk = frag_std(sm.kt[0], ST, kr, 32 * ks, q4);
+                        w[tb][kb] = mfma(ah, bk, w[tb][kb]);
+                        w[tb][kb] = mfma(al, bk, w[tb][kb]);
+                        if constexpr (SPL)
+                            w[tb][kb] = mfma(ah, frag_std(sm.kt[NP - 1], ST, kr, 32 * ks, q4), w[tb][kb]);
+                    }
                 }
-            }
-        __syncthreads();                         // V^T is dead: its space takes -W
+        }
+        __syncthreads();                         // V^T is dead: its plane 0 takes -W
+        if (wact) {
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
+            for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-            for (int kb = 0; kb < WB; ++kb)
+                for (int kb = 0; kb < WB; ++kb)
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    sm.vt_w[(16 * tb + 4 * q4 + r) * SK + 16 * (wave * WB + kb) + l16] = f32_to_bf16(-w[tb][kb][r]);
+                    for (int r = 0; r < 4; ++r)
+                        sm.vt_w[0][(16 * tb + 4 * q4 + r) * SK + 16 * (wave * WB + kb) + l16] = f32_to_bf16(-w[tb][kb][r]);
+        }
         __syncthreads();                         // -W visible to all waves
 
-        // ---------------- U = Ut - W S0^T ;  O1 = Q S0^T  (state split per k-step
-        // into hi/lo B fragments with permuted k-slots)
-        f32x4 o[4][VB];
+        if (vact) {
+            // ------------ U = Ut - W S0^T ;  O1 = Q S0^T  (state split per k-step
+            // into hi/lo B fragments with permuted k-slots)
+            f32x4 o[4][VB];
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
+            for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-            for (int vb = 0; vb < VB; ++vb) o[tb][vb] = f32x4{0, 0, 0, 0};
+                for (int vb = 0; vb < VB; ++vb) o[tb][vb] = f32x4{0, 0, 0, 0};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            bf16x8 sh[VB], sl[VB];
-#pragma unroll
-            for (int vb = 0; vb < VB; ++vb) {
-                uint2 h0, l0, h1, l1;
-                split4(st[2 * ks][vb], h0, l0);
-                split4(st[2 * ks + 1][vb], h1, l1);
-                sh[vb] = as_bf16x8(cat(h0, h1));
-                sl[vb] = as_bf16x8(cat(l0, l1));
-            }
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                const bf16x8 aw = frag_perm(sm.vt_w, SK, 16 * tb + l16, 32 * ks, q4);
-                const bf16x8 aq = frag_perm(sm.q, SK, 16 * tb + l16, 32 * ks, q4);
+            for (int ks = 0; ks < KS; ++ks) {
+                bf16x8 sh[VB], sl[VB];
 #pragma unroll
                 for (int vb = 0; vb < VB; ++vb) {
-                    u[tb][vb] = mfma(aw, sh[vb], u[tb][vb]);
-                    u[tb][vb] = mfma(aw, sl[vb], u[tb][vb]);
-                    o[tb][vb] = mfma(aq, sh[vb], o[tb][vb]);
-                    o[tb][vb] = mfma(aq, sl[vb], o[tb][vb]);
+                    uint2 h0, l0, h1, l1;
+                    split4(st[2 * ks][vb], h0, l0);
+                    split4(st[2 * ks + 1][vb], h1, l1);
+                    sh[vb] = as_bf16x8(cat(h0, h1));
+                    sl[vb] = as_bf16x8(cat(l0, l1));
+                }
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) {
+                    const bf16x8 aw = frag_perm(sm.vt_w[0], SK, 16 * tb + l16, 32 * ks, q4);
+                    const bf16x8 aq = frag_perm(sm.q[0], SK, 16 * tb + l16, 32 * ks, q4);
+#pragma unroll
+                    for (int vb = 0; vb < VB; ++vb) {
+                        u[tb][vb] = mfma(aw, sh[vb], u[tb][vb]);
+                        u[tb][vb] = mfma(aw, sl[vb], u[tb][vb]);
+                        o[tb][vb] = mfma(aq, sh[vb], o[tb][vb]);
+                        o[tb][vb] = mfma(aq, sl[vb], o[tb][vb]);
+                    }
+                    if constexpr (SPL) {
+                        const bf16x8 aql = frag_perm(sm.q[NP - 1], SK, 16 * tb + l16, 32 * ks, q4);
+#pragma unroll
+                        for (int vb = 0; vb < VB; ++vb) o[tb][vb] = mfma(aql, sh[vb], o[tb][vb]);
+                    }
                 }
             }
-        }
-        // O1 rows scaled by e^gamma_t rq_t
+            // O1 rows scaled by e^gamma_t rq_t
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
+            for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float e = sm.eg[16 * tb + 4 * q4 + r];
+                for (int r = 0; r < 4; ++r) {
+                    const float e = sm.eg[16 * tb + 4 * q4 + r];
 #pragma unroll
-                for (int vb = 0; vb < VB; ++vb) o[tb][vb][r] *= e;
-            }
+                    for (int vb = 0; vb < VB; ++vb) o[tb][vb][r] *= e;
+                }
 
-        // ---------------- O += (M o P) U   (U split, permuted t-slots)
-        bf16x8 uh[2][VB], ul[2][VB];
+            // ------------ O += (M o P) U   (U split, permuted t-slots)
+            bf16x8 uh[2][VB], ul[2][VB];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int vb = 0; vb < VB; ++vb) {
-                uint2 h0, l0, h1, l1;
-                split4(u[2 * ks][vb], h0, l0);
-                split4(u[2 * ks + 1][vb], h1, l1);
-                uh[ks][vb] = as_bf16x8(cat(h0, h1));
-                ul[ks][vb] = as_bf16x8(cat(l0, l1));
-            }
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                if (32 * ks > 16 * tb + 15) continue;          // strictly above the diagonal
-                const bf16x8 mh = frag_perm(sm.mp, ST, 16 * tb + l16, 32 * ks, q4);
-                const bf16x8 ml = frag_perm(sm.mp + CH * ST, ST, 16 * tb + l16, 32 * ks, q4);
+            for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
                 for (int vb = 0; vb < VB; ++vb) {
-                    o[tb][vb] = mfma(mh, uh[ks][vb], o[tb][vb]);
-                    o[tb][vb] = mfma(mh, ul[ks][vb], o[tb][vb]);
-                    o[tb][vb] = mfma(ml, uh[ks][vb], o[tb][vb]);
+                    uint2 h0, l0, h1, l1;
+                    split4(u[2 * ks][vb], h0, l0);
+                    split4(u[2 * ks + 1][vb], h1, l1);
+                    uh[ks][vb] = as_bf16x8(cat(h0, h1));
+                    ul[ks][vb] = as_bf16x8(cat(l0, l1));
                 }
-            }
-        // store O rows t < L
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
+            for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * tb + 4 * q4 + r;
-                if (t < L) {
+                for (int ks = 0; ks < 2; ++ks) {
+                    if (32 * ks > 16 * tb + 15) continue;          // strictly above the diagonal
+                    const bf16x8 mh = frag_perm(sm.mp, ST, 16 * tb + l16, 32 * ks, q4);
+                    const bf16x8 ml = frag_perm(sm.mp + CH * ST, ST, 16 * tb + l16, 32 * ks, q4);
 #pragma unroll
-                    for (int vb = 0; vb < VB; ++vb)
-                        elem<OT>::st(out + (static_cast<size_t>(c0 + t) * HV + hv) * DV + 16 * (wave * VB + vb) + l16,
-                                     o[tb][vb][r]);
+                    for (int vb = 0; vb < VB; ++vb) {
+                        o[tb][vb] = mfma(mh, uh[ks][vb], o[tb][vb]);
+                        o[tb][vb] = mfma(mh, ul[ks][vb], o[tb][vb]);
+                        o[tb][vb] = mfma(ml, uh[ks][vb], o[tb][vb]);
+                    }
                 }
-            }
+            // store O rows t < L
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 16 * tb + 4 * q4 + r;
+                    if (t < L) {
+#pragma unroll
+                        for (int vb = 0; vb < VB; ++vb)
+                            elem<OT>::st(out + (static_cast<size_t>(c0 + t) * HV + hv) * D + 16 * (wave * VB + vb) + l16,
+                                         o[tb][vb][r]);
+                    }
+                }
+        }
 
         if (c0 + CH < t1) fetch(c0 + CH, min(CH, t1 - c0 - CH));   // next chunk, in flight
 
-        // ---------------- S0^T <- e^{gamma_L} S0^T + K^T (cK . U)
-        bf16x8 ch[2][VB], cl[2][VB];
+        if (vact) {
+            // ------------ S0^T <- e^{gamma_L} S0^T + K^T (cK . U)
+            bf16x8 ch[2][VB], cl[2][VB];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+            for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int vb = 0; vb < VB; ++vb) {
-                f32x4 a = u[2 * ks][vb], b = u[2 * ks + 1][vb];
+                for (int vb = 0; vb < VB; ++vb) {
+                    f32x4 a = u[2 * ks][vb], b = u[2 * ks + 1][vb];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    a[r] *= sm.ck[32 * ks + 4 * q4 + r];
-                    b[r] *= sm.ck[32 * ks + 16 + 4 * q4 + r];
+                    for (int r = 0; r < 4; ++r) {
+                        a[r] *= sm.ck[32 * ks + 4 * q4 + r];
+                        b[r] *= sm.ck[32 * ks + 16 + 4 * q4 + r];
+                    }
+                    uint2 h0, l0, h1, l1;
+                    split4(a, h0, l0);
+                    split4(b, h1, l1);
+                    ch[ks][vb] = as_bf16x8(cat(h0, h1));
+                    cl[ks][vb] = as_bf16x8(cat(l0, l1));
                 }
-                uint2 h0, l0, h1, l1;
-                split4(a, h0, l0);
-                split4(b, h1, l1);
-                ch[ks][vb] = as_bf16x8(cat(h0, h1));
-                cl[ks][vb] = as_bf16x8(cat(l0, l1));
-            }
-        const float egl = sm.egl;
+            const float egl = sm.egl;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            bf16x8 ak[2];
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) ak[ks] = frag_perm(sm.kt, ST, 16 * kb + l16, 32 * ks, q4);
-#pragma unroll
-            for (int vb = 0; vb < VB; ++vb) {
-                f32x4 acc = st[kb][vb];
-                acc[0] *= egl; acc[1] *= egl; acc[2] *= egl; acc[3] *= egl;
+            for (int kb = 0; kb < KB; ++kb) {
+                bf16x8 ak[2], akl[2];
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
-                    acc = mfma(ak[ks], ch[ks][vb], acc);
-                    acc = mfma(ak[ks], cl[ks][vb], acc);
+                    ak[ks] = frag_perm(sm.kt[0], ST, 16 * kb + l16, 32 * ks, q4);
+                    akl[ks] = frag_perm(sm.kt[NP - 1], ST, 16 * kb + l16, 32 * ks, q4);
                 }
-                st[kb][vb] = acc;
+#pragma unroll
+                for (int vb = 0; vb < VB; ++vb) {
+                    f32x4 acc = st[kb][vb];
+                    acc[0] *= egl; acc[1] *= egl; acc[2] *= egl; acc[3] *= egl;
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks) {
+                        acc = mfma(ak[ks], ch[ks][vb], acc);
+                        acc = mfma(ak[ks], cl[ks][vb], acc);
+                        if constexpr (SPL) acc = mfma(akl[ks], ch[ks][vb], acc);
+                    }
+                    st[kb][vb] = acc;
+                }
             }
         }
         __syncthreads();                         // LDS is rewritten by the next chunk
     }
 
     // ---- final state back to the slot
+    if (vact) {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int vb = 0; vb < VB; ++vb) {
-            const int v = 16 * (wave * VB + vb) + l16;
-            *reinterpret_cast<float4*>(S + static_cast<size_t>(v) * DK + 16 * kb + 4 * q4) =
-                make_float4(st[kb][vb][0], st[kb][vb][1], st[kb][vb][2], st[kb][vb][3]);
-        }
+            for (int vb = 0; vb < VB; ++vb) {
+                const int v = 16 * (wave * VB + vb) + l16;
+                *reinterpret_cast<float4*>(S + static_cast<size_t>(v) * D + 16 * kb + 4 * q4) =
+                    make_float4(st[kb][vb][0], st[kb][vb][1], st[kb][vb][2], st[kb][vb][3]);
+            }
+    }
 }
 
 namespace {
-template <int D, typename OT>
+template <int D, typename IT, typename OT>
 hipError_t run_prefill(const void* q, const void* k, const void* v, const float* g,
                        const float* beta, const int32_t* cu, int32_t n_seqs, const int32_t* slot,
                        float* rec, void* out, const gdn_dims& d, float scale, int32_t flags,
                        const int32_t* err, hipStream_t st) {
     dim3 grid(d.num_v_heads, n_seqs);
-    return launch(prefill_kernel<D, D, OT>, grid, dim3(256), 0, st,
-                  static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
-                  static_cast<const bf16_t*>(v), g, beta, cu, slot, rec, static_cast<OT*>(out),
+    return launch(prefill_kernel<D, IT, OT>, grid, dim3(256), 0, st,
+                  static_cast<const IT*>(q), static_cast<const IT*>(k),
+                  static_cast<const IT*>(v), g, beta, cu, slot, rec, static_cast<OT*>(out),
                   d.num_k_heads, d.num_v_heads, scale, flags, err);
+}
+
+template <int D, typename IT>
+hipError_t pick_out(gdn_dtype out_dt, const void* q, const void* k, const void* v, const float* g,
+                    const float* beta, const int32_t* cu, int32_t n_seqs, const int32_t* slot,
+                    float* rec, void* out, const gdn_dims& d, float scale, int32_t flags,
+                    const int32_t* err, hipStream_t st) {
+    return out_dt == GDN_BF16
+        ? run_prefill<D, IT, bf16_t>(q, k, v, g, beta, cu, n_seqs, slot, rec, out, d, scale, flags, err, st)
+        : run_prefill<D, IT, float>(q, k, v, g, beta, cu, n_seqs, slot, rec, out, d, scale, flags, err, st);
 }
 }  // namespace
 
+// Head dims 32, 64 and 128 with d_k == d_v; fp32 inputs (hi/lo planes in LDS)
+// only up to 64, where the doubled input planes fit in LDS.
 bool prefill_supported(const gdn_dims& d, gdn_dtype in_dt) {
-    return in_dt == GDN_BF16 && d.head_k_dim == d.head_v_dim &&
-           (d.head_k_dim == 128 || d.head_k_dim == 64);
+    const int D = d.head_k_dim;
+    if (d.head_v_dim != D || (D != 32 && D != 64 && D != 128)) return false;
+    return in_dt == GDN_BF16 || (in_dt == GDN_F32 && D <= 64);
 }
 
 hipError_t launch_prefill(const void* q, const void* k, const void* v, gdn_dtype in_dt,
@@ -629,13 +713,14 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, gdn_dtype
                           hipStream_t st) {
     if (n_seqs == 0) return hipSuccess;
     if (!prefill_supported(d, in_dt)) return hipErrorInvalidValue;
-    if (d.head_k_dim == 128)
-        return out_dt == GDN_BF16
-            ? run_prefill<128, bf16_t>(q, k, v, g, beta, cu, n_seqs, slot, rec, out, d, scale, flags, err, st)
-            : run_prefill<128, float>(q, k, v, g, beta, cu, n_seqs, slot, rec, out, d, scale, flags, err, st);
-    return out_dt == GDN_BF16
-        ? run_prefill<64, bf16_t>(q, k, v, g, beta, cu, n_seqs, slot, rec, out, d, scale, flags, err, st)
-        : run_prefill<64, float>(q, k, v, g, beta, cu, n_seqs, slot, rec, out, d, scale, flags, err, st);
+    const int D = d.head_k_dim;
+    if (in_dt == GDN_F32) {
+        if (D == 32) return pick_out<32, float>(out_dt, q, k, v, g, beta, cu, n_seqs, slot, rec, out, d, scale, flags, err, st);
+        return pick_out<64, float>(out_dt, q, k, v, g, beta, cu, n_seqs, slot, rec, out, d, scale, flags, err, st);
+    }
+    if (D == 32) return pick_out<32, bf16_t>(out_dt, q, k, v, g, beta, cu, n_seqs, slot, rec, out, d, scale, flags, err, st);
+    if (D == 64) return pick_out<64, bf16_t>(out_dt, q, k, v, g, beta, cu, n_seqs, slot, rec, out, d, scale, flags, err, st);
+    return pick_out<128, bf16_t>(out_dt, q, k, v, g, beta, cu, n_seqs, slot, rec, out, d, scale, flags, err, st);
 }
 
 }  // namespace gdn

@@ -163,7 +163,7 @@ def tiny_config(seed=0):
     v ~ N(0,1), beta = sigmoid(N(0,1)), g = -softplus(N(0,1)), zero states,
     8-slot cache; decode mixed_qkv ~ N(0, 1), conv weight ~ U(-1/2, 1/2)."""
     H, HV, d, W, n_seqs, T_each, steps, num_slots = 2, 4, 32, 4, 2, 64, 8, 8
-    gen = _gen(seed)
+    gen = _gen(seed + 1000)            # decode draws: a stream apart from the prefill's
     pre = prefill_inputs([T_each] * n_seqs, num_slots, H=H, HV=HV, dk=d, dv=d,
                          in_dtype=torch.float32, seed=seed, state_std=0.0,
                          g_mode="softplus", qk_normalised=True)
