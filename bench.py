@@ -68,6 +68,29 @@ def prefill_bytes(total_tokens, n_seqs, in_bytes=2, out_bytes=2):
     return total_tokens * per_tok + n_seqs * 2 * HV * DV * DK * 4
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_rec_kernel_b256_traffic.txt")
+DECODE_SRC = os.path.join(ROOT, "gated_deltanet_recurrent_gdn_amd", "csrc", "decode.hip")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the recurrence kernel at batch 256 from the
+    committed counter runs (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None
+    when decode.hip has changed since those counters were taken."""
+    import hashlib
+    try:
+        kv = {}
+        for line in open(TRAFFIC_FILE):
+            if "=" in line and not line.lstrip().startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+        src = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
+        if kv.get("decode_hip_sha256") != src:
+            return None
+        return int(kv["fetch_bytes_per_launch"]) + int(kv["write_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -78,6 +101,10 @@ def parse():
                     help="wall-clock budget of the oracle sample")
     ap.add_argument("--validate", action="store_true",
                     help="time with device-side index validation on")
+    ap.add_argument("--eager", action="store_true",
+                    help="time decode steps as eager launches instead of graph replay "
+                         "(for counter collection)")
+
     return ap.parse_args()
 
 
@@ -271,11 +298,24 @@ def main():
     pre = PrefillSetup(seed=3, dev="cuda")
     torch.cuda.synchronize()
 
-    # decode buckets: graph replay of one step per disjoint slot set
-    g_big, r_big = big.capture(args.validate)
-    g_small, r_small = small.capture(args.validate)
-    ms_big = time_graph(torch, g_big, r_big, args.steps, args.warmup)
-    ms_small = time_graph(torch, g_small, r_small, args.steps, args.warmup)
+    # copy calibration for counter runs: one device-to-device copy of 1 GiB
+    # (1 GiB read + 1 GiB written by torch's elementwise copy kernel)
+    cal_src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    cal_dst = torch.empty_like(cal_src)
+    cal_dst.copy_(cal_src)
+    torch.cuda.synchronize()
+    del cal_src, cal_dst
+
+    if args.eager:
+        r_big = r_small = 1
+        ms_big = time_loop(torch, lambda: big.step(args.validate), args.steps, args.warmup)
+        ms_small = time_loop(torch, lambda: small.step(args.validate), args.steps, args.warmup)
+    else:
+        # decode buckets: graph replay of one step per disjoint slot set
+        g_big, r_big = big.capture(args.validate)
+        g_small, r_small = small.capture(args.validate)
+        ms_big = time_graph(torch, g_big, r_big, args.steps, args.warmup)
+        ms_small = time_graph(torch, g_small, r_small, args.steps, args.warmup)
     # prefill, eager (one call is milliseconds)
     ms_pre = time_loop(torch, lambda: pre.step(args.validate), args.steps, args.warmup)
     # dominant kernel alone (the decode recurrence), eager launches with events
@@ -306,8 +346,9 @@ def main():
         "decode_b16_GBps": round(gbs_small, 2),
         "decode_b16_ms_mean": round(mean(ms_small), 5),
         "decode_b16_pct_hbm_peak": round(100 * gbs_small / HBM_PEAK_GBS, 2),
-        "decode_timing": "HIP graph replay, one step per disjoint slot set "
-                         f"({r_big} sets at batch 256, {r_small} at batch 16)",
+        "decode_timing": ("eager launches with HIP events" if args.eager else
+                          "HIP graph replay, one step per disjoint slot set "
+                          f"({r_big} sets at batch 256, {r_small} at batch 16)"),
         "prefill_tokens": pre.T, "prefill_lengths": pre.lengths,
         "prefill_ms_mean": round(pre_ms, 4), "prefill_ms_min": round(min(ms_pre), 4),
         "prefill_tokens_per_s": round(pre_tps, 1),
@@ -324,6 +365,8 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args.cpu_seconds)
         extra["cpu_baseline_prefill"] = cpu_baseline_prefill(max(4.0, args.cpu_seconds / 2))
+
+    traffic = measured_traffic()
 
     line = {
         "metric": "GDN decode HBM GB/s (% peak) at batch 16/256; prefill tokens/s (% MFMA)",
@@ -345,7 +388,7 @@ def main():
                    "global_batch": 256, "seq_len": 1, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "kernel": "decode_rec_kernel",
                      "achieved": round(rec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(rec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(rec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "avg_launch_ms": round(rec_ms, 5),
                      "algorithmic_bytes_per_launch": rec_bytes},
         "cpu_baseline": cpu,

@@ -73,11 +73,16 @@ gdn_status gdn_conv_update(const void* x, gdn_dtype x_dt, const int32_t* cu_seql
     if (n_seqs < 0 || total_tokens < 0 || num_slots < 1 || dim <= 0 || width != 4)
         return GDN_ERR_DIMS;
     if (!cu_seqlens && total_tokens != n_seqs) return GDN_ERR_DIMS;
+    if (!cu_seqlens && dim % 4 != 0) return GDN_ERR_DIMS;     // decode form: 4 channels/thread
     if (n_seqs > 65535) return GDN_ERR_DIMS;
     if (!dtype_ok(x_dt) || !dtype_ok(cs_dt) || !dtype_ok(w_dt) || !dtype_ok(out_dt))
         return GDN_ERR_DTYPE;
     if (n_seqs > 0 && (!slot_idx || !conv_state || !weight)) return GDN_ERR_NULL;
     if (total_tokens > 0 && (!x || !out)) return GDN_ERR_NULL;
+    if (!cu_seqlens && n_seqs > 0 &&
+        (!aligned16(x) || !aligned16(out) || !aligned16(conv_state) || !aligned16(weight) ||
+         (bias && !aligned16(bias))))
+        return GDN_ERR_ALIGN;
     auto s = static_cast<hipStream_t>(stream);
     if (flags & GDN_FLAG_VALIDATE)
         GDN_TRY_LAUNCH(launch_validate(slot_idx, n_seqs, num_slots, cu_seqlens, total_tokens,
@@ -107,13 +112,16 @@ gdn_status gdn_decode_step(const void* mixed_qkv, gdn_dtype x_dt, const float* g
     if (gdn_status st = check_flags(flags, KNOWN_FLAGS, err_flag)) return st;
     if (gdn_status st = check_dims(dims)) return st;
     if (batch < 0 || batch > 65535 || num_slots < 1) return GDN_ERR_DIMS;
+    if (static_cast<int64_t>(batch) * dims->num_v_heads > (1 << 24)) return GDN_ERR_DIMS;
     if (!dtype_ok(x_dt) || !dtype_ok(cs_dt) || !dtype_ok(w_dt) || !dtype_ok(out_dt))
         return GDN_ERR_DTYPE;
     if (batch > 0) {
         if (!mixed_qkv || !g || !beta || !slot_idx || !conv_state || !conv_weight ||
             !rec_state || !out || !workspace)
             return GDN_ERR_NULL;
-        if (!aligned16(rec_state) || !aligned16(workspace)) return GDN_ERR_ALIGN;
+        if (!aligned16(rec_state) || !aligned16(workspace) || !aligned16(mixed_qkv) ||
+            !aligned16(conv_state) || !aligned16(conv_weight) || (conv_bias && !aligned16(conv_bias)))
+            return GDN_ERR_ALIGN;
         if (workspace_bytes < gdn_decode_workspace_size(dims, batch)) return GDN_ERR_WORKSPACE;
     }
     auto s = static_cast<hipStream_t>(stream);
@@ -140,6 +148,7 @@ gdn_status gdn_decode_recurrent(const void* qkv, gdn_dtype qkv_dt, const float* 
         return st;
     if (gdn_status st = check_dims(dims)) return st;
     if (batch < 0 || batch > 65535 || num_slots < 1) return GDN_ERR_DIMS;
+    if (static_cast<int64_t>(batch) * dims->num_v_heads > (1 << 24)) return GDN_ERR_DIMS;
     if (!dtype_ok(qkv_dt) || !dtype_ok(out_dt)) return GDN_ERR_DTYPE;
     if (batch > 0) {
         if (!qkv || !g || !beta || !slot_idx || !rec_state || !out) return GDN_ERR_NULL;

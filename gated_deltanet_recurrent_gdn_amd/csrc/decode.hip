@@ -21,6 +21,8 @@
 // fixed-order fma chain followed by the 8-lane DPP butterfly `sum8`: the order
 // depends on nothing but dk, so results are batch-invariant and replay
 // bitwise.  No LDS is used at all.
+#include <atomic>
+
 #include "gdn_device.hpp"
 #include "gdn_internal.hpp"
 
@@ -37,17 +39,46 @@ template <> __device__ __forceinline__ float4 load4<bf16_t>(const bf16_t* p) {
                        __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
 }
 
-template <int DK, int RPL, typename YT, typename OT>
-__global__ __launch_bounds__(256) void decode_rec_kernel(
+// Workgroups resident per CU in the persistent grid, and whether the state
+// stream uses nontemporal loads/stores (it is read once and written once).
+#ifndef GDN_DECODE_WG_PER_CU
+#define GDN_DECODE_WG_PER_CU 16
+#endif
+#ifndef GDN_DECODE_NT
+#define GDN_DECODE_NT 1
+#endif
+// Largest rows-per-lane step count (a workgroup item covers 32 x RPL rows).
+// Small items (32 rows, 16 KB of state) measured fastest: the workgroups in
+// flight then stream a narrower window of the cache.
+#ifndef GDN_DECODE_RPL_MAX
+#define GDN_DECODE_RPL_MAX 1
+#endif
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float4 state_ld(const float* p) {
+#if GDN_DECODE_NT
+    const v4f v = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+#else
+    return *reinterpret_cast<const float4*>(p);
+#endif
+}
+__device__ __forceinline__ void state_st(float* p, const float4& x) {
+#if GDN_DECODE_NT
+    const v4f v = {x.x, x.y, x.z, x.w};
+    __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(p));
+#else
+    *reinterpret_cast<float4*>(p) = x;
+#endif
+}
+
+template <int DK, int RPL, bool FULL, typename YT, typename OT>
+__device__ __forceinline__ void rec_item(
     const YT* __restrict__ y, const float* __restrict__ g, const float* __restrict__ beta,
     const int32_t* __restrict__ slot, float* __restrict__ rec, OT* __restrict__ out, int32_t H,
-    int32_t HV, int32_t dv, int32_t tiles_per_head, float scale, int32_t flags,
-    const int32_t* __restrict__ err_flag) {
+    int32_t HV, int32_t dv, int b, int hv, int tile, float scale, int32_t flags) {
     constexpr int NV = DK / 32;               // float4 per lane per row
-    if (call_rejected(err_flag)) return;
-    const int b = blockIdx.y;
-    const int hv = blockIdx.x / tiles_per_head;
-    const int tile = blockIdx.x - hv * tiles_per_head;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int sub = lane & 7;
@@ -60,10 +91,10 @@ __global__ __launch_bounds__(256) void decode_rec_kernel(
 #pragma unroll
             for (int r = 0; r < RPL; ++r) {
                 const int row = row0 + 32 * r;
-                if (row < dv) elem<OT>::st(ob + row, 0.0f);
+                if (FULL || row < dv) elem<OT>::st(ob + row, 0.0f);
             }
         }
-        return;
+        return;                               // next item
     }
 
     const int D = 2 * H * DK + HV * dv;
@@ -71,25 +102,33 @@ __global__ __launch_bounds__(256) void decode_rec_kernel(
     const YT* yb = y + static_cast<size_t>(b) * D;
     float* Sb = rec + (static_cast<size_t>(s) * HV + hv) * static_cast<size_t>(dv) * DK;
 
-    // 1. issue the state loads first (the long-latency HBM traffic)
-    float4 S[RPL][NV];
-#pragma unroll
-    for (int r = 0; r < RPL; ++r) {
-        const int row = row0 + 32 * r;
-#pragma unroll
-        for (int i = 0; i < NV; ++i)
-            S[r][i] = (row < dv)
-                ? *reinterpret_cast<const float4*>(Sb + static_cast<size_t>(row) * DK + 32 * i + 4 * sub)
-                : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-
-    // 2. q, k fragments of key head h (L2-resident activations) and their norms
+    // 1. q, k fragments of key head h first (small, L2-resident activations)
     float4 qf[NV], kf[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         qf[i] = load4<YT>(yb + h * DK + 32 * i + 4 * sub);
         kf[i] = load4<YT>(yb + H * DK + h * DK + 32 * i + 4 * sub);
     }
+    const YT* vb = yb + 2 * H * DK + hv * dv;
+    float vv[RPL];
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+        const int row = row0 + 32 * r;
+        vv[r] = (FULL || row < dv) ? elem<YT>::ld(vb + row) : 0.0f;
+    }
+    // 2. then the state loads (the long-latency HBM stream): with full tiles
+    //    (no row guards) the norm math below waits only for q, k and v, and
+    //    each row only for its own loads
+    float4 S[RPL][NV];
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+        const int row = row0 + 32 * r;
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            S[r][i] = (FULL || row < dv) ? state_ld(Sb + static_cast<size_t>(row) * DK + 32 * i + 4 * sub)
+                                         : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+
     float qmul = scale, kmul = 1.0f;
     if (flags & GDN_FLAG_QK_L2NORM) {
         float sq = 0.f, sk = 0.f;
@@ -113,13 +152,11 @@ __global__ __launch_bounds__(256) void decode_rec_kernel(
 
     const float alpha = expf(g[static_cast<size_t>(b) * HV + hv]);
     const float bt = beta[static_cast<size_t>(b) * HV + hv];
-    const YT* vb = yb + 2 * H * DK + hv * dv;
 
     // 3. per row: decay, predict, delta update, output
 #pragma unroll
     for (int r = 0; r < RPL; ++r) {
         const int row = row0 + 32 * r;
-        const float vv = (row < dv) ? elem<YT>::ld(vb + row) : 0.0f;
         float u = 0.f;
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
@@ -128,7 +165,7 @@ __global__ __launch_bounds__(256) void decode_rec_kernel(
             u = fmaf(S[r][i].z, kf[i].z, u); u = fmaf(S[r][i].w, kf[i].w, u);
         }
         u = sum8(u);
-        const float delta = bt * (vv - u);
+        const float delta = bt * (vv[r] - u);
         float o = 0.f;
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
@@ -138,12 +175,30 @@ __global__ __launch_bounds__(256) void decode_rec_kernel(
             o = fmaf(S[r][i].z, qf[i].z, o); o = fmaf(S[r][i].w, qf[i].w, o);
         }
         o = sum8(o);
-        if (row < dv) {
+        if (FULL || row < dv) {
 #pragma unroll
             for (int i = 0; i < NV; ++i)
-                *reinterpret_cast<float4*>(Sb + static_cast<size_t>(row) * DK + 32 * i + 4 * sub) = S[r][i];
+                state_st(Sb + static_cast<size_t>(row) * DK + 32 * i + 4 * sub, S[r][i]);
             if (sub == 0) elem<OT>::st(ob + row, o);
         }
+    }
+}
+
+template <int DK, int RPL, bool FULL, typename YT, typename OT>
+__global__ __launch_bounds__(256) void decode_rec_kernel(
+    const YT* __restrict__ y, const float* __restrict__ g, const float* __restrict__ beta,
+    const int32_t* __restrict__ slot, float* __restrict__ rec, OT* __restrict__ out, int32_t H,
+    int32_t HV, int32_t dv, int32_t tiles_per_head, int32_t n_items, float scale,
+    int32_t flags, const int32_t* __restrict__ err_flag) {
+    constexpr int NV = DK / 32;               // float4 per lane per row
+    if (call_rejected(err_flag)) return;
+    // persistent grid: workgroup-uniform loop over (row, value head, tile) items
+    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+        const int per_row = HV * tiles_per_head;
+        const int b = item / per_row;
+        const int hv = (item - b * per_row) / tiles_per_head;
+        const int tile = item - b * per_row - hv * tiles_per_head;
+        rec_item<DK, RPL, FULL, YT, OT>(y, g, beta, slot, rec, out, H, HV, dv, b, hv, tile, scale, flags);
     }
 }
 
@@ -154,15 +209,38 @@ struct RecArgs {
     hipStream_t st;
 };
 
-template <int DK, int RPL, typename YT, typename OT>
-hipError_t run_rec(const RecArgs& a) {
+// Compute units of the current device, queried once per device (a relaxed
+// atomic cache: concurrent first calls store the same value).
+int cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+template <int DK, int RPL, bool FULL, typename YT, typename OT>
+hipError_t run_rec_t(const RecArgs& a) {
     const int rows_per_wg = 32 * RPL;
     const int tiles = (a.d->head_v_dim + rows_per_wg - 1) / rows_per_wg;
-    dim3 grid(a.d->num_v_heads * tiles, a.batch);
-    return launch(decode_rec_kernel<DK, RPL, YT, OT>, grid, dim3(256), 0, a.st,
+    const int64_t items = static_cast<int64_t>(a.batch) * a.d->num_v_heads * tiles;
+    const int64_t resident = static_cast<int64_t>(cu_count()) * GDN_DECODE_WG_PER_CU;
+    const int grid = static_cast<int>(items < resident ? items : resident);
+    return launch(decode_rec_kernel<DK, RPL, FULL, YT, OT>, dim3(grid), dim3(256), 0, a.st,
                   static_cast<const YT*>(a.y), a.g, a.beta, a.slot, a.rec,
                   static_cast<OT*>(a.out), a.d->num_k_heads, a.d->num_v_heads,
-                  a.d->head_v_dim, tiles, a.scale, a.flags, a.err);
+                  a.d->head_v_dim, tiles, static_cast<int32_t>(items), a.scale, a.flags, a.err);
+}
+
+template <int DK, int RPL, typename YT, typename OT>
+hipError_t run_rec(const RecArgs& a) {
+    if (a.d->head_v_dim % (32 * RPL) == 0) return run_rec_t<DK, RPL, true, YT, OT>(a);
+    return run_rec_t<DK, RPL, false, YT, OT>(a);
 }
 
 // Rows per lane: as many 32-row steps as the head needs (up to 4), so one
@@ -171,8 +249,8 @@ hipError_t run_rec(const RecArgs& a) {
 template <int DK, typename YT, typename OT>
 hipError_t pick_rpl(const RecArgs& a) {
     const int dv = a.d->head_v_dim;
-    if (dv > 64) return run_rec<DK, 4, YT, OT>(a);
-    if (dv > 32) return run_rec<DK, 2, YT, OT>(a);
+    if (dv > 64 && GDN_DECODE_RPL_MAX >= 4) return run_rec<DK, 4, YT, OT>(a);
+    if (dv > 32 && GDN_DECODE_RPL_MAX >= 2) return run_rec<DK, 2, YT, OT>(a);
     return run_rec<DK, 1, YT, OT>(a);
 }
 
