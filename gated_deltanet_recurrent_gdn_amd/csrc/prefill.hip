@@ -254,39 +254,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(
             }
         }
         if (tid < CH) sm.beta[tid] = pbeta;
-        float gt = pg;                           // wave 0: this lane's g, scanned below
-        __syncthreads();
-
-        // ---------------- row norms (8 lanes per row, the decode kernel's order;
-        // fp32 inputs as hi + lo) and the cumulative log-decay (wave 0, a
-        // fixed-order inclusive scan)
-        for (int pass = 0; pass < 4; ++pass) {
-            const int rowid = pass * 32 + (tid >> 3);
-            const int sub = tid & 7;
-            const int rr = (rowid < CH) ? rowid : rowid - CH;
-            const bf16_t* rh = (rowid < CH) ? &sm.k[0][rr * SK] : &sm.q[0][rr * SK];
-            const bf16_t* rl = (rowid < CH) ? &sm.k[NP - 1][rr * SK] : &sm.q[NP - 1][rr * SK];
-            float acc = 0.f;
-#pragma unroll
-            for (int i = 0; i < D / 32; ++i) {
-                const uint2 u = *reinterpret_cast<const uint2*>(rh + 32 * i + 4 * sub);
-                float x0 = bf16lo_to_f32(u.x), x1 = bf16hi_to_f32(u.x);
-                float x2 = bf16lo_to_f32(u.y), x3 = bf16hi_to_f32(u.y);
-                if constexpr (SPL) {
-                    const uint2 w = *reinterpret_cast<const uint2*>(rl + 32 * i + 4 * sub);
-                    x0 += bf16lo_to_f32(w.x); x1 += bf16hi_to_f32(w.x);
-                    x2 += bf16lo_to_f32(w.y); x3 += bf16hi_to_f32(w.y);
-                }
-                acc = fmaf(x0, x0, acc); acc = fmaf(x1, x1, acc);
-                acc = fmaf(x2, x2, acc); acc = fmaf(x3, x3, acc);
-            }
-            acc = sum8(acc);
-            if (sub == 0) {
-                if (rowid < CH) sm.rk[rr] = norm ? 1.0f / sqrtf(acc + 1e-6f) : 1.0f;
-                else sm.rq[rr] = norm ? scale / sqrtf(acc + 1e-6f) : scale;
-            }
-        }
-        if (wave == 0) {
+        if (wave == 0) {                         // cumulative log-decay: fixed-order wave scan
+            float gt = pg;
 #pragma unroll
             for (int d = 1; d < 64; d <<= 1) {
                 const float y = __shfl_up(gt, d, 64);
@@ -296,27 +265,20 @@ __global__ __launch_bounds__(256) void prefill_kernel(
         }
         __syncthreads();
 
-        // ---------------- per-token coefficients (wave 0) and, in every wave,
-        // G = K K^T, P = Q K^T on MFMA with the epilogue forming A (fp32 into
-        // sm.g) and M o P (hi/lo bf16 into sm.mp) straight from the accumulators
-        if (tid < CH) {
-            const float gl = sm.gam[L - 1];
-            const float gv = sm.gam[tid];
-            const float et = expf(gv);
-            sm.eg[tid] = et * sm.rq[tid];
-            sm.ck[tid] = (tid < L) ? expf(gl - gv) * sm.rk[tid] : 0.0f;
-            sm.cwc[tid] = sm.beta[tid] * et * sm.rk[tid];
-            if (tid == 0) sm.egl = expf(gl);
-        }
+        // ---------------- G = K K^T, P = Q K^T and the diagonal block of Q Q^T on
+        // MFMA (raw x raw: hh, plus hl + lh for split inputs).  The row norms come
+        // from the diagonals of K K^T and Q Q^T (sums of squares in the MFMA's
+        // fixed order); after a barrier the epilogue forms A (fp32 into sm.g) and
+        // M o P (hi/lo bf16 into sm.mp) straight from the accumulators.
         {
             const int tb = wave;
-            f32x4 accg[4], accp[4];
+            f32x4 accg[4], accp[4], accq = f32x4{0, 0, 0, 0};
 #pragma unroll
             for (int jb = 0; jb < 4; ++jb) { accg[jb] = f32x4{0, 0, 0, 0}; accp[jb] = f32x4{0, 0, 0, 0}; }
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-                for (int pa = 0; pa < NP; ++pa) {        // raw x raw: hh (+ hl + lh)
+                for (int pa = 0; pa < NP; ++pa) {
                     const bf16x8 ak = frag_std(sm.k[pa], SK, 16 * tb + l16, 32 * ks, q4);
                     const bf16x8 aq = frag_std(sm.q[pa], SK, 16 * tb + l16, 32 * ks, q4);
 #pragma unroll
@@ -327,8 +289,29 @@ __global__ __launch_bounds__(256) void prefill_kernel(
                             accg[jb] = mfma(ak, bk, accg[jb]);
                             accp[jb] = mfma(aq, bk, accp[jb]);
                         }
+                        accq = mfma(aq, frag_std(sm.q[pb], SK, 16 * tb + l16, 32 * ks, q4), accq);
                     }
                 }
+            }
+            // diagonal element (16 tb + 4 q4 + r, 16 tb + l16) with 4 q4 + r == l16
+            const int r0 = l16 - 4 * q4;
+            if (r0 >= 0 && r0 < 4) {
+                float dk = accg[tb][0], dq = accq[0];
+#pragma unroll
+                for (int r = 1; r < 4; ++r)
+                    if (r == r0) { dk = accg[tb][r]; dq = accq[r]; }
+                sm.rk[16 * tb + l16] = norm ? 1.0f / sqrtf(dk + 1e-6f) : 1.0f;
+                sm.rq[16 * tb + l16] = norm ? scale / sqrtf(dq + 1e-6f) : scale;
+            }
+            __syncthreads();
+            if (tid < CH) {                      // per-token coefficients (wave 0)
+                const float gl = sm.gam[L - 1];
+                const float gv = sm.gam[tid];
+                const float et = expf(gv);
+                sm.eg[tid] = et * sm.rq[tid];
+                sm.ck[tid] = (tid < L) ? expf(gl - gv) * sm.rk[tid] : 0.0f;
+                sm.cwc[tid] = sm.beta[tid] * et * sm.rk[tid];
+                if (tid == 0) sm.egl = expf(gl);
             }
             float gr[4], brk[4], rqr[4];
 #pragma unroll
@@ -527,13 +510,14 @@ __global__ __launch_bounds__(256) void prefill_kernel(
         __syncthreads();                         // -W visible to all waves
 
         if (vact) {
-            // ------------ U = Ut - W S0^T ;  O1 = Q S0^T  (state split per k-step
-            // into hi/lo B fragments with permuted k-slots)
-            f32x4 o[4][VB];
+            // ------------ U = Ut - W S0^T and, transposed, O1^T = S0 Q^T.  The
+            // state's hi/lo fragments (permuted k-slots) are the B operand of the
+            // first and, holding the same values, the A operand of the second.
+            f32x4 o[VB][4];                      // O^T tiles (v-block, t-block)
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb)
+            for (int vb = 0; vb < VB; ++vb)
 #pragma unroll
-                for (int vb = 0; vb < VB; ++vb) o[tb][vb] = f32x4{0, 0, 0, 0};
+                for (int tb = 0; tb < 4; ++tb) o[vb][tb] = f32x4{0, 0, 0, 0};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 bf16x8 sh[VB], sl[VB];
@@ -548,32 +532,32 @@ __global__ __launch_bounds__(256) void prefill_kernel(
 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb) {
                     const bf16x8 aw = frag_perm(sm.vt_w[0], SK, 16 * tb + l16, 32 * ks, q4);
-                    const bf16x8 aq = frag_perm(sm.q[0], SK, 16 * tb + l16, 32 * ks, q4);
+                    const bf16x8 bq = frag_perm(sm.q[0], SK, 16 * tb + l16, 32 * ks, q4);
 #pragma unroll
                     for (int vb = 0; vb < VB; ++vb) {
                         u[tb][vb] = mfma(aw, sh[vb], u[tb][vb]);
                         u[tb][vb] = mfma(aw, sl[vb], u[tb][vb]);
-                        o[tb][vb] = mfma(aq, sh[vb], o[tb][vb]);
-                        o[tb][vb] = mfma(aq, sl[vb], o[tb][vb]);
+                        o[vb][tb] = mfma(sh[vb], bq, o[vb][tb]);
+                        o[vb][tb] = mfma(sl[vb], bq, o[vb][tb]);
                     }
                     if constexpr (SPL) {
-                        const bf16x8 aql = frag_perm(sm.q[NP - 1], SK, 16 * tb + l16, 32 * ks, q4);
+                        const bf16x8 bql = frag_perm(sm.q[NP - 1], SK, 16 * tb + l16, 32 * ks, q4);
 #pragma unroll
-                        for (int vb = 0; vb < VB; ++vb) o[tb][vb] = mfma(aql, sh[vb], o[tb][vb]);
+                        for (int vb = 0; vb < VB; ++vb) o[vb][tb] = mfma(sh[vb], bql, o[vb][tb]);
                     }
                 }
             }
-            // O1 rows scaled by e^gamma_t rq_t
+            // O1^T columns (tokens) scaled by e^gamma_t rq_t
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb)
+            for (int tb = 0; tb < 4; ++tb) {
+                const float e = sm.eg[16 * tb + l16];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float e = sm.eg[16 * tb + 4 * q4 + r];
-#pragma unroll
-                    for (int vb = 0; vb < VB; ++vb) o[tb][vb][r] *= e;
+                for (int vb = 0; vb < VB; ++vb) {
+                    o[vb][tb][0] *= e; o[vb][tb][1] *= e; o[vb][tb][2] *= e; o[vb][tb][3] *= e;
                 }
+            }
 
-            // ------------ O += (M o P) U   (U split, permuted t-slots)
+            // ------------ O^T += U^T (M o P)^T  (U split: A operand, permuted t-slots)
             bf16x8 uh[2][VB], ul[2][VB];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
@@ -594,27 +578,31 @@ __global__ __launch_bounds__(256) void prefill_kernel(
                     const bf16x8 ml = frag_perm(sm.mp + CH * ST, ST, 16 * tb + l16, 32 * ks, q4);
 #pragma unroll
                     for (int vb = 0; vb < VB; ++vb) {
-                        o[tb][vb] = mfma(mh, uh[ks][vb], o[tb][vb]);
-                        o[tb][vb] = mfma(mh, ul[ks][vb], o[tb][vb]);
-                        o[tb][vb] = mfma(ml, uh[ks][vb], o[tb][vb]);
+                        o[vb][tb] = mfma(uh[ks][vb], mh, o[vb][tb]);
+                        o[vb][tb] = mfma(ul[ks][vb], mh, o[vb][tb]);
+                        o[vb][tb] = mfma(uh[ks][vb], ml, o[vb][tb]);
                     }
                 }
-            // store O rows t < L
+            // store O: lane holds O[t = 16 tb + l16][v = 16 (wave VB + vb) + 4 q4 .. + 3]
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb)
+            for (int tb = 0; tb < 4; ++tb) {
+                const int t = 16 * tb + l16;
+                if (t < L) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = 16 * tb + 4 * q4 + r;
-                    if (t < L) {
-#pragma unroll
-                        for (int vb = 0; vb < VB; ++vb)
-                            elem<OT>::st(out + (static_cast<size_t>(c0 + t) * HV + hv) * D + 16 * (wave * VB + vb) + l16,
-                                         o[tb][vb][r]);
+                    for (int vb = 0; vb < VB; ++vb) {
+                        OT* dst = out + (static_cast<size_t>(c0 + t) * HV + hv) * D + 16 * (wave * VB + vb) + 4 * q4;
+                        if constexpr (sizeof(OT) == 4) {
+                            *reinterpret_cast<float4*>(dst) =
+                                make_float4(o[vb][tb][0], o[vb][tb][1], o[vb][tb][2], o[vb][tb][3]);
+                        } else {
+                            *reinterpret_cast<uint2*>(dst) =
+                                make_uint2(pack_bf16x2(o[vb][tb][0], o[vb][tb][1]),
+                                           pack_bf16x2(o[vb][tb][2], o[vb][tb][3]));
+                        }
                     }
                 }
+            }
         }
-
-        if (c0 + CH < t1) fetch(c0 + CH, min(CH, t1 - c0 - CH));   // next chunk, in flight
 
         if (vact) {
             // ------------ S0^T <- e^{gamma_L} S0^T + K^T (cK . U)
@@ -635,6 +623,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(
                     ch[ks][vb] = as_bf16x8(cat(h0, h1));
                     cl[ks][vb] = as_bf16x8(cat(l0, l1));
                 }
+            if (c0 + CH < t1) fetch(c0 + CH, min(CH, t1 - c0 - CH));   // next chunk, in flight
             const float egl = sm.egl;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
@@ -658,6 +647,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(
                 }
             }
         }
+        if (!vact && c0 + CH < t1) fetch(c0 + CH, min(CH, t1 - c0 - CH));
         __syncthreads();                         // LDS is rewritten by the next chunk
     }
 
