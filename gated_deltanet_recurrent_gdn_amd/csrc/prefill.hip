@@ -14,9 +14,10 @@
 // inverted by exact fp32 forward substitution (not Newton-Schulz) and merged
 // 16 -> 32 -> 64 with T21 = -T22 A21 T11.
 //
-// Design.  One workgroup per (sequence, value head) walks the sequence's
-// chunks in order with the state resident on chip: wave w owns 32 value
-// columns of S0^T (DK x DV) in MFMA accumulator registers.  Every contraction
+// Design.  One workgroup of eight waves per (sequence, value head) walks the
+// sequence's chunks in order with the state resident on chip: wave w owns 16
+// value columns of S0^T (DK x DV) in MFMA accumulator registers (two waves per
+// SIMD, so one wave's LDS and MFMA latency hides behind the other's work).  Every contraction
 // is v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  Raw bf16 inputs (K, Q,
 // V) are exact MFMA operands; fp32-derived operands that the error budget
 // cannot afford to round once (T-derived coefficients, U, the masked decayed
@@ -62,6 +63,43 @@ __device__ __forceinline__ void split4(const f32x4& x, uint2& hi, uint2& lo) {
     hi = make_uint2(h01, h23);
     lo = make_uint2(pack_bf16x2(x[0] - bf16lo_to_f32(h01), x[1] - bf16hi_to_f32(h01)),
                     pack_bf16x2(x[2] - bf16lo_to_f32(h23), x[3] - bf16hi_to_f32(h23)));
+}
+
+// Raw buffer access.  The descriptor holds a workgroup-uniform base and a byte
+// range; each lane adds a 32-bit offset.  Loads past the range return zero and
+// stores past it are dropped, which masks a partial chunk's missing rows.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int RSRC_WORD3 = 0x00020000;          // raw buffer, 32-bit data format (gfx9 family)
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), RSRC_WORD3);
+}
+__device__ __forceinline__ uint4 buf_ld16(rsrc_t r, uint32_t off) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ float buf_ld4f(rsrc_t r, uint32_t off) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ void buf_st16(rsrc_t r, uint32_t off, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{a, b, c, d}, r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_st8(rsrc_t r, uint32_t off, uint32_t a, uint32_t b) {
+    typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{a, b}, r, off, 0, 0);
+}
+
+// Broadcast lane j of each 16-lane row to the whole row (DPP row_newbcast,
+// controls 0x150 + j on CDNA); j must fold to a constant.
+__device__ __forceinline__ float row_bcast(float x, int j) {
+#define GDN_RB(J) case J: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + J, 0xF, 0xF, false))
+    switch (j) {
+        GDN_RB(0); GDN_RB(1); GDN_RB(2); GDN_RB(3); GDN_RB(4); GDN_RB(5); GDN_RB(6); GDN_RB(7);
+        GDN_RB(8); GDN_RB(9); GDN_RB(10); GDN_RB(11); GDN_RB(12); GDN_RB(13); GDN_RB(14);
+        default: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + 15, 0xF, 0xF, false));
+    }
+#undef GDN_RB
 }
 
 // Standard-slot fragment: 8 consecutive bf16 at row `row`, column c0 + 8q.
@@ -128,8 +166,11 @@ struct PrefillSmem {
 
 // D: head dim (d_k = d_v).  IT: input element type (bf16_t, or float read as
 // hi/lo bf16 planes).  OT: output element type.
+constexpr int PF_NW = 8;                 // waves per workgroup
+constexpr int PF_NT = 64 * PF_NW;        // threads per workgroup
+
 template <int D, typename IT, typename OT>
-__global__ __launch_bounds__(256) void prefill_kernel(
+__global__ __launch_bounds__(PF_NT) void prefill_kernel(
     const IT* __restrict__ qg, const IT* __restrict__ kg, const IT* __restrict__ vg,
     const float* __restrict__ gg, const float* __restrict__ bg, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ slot, float* __restrict__ rec, OT* __restrict__ out, int32_t H,
@@ -137,12 +178,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     constexpr bool SPL = sizeof(IT) == 4;        // fp32 inputs: hi/lo planes
     constexpr int NP = SPL ? 2 : 1;
     static_assert(D == 32 || D == 64 || D == 128, "head dim");
-    constexpr int NW = 4;                        // waves
+    constexpr int NW = PF_NW;                    // waves
     constexpr int KB = D / 16;                   // 16-row key blocks of the state
     constexpr int KS = D / 32;                   // 32-wide k-steps over the head dim
-    constexpr int VB = (D / 64 > 0) ? D / 64 : 1;    // 16-wide value blocks per wave
-    constexpr int WB = (KB / NW > 0) ? KB / NW : 1;  // 16-wide key blocks of W per wave
-    constexpr int CP = (D / 64 > 0) ? D / 64 : 1;    // load passes of 64 columns
+    constexpr int VB = (D / 16 / NW > 0) ? D / 16 / NW : 1;   // 16-wide value blocks per wave
+    constexpr int WB = (KB / NW > 0) ? KB / NW : 1;           // 16-wide key blocks of W per wave
+    constexpr int CG = PF_NT / 32;               // 8-column groups per load pass
+    constexpr int CP = (D / (8 * CG) > 0) ? D / (8 * CG) : 1; // load passes
     constexpr int WPE = SPL ? 2 : 1;             // uint4 words per 8 input elements
     using Sm = PrefillSmem<D, SPL>;
     constexpr int SK = Sm::SK, ST = Sm::ST, SF = Sm::SF;
@@ -165,7 +207,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     const bool wact = wave * WB < KB;            // this wave owns W columns
 
     if (s <= 0) {                                // inactive: zero outputs, state untouched
-        for (int64_t i = tid; i < static_cast<int64_t>(t1 - t0) * D; i += 256) {
+        for (int64_t i = tid; i < static_cast<int64_t>(t1 - t0) * D; i += PF_NT) {
             const int64_t t = t0 + i / D;
             elem<OT>::st(out + (t * HV + hv) * D + i % D, 0.0f);
         }
@@ -191,34 +233,47 @@ __global__ __launch_bounds__(256) void prefill_kernel(
         }
 
     // Chunk loads.  Thread (tp, cg) moves token rows 2tp, 2tp+1 at columns
-    // 8 (cg + 8 pass); K^T / V^T receive 32-bit (t, t+1) pairs, so the 64 lanes
+    // 8 (cg + CG pass); K^T / V^T receive 32-bit (t, t+1) pairs, so the 64 lanes
     // of a wave store to 64 distinct banks.  The next chunk's loads are issued
     // during the current chunk's state update and staged at the loop top.
     const int tp = tid & 31;
-    const int cg = tid >> 5;                     // 0..7
+    const int cg = tid >> 5;                     // 0..CG-1
     const int ta = 2 * tp;
     uint4 pk[CP][2][WPE], pq[CP][2][WPE], pv[CP][2][WPE];
     float pbeta = 0.0f, pg = 0.0f;
+    // Loads go through buffer descriptors over the chunk's rows (the entry
+    // point's dims bound a chunk's span, 64 HV D elements, below 2^28 bytes),
+    // so rows past the chunk's length read as zero.
+    const uint32_t off_kq = static_cast<uint32_t>(h * D) * sizeof(IT);
+    const uint32_t off_v = static_cast<uint32_t>(hv * D) * sizeof(IT);
+    const uint32_t row_kq = static_cast<uint32_t>(H * D) * sizeof(IT);
+    const uint32_t row_v = static_cast<uint32_t>(HV * D) * sizeof(IT);
     auto fetch = [&](int32_t c, int Lc) {
+        const rsrc_t rk_ = make_rsrc(kg + static_cast<size_t>(c) * H * D, Lc * row_kq);
+        const rsrc_t rq_ = make_rsrc(qg + static_cast<size_t>(c) * H * D, Lc * row_kq);
+        const rsrc_t rv_ = make_rsrc(vg + static_cast<size_t>(c) * HV * D, Lc * row_v);
 #pragma unroll
         for (int pass = 0; pass < CP; ++pass) {
-            const int k0 = 8 * (cg + 8 * pass);
+            const int k0 = 8 * (cg + CG * pass);
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
-                const int t = ta + e;
-                const bool ok = (t < Lc) && (k0 < D);
-                const size_t off = (static_cast<size_t>(c + t) * H + h) * D + k0;
-                const size_t offv = (static_cast<size_t>(c + t) * HV + hv) * D + k0;
+                const uint32_t t = ta + e;
+                const uint32_t kk = k0 * sizeof(IT);
 #pragma unroll
                 for (int w = 0; w < WPE; ++w) {
-                    pk[pass][e][w] = ok ? reinterpret_cast<const uint4*>(kg + off)[w] : make_uint4(0, 0, 0, 0);
-                    pq[pass][e][w] = ok ? reinterpret_cast<const uint4*>(qg + off)[w] : make_uint4(0, 0, 0, 0);
-                    pv[pass][e][w] = ok ? reinterpret_cast<const uint4*>(vg + offv)[w] : make_uint4(0, 0, 0, 0);
+                    if (8 * CG * CP == D || k0 < D) {
+                        pk[pass][e][w] = buf_ld16(rk_, t * row_kq + off_kq + kk + 16 * w);
+                        pq[pass][e][w] = buf_ld16(rq_, t * row_kq + off_kq + kk + 16 * w);
+                        pv[pass][e][w] = buf_ld16(rv_, t * row_v + off_v + kk + 16 * w);
+                    }
                 }
             }
         }
-        pbeta = (tid < Lc) ? bg[static_cast<size_t>(c + tid) * HV + hv] : 0.0f;   // used by tid < 64
-        pg = (tid < Lc) ? gg[static_cast<size_t>(c + tid) * HV + hv] : 0.0f;      // used by wave 0
+        const rsrc_t rb = make_rsrc(bg + static_cast<size_t>(c) * HV, Lc * HV * 4);
+        const rsrc_t rg = make_rsrc(gg + static_cast<size_t>(c) * HV, Lc * HV * 4);
+        const uint32_t ob = static_cast<uint32_t>(min(tid, CH) * HV + hv) * 4;
+        pbeta = buf_ld4f(rb, ob);                // used by tid < 64
+        pg = buf_ld4f(rg, ob);                   // used by wave 0
     };
     fetch(t0, min(CH, t1 - t0));
 
@@ -228,7 +283,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(
         // ---------------- stage the fetched chunk into LDS (planes hi [, lo])
 #pragma unroll
         for (int pass = 0; pass < CP; ++pass) {
-            const int k0 = 8 * (cg + 8 * pass);
+            const int k0 = 8 * (cg + CG * pass);
             if (k0 < D) {
                 uint4 kw[2][2], qw[2][2], vw[2][2];      // [row][plane]
 #pragma unroll
@@ -266,15 +321,19 @@ __global__ __launch_bounds__(256) void prefill_kernel(
         __syncthreads();
 
         // ---------------- G = K K^T, P = Q K^T and the diagonal block of Q Q^T on
-        // MFMA (raw x raw: hh, plus hl + lh for split inputs).  The row norms come
-        // from the diagonals of K K^T and Q Q^T (sums of squares in the MFMA's
-        // fixed order); after a barrier the epilogue forms A (fp32 into sm.g) and
+        // MFMA (raw x raw: hh, plus hl + lh for split inputs), computed as
+        // transposed tiles (key block as the A operand) so that a lane holds one
+        // row i and four consecutive columns c.  The row norms come from the
+        // diagonals of K K^T and Q Q^T (sums of squares in the MFMA's fixed
+        // order); after a barrier the epilogue forms A (fp32 into sm.g) and
         // M o P (hi/lo bf16 into sm.mp) straight from the accumulators.
         {
-            const int tb = wave;
-            f32x4 accg[4], accp[4], accq = f32x4{0, 0, 0, 0};
+            const int tb = wave & 3;             // 16-token row block
+            const int jh = wave >> 2;            // column blocks 2 jh, 2 jh + 1
+            const bool diag = (tb >> 1) == jh;   // this wave also owns block (tb, tb)
+            f32x4 accg[2], accp[2], accq = f32x4{0, 0, 0, 0};
 #pragma unroll
-            for (int jb = 0; jb < 4; ++jb) { accg[jb] = f32x4{0, 0, 0, 0}; accp[jb] = f32x4{0, 0, 0, 0}; }
+            for (int j = 0; j < 2; ++j) { accg[j] = f32x4{0, 0, 0, 0}; accp[j] = f32x4{0, 0, 0, 0}; }
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
@@ -284,24 +343,28 @@ __global__ __launch_bounds__(256) void prefill_kernel(
 #pragma unroll
                     for (int pb = 0; pb < NP - pa; ++pb) {
 #pragma unroll
-                        for (int jb = 0; jb < 4; ++jb) {
-                            const bf16x8 bk = frag_std(sm.k[pb], SK, 16 * jb + l16, 32 * ks, q4);
-                            accg[jb] = mfma(ak, bk, accg[jb]);
-                            accp[jb] = mfma(aq, bk, accp[jb]);
+                        for (int j = 0; j < 2; ++j) {
+                            const bf16x8 bk = frag_std(sm.k[pb], SK, 16 * (2 * jh + j) + l16, 32 * ks, q4);
+                            accg[j] = mfma(bk, ak, accg[j]);
+                            accp[j] = mfma(bk, aq, accp[j]);
                         }
-                        accq = mfma(aq, frag_std(sm.q[pb], SK, 16 * tb + l16, 32 * ks, q4), accq);
+                        if (diag)
+                            accq = mfma(frag_std(sm.q[pb], SK, 16 * tb + l16, 32 * ks, q4), aq, accq);
                     }
                 }
             }
-            // diagonal element (16 tb + 4 q4 + r, 16 tb + l16) with 4 q4 + r == l16
+            // lane holds G[i][c + r], P[i][c + r] for i = 16 tb + l16, c = 16 jc + 4 q4;
+            // the diagonal element (i, i) sits at r = l16 - 4 q4 of column block tb
+            const int i = 16 * tb + l16;
             const int r0 = l16 - 4 * q4;
-            if (r0 >= 0 && r0 < 4) {
-                float dk = accg[tb][0], dq = accq[0];
+            if (diag && r0 >= 0 && r0 < 4) {
+                const f32x4 gd = accg[tb & 1];
+                float dk = gd[0], dq = accq[0];
 #pragma unroll
                 for (int r = 1; r < 4; ++r)
-                    if (r == r0) { dk = accg[tb][r]; dq = accq[r]; }
-                sm.rk[16 * tb + l16] = norm ? 1.0f / sqrtf(dk + 1e-6f) : 1.0f;
-                sm.rq[16 * tb + l16] = norm ? scale / sqrtf(dq + 1e-6f) : scale;
+                    if (r == r0) { dk = gd[r]; dq = accq[r]; }
+                sm.rk[i] = norm ? 1.0f / sqrtf(dk + 1e-6f) : 1.0f;
+                sm.rq[i] = norm ? scale / sqrtf(dq + 1e-6f) : scale;
             }
             __syncthreads();
             if (tid < CH) {                      // per-token coefficients (wave 0)
@@ -313,59 +376,55 @@ __global__ __launch_bounds__(256) void prefill_kernel(
                 sm.cwc[tid] = sm.beta[tid] * et * sm.rk[tid];
                 if (tid == 0) sm.egl = expf(gl);
             }
-            float gr[4], brk[4], rqr[4];
+            const float gi = sm.gam[i];
+            const float brk = sm.beta[i] * sm.rk[i];
+            const float rqi = sm.rq[i];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * tb + 4 * q4 + r;
-                gr[r] = sm.gam[i];
-                brk[r] = sm.beta[i] * sm.rk[i];
-                rqr[r] = sm.rq[i];
-            }
-#pragma unroll
-            for (int jb = 0; jb < 4; ++jb) {
-                const int c = 16 * jb + l16;
-                const float gc = sm.gam[c];
-                const float rkc = sm.rk[c];
+            for (int j = 0; j < 2; ++j) {
+                const int c = 16 * (2 * jh + j) + 4 * q4;
+                const float4 gc = *reinterpret_cast<const float4*>(&sm.gam[c]);
+                const float4 rkc = *reinterpret_cast<const float4*>(&sm.rk[c]);
+                const float gcs[4] = {gc.x, gc.y, gc.z, gc.w};
+                const float rks[4] = {rkc.x, rkc.y, rkc.z, rkc.w};
+                f32x4 a, mp;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int i = 16 * tb + 4 * q4 + r;
-                    const float dec = (c <= i) ? expf(gr[r] - gc) : 0.0f;
-                    sm.g[i * SF + c] = (c < i) ? (brk[r] * rkc) * (dec * accg[jb][r]) : 0.0f;
-                    const float mp = (rqr[r] * rkc) * (dec * accp[jb][r]);
-                    const bf16_t hi = f32_to_bf16(mp);
-                    sm.mp[i * ST + c] = hi;
-                    sm.mp[CH * ST + i * ST + c] = f32_to_bf16(mp - bf16_to_f32(hi));
+                    const float dec = (c + r <= i) ? expf(gi - gcs[r]) : 0.0f;
+                    a[r] = (c + r < i) ? (brk * rks[r]) * (dec * accg[j][r]) : 0.0f;
+                    mp[r] = (rqi * rks[r]) * (dec * accp[j][r]);
                 }
+                *reinterpret_cast<float4*>(&sm.g[i * SF + c]) = make_float4(a[0], a[1], a[2], a[3]);
+                uint2 h2, l2;
+                split4(mp, h2, l2);
+                *reinterpret_cast<uint2*>(&sm.mp[i * ST + c]) = h2;
+                *reinterpret_cast<uint2*>(&sm.mp[CH * ST + i * ST + c]) = l2;
             }
         }
         __syncthreads();
 
         // ---------------- T = (I + A)^-1.  Diagonal 16x16 blocks by forward
-        // substitution (wave 0: lane = 16 block + column); the upper triangle of
+        // substitution (wave 0: lane = 16 block + column c).  Lane c holds column
+        // c of each row of the block; row r's entry A[r][j] reaches every lane of
+        // the block by a DPP row broadcast from lane j.  Right-looking order: once
+        // T[j][c] is final, every later row r adds A[r][j] T[j][c], so each row
+        // still accumulates its terms in ascending j.  The upper triangle of
         // sm.g is zero from the epilogue above and stays zero.
         if (wave == 0) {
             const int b = lane >> 4;
             const int c = lane & 15;
-            const float* blk = &sm.g[(16 * b) * SF + 16 * b];
-            float tc[16];
+            float* blk = &sm.g[(16 * b) * SF + 16 * b];
+            float ar[16], acc[16], tc[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) tc[r] = (r == c) ? 1.0f : 0.0f;
+            for (int r = 1; r < 16; ++r) { ar[r] = blk[r * SF + c]; acc[r] = 0.0f; }
+            tc[0] = (c == 0) ? 1.0f : 0.0f;
 #pragma unroll
-            for (int r = 1; r < 16; ++r) {
-                float arow[16];
+            for (int j = 0; j < 15; ++j) {
 #pragma unroll
-                for (int j4 = 0; j4 < (r + 3) / 4; ++j4) {
-                    const float4 a4 = *reinterpret_cast<const float4*>(blk + r * SF + 4 * j4);
-                    arow[4 * j4] = a4.x; arow[4 * j4 + 1] = a4.y;
-                    arow[4 * j4 + 2] = a4.z; arow[4 * j4 + 3] = a4.w;
-                }
-                float acc = 0.f;
-#pragma unroll
-                for (int j = 0; j < r; ++j) acc = fmaf(arow[j], tc[j], acc);
-                tc[r] = (r > c) ? -acc : tc[r];
+                for (int r = j + 1; r < 16; ++r) acc[r] = fmaf(row_bcast(ar[r], j), tc[j], acc[r]);
+                tc[j + 1] = (j + 1 > c) ? -acc[j + 1] : ((j + 1 == c) ? 1.0f : 0.0f);
             }
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sm.g[(16 * b + r) * SF + 16 * b + c] = tc[r];
+            for (int r = 0; r < 16; ++r) blk[r * SF + c] = tc[r];
         }
         __syncthreads();
         // merge 16 -> 32 for block pairs p = (0,1), (2,3) on fp32 MFMA (waves 0, 1):
@@ -392,9 +451,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(
             for (int r = 0; r < 4; ++r) sm.g[(b1 + 4 * q4 + r) * SF + b0 + l16] = -t[r];
         }
         __syncthreads();
-        // merge 32 -> 64 (wave = 16x16 output tile (ti, tj)): X = A[32:64][0:32] T11,
+        // merge 32 -> 64 (waves 0..3: 16x16 output tile (ti, tj)): X = A[32:64][0:32] T11,
         // T21 = -T22 X.  T11's block (0, 1) and T22's block (0, 1) are zero: skipped.
-        {
+        if (wave < 4) {
             const int ti = wave >> 1, tj = wave & 1;
             f32x4 x = f32x4{0, 0, 0, 0};
 #pragma unroll
@@ -407,7 +466,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(
             for (int r = 0; r < 4; ++r) sm.pc.x[(16 * ti + 4 * q4 + r) * 36 + 16 * tj + l16] = x[r];
         }
         __syncthreads();
-        {
+        if (wave < 4) {
             const int ti = wave >> 1, tj = wave & 1;
             f32x4 t = f32x4{0, 0, 0, 0};
 #pragma unroll
@@ -422,12 +481,12 @@ __global__ __launch_bounds__(256) void prefill_kernel(
         __syncthreads();
 
         // ---------------- coefficients cW = T diag(cwc), cU = T diag(beta), split
-        // (thread: row r, 16 columns; T's upper triangle is exactly zero)
+        // (thread: row r, 8 columns; T's upper triangle is exactly zero)
         {
-            const int r = tid >> 2, cb = 16 * (tid & 3);
-            uint32_t wh[8], wl[8], uh[8], ul[8];
+            const int r = tid >> 3, cb = 8 * (tid & 7);
+            uint32_t wh[4], wl[4], uh[4], ul[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < 2; ++j) {
                 const float4 t = *reinterpret_cast<const float4*>(&sm.g[r * SF + cb + 4 * j]);
                 const float4 cw = *reinterpret_cast<const float4*>(&sm.cwc[cb + 4 * j]);
                 const float4 bt = *reinterpret_cast<const float4*>(&sm.beta[cb + 4 * j]);
@@ -439,13 +498,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(
             }
             bf16_t* base = sm.pc.c + r * ST + cb;
             *reinterpret_cast<uint4*>(base + 0 * CH * ST) = make_uint4(wh[0], wh[1], wh[2], wh[3]);
-            *reinterpret_cast<uint4*>(base + 0 * CH * ST + 8) = make_uint4(wh[4], wh[5], wh[6], wh[7]);
             *reinterpret_cast<uint4*>(base + 1 * CH * ST) = make_uint4(wl[0], wl[1], wl[2], wl[3]);
-            *reinterpret_cast<uint4*>(base + 1 * CH * ST + 8) = make_uint4(wl[4], wl[5], wl[6], wl[7]);
             *reinterpret_cast<uint4*>(base + 2 * CH * ST) = make_uint4(uh[0], uh[1], uh[2], uh[3]);
-            *reinterpret_cast<uint4*>(base + 2 * CH * ST + 8) = make_uint4(uh[4], uh[5], uh[6], uh[7]);
             *reinterpret_cast<uint4*>(base + 3 * CH * ST) = make_uint4(ul[0], ul[1], ul[2], ul[3]);
-            *reinterpret_cast<uint4*>(base + 3 * CH * ST + 8) = make_uint4(ul[4], ul[5], ul[6], ul[7]);
         }
         __syncthreads();
 
@@ -583,22 +638,22 @@ __global__ __launch_bounds__(256) void prefill_kernel(
                         o[vb][tb] = mfma(uh[ks][vb], ml, o[vb][tb]);
                     }
                 }
-            // store O: lane holds O[t = 16 tb + l16][v = 16 (wave VB + vb) + 4 q4 .. + 3]
+            // store O: lane holds O[t = 16 tb + l16][v = 16 (wave VB + vb) + 4 q4 .. + 3];
+            // rows t >= L fall outside the descriptor's range and are dropped
+            const uint32_t row_o = static_cast<uint32_t>(HV * D) * sizeof(OT);
+            const rsrc_t ro = make_rsrc(out + static_cast<size_t>(c0) * HV * D, L * row_o);
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) {
-                const int t = 16 * tb + l16;
-                if (t < L) {
 #pragma unroll
-                    for (int vb = 0; vb < VB; ++vb) {
-                        OT* dst = out + (static_cast<size_t>(c0 + t) * HV + hv) * D + 16 * (wave * VB + vb) + 4 * q4;
-                        if constexpr (sizeof(OT) == 4) {
-                            *reinterpret_cast<float4*>(dst) =
-                                make_float4(o[vb][tb][0], o[vb][tb][1], o[vb][tb][2], o[vb][tb][3]);
-                        } else {
-                            *reinterpret_cast<uint2*>(dst) =
-                                make_uint2(pack_bf16x2(o[vb][tb][0], o[vb][tb][1]),
-                                           pack_bf16x2(o[vb][tb][2], o[vb][tb][3]));
-                        }
+                for (int vb = 0; vb < VB; ++vb) {
+                    const uint32_t off = static_cast<uint32_t>(16 * tb + l16) * row_o +
+                        static_cast<uint32_t>(hv * D + 16 * (wave * VB + vb) + 4 * q4) * sizeof(OT);
+                    if constexpr (sizeof(OT) == 4) {
+                        buf_st16(ro, off, __float_as_uint(o[vb][tb][0]), __float_as_uint(o[vb][tb][1]),
+                                 __float_as_uint(o[vb][tb][2]), __float_as_uint(o[vb][tb][3]));
+                    } else {
+                        buf_st8(ro, off, pack_bf16x2(o[vb][tb][0], o[vb][tb][1]),
+                                pack_bf16x2(o[vb][tb][2], o[vb][tb][3]));
                     }
                 }
             }
@@ -671,7 +726,7 @@ hipError_t run_prefill(const void* q, const void* k, const void* v, const float*
                        float* rec, void* out, const gdn_dims& d, float scale, int32_t flags,
                        const int32_t* err, hipStream_t st) {
     dim3 grid(d.num_v_heads, n_seqs);
-    return launch(prefill_kernel<D, IT, OT>, grid, dim3(256), 0, st,
+    return launch(prefill_kernel<D, IT, OT>, grid, dim3(PF_NT), 0, st,
                   static_cast<const IT*>(q), static_cast<const IT*>(k),
                   static_cast<const IT*>(v), g, beta, cu, slot, rec, static_cast<OT*>(out),
                   d.num_k_heads, d.num_v_heads, scale, flags, err);
