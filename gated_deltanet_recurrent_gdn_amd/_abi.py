@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libgdn.so")
 
 GDN_F32, GDN_BF16 = 0, 1
 FLAG_SILU, FLAG_QK_L2NORM, FLAG_VALIDATE = 1, 2, 4
+FLAG_STEP_FUSED, FLAG_STEP_SPLIT = 8, 16
 EFLAG_SLOT_RANGE, EFLAG_SLOT_REPEAT, EFLAG_SEQLENS = 1, 2, 4
 DEFAULT_DECODE_FLAGS = FLAG_SILU | FLAG_QK_L2NORM
 DEFAULT_PREFILL_FLAGS = FLAG_QK_L2NORM

@@ -109,10 +109,14 @@ gdn_status gdn_decode_step(const void* mixed_qkv, gdn_dtype x_dt, const float* g
                            int32_t num_slots, void* out, gdn_dtype out_dt, const gdn_dims* dims,
                            float scale, int32_t flags, void* workspace, size_t workspace_bytes,
                            int32_t* err_flag, void* stream) {
-    if (gdn_status st = check_flags(flags, KNOWN_FLAGS, err_flag)) return st;
+    if (gdn_status st = check_flags(flags, KNOWN_FLAGS | GDN_FLAG_STEP_FUSED | GDN_FLAG_STEP_SPLIT,
+                                    err_flag))
+        return st;
+    if ((flags & GDN_FLAG_STEP_FUSED) && (flags & GDN_FLAG_STEP_SPLIT)) return GDN_ERR_FLAGS;
     if (gdn_status st = check_dims(dims)) return st;
     if (batch < 0 || batch > 65535 || num_slots < 1) return GDN_ERR_DIMS;
     if (static_cast<int64_t>(batch) * dims->num_v_heads > (1 << 24)) return GDN_ERR_DIMS;
+    if ((flags & GDN_FLAG_STEP_FUSED) && !decode_step_fused_fits(*dims)) return GDN_ERR_DIMS;
     if (!dtype_ok(x_dt) || !dtype_ok(cs_dt) || !dtype_ok(w_dt) || !dtype_ok(out_dt))
         return GDN_ERR_DTYPE;
     if (batch > 0) {
@@ -129,13 +133,22 @@ gdn_status gdn_decode_step(const void* mixed_qkv, gdn_dtype x_dt, const float* g
         GDN_TRY_LAUNCH(launch_validate(slot_idx, batch, num_slots, nullptr, 0, err_flag, s));
     if (batch == 0) return GDN_OK;
     const int32_t* ef = (flags & GDN_FLAG_VALIDATE) ? err_flag : nullptr;
+    const int32_t kflags = flags & ~(GDN_FLAG_STEP_FUSED | GDN_FLAG_STEP_SPLIT);
+    const bool fused = (flags & GDN_FLAG_STEP_FUSED) ||
+                       (!(flags & GDN_FLAG_STEP_SPLIT) && decode_step_use_fused(*dims, batch));
+    if (fused) {
+        GDN_TRY_LAUNCH(launch_decode_step_fused(mixed_qkv, x_dt, g, beta, slot_idx, batch, conv_state,
+                                                cs_dt, conv_weight, conv_bias, w_dt, rec_state, out,
+                                                out_dt, *dims, scale, kflags, ef, s));
+        return GDN_OK;
+    }
     const int32_t D = static_cast<int32_t>(conv_channels(dims));
     float* y = static_cast<float*>(workspace);
     GDN_TRY_LAUNCH(launch_conv_decode(mixed_qkv, x_dt, slot_idx, batch, conv_state, cs_dt,
                                       conv_weight, conv_bias, w_dt, y, GDN_F32, D,
-                                      flags & GDN_FLAG_SILU, ef, s));
+                                      kflags & GDN_FLAG_SILU, ef, s));
     GDN_TRY_LAUNCH(launch_decode_rec(y, GDN_F32, g, beta, slot_idx, batch, rec_state, out,
-                                     out_dt, *dims, scale, flags, ef, s));
+                                     out_dt, *dims, scale, kflags, ef, s));
     return GDN_OK;
 }
 

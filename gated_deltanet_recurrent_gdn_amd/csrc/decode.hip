@@ -23,6 +23,7 @@
 // bitwise.  No LDS is used at all.
 #include <atomic>
 
+#include "conv_io.hpp"
 #include "gdn_device.hpp"
 #include "gdn_internal.hpp"
 
@@ -202,6 +203,158 @@ __global__ __launch_bounds__(256) void decode_rec_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Fused decode step.  One workgroup per (row b, key head h) group owns the
+// group's conv channels -- q_h, k_h and the v channels of the G = HV / H value
+// heads that share h -- so it reads and rolls them with no other workgroup
+// touching them, and keeps the post-conv activations in LDS instead of an HBM
+// workspace.  The recurrence then streams the group's G dv state rows in
+// passes of 32 rows with the per-row arithmetic of rec_item, in the same
+// order, so this kernel and the conv kernel + decode_rec_kernel pair give
+// bitwise-identical results.  The first pass's state loads are issued right
+// after the conv's own loads, so that they are in flight during the conv.
+// ---------------------------------------------------------------------------
+template <int DK, typename XT, typename CT, typename WT, typename OT>
+__global__ __launch_bounds__(256) void decode_step_kernel(
+    const XT* __restrict__ x, const float* __restrict__ g, const float* __restrict__ beta,
+    const int32_t* __restrict__ slot, CT* __restrict__ cs, const WT* __restrict__ w,
+    const WT* __restrict__ bias, float* __restrict__ rec, OT* __restrict__ out, int32_t H,
+    int32_t HV, int32_t dv, int32_t n_groups, float scale, int32_t flags,
+    const int32_t* __restrict__ err_flag) {
+    constexpr int NV = DK / 32;               // float4 per lane per row
+    extern __shared__ float ys[];             // [q_h (DK) | k_h (DK) | v of the group (G dv)]
+    if (call_rejected(err_flag)) return;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int sub = lane & 7;
+    const int rl = wave * 8 + (lane >> 3);    // row within a 32-row pass
+    const int G = HV / H;
+    const int R = G * dv;                     // state rows of the group
+    const int D = 2 * H * DK + HV * dv;
+    const int units = (2 * DK + R) / 4;       // conv work: 4 channels per unit
+
+    for (int grp = blockIdx.x; grp < n_groups; grp += gridDim.x) {
+        const int b = grp / H;
+        const int h = grp - b * H;
+        const int32_t s = slot[b];
+        OT* ob = out + (static_cast<size_t>(b) * HV + static_cast<size_t>(h) * G) * dv;
+        if (s <= 0) {                         // inactive row: zeros, caches untouched
+            for (int r = threadIdx.x; r < R; r += 256) elem<OT>::st(ob + r, 0.0f);
+            continue;
+        }
+        float* Sg = rec + ((static_cast<size_t>(s) * HV + static_cast<size_t>(h) * G) * dv) * DK;
+
+        auto fetch = [&](float4 (&St)[NV], int r0) {
+#pragma unroll
+            for (int i = 0; i < NV; ++i)
+                St[i] = state_ld(Sg + static_cast<size_t>(r0 + rl) * DK + 32 * i + 4 * sub);
+        };
+        float4 S[NV];
+
+        // conv of the group's channels into LDS (and the in-place roll).  With
+        // one 4-channel unit per thread, the unit's loads go out first and the
+        // first pass's state loads after them, so the conv math waits for its
+        // own loads only and the state rows are in flight during it.
+        const XT* xb = x + static_cast<size_t>(b) * D;
+        CT* csb = cs + static_cast<size_t>(s) * D * (CONV_W - 1);
+        auto channel = [&](int lc) {
+            return (lc < DK) ? h * DK + lc
+                 : (lc < 2 * DK) ? H * DK + h * DK + (lc - DK)
+                                 : 2 * H * DK + h * R + (lc - 2 * DK);
+        };
+        const bool silu_on = (flags & GDN_FLAG_SILU) != 0;
+        if (units <= 256) {
+            // threads past the last unit re-read unit 0 (loads stay unconditional)
+            const bool mine = static_cast<int>(threadIdx.x) < units;
+            const int lc = mine ? 4 * static_cast<int>(threadIdx.x) : 0;
+            const int c = channel(lc);
+            Conv4In<XT, CT, WT> in;
+            conv4_load<XT, CT, WT>(xb + c, csb + static_cast<size_t>(c) * (CONV_W - 1), w + c * CONV_W,
+                                   bias ? bias + c : nullptr, in);
+            fetch(S, 0);
+            if (mine) {
+                float y[4];
+                conv4_finish<XT, CT, WT>(in, csb + static_cast<size_t>(c) * (CONV_W - 1), silu_on, y);
+                *reinterpret_cast<float4*>(&ys[lc]) = make_float4(y[0], y[1], y[2], y[3]);
+            }
+        } else {
+            for (int u = threadIdx.x; u < units; u += 256) {
+                const int lc = 4 * u;
+                const int c = channel(lc);
+                float y[4];
+                conv4_token<XT, CT, WT>(xb + c, csb + static_cast<size_t>(c) * (CONV_W - 1), w + c * CONV_W,
+                                        bias ? bias + c : nullptr, silu_on, y);
+                *reinterpret_cast<float4*>(&ys[lc]) = make_float4(y[0], y[1], y[2], y[3]);
+            }
+            fetch(S, 0);
+        }
+        __syncthreads();
+
+        float4 qf[NV], kf[NV];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            qf[i] = *reinterpret_cast<const float4*>(&ys[32 * i + 4 * sub]);
+            kf[i] = *reinterpret_cast<const float4*>(&ys[DK + 32 * i + 4 * sub]);
+        }
+        float qmul = scale, kmul = 1.0f;
+        if (flags & GDN_FLAG_QK_L2NORM) {
+            float sq = 0.f, sk = 0.f;
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                sq = fmaf(qf[i].x, qf[i].x, sq); sq = fmaf(qf[i].y, qf[i].y, sq);
+                sq = fmaf(qf[i].z, qf[i].z, sq); sq = fmaf(qf[i].w, qf[i].w, sq);
+                sk = fmaf(kf[i].x, kf[i].x, sk); sk = fmaf(kf[i].y, kf[i].y, sk);
+                sk = fmaf(kf[i].z, kf[i].z, sk); sk = fmaf(kf[i].w, kf[i].w, sk);
+            }
+            sq = sum8(sq);
+            sk = sum8(sk);
+            qmul = scale / sqrtf(sq + 1e-6f);
+            kmul = 1.0f / sqrtf(sk + 1e-6f);
+        }
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            qf[i].x *= qmul; qf[i].y *= qmul; qf[i].z *= qmul; qf[i].w *= qmul;
+            kf[i].x *= kmul; kf[i].y *= kmul; kf[i].z *= kmul; kf[i].w *= kmul;
+        }
+
+        // the passes: pass 0's rows are already in S
+        auto pass = [&](int r0) {
+            const int r = r0 + rl;
+            const int hv = h * G + r0 / dv;   // a pass lies inside one head (dv % 32 == 0)
+            const float alpha = expf(g[static_cast<size_t>(b) * HV + hv]);
+            const float bt = beta[static_cast<size_t>(b) * HV + hv];
+            const float vr = ys[2 * DK + r];
+            float u = 0.f;
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                S[i].x *= alpha; S[i].y *= alpha; S[i].z *= alpha; S[i].w *= alpha;
+                u = fmaf(S[i].x, kf[i].x, u); u = fmaf(S[i].y, kf[i].y, u);
+                u = fmaf(S[i].z, kf[i].z, u); u = fmaf(S[i].w, kf[i].w, u);
+            }
+            u = sum8(u);
+            const float delta = bt * (vr - u);
+            float o = 0.f;
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                S[i].x = fmaf(delta, kf[i].x, S[i].x); S[i].y = fmaf(delta, kf[i].y, S[i].y);
+                S[i].z = fmaf(delta, kf[i].z, S[i].z); S[i].w = fmaf(delta, kf[i].w, S[i].w);
+                o = fmaf(S[i].x, qf[i].x, o); o = fmaf(S[i].y, qf[i].y, o);
+                o = fmaf(S[i].z, qf[i].z, o); o = fmaf(S[i].w, qf[i].w, o);
+            }
+            o = sum8(o);
+#pragma unroll
+            for (int i = 0; i < NV; ++i) state_st(Sg + static_cast<size_t>(r) * DK + 32 * i + 4 * sub, S[i]);
+            if (sub == 0) elem<OT>::st(ob + r, o);
+        };
+        pass(0);
+        for (int r0 = 32; r0 < R; r0 += 32) {
+            fetch(S, r0);
+            pass(r0);
+        }
+        __syncthreads();                      // ys is rewritten by the next group
+    }
+}
+
 namespace {
 struct RecArgs {
     const void* y; const float* g; const float* beta; const int32_t* slot; int32_t batch;
@@ -265,6 +418,88 @@ hipError_t pick_dk(const RecArgs& a) {
     }
 }
 }  // namespace
+
+// Workgroups per CU in the fused step's persistent grid.
+#ifndef GDN_STEP_WG_PER_CU
+#define GDN_STEP_WG_PER_CU GDN_DECODE_WG_PER_CU
+#endif
+
+namespace {
+struct StepArgs {
+    const void* x; const float* g; const float* beta; const int32_t* slot; int32_t batch;
+    void* cs; const void* w; const void* bias; float* rec; void* out; const gdn_dims* d;
+    float scale; int32_t flags; const int32_t* err; hipStream_t st;
+};
+
+template <int DK, typename XT, typename CT, typename WT, typename OT>
+hipError_t run_step(const StepArgs& a) {
+    const int G = a.d->num_v_heads / a.d->num_k_heads;
+    const size_t lds = static_cast<size_t>(2 * DK + G * a.d->head_v_dim) * sizeof(float);
+    const int64_t groups = static_cast<int64_t>(a.batch) * a.d->num_k_heads;
+    const int64_t resident = static_cast<int64_t>(cu_count()) * GDN_STEP_WG_PER_CU;
+    const int grid = static_cast<int>(groups < resident ? groups : resident);
+    return launch(decode_step_kernel<DK, XT, CT, WT, OT>, dim3(grid), dim3(256), lds, a.st,
+                  static_cast<const XT*>(a.x), a.g, a.beta, a.slot, static_cast<CT*>(a.cs),
+                  static_cast<const WT*>(a.w), static_cast<const WT*>(a.bias), a.rec,
+                  static_cast<OT*>(a.out), a.d->num_k_heads, a.d->num_v_heads,
+                  a.d->head_v_dim, static_cast<int32_t>(groups), a.scale, a.flags, a.err);
+}
+
+template <int DK, typename XT, typename CT, typename WT>
+hipError_t step_o(gdn_dtype o, const StepArgs& a) {
+    return o == GDN_BF16 ? run_step<DK, XT, CT, WT, bf16_t>(a) : run_step<DK, XT, CT, WT, float>(a);
+}
+template <int DK, typename XT, typename CT>
+hipError_t step_w(gdn_dtype wt, gdn_dtype o, const StepArgs& a) {
+    return wt == GDN_BF16 ? step_o<DK, XT, CT, bf16_t>(o, a) : step_o<DK, XT, CT, float>(o, a);
+}
+template <int DK, typename XT>
+hipError_t step_c(gdn_dtype c, gdn_dtype wt, gdn_dtype o, const StepArgs& a) {
+    return c == GDN_BF16 ? step_w<DK, XT, bf16_t>(wt, o, a) : step_w<DK, XT, float>(wt, o, a);
+}
+template <int DK>
+hipError_t step_x(gdn_dtype xt, gdn_dtype c, gdn_dtype wt, gdn_dtype o, const StepArgs& a) {
+    return xt == GDN_BF16 ? step_c<DK, bf16_t>(c, wt, o, a) : step_c<DK, float>(c, wt, o, a);
+}
+}  // namespace
+
+// The fused step is chosen below this many (row, key head) groups per CU.
+// Measured at H = 16, HV = 32, d = 128 on 256 CUs: batch 16 (1 group per CU)
+// fused 19.0 us vs 20.1 us for the pair; batch 32 even; batch 64 and 256 the
+// pair is ~4-5% faster (its 32-row recurrence items stream the state with
+// more workgroups in flight than the fused kernel's 8-pass groups).
+#ifndef GDN_DECODE_FUSED_MAX_GROUPS_PER_CU
+#define GDN_DECODE_FUSED_MAX_GROUPS_PER_CU 2
+#endif
+
+bool decode_step_fused_fits(const gdn_dims& d) {
+    const int64_t lds = (2LL * d.head_k_dim + static_cast<int64_t>(d.num_v_heads / d.num_k_heads) * d.head_v_dim) *
+                        static_cast<int64_t>(sizeof(float));
+    return lds <= 65536;
+}
+
+bool decode_step_use_fused(const gdn_dims& d, int32_t batch) {
+    return decode_step_fused_fits(d) &&
+           static_cast<int64_t>(batch) * d.num_k_heads < static_cast<int64_t>(GDN_DECODE_FUSED_MAX_GROUPS_PER_CU) * cu_count();
+}
+
+hipError_t launch_decode_step_fused(const void* x, gdn_dtype x_dt, const float* g,
+                                    const float* beta, const int32_t* slot_idx, int32_t batch,
+                                    void* conv_state, gdn_dtype cs_dt, const void* weight,
+                                    const void* bias, gdn_dtype w_dt, float* rec_state, void* out,
+                                    gdn_dtype out_dt, const gdn_dims& dims, float scale,
+                                    int32_t flags, const int32_t* err_flag, hipStream_t stream) {
+    if (batch == 0) return hipSuccess;
+    const StepArgs a{x, g, beta, slot_idx, batch, conv_state, weight, bias, rec_state, out,
+                     &dims, scale, flags, err_flag, stream};
+    switch (dims.head_k_dim) {
+        case 32: return step_x<32>(x_dt, cs_dt, w_dt, out_dt, a);
+        case 64: return step_x<64>(x_dt, cs_dt, w_dt, out_dt, a);
+        case 128: return step_x<128>(x_dt, cs_dt, w_dt, out_dt, a);
+        case 256: return step_x<256>(x_dt, cs_dt, w_dt, out_dt, a);
+        default: return hipErrorInvalidValue;
+    }
+}
 
 hipError_t launch_decode_rec(const void* y, gdn_dtype y_dt, const float* g, const float* beta,
                              const int32_t* slot_idx, int32_t batch, float* rec_state,

@@ -50,6 +50,19 @@ hipError_t launch_decode_rec(const void* y, gdn_dtype y_dt, const float* g, cons
                              void* out, gdn_dtype out_dt, const gdn_dims& dims, float scale,
                              int32_t flags, const int32_t* err_flag, hipStream_t stream);
 
+// Fused decode step (conv + SiLU + norms + recurrence in one kernel, one
+// workgroup per (row, key head) group, activations in LDS).  Chosen for small
+// batches (few groups per CU) when a group's activations fit in LDS; its
+// results equal those of the conv + recurrence pair bitwise.
+bool decode_step_fused_fits(const gdn_dims& d);
+bool decode_step_use_fused(const gdn_dims& d, int32_t batch);
+hipError_t launch_decode_step_fused(const void* x, gdn_dtype x_dt, const float* g,
+                                    const float* beta, const int32_t* slot_idx, int32_t batch,
+                                    void* conv_state, gdn_dtype cs_dt, const void* weight,
+                                    const void* bias, gdn_dtype w_dt, float* rec_state, void* out,
+                                    gdn_dtype out_dt, const gdn_dims& dims, float scale,
+                                    int32_t flags, const int32_t* err_flag, hipStream_t stream);
+
 // Chunked prefill: one workgroup per (sequence, value head).
 bool prefill_supported(const gdn_dims& d, gdn_dtype in_dt);
 hipError_t launch_prefill(const void* q, const void* k, const void* v, gdn_dtype in_dt,

@@ -74,7 +74,9 @@ typedef enum {
 enum {
     GDN_FLAG_SILU = 1,      /* SiLU after the conv (decode step, conv update)    */
     GDN_FLAG_QK_L2NORM = 2, /* q, k <- x / sqrt(sum(x*x) + 1e-6) before use      */
-    GDN_FLAG_VALIDATE = 4   /* device-side index validation, see above           */
+    GDN_FLAG_VALIDATE = 4,  /* device-side index validation, see above           */
+    GDN_FLAG_STEP_FUSED = 8,  /* gdn_decode_step: force the one-kernel path      */
+    GDN_FLAG_STEP_SPLIT = 16  /* gdn_decode_step: force conv kernel + recurrence  */
 };
 
 enum {                      /* bits written to *err_flag under GDN_FLAG_VALIDATE */
@@ -149,9 +151,20 @@ size_t gdn_decode_workspace_size(const gdn_dims* dims, int32_t batch);
  *   out          [batch, HV, dv], out_dt (GDN_F32 or GDN_BF16)
  *   scale        multiplies q after the norm (k is never scaled); usually
  *                dk^-1/2
- *   flags        GDN_FLAG_SILU | GDN_FLAG_QK_L2NORM | GDN_FLAG_VALIDATE
+ *   flags        GDN_FLAG_SILU | GDN_FLAG_QK_L2NORM | GDN_FLAG_VALIDATE, and
+ *                at most one of GDN_FLAG_STEP_FUSED / GDN_FLAG_STEP_SPLIT
  *   workspace    >= gdn_decode_workspace_size(dims, batch) bytes of device
  *                memory, contents irrelevant; not retained after the call
+ *
+ * Two kernel paths compute the step, with bitwise-identical results: a fused
+ * kernel (one workgroup per (row, key head) group: conv of q_h, k_h and the
+ * value heads sharing h into LDS, then their recurrence) and a conv kernel
+ * writing the fp32 activations to the workspace followed by the recurrence
+ * kernel.  By default the fused kernel runs for small batches (fewer than two
+ * (row, key head) groups per compute unit) when (2 dk + (HV / H) dv) * 4 bytes
+ * fit in 64 KiB of LDS; the STEP flags force a path (GDN_ERR_DIMS if the fused
+ * kernel is forced where the group does not fit, GDN_ERR_FLAGS if both are
+ * set).
  */
 gdn_status gdn_decode_step(const void* mixed_qkv, gdn_dtype x_dt,
                            const float* g, const float* beta,

@@ -46,9 +46,14 @@ def to_dev(inp, device="cuda"):
     return out
 
 
+PATH_FLAGS = {None: 0, "fused": gdn.FLAG_STEP_FUSED, "split": gdn.FLAG_STEP_SPLIT}
+
+
 def run_decode_gpu(d, scale, flags=gdn.DEFAULT_DECODE_FLAGS, out_dtype=torch.float32,
-                   err_flag=None):
-    """d: dict of GPU tensors (decode_inputs layout); caches updated in place."""
+                   err_flag=None, path=None):
+    """d: dict of GPU tensors (decode_inputs layout); caches updated in place.
+    path: None (the library's choice), "fused" or "split" (forced kernel path)."""
+    flags |= PATH_FLAGS[path]
     dims = gdn.make_dims(d["dims"]["H"], d["dims"]["HV"], d["dims"]["dk"], d["dims"]["dv"],
                          d["dims"]["W"])
     B = d["mixed_qkv"].shape[0]

@@ -74,6 +74,8 @@ def _decode(lib, dims=None, batch=4, flags=3, x=FAKE, rec=FAKE, ws=FAKE, ws_byte
     (dict(out_dt=2), ERR_DTYPE),
     (dict(flags=64), ERR_FLAGS),
     (dict(flags=7, err=None), ERR_FLAGS),          # VALIDATE without err_flag
+    (dict(flags=3 | 8 | 16), ERR_FLAGS),           # both decode-step paths forced
+    (dict(flags=3 | 8, dims=_dims(H=1, HV=128, dv=256)), ERR_DIMS),   # fused group > 64 KiB LDS
     (dict(x=None), ERR_NULL),
     (dict(ws=None), ERR_NULL),
     (dict(rec=MISALIGNED), ERR_ALIGN),

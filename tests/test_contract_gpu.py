@@ -33,13 +33,14 @@ def _clone(d):
     return {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
 
 
-def test_null_slots_untouched():
+@pytest.mark.parametrize("path", ["fused", "split"])
+def test_null_slots_untouched(path):
     d = to_dev(gi.decode_inputs(16, 64, seed=9))
     d["slot_idx"][3] = 0
     d["slot_idx"][7] = -5
     d["slot_idx"][11] = 0
     before_rs, before_cs = d["rec_state"].clone(), d["conv_state"].clone()
-    out = run_decode_gpu(d, SCALE)
+    out = run_decode_gpu(d, SCALE, path=path)
     torch.cuda.synchronize()
     for r in (3, 7, 11):
         assert torch.all(out[r] == 0)
@@ -51,9 +52,10 @@ def test_null_slots_untouched():
     assert torch.equal(before_rs[0], d["rec_state"][0])
 
 
+@pytest.mark.parametrize("path", ["fused", "split"])
 @pytest.mark.parametrize("bad,bit", [("range", gdn.EFLAG_SLOT_RANGE),
                                      ("repeat", gdn.EFLAG_SLOT_REPEAT)])
-def test_validation_fails_closed(bad, bit):
+def test_validation_fails_closed(bad, bit, path):
     # 33 slots of memory, 32 exposed: slot 32 is out of range for the call but
     # still allocated, so a missed check could not fault
     d = gi.decode_inputs(9, 32, seed=10)
@@ -70,7 +72,7 @@ def test_validation_fails_closed(bad, bit):
     before = {k: v.clone() for k, v in full.items()}
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     out = run_decode_gpu(d, SCALE, flags=gdn.DEFAULT_DECODE_FLAGS | gdn.FLAG_VALIDATE,
-                         err_flag=err)
+                         err_flag=err, path=path)
     torch.cuda.synchronize()
     assert int(err.item()) & bit
     assert torch.isnan(out).all(), "a rejected call must not write the output"

@@ -42,47 +42,51 @@ def _untouched(before, after, used):
     return torch.equal(before[mask], after.cpu()[mask])
 
 
+@pytest.mark.parametrize("path", ["fused", "split"])
 @pytest.mark.parametrize("act_dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("bias", [False, True])
-def test_decode_tiny(act_dtype, bias):
+def test_decode_tiny(act_dtype, bias, path):
     d = gi.decode_inputs(6, 8, H=2, HV=4, dk=32, dv=32, act_dtype=act_dtype, seed=0,
                          g_mode="softplus", conv_bias=bias)
     d["slot_idx"][2] = 0           # a padded row
     d["slot_idx"][4] = -1
     g = to_dev(d)
-    out = run_decode_gpu(g, 1 / math.sqrt(32))
+    out = run_decode_gpu(g, 1 / math.sqrt(32), path=path)
     torch.cuda.synchronize()
     _check_rows(d, g, out, list(range(6)), 1 / math.sqrt(32))
     assert _untouched(d["rec_state"], g["rec_state"], d["slot_idx"].tolist())
     assert _untouched(d["conv_state"], g["conv_state"], d["slot_idx"].tolist())
 
 
+@pytest.mark.parametrize("path", [None, "split"])
 @pytest.mark.parametrize("B", [1, 2, 4, 8, 16])
-def test_decode_qwen_buckets(B):
+def test_decode_qwen_buckets(B, path):
     d = gi.decode_inputs(B, 256, seed=1)
     g = to_dev(d)
-    out = run_decode_gpu(g, 128 ** -0.5)
+    out = run_decode_gpu(g, 128 ** -0.5, path=path)
     torch.cuda.synchronize()
     _check_rows(d, g, out, list(range(B)), 128 ** -0.5)
     assert _untouched(d["rec_state"], g["rec_state"], d["slot_idx"].tolist())
     assert _untouched(d["conv_state"], g["conv_state"], d["slot_idx"].tolist())
 
 
+@pytest.mark.parametrize("path", ["fused", "split"])
 @pytest.mark.parametrize("dk,dv", [(64, 64), (128, 96), (256, 128), (32, 128)])
-def test_decode_other_head_dims(dk, dv):
+def test_decode_other_head_dims(dk, dv, path):
     d = gi.decode_inputs(5, 9, H=2, HV=4, dk=dk, dv=dv, seed=7)
     d["slot_idx"][1] = 0
     g = to_dev(d)
-    out = run_decode_gpu(g, dk ** -0.5)
+    out = run_decode_gpu(g, dk ** -0.5, path=path)
     torch.cuda.synchronize()
     _check_rows(d, g, out, list(range(5)), dk ** -0.5)
 
 
+@pytest.mark.parametrize("path", ["fused", "split"])
 @pytest.mark.parametrize("flags", [0, gdn.FLAG_SILU, gdn.FLAG_QK_L2NORM])
-def test_decode_flag_variants(flags):
+def test_decode_flag_variants(flags, path):
     d = gi.decode_inputs(4, 16, seed=5)
     g = to_dev(d)
-    out = run_decode_gpu(g, 128 ** -0.5, flags=flags)
+    out = run_decode_gpu(g, 128 ** -0.5, flags=flags, path=path)
     torch.cuda.synchronize()
     _check_rows(d, g, out, list(range(4)), 128 ** -0.5, flags=flags)
 
@@ -103,12 +107,13 @@ def large_cache():
     return d
 
 
+@pytest.mark.parametrize("path", [None, "fused"])
 @pytest.mark.parametrize("B", [256, 1024])
-def test_decode_large_batch_sampled(large_cache, B):
+def test_decode_large_batch_sampled(large_cache, B, path):
     d = {k: (v[:B] if k in ("mixed_qkv", "g", "beta", "slot_idx") else v)
          for k, v in large_cache.items()}
     g = to_dev(d)
-    out = run_decode_gpu(g, 128 ** -0.5)
+    out = run_decode_gpu(g, 128 ** -0.5, path=path)
     torch.cuda.synchronize()
     rng = np.random.default_rng(B)
     rows = sorted(rng.choice(B, 48, replace=False).tolist())
@@ -128,3 +133,40 @@ def test_decode_empty_batch():
     torch.cuda.synchronize()
     assert out.shape[0] == 0
     assert int(err.item()) == 0
+
+
+# The fused step and the conv + recurrence pair must agree bitwise on outputs,
+# recurrent state and conv cache, for every dtype mix, head shape and flag set.
+_PATH_CASES = [
+    # (H, HV, dk, dv, x dtype, conv cache dtype, weight dtype, out dtype, bias, flags)
+    (2, 4, 32, 32, "f32", "f32", "f32", "f32", True, gdn.DEFAULT_DECODE_FLAGS),
+    (16, 32, 128, 128, "bf16", "bf16", "bf16", "f32", False, gdn.DEFAULT_DECODE_FLAGS),
+    (16, 32, 128, 128, "bf16", "bf16", "bf16", "bf16", True, gdn.DEFAULT_DECODE_FLAGS),
+    (4, 16, 64, 96, "f32", "bf16", "f32", "f32", True, gdn.DEFAULT_DECODE_FLAGS),
+    (2, 2, 256, 128, "bf16", "f32", "bf16", "bf16", False, gdn.DEFAULT_DECODE_FLAGS),
+    (1, 8, 128, 32, "bf16", "bf16", "f32", "f32", True, gdn.FLAG_SILU),
+    (3, 6, 32, 256, "f32", "f32", "bf16", "f32", False, 0),
+    (2, 4, 64, 64, "bf16", "bf16", "bf16", "f32", True, gdn.FLAG_QK_L2NORM),
+]
+_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+@pytest.mark.parametrize("case", _PATH_CASES, ids=lambda c: "-".join(map(str, c[:8])))
+def test_fused_equals_split_bitwise(case):
+    H, HV, dk, dv, xd, cd, wd, od, bias, flags = case
+    d = gi.decode_inputs(11, 24, H=H, HV=HV, dk=dk, dv=dv, seed=40 + dk + dv, conv_bias=bias)
+    d["mixed_qkv"] = d["mixed_qkv"].to(_DT[xd])
+    d["conv_state"] = d["conv_state"].to(_DT[cd])
+    d["conv_weight"] = d["conv_weight"].to(_DT[wd])
+    if bias:
+        d["conv_bias"] = d["conv_bias"].to(_DT[wd])
+    d["slot_idx"][3] = 0
+    d["slot_idx"][8] = -2
+    a, b = to_dev(d), to_dev(d)
+    oa = run_decode_gpu(a, dk ** -0.5, flags=flags, out_dtype=_DT[od], path="fused")
+    ob = run_decode_gpu(b, dk ** -0.5, flags=flags, out_dtype=_DT[od], path="split")
+    torch.cuda.synchronize()
+    assert torch.equal(oa, ob)
+    assert torch.equal(a["rec_state"], b["rec_state"])
+    assert torch.equal(a["conv_state"], b["conv_state"])
+    assert not torch.isnan(oa).any()
