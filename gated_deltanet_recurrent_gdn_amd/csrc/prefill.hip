@@ -90,6 +90,13 @@ __device__ __forceinline__ void buf_st8(rsrc_t r, uint32_t off, uint32_t a, uint
     __builtin_amdgcn_raw_buffer_store_b64(u32x2{a, b}, r, off, 0, 0);
 }
 
+// One step of an inclusive wave prefix sum: the DPP-moved value, or zero in
+// lanes whose source lies outside the row or whose row is masked off.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_scan_step(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xF, false));
+}
+
 // Broadcast lane j of each 16-lane row to the whole row (DPP row_newbcast,
 // controls 0x150 + j on CDNA); j must fold to a constant.
 __device__ __forceinline__ float row_bcast(float x, int j) {
@@ -154,11 +161,12 @@ struct PrefillSmem {
     bf16_t q[NP][CH * SK];                      // Q   [t][k]
     bf16_t kt[NP][D * ST];                      // K^T [k][t]
     bf16_t vt_w[NP][VW];                        // V^T [v][t]; later -W [t][k] in plane 0
-    float g[CH * SF];                           // A, then T in place (lower, unit diag, zero upper)
-    union {
+    float g[CH * SF];                           // A, then T in place (lower, unit diag, zero upper),
+                                                // except T's block [32:64][0:32], which is in xs
+    struct {
         bf16_t c[4 * CH * ST];                  // cW hi, cW lo, cU hi, cU lo   [t][t']
-        float x[32 * 36];                       // merge scratch X
     } pc;
+    float xs[32 * 36];                          // merge scratch X; finally T[32:64][0:32]
     bf16_t mp[2 * CH * ST];                     // (M o P) hi, lo   [t][t']
     float gam[CH], beta[CH], rk[CH], rq[CH], eg[CH], ck[CH], cwc[CH];
     float egl;
@@ -309,13 +317,14 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
             }
         }
         if (tid < CH) sm.beta[tid] = pbeta;
-        if (wave == 0) {                         // cumulative log-decay: fixed-order wave scan
+        if (wave == 0) {                         // cumulative log-decay: fixed-order DPP wave scan
             float gt = pg;
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const float y = __shfl_up(gt, d, 64);
-                if (lane >= d) gt += y;
-            }
+            gt += dpp_scan_step<0x111, 0xF>(gt);     // row_shr:1 .. row_shr:8 inside each 16-lane row
+            gt += dpp_scan_step<0x112, 0xF>(gt);
+            gt += dpp_scan_step<0x114, 0xF>(gt);
+            gt += dpp_scan_step<0x118, 0xF>(gt);
+            gt += dpp_scan_step<0x142, 0xA>(gt);     // row_bcast:15 -> rows 1, 3
+            gt += dpp_scan_step<0x143, 0xC>(gt);     // row_bcast:31 -> rows 2, 3
             sm.gam[lane] = gt;
         }
         __syncthreads();
@@ -427,56 +436,83 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
             for (int r = 0; r < 16; ++r) blk[r * SF + c] = tc[r];
         }
         __syncthreads();
-        // merge 16 -> 32 for block pairs p = (0,1), (2,3) on fp32 MFMA (waves 0, 1):
-        // X = A21 T11 into the scratch area, then T21 = -T22 X
+        // merge 16 -> 32 for block pairs p = (0,1), (2,3) on fp32 MFMA (wave p):
+        // X = A21 T11 goes through the LDS scratch and straight back into the same
+        // wave (LDS is in order within a wave; the fence keeps the compiler from
+        // reordering), then T21 = -T22 X.  Operands are loaded before the MFMAs.
         if (wave < 2) {
             const int b0 = 32 * wave, b1 = b0 + 16;
+            float a[4], bb[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                a[kk] = sm.g[(b1 + l16) * SF + b0 + 4 * kk + q4];
+                bb[kk] = sm.g[(b0 + 4 * kk + q4) * SF + b0 + l16];
+            }
             f32x4 x = f32x4{0, 0, 0, 0};
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                x = mfma4(sm.g[(b1 + l16) * SF + b0 + 4 * kk + q4],
-                          sm.g[(b0 + 4 * kk + q4) * SF + b0 + l16], x);
+            for (int kk = 0; kk < 4; ++kk) x = mfma4(a[kk], bb[kk], x);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sm.pc.x[(16 * wave + 4 * q4 + r) * 36 + l16] = x[r];
-        }
-        __syncthreads();
-        if (wave < 2) {
-            const int b0 = 32 * wave, b1 = b0 + 16;
+            for (int r = 0; r < 4; ++r) sm.xs[(16 * wave + 4 * q4 + r) * 36 + l16] = x[r];
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                a[kk] = sm.g[(b1 + l16) * SF + b1 + 4 * kk + q4];
+                bb[kk] = sm.xs[(16 * wave + 4 * kk + q4) * 36 + l16];
+            }
             f32x4 t = f32x4{0, 0, 0, 0};
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                t = mfma4(sm.g[(b1 + l16) * SF + b1 + 4 * kk + q4],
-                          sm.pc.x[(16 * wave + 4 * kk + q4) * 36 + l16], t);
+            for (int kk = 0; kk < 4; ++kk) t = mfma4(a[kk], bb[kk], t);
 #pragma unroll
             for (int r = 0; r < 4; ++r) sm.g[(b1 + 4 * q4 + r) * SF + b0 + l16] = -t[r];
         }
         __syncthreads();
-        // merge 32 -> 64 (waves 0..3: 16x16 output tile (ti, tj)): X = A[32:64][0:32] T11,
-        // T21 = -T22 X.  T11's block (0, 1) and T22's block (0, 1) are zero: skipped.
-        if (wave < 4) {
-            const int ti = wave >> 1, tj = wave & 1;
-            f32x4 x = f32x4{0, 0, 0, 0};
+        // merge 32 -> 64 (wave tj < 2: output column block tj of the lower-left
+        // 32x32 block, both row blocks ti): X[:, tj] = A[32:64][0:32] T11[:, tj],
+        // then T21[:, tj] = -T22 X[:, tj], the same wave-local LDS round trip;
+        // T21 is left in xs.  T11's block (0, 1) and T22's block (0, 1) are zero:
+        // skipped.
+        if (wave < 2) {
+            const int tj = wave;
+            const int k0 = 4 * tj;                 // T11[:, tj] is zero above row 16 tj
+            float a[2][8], bb[8];
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) {
-                if (tj == 1 && kk < 4) continue;
-                x = mfma4(sm.g[(32 + 16 * ti + l16) * SF + 4 * kk + q4],
-                          sm.g[(4 * kk + q4) * SF + 16 * tj + l16], x);
-            }
+                if (kk < k0) continue;
+                bb[kk] = sm.g[(4 * kk + q4) * SF + 16 * tj + l16];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sm.pc.x[(16 * ti + 4 * q4 + r) * 36 + 16 * tj + l16] = x[r];
-        }
-        __syncthreads();
-        if (wave < 4) {
-            const int ti = wave >> 1, tj = wave & 1;
-            f32x4 t = f32x4{0, 0, 0, 0};
+                for (int ti = 0; ti < 2; ++ti) a[ti][kk] = sm.g[(32 + 16 * ti + l16) * SF + 4 * kk + q4];
+            }
+            f32x4 x[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) {
-                if (ti == 0 && kk >= 4) continue;
-                t = mfma4(sm.g[(32 + 16 * ti + l16) * SF + 32 + 4 * kk + q4],
-                          sm.pc.x[(4 * kk + q4) * 36 + 16 * tj + l16], t);
+                if (kk < k0) continue;
+#pragma unroll
+                for (int ti = 0; ti < 2; ++ti) x[ti] = mfma4(a[ti][kk], bb[kk], x[ti]);
             }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sm.g[(32 + 16 * ti + 4 * q4 + r) * SF + 16 * tj + l16] = -t[r];
+            for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sm.xs[(16 * ti + 4 * q4 + r) * 36 + 16 * tj + l16] = x[ti][r];
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+                bb[kk] = sm.xs[(4 * kk + q4) * 36 + 16 * tj + l16];
+#pragma unroll
+                for (int ti = 0; ti < 2; ++ti) a[ti][kk] = sm.g[(32 + 16 * ti + l16) * SF + 32 + 4 * kk + q4];
+            }
+            f32x4 t[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+                t[1] = mfma4(a[1][kk], bb[kk], t[1]);
+                if (kk < 4) t[0] = mfma4(a[0][kk], bb[kk], t[0]);   // T22 row block 0 is zero past col 16
+            }
+            // T21[:, tj] replaces this wave's own column of X (its reads of X are
+            // done); sm.g's block [32:64][0:32] still holds A21, which the other
+            // wave may be reading
+#pragma unroll
+            for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sm.xs[(16 * ti + 4 * q4 + r) * 36 + 16 * tj + l16] = -t[ti][r];
         }
         __syncthreads();
 
@@ -485,9 +521,10 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
         {
             const int r = tid >> 3, cb = 8 * (tid & 7);
             uint32_t wh[4], wl[4], uh[4], ul[4];
+            const float* trow = (r >= 32 && cb < 32) ? &sm.xs[(r - 32) * 36 + cb] : &sm.g[r * SF + cb];
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                const float4 t = *reinterpret_cast<const float4*>(&sm.g[r * SF + cb + 4 * j]);
+                const float4 t = *reinterpret_cast<const float4*>(trow + 4 * j);
                 const float4 cw = *reinterpret_cast<const float4*>(&sm.cwc[cb + 4 * j]);
                 const float4 bt = *reinterpret_cast<const float4*>(&sm.beta[cb + 4 * j]);
                 const f32x4 w = {t.x * cw.x, t.y * cw.y, t.z * cw.z, t.w * cw.w};
