@@ -51,7 +51,9 @@ def load(path: str = None):
                                        i32, i32, i32, i32, i32, f64, i32]
     lib.oracle_prefill.argtypes = [P, P, P, P, P, P, i32, i64, P, P, i32, P,
                                    i32, i32, i32, i32, f64, i32]
-    for f in (lib.oracle_conv_update, lib.oracle_decode_step, lib.oracle_prefill):
+    lib.oracle_gating.argtypes = [P, P, P, P, i64, i32, P, P]
+    for f in (lib.oracle_conv_update, lib.oracle_decode_step, lib.oracle_prefill,
+              lib.oracle_gating):
         f.restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -143,3 +145,19 @@ def prefill(q, k, v, g, beta, cu_seqlens, slot_idx, rec_state, scale,
     if rc:
         raise OracleError(rc)
     return out
+
+
+def gating(a, b, A_log, dt_bias, lib=None):
+    """Fused gating in fp64: returns (g, beta), each shaped like ``a`` [rows, HV]."""
+    lib = lib or load()
+    a, b, A_log, dt_bias = (_f64(x) for x in (a, b, A_log, dt_bias))
+    rows, HV = a.shape
+    if b.shape != a.shape or A_log.shape != (HV,) or dt_bias.shape != (HV,):
+        raise ValueError("gating shapes: a, b [rows, HV]; A_log, dt_bias [HV]")
+    g = np.full(a.shape, np.nan)
+    beta = np.full(a.shape, np.nan)
+    rc = lib.oracle_gating(_ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias), rows, HV,
+                           _ptr(g), _ptr(beta))
+    if rc:
+        raise OracleError(rc)
+    return g, beta

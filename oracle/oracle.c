@@ -241,3 +241,27 @@ int oracle_prefill(const double* qin, const double* kin, const double* vin,
     free(q); free(k);
     return 0;
 }
+
+/* [P1] "How the golden relates to the kernel", item 1: fused fp32 gating with
+ * the softplus threshold at 20.  Here in fp64; log1p keeps log(1 + e^x)
+ * accurate where e^x is small. */
+static double softplus_thresholded(double x)
+{
+    return (x <= 20.0) ? log1p(exp(x)) : x;
+}
+
+int oracle_gating(const double* a, const double* b, const double* A_log,
+                  const double* dt_bias, int64_t rows, int32_t num_v_heads,
+                  double* g, double* beta)
+{
+    if (rows < 0 || num_v_heads <= 0) return ORACLE_ERR_ARGS;
+    if (rows > 0 && (!a || !b || !A_log || !dt_bias || !g || !beta)) return ORACLE_ERR_ARGS;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int32_t h = 0; h < num_v_heads; ++h) {
+            const int64_t i = r * num_v_heads + h;
+            g[i] = -exp(A_log[h]) * softplus_thresholded(a[i] + dt_bias[h]);
+            beta[i] = 1.0 / (1.0 + exp(-b[i]));
+        }
+    }
+    return 0;
+}

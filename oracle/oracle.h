@@ -102,6 +102,21 @@ int oracle_prefill(const double* q, const double* k, const double* v,
                    int32_t head_k_dim, int32_t head_v_dim,
                    double scale, int32_t flags);
 
+/*
+ * Fused gating ([P1] "How the golden relates to the kernel", item 1): for
+ * each row r and value head h,
+ *   x = a[r, h] + dt_bias[h]
+ *   softplus(x) = log(1 + exp(x)) for x <= 20, and x itself above 20 (the
+ *                 kernel's threshold branch)
+ *   g[r, h]    = -exp(A_log[h]) * softplus(x)
+ *   beta[r, h] = 1 / (1 + exp(-b[r, h]))           (sigmoid)
+ *
+ *   a, b       [rows, HV]; A_log, dt_bias [HV]; g, beta [rows, HV] (outputs)
+ */
+int oracle_gating(const double* a, const double* b, const double* A_log,
+                  const double* dt_bias, int64_t rows, int32_t num_v_heads,
+                  double* g, double* beta);
+
 #ifdef __cplusplus
 }
 #endif

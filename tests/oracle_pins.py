@@ -290,9 +290,45 @@ def pin_slot_contract(lib):
             raise AssertionError(f"bad cu_seqlens {cu} accepted")
 
 
+# --- G6: fused gating ([P1] "How the golden relates to the kernel", item 1) --
+def pin_gating(lib):
+    """beta against scipy's expit; softplus against numpy's logaddexp(0, x)
+    below the threshold and the identity above it; g's closed forms at
+    a + dt_bias = 0 (-exp(A_log) ln 2); per-head A_log / dt_bias indexing;
+    dt_bias enters additively (shifting a by c and dt_bias by -c changes
+    nothing)."""
+    rng = np.random.default_rng(41)
+    rows, HV = 7, 5
+    a = rng.standard_normal((rows, HV)) * 4.0
+    a[0, :] = [-30.0, -1.0, 19.5, 20.5, 40.0]
+    b = rng.standard_normal((rows, HV)) * 3.0
+    b[1, :] = [0.0, -50.0, 50.0, 1.0, -1.0]
+    A_log = rng.standard_normal(HV)
+    dt_bias = np.array([0.0, 0.5, 0.5, 0.5, -0.25])
+    a[0, :] -= dt_bias                       # row 0 probes x = a + dt_bias exactly
+    g, beta = oracle.gating(a, b, A_log, dt_bias, lib=lib)
+    assert np.allclose(beta, expit(b), rtol=1e-15, atol=0), "beta must be sigmoid(b)"
+    x = a + dt_bias[None, :]
+    sp = np.where(x <= 20.0, np.logaddexp(0.0, x), x)
+    assert np.allclose(g, -np.exp(A_log)[None, :] * sp, rtol=1e-14, atol=0)
+    # threshold branch: identity above 20 (exactly), log1p(exp) at and below
+    assert g[0, 3] == -math.exp(A_log[3]) * x[0, 3]
+    assert g[0, 4] == -math.exp(A_log[4]) * x[0, 4]
+    assert abs(g[0, 2] / -math.exp(A_log[2]) - (19.5 + math.log1p(math.exp(-19.5)))) < 1e-13
+    # closed form at x = 0 and A_log = log 3
+    g0, _ = oracle.gating(np.zeros((1, 2)), np.zeros((1, 2)), np.array([0.0, math.log(3.0)]),
+                          np.zeros(2), lib=lib)
+    assert abs(g0[0, 0] + math.log(2.0)) < 1e-15 and abs(g0[0, 1] + 3 * math.log(2.0)) < 1e-14
+    # additive dt_bias
+    g1, _ = oracle.gating(a + 0.75, b, A_log, dt_bias - 0.75, lib=lib)
+    assert np.allclose(g1, g, rtol=1e-13, atol=0)
+    assert np.all(g <= 0.0) and np.all((beta >= 0.0) & (beta <= 1.0))
+
+
 ALL_PINS = [pin_identity_step, pin_delta_rule_unit_key, pin_decay, pin_overwrite,
             pin_brute_force_matrix_form, pin_qk_norm, pin_gqa_map, pin_conv_sliding_window,
-            pin_silu, pin_decode_split, pin_chunked_equals_token, pin_slot_contract]
+            pin_silu, pin_decode_split, pin_chunked_equals_token, pin_slot_contract,
+            pin_gating]
 
 
 def run_all(lib):

@@ -84,6 +84,19 @@ MUTANTS = [
      "for (int64_t t = start; t < end; ++t) {\n                prepare_qk",
      "for (int64_t t = start; t < end; ++t) {\n                if (t > start) memset(S, 0, sizeof(double) * (size_t)dv * dk);\n                prepare_qk",
      ["pin_brute_force_matrix_form", "pin_chunked_equals_token"]),
+    ("gating_no_threshold", "return (x <= 20.0) ? log1p(exp(x)) : x;",
+     "return log(exp(x));", ["pin_gating"]),
+    ("gating_threshold_branch_swapped", "return (x <= 20.0) ? log1p(exp(x)) : x;",
+     "return (x > 20.0) ? log1p(exp(x)) : x;", ["pin_gating"]),
+    ("gating_dt_bias_dropped", "softplus_thresholded(a[i] + dt_bias[h])",
+     "softplus_thresholded(a[i])", ["pin_gating"]),
+    ("gating_A_log_not_exponentiated", "g[i] = -exp(A_log[h]) *",
+     "g[i] = -A_log[h] *", ["pin_gating"]),
+    ("gating_head_index_by_row", "g[i] = -exp(A_log[h]) * softplus_thresholded(a[i] + dt_bias[h]);",
+     "g[i] = -exp(A_log[r % num_v_heads]) * softplus_thresholded(a[i] + dt_bias[r % num_v_heads]);",
+     ["pin_gating"]),
+    ("gating_beta_sign", "beta[i] = 1.0 / (1.0 + exp(-b[i]));",
+     "beta[i] = 1.0 / (1.0 + exp(b[i]));", ["pin_gating"]),
 ]
 
 
