@@ -132,6 +132,14 @@ class DecodeSetup:
         self.y = torch.empty(batch, D, device=dev)          # post-conv activations
         self.scale = DK ** -0.5
         self.i = 0
+        self.gate = None
+
+    def use_gating(self, seed):
+        """Switch the step to the fused-gating call (raw a, b projections in bf16)."""
+        import gdn_inputs as gi
+        gt = gi.gating_inputs(self.batch, HV, seed=seed)
+        gt = {k: v.to(self.out.device) for k, v in gt.items()}
+        self.gate = self.gdn.GateInputs(gt["a"], gt["b"], gt["A_log"], gt["dt_bias"])
 
     def step(self, validate=False):
         gdn = self.gdn
@@ -139,6 +147,12 @@ class DecodeSetup:
         slots = self.slot_sets[self.i % len(self.slot_sets)]
         self.i += 1
         flags = gdn.DEFAULT_DECODE_FLAGS | (gdn.FLAG_VALIDATE if validate else 0)
+        if self.gate is not None:
+            gdn.gdn_decode_step_gated(d["mixed_qkv"], self.gate, slots, d["conv_state"],
+                                      d["conv_weight"], d["rec_state"], self.out, self.dims,
+                                      self.scale, flags=flags, workspace=self.ws,
+                                      err_flag=self.err if validate else None)
+            return
         gdn.gdn_decode_step(d["mixed_qkv"], d["g"], d["beta"], slots, d["conv_state"],
                             d["conv_weight"], d["rec_state"], self.out, self.dims, self.scale,
                             flags=flags, workspace=self.ws,
@@ -193,11 +207,24 @@ class PrefillSetup:
         self.dims = gdn.make_dims(H, HV, DK, DV, W)
         self.out = torch.empty(self.T, HV, DV, dtype=torch.bfloat16, device=dev)
         self.err = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.gate = None
+
+    def use_gating(self, seed):
+        import gdn_inputs as gi
+        gt = gi.gating_inputs(self.T, HV, seed=seed)
+        gt = {k: v.to(self.out.device) for k, v in gt.items()}
+        self.gate = self.gdn.GateInputs(gt["a"], gt["b"], gt["A_log"], gt["dt_bias"])
 
     def step(self, validate=False):
         gdn = self.gdn
         p = self.p
         flags = gdn.FLAG_QK_L2NORM | (gdn.FLAG_VALIDATE if validate else 0)
+        if self.gate is not None:
+            gdn.gdn_prefill_chunked_gated(p["q"], p["k"], p["v"], self.gate, p["cu_seqlens"],
+                                          p["slot_idx"], p["rec_state"], self.out, self.dims,
+                                          DK ** -0.5, flags=flags,
+                                          err_flag=self.err if validate else None)
+            return
         gdn.gdn_prefill_chunked(p["q"], p["k"], p["v"], p["g"], p["beta"], p["cu_seqlens"],
                                 p["slot_idx"], p["rec_state"], self.out, self.dims, DK ** -0.5,
                                 flags=flags, err_flag=self.err if validate else None)
@@ -322,11 +349,24 @@ def main():
     big.prepare_rec()
     ms_rec = time_loop(torch, big.rec_step, args.steps, args.warmup)
     torch.cuda.synchronize()
+    # the same batch-256 step and prefill with the gating fused in (raw a, b)
+    big.use_gating(seed=7)
+    pre.use_gating(seed=8)
+    if args.eager:
+        ms_big_g = time_loop(torch, lambda: big.step(args.validate), args.steps, args.warmup)
+    else:
+        g_big_g, r_big_g = big.capture(args.validate)
+        ms_big_g = time_graph(torch, g_big_g, r_big_g, args.steps, args.warmup)
+    ms_pre_g = time_loop(torch, lambda: pre.step(args.validate), max(3, args.steps // 4),
+                         max(1, args.warmup // 4))
+    torch.cuda.synchronize()
 
     mean = lambda xs: sum(xs) / len(xs)  # noqa: E731
     med = lambda xs: sorted(xs)[len(xs) // 2]  # noqa: E731
     step_bytes_big = 256 * decode_bytes_per_seq() + conv_weight_bytes()
     step_bytes_small = 16 * decode_bytes_per_seq() + conv_weight_bytes()
+    # gated step: bf16 a, b (4 B per head) replace fp32 g, beta (8 B), plus A_log, dt_bias
+    step_bytes_big_gated = step_bytes_big - 256 * HV * 4 + 2 * HV * 4
     gbs_big = step_bytes_big / (mean(ms_big) * 1e-3) / 1e9
     gbs_small = step_bytes_small / (mean(ms_small) * 1e-3) / 1e9
     rec_ms = mean(ms_rec)
@@ -356,6 +396,11 @@ def main():
         "prefill_pct_mfma_peak": round(100 * pre_tflops / BF16_PEAK_TFLOPS, 2),
         "prefill_algorithmic_flops": pre_flops, "prefill_algorithmic_bytes": pre_bytes,
         "prefill_pct_hbm_peak": round(100 * pre_bytes / (pre_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+        "decode_b256_gated_ms_mean": round(mean(ms_big_g), 5),
+        "decode_b256_gated_GBps": round(step_bytes_big_gated / (mean(ms_big_g) * 1e-3) / 1e9, 2),
+        "prefill_gated_ms_mean": round(mean(ms_pre_g), 4),
+        "gated_note": ("the same steps through gdn_decode_step_gated / gdn_prefill_chunked_gated: "
+                       "g and beta computed in-kernel from bf16 a, b and fp32 A_log, dt_bias"),
         "validate": bool(args.validate),
     }
 

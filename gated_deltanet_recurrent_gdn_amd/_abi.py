@@ -26,8 +26,9 @@ _STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_DIMS", 3: "GDN_ERR_DTYPE"
            4: "GDN_ERR_ALIGN", 5: "GDN_ERR_WORKSPACE", 6: "GDN_ERR_LAUNCH", 7: "GDN_ERR_FLAGS"}
 
 EXPORTED = ["gdn_conv_update", "gdn_decode_workspace_size", "gdn_decode_step",
-            "gdn_decode_recurrent",
-            "gdn_prefill_workspace_size", "gdn_prefill_chunked", "gdn_strerror"]
+            "gdn_decode_step_gated", "gdn_decode_recurrent",
+            "gdn_prefill_workspace_size", "gdn_prefill_chunked", "gdn_prefill_chunked_gated",
+            "gdn_strerror"]
 
 
 class GDNError(RuntimeError):
@@ -40,6 +41,19 @@ class gdn_dims(ctypes.Structure):
     _fields_ = [("num_k_heads", ctypes.c_int32), ("num_v_heads", ctypes.c_int32),
                 ("head_k_dim", ctypes.c_int32), ("head_v_dim", ctypes.c_int32),
                 ("conv_width", ctypes.c_int32)]
+
+
+class gdn_gate_inputs(ctypes.Structure):
+    _fields_ = [("a", ctypes.c_void_p), ("b", ctypes.c_void_p), ("ab_dt", ctypes.c_int32),
+                ("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p)]
+
+
+class GateInputs:
+    """Raw gating inputs for the *_gated calls: a, b [rows, HV] (bf16 or fp32,
+    the layout of the g / beta they replace), A_log and dt_bias [HV] fp32."""
+
+    def __init__(self, a, b, A_log, dt_bias):
+        self.a, self.b, self.A_log, self.dt_bias = a, b, A_log, dt_bias
 
 
 _lib = None
@@ -69,10 +83,15 @@ def load_library(path: str = None):
     lib.gdn_prefill_workspace_size.restype = sz
     lib.gdn_prefill_chunked.argtypes = [P, P, P, i32, P, P, P, i32, i32, P, P, i32, P, i32,
                                         D, f32, i32, P, sz, P, P]
+    G = ctypes.POINTER(gdn_gate_inputs)
+    lib.gdn_decode_step_gated.argtypes = [P, i32, G, P, i32, P, i32, P, P, i32, P, i32, P, i32,
+                                          D, f32, i32, P, sz, P, P]
+    lib.gdn_prefill_chunked_gated.argtypes = [P, P, P, i32, G, P, i32, i32, P, P, i32, P, i32,
+                                              D, f32, i32, P, sz, P, P]
     lib.gdn_strerror.argtypes = [i32]
     lib.gdn_strerror.restype = ctypes.c_char_p
     for f in (lib.gdn_conv_update, lib.gdn_decode_step, lib.gdn_decode_recurrent,
-              lib.gdn_prefill_chunked):
+              lib.gdn_prefill_chunked, lib.gdn_decode_step_gated, lib.gdn_prefill_chunked_gated):
         f.restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -127,6 +146,14 @@ def _check(fn, status):
         raise GDNError(fn, status)
 
 
+def _gate_struct(gate: GateInputs, rows: int, HV: int) -> gdn_gate_inputs:
+    _dev(gate.a, "a", shape=(rows, HV)); _dev(gate.b, "b", gate.a.dtype, (rows, HV))
+    _dev(gate.A_log, "A_log", torch.float32, (HV,))
+    _dev(gate.dt_bias, "dt_bias", torch.float32, (HV,))
+    return gdn_gate_inputs(gate.a.data_ptr(), gate.b.data_ptr(), _dt(gate.a),
+                           gate.A_log.data_ptr(), gate.dt_bias.data_ptr())
+
+
 # --------------------------------------------------------------------------
 # entry points
 # --------------------------------------------------------------------------
@@ -155,17 +182,15 @@ def gdn_decode_workspace_size(dims: gdn_dims, batch: int) -> int:
     return int(load_library().gdn_decode_workspace_size(ctypes.byref(dims), int(batch)))
 
 
-def gdn_decode_step(mixed_qkv, g, beta, slot_idx, conv_state, conv_weight, rec_state, out,
-                    dims: gdn_dims, scale, conv_bias=None, flags=DEFAULT_DECODE_FLAGS,
-                    workspace=None, err_flag=None, stream=None):
-    """One decode token per row (gdn.h: gdn_decode_step).  Caches in place;
-    ``out`` [B, HV, dv] receives o.  A workspace is allocated when not given."""
+def _decode_step(fn, mixed_qkv, gb, gate, slot_idx, conv_state, conv_weight, rec_state, out,
+                 dims, scale, conv_bias, flags, workspace, err_flag, stream):
     lib = load_library()
     B = mixed_qkv.shape[0]
     HV, dk, dv = dims.num_v_heads, dims.head_k_dim, dims.head_v_dim
     D = 2 * dims.num_k_heads * dk + HV * dv
     _dev(mixed_qkv, "mixed_qkv", shape=(B, D))
-    _dev(g, "g", torch.float32, (B, HV)); _dev(beta, "beta", torch.float32, (B, HV))
+    if gate is None:
+        _dev(gb[0], "g", torch.float32, (B, HV)); _dev(gb[1], "beta", torch.float32, (B, HV))
     _dev(slot_idx, "slot_idx", torch.int32, (B,))
     _dev(conv_state, "conv_state"); _dev(conv_weight, "conv_weight")
     _dev(conv_bias, "conv_bias", conv_weight.dtype)
@@ -180,12 +205,36 @@ def gdn_decode_step(mixed_qkv, g, beta, slot_idx, conv_state, conv_weight, rec_s
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=mixed_qkv.device)
     _dev(workspace, "workspace")
-    _check("gdn_decode_step", lib.gdn_decode_step(
-        _p(mixed_qkv), _dt(mixed_qkv), _p(g), _p(beta), _p(slot_idx), B, _p(conv_state),
-        _dt(conv_state), _p(conv_weight), _p(conv_bias), _dt(conv_weight), _p(rec_state), ns,
-        _p(out), _dt(out), ctypes.byref(dims), float(scale), flags, _p(workspace),
-        workspace.numel() * workspace.element_size(), _p(err_flag), _stream(stream)))
+    rest = (_p(slot_idx), B, _p(conv_state), _dt(conv_state), _p(conv_weight), _p(conv_bias),
+            _dt(conv_weight), _p(rec_state), ns, _p(out), _dt(out), ctypes.byref(dims),
+            float(scale), flags, _p(workspace), workspace.numel() * workspace.element_size(),
+            _p(err_flag), _stream(stream))
+    if gate is None:
+        status = lib.gdn_decode_step(_p(mixed_qkv), _dt(mixed_qkv), _p(gb[0]), _p(gb[1]), *rest)
+    else:
+        gs = _gate_struct(gate, B, HV)
+        status = lib.gdn_decode_step_gated(_p(mixed_qkv), _dt(mixed_qkv), ctypes.byref(gs), *rest)
+    _check(fn, status)
     return out
+
+
+def gdn_decode_step(mixed_qkv, g, beta, slot_idx, conv_state, conv_weight, rec_state, out,
+                    dims: gdn_dims, scale, conv_bias=None, flags=DEFAULT_DECODE_FLAGS,
+                    workspace=None, err_flag=None, stream=None):
+    """One decode token per row (gdn.h: gdn_decode_step).  Caches in place;
+    ``out`` [B, HV, dv] receives o.  A workspace is allocated when not given."""
+    return _decode_step("gdn_decode_step", mixed_qkv, (g, beta), None, slot_idx, conv_state,
+                        conv_weight, rec_state, out, dims, scale, conv_bias, flags, workspace,
+                        err_flag, stream)
+
+
+def gdn_decode_step_gated(mixed_qkv, gate: GateInputs, slot_idx, conv_state, conv_weight,
+                          rec_state, out, dims: gdn_dims, scale, conv_bias=None,
+                          flags=DEFAULT_DECODE_FLAGS, workspace=None, err_flag=None, stream=None):
+    """gdn_decode_step with the gating fused in (gdn.h: gdn_decode_step_gated)."""
+    return _decode_step("gdn_decode_step_gated", mixed_qkv, None, gate, slot_idx, conv_state,
+                        conv_weight, rec_state, out, dims, scale, conv_bias, flags, workspace,
+                        err_flag, stream)
 
 
 def gdn_decode_recurrent(qkv, g, beta, slot_idx, rec_state, out, dims: gdn_dims, scale,
@@ -214,18 +263,16 @@ def gdn_prefill_workspace_size(dims: gdn_dims, n_seqs: int, total_tokens: int) -
                                                           int(total_tokens)))
 
 
-def gdn_prefill_chunked(q, k, v, g, beta, cu_seqlens, slot_idx, rec_state, out,
-                        dims: gdn_dims, scale, flags=DEFAULT_PREFILL_FLAGS, workspace=None,
-                        err_flag=None, stream=None):
-    """Varlen chunked prefill (gdn.h: gdn_prefill_chunked).  ``rec_state`` is
-    read and written in place; ``out`` [T, HV, dv] receives o."""
+def _prefill(fn, q, k, v, gb, gate, cu_seqlens, slot_idx, rec_state, out, dims, scale, flags,
+             workspace, err_flag, stream):
     lib = load_library()
     T = q.shape[0]
     H, HV, dk, dv = dims.num_k_heads, dims.num_v_heads, dims.head_k_dim, dims.head_v_dim
     n = slot_idx.shape[0]
     _dev(q, "q", shape=(T, H, dk)); _dev(k, "k", q.dtype, (T, H, dk))
     _dev(v, "v", q.dtype, (T, HV, dv))
-    _dev(g, "g", torch.float32, (T, HV)); _dev(beta, "beta", torch.float32, (T, HV))
+    if gate is None:
+        _dev(gb[0], "g", torch.float32, (T, HV)); _dev(gb[1], "beta", torch.float32, (T, HV))
     _dev(cu_seqlens, "cu_seqlens", torch.int32, (n + 1,))
     _dev(slot_idx, "slot_idx", torch.int32, (n,))
     _dev(rec_state, "rec_state", torch.float32); _dev(out, "out", shape=(T, HV, dv))
@@ -236,9 +283,30 @@ def gdn_prefill_chunked(q, k, v, g, beta, cu_seqlens, slot_idx, rec_state, out,
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _dev(workspace, "workspace")
-    _check("gdn_prefill_chunked", lib.gdn_prefill_chunked(
-        _p(q), _p(k), _p(v), _dt(q), _p(g), _p(beta), _p(cu_seqlens), n, T, _p(slot_idx),
-        _p(rec_state), rec_state.shape[0], _p(out), _dt(out), ctypes.byref(dims), float(scale),
-        flags, _p(workspace), workspace.numel() * workspace.element_size(), _p(err_flag),
-        _stream(stream)))
+    rest = (_p(cu_seqlens), n, T, _p(slot_idx), _p(rec_state), rec_state.shape[0], _p(out),
+            _dt(out), ctypes.byref(dims), float(scale), flags, _p(workspace),
+            workspace.numel() * workspace.element_size(), _p(err_flag), _stream(stream))
+    if gate is None:
+        status = lib.gdn_prefill_chunked(_p(q), _p(k), _p(v), _dt(q), _p(gb[0]), _p(gb[1]), *rest)
+    else:
+        gs = _gate_struct(gate, T, HV)
+        status = lib.gdn_prefill_chunked_gated(_p(q), _p(k), _p(v), _dt(q), ctypes.byref(gs), *rest)
+    _check(fn, status)
     return out
+
+
+def gdn_prefill_chunked(q, k, v, g, beta, cu_seqlens, slot_idx, rec_state, out,
+                        dims: gdn_dims, scale, flags=DEFAULT_PREFILL_FLAGS, workspace=None,
+                        err_flag=None, stream=None):
+    """Varlen chunked prefill (gdn.h: gdn_prefill_chunked).  ``rec_state`` is
+    read and written in place; ``out`` [T, HV, dv] receives o."""
+    return _prefill("gdn_prefill_chunked", q, k, v, (g, beta), None, cu_seqlens, slot_idx,
+                    rec_state, out, dims, scale, flags, workspace, err_flag, stream)
+
+
+def gdn_prefill_chunked_gated(q, k, v, gate: GateInputs, cu_seqlens, slot_idx, rec_state, out,
+                              dims: gdn_dims, scale, flags=DEFAULT_PREFILL_FLAGS, workspace=None,
+                              err_flag=None, stream=None):
+    """gdn_prefill_chunked with the gating fused in (gdn.h: gdn_prefill_chunked_gated)."""
+    return _prefill("gdn_prefill_chunked_gated", q, k, v, None, gate, cu_seqlens, slot_idx,
+                    rec_state, out, dims, scale, flags, workspace, err_flag, stream)

@@ -102,13 +102,34 @@ size_t gdn_decode_workspace_size(const gdn_dims* dims, int32_t batch) {
     return round256(static_cast<size_t>(batch) * static_cast<size_t>(conv_channels(dims)) * sizeof(float));
 }
 
-gdn_status gdn_decode_step(const void* mixed_qkv, gdn_dtype x_dt, const float* g,
-                           const float* beta, const int32_t* slot_idx, int32_t batch,
-                           void* conv_state, gdn_dtype cs_dt, const void* conv_weight,
-                           const void* conv_bias, gdn_dtype w_dt, float* rec_state,
-                           int32_t num_slots, void* out, gdn_dtype out_dt, const gdn_dims* dims,
-                           float scale, int32_t flags, void* workspace, size_t workspace_bytes,
-                           int32_t* err_flag, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The gate source checks shared by the direct and the gated entry points.
+gdn_status gate_args(const float* g, const float* beta, const gdn_gate_inputs* gi, bool rows,
+                     GateArgs& ga) {
+    ga = GateArgs{g, beta, nullptr, nullptr, nullptr, nullptr, 0};
+    if (gi) {
+        if (!dtype_ok(gi->ab_dt)) return GDN_ERR_DTYPE;
+        if (rows && (!gi->a || !gi->b || !gi->A_log || !gi->dt_bias)) return GDN_ERR_NULL;
+        ga = GateArgs{nullptr, nullptr, gi->a, gi->b, gi->A_log, gi->dt_bias,
+                      gi->ab_dt == GDN_BF16 ? 1 : 0};
+        if (!rows) ga.a = nullptr;
+    } else if (rows && (!g || !beta)) {
+        return GDN_ERR_NULL;
+    }
+    return GDN_OK;
+}
+
+gdn_status decode_step_impl(const void* mixed_qkv, gdn_dtype x_dt, const float* g,
+                            const float* beta, const gdn_gate_inputs* gate,
+                            const int32_t* slot_idx, int32_t batch, void* conv_state,
+                            gdn_dtype cs_dt, const void* conv_weight, const void* conv_bias,
+                            gdn_dtype w_dt, float* rec_state, int32_t num_slots, void* out,
+                            gdn_dtype out_dt, const gdn_dims* dims, float scale, int32_t flags,
+                            void* workspace, size_t workspace_bytes, int32_t* err_flag,
+                            void* stream) {
     if (gdn_status st = check_flags(flags, KNOWN_FLAGS | GDN_FLAG_STEP_FUSED | GDN_FLAG_STEP_SPLIT,
                                     err_flag))
         return st;
@@ -119,9 +140,11 @@ gdn_status gdn_decode_step(const void* mixed_qkv, gdn_dtype x_dt, const float* g
     if ((flags & GDN_FLAG_STEP_FUSED) && !decode_step_fused_fits(*dims)) return GDN_ERR_DIMS;
     if (!dtype_ok(x_dt) || !dtype_ok(cs_dt) || !dtype_ok(w_dt) || !dtype_ok(out_dt))
         return GDN_ERR_DTYPE;
+    GateArgs ga;
+    if (gdn_status st = gate_args(g, beta, gate, batch > 0, ga)) return st;
     if (batch > 0) {
-        if (!mixed_qkv || !g || !beta || !slot_idx || !conv_state || !conv_weight ||
-            !rec_state || !out || !workspace)
+        if (!mixed_qkv || !slot_idx || !conv_state || !conv_weight || !rec_state || !out ||
+            !workspace)
             return GDN_ERR_NULL;
         if (!aligned16(rec_state) || !aligned16(workspace) || !aligned16(mixed_qkv) ||
             !aligned16(conv_state) || !aligned16(conv_weight) || (conv_bias && !aligned16(conv_bias)))
@@ -137,7 +160,7 @@ gdn_status gdn_decode_step(const void* mixed_qkv, gdn_dtype x_dt, const float* g
     const bool fused = (flags & GDN_FLAG_STEP_FUSED) ||
                        (!(flags & GDN_FLAG_STEP_SPLIT) && decode_step_use_fused(*dims, batch));
     if (fused) {
-        GDN_TRY_LAUNCH(launch_decode_step_fused(mixed_qkv, x_dt, g, beta, slot_idx, batch, conv_state,
+        GDN_TRY_LAUNCH(launch_decode_step_fused(mixed_qkv, x_dt, ga, slot_idx, batch, conv_state,
                                                 cs_dt, conv_weight, conv_bias, w_dt, rec_state, out,
                                                 out_dt, *dims, scale, kflags, ef, s));
         return GDN_OK;
@@ -147,9 +170,70 @@ gdn_status gdn_decode_step(const void* mixed_qkv, gdn_dtype x_dt, const float* g
     GDN_TRY_LAUNCH(launch_conv_decode(mixed_qkv, x_dt, slot_idx, batch, conv_state, cs_dt,
                                       conv_weight, conv_bias, w_dt, y, GDN_F32, D,
                                       kflags & GDN_FLAG_SILU, ef, s));
-    GDN_TRY_LAUNCH(launch_decode_rec(y, GDN_F32, g, beta, slot_idx, batch, rec_state, out,
+    GDN_TRY_LAUNCH(launch_decode_rec(y, GDN_F32, ga, slot_idx, batch, rec_state, out,
                                      out_dt, *dims, scale, kflags, ef, s));
     return GDN_OK;
+}
+
+gdn_status prefill_impl(const void* q, const void* k, const void* v, gdn_dtype in_dt,
+                        const float* g, const float* beta, const gdn_gate_inputs* gate,
+                        const int32_t* cu_seqlens, int32_t n_seqs, int32_t total_tokens,
+                        const int32_t* slot_idx, float* rec_state, int32_t num_slots, void* out,
+                        gdn_dtype out_dt, const gdn_dims* dims, float scale, int32_t flags,
+                        int32_t* err_flag, void* stream) {
+    if (gdn_status st = check_flags(flags, GDN_FLAG_QK_L2NORM | GDN_FLAG_VALIDATE, err_flag))
+        return st;
+    if (gdn_status st = check_dims(dims)) return st;
+    if (n_seqs < 0 || n_seqs > 65535 || total_tokens < 0 || num_slots < 1) return GDN_ERR_DIMS;
+    if (!dtype_ok(in_dt) || !dtype_ok(out_dt)) return GDN_ERR_DTYPE;
+    if (dims->head_k_dim != dims->head_v_dim || dims->head_k_dim > 128) return GDN_ERR_DIMS;
+    if (!prefill_supported(*dims, in_dt)) return GDN_ERR_DTYPE;
+    GateArgs ga;
+    if (gdn_status st = gate_args(g, beta, gate, total_tokens > 0, ga)) return st;
+    if (n_seqs > 0 && (!cu_seqlens || !slot_idx || !rec_state)) return GDN_ERR_NULL;
+    if (total_tokens > 0 && (!q || !k || !v || !out)) return GDN_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(rec_state))
+        return GDN_ERR_ALIGN;
+    auto s = static_cast<hipStream_t>(stream);
+    if (flags & GDN_FLAG_VALIDATE)
+        GDN_TRY_LAUNCH(launch_validate(slot_idx, n_seqs, num_slots, cu_seqlens, total_tokens,
+                                       err_flag, s));
+    const int32_t* ef = (flags & GDN_FLAG_VALIDATE) ? err_flag : nullptr;
+    GDN_TRY_LAUNCH(launch_prefill(q, k, v, in_dt, ga, cu_seqlens, n_seqs, slot_idx,
+                                  rec_state, out, out_dt, *dims, scale, flags, ef, s));
+    return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_decode_step(const void* mixed_qkv, gdn_dtype x_dt, const float* g,
+                           const float* beta, const int32_t* slot_idx, int32_t batch,
+                           void* conv_state, gdn_dtype cs_dt, const void* conv_weight,
+                           const void* conv_bias, gdn_dtype w_dt, float* rec_state,
+                           int32_t num_slots, void* out, gdn_dtype out_dt, const gdn_dims* dims,
+                           float scale, int32_t flags, void* workspace, size_t workspace_bytes,
+                           int32_t* err_flag, void* stream) {
+    return decode_step_impl(mixed_qkv, x_dt, g, beta, nullptr, slot_idx, batch, conv_state,
+                            cs_dt, conv_weight, conv_bias, w_dt, rec_state, num_slots, out,
+                            out_dt, dims, scale, flags, workspace, workspace_bytes, err_flag,
+                            stream);
+}
+
+gdn_status gdn_decode_step_gated(const void* mixed_qkv, gdn_dtype x_dt,
+                                 const gdn_gate_inputs* gate, const int32_t* slot_idx,
+                                 int32_t batch, void* conv_state, gdn_dtype cs_dt,
+                                 const void* conv_weight, const void* conv_bias, gdn_dtype w_dt,
+                                 float* rec_state, int32_t num_slots, void* out, gdn_dtype out_dt,
+                                 const gdn_dims* dims, float scale, int32_t flags,
+                                 void* workspace, size_t workspace_bytes, int32_t* err_flag,
+                                 void* stream) {
+    if (!gate) return GDN_ERR_NULL;
+    return decode_step_impl(mixed_qkv, x_dt, nullptr, nullptr, gate, slot_idx, batch,
+                            conv_state, cs_dt, conv_weight, conv_bias, w_dt, rec_state,
+                            num_slots, out, out_dt, dims, scale, flags, workspace,
+                            workspace_bytes, err_flag, stream);
 }
 
 gdn_status gdn_decode_recurrent(const void* qkv, gdn_dtype qkv_dt, const float* g,
@@ -163,15 +247,17 @@ gdn_status gdn_decode_recurrent(const void* qkv, gdn_dtype qkv_dt, const float* 
     if (batch < 0 || batch > 65535 || num_slots < 1) return GDN_ERR_DIMS;
     if (static_cast<int64_t>(batch) * dims->num_v_heads > (1 << 24)) return GDN_ERR_DIMS;
     if (!dtype_ok(qkv_dt) || !dtype_ok(out_dt)) return GDN_ERR_DTYPE;
+    GateArgs ga;
+    if (gdn_status st = gate_args(g, beta, nullptr, batch > 0, ga)) return st;
     if (batch > 0) {
-        if (!qkv || !g || !beta || !slot_idx || !rec_state || !out) return GDN_ERR_NULL;
+        if (!qkv || !slot_idx || !rec_state || !out) return GDN_ERR_NULL;
         if (!aligned16(rec_state) || !aligned16(qkv)) return GDN_ERR_ALIGN;
     }
     auto s = static_cast<hipStream_t>(stream);
     if (flags & GDN_FLAG_VALIDATE)
         GDN_TRY_LAUNCH(launch_validate(slot_idx, batch, num_slots, nullptr, 0, err_flag, s));
     const int32_t* ef = (flags & GDN_FLAG_VALIDATE) ? err_flag : nullptr;
-    GDN_TRY_LAUNCH(launch_decode_rec(qkv, qkv_dt, g, beta, slot_idx, batch, rec_state, out,
+    GDN_TRY_LAUNCH(launch_decode_rec(qkv, qkv_dt, ga, slot_idx, batch, rec_state, out,
                                      out_dt, *dims, scale, flags, ef, s));
     return GDN_OK;
 }
@@ -189,25 +275,24 @@ gdn_status gdn_prefill_chunked(const void* q, const void* k, const void* v, gdn_
                                const gdn_dims* dims, float scale, int32_t flags, void* workspace,
                                size_t workspace_bytes, int32_t* err_flag, void* stream) {
     (void)workspace; (void)workspace_bytes;
-    if (gdn_status st = check_flags(flags, GDN_FLAG_QK_L2NORM | GDN_FLAG_VALIDATE, err_flag))
-        return st;
-    if (gdn_status st = check_dims(dims)) return st;
-    if (n_seqs < 0 || n_seqs > 65535 || total_tokens < 0 || num_slots < 1) return GDN_ERR_DIMS;
-    if (!dtype_ok(in_dt) || !dtype_ok(out_dt)) return GDN_ERR_DTYPE;
-    if (dims->head_k_dim != dims->head_v_dim || dims->head_k_dim > 128) return GDN_ERR_DIMS;
-    if (!prefill_supported(*dims, in_dt)) return GDN_ERR_DTYPE;
-    if (n_seqs > 0 && (!cu_seqlens || !slot_idx || !rec_state)) return GDN_ERR_NULL;
-    if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !out)) return GDN_ERR_NULL;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(rec_state))
-        return GDN_ERR_ALIGN;
-    auto s = static_cast<hipStream_t>(stream);
-    if (flags & GDN_FLAG_VALIDATE)
-        GDN_TRY_LAUNCH(launch_validate(slot_idx, n_seqs, num_slots, cu_seqlens, total_tokens,
-                                       err_flag, s));
-    const int32_t* ef = (flags & GDN_FLAG_VALIDATE) ? err_flag : nullptr;
-    GDN_TRY_LAUNCH(launch_prefill(q, k, v, in_dt, g, beta, cu_seqlens, n_seqs, slot_idx,
-                                  rec_state, out, out_dt, *dims, scale, flags, ef, s));
-    return GDN_OK;
+    return prefill_impl(q, k, v, in_dt, g, beta, nullptr, cu_seqlens, n_seqs, total_tokens,
+                        slot_idx, rec_state, num_slots, out, out_dt, dims, scale, flags,
+                        err_flag, stream);
+}
+
+gdn_status gdn_prefill_chunked_gated(const void* q, const void* k, const void* v,
+                                     gdn_dtype in_dt, const gdn_gate_inputs* gate,
+                                     const int32_t* cu_seqlens, int32_t n_seqs,
+                                     int32_t total_tokens, const int32_t* slot_idx,
+                                     float* rec_state, int32_t num_slots, void* out,
+                                     gdn_dtype out_dt, const gdn_dims* dims, float scale,
+                                     int32_t flags, void* workspace, size_t workspace_bytes,
+                                     int32_t* err_flag, void* stream) {
+    (void)workspace; (void)workspace_bytes;
+    if (!gate) return GDN_ERR_NULL;
+    return prefill_impl(q, k, v, in_dt, nullptr, nullptr, gate, cu_seqlens, n_seqs,
+                        total_tokens, slot_idx, rec_state, num_slots, out, out_dt, dims, scale,
+                        flags, err_flag, stream);
 }
 
 }  // extern "C"

@@ -24,6 +24,7 @@
 #include <atomic>
 
 #include "conv_io.hpp"
+#include "gate.hpp"
 #include "gdn_device.hpp"
 #include "gdn_internal.hpp"
 
@@ -74,9 +75,9 @@ __device__ __forceinline__ void state_st(float* p, const float4& x) {
 #endif
 }
 
-template <int DK, int RPL, bool FULL, typename YT, typename OT>
+template <int DK, int RPL, bool FULL, bool GATED, typename YT, typename OT>
 __device__ __forceinline__ void rec_item(
-    const YT* __restrict__ y, const float* __restrict__ g, const float* __restrict__ beta,
+    const YT* __restrict__ y, const GateArgs& ga,
     const int32_t* __restrict__ slot, float* __restrict__ rec, OT* __restrict__ out, int32_t H,
     int32_t HV, int32_t dv, int b, int hv, int tile, float scale, int32_t flags) {
     constexpr int NV = DK / 32;               // float4 per lane per row
@@ -96,6 +97,15 @@ __device__ __forceinline__ void rec_item(
             }
         }
         return;                               // next item
+    }
+
+    // 0. fused gating: its inputs first, so their (in-order) wait never waits
+    //    for the state
+    float gx0 = 0.0f, gx1 = 0.0f;
+    GateHead gh{0.0f, 0.0f};
+    if constexpr (GATED) {
+        gate_raw(ga, static_cast<size_t>(b) * HV + hv, gx0, gx1);
+        gh = gate_head(ga, hv);
     }
 
     const int D = 2 * H * DK + HV * dv;
@@ -151,8 +161,14 @@ __device__ __forceinline__ void rec_item(
         kf[i].x *= kmul; kf[i].y *= kmul; kf[i].z *= kmul; kf[i].w *= kmul;
     }
 
-    const float alpha = expf(g[static_cast<size_t>(b) * HV + hv]);
-    const float bt = beta[static_cast<size_t>(b) * HV + hv];
+    float gv, bt;
+    if constexpr (GATED) {
+        gate_finish(ga, gh, gx0, gx1, gv, bt);
+    } else {
+        gv = ga.g[static_cast<size_t>(b) * HV + hv];
+        bt = ga.beta[static_cast<size_t>(b) * HV + hv];
+    }
+    const float alpha = expf(gv);
 
     // 3. per row: decay, predict, delta update, output
 #pragma unroll
@@ -185,9 +201,9 @@ __device__ __forceinline__ void rec_item(
     }
 }
 
-template <int DK, int RPL, bool FULL, typename YT, typename OT>
+template <int DK, int RPL, bool FULL, bool GATED, typename YT, typename OT>
 __global__ __launch_bounds__(256) void decode_rec_kernel(
-    const YT* __restrict__ y, const float* __restrict__ g, const float* __restrict__ beta,
+    const YT* __restrict__ y, const GateArgs ga,
     const int32_t* __restrict__ slot, float* __restrict__ rec, OT* __restrict__ out, int32_t H,
     int32_t HV, int32_t dv, int32_t tiles_per_head, int32_t n_items, float scale,
     int32_t flags, const int32_t* __restrict__ err_flag) {
@@ -199,7 +215,7 @@ __global__ __launch_bounds__(256) void decode_rec_kernel(
         const int b = item / per_row;
         const int hv = (item - b * per_row) / tiles_per_head;
         const int tile = item - b * per_row - hv * tiles_per_head;
-        rec_item<DK, RPL, FULL, YT, OT>(y, g, beta, slot, rec, out, H, HV, dv, b, hv, tile, scale, flags);
+        rec_item<DK, RPL, FULL, GATED, YT, OT>(y, ga, slot, rec, out, H, HV, dv, b, hv, tile, scale, flags);
     }
 }
 
@@ -216,13 +232,13 @@ __global__ __launch_bounds__(256) void decode_rec_kernel(
 // ---------------------------------------------------------------------------
 template <int DK, typename XT, typename CT, typename WT, typename OT>
 __global__ __launch_bounds__(256) void decode_step_kernel(
-    const XT* __restrict__ x, const float* __restrict__ g, const float* __restrict__ beta,
+    const XT* __restrict__ x, const GateArgs ga,
     const int32_t* __restrict__ slot, CT* __restrict__ cs, const WT* __restrict__ w,
     const WT* __restrict__ bias, float* __restrict__ rec, OT* __restrict__ out, int32_t H,
     int32_t HV, int32_t dv, int32_t n_groups, float scale, int32_t flags,
     const int32_t* __restrict__ err_flag) {
     constexpr int NV = DK / 32;               // float4 per lane per row
-    extern __shared__ float ys[];             // [q_h (DK) | k_h (DK) | v of the group (G dv)]
+    extern __shared__ float ys[];             // [q_h (DK) | k_h (DK) | v of the group (G dv) | (g, beta) x G]
     if (call_rejected(err_flag)) return;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -263,6 +279,14 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
                                  : 2 * H * DK + h * R + (lc - 2 * DK);
         };
         const bool silu_on = (flags & GDN_FLAG_SILU) != 0;
+        float* gs = ys + 2 * DK + R;          // gates of the group's value heads
+        float gx0 = 0.0f, gx1 = 0.0f;
+        GateHead gh{0.0f, 0.0f};
+        const bool gate_lane = static_cast<int>(threadIdx.x) < G;
+        if (gate_lane) {                      // issued before the conv and state loads
+            gate_raw(ga, static_cast<size_t>(b) * HV + h * G + threadIdx.x, gx0, gx1);
+            gh = gate_head(ga, h * G + threadIdx.x);
+        }
         if (units <= 256) {
             // threads past the last unit re-read unit 0 (loads stay unconditional)
             const bool mine = static_cast<int>(threadIdx.x) < units;
@@ -287,6 +311,19 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
                 *reinterpret_cast<float4*>(&ys[lc]) = make_float4(y[0], y[1], y[2], y[3]);
             }
             fetch(S, 0);
+        }
+        if (gate_lane) {
+            float gv, bv;
+            gate_finish(ga, gh, gx0, gx1, gv, bv);
+            gs[2 * threadIdx.x] = gv;
+            gs[2 * threadIdx.x + 1] = bv;
+        }
+        for (int t = threadIdx.x + 256; t < G; t += 256) {   // groups of more than 256 heads
+            float x0, x1, gv, bv;
+            gate_raw(ga, static_cast<size_t>(b) * HV + h * G + t, x0, x1);
+            gate_finish(ga, gate_head(ga, h * G + t), x0, x1, gv, bv);
+            gs[2 * t] = gv;
+            gs[2 * t + 1] = bv;
         }
         __syncthreads();
 
@@ -320,9 +357,9 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         // the passes: pass 0's rows are already in S
         auto pass = [&](int r0) {
             const int r = r0 + rl;
-            const int hv = h * G + r0 / dv;   // a pass lies inside one head (dv % 32 == 0)
-            const float alpha = expf(g[static_cast<size_t>(b) * HV + hv]);
-            const float bt = beta[static_cast<size_t>(b) * HV + hv];
+            const int gi = r0 / dv;           // a pass lies inside one head (dv % 32 == 0)
+            const float alpha = expf(gs[2 * gi]);
+            const float bt = gs[2 * gi + 1];
             const float vr = ys[2 * DK + r];
             float u = 0.f;
 #pragma unroll
@@ -357,7 +394,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
 
 namespace {
 struct RecArgs {
-    const void* y; const float* g; const float* beta; const int32_t* slot; int32_t batch;
+    const void* y; GateArgs gate; const int32_t* slot; int32_t batch;
     float* rec; void* out; const gdn_dims* d; float scale; int32_t flags; const int32_t* err;
     hipStream_t st;
 };
@@ -377,17 +414,23 @@ int cu_count() {
     return n;
 }
 
-template <int DK, int RPL, bool FULL, typename YT, typename OT>
-hipError_t run_rec_t(const RecArgs& a) {
+template <int DK, int RPL, bool FULL, bool GATED, typename YT, typename OT>
+hipError_t run_rec_g(const RecArgs& a) {
     const int rows_per_wg = 32 * RPL;
     const int tiles = (a.d->head_v_dim + rows_per_wg - 1) / rows_per_wg;
     const int64_t items = static_cast<int64_t>(a.batch) * a.d->num_v_heads * tiles;
     const int64_t resident = static_cast<int64_t>(cu_count()) * GDN_DECODE_WG_PER_CU;
     const int grid = static_cast<int>(items < resident ? items : resident);
-    return launch(decode_rec_kernel<DK, RPL, FULL, YT, OT>, dim3(grid), dim3(256), 0, a.st,
-                  static_cast<const YT*>(a.y), a.g, a.beta, a.slot, a.rec,
+    return launch(decode_rec_kernel<DK, RPL, FULL, GATED, YT, OT>, dim3(grid), dim3(256), 0, a.st,
+                  static_cast<const YT*>(a.y), a.gate, a.slot, a.rec,
                   static_cast<OT*>(a.out), a.d->num_k_heads, a.d->num_v_heads,
                   a.d->head_v_dim, tiles, static_cast<int32_t>(items), a.scale, a.flags, a.err);
+}
+
+template <int DK, int RPL, bool FULL, typename YT, typename OT>
+hipError_t run_rec_t(const RecArgs& a) {
+    if (a.gate.a) return run_rec_g<DK, RPL, FULL, true, YT, OT>(a);
+    return run_rec_g<DK, RPL, FULL, false, YT, OT>(a);
 }
 
 template <int DK, int RPL, typename YT, typename OT>
@@ -426,7 +469,7 @@ hipError_t pick_dk(const RecArgs& a) {
 
 namespace {
 struct StepArgs {
-    const void* x; const float* g; const float* beta; const int32_t* slot; int32_t batch;
+    const void* x; GateArgs gate; const int32_t* slot; int32_t batch;
     void* cs; const void* w; const void* bias; float* rec; void* out; const gdn_dims* d;
     float scale; int32_t flags; const int32_t* err; hipStream_t st;
 };
@@ -434,12 +477,12 @@ struct StepArgs {
 template <int DK, typename XT, typename CT, typename WT, typename OT>
 hipError_t run_step(const StepArgs& a) {
     const int G = a.d->num_v_heads / a.d->num_k_heads;
-    const size_t lds = static_cast<size_t>(2 * DK + G * a.d->head_v_dim) * sizeof(float);
+    const size_t lds = static_cast<size_t>(2 * DK + G * a.d->head_v_dim + 2 * G) * sizeof(float);
     const int64_t groups = static_cast<int64_t>(a.batch) * a.d->num_k_heads;
     const int64_t resident = static_cast<int64_t>(cu_count()) * GDN_STEP_WG_PER_CU;
     const int grid = static_cast<int>(groups < resident ? groups : resident);
     return launch(decode_step_kernel<DK, XT, CT, WT, OT>, dim3(grid), dim3(256), lds, a.st,
-                  static_cast<const XT*>(a.x), a.g, a.beta, a.slot, static_cast<CT*>(a.cs),
+                  static_cast<const XT*>(a.x), a.gate, a.slot, static_cast<CT*>(a.cs),
                   static_cast<const WT*>(a.w), static_cast<const WT*>(a.bias), a.rec,
                   static_cast<OT*>(a.out), a.d->num_k_heads, a.d->num_v_heads,
                   a.d->head_v_dim, static_cast<int32_t>(groups), a.scale, a.flags, a.err);
@@ -473,8 +516,8 @@ hipError_t step_x(gdn_dtype xt, gdn_dtype c, gdn_dtype wt, gdn_dtype o, const St
 #endif
 
 bool decode_step_fused_fits(const gdn_dims& d) {
-    const int64_t lds = (2LL * d.head_k_dim + static_cast<int64_t>(d.num_v_heads / d.num_k_heads) * d.head_v_dim) *
-                        static_cast<int64_t>(sizeof(float));
+    const int64_t G = d.num_v_heads / d.num_k_heads;
+    const int64_t lds = (2LL * d.head_k_dim + G * d.head_v_dim + 2 * G) * static_cast<int64_t>(sizeof(float));
     return lds <= 65536;
 }
 
@@ -483,14 +526,14 @@ bool decode_step_use_fused(const gdn_dims& d, int32_t batch) {
            static_cast<int64_t>(batch) * d.num_k_heads < static_cast<int64_t>(GDN_DECODE_FUSED_MAX_GROUPS_PER_CU) * cu_count();
 }
 
-hipError_t launch_decode_step_fused(const void* x, gdn_dtype x_dt, const float* g,
-                                    const float* beta, const int32_t* slot_idx, int32_t batch,
+hipError_t launch_decode_step_fused(const void* x, gdn_dtype x_dt, const GateArgs& gate,
+                                    const int32_t* slot_idx, int32_t batch,
                                     void* conv_state, gdn_dtype cs_dt, const void* weight,
                                     const void* bias, gdn_dtype w_dt, float* rec_state, void* out,
                                     gdn_dtype out_dt, const gdn_dims& dims, float scale,
                                     int32_t flags, const int32_t* err_flag, hipStream_t stream) {
     if (batch == 0) return hipSuccess;
-    const StepArgs a{x, g, beta, slot_idx, batch, conv_state, weight, bias, rec_state, out,
+    const StepArgs a{x, gate, slot_idx, batch, conv_state, weight, bias, rec_state, out,
                      &dims, scale, flags, err_flag, stream};
     switch (dims.head_k_dim) {
         case 32: return step_x<32>(x_dt, cs_dt, w_dt, out_dt, a);
@@ -501,12 +544,12 @@ hipError_t launch_decode_step_fused(const void* x, gdn_dtype x_dt, const float* 
     }
 }
 
-hipError_t launch_decode_rec(const void* y, gdn_dtype y_dt, const float* g, const float* beta,
+hipError_t launch_decode_rec(const void* y, gdn_dtype y_dt, const GateArgs& gate,
                              const int32_t* slot_idx, int32_t batch, float* rec_state,
                              void* out, gdn_dtype out_dt, const gdn_dims& dims, float scale,
                              int32_t flags, const int32_t* err_flag, hipStream_t stream) {
     if (batch == 0) return hipSuccess;
-    const RecArgs a{y, g, beta, slot_idx, batch, rec_state, out, &dims, scale, flags, err_flag,
+    const RecArgs a{y, gate, slot_idx, batch, rec_state, out, &dims, scale, flags, err_flag,
                     stream};
     if (y_dt == GDN_BF16)
         return out_dt == GDN_BF16 ? pick_dk<bf16_t, bf16_t>(a) : pick_dk<bf16_t, float>(a);

@@ -24,6 +24,20 @@ hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem,
     return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, p, shmem, stream);
 }
 
+// Source of the per-(token, value head) log-decay g and write strength beta:
+// the arrays g, beta [rows, HV] fp32, or, when `a` is non-null, fused gating
+// from the projections a, b [rows, HV] (bf16 when ab_bf16, else fp32) and the
+// per-head A_log, dt_bias [HV] fp32.
+struct GateArgs {
+    const float* g;
+    const float* beta;
+    const void* a;
+    const void* b;
+    const float* A_log;
+    const float* dt_bias;
+    int32_t ab_bf16;
+};
+
 // Writes *err_flag (0 or GDN_EFLAG_* bits) for n slot indices and, when cu is
 // non-null, cu_seqlens[n + 1] against total.
 hipError_t launch_validate(const int32_t* slot_idx, int32_t n, int32_t num_slots,
@@ -45,7 +59,7 @@ hipError_t launch_conv_varlen(const void* x, gdn_dtype x_dt, const int32_t* cu_s
                               int32_t flags, const int32_t* err_flag, hipStream_t stream);
 
 // Gated delta-rule decode update from the post-conv activations y [B, D].
-hipError_t launch_decode_rec(const void* y, gdn_dtype y_dt, const float* g, const float* beta,
+hipError_t launch_decode_rec(const void* y, gdn_dtype y_dt, const GateArgs& gate,
                              const int32_t* slot_idx, int32_t batch, float* rec_state,
                              void* out, gdn_dtype out_dt, const gdn_dims& dims, float scale,
                              int32_t flags, const int32_t* err_flag, hipStream_t stream);
@@ -56,8 +70,8 @@ hipError_t launch_decode_rec(const void* y, gdn_dtype y_dt, const float* g, cons
 // results equal those of the conv + recurrence pair bitwise.
 bool decode_step_fused_fits(const gdn_dims& d);
 bool decode_step_use_fused(const gdn_dims& d, int32_t batch);
-hipError_t launch_decode_step_fused(const void* x, gdn_dtype x_dt, const float* g,
-                                    const float* beta, const int32_t* slot_idx, int32_t batch,
+hipError_t launch_decode_step_fused(const void* x, gdn_dtype x_dt, const GateArgs& gate,
+                                    const int32_t* slot_idx, int32_t batch,
                                     void* conv_state, gdn_dtype cs_dt, const void* weight,
                                     const void* bias, gdn_dtype w_dt, float* rec_state, void* out,
                                     gdn_dtype out_dt, const gdn_dims& dims, float scale,
@@ -66,7 +80,7 @@ hipError_t launch_decode_step_fused(const void* x, gdn_dtype x_dt, const float* 
 // Chunked prefill: one workgroup per (sequence, value head).
 bool prefill_supported(const gdn_dims& d, gdn_dtype in_dt);
 hipError_t launch_prefill(const void* q, const void* k, const void* v, gdn_dtype in_dt,
-                          const float* g, const float* beta, const int32_t* cu, int32_t n_seqs,
+                          const GateArgs& gate, const int32_t* cu, int32_t n_seqs,
                           const int32_t* slot, float* rec, void* out, gdn_dtype out_dt,
                           const gdn_dims& d, float scale, int32_t flags, const int32_t* err,
                           hipStream_t st);

@@ -32,6 +32,7 @@
 // 16 + 4q + s - 4 (s >= 4), which is exactly what two vertically adjacent
 // accumulator tiles hold in one lane.  With permuted slots the state, U and
 // (cK . U) feed MFMA B operands straight from accumulator registers.
+#include "gate.hpp"
 #include "gdn_device.hpp"
 #include "gdn_internal.hpp"
 
@@ -80,6 +81,9 @@ __device__ __forceinline__ uint4 buf_ld16(rsrc_t r, uint32_t off) {
 }
 __device__ __forceinline__ float buf_ld4f(rsrc_t r, uint32_t off) {
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ bf16_t buf_ld2(rsrc_t r, uint32_t off) {
+    return static_cast<bf16_t>(__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
 }
 __device__ __forceinline__ void buf_st16(rsrc_t r, uint32_t off, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
     typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
@@ -180,7 +184,7 @@ constexpr int PF_NT = 64 * PF_NW;        // threads per workgroup
 template <int D, typename IT, typename OT>
 __global__ __launch_bounds__(PF_NT) void prefill_kernel(
     const IT* __restrict__ qg, const IT* __restrict__ kg, const IT* __restrict__ vg,
-    const float* __restrict__ gg, const float* __restrict__ bg, const int32_t* __restrict__ cu,
+    const GateArgs ga, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ slot, float* __restrict__ rec, OT* __restrict__ out, int32_t H,
     int32_t HV, float scale, int32_t flags, const int32_t* __restrict__ err_flag) {
     constexpr bool SPL = sizeof(IT) == 4;        // fp32 inputs: hi/lo planes
@@ -249,6 +253,7 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
     const int ta = 2 * tp;
     uint4 pk[CP][2][WPE], pq[CP][2][WPE], pv[CP][2][WPE];
     float pbeta = 0.0f, pg = 0.0f;
+    const GateHead gh = gate_head(ga, hv);       // per-head gating constants, loaded once
     // Loads go through buffer descriptors over the chunk's rows (the entry
     // point's dims bound a chunk's span, 64 HV D elements, below 2^28 bytes),
     // so rows past the chunk's length read as zero.
@@ -277,11 +282,22 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
                 }
             }
         }
-        const rsrc_t rb = make_rsrc(bg + static_cast<size_t>(c) * HV, Lc * HV * 4);
-        const rsrc_t rg = make_rsrc(gg + static_cast<size_t>(c) * HV, Lc * HV * 4);
-        const uint32_t ob = static_cast<uint32_t>(min(tid, CH) * HV + hv) * 4;
-        pbeta = buf_ld4f(rb, ob);                // used by tid < 64
-        pg = buf_ld4f(rg, ob);                   // used by wave 0
+        // the chunk's raw gate values (g and beta, or a and b for fused gating);
+        // used by wave 0 at the loop top
+        const bool half = ga.a != nullptr && ga.ab_bf16;
+        const uint32_t es = half ? 2 : 4;
+        const char* s0 = static_cast<const char*>(ga.a ? ga.a : static_cast<const void*>(ga.g));
+        const char* s1 = static_cast<const char*>(ga.a ? ga.b : static_cast<const void*>(ga.beta));
+        const rsrc_t r0 = make_rsrc(s0 + static_cast<size_t>(c) * HV * es, Lc * HV * es);
+        const rsrc_t r1 = make_rsrc(s1 + static_cast<size_t>(c) * HV * es, Lc * HV * es);
+        const uint32_t ob = static_cast<uint32_t>(min(tid, CH) * HV + hv) * es;
+        if (half) {
+            pg = bf16_to_f32(buf_ld2(r0, ob));
+            pbeta = bf16_to_f32(buf_ld2(r1, ob));
+        } else {
+            pg = buf_ld4f(r0, ob);
+            pbeta = buf_ld4f(r1, ob);
+        }
     };
     fetch(t0, min(CH, t1 - t0));
 
@@ -316,9 +332,11 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
                 }
             }
         }
-        if (tid < CH) sm.beta[tid] = pbeta;
-        if (wave == 0) {                         // cumulative log-decay: fixed-order DPP wave scan
-            float gt = pg;
+        if (wave == 0) {                         // gate, then the cumulative log-decay:
+            float gt, bv;                        // fixed-order DPP wave scan
+            gate_finish(ga, gh, pg, pbeta, gt, bv);
+            if (lane >= L) { gt = 0.0f; bv = 0.0f; }   // rows past the chunk (raw values read as 0)
+            sm.beta[lane] = bv;
             gt += dpp_scan_step<0x111, 0xF>(gt);     // row_shr:1 .. row_shr:8 inside each 16-lane row
             gt += dpp_scan_step<0x112, 0xF>(gt);
             gt += dpp_scan_step<0x114, 0xF>(gt);
@@ -758,25 +776,25 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
 
 namespace {
 template <int D, typename IT, typename OT>
-hipError_t run_prefill(const void* q, const void* k, const void* v, const float* g,
-                       const float* beta, const int32_t* cu, int32_t n_seqs, const int32_t* slot,
+hipError_t run_prefill(const void* q, const void* k, const void* v, const GateArgs& ga,
+                       const int32_t* cu, int32_t n_seqs, const int32_t* slot,
                        float* rec, void* out, const gdn_dims& d, float scale, int32_t flags,
                        const int32_t* err, hipStream_t st) {
     dim3 grid(d.num_v_heads, n_seqs);
     return launch(prefill_kernel<D, IT, OT>, grid, dim3(PF_NT), 0, st,
                   static_cast<const IT*>(q), static_cast<const IT*>(k),
-                  static_cast<const IT*>(v), g, beta, cu, slot, rec, static_cast<OT*>(out),
+                  static_cast<const IT*>(v), ga, cu, slot, rec, static_cast<OT*>(out),
                   d.num_k_heads, d.num_v_heads, scale, flags, err);
 }
 
 template <int D, typename IT>
-hipError_t pick_out(gdn_dtype out_dt, const void* q, const void* k, const void* v, const float* g,
-                    const float* beta, const int32_t* cu, int32_t n_seqs, const int32_t* slot,
+hipError_t pick_out(gdn_dtype out_dt, const void* q, const void* k, const void* v, const GateArgs& ga,
+                    const int32_t* cu, int32_t n_seqs, const int32_t* slot,
                     float* rec, void* out, const gdn_dims& d, float scale, int32_t flags,
                     const int32_t* err, hipStream_t st) {
     return out_dt == GDN_BF16
-        ? run_prefill<D, IT, bf16_t>(q, k, v, g, beta, cu, n_seqs, slot, rec, out, d, scale, flags, err, st)
-        : run_prefill<D, IT, float>(q, k, v, g, beta, cu, n_seqs, slot, rec, out, d, scale, flags, err, st);
+        ? run_prefill<D, IT, bf16_t>(q, k, v, ga, cu, n_seqs, slot, rec, out, d, scale, flags, err, st)
+        : run_prefill<D, IT, float>(q, k, v, ga, cu, n_seqs, slot, rec, out, d, scale, flags, err, st);
 }
 }  // namespace
 
@@ -789,7 +807,7 @@ bool prefill_supported(const gdn_dims& d, gdn_dtype in_dt) {
 }
 
 hipError_t launch_prefill(const void* q, const void* k, const void* v, gdn_dtype in_dt,
-                          const float* g, const float* beta, const int32_t* cu, int32_t n_seqs,
+                          const GateArgs& ga, const int32_t* cu, int32_t n_seqs,
                           const int32_t* slot, float* rec, void* out, gdn_dtype out_dt,
                           const gdn_dims& d, float scale, int32_t flags, const int32_t* err,
                           hipStream_t st) {
@@ -797,12 +815,12 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, gdn_dtype
     if (!prefill_supported(d, in_dt)) return hipErrorInvalidValue;
     const int D = d.head_k_dim;
     if (in_dt == GDN_F32) {
-        if (D == 32) return pick_out<32, float>(out_dt, q, k, v, g, beta, cu, n_seqs, slot, rec, out, d, scale, flags, err, st);
-        return pick_out<64, float>(out_dt, q, k, v, g, beta, cu, n_seqs, slot, rec, out, d, scale, flags, err, st);
+        if (D == 32) return pick_out<32, float>(out_dt, q, k, v, ga, cu, n_seqs, slot, rec, out, d, scale, flags, err, st);
+        return pick_out<64, float>(out_dt, q, k, v, ga, cu, n_seqs, slot, rec, out, d, scale, flags, err, st);
     }
-    if (D == 32) return pick_out<32, bf16_t>(out_dt, q, k, v, g, beta, cu, n_seqs, slot, rec, out, d, scale, flags, err, st);
-    if (D == 64) return pick_out<64, bf16_t>(out_dt, q, k, v, g, beta, cu, n_seqs, slot, rec, out, d, scale, flags, err, st);
-    return pick_out<128, bf16_t>(out_dt, q, k, v, g, beta, cu, n_seqs, slot, rec, out, d, scale, flags, err, st);
+    if (D == 32) return pick_out<32, bf16_t>(out_dt, q, k, v, ga, cu, n_seqs, slot, rec, out, d, scale, flags, err, st);
+    if (D == 64) return pick_out<64, bf16_t>(out_dt, q, k, v, ga, cu, n_seqs, slot, rec, out, d, scale, flags, err, st);
+    return pick_out<128, bf16_t>(out_dt, q, k, v, ga, cu, n_seqs, slot, rec, out, d, scale, flags, err, st);
 }
 
 }  // namespace gdn

@@ -86,6 +86,26 @@ def decode_inputs(batch, num_slots, H=16, HV=32, dk=128, dv=128, W=4,
                 dims=dict(H=H, HV=HV, dk=dk, dv=dv, W=W))
 
 
+def gating_inputs(rows, HV, seed=0, ab_dtype=torch.bfloat16, threshold_frac=0.05):
+    """Raw projections for fused gating.
+
+    * a [rows, HV] ab_dtype ~ 3 N(0, 1); a fraction ``threshold_frac`` of the
+      entries is shifted by +25 so that a + dt_bias exceeds the softplus
+      threshold (20)
+    * b [rows, HV] ab_dtype ~ 2 N(0, 1)
+    * A_log [HV] fp32 ~ U(0, log 16)
+    * dt_bias [HV] fp32 ~ U(-7, -2)
+    """
+    gen = torch.Generator().manual_seed(seed + 3000)
+    a = 3.0 * torch.randn(rows, HV, generator=gen)
+    big = torch.rand(rows, HV, generator=gen) < threshold_frac
+    a = a + 25.0 * big
+    b = 2.0 * torch.randn(rows, HV, generator=gen)
+    A_log = torch.rand(HV, generator=gen) * 2.772588722239781
+    dt_bias = -2.0 - 5.0 * torch.rand(HV, generator=gen)
+    return dict(a=a.to(ab_dtype), b=b.to(ab_dtype), A_log=A_log.float(), dt_bias=dt_bias.float())
+
+
 def seqlens_uniform(n_seqs, lo, hi, gen):
     """n_seqs integer lengths uniform in [lo, hi]."""
     return torch.randint(lo, hi + 1, (n_seqs,), generator=gen).tolist()

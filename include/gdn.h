@@ -8,6 +8,9 @@
  *   gdn_decode_recurrent the recurrent half of the decode step alone
  *   gdn_prefill_chunked  varlen chunked (64-token, WY/UT) prefill on post-conv
  *                        q/k/v, reading and writing the same state cache
+ *   gdn_decode_step_gated, gdn_prefill_chunked_gated
+ *                        the same two calls with the gating fused in: g and
+ *                        beta computed in-kernel from the raw projections
  *
  * Sources (pages, by title and section):
  *   [P1] RL-Kernel PR #469 "C6: GDN decode-step goldens and recurrent/conv
@@ -98,6 +101,23 @@ typedef struct {
     int32_t head_v_dim;    /* dv */
     int32_t conv_width;    /* W  */
 } gdn_dims;
+
+/* Inputs of the fused gating ([P1] "How the golden relates to the kernel",
+   item 1), computed in fp32 inside the kernels for each (row or token r,
+   value head h):
+     beta[r, h] = 1 / (1 + exp(-b[r, h]))
+     g[r, h]    = -exp(A_log[h]) * softplus(a[r, h] + dt_bias[h]),
+     softplus(x) = x for x > 20, else log(1 + exp(x)) (evaluated as log1p).
+   All device memory, caller-owned, read only.  a and b have the layout of the
+   g and beta arrays they replace ([rows, HV]); no alignment beyond the
+   element's own is needed. */
+typedef struct {
+    const void* a;           /* [rows, HV] ab_dt: decay-gate pre-activation  */
+    const void* b;           /* [rows, HV] ab_dt: beta pre-activation        */
+    gdn_dtype ab_dt;         /* GDN_F32 or GDN_BF16                          */
+    const float* A_log;      /* [HV] fp32                                    */
+    const float* dt_bias;    /* [HV] fp32                                    */
+} gdn_gate_inputs;
 
 /*
  * gdn_conv_update -- causal depthwise conv1d with per-slot left context
@@ -234,6 +254,36 @@ gdn_status gdn_prefill_chunked(const void* q, const void* k, const void* v, gdn_
                                const gdn_dims* dims, float scale, int32_t flags,
                                void* workspace, size_t workspace_bytes,
                                int32_t* err_flag, void* stream);
+
+/*
+ * gdn_decode_step_gated / gdn_prefill_chunked_gated -- gdn_decode_step and
+ * gdn_prefill_chunked with the gating fused in ([P1] "How the golden relates
+ * to the kernel", item 1): `gate` (host pointer to a gdn_gate_inputs whose
+ * arrays are device memory) replaces the g and beta arrays; every other
+ * argument, the error codes and the fail-closed behaviour are as in the
+ * ungated call.  GDN_ERR_NULL if gate is NULL or, with rows to process, any
+ * of its arrays is; GDN_ERR_DTYPE if ab_dt is not GDN_F32 / GDN_BF16.
+ */
+gdn_status gdn_decode_step_gated(const void* mixed_qkv, gdn_dtype x_dt,
+                                 const gdn_gate_inputs* gate,
+                                 const int32_t* slot_idx, int32_t batch,
+                                 void* conv_state, gdn_dtype cs_dt,
+                                 const void* conv_weight, const void* conv_bias, gdn_dtype w_dt,
+                                 float* rec_state, int32_t num_slots,
+                                 void* out, gdn_dtype out_dt,
+                                 const gdn_dims* dims, float scale, int32_t flags,
+                                 void* workspace, size_t workspace_bytes,
+                                 int32_t* err_flag, void* stream);
+
+gdn_status gdn_prefill_chunked_gated(const void* q, const void* k, const void* v,
+                                     gdn_dtype in_dt, const gdn_gate_inputs* gate,
+                                     const int32_t* cu_seqlens, int32_t n_seqs,
+                                     int32_t total_tokens, const int32_t* slot_idx,
+                                     float* rec_state, int32_t num_slots,
+                                     void* out, gdn_dtype out_dt,
+                                     const gdn_dims* dims, float scale, int32_t flags,
+                                     void* workspace, size_t workspace_bytes,
+                                     int32_t* err_flag, void* stream);
 
 /* gdn_strerror -- static, NUL-terminated description of a status code. */
 const char* gdn_strerror(gdn_status s);

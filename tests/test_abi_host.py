@@ -130,3 +130,42 @@ def test_binding_refuses_cpu_tensors():
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(ImportError):
         _abi.load_library(str(tmp_path / "libgdn_missing.so"))
+
+
+def _gate(a=FAKE, b=FAKE, ab_dt=1, A_log=FAKE, dt_bias=FAKE):
+    return ctypes.byref(gdn.gdn_gate_inputs(a, b, ab_dt, A_log, dt_bias))
+
+
+def _decode_gated(lib, gate, batch=4, flags=3):
+    return lib.gdn_decode_step_gated(FAKE, 1, gate, FAKE, batch, FAKE, 1, FAKE, None, 1, FAKE,
+                                     8, FAKE, 0, _dims(), 0.1, flags, FAKE, 1 << 30, None, None)
+
+
+def _prefill_gated(lib, gate, total=64):
+    return lib.gdn_prefill_chunked_gated(FAKE, FAKE, FAKE, 1, gate, FAKE, 1, total, FAKE, FAKE,
+                                         8, FAKE, 1, _dims(), 0.1, 2, None, 0, None, None)
+
+
+@pytest.mark.parametrize("gate,code", [
+    (None, ERR_NULL),
+    ("a", ERR_NULL), ("b", ERR_NULL), ("A_log", ERR_NULL), ("dt_bias", ERR_NULL),
+    ("dtype", ERR_DTYPE),
+])
+def test_gated_calls_reject(lib, gate, code):
+    if gate is None:
+        g = None
+    elif gate == "dtype":
+        g = _gate(ab_dt=7)
+    else:
+        g = _gate(**{gate: None})
+    assert _decode_gated(lib, g) == code
+    assert _prefill_gated(lib, g) == code
+
+
+def test_gated_calls_empty_is_ok(lib):
+    # nothing to process: the gate arrays are not needed (batch 0 / zero tokens, no sequences)
+    g = _gate(a=None, b=None, A_log=None, dt_bias=None)
+    assert lib.gdn_decode_step_gated(None, 1, g, None, 0, None, 1, None, None, 1, None, 8, None,
+                                     0, _dims(), 0.1, 3, None, 0, None, None) == OK
+    assert lib.gdn_prefill_chunked_gated(None, None, None, 1, g, None, 0, 0, None, None, 8, None,
+                                         1, _dims(), 0.1, 2, None, 0, None, None) == OK
