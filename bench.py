@@ -357,8 +357,7 @@ def main():
     else:
         g_big_g, r_big_g = big.capture(args.validate)
         ms_big_g = time_graph(torch, g_big_g, r_big_g, args.steps, args.warmup)
-    ms_pre_g = time_loop(torch, lambda: pre.step(args.validate), max(3, args.steps // 4),
-                         max(1, args.warmup // 4))
+    ms_pre_g = time_loop(torch, lambda: pre.step(args.validate), args.steps, args.warmup)
     torch.cuda.synchronize()
 
     mean = lambda xs: sum(xs) / len(xs)  # noqa: E731

@@ -252,7 +252,7 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
     const int cg = tid >> 5;                     // 0..CG-1
     const int ta = 2 * tp;
     uint4 pk[CP][2][WPE], pq[CP][2][WPE], pv[CP][2][WPE];
-    float pbeta = 0.0f, pg = 0.0f;
+    uint32_t pbeta = 0, pg = 0;                  // raw bits of the chunk's gate inputs
     const GateHead gh = gate_head(ga, hv);       // per-head gating constants, loaded once
     // Loads go through buffer descriptors over the chunk's rows (the entry
     // point's dims bound a chunk's span, 64 HV D elements, below 2^28 bytes),
@@ -291,12 +291,13 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
         const rsrc_t r0 = make_rsrc(s0 + static_cast<size_t>(c) * HV * es, Lc * HV * es);
         const rsrc_t r1 = make_rsrc(s1 + static_cast<size_t>(c) * HV * es, Lc * HV * es);
         const uint32_t ob = static_cast<uint32_t>(min(tid, CH) * HV + hv) * es;
+        // raw bits only: converting here would wait for every load issued above
         if (half) {
-            pg = bf16_to_f32(buf_ld2(r0, ob));
-            pbeta = bf16_to_f32(buf_ld2(r1, ob));
+            pg = buf_ld2(r0, ob);
+            pbeta = buf_ld2(r1, ob);
         } else {
-            pg = buf_ld4f(r0, ob);
-            pbeta = buf_ld4f(r1, ob);
+            pg = __builtin_amdgcn_raw_buffer_load_b32(r0, ob, 0, 0);
+            pbeta = __builtin_amdgcn_raw_buffer_load_b32(r1, ob, 0, 0);
         }
     };
     fetch(t0, min(CH, t1 - t0));
@@ -334,7 +335,9 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
         }
         if (wave == 0) {                         // gate, then the cumulative log-decay:
             float gt, bv;                        // fixed-order DPP wave scan
-            gate_finish(ga, gh, pg, pbeta, gt, bv);
+            const bool half = ga.a != nullptr && ga.ab_bf16;
+            gate_finish(ga, gh, half ? bf16_to_f32(static_cast<bf16_t>(pg)) : __uint_as_float(pg),
+                        half ? bf16_to_f32(static_cast<bf16_t>(pbeta)) : __uint_as_float(pbeta), gt, bv);
             if (lane >= L) { gt = 0.0f; bv = 0.0f; }   // rows past the chunk (raw values read as 0)
             sm.beta[lane] = bv;
             gt += dpp_scan_step<0x111, 0xF>(gt);     // row_shr:1 .. row_shr:8 inside each 16-lane row
