@@ -191,6 +191,44 @@ class DecodeSetup:
                                  self.dims, self.scale)
 
 
+class MixedSetup:
+    """A mixed step on the batch-256 decode workload's caches: its first slot
+    set's 256 decode rows plus two 1024-token prefill sequences on slots that
+    no decode slot set uses."""
+
+    def __init__(self, big, seed, dev):
+        import torch
+        import gdn_inputs as gi
+        self.torch, self.gdn, self.big = torch, big.gdn, big
+        self.lengths = [1024, 1024]
+        T = sum(self.lengths)
+        gen = torch.Generator().manual_seed(seed)
+        xp = torch.randn(T, D, generator=gen).to(torch.bfloat16)
+        gp = -torch.rand(T, HV, generator=gen)
+        bp = torch.sigmoid(torch.randn(T, HV, generator=gen))
+        d = big.d
+        self.x = torch.cat([d["mixed_qkv"], xp.to(dev)])
+        self.g = torch.cat([d["g"], gp.to(dev)])
+        self.beta = torch.cat([d["beta"], bp.to(dev)])
+        used = set(torch.cat(big.slot_sets).tolist())
+        spare = [s for s in range(1, d["rec_state"].shape[0]) if s not in used][:2]
+        self.slots = torch.cat([big.slot_sets[0],
+                                torch.tensor(spare, dtype=torch.int32, device=dev)])
+        self.cu = gi.cu_from_lengths(self.lengths).to(dev)
+        self.out = torch.empty(256 + T, HV, DV, device=dev)
+        dims = big.dims
+        self.ws = torch.empty(big.gdn.gdn_mixed_workspace_size(dims, 256, T), dtype=torch.uint8,
+                              device=dev)
+        self.T = T
+
+    def step(self):
+        b = self.big
+        d = b.d
+        self.gdn.gdn_mixed_step(self.x, self.g, self.beta, 256, self.cu, self.slots,
+                                d["conv_state"], d["conv_weight"], d["rec_state"], self.out,
+                                b.dims, b.scale, workspace=self.ws)
+
+
 class PrefillSetup:
     """The varlen prefill workload: 8 sequences, lengths uniform in [512, 8192]."""
 
@@ -349,6 +387,9 @@ def main():
     big.prepare_rec()
     ms_rec = time_loop(torch, big.rec_step, args.steps, args.warmup)
     torch.cuda.synchronize()
+    # a mixed step: the batch-256 decode rows plus two 1024-token prefills
+    mixed = MixedSetup(big, seed=9, dev="cuda")
+    ms_mixed = time_loop(torch, mixed.step, args.steps, args.warmup)
     # the same batch-256 step and prefill with the gating fused in (raw a, b)
     big.use_gating(seed=7)
     pre.use_gating(seed=8)
@@ -395,6 +436,9 @@ def main():
         "prefill_pct_mfma_peak": round(100 * pre_tflops / BF16_PEAK_TFLOPS, 2),
         "prefill_algorithmic_flops": pre_flops, "prefill_algorithmic_bytes": pre_bytes,
         "prefill_pct_hbm_peak": round(100 * pre_bytes / (pre_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+        "mixed_step_ms_mean": round(mean(ms_mixed), 4),
+        "mixed_step_note": ("gdn_mixed_step, eager: the 256 decode rows of the batch-256 "
+                            "workload plus two 1024-token prefill sequences (pre-conv input)"),
         "decode_b256_gated_ms_mean": round(mean(ms_big_g), 5),
         "decode_b256_gated_GBps": round(step_bytes_big_gated / (mean(ms_big_g) * 1e-3) / 1e9, 2),
         "prefill_gated_ms_mean": round(mean(ms_pre_g), 4),

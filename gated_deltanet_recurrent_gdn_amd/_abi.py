@@ -28,7 +28,7 @@ _STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_DIMS", 3: "GDN_ERR_DTYPE"
 EXPORTED = ["gdn_conv_update", "gdn_decode_workspace_size", "gdn_decode_step",
             "gdn_decode_step_gated", "gdn_decode_recurrent",
             "gdn_prefill_workspace_size", "gdn_prefill_chunked", "gdn_prefill_chunked_gated",
-            "gdn_strerror"]
+            "gdn_mixed_workspace_size", "gdn_mixed_step", "gdn_strerror"]
 
 
 class GDNError(RuntimeError):
@@ -88,10 +88,15 @@ def load_library(path: str = None):
                                           D, f32, i32, P, sz, P, P]
     lib.gdn_prefill_chunked_gated.argtypes = [P, P, P, i32, G, P, i32, i32, P, P, i32, P, i32,
                                               D, f32, i32, P, sz, P, P]
+    lib.gdn_mixed_workspace_size.argtypes = [D, i32, i32]
+    lib.gdn_mixed_workspace_size.restype = sz
+    lib.gdn_mixed_step.argtypes = [P, i32, P, P, i32, P, i32, i32, P, P, i32, P, P, i32, P, i32,
+                                   P, i32, D, f32, i32, P, sz, P, P]
     lib.gdn_strerror.argtypes = [i32]
     lib.gdn_strerror.restype = ctypes.c_char_p
     for f in (lib.gdn_conv_update, lib.gdn_decode_step, lib.gdn_decode_recurrent,
-              lib.gdn_prefill_chunked, lib.gdn_decode_step_gated, lib.gdn_prefill_chunked_gated):
+              lib.gdn_prefill_chunked, lib.gdn_decode_step_gated, lib.gdn_prefill_chunked_gated,
+              lib.gdn_mixed_step):
         f.restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -310,3 +315,48 @@ def gdn_prefill_chunked_gated(q, k, v, gate: GateInputs, cu_seqlens, slot_idx, r
     """gdn_prefill_chunked with the gating fused in (gdn.h: gdn_prefill_chunked_gated)."""
     return _prefill("gdn_prefill_chunked_gated", q, k, v, None, gate, cu_seqlens, slot_idx,
                     rec_state, out, dims, scale, flags, workspace, err_flag, stream)
+
+
+def gdn_mixed_workspace_size(dims: gdn_dims, n_dec: int, total_pre: int) -> int:
+    return int(load_library().gdn_mixed_workspace_size(ctypes.byref(dims), int(n_dec),
+                                                        int(total_pre)))
+
+
+def gdn_mixed_step(x, g, beta, n_dec, cu_seqlens, slot_idx, conv_state, conv_weight, rec_state,
+                   out, dims: gdn_dims, scale, conv_bias=None, flags=DEFAULT_DECODE_FLAGS,
+                   workspace=None, err_flag=None, stream=None):
+    """One step with ``n_dec`` decode rows followed by prefill sequences
+    (gdn.h: gdn_mixed_step).  ``x`` [n_dec + T, D] pre-conv, ``cu_seqlens``
+    [n_pre + 1] over the T prefill tokens (or None), ``slot_idx`` [n_dec + n_pre],
+    ``out`` [n_dec + T, HV, dv].  Caches updated in place."""
+    lib = load_library()
+    rows = x.shape[0]
+    HV, dk, dv = dims.num_v_heads, dims.head_k_dim, dims.head_v_dim
+    D = 2 * dims.num_k_heads * dk + HV * dv
+    n_dec = int(n_dec)
+    T = rows - n_dec
+    n_pre = 0 if cu_seqlens is None else cu_seqlens.shape[0] - 1
+    _dev(x, "x", shape=(rows, D))
+    _dev(g, "g", torch.float32, (rows, HV)); _dev(beta, "beta", torch.float32, (rows, HV))
+    _dev(cu_seqlens, "cu_seqlens", torch.int32, None if cu_seqlens is None else (n_pre + 1,))
+    _dev(slot_idx, "slot_idx", torch.int32, (n_dec + n_pre,))
+    _dev(conv_state, "conv_state"); _dev(conv_weight, "conv_weight")
+    _dev(conv_bias, "conv_bias", conv_weight.dtype)
+    _dev(rec_state, "rec_state", torch.float32)
+    _dev(out, "out", shape=(rows, HV, dv)); _dev(err_flag, "err_flag", torch.int32)
+    ns = rec_state.shape[0]
+    if tuple(rec_state.shape[1:]) != (HV, dv, dk):
+        raise ValueError("rec_state must be [num_slots, HV, dv, dk]")
+    if tuple(conv_state.shape) != (ns, D, dims.conv_width - 1):
+        raise ValueError("conv_state must be [num_slots, D, W-1] with the rec_state slot count")
+    need = gdn_mixed_workspace_size(dims, n_dec, T)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _dev(workspace, "workspace")
+    _check("gdn_mixed_step", lib.gdn_mixed_step(
+        _p(x), _dt(x), _p(g), _p(beta), n_dec, _p(cu_seqlens), n_pre, T, _p(slot_idx),
+        _p(conv_state), _dt(conv_state), _p(conv_weight), _p(conv_bias), _dt(conv_weight),
+        _p(rec_state), ns, _p(out), _dt(out), ctypes.byref(dims), float(scale), flags,
+        _p(workspace), workspace.numel() * workspace.element_size(), _p(err_flag),
+        _stream(stream)))
+    return out

@@ -85,7 +85,7 @@ gdn_status gdn_conv_update(const void* x, gdn_dtype x_dt, const int32_t* cu_seql
         return GDN_ERR_ALIGN;
     auto s = static_cast<hipStream_t>(stream);
     if (flags & GDN_FLAG_VALIDATE)
-        GDN_TRY_LAUNCH(launch_validate(slot_idx, n_seqs, num_slots, cu_seqlens, total_tokens,
+        GDN_TRY_LAUNCH(launch_validate(slot_idx, n_seqs, num_slots, cu_seqlens, n_seqs, total_tokens,
                                        err_flag, s));
     const int32_t* ef = (flags & GDN_FLAG_VALIDATE) ? err_flag : nullptr;
     if (cu_seqlens)
@@ -122,6 +122,34 @@ gdn_status gate_args(const float* g, const float* beta, const gdn_gate_inputs* g
     return GDN_OK;
 }
 
+// The decode step's kernels for `batch` rows (after the checks and the
+// optional validation): the fused kernel or the conv + recurrence pair.
+gdn_status decode_step_launch(const void* mixed_qkv, gdn_dtype x_dt, const GateArgs& ga,
+                              const int32_t* slot_idx, int32_t batch, void* conv_state,
+                              gdn_dtype cs_dt, const void* conv_weight, const void* conv_bias,
+                              gdn_dtype w_dt, float* rec_state, void* out, gdn_dtype out_dt,
+                              const gdn_dims* dims, float scale, int32_t flags, void* workspace,
+                              const int32_t* ef, hipStream_t s) {
+    if (batch == 0) return GDN_OK;
+    const int32_t kflags = flags & ~(GDN_FLAG_STEP_FUSED | GDN_FLAG_STEP_SPLIT);
+    const bool fused = (flags & GDN_FLAG_STEP_FUSED) ||
+                       (!(flags & GDN_FLAG_STEP_SPLIT) && decode_step_use_fused(*dims, batch));
+    if (fused) {
+        GDN_TRY_LAUNCH(launch_decode_step_fused(mixed_qkv, x_dt, ga, slot_idx, batch, conv_state,
+                                                cs_dt, conv_weight, conv_bias, w_dt, rec_state, out,
+                                                out_dt, *dims, scale, kflags, ef, s));
+        return GDN_OK;
+    }
+    const int32_t D = static_cast<int32_t>(conv_channels(dims));
+    float* y = static_cast<float*>(workspace);
+    GDN_TRY_LAUNCH(launch_conv_decode(mixed_qkv, x_dt, slot_idx, batch, conv_state, cs_dt,
+                                      conv_weight, conv_bias, w_dt, y, GDN_F32, D,
+                                      kflags & GDN_FLAG_SILU, ef, s));
+    GDN_TRY_LAUNCH(launch_decode_rec(y, GDN_F32, ga, slot_idx, batch, rec_state, out,
+                                     out_dt, *dims, scale, kflags, ef, s));
+    return GDN_OK;
+}
+
 gdn_status decode_step_impl(const void* mixed_qkv, gdn_dtype x_dt, const float* g,
                             const float* beta, const gdn_gate_inputs* gate,
                             const int32_t* slot_idx, int32_t batch, void* conv_state,
@@ -153,26 +181,11 @@ gdn_status decode_step_impl(const void* mixed_qkv, gdn_dtype x_dt, const float* 
     }
     auto s = static_cast<hipStream_t>(stream);
     if (flags & GDN_FLAG_VALIDATE)
-        GDN_TRY_LAUNCH(launch_validate(slot_idx, batch, num_slots, nullptr, 0, err_flag, s));
-    if (batch == 0) return GDN_OK;
+        GDN_TRY_LAUNCH(launch_validate(slot_idx, batch, num_slots, nullptr, 0, 0, err_flag, s));
     const int32_t* ef = (flags & GDN_FLAG_VALIDATE) ? err_flag : nullptr;
-    const int32_t kflags = flags & ~(GDN_FLAG_STEP_FUSED | GDN_FLAG_STEP_SPLIT);
-    const bool fused = (flags & GDN_FLAG_STEP_FUSED) ||
-                       (!(flags & GDN_FLAG_STEP_SPLIT) && decode_step_use_fused(*dims, batch));
-    if (fused) {
-        GDN_TRY_LAUNCH(launch_decode_step_fused(mixed_qkv, x_dt, ga, slot_idx, batch, conv_state,
-                                                cs_dt, conv_weight, conv_bias, w_dt, rec_state, out,
-                                                out_dt, *dims, scale, kflags, ef, s));
-        return GDN_OK;
-    }
-    const int32_t D = static_cast<int32_t>(conv_channels(dims));
-    float* y = static_cast<float*>(workspace);
-    GDN_TRY_LAUNCH(launch_conv_decode(mixed_qkv, x_dt, slot_idx, batch, conv_state, cs_dt,
-                                      conv_weight, conv_bias, w_dt, y, GDN_F32, D,
-                                      kflags & GDN_FLAG_SILU, ef, s));
-    GDN_TRY_LAUNCH(launch_decode_rec(y, GDN_F32, ga, slot_idx, batch, rec_state, out,
-                                     out_dt, *dims, scale, kflags, ef, s));
-    return GDN_OK;
+    return decode_step_launch(mixed_qkv, x_dt, ga, slot_idx, batch, conv_state, cs_dt, conv_weight,
+                              conv_bias, w_dt, rec_state, out, out_dt, dims, scale, flags,
+                              workspace, ef, s);
 }
 
 gdn_status prefill_impl(const void* q, const void* k, const void* v, gdn_dtype in_dt,
@@ -196,11 +209,13 @@ gdn_status prefill_impl(const void* q, const void* k, const void* v, gdn_dtype i
         return GDN_ERR_ALIGN;
     auto s = static_cast<hipStream_t>(stream);
     if (flags & GDN_FLAG_VALIDATE)
-        GDN_TRY_LAUNCH(launch_validate(slot_idx, n_seqs, num_slots, cu_seqlens, total_tokens,
+        GDN_TRY_LAUNCH(launch_validate(slot_idx, n_seqs, num_slots, cu_seqlens, n_seqs, total_tokens,
                                        err_flag, s));
     const int32_t* ef = (flags & GDN_FLAG_VALIDATE) ? err_flag : nullptr;
     GDN_TRY_LAUNCH(launch_prefill(q, k, v, in_dt, ga, cu_seqlens, n_seqs, slot_idx,
-                                  rec_state, out, out_dt, *dims, scale, flags, ef, s));
+                                  rec_state, out, out_dt, *dims,
+                                  dims->num_k_heads * dims->head_k_dim,
+                                  dims->num_v_heads * dims->head_v_dim, scale, flags, ef, s));
     return GDN_OK;
 }
 
@@ -255,7 +270,7 @@ gdn_status gdn_decode_recurrent(const void* qkv, gdn_dtype qkv_dt, const float* 
     }
     auto s = static_cast<hipStream_t>(stream);
     if (flags & GDN_FLAG_VALIDATE)
-        GDN_TRY_LAUNCH(launch_validate(slot_idx, batch, num_slots, nullptr, 0, err_flag, s));
+        GDN_TRY_LAUNCH(launch_validate(slot_idx, batch, num_slots, nullptr, 0, 0, err_flag, s));
     const int32_t* ef = (flags & GDN_FLAG_VALIDATE) ? err_flag : nullptr;
     GDN_TRY_LAUNCH(launch_decode_rec(qkv, qkv_dt, ga, slot_idx, batch, rec_state, out,
                                      out_dt, *dims, scale, flags, ef, s));
@@ -293,6 +308,87 @@ gdn_status gdn_prefill_chunked_gated(const void* q, const void* k, const void* v
     return prefill_impl(q, k, v, in_dt, nullptr, nullptr, gate, cu_seqlens, n_seqs,
                         total_tokens, slot_idx, rec_state, num_slots, out, out_dt, dims, scale,
                         flags, err_flag, stream);
+}
+
+size_t gdn_mixed_workspace_size(const gdn_dims* dims, int32_t n_dec, int32_t total_pre) {
+    if (check_dims(dims) != GDN_OK || n_dec < 0 || total_pre < 0) return 0;
+    const size_t D = static_cast<size_t>(conv_channels(dims));
+    return round256(static_cast<size_t>(n_dec) * D * sizeof(float)) +
+           round256(static_cast<size_t>(total_pre) * D * sizeof(uint16_t));
+}
+
+gdn_status gdn_mixed_step(const void* x, gdn_dtype x_dt, const float* g, const float* beta,
+                          int32_t n_dec, const int32_t* cu_seqlens, int32_t n_pre,
+                          int32_t total_pre, const int32_t* slot_idx, void* conv_state,
+                          gdn_dtype cs_dt, const void* conv_weight, const void* conv_bias,
+                          gdn_dtype w_dt, float* rec_state, int32_t num_slots, void* out,
+                          gdn_dtype out_dt, const gdn_dims* dims, float scale, int32_t flags,
+                          void* workspace, size_t workspace_bytes, int32_t* err_flag,
+                          void* stream) {
+    if (gdn_status st = check_flags(flags, KNOWN_FLAGS | GDN_FLAG_STEP_FUSED | GDN_FLAG_STEP_SPLIT,
+                                    err_flag))
+        return st;
+    if ((flags & GDN_FLAG_STEP_FUSED) && (flags & GDN_FLAG_STEP_SPLIT)) return GDN_ERR_FLAGS;
+    if (gdn_status st = check_dims(dims)) return st;
+    if (n_dec < 0 || n_pre < 0 || total_pre < 0 || num_slots < 1) return GDN_ERR_DIMS;
+    if (static_cast<int64_t>(n_dec) + n_pre > 65535) return GDN_ERR_DIMS;
+    if (static_cast<int64_t>(n_dec) * dims->num_v_heads > (1 << 24)) return GDN_ERR_DIMS;
+    if (static_cast<int64_t>(n_dec) + total_pre > (1LL << 31) - 1) return GDN_ERR_DIMS;
+    if ((flags & GDN_FLAG_STEP_FUSED) && !decode_step_fused_fits(*dims)) return GDN_ERR_DIMS;
+    if (n_pre > 0 && (dims->head_k_dim != dims->head_v_dim || dims->head_k_dim > 128 ||
+                      !prefill_supported(*dims, GDN_BF16)))
+        return GDN_ERR_DIMS;
+    if (!dtype_ok(x_dt) || !dtype_ok(cs_dt) || !dtype_ok(w_dt) || !dtype_ok(out_dt))
+        return GDN_ERR_DTYPE;
+    const int64_t rows = static_cast<int64_t>(n_dec) + total_pre;
+    GateArgs ga;
+    if (gdn_status st = gate_args(g, beta, nullptr, rows > 0, ga)) return st;
+    if (n_dec + n_pre > 0 && (!slot_idx || !conv_state || !conv_weight || !rec_state))
+        return GDN_ERR_NULL;
+    if (n_pre > 0 && !cu_seqlens) return GDN_ERR_NULL;
+    if (rows > 0 && (!x || !out || !workspace)) return GDN_ERR_NULL;
+    if (!aligned16(x) || !aligned16(rec_state) || !aligned16(workspace) || !aligned16(conv_state) ||
+        !aligned16(conv_weight) || (conv_bias && !aligned16(conv_bias)))
+        return GDN_ERR_ALIGN;
+    if (rows > 0 && workspace_bytes < gdn_mixed_workspace_size(dims, n_dec, total_pre))
+        return GDN_ERR_WORKSPACE;
+    auto s = static_cast<hipStream_t>(stream);
+    if (flags & GDN_FLAG_VALIDATE)
+        GDN_TRY_LAUNCH(launch_validate(slot_idx, n_dec + n_pre, num_slots, n_pre > 0 ? cu_seqlens : nullptr,
+                                       n_pre, total_pre, err_flag, s));
+    const int32_t* ef = (flags & GDN_FLAG_VALIDATE) ? err_flag : nullptr;
+    const int32_t D = static_cast<int32_t>(conv_channels(dims));
+    const int32_t HV = dims->num_v_heads, dv = dims->head_v_dim;
+    const size_t esx = (x_dt == GDN_BF16) ? 2 : 4;
+    const size_t eso = (out_dt == GDN_BF16) ? 2 : 4;
+
+    // decode rows: exactly the decode-only step's kernels (rows 0 .. n_dec-1)
+    if (gdn_status st = decode_step_launch(x, x_dt, ga, slot_idx, n_dec, conv_state, cs_dt,
+                                           conv_weight, conv_bias, w_dt, rec_state, out, out_dt,
+                                           dims, scale, flags, workspace, ef, s))
+        return st;
+    if (n_pre == 0 || total_pre == 0) {
+        // sequences without tokens leave their state untouched: nothing to launch
+        return GDN_OK;
+    }
+    // prefill tokens (rows n_dec ..): varlen conv into bf16 activations, then
+    // the chunked prefill reading q, k, v as slices of those rows
+    const char* xp = static_cast<const char*>(x) + static_cast<size_t>(n_dec) * D * esx;
+    uint16_t* yp = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) +
+                                           round256(static_cast<size_t>(n_dec) * D * sizeof(float)));
+    const int32_t* sp = slot_idx + n_dec;
+    GDN_TRY_LAUNCH(launch_conv_varlen(xp, x_dt, cu_seqlens, n_pre, sp, conv_state, cs_dt,
+                                      conv_weight, conv_bias, w_dt, yp, GDN_BF16, D,
+                                      flags & GDN_FLAG_SILU, ef, s));
+    GateArgs gp = ga;
+    gp.g = ga.g + static_cast<size_t>(n_dec) * HV;
+    gp.beta = ga.beta + static_cast<size_t>(n_dec) * HV;
+    const int32_t Hdk = dims->num_k_heads * dims->head_k_dim;
+    void* op = static_cast<char*>(out) + static_cast<size_t>(n_dec) * HV * dv * eso;
+    GDN_TRY_LAUNCH(launch_prefill(yp, yp + Hdk, yp + 2 * Hdk, GDN_BF16, gp, cu_seqlens, n_pre, sp,
+                                  rec_state, op, out_dt, *dims, D, D, scale,
+                                  flags & (GDN_FLAG_QK_L2NORM), ef, s));
+    return GDN_OK;
 }
 
 }  // extern "C"

@@ -39,10 +39,10 @@ struct GateArgs {
 };
 
 // Writes *err_flag (0 or GDN_EFLAG_* bits) for n slot indices and, when cu is
-// non-null, cu_seqlens[n + 1] against total.
+// non-null, cu_seqlens[n_cu + 1] against total.
 hipError_t launch_validate(const int32_t* slot_idx, int32_t n, int32_t num_slots,
-                           const int32_t* cu_seqlens, int32_t total, int32_t* err_flag,
-                           hipStream_t stream);
+                           const int32_t* cu_seqlens, int32_t n_cu, int32_t total,
+                           int32_t* err_flag, hipStream_t stream);
 
 // Conv update, one token per row (decode).  out_dt may be GDN_F32 / GDN_BF16.
 hipError_t launch_conv_decode(const void* x, gdn_dtype x_dt, const int32_t* slot_idx,
@@ -79,10 +79,12 @@ hipError_t launch_decode_step_fused(const void* x, gdn_dtype x_dt, const GateArg
 
 // Chunked prefill: one workgroup per (sequence, value head).
 bool prefill_supported(const gdn_dims& d, gdn_dtype in_dt);
+// q, k rows are sqk elements apart and v rows sv (H dk and HV dv for separate
+// tensors; the conv width when they are slices of one activation row).
 hipError_t launch_prefill(const void* q, const void* k, const void* v, gdn_dtype in_dt,
                           const GateArgs& gate, const int32_t* cu, int32_t n_seqs,
                           const int32_t* slot, float* rec, void* out, gdn_dtype out_dt,
-                          const gdn_dims& d, float scale, int32_t flags, const int32_t* err,
-                          hipStream_t st);
+                          const gdn_dims& d, int32_t sqk, int32_t sv, float scale, int32_t flags,
+                          const int32_t* err, hipStream_t st);
 
 }  // namespace gdn

@@ -186,7 +186,8 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
     const IT* __restrict__ qg, const IT* __restrict__ kg, const IT* __restrict__ vg,
     const GateArgs ga, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ slot, float* __restrict__ rec, OT* __restrict__ out, int32_t H,
-    int32_t HV, float scale, int32_t flags, const int32_t* __restrict__ err_flag) {
+    int32_t HV, int32_t sqk, int32_t sv, float scale, int32_t flags,
+    const int32_t* __restrict__ err_flag) {
     constexpr bool SPL = sizeof(IT) == 4;        // fp32 inputs: hi/lo planes
     constexpr int NP = SPL ? 2 : 1;
     static_assert(D == 32 || D == 64 || D == 128, "head dim");
@@ -257,14 +258,16 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
     // Loads go through buffer descriptors over the chunk's rows (the entry
     // point's dims bound a chunk's span, 64 HV D elements, below 2^28 bytes),
     // so rows past the chunk's length read as zero.
+    // Token rows are sqk (q, k) and sv (v) elements apart: H D and HV D for
+    // separate q, k, v tensors, the conv width for slices of one activation row.
     const uint32_t off_kq = static_cast<uint32_t>(h * D) * sizeof(IT);
     const uint32_t off_v = static_cast<uint32_t>(hv * D) * sizeof(IT);
-    const uint32_t row_kq = static_cast<uint32_t>(H * D) * sizeof(IT);
-    const uint32_t row_v = static_cast<uint32_t>(HV * D) * sizeof(IT);
+    const uint32_t row_kq = static_cast<uint32_t>(sqk) * sizeof(IT);
+    const uint32_t row_v = static_cast<uint32_t>(sv) * sizeof(IT);
     auto fetch = [&](int32_t c, int Lc) {
-        const rsrc_t rk_ = make_rsrc(kg + static_cast<size_t>(c) * H * D, Lc * row_kq);
-        const rsrc_t rq_ = make_rsrc(qg + static_cast<size_t>(c) * H * D, Lc * row_kq);
-        const rsrc_t rv_ = make_rsrc(vg + static_cast<size_t>(c) * HV * D, Lc * row_v);
+        const rsrc_t rk_ = make_rsrc(kg + static_cast<size_t>(c) * sqk, Lc * row_kq);
+        const rsrc_t rq_ = make_rsrc(qg + static_cast<size_t>(c) * sqk, Lc * row_kq);
+        const rsrc_t rv_ = make_rsrc(vg + static_cast<size_t>(c) * sv, Lc * row_v);
 #pragma unroll
         for (int pass = 0; pass < CP; ++pass) {
             const int k0 = 8 * (cg + CG * pass);
@@ -781,23 +784,23 @@ namespace {
 template <int D, typename IT, typename OT>
 hipError_t run_prefill(const void* q, const void* k, const void* v, const GateArgs& ga,
                        const int32_t* cu, int32_t n_seqs, const int32_t* slot,
-                       float* rec, void* out, const gdn_dims& d, float scale, int32_t flags,
-                       const int32_t* err, hipStream_t st) {
+                       float* rec, void* out, const gdn_dims& d, int32_t sqk, int32_t sv,
+                       float scale, int32_t flags, const int32_t* err, hipStream_t st) {
     dim3 grid(d.num_v_heads, n_seqs);
     return launch(prefill_kernel<D, IT, OT>, grid, dim3(PF_NT), 0, st,
                   static_cast<const IT*>(q), static_cast<const IT*>(k),
                   static_cast<const IT*>(v), ga, cu, slot, rec, static_cast<OT*>(out),
-                  d.num_k_heads, d.num_v_heads, scale, flags, err);
+                  d.num_k_heads, d.num_v_heads, sqk, sv, scale, flags, err);
 }
 
 template <int D, typename IT>
 hipError_t pick_out(gdn_dtype out_dt, const void* q, const void* k, const void* v, const GateArgs& ga,
                     const int32_t* cu, int32_t n_seqs, const int32_t* slot,
-                    float* rec, void* out, const gdn_dims& d, float scale, int32_t flags,
-                    const int32_t* err, hipStream_t st) {
+                    float* rec, void* out, const gdn_dims& d, int32_t sqk, int32_t sv, float scale,
+                    int32_t flags, const int32_t* err, hipStream_t st) {
     return out_dt == GDN_BF16
-        ? run_prefill<D, IT, bf16_t>(q, k, v, ga, cu, n_seqs, slot, rec, out, d, scale, flags, err, st)
-        : run_prefill<D, IT, float>(q, k, v, ga, cu, n_seqs, slot, rec, out, d, scale, flags, err, st);
+        ? run_prefill<D, IT, bf16_t>(q, k, v, ga, cu, n_seqs, slot, rec, out, d, sqk, sv, scale, flags, err, st)
+        : run_prefill<D, IT, float>(q, k, v, ga, cu, n_seqs, slot, rec, out, d, sqk, sv, scale, flags, err, st);
 }
 }  // namespace
 
@@ -812,18 +815,18 @@ bool prefill_supported(const gdn_dims& d, gdn_dtype in_dt) {
 hipError_t launch_prefill(const void* q, const void* k, const void* v, gdn_dtype in_dt,
                           const GateArgs& ga, const int32_t* cu, int32_t n_seqs,
                           const int32_t* slot, float* rec, void* out, gdn_dtype out_dt,
-                          const gdn_dims& d, float scale, int32_t flags, const int32_t* err,
-                          hipStream_t st) {
+                          const gdn_dims& d, int32_t sqk, int32_t sv, float scale, int32_t flags,
+                          const int32_t* err, hipStream_t st) {
     if (n_seqs == 0) return hipSuccess;
     if (!prefill_supported(d, in_dt)) return hipErrorInvalidValue;
     const int D = d.head_k_dim;
     if (in_dt == GDN_F32) {
-        if (D == 32) return pick_out<32, float>(out_dt, q, k, v, ga, cu, n_seqs, slot, rec, out, d, scale, flags, err, st);
-        return pick_out<64, float>(out_dt, q, k, v, ga, cu, n_seqs, slot, rec, out, d, scale, flags, err, st);
+        if (D == 32) return pick_out<32, float>(out_dt, q, k, v, ga, cu, n_seqs, slot, rec, out, d, sqk, sv, scale, flags, err, st);
+        return pick_out<64, float>(out_dt, q, k, v, ga, cu, n_seqs, slot, rec, out, d, sqk, sv, scale, flags, err, st);
     }
-    if (D == 32) return pick_out<32, bf16_t>(out_dt, q, k, v, ga, cu, n_seqs, slot, rec, out, d, scale, flags, err, st);
-    if (D == 64) return pick_out<64, bf16_t>(out_dt, q, k, v, ga, cu, n_seqs, slot, rec, out, d, scale, flags, err, st);
-    return pick_out<128, bf16_t>(out_dt, q, k, v, ga, cu, n_seqs, slot, rec, out, d, scale, flags, err, st);
+    if (D == 32) return pick_out<32, bf16_t>(out_dt, q, k, v, ga, cu, n_seqs, slot, rec, out, d, sqk, sv, scale, flags, err, st);
+    if (D == 64) return pick_out<64, bf16_t>(out_dt, q, k, v, ga, cu, n_seqs, slot, rec, out, d, sqk, sv, scale, flags, err, st);
+    return pick_out<128, bf16_t>(out_dt, q, k, v, ga, cu, n_seqs, slot, rec, out, d, sqk, sv, scale, flags, err, st);
 }
 
 }  // namespace gdn

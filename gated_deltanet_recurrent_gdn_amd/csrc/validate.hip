@@ -16,9 +16,12 @@ namespace gdn {
 
 constexpr int VAL_THREADS = 1024;
 
+// n slot indices; cu (when non-null) describes n_cu sequences (n_cu + 1 offsets)
+// over `total` tokens -- n_cu == n except in a mixed step, whose slot list also
+// holds the decode rows before the prefill sequences.
 __global__ __launch_bounds__(VAL_THREADS) void validate_kernel(
     const int32_t* __restrict__ slot, int32_t n, int32_t num_slots,
-    const int32_t* __restrict__ cu, int32_t total, int32_t* __restrict__ err_flag) {
+    const int32_t* __restrict__ cu, int32_t n_cu, int32_t total, int32_t* __restrict__ err_flag) {
     __shared__ int32_t tile[VAL_THREADS];
     __shared__ int32_t bits_sh;
     const int tid = threadIdx.x;
@@ -27,9 +30,12 @@ __global__ __launch_bounds__(VAL_THREADS) void validate_kernel(
     for (int i = tid; i < n; i += VAL_THREADS) {
         const int32_t s = slot[i];
         if (s > 0 && s >= num_slots) bits |= GDN_EFLAG_SLOT_RANGE;
-        if (cu != nullptr && cu[i + 1] < cu[i]) bits |= GDN_EFLAG_SEQLENS;
     }
-    if (cu != nullptr && tid == 0 && (cu[0] != 0 || cu[n] != total)) bits |= GDN_EFLAG_SEQLENS;
+    if (cu != nullptr) {
+        for (int i = tid; i < n_cu; i += VAL_THREADS)
+            if (cu[i + 1] < cu[i]) bits |= GDN_EFLAG_SEQLENS;
+        if (tid == 0 && (cu[0] != 0 || cu[n_cu] != total)) bits |= GDN_EFLAG_SEQLENS;
+    }
 
     for (int i0 = 0; i0 < n; i0 += VAL_THREADS) {          // uniform loop
         const int i = i0 + tid;
@@ -52,10 +58,10 @@ __global__ __launch_bounds__(VAL_THREADS) void validate_kernel(
 }
 
 hipError_t launch_validate(const int32_t* slot_idx, int32_t n, int32_t num_slots,
-                           const int32_t* cu_seqlens, int32_t total, int32_t* err_flag,
-                           hipStream_t stream) {
+                           const int32_t* cu_seqlens, int32_t n_cu, int32_t total,
+                           int32_t* err_flag, hipStream_t stream) {
     return launch(validate_kernel, dim3(1), dim3(VAL_THREADS), 0, stream, slot_idx, n,
-                  num_slots, cu_seqlens, total, err_flag);
+                  num_slots, cu_seqlens, n_cu, total, err_flag);
 }
 
 }  // namespace gdn

@@ -11,6 +11,9 @@
  *   gdn_decode_step_gated, gdn_prefill_chunked_gated
  *                        the same two calls with the gating fused in: g and
  *                        beta computed in-kernel from the raw projections
+ *   gdn_mixed_step       one step holding decode rows and prefill sequences,
+ *                        the decode rows computed exactly as in a decode-only
+ *                        step
  *
  * Sources (pages, by title and section):
  *   [P1] RL-Kernel PR #469 "C6: GDN decode-step goldens and recurrent/conv
@@ -284,6 +287,64 @@ gdn_status gdn_prefill_chunked_gated(const void* q, const void* k, const void* v
                                      const gdn_dims* dims, float scale, int32_t flags,
                                      void* workspace, size_t workspace_bytes,
                                      int32_t* err_flag, void* stream);
+
+/*
+ * gdn_mixed_workspace_size -- bytes of device workspace gdn_mixed_step needs:
+ * the decode rows' fp32 activations (n_dec * D * 4) and the prefill tokens'
+ * bf16 activations (total_pre * D * 2), each rounded up to 256.  0 for
+ * unsupported dims or negative sizes.
+ */
+size_t gdn_mixed_workspace_size(const gdn_dims* dims, int32_t n_dec, int32_t total_pre);
+
+/*
+ * gdn_mixed_step -- one serving step that holds both cached decode rows and
+ * prefill sequences ([P1] "Not reproducible from this branch: the mixed
+ * decode+prefill measurement": with the decode rows of a mixed step routed
+ * through a different recurrent kernel, their state depended on the step's
+ * composition; the proposed fix routes them through the decode kernel and
+ * aligns non-final chunked-prefill calls to the 64-token grid).
+ *
+ * The decode rows run exactly the kernels of gdn_decode_step for n_dec rows,
+ * so every decode row's output, recurrent state and conv state are bitwise
+ * independent of what else the step holds.  The prefill tokens go through
+ * the varlen conv (SiLU per flags) into bf16 activations -- the serving path's
+ * convention -- and then the chunked prefill.  A sequence prefilled over
+ * several calls equals one whole prefill bitwise when every non-final call
+ * covers a multiple of 64 of its tokens (the chunk grid then coincides).
+ *
+ *   x            [n_dec + total_pre, D], x_dt: the n_dec decode rows, then the
+ *                prefill tokens (pre-conv mixed q | k | v)
+ *   g, beta      [n_dec + total_pre, HV] fp32, in the same row order
+ *   n_dec        decode rows (one token each)
+ *   cu_seqlens   [n_pre + 1] offsets of the prefill sequences within the
+ *                total_pre prefill tokens (cu_seqlens[0] == 0); may be NULL
+ *                when n_pre == 0
+ *   slot_idx     [n_dec + n_pre]: the decode rows' slots, then the prefill
+ *                sequences'; <= 0 inactive; active slots distinct across
+ *                both parts
+ *   conv_state, conv_weight, conv_bias, rec_state, num_slots, scale:
+ *                as for gdn_decode_step (the prefill part reads and rolls
+ *                the same conv cache and recurrent cache)
+ *   out          [n_dec + total_pre, HV, dv], out_dt
+ *   flags        GDN_FLAG_SILU | GDN_FLAG_QK_L2NORM | GDN_FLAG_VALIDATE (one
+ *                validation over all slot indices and cu_seqlens), and the
+ *                decode rows' GDN_FLAG_STEP_FUSED / GDN_FLAG_STEP_SPLIT
+ *   workspace    >= gdn_mixed_workspace_size(dims, n_dec, total_pre) bytes
+ * The prefill part needs dk == dv <= 128 (GDN_ERR_DIMS otherwise, when
+ * n_pre > 0).
+ */
+gdn_status gdn_mixed_step(const void* x, gdn_dtype x_dt,
+                          const float* g, const float* beta,
+                          int32_t n_dec,
+                          const int32_t* cu_seqlens, int32_t n_pre, int32_t total_pre,
+                          const int32_t* slot_idx,
+                          void* conv_state, gdn_dtype cs_dt,
+                          const void* conv_weight, const void* conv_bias, gdn_dtype w_dt,
+                          float* rec_state, int32_t num_slots,
+                          void* out, gdn_dtype out_dt,
+                          const gdn_dims* dims, float scale, int32_t flags,
+                          void* workspace, size_t workspace_bytes,
+                          int32_t* err_flag, void* stream);
 
 /* gdn_strerror -- static, NUL-terminated description of a status code. */
 const char* gdn_strerror(gdn_status s);

@@ -169,3 +169,39 @@ def test_gated_calls_empty_is_ok(lib):
                                      0, _dims(), 0.1, 3, None, 0, None, None) == OK
     assert lib.gdn_prefill_chunked_gated(None, None, None, 1, g, None, 0, 0, None, None, 8, None,
                                          1, _dims(), 0.1, 2, None, 0, None, None) == OK
+
+
+def _mixed(lib, dims=None, n_dec=2, cu=FAKE, n_pre=1, total=64, flags=3, ws=FAKE,
+           ws_bytes=1 << 30, err=None):
+    return lib.gdn_mixed_step(FAKE, 1, FAKE, FAKE, n_dec, cu, n_pre, total, FAKE, FAKE, 1, FAKE,
+                              None, 1, FAKE, 8, FAKE, 0, dims or _dims(), 0.1, flags, ws,
+                              ws_bytes, err, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(flags=3 | 8 | 16), ERR_FLAGS),
+    (dict(flags=64), ERR_FLAGS),
+    (dict(n_dec=-1), ERR_DIMS),
+    (dict(n_pre=-1), ERR_DIMS),
+    (dict(dims=_dims(dk=256, dv=256)), ERR_DIMS),      # prefill part needs d <= 128
+    (dict(dims=_dims(dk=128, dv=64)), ERR_DIMS),       # and dk == dv
+    (dict(cu=None), ERR_NULL),
+    (dict(ws=None), ERR_NULL),
+    (dict(ws_bytes=16), ERR_WS),
+])
+def test_mixed_step_rejects(lib, kw, code):
+    assert _mixed(lib, **kw) == code
+
+
+def test_mixed_step_decode_only_dims_ok_without_prefill(lib):
+    # d = 256 is fine when the step holds no prefill sequence (rejected later
+    # only by the null test pointers, which the empty call never touches)
+    assert _mixed(lib, dims=_dims(dk=256, dv=256), n_dec=0, n_pre=0, total=0, cu=None,
+                  ws=None) == OK
+
+
+def test_mixed_workspace_size(lib):
+    d = _dims()
+    D = 2 * 16 * 128 + 32 * 128
+    assert lib.gdn_mixed_workspace_size(d, 3, 10) == (
+        ((3 * D * 4 + 255) // 256) * 256 + ((10 * D * 2 + 255) // 256) * 256)
