@@ -20,6 +20,8 @@ from . import build as _build
 
 FLAG_SILU = 1
 FLAG_QK_L2NORM = 2
+NORM_GATE_SIGMOID = 1
+NORM_ZERO_CENTRED = 2
 
 ERR_SLOT_RANGE = 1
 ERR_SLOT_REPEAT = 2
@@ -52,8 +54,9 @@ def load(path: str = None):
     lib.oracle_prefill.argtypes = [P, P, P, P, P, P, i32, i64, P, P, i32, P,
                                    i32, i32, i32, i32, f64, i32]
     lib.oracle_gating.argtypes = [P, P, P, P, i64, i32, P, P]
+    lib.oracle_gated_rmsnorm.argtypes = [P, P, P, i64, i32, ctypes.c_double, i32, P]
     for f in (lib.oracle_conv_update, lib.oracle_decode_step, lib.oracle_prefill,
-              lib.oracle_gating):
+              lib.oracle_gating, lib.oracle_gated_rmsnorm):
         f.restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -161,3 +164,22 @@ def gating(a, b, A_log, dt_bias, lib=None):
     if rc:
         raise OracleError(rc)
     return g, beta
+
+
+def gated_rmsnorm(x, weight, z=None, eps=1e-6, flags=0, lib=None):
+    """Gated RMSNorm over the last axis of ``x`` [..., dim] in fp64."""
+    lib = lib or load()
+    x = _f64(x)
+    shape = x.shape
+    dim = shape[-1]
+    rows = int(np.prod(shape[:-1])) if len(shape) > 1 else 1
+    w = _f64(weight)
+    zz = None if z is None else _f64(z)
+    if w.shape != (dim,) or (zz is not None and zz.shape != shape):
+        raise ValueError("gated_rmsnorm: weight [dim], z shaped like x")
+    out = np.full(shape, np.nan)
+    rc = lib.oracle_gated_rmsnorm(_ptr(x), _ptr(zz), _ptr(w), rows, dim, float(eps), flags,
+                                  _ptr(out))
+    if rc:
+        raise OracleError(rc)
+    return out

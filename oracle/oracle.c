@@ -265,3 +265,28 @@ int oracle_gating(const double* a, const double* b, const double* A_log,
     }
     return 0;
 }
+
+/* Gated RMSNorm: the plain definition (norm first, then weight and gate). */
+int oracle_gated_rmsnorm(const double* x, const double* z, const double* weight,
+                         int64_t rows, int32_t dim, double eps, int32_t flags, double* out)
+{
+    if (rows < 0 || dim <= 0 || eps < 0.0) return ORACLE_ERR_ARGS;
+    if (rows > 0 && (!x || !weight || !out)) return ORACLE_ERR_ARGS;
+    for (int64_t r = 0; r < rows; ++r) {
+        const double* xr = x + r * dim;
+        double ss = 0.0;
+        for (int32_t j = 0; j < dim; ++j) ss += xr[j] * xr[j];
+        const double rms = sqrt(ss / dim + eps);
+        for (int32_t j = 0; j < dim; ++j) {
+            const double w = (flags & ORACLE_NORM_ZERO_CENTRED) ? weight[j] + 1.0 : weight[j];
+            double gate = 1.0;
+            if (z) {
+                const double zj = z[r * dim + j];
+                const double sig = 1.0 / (1.0 + exp(-zj));
+                gate = (flags & ORACLE_NORM_GATE_SIGMOID) ? sig : zj * sig;
+            }
+            out[r * dim + j] = (rms > 0.0 ? xr[j] / rms : 0.0) * w * gate;
+        }
+    }
+    return 0;
+}

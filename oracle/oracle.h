@@ -117,6 +117,22 @@ int oracle_gating(const double* a, const double* b, const double* A_log,
                   const double* dt_bias, int64_t rows, int32_t num_v_heads,
                   double* g, double* beta);
 
+/*
+ * Gated RMSNorm of the GDN block's output ([P1] "Latest Status": zero-centred
+ * and gated RMSNorm operators with SiLU or sigmoid gating and a weight
+ * offset; the pages print no formula, so the plain definition is taken):
+ * for each row r of `dim` values,
+ *   rms     = sqrt(sum_j x[r, j]^2 / dim + eps)
+ *   out[r, j] = (x[r, j] / rms) * w'[j] * act(z[r, j])
+ * with w' = weight + 1 under ORACLE_NORM_ZERO_CENTRED (else weight), act =
+ * SiLU (y / (1 + e^-y)) or, under ORACLE_NORM_GATE_SIGMOID, 1 / (1 + e^-y);
+ * z == NULL means no gate (act = 1).  The norm comes before the gate.
+ */
+#define ORACLE_NORM_GATE_SIGMOID 1
+#define ORACLE_NORM_ZERO_CENTRED 2
+int oracle_gated_rmsnorm(const double* x, const double* z, const double* weight,
+                         int64_t rows, int32_t dim, double eps, int32_t flags, double* out);
+
 #ifdef __cplusplus
 }
 #endif

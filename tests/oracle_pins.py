@@ -325,10 +325,54 @@ def pin_gating(lib):
     assert np.all(g <= 0.0) and np.all((beta >= 0.0) & (beta <= 1.0))
 
 
+# --- gated RMSNorm epilogue (plain definition; [P1] "Latest Status") ------------
+def pin_gated_rmsnorm(lib):
+    """Facts about an RMS normalisation that do not restate the formula:
+    with eps = 0 and unit weights the normalised row has sum of squares
+    exactly dim (catches sum-vs-mean, a missing sqrt) and is invariant to
+    scaling the row; SiLU(0) = 0 and sigmoid(0) = 1/2 fix the gate forms; a
+    weight of -1 under the zero-centred offset gives zeros; a zero row stays
+    zero; rows are independent (each row alone equals the row in a batch);
+    large gate inputs make SiLU the identity and sigmoid 1."""
+    rng = np.random.default_rng(51)
+    rows, dim = 6, 48
+    x = rng.standard_normal((rows, dim)) * rng.uniform(0.1, 10.0, (rows, 1))
+    ones = np.ones(dim)
+    y = oracle.gated_rmsnorm(x, ones, eps=0.0, lib=lib)
+    assert np.allclose((y ** 2).sum(axis=1), dim, rtol=1e-13, atol=0)
+    y7 = oracle.gated_rmsnorm(7.5 * x, ones, eps=0.0, lib=lib)
+    assert np.allclose(y7, y, rtol=1e-13, atol=0)
+    w = rng.standard_normal(dim)
+    yw = oracle.gated_rmsnorm(x, w, eps=0.0, lib=lib)
+    assert np.allclose(yw, y * w[None, :], rtol=1e-13, atol=1e-15)
+    z0 = np.zeros_like(x)
+    assert np.all(oracle.gated_rmsnorm(x, w, z=z0, eps=0.0, lib=lib) == 0.0)        # SiLU(0) = 0
+    ys = oracle.gated_rmsnorm(x, w, z=z0, eps=0.0, flags=oracle.NORM_GATE_SIGMOID, lib=lib)
+    assert np.allclose(ys, 0.5 * yw, rtol=1e-15, atol=0)                             # sigmoid(0)
+    zbig = np.full_like(x, 60.0)
+    assert np.allclose(oracle.gated_rmsnorm(x, w, z=zbig, eps=0.0, lib=lib), 60.0 * yw,
+                       rtol=1e-13, atol=1e-13)                                       # SiLU ~ id
+    assert np.allclose(oracle.gated_rmsnorm(x, w, z=zbig, eps=0.0,
+                                            flags=oracle.NORM_GATE_SIGMOID, lib=lib), yw,
+                       rtol=1e-13, atol=1e-15)                                        # sigmoid ~ 1
+    assert np.all(oracle.gated_rmsnorm(x, -ones, eps=1e-6, flags=oracle.NORM_ZERO_CENTRED,
+                                       lib=lib) == 0.0)
+    xz = x.copy(); xz[2] = 0.0
+    assert np.all(oracle.gated_rmsnorm(xz, w, eps=1e-6, lib=lib)[2] == 0.0)
+    z = rng.standard_normal(x.shape)
+    full = oracle.gated_rmsnorm(x, w, z=z, eps=1e-5, lib=lib)
+    for r in range(rows):
+        one = oracle.gated_rmsnorm(x[r:r + 1], w, z=z[r:r + 1], eps=1e-5, lib=lib)
+        assert np.array_equal(one[0], full[r])
+    # eps enters under the root: for a row of equal values c, y = c / sqrt(c^2 + eps)
+    c = np.full((1, dim), 0.01)
+    assert abs(oracle.gated_rmsnorm(c, ones, eps=1e-4, lib=lib)[0, 0] - 0.01 / math.sqrt(1e-4 + 1e-4)) < 1e-15
+
+
 ALL_PINS = [pin_identity_step, pin_delta_rule_unit_key, pin_decay, pin_overwrite,
             pin_brute_force_matrix_form, pin_qk_norm, pin_gqa_map, pin_conv_sliding_window,
             pin_silu, pin_decode_split, pin_chunked_equals_token, pin_slot_contract,
-            pin_gating]
+            pin_gating, pin_gated_rmsnorm]
 
 
 def run_all(lib):

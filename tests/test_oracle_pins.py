@@ -97,6 +97,18 @@ MUTANTS = [
      ["pin_gating"]),
     ("gating_beta_sign", "beta[i] = 1.0 / (1.0 + exp(-b[i]));",
      "beta[i] = 1.0 / (1.0 + exp(b[i]));", ["pin_gating"]),
+    ("rmsnorm_sum_not_mean", "const double rms = sqrt(ss / dim + eps);",
+     "const double rms = sqrt(ss + eps);", ["pin_gated_rmsnorm"]),
+    ("rmsnorm_no_sqrt", "const double rms = sqrt(ss / dim + eps);",
+     "const double rms = ss / dim + eps;", ["pin_gated_rmsnorm"]),
+    ("rmsnorm_eps_outside_root", "const double rms = sqrt(ss / dim + eps);",
+     "const double rms = sqrt(ss / dim) + eps;", ["pin_gated_rmsnorm"]),
+    ("rmsnorm_gate_swapped", "gate = (flags & ORACLE_NORM_GATE_SIGMOID) ? sig : zj * sig;",
+     "gate = (flags & ORACLE_NORM_GATE_SIGMOID) ? zj * sig : sig;", ["pin_gated_rmsnorm"]),
+    ("rmsnorm_offset_dropped", "? weight[j] + 1.0 : weight[j];", "? weight[j] : weight[j];",
+     ["pin_gated_rmsnorm"]),
+    ("rmsnorm_weight_by_row", "? weight[j] + 1.0 : weight[j];",
+     "? weight[j] + 1.0 : weight[r % dim];", ["pin_gated_rmsnorm"]),
 ]
 
 
