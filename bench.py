@@ -387,6 +387,13 @@ def main():
     big.prepare_rec()
     ms_rec = time_loop(torch, big.rec_step, args.steps, args.warmup)
     torch.cuda.synchronize()
+    # gated RMSNorm epilogue on the prefill output (o [T, HV, dv] bf16, z bf16, w fp32)
+    zn = torch.randn(pre.T, HV, DV, device=dev).to(torch.bfloat16)
+    wn = torch.ones(DV, device=dev)
+    yn = torch.empty_like(pre.out)
+    ms_norm = time_loop(torch, lambda: gdn.gdn_gated_rmsnorm(pre.out, wn, yn, z=zn),
+                        args.steps, args.warmup)
+    norm_bytes = pre.T * HV * DV * 2 * 3 + DV * 4
     # a mixed step: the batch-256 decode rows plus two 1024-token prefills
     mixed = MixedSetup(big, seed=9, dev="cuda")
     ms_mixed = time_loop(torch, mixed.step, args.steps, args.warmup)
@@ -436,6 +443,10 @@ def main():
         "prefill_pct_mfma_peak": round(100 * pre_tflops / BF16_PEAK_TFLOPS, 2),
         "prefill_algorithmic_flops": pre_flops, "prefill_algorithmic_bytes": pre_bytes,
         "prefill_pct_hbm_peak": round(100 * pre_bytes / (pre_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+        "gated_rmsnorm_ms_mean": round(mean(ms_norm), 4),
+        "gated_rmsnorm_GBps": round(norm_bytes / (mean(ms_norm) * 1e-3) / 1e9, 1),
+        "gated_rmsnorm_note": ("gdn_gated_rmsnorm on the prefill output: "
+                               f"{pre.T * HV} rows of {DV}, bf16 x, z, out, fp32 weight"),
         "mixed_step_ms_mean": round(mean(ms_mixed), 4),
         "mixed_step_note": ("gdn_mixed_step, eager: the 256 decode rows of the batch-256 "
                             "workload plus two 1024-token prefill sequences (pre-conv input)"),

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libgdn.so")
 GDN_F32, GDN_BF16 = 0, 1
 FLAG_SILU, FLAG_QK_L2NORM, FLAG_VALIDATE = 1, 2, 4
 FLAG_STEP_FUSED, FLAG_STEP_SPLIT = 8, 16
+NORM_GATE_SIGMOID, NORM_ZERO_CENTRED = 1, 2
 EFLAG_SLOT_RANGE, EFLAG_SLOT_REPEAT, EFLAG_SEQLENS = 1, 2, 4
 DEFAULT_DECODE_FLAGS = FLAG_SILU | FLAG_QK_L2NORM
 DEFAULT_PREFILL_FLAGS = FLAG_QK_L2NORM
@@ -28,7 +29,7 @@ _STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_DIMS", 3: "GDN_ERR_DTYPE"
 EXPORTED = ["gdn_conv_update", "gdn_decode_workspace_size", "gdn_decode_step",
             "gdn_decode_step_gated", "gdn_decode_recurrent",
             "gdn_prefill_workspace_size", "gdn_prefill_chunked", "gdn_prefill_chunked_gated",
-            "gdn_mixed_workspace_size", "gdn_mixed_step", "gdn_strerror"]
+            "gdn_mixed_workspace_size", "gdn_mixed_step", "gdn_gated_rmsnorm", "gdn_strerror"]
 
 
 class GDNError(RuntimeError):
@@ -92,11 +93,12 @@ def load_library(path: str = None):
     lib.gdn_mixed_workspace_size.restype = sz
     lib.gdn_mixed_step.argtypes = [P, i32, P, P, i32, P, i32, i32, P, P, i32, P, P, i32, P, i32,
                                    P, i32, D, f32, i32, P, sz, P, P]
+    lib.gdn_gated_rmsnorm.argtypes = [P, i32, P, P, i32, ctypes.c_int64, i32, f32, i32, P, i32, P]
     lib.gdn_strerror.argtypes = [i32]
     lib.gdn_strerror.restype = ctypes.c_char_p
     for f in (lib.gdn_conv_update, lib.gdn_decode_step, lib.gdn_decode_recurrent,
               lib.gdn_prefill_chunked, lib.gdn_decode_step_gated, lib.gdn_prefill_chunked_gated,
-              lib.gdn_mixed_step):
+              lib.gdn_mixed_step, lib.gdn_gated_rmsnorm):
         f.restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -359,4 +361,18 @@ def gdn_mixed_step(x, g, beta, n_dec, cu_seqlens, slot_idx, conv_state, conv_wei
         _p(rec_state), ns, _p(out), _dt(out), ctypes.byref(dims), float(scale), flags,
         _p(workspace), workspace.numel() * workspace.element_size(), _p(err_flag),
         _stream(stream)))
+    return out
+
+
+def gdn_gated_rmsnorm(x, weight, out, z=None, eps=1e-6, flags=0, stream=None):
+    """Gated RMSNorm over the last axis (gdn.h: gdn_gated_rmsnorm): ``x`` and
+    ``z`` [..., dim] (z in x's dtype, or None), ``weight`` [dim]; ``out`` may be x."""
+    lib = load_library()
+    dim = x.shape[-1]
+    rows = x.numel() // dim if dim else 0
+    _dev(x, "x"); _dev(z, "z", x.dtype, None if z is None else tuple(x.shape))
+    _dev(weight, "weight", shape=(dim,)); _dev(out, "out", shape=tuple(x.shape))
+    _check("gdn_gated_rmsnorm", lib.gdn_gated_rmsnorm(
+        _p(x), _dt(x), _p(z), _p(weight), _dt(weight), rows, dim, float(eps), flags, _p(out),
+        _dt(out), _stream(stream)))
     return out

@@ -391,4 +391,19 @@ gdn_status gdn_mixed_step(const void* x, gdn_dtype x_dt, const float* g, const f
     return GDN_OK;
 }
 
+gdn_status gdn_gated_rmsnorm(const void* x, gdn_dtype x_dt, const void* z, const void* weight,
+                             gdn_dtype w_dt, int64_t rows, int32_t dim, float eps, int32_t flags,
+                             void* out, gdn_dtype out_dt, void* stream) {
+    if (flags & ~(GDN_NORM_GATE_SIGMOID | GDN_NORM_ZERO_CENTRED)) return GDN_ERR_FLAGS;
+    if (rows < 0 || dim < 4 || dim > 1024 || dim % 4 != 0 || !(eps >= 0.0f)) return GDN_ERR_DIMS;
+    if (rows > (static_cast<int64_t>(1) << 32)) return GDN_ERR_DIMS;
+    if (!dtype_ok(x_dt) || !dtype_ok(w_dt) || !dtype_ok(out_dt)) return GDN_ERR_DTYPE;
+    if (rows > 0 && (!x || !weight || !out)) return GDN_ERR_NULL;
+    if (!aligned16(x) || !aligned16(weight) || !aligned16(out) || (z && !aligned16(z)))
+        return GDN_ERR_ALIGN;
+    GDN_TRY_LAUNCH(launch_gated_rmsnorm(x, x_dt, z, weight, w_dt, out, out_dt, rows, dim, eps,
+                                        flags, static_cast<hipStream_t>(stream)));
+    return GDN_OK;
+}
+
 }  // extern "C"

@@ -87,4 +87,9 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, gdn_dtype
                           const gdn_dims& d, int32_t sqk, int32_t sv, float scale, int32_t flags,
                           const int32_t* err, hipStream_t st);
 
+// Gated RMSNorm over rows of `dim` values (z has x's dtype; NULL = no gate).
+hipError_t launch_gated_rmsnorm(const void* x, gdn_dtype x_dt, const void* z, const void* w,
+                                gdn_dtype w_dt, void* out, gdn_dtype out_dt, int64_t rows,
+                                int32_t dim, float eps, int32_t flags, hipStream_t st);
+
 }  // namespace gdn

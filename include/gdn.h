@@ -85,6 +85,11 @@ enum {
     GDN_FLAG_STEP_SPLIT = 16  /* gdn_decode_step: force conv kernel + recurrence  */
 };
 
+enum {                      /* flags of gdn_gated_rmsnorm                         */
+    GDN_NORM_GATE_SIGMOID = 1,  /* gate = sigmoid(z) instead of SiLU(z)           */
+    GDN_NORM_ZERO_CENTRED = 2   /* weight enters as weight + 1                    */
+};
+
 enum {                      /* bits written to *err_flag under GDN_FLAG_VALIDATE */
     GDN_EFLAG_SLOT_RANGE = 1,   /* an active slot >= num_slots                   */
     GDN_EFLAG_SLOT_REPEAT = 2,  /* an active slot appears twice                  */
@@ -345,6 +350,28 @@ gdn_status gdn_mixed_step(const void* x, gdn_dtype x_dt,
                           const gdn_dims* dims, float scale, int32_t flags,
                           void* workspace, size_t workspace_bytes,
                           int32_t* err_flag, void* stream);
+
+/*
+ * gdn_gated_rmsnorm -- the gated RMSNorm that follows the GDN core in the
+ * block ([P1] "Latest Status": zero-centred and gated RMSNorm with SiLU or
+ * sigmoid gating; the pages print no formula, the plain definition is used,
+ * the norm before the gate):
+ *   out[r, j] = x[r, j] / sqrt(sum_j x[r, j]^2 / dim + eps) * w'[j] * act(z[r, j])
+ *   w' = weight + 1 under GDN_NORM_ZERO_CENTRED, else weight;
+ *   act = SiLU, or sigmoid under GDN_NORM_GATE_SIGMOID; z == NULL: no gate.
+ *
+ *   x            [rows, dim] x_dt (e.g. o viewed as [tokens * HV, dv])
+ *   z            [rows, dim] in x_dt, or NULL
+ *   weight       [dim] w_dt
+ *   out          [rows, dim] out_dt; may be x itself (each row is read into
+ *                registers before it is written)
+ *   dim          a multiple of 4, 4 ... 1024; eps >= 0
+ * Per-row fp32 arithmetic with a fixed reduction order: batch-invariant.
+ */
+gdn_status gdn_gated_rmsnorm(const void* x, gdn_dtype x_dt, const void* z,
+                             const void* weight, gdn_dtype w_dt,
+                             int64_t rows, int32_t dim, float eps, int32_t flags,
+                             void* out, gdn_dtype out_dt, void* stream);
 
 /* gdn_strerror -- static, NUL-terminated description of a status code. */
 const char* gdn_strerror(gdn_status s);

@@ -205,3 +205,20 @@ def test_mixed_workspace_size(lib):
     D = 2 * 16 * 128 + 32 * 128
     assert lib.gdn_mixed_workspace_size(d, 3, 10) == (
         ((3 * D * 4 + 255) // 256) * 256 + ((10 * D * 2 + 255) // 256) * 256)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(flags=4), ERR_FLAGS),
+    (dict(dim=2), ERR_DIMS), (dict(dim=1028), ERR_DIMS), (dict(dim=130), ERR_DIMS),
+    (dict(eps=-1.0), ERR_DIMS), (dict(eps=float("nan")), ERR_DIMS), (dict(rows=-1), ERR_DIMS),
+    (dict(x_dt=9), ERR_DTYPE),
+    (dict(x=None), ERR_NULL),
+    (dict(out=MISALIGNED), ERR_ALIGN),
+])
+def test_gated_rmsnorm_rejects(lib, kw, code):
+    a = dict(x=FAKE, x_dt=1, z=None, w=FAKE, w_dt=0, rows=8, dim=128, eps=1e-6, flags=0,
+             out=FAKE, out_dt=1)
+    a.update(kw)
+    assert lib.gdn_gated_rmsnorm(a["x"], a["x_dt"], a["z"], a["w"], a["w_dt"], a["rows"],
+                                 a["dim"], a["eps"], a["flags"], a["out"], a["out_dt"],
+                                 None) == code
