@@ -394,6 +394,11 @@ def main():
     ms_norm = time_loop(torch, lambda: gdn.gdn_gated_rmsnorm(pre.out, wn, yn, z=zn),
                         args.steps, args.warmup)
     norm_bytes = pre.T * HV * DV * 2 * 3 + DV * 4
+    # the prefill with the Newton-Schulz (4 bf16 rounds) block-inverse variant
+    ms_pre_ns4 = time_loop(torch, lambda: gdn.gdn_prefill_chunked(
+        pre.p["q"], pre.p["k"], pre.p["v"], pre.p["g"], pre.p["beta"], pre.p["cu_seqlens"],
+        pre.p["slot_idx"], pre.p["rec_state"], pre.out, pre.dims, DK ** -0.5,
+        flags=gdn.FLAG_QK_L2NORM | gdn.FLAG_PREFILL_NS4), args.steps, args.warmup)
     # a mixed step: the batch-256 decode rows plus two 1024-token prefills
     mixed = MixedSetup(big, seed=9, dev="cuda")
     ms_mixed = time_loop(torch, mixed.step, args.steps, args.warmup)
@@ -443,6 +448,7 @@ def main():
         "prefill_pct_mfma_peak": round(100 * pre_tflops / BF16_PEAK_TFLOPS, 2),
         "prefill_algorithmic_flops": pre_flops, "prefill_algorithmic_bytes": pre_bytes,
         "prefill_pct_hbm_peak": round(100 * pre_bytes / (pre_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+        "prefill_ns4_ms_mean": round(mean(ms_pre_ns4), 4),
         "gated_rmsnorm_ms_mean": round(mean(ms_norm), 4),
         "gated_rmsnorm_GBps": round(norm_bytes / (mean(ms_norm) * 1e-3) / 1e9, 1),
         "gated_rmsnorm_note": ("gdn_gated_rmsnorm on the prefill output: "

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libgdn.so")
 GDN_F32, GDN_BF16 = 0, 1
 FLAG_SILU, FLAG_QK_L2NORM, FLAG_VALIDATE = 1, 2, 4
 FLAG_STEP_FUSED, FLAG_STEP_SPLIT = 8, 16
+FLAG_PREFILL_NS3, FLAG_PREFILL_NS4 = 32, 64
 NORM_GATE_SIGMOID, NORM_ZERO_CENTRED = 1, 2
 EFLAG_SLOT_RANGE, EFLAG_SLOT_REPEAT, EFLAG_SEQLENS = 1, 2, 4
 DEFAULT_DECODE_FLAGS = FLAG_SILU | FLAG_QK_L2NORM

@@ -194,8 +194,11 @@ gdn_status prefill_impl(const void* q, const void* k, const void* v, gdn_dtype i
                         const int32_t* slot_idx, float* rec_state, int32_t num_slots, void* out,
                         gdn_dtype out_dt, const gdn_dims* dims, float scale, int32_t flags,
                         int32_t* err_flag, void* stream) {
-    if (gdn_status st = check_flags(flags, GDN_FLAG_QK_L2NORM | GDN_FLAG_VALIDATE, err_flag))
+    if (gdn_status st = check_flags(flags, GDN_FLAG_QK_L2NORM | GDN_FLAG_VALIDATE |
+                                               GDN_FLAG_PREFILL_NS3 | GDN_FLAG_PREFILL_NS4,
+                                    err_flag))
         return st;
+    if ((flags & GDN_FLAG_PREFILL_NS3) && (flags & GDN_FLAG_PREFILL_NS4)) return GDN_ERR_FLAGS;
     if (gdn_status st = check_dims(dims)) return st;
     if (n_seqs < 0 || n_seqs > 65535 || total_tokens < 0 || num_slots < 1) return GDN_ERR_DIMS;
     if (!dtype_ok(in_dt) || !dtype_ok(out_dt)) return GDN_ERR_DTYPE;

@@ -152,6 +152,72 @@ __device__ __forceinline__ void store_pairs_t(bf16_t* arr, int stride, int c0, i
     }
 }
 
+// Newton-Schulz inverse of one 16x16 unit-lower block L = I + A (A strictly
+// lower, fp32 at blk with row stride sf), as the pages' CuteDSL prefill does
+// it: X0 = I - A, then `rounds` times X <- X (2I - L X), with L, every product
+// 2I - L X and every X rounded to bf16 (vLLM PR #53864, "Numerical root cause
+// and fix": three rounds are exact in exact arithmetic for 16x16, since the
+// error after round n is A^(2^(n+1)), but can fail with bf16 intermediates on
+// correlated keys; four fixed it there).  The result (its bf16 values) goes
+// back to blk in fp32.  One wave; scratch holds 512 bf16 (X^T, then the 2I - LX
+// transpose, and X), wave-local.  Products run on v_mfma_f32_16x16x32_bf16 with
+// the upper half of K zero: lane (q, i) supplies A[i][8q + s] and B[8q + s][i]
+// for q < 2, zeros for q >= 2, and holds D[4q + r][i].
+__device__ __forceinline__ void ns_block_inverse(float* blk, int sf, bf16_t* scratch, int rounds,
+                                                 int i, int q) {
+    bf16_t* Xt = scratch;          // X^T [j][k], then (2I - L X)^T
+    bf16_t* Xr = scratch + 256;    // X [i][k]
+    const bf16x8 zero8 = as_bf16x8(make_uint4(0, 0, 0, 0));
+    // L (A operand, row i, columns 8q .. 8q+7), rounded to bf16
+    bf16x8 aL = zero8;
+    if (q < 2) {
+        uint32_t w[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int k0 = 8 * q + 2 * s;
+            const float l0 = blk[i * sf + k0] + (i == k0 ? 1.0f : 0.0f);
+            const float l1 = blk[i * sf + k0 + 1] + (i == k0 + 1 ? 1.0f : 0.0f);
+            w[s] = pack_bf16x2(l0, l1);
+        }
+        aL = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
+    }
+    // X0 = I - A in the accumulator layout: lane holds X0[4q + r][i]
+    f32x4 x;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int row = 4 * q + r;
+        x[r] = (row == i ? 1.0f : 0.0f) - blk[row * sf + i];
+    }
+    auto store_x = [&](const f32x4& v) {     // X^T rows (contiguous) and X rows (scattered)
+        const uint32_t h01 = pack_bf16x2(v[0], v[1]), h23 = pack_bf16x2(v[2], v[3]);
+        *reinterpret_cast<uint2*>(&Xt[i * 16 + 4 * q]) = make_uint2(h01, h23);
+        Xr[(4 * q + 0) * 16 + i] = static_cast<bf16_t>(h01 & 0xffffu);
+        Xr[(4 * q + 1) * 16 + i] = static_cast<bf16_t>(h01 >> 16);
+        Xr[(4 * q + 2) * 16 + i] = static_cast<bf16_t>(h23 & 0xffffu);
+        Xr[(4 * q + 3) * 16 + i] = static_cast<bf16_t>(h23 >> 16);
+    };
+    store_x(x);
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    for (int n = 0; n < rounds; ++n) {
+        const bf16x8 bX = (q < 2) ? frag_std(Xt, 16, i, 0, q) : zero8;   // X[8q + s][i]
+        const bf16x8 aX = (q < 2) ? frag_std(Xr, 16, i, 0, q) : zero8;   // X[i][8q + s]
+        const f32x4 p = mfma(aL, bX, f32x4{0, 0, 0, 0});                   // (L X)[4q + r][i]
+        f32x4 zz;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) zz[r] = ((4 * q + r) == i ? 2.0f : 0.0f) - p[r];
+        *reinterpret_cast<uint2*>(&Xt[i * 16 + 4 * q]) =
+            make_uint2(pack_bf16x2(zz[0], zz[1]), pack_bf16x2(zz[2], zz[3]));   // (2I - LX)^T
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        const bf16x8 bZ = (q < 2) ? frag_std(Xt, 16, i, 0, q) : zero8;   // (2I - LX)[8q + s][i]
+        x = mfma(aX, bZ, f32x4{0, 0, 0, 0});                               // X (2I - L X)
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        store_x(x);
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) blk[(4 * q + r) * sf + i] = bf16_to_f32(f32_to_bf16(x[r]));
+}
+
 // LDS of one workgroup.  NP planes hold a raw input as bf16 (NP = 1) or as
 // bf16 hi + lo parts of fp32 values (NP = 2).
 template <int D, bool SPL>
@@ -181,12 +247,12 @@ struct PrefillSmem {
 constexpr int PF_NW = 8;                 // waves per workgroup
 constexpr int PF_NT = 64 * PF_NW;        // threads per workgroup
 
-template <int D, typename IT, typename OT>
+template <int D, typename IT, typename OT, bool NSV>
 __global__ __launch_bounds__(PF_NT) void prefill_kernel(
     const IT* __restrict__ qg, const IT* __restrict__ kg, const IT* __restrict__ vg,
     const GateArgs ga, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ slot, float* __restrict__ rec, OT* __restrict__ out, int32_t H,
-    int32_t HV, int32_t sqk, int32_t sv, float scale, int32_t flags,
+    int32_t HV, int32_t sqk, int32_t sv, float scale, int32_t flags, int32_t ns_rounds,
     const int32_t* __restrict__ err_flag) {
     constexpr bool SPL = sizeof(IT) == 4;        // fp32 inputs: hi/lo planes
     constexpr int NP = SPL ? 2 : 1;
@@ -442,7 +508,14 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
         // T[j][c] is final, every later row r adds A[r][j] T[j][c], so each row
         // still accumulates its terms in ascending j.  The upper triangle of
         // sm.g is zero from the epilogue above and stays zero.
-        if (wave == 0) {
+        // With ns_rounds > 0 the blocks are instead inverted by Newton-Schulz with
+        // bf16 intermediates (an A/B variant reproducing vLLM PR #53864,
+        // "Numerical root cause and fix"): waves 0-3, one block each.
+        if constexpr (NSV) {
+            if (wave < 4) ns_block_inverse(&sm.g[(16 * wave) * SF + 16 * wave], SF,
+                                           reinterpret_cast<bf16_t*>(sm.xs) + 512 * wave, ns_rounds,
+                                           l16, q4);
+        } else if (wave == 0) {
             const int b = lane >> 4;
             const int c = lane & 15;
             float* blk = &sm.g[(16 * b) * SF + 16 * b];
@@ -787,10 +860,16 @@ hipError_t run_prefill(const void* q, const void* k, const void* v, const GateAr
                        float* rec, void* out, const gdn_dims& d, int32_t sqk, int32_t sv,
                        float scale, int32_t flags, const int32_t* err, hipStream_t st) {
     dim3 grid(d.num_v_heads, n_seqs);
-    return launch(prefill_kernel<D, IT, OT>, grid, dim3(PF_NT), 0, st,
+    const int32_t ns = (flags & GDN_FLAG_PREFILL_NS3) ? 3 : (flags & GDN_FLAG_PREFILL_NS4) ? 4 : 0;
+    if (ns > 0)
+        return launch(prefill_kernel<D, IT, OT, true>, grid, dim3(PF_NT), 0, st,
+                      static_cast<const IT*>(q), static_cast<const IT*>(k),
+                      static_cast<const IT*>(v), ga, cu, slot, rec, static_cast<OT*>(out),
+                      d.num_k_heads, d.num_v_heads, sqk, sv, scale, flags, ns, err);
+    return launch(prefill_kernel<D, IT, OT, false>, grid, dim3(PF_NT), 0, st,
                   static_cast<const IT*>(q), static_cast<const IT*>(k),
                   static_cast<const IT*>(v), ga, cu, slot, rec, static_cast<OT*>(out),
-                  d.num_k_heads, d.num_v_heads, sqk, sv, scale, flags, err);
+                  d.num_k_heads, d.num_v_heads, sqk, sv, scale, flags, 0, err);
 }
 
 template <int D, typename IT>

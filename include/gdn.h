@@ -82,7 +82,9 @@ enum {
     GDN_FLAG_QK_L2NORM = 2, /* q, k <- x / sqrt(sum(x*x) + 1e-6) before use      */
     GDN_FLAG_VALIDATE = 4,  /* device-side index validation, see above           */
     GDN_FLAG_STEP_FUSED = 8,  /* gdn_decode_step: force the one-kernel path      */
-    GDN_FLAG_STEP_SPLIT = 16  /* gdn_decode_step: force conv kernel + recurrence  */
+    GDN_FLAG_STEP_SPLIT = 16, /* gdn_decode_step: force conv kernel + recurrence  */
+    GDN_FLAG_PREFILL_NS3 = 32, /* prefill A/B variant: diagonal KK^T blocks by   */
+    GDN_FLAG_PREFILL_NS4 = 64  /* 3 or 4 bf16 Newton-Schulz rounds (see below)   */
 };
 
 enum {                      /* flags of gdn_gated_rmsnorm                         */
@@ -250,7 +252,12 @@ size_t gdn_prefill_workspace_size(const gdn_dims* dims, int32_t n_seqs, int32_t 
  *                from rec_state[slot] and its final state is written back
  *                there (zero-fill a fresh slot first)
  *   out          [total_tokens, HV, dv], out_dt
- *   scale, flags as for gdn_decode_step (GDN_FLAG_QK_L2NORM, GDN_FLAG_VALIDATE)
+ *   scale, flags as for gdn_decode_step (GDN_FLAG_QK_L2NORM, GDN_FLAG_VALIDATE),
+ *                plus at most one of GDN_FLAG_PREFILL_NS3 / GDN_FLAG_PREFILL_NS4: a
+ *                numerics A/B variant that inverts the 16x16 diagonal KK^T blocks
+ *                by 3 or 4 Newton-Schulz rounds with bf16 intermediates, as [P4]
+ *                "Numerical root cause and fix" describes, instead of the default
+ *                exact fp32 forward substitution
  *   workspace    >= gdn_prefill_workspace_size(...) bytes of device memory
  */
 gdn_status gdn_prefill_chunked(const void* q, const void* k, const void* v, gdn_dtype in_dt,

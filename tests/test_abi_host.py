@@ -222,3 +222,9 @@ def test_gated_rmsnorm_rejects(lib, kw, code):
     assert lib.gdn_gated_rmsnorm(a["x"], a["x_dt"], a["z"], a["w"], a["w_dt"], a["rows"],
                                  a["dim"], a["eps"], a["flags"], a["out"], a["out_dt"],
                                  None) == code
+
+
+def test_prefill_rejects_both_newton_schulz_variants(lib):
+    assert lib.gdn_prefill_chunked(FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 1, 64, FAKE, FAKE, 8,
+                                   FAKE, 1, _dims(), 0.1, 2 | 32 | 64, None, 0, None,
+                                   None) == ERR_FLAGS

@@ -205,3 +205,46 @@ def test_prefill_then_decode_continues_state():
     assert rel_err(f64(o), o_ref) <= PREFILL_TOL
     act = p["slot_idx"].tolist()
     assert rel_err(f64(g["rec_state"][act]), rec[act]) <= PREFILL_TOL
+
+
+# ---------------------------------------------------------------------------
+# Newton-Schulz A/B variant (vLLM PR #53864, "Numerical root cause and fix"):
+# inverting the 16x16 diagonal KK^T blocks by three bf16 Newton-Schulz rounds
+# fails on highly correlated keys, four rounds repair it to the bf16-inverse
+# level; the default exact fp32 forward substitution stays well inside 5e-3.
+def _run_flags(p, extra):
+    g = to_dev(p)
+    return g, run_prefill_gpu(g, 128 ** -0.5, flags=gdn.FLAG_QK_L2NORM | extra)
+
+
+def _errs(p, g, out, heads):
+    o_ref, s_ref = oracle_heads(p, heads, 128 ** -0.5)
+    slots = p["slot_idx"].tolist()
+    sg = np.stack([f64(g["rec_state"][s][heads]) for s in slots])
+    return rel_err(f64(out[:, heads]), o_ref), rel_err(sg, s_ref)
+
+
+def test_newton_schulz_three_rounds_fail_on_correlated_keys():
+    p = gi.stress_prefill_inputs(64)
+    heads = [0, 1, 17, 31]
+    g3, o3 = _run_flags(p, gdn.FLAG_PREFILL_NS3)
+    g4, o4 = _run_flags(p, gdn.FLAG_PREFILL_NS4)
+    gf, of = _run_flags(p, 0)
+    torch.cuda.synchronize()
+    e3 = _errs(p, g3, o3, heads)
+    e4 = _errs(p, g4, o4, heads)
+    ef = _errs(p, gf, of, heads)
+    print(f"\nNS3 {e3[0]:.2e}/{e3[1]:.2e}  NS4 {e4[0]:.2e}/{e4[1]:.2e}  fwd {ef[0]:.2e}/{ef[1]:.2e}")
+    assert not (e3[0] < 1.0), "three bf16 rounds should fail on correlated keys"
+    assert e4[0] < 1e-2 and e4[1] < 1e-2, "four rounds should repair it"
+    assert ef[0] <= PREFILL_TOL and ef[1] <= PREFILL_TOL
+    assert ef[1] < e4[1] / 10, "exact substitution keeps the state far closer than NS4"
+
+
+def test_newton_schulz_variants_agree_on_random_keys():
+    p = gi.prefill_inputs([64, 130, 300], 6, seed=9)
+    for fl in (gdn.FLAG_PREFILL_NS3, gdn.FLAG_PREFILL_NS4):
+        g, out = _run_flags(p, fl)
+        torch.cuda.synchronize()
+        eo, es = _errs(p, g, out, [0, 9, 31])
+        assert eo <= PREFILL_TOL and es <= PREFILL_TOL, (fl, eo, es)
