@@ -14,9 +14,11 @@ state written in a recent step.
 
 Prints ONE JSON line.  `value` is the decode step's algorithmic HBM bytes per
 second at batch 256 (GB/s); the batch-16 decode rate and the prefill tokens/s
-ride along in "extra".  "roofline" reports the dominant kernel (the decode
-recurrence) timed alone with HIP events over the timed region; "cpu_baseline"
-is the fp64 oracle on a bounded sample of the same workload.
+ride along in "extra".  "roofline" reports the headline step's kernel (at
+batch 256 the step is one fused conv + recurrence kernel) timed alone with HIP
+events over eager launches; the conv + recurrence pair that the step uses below
+one (row, key head) group per CU is timed alongside.  "cpu_baseline" is the
+fp64 oracle on a bounded sample of the same workload.
 """
 import argparse
 import json
@@ -68,12 +70,12 @@ def prefill_bytes(total_tokens, n_seqs, in_bytes=2, out_bytes=2):
     return total_tokens * per_tok + n_seqs * 2 * HV * DV * DK * 4
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_rec_kernel_b256_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_step_kernel_b256_traffic.txt")
 DECODE_SRC = os.path.join(ROOT, "gated_deltanet_recurrent_gdn_amd", "csrc", "decode.hip")
 
 
 def measured_traffic():
-    """HBM bytes per launch of the recurrence kernel at batch 256 from the
+    """HBM bytes per launch of the fused step kernel at batch 256 from the
     committed counter runs (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None
     when decode.hip has changed since those counters were taken."""
     import hashlib
@@ -383,7 +385,10 @@ def main():
         ms_small = time_graph(torch, g_small, r_small, args.steps, args.warmup)
     # prefill, eager (one call is milliseconds)
     ms_pre = time_loop(torch, lambda: pre.step(args.validate), args.steps, args.warmup)
-    # dominant kernel alone (the decode recurrence), eager launches with events
+    # the headline step's kernel alone (the fused step at batch 256), eager
+    # launches bracketed by events on the stream they run on
+    ms_step_k = time_loop(torch, big.step, args.steps, args.warmup)
+    # the split path's recurrence kernel alone (post-conv activations in)
     big.prepare_rec()
     ms_rec = time_loop(torch, big.rec_step, args.steps, args.warmup)
     torch.cuda.synchronize()
@@ -424,6 +429,8 @@ def main():
     rec_ms = mean(ms_rec)
     rec_bytes = 256 * rec_bytes_per_seq()
     rec_gbs = rec_bytes / (rec_ms * 1e-3) / 1e9
+    stepk_ms = mean(ms_step_k)
+    stepk_gbs = step_bytes_big / (stepk_ms * 1e-3) / 1e9
     pre_ms = mean(ms_pre)
     pre_flops = prefill_flops(pre.lengths)
     pre_bytes = prefill_bytes(pre.T, len(pre.lengths))
@@ -456,6 +463,11 @@ def main():
         "mixed_step_ms_mean": round(mean(ms_mixed), 4),
         "mixed_step_note": ("gdn_mixed_step, eager: the 256 decode rows of the batch-256 "
                             "workload plus two 1024-token prefill sequences (pre-conv input)"),
+        "decode_rec_kernel_b256_ms_mean": round(rec_ms, 5),
+        "decode_rec_kernel_b256_GBps": round(rec_gbs, 2),
+        "decode_rec_kernel_b256_pct_hbm_peak": round(100 * rec_gbs / HBM_PEAK_GBS, 2),
+        "decode_rec_kernel_note": ("gdn_decode_recurrent alone at batch 256 (fp32 post-conv "
+                                   "activations in): the recurrence of the split path"),
         "decode_b256_gated_ms_mean": round(mean(ms_big_g), 5),
         "decode_b256_gated_GBps": round(step_bytes_big_gated / (mean(ms_big_g) * 1e-3) / 1e9, 2),
         "prefill_gated_ms_mean": round(mean(ms_pre_g), 4),
@@ -491,11 +503,11 @@ def main():
                                "step also runs decode batch 16 and the 8-sequence varlen "
                                "prefill (see extra)",
                    "global_batch": 256, "seq_len": 1, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "hbm", "kernel": "decode_rec_kernel",
-                     "achieved": round(rec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(rec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "avg_launch_ms": round(rec_ms, 5),
-                     "algorithmic_bytes_per_launch": rec_bytes},
+        "roofline": {"bound": "hbm", "kernel": "decode_step_kernel",
+                     "achieved": round(stepk_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(stepk_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "avg_launch_ms": round(stepk_ms, 5),
+                     "algorithmic_bytes_per_launch": step_bytes_big},
         "cpu_baseline": cpu,
         "extra": extra,
     }

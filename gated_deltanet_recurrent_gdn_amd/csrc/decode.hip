@@ -225,13 +225,18 @@ __global__ __launch_bounds__(256) void decode_rec_kernel(
 // heads that share h -- so it reads and rolls them with no other workgroup
 // touching them, and keeps the post-conv activations in LDS instead of an HBM
 // workspace.  The recurrence then streams the group's G dv state rows in
-// passes of 32 rows with the per-row arithmetic of rec_item, in the same
+// passes of NT / 8 rows with the per-row arithmetic of rec_item, in the same
 // order, so this kernel and the conv kernel + decode_rec_kernel pair give
 // bitwise-identical results.  The first pass's state loads are issued right
 // after the conv's own loads, so that they are in flight during the conv.
 // ---------------------------------------------------------------------------
+// Threads per fused-step workgroup: a pass streams NT / 8 state rows.
+#ifndef GDN_STEP_NT
+#define GDN_STEP_NT 1024
+#endif
+
 template <int DK, typename XT, typename CT, typename WT, typename OT>
-__global__ __launch_bounds__(256) void decode_step_kernel(
+__global__ __launch_bounds__(GDN_STEP_NT) void decode_step_kernel(
     const XT* __restrict__ x, const GateArgs ga,
     const int32_t* __restrict__ slot, CT* __restrict__ cs, const WT* __restrict__ w,
     const WT* __restrict__ bias, float* __restrict__ rec, OT* __restrict__ out, int32_t H,
@@ -243,7 +248,9 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int sub = lane & 7;
-    const int rl = wave * 8 + (lane >> 3);    // row within a 32-row pass
+    constexpr int NT = GDN_STEP_NT;
+    constexpr int RP = NT / 8;                // state rows per pass
+    const int rl = wave * 8 + (lane >> 3);    // row within a pass
     const int G = HV / H;
     const int R = G * dv;                     // state rows of the group
     const int D = 2 * H * DK + HV * dv;
@@ -255,15 +262,17 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         const int32_t s = slot[b];
         OT* ob = out + (static_cast<size_t>(b) * HV + static_cast<size_t>(h) * G) * dv;
         if (s <= 0) {                         // inactive row: zeros, caches untouched
-            for (int r = threadIdx.x; r < R; r += 256) elem<OT>::st(ob + r, 0.0f);
+            for (int r = threadIdx.x; r < R; r += NT) elem<OT>::st(ob + r, 0.0f);
             continue;
         }
         float* Sg = rec + ((static_cast<size_t>(s) * HV + static_cast<size_t>(h) * G) * dv) * DK;
 
         auto fetch = [&](float4 (&St)[NV], int r0) {
+            if (r0 + rl < R) {                // the 8 lanes of a row share the test
 #pragma unroll
-            for (int i = 0; i < NV; ++i)
-                St[i] = state_ld(Sg + static_cast<size_t>(r0 + rl) * DK + 32 * i + 4 * sub);
+                for (int i = 0; i < NV; ++i)
+                    St[i] = state_ld(Sg + static_cast<size_t>(r0 + rl) * DK + 32 * i + 4 * sub);
+            }
         };
         float4 S[NV];
 
@@ -287,7 +296,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
             gate_raw(ga, static_cast<size_t>(b) * HV + h * G + threadIdx.x, gx0, gx1);
             gh = gate_head(ga, h * G + threadIdx.x);
         }
-        if (units <= 256) {
+        if (units <= NT) {
             // threads past the last unit re-read unit 0 (loads stay unconditional)
             const bool mine = static_cast<int>(threadIdx.x) < units;
             const int lc = mine ? 4 * static_cast<int>(threadIdx.x) : 0;
@@ -302,7 +311,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
                 *reinterpret_cast<float4*>(&ys[lc]) = make_float4(y[0], y[1], y[2], y[3]);
             }
         } else {
-            for (int u = threadIdx.x; u < units; u += 256) {
+            for (int u = threadIdx.x; u < units; u += NT) {
                 const int lc = 4 * u;
                 const int c = channel(lc);
                 float y[4];
@@ -318,7 +327,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
             gs[2 * threadIdx.x] = gv;
             gs[2 * threadIdx.x + 1] = bv;
         }
-        for (int t = threadIdx.x + 256; t < G; t += 256) {   // groups of more than 256 heads
+        for (int t = threadIdx.x + NT; t < G; t += NT) {     // groups of more than NT heads
             float x0, x1, gv, bv;
             gate_raw(ga, static_cast<size_t>(b) * HV + h * G + t, x0, x1);
             gate_finish(ga, gate_head(ga, h * G + t), x0, x1, gv, bv);
@@ -357,7 +366,8 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         // the passes: pass 0's rows are already in S
         auto pass = [&](int r0) {
             const int r = r0 + rl;
-            const int gi = r0 / dv;           // a pass lies inside one head (dv % 32 == 0)
+            if (r >= R) return;               // the 8 lanes of a row share the test
+            const int gi = r / dv;            // this row's value head within the group
             const float alpha = expf(gs[2 * gi]);
             const float bt = gs[2 * gi + 1];
             const float vr = ys[2 * DK + r];
@@ -384,7 +394,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
             if (sub == 0) elem<OT>::st(ob + r, o);
         };
         pass(0);
-        for (int r0 = 32; r0 < R; r0 += 32) {
+        for (int r0 = RP; r0 < R; r0 += RP) {
             fetch(S, r0);
             pass(r0);
         }
@@ -481,7 +491,7 @@ hipError_t run_step(const StepArgs& a) {
     const int64_t groups = static_cast<int64_t>(a.batch) * a.d->num_k_heads;
     const int64_t resident = static_cast<int64_t>(cu_count()) * GDN_STEP_WG_PER_CU;
     const int grid = static_cast<int>(groups < resident ? groups : resident);
-    return launch(decode_step_kernel<DK, XT, CT, WT, OT>, dim3(grid), dim3(256), lds, a.st,
+    return launch(decode_step_kernel<DK, XT, CT, WT, OT>, dim3(grid), dim3(GDN_STEP_NT), lds, a.st,
                   static_cast<const XT*>(a.x), a.gate, a.slot, static_cast<CT*>(a.cs),
                   static_cast<const WT*>(a.w), static_cast<const WT*>(a.bias), a.rec,
                   static_cast<OT*>(a.out), a.d->num_k_heads, a.d->num_v_heads,
@@ -506,13 +516,14 @@ hipError_t step_x(gdn_dtype xt, gdn_dtype c, gdn_dtype wt, gdn_dtype o, const St
 }
 }  // namespace
 
-// The fused step is chosen below this many (row, key head) groups per CU.
-// Measured at H = 16, HV = 32, d = 128 on 256 CUs: batch 16 (1 group per CU)
-// fused 19.0 us vs 20.1 us for the pair; batch 32 even; batch 64 and 256 the
-// pair is ~4-5% faster (its 32-row recurrence items stream the state with
-// more workgroups in flight than the fused kernel's 8-pass groups).
-#ifndef GDN_DECODE_FUSED_MAX_GROUPS_PER_CU
-#define GDN_DECODE_FUSED_MAX_GROUPS_PER_CU 2
+// The fused step is chosen from this many (row, key head) groups per CU on.
+// Measured (graph replay, H = 16, HV = 32, d = 128, 256 CUs, 1024-thread
+// groups): batch 256 fused 203.3 us vs 206.1 us for the conv + recurrence
+// pair; batch 16 17.5 vs 17.9; batch 32 and 64 within 2%; below one group per
+// CU the pair's 32-row items spread the few rows over more CUs (batch 1: 7.0
+// vs 9.3 us, batch 4: 9.3 vs 10.4).
+#ifndef GDN_DECODE_FUSED_MIN_GROUPS_PER_CU
+#define GDN_DECODE_FUSED_MIN_GROUPS_PER_CU 1
 #endif
 
 bool decode_step_fused_fits(const gdn_dims& d) {
@@ -523,7 +534,8 @@ bool decode_step_fused_fits(const gdn_dims& d) {
 
 bool decode_step_use_fused(const gdn_dims& d, int32_t batch) {
     return decode_step_fused_fits(d) &&
-           static_cast<int64_t>(batch) * d.num_k_heads < static_cast<int64_t>(GDN_DECODE_FUSED_MAX_GROUPS_PER_CU) * cu_count();
+           static_cast<int64_t>(batch) * d.num_k_heads >=
+               static_cast<int64_t>(GDN_DECODE_FUSED_MIN_GROUPS_PER_CU) * cu_count();
 }
 
 hipError_t launch_decode_step_fused(const void* x, gdn_dtype x_dt, const GateArgs& gate,
