@@ -348,6 +348,11 @@ def cpu_baseline_prefill(budget_s):
                       f"{dt:.1f} s, single-threaded fp64 C, token by token"}
 
 
+def gi_stress(T):
+    import gdn_inputs as gi
+    return gi.stress_prefill_inputs(T)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -404,6 +409,23 @@ def main():
         pre.p["q"], pre.p["k"], pre.p["v"], pre.p["g"], pre.p["beta"], pre.p["cu_seqlens"],
         pre.p["slot_idx"], pre.p["rec_state"], pre.out, pre.dims, DK ** -0.5,
         flags=gdn.FLAG_QK_L2NORM | gdn.FLAG_PREFILL_NS4), args.steps, args.warmup)
+    # one long sequence (the correlated-key stress shape, 16384 tokens): whole-
+    # sequence run vs the segment-parallel schedule the call picks by itself
+    lp = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v)
+          for k, v in gi_stress(16384).items()}
+    lp_out = torch.empty(16384, HV, DV, dtype=torch.bfloat16, device=dev)
+    lp_ws = torch.empty(max(1, gdn.gdn_prefill_workspace_size(pre.dims, 1, 16384)),
+                        dtype=torch.uint8, device=dev)
+
+    def long_prefill(extra_flags):
+        gdn.gdn_prefill_chunked(lp["q"], lp["k"], lp["v"], lp["g"], lp["beta"], lp["cu_seqlens"],
+                                lp["slot_idx"], lp["rec_state"], lp_out, pre.dims, DK ** -0.5,
+                                flags=gdn.FLAG_QK_L2NORM | extra_flags, workspace=lp_ws)
+    lsteps = max(3, args.steps // 4)
+    ms_long_seq = time_loop(torch, lambda: long_prefill(gdn.FLAG_PREFILL_SEQUENTIAL), lsteps,
+                            max(1, args.warmup // 2))
+    ms_long_seg = time_loop(torch, lambda: long_prefill(0), lsteps, max(1, args.warmup // 2))
+    del lp, lp_out, lp_ws
     # a mixed step: the batch-256 decode rows plus two 1024-token prefills
     mixed = MixedSetup(big, seed=9, dev="cuda")
     ms_mixed = time_loop(torch, mixed.step, args.steps, args.warmup)
@@ -456,6 +478,13 @@ def main():
         "prefill_algorithmic_flops": pre_flops, "prefill_algorithmic_bytes": pre_bytes,
         "prefill_pct_hbm_peak": round(100 * pre_bytes / (pre_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
         "prefill_ns4_ms_mean": round(mean(ms_pre_ns4), 4),
+        "prefill_long_seq_ms_whole": round(mean(ms_long_seq), 4),
+        "prefill_long_seq_ms_segmented": round(mean(ms_long_seg), 4),
+        "prefill_long_seq_tokens_per_s_segmented": round(16384 / (mean(ms_long_seg) * 1e-3), 1),
+        "prefill_long_seq_note": ("one 16384-token sequence (correlated keys, beta 0.9, g 0; "
+                                  "H=16 HV=32 d=128): gdn_prefill_chunked with "
+                                  "GDN_FLAG_PREFILL_SEQUENTIAL vs the segment-parallel schedule "
+                                  "it picks with its workspace"),
         "gated_rmsnorm_ms_mean": round(mean(ms_norm), 4),
         "gated_rmsnorm_GBps": round(norm_bytes / (mean(ms_norm) * 1e-3) / 1e9, 1),
         "gated_rmsnorm_note": ("gdn_gated_rmsnorm on the prefill output: "

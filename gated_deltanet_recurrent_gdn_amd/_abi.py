@@ -19,6 +19,7 @@ GDN_F32, GDN_BF16 = 0, 1
 FLAG_SILU, FLAG_QK_L2NORM, FLAG_VALIDATE = 1, 2, 4
 FLAG_STEP_FUSED, FLAG_STEP_SPLIT = 8, 16
 FLAG_PREFILL_NS3, FLAG_PREFILL_NS4 = 32, 64
+FLAG_PREFILL_SEQUENTIAL = 128
 NORM_GATE_SIGMOID, NORM_ZERO_CENTRED = 1, 2
 EFLAG_SLOT_RANGE, EFLAG_SLOT_REPEAT, EFLAG_SEQLENS = 1, 2, 4
 DEFAULT_DECODE_FLAGS = FLAG_SILU | FLAG_QK_L2NORM
@@ -30,6 +31,7 @@ _STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_DIMS", 3: "GDN_ERR_DTYPE"
 EXPORTED = ["gdn_conv_update", "gdn_decode_workspace_size", "gdn_decode_step",
             "gdn_decode_step_gated", "gdn_decode_recurrent",
             "gdn_prefill_workspace_size", "gdn_prefill_chunked", "gdn_prefill_chunked_gated",
+            "gdn_prefill_segmented_workspace_size", "gdn_prefill_segmented",
             "gdn_mixed_workspace_size", "gdn_mixed_step", "gdn_gated_rmsnorm", "gdn_strerror"]
 
 
@@ -90,6 +92,10 @@ def load_library(path: str = None):
                                           D, f32, i32, P, sz, P, P]
     lib.gdn_prefill_chunked_gated.argtypes = [P, P, P, i32, G, P, i32, i32, P, P, i32, P, i32,
                                               D, f32, i32, P, sz, P, P]
+    lib.gdn_prefill_segmented_workspace_size.argtypes = [D, i32, i32, i32]
+    lib.gdn_prefill_segmented_workspace_size.restype = sz
+    lib.gdn_prefill_segmented.argtypes = [P, P, P, i32, P, P, G, P, i32, i32, P, P, i32, P, i32,
+                                          D, f32, i32, i32, P, sz, P, P]
     lib.gdn_mixed_workspace_size.argtypes = [D, i32, i32]
     lib.gdn_mixed_workspace_size.restype = sz
     lib.gdn_mixed_step.argtypes = [P, i32, P, P, i32, P, i32, i32, P, P, i32, P, P, i32, P, i32,
@@ -99,7 +105,7 @@ def load_library(path: str = None):
     lib.gdn_strerror.restype = ctypes.c_char_p
     for f in (lib.gdn_conv_update, lib.gdn_decode_step, lib.gdn_decode_recurrent,
               lib.gdn_prefill_chunked, lib.gdn_decode_step_gated, lib.gdn_prefill_chunked_gated,
-              lib.gdn_mixed_step, lib.gdn_gated_rmsnorm):
+              lib.gdn_mixed_step, lib.gdn_gated_rmsnorm, lib.gdn_prefill_segmented):
         f.restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -271,8 +277,14 @@ def gdn_prefill_workspace_size(dims: gdn_dims, n_seqs: int, total_tokens: int) -
                                                           int(total_tokens)))
 
 
+def gdn_prefill_segmented_workspace_size(dims: gdn_dims, n_seqs: int, total_tokens: int,
+                                         seg_len: int) -> int:
+    return int(load_library().gdn_prefill_segmented_workspace_size(
+        ctypes.byref(dims), int(n_seqs), int(total_tokens), int(seg_len)))
+
+
 def _prefill(fn, q, k, v, gb, gate, cu_seqlens, slot_idx, rec_state, out, dims, scale, flags,
-             workspace, err_flag, stream):
+             workspace, err_flag, stream, seg_len=None):
     lib = load_library()
     T = q.shape[0]
     H, HV, dk, dv = dims.num_k_heads, dims.num_v_heads, dims.head_k_dim, dims.head_v_dim
@@ -287,10 +299,21 @@ def _prefill(fn, q, k, v, gb, gate, cu_seqlens, slot_idx, rec_state, out, dims, 
     _dev(err_flag, "err_flag", torch.int32)
     if tuple(rec_state.shape[1:]) != (HV, dv, dk):
         raise ValueError("rec_state must be [num_slots, HV, dv, dk]")
-    need = gdn_prefill_workspace_size(dims, n, T)
+    need = (gdn_prefill_workspace_size(dims, n, T) if seg_len is None else
+            gdn_prefill_segmented_workspace_size(dims, n, T, seg_len))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _dev(workspace, "workspace")
+    if seg_len is not None:
+        gs = None if gate is None else _gate_struct(gate, T, HV)
+        status = lib.gdn_prefill_segmented(
+            _p(q), _p(k), _p(v), _dt(q), _p(gb[0]) if gate is None else None,
+            _p(gb[1]) if gate is None else None, None if gs is None else ctypes.byref(gs),
+            _p(cu_seqlens), n, T, _p(slot_idx), _p(rec_state), rec_state.shape[0], _p(out),
+            _dt(out), ctypes.byref(dims), float(scale), flags, int(seg_len), _p(workspace),
+            workspace.numel() * workspace.element_size(), _p(err_flag), _stream(stream))
+        _check(fn, status)
+        return out
     rest = (_p(cu_seqlens), n, T, _p(slot_idx), _p(rec_state), rec_state.shape[0], _p(out),
             _dt(out), ctypes.byref(dims), float(scale), flags, _p(workspace),
             workspace.numel() * workspace.element_size(), _p(err_flag), _stream(stream))
@@ -318,6 +341,18 @@ def gdn_prefill_chunked_gated(q, k, v, gate: GateInputs, cu_seqlens, slot_idx, r
     """gdn_prefill_chunked with the gating fused in (gdn.h: gdn_prefill_chunked_gated)."""
     return _prefill("gdn_prefill_chunked_gated", q, k, v, None, gate, cu_seqlens, slot_idx,
                     rec_state, out, dims, scale, flags, workspace, err_flag, stream)
+
+
+def gdn_prefill_segmented(q, k, v, g, beta, cu_seqlens, slot_idx, rec_state, out,
+                          dims: gdn_dims, scale, seg_len: int, flags=DEFAULT_PREFILL_FLAGS,
+                          gate: GateInputs = None, workspace=None, err_flag=None, stream=None):
+    """Segment-parallel prefill with seg_len-token segments (gdn.h:
+    gdn_prefill_segmented); with ``gate`` given, g and beta must be None."""
+    if gate is not None and (g is not None or beta is not None):
+        raise ValueError("pass either g and beta or gate")
+    return _prefill("gdn_prefill_segmented", q, k, v, (g, beta), gate, cu_seqlens, slot_idx,
+                    rec_state, out, dims, scale, flags, workspace, err_flag, stream,
+                    seg_len=seg_len)
 
 
 def gdn_mixed_workspace_size(dims: gdn_dims, n_dec: int, total_pre: int) -> int:

@@ -193,9 +193,11 @@ gdn_status prefill_impl(const void* q, const void* k, const void* v, gdn_dtype i
                         const int32_t* cu_seqlens, int32_t n_seqs, int32_t total_tokens,
                         const int32_t* slot_idx, float* rec_state, int32_t num_slots, void* out,
                         gdn_dtype out_dt, const gdn_dims* dims, float scale, int32_t flags,
+                        int32_t seg_len, void* workspace, size_t workspace_bytes,
                         int32_t* err_flag, void* stream) {
     if (gdn_status st = check_flags(flags, GDN_FLAG_QK_L2NORM | GDN_FLAG_VALIDATE |
-                                               GDN_FLAG_PREFILL_NS3 | GDN_FLAG_PREFILL_NS4,
+                                               GDN_FLAG_PREFILL_NS3 | GDN_FLAG_PREFILL_NS4 |
+                                               GDN_FLAG_PREFILL_SEQUENTIAL,
                                     err_flag))
         return st;
     if ((flags & GDN_FLAG_PREFILL_NS3) && (flags & GDN_FLAG_PREFILL_NS4)) return GDN_ERR_FLAGS;
@@ -210,15 +212,41 @@ gdn_status prefill_impl(const void* q, const void* k, const void* v, gdn_dtype i
     if (total_tokens > 0 && (!q || !k || !v || !out)) return GDN_ERR_NULL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(rec_state))
         return GDN_ERR_ALIGN;
+    if (seg_len > 0) {                           // explicit segment length
+        if (seg_len % 64 != 0) return GDN_ERR_DIMS;
+        if (flags & GDN_FLAG_PREFILL_SEQUENTIAL) return GDN_ERR_FLAGS;
+        if ((total_tokens + seg_len - 1) / seg_len > 32768) return GDN_ERR_DIMS;
+        if (n_seqs > 0 && total_tokens > 0) {
+            if (!workspace) return GDN_ERR_WORKSPACE;
+            if (workspace_bytes < prefill_segmented_workspace(*dims, n_seqs, total_tokens, seg_len))
+                return GDN_ERR_WORKSPACE;
+            if (!aligned16(workspace)) return GDN_ERR_ALIGN;
+        }
+    } else if (seg_len < 0) {                    // the plain call: segments when they pay
+        seg_len = (flags & GDN_FLAG_PREFILL_SEQUENTIAL)
+            ? 0 : prefill_auto_segment_len(*dims, n_seqs, total_tokens);
+        if (seg_len > 0 &&
+            (!workspace || !aligned16(workspace) ||
+             workspace_bytes < prefill_segmented_workspace(*dims, n_seqs, total_tokens, seg_len)))
+            seg_len = 0;
+    } else {
+        return GDN_ERR_DIMS;
+    }
     auto s = static_cast<hipStream_t>(stream);
     if (flags & GDN_FLAG_VALIDATE)
         GDN_TRY_LAUNCH(launch_validate(slot_idx, n_seqs, num_slots, cu_seqlens, n_seqs, total_tokens,
                                        err_flag, s));
     const int32_t* ef = (flags & GDN_FLAG_VALIDATE) ? err_flag : nullptr;
-    GDN_TRY_LAUNCH(launch_prefill(q, k, v, in_dt, ga, cu_seqlens, n_seqs, slot_idx,
-                                  rec_state, out, out_dt, *dims,
-                                  dims->num_k_heads * dims->head_k_dim,
-                                  dims->num_v_heads * dims->head_v_dim, scale, flags, ef, s));
+    const int32_t sqk = dims->num_k_heads * dims->head_k_dim;
+    const int32_t sv = dims->num_v_heads * dims->head_v_dim;
+    if (seg_len > 0 && n_seqs > 0 && total_tokens > 0)
+        GDN_TRY_LAUNCH(launch_prefill_segmented(q, k, v, in_dt, ga, cu_seqlens, n_seqs,
+                                                total_tokens, slot_idx, rec_state, out, out_dt,
+                                                *dims, sqk, sv, scale, flags, seg_len,
+                                                static_cast<float*>(workspace), ef, s));
+    else
+        GDN_TRY_LAUNCH(launch_prefill(q, k, v, in_dt, ga, cu_seqlens, n_seqs, slot_idx,
+                                      rec_state, out, out_dt, *dims, sqk, sv, scale, flags, ef, s));
     return GDN_OK;
 }
 
@@ -281,9 +309,35 @@ gdn_status gdn_decode_recurrent(const void* qkv, gdn_dtype qkv_dt, const float* 
 }
 
 size_t gdn_prefill_workspace_size(const gdn_dims* dims, int32_t n_seqs, int32_t total_tokens) {
-    // The fused prefill keeps every intermediate on chip: no workspace.
-    (void)dims; (void)n_seqs; (void)total_tokens;
-    return 0;
+    // Whole-sequence runs keep every intermediate on chip; the segment-parallel
+    // schedule, where the call would choose it, needs its segment matrices.
+    if (check_dims(dims) != GDN_OK || n_seqs <= 0 || total_tokens <= 0) return 0;
+    if (dims->head_k_dim != dims->head_v_dim || dims->head_k_dim > 128) return 0;
+    return prefill_segmented_workspace(*dims, n_seqs, total_tokens,
+                                       prefill_auto_segment_len(*dims, n_seqs, total_tokens));
+}
+
+size_t gdn_prefill_segmented_workspace_size(const gdn_dims* dims, int32_t n_seqs,
+                                            int32_t total_tokens, int32_t seg_len) {
+    if (check_dims(dims) != GDN_OK || n_seqs < 0 || total_tokens < 0) return 0;
+    if (seg_len <= 0 || seg_len % 64 != 0) return 0;
+    if (dims->head_k_dim != dims->head_v_dim || dims->head_k_dim > 128) return 0;
+    return prefill_segmented_workspace(*dims, n_seqs, total_tokens, seg_len);
+}
+
+gdn_status gdn_prefill_segmented(const void* q, const void* k, const void* v, gdn_dtype in_dt,
+                                 const float* g, const float* beta, const gdn_gate_inputs* gate,
+                                 const int32_t* cu_seqlens, int32_t n_seqs, int32_t total_tokens,
+                                 const int32_t* slot_idx, float* rec_state, int32_t num_slots,
+                                 void* out, gdn_dtype out_dt, const gdn_dims* dims, float scale,
+                                 int32_t flags, int32_t seg_len, void* workspace,
+                                 size_t workspace_bytes, int32_t* err_flag, void* stream) {
+    if (seg_len <= 0) return GDN_ERR_DIMS;
+    if (gate && (g || beta)) return GDN_ERR_FLAGS;
+    return prefill_impl(q, k, v, in_dt, gate ? nullptr : g, gate ? nullptr : beta, gate,
+                        cu_seqlens, n_seqs, total_tokens, slot_idx, rec_state, num_slots, out,
+                        out_dt, dims, scale, flags, seg_len, workspace, workspace_bytes,
+                        err_flag, stream);
 }
 
 gdn_status gdn_prefill_chunked(const void* q, const void* k, const void* v, gdn_dtype in_dt,
@@ -292,10 +346,9 @@ gdn_status gdn_prefill_chunked(const void* q, const void* k, const void* v, gdn_
                                float* rec_state, int32_t num_slots, void* out, gdn_dtype out_dt,
                                const gdn_dims* dims, float scale, int32_t flags, void* workspace,
                                size_t workspace_bytes, int32_t* err_flag, void* stream) {
-    (void)workspace; (void)workspace_bytes;
     return prefill_impl(q, k, v, in_dt, g, beta, nullptr, cu_seqlens, n_seqs, total_tokens,
-                        slot_idx, rec_state, num_slots, out, out_dt, dims, scale, flags,
-                        err_flag, stream);
+                        slot_idx, rec_state, num_slots, out, out_dt, dims, scale, flags, -1,
+                        workspace, workspace_bytes, err_flag, stream);
 }
 
 gdn_status gdn_prefill_chunked_gated(const void* q, const void* k, const void* v,
@@ -306,11 +359,10 @@ gdn_status gdn_prefill_chunked_gated(const void* q, const void* k, const void* v
                                      gdn_dtype out_dt, const gdn_dims* dims, float scale,
                                      int32_t flags, void* workspace, size_t workspace_bytes,
                                      int32_t* err_flag, void* stream) {
-    (void)workspace; (void)workspace_bytes;
     if (!gate) return GDN_ERR_NULL;
     return prefill_impl(q, k, v, in_dt, nullptr, nullptr, gate, cu_seqlens, n_seqs,
                         total_tokens, slot_idx, rec_state, num_slots, out, out_dt, dims, scale,
-                        flags, err_flag, stream);
+                        flags, -1, workspace, workspace_bytes, err_flag, stream);
 }
 
 size_t gdn_mixed_workspace_size(const gdn_dims* dims, int32_t n_dec, int32_t total_pre) {

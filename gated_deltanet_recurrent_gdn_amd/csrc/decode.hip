@@ -402,13 +402,6 @@ __global__ __launch_bounds__(GDN_STEP_NT) void decode_step_kernel(
     }
 }
 
-namespace {
-struct RecArgs {
-    const void* y; GateArgs gate; const int32_t* slot; int32_t batch;
-    float* rec; void* out; const gdn_dims* d; float scale; int32_t flags; const int32_t* err;
-    hipStream_t st;
-};
-
 // Compute units of the current device, queried once per device (a relaxed
 // atomic cache: concurrent first calls store the same value).
 int cu_count() {
@@ -423,6 +416,15 @@ int cu_count() {
     }
     return n;
 }
+
+namespace {
+struct RecArgs {
+    const void* y; GateArgs gate; const int32_t* slot; int32_t batch;
+    float* rec; void* out; const gdn_dims* d; float scale; int32_t flags; const int32_t* err;
+    hipStream_t st;
+};
+
+
 
 template <int DK, int RPL, bool FULL, bool GATED, typename YT, typename OT>
 hipError_t run_rec_g(const RecArgs& a) {
@@ -533,7 +535,9 @@ bool decode_step_fused_fits(const gdn_dims& d) {
 }
 
 bool decode_step_use_fused(const gdn_dims& d, int32_t batch) {
-    return decode_step_fused_fits(d) &&
+    // dk > 128 stays on the pair: the 1024-thread fused kernel (128 VGPRs)
+    // spills its per-row registers there
+    return decode_step_fused_fits(d) && d.head_k_dim <= 128 &&
            static_cast<int64_t>(batch) * d.num_k_heads >=
                static_cast<int64_t>(GDN_DECODE_FUSED_MIN_GROUPS_PER_CU) * cu_count();
 }

@@ -247,13 +247,26 @@ struct PrefillSmem {
 constexpr int PF_NW = 8;                 // waves per workgroup
 constexpr int PF_NT = 64 * PF_NW;        // threads per workgroup
 
-template <int D, typename IT, typename OT, bool NSV>
+// Which part of each sequence a launch walks.  Pass 0: whole sequences.
+// Segment passes (segments of seg_len tokens, a multiple of CH; blockIdx.z
+// picks the segment): pass 1 runs segment 0 from the slot's state (z = 0) and
+// each middle segment j from the zero state (z = 2j, its B) and from the
+// identity with v = 0 (z = 2j + 1, its P), the last two without outputs;
+// pass 2 reruns segment j = z + 1 from its composed start state.  ws holds
+// the D x D fp32 matrices [segment id][start, P, B][value head].
+struct SegArgs {
+    float* ws;
+    int32_t seg_len;
+    int32_t pass;
+};
+
+template <int D, typename IT, typename OT, bool NSV, bool SEG>
 __global__ __launch_bounds__(PF_NT) void prefill_kernel(
     const IT* __restrict__ qg, const IT* __restrict__ kg, const IT* __restrict__ vg,
     const GateArgs ga, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ slot, float* __restrict__ rec, OT* __restrict__ out, int32_t H,
     int32_t HV, int32_t sqk, int32_t sv, float scale, int32_t flags, int32_t ns_rounds,
-    const int32_t* __restrict__ err_flag) {
+    const SegArgs sg, const int32_t* __restrict__ err_flag) {
     constexpr bool SPL = sizeof(IT) == 4;        // fp32 inputs: hi/lo planes
     constexpr int NP = SPL ? 2 : 1;
     static_assert(D == 32 || D == 64 || D == 128, "head dim");
@@ -286,6 +299,7 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
     const bool wact = wave * WB < KB;            // this wave owns W columns
 
     if (s <= 0) {                                // inactive: zero outputs, state untouched
+        if (SEG && (sg.pass == 2 || blockIdx.z != 0)) return;
         for (int64_t i = tid; i < static_cast<int64_t>(t1 - t0) * D; i += PF_NT) {
             const int64_t t = t0 + i / D;
             elem<OT>::st(out + (t * HV + hv) * D + i % D, 0.0f);
@@ -295,6 +309,50 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
     if (t1 <= t0) return;                        // empty sequence: state untouched
 
     float* S = rec + (static_cast<size_t>(s) * HV + hv) * static_cast<size_t>(D) * D;
+
+    // The tokens [a0, a1) this workgroup walks, where its start state comes
+    // from (0: the slot, 1: zero, 2: identity, 3: `init`), whether it writes
+    // outputs and reads v, and where its end state goes (nullptr: dropped).
+    // Whole-sequence launches (SEG false) compile none of the segment logic.
+    int32_t a0 = t0, a1 = t1;
+    int init_mode = 0;
+    const float* init = S;
+    float* fin = S;
+    bool wo = true, vzero = false;
+    if constexpr (SEG) {
+        const int32_t seg = sg.seg_len;
+        const int32_t nseg = (t1 - t0 + seg - 1) / seg;
+        const int64_t id0 = n + t0 / seg;        // segment id of the sequence's first segment
+        auto wsm = [&](int64_t id, int kind) {
+            return sg.ws + ((id * 3 + kind) * HV + hv) * static_cast<size_t>(D) * D;
+        };
+        const int z = blockIdx.z;
+        if (sg.pass == 1) {
+            const int j = z >> 1;
+            if (nseg <= 1) {
+                if (z != 0) return;              // one segment: the whole run, as pass 0
+            } else if (j == 0) {
+                if (z != 0) return;
+                a1 = t0 + seg;
+                fin = wsm(id0 + 1, 0);           // start state of segment 1
+            } else {
+                if (j > nseg - 2) return;
+                a0 = t0 + j * seg;
+                a1 = a0 + seg;
+                wo = false;
+                if (z & 1) { init_mode = 2; vzero = true; fin = wsm(id0 + j, 1); }
+                else       { init_mode = 1; fin = wsm(id0 + j, 2); }
+            }
+        } else {
+            const int j = z + 1;
+            if (nseg <= 1 || j > nseg - 1) return;
+            a0 = t0 + j * seg;
+            a1 = min(a0 + seg, t1);
+            init_mode = 3;
+            init = wsm(id0 + j, 0);
+            fin = (j == nseg - 1) ? S : nullptr;
+        }
+    }
 
     // ---- state S0^T [k][v] in accumulator layout: tile (kb, vb) lane holds
     //      S0^T[16 kb + 4 q4 + r][16 (wave VB + vb) + l16] = S[v][k..k+3]
@@ -306,8 +364,13 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
             st[kb][vb] = f32x4{0, 0, 0, 0};
             if (vact) {
                 const int v = 16 * (wave * VB + vb) + l16;
-                const float4 x = *reinterpret_cast<const float4*>(S + static_cast<size_t>(v) * D + 16 * kb + 4 * q4);
-                st[kb][vb] = f32x4{x.x, x.y, x.z, x.w};
+                if (!SEG || init_mode == 0 || init_mode == 3) {
+                    const float4 x = *reinterpret_cast<const float4*>(init + static_cast<size_t>(v) * D + 16 * kb + 4 * q4);
+                    st[kb][vb] = f32x4{x.x, x.y, x.z, x.w};
+                } else if (init_mode == 2) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) st[kb][vb][r] = (16 * kb + 4 * q4 + r == v) ? 1.0f : 0.0f;
+                }
             }
         }
 
@@ -333,7 +396,7 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
     auto fetch = [&](int32_t c, int Lc) {
         const rsrc_t rk_ = make_rsrc(kg + static_cast<size_t>(c) * sqk, Lc * row_kq);
         const rsrc_t rq_ = make_rsrc(qg + static_cast<size_t>(c) * sqk, Lc * row_kq);
-        const rsrc_t rv_ = make_rsrc(vg + static_cast<size_t>(c) * sv, Lc * row_v);
+        const rsrc_t rv_ = make_rsrc(vg + static_cast<size_t>(c) * sv, vzero ? 0u : Lc * row_v);
 #pragma unroll
         for (int pass = 0; pass < CP; ++pass) {
             const int k0 = 8 * (cg + CG * pass);
@@ -369,10 +432,10 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
             pbeta = __builtin_amdgcn_raw_buffer_load_b32(r1, ob, 0, 0);
         }
     };
-    fetch(t0, min(CH, t1 - t0));
+    fetch(a0, min(CH, a1 - a0));
 
-    for (int32_t c0 = t0; c0 < t1; c0 += CH) {
-        const int L = min(CH, t1 - c0);
+    for (int32_t c0 = a0; c0 < a1; c0 += CH) {
+        const int L = min(CH, a1 - c0);
 
         // ---------------- stage the fetched chunk into LDS (planes hi [, lo])
 #pragma unroll
@@ -698,7 +761,32 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
         }
         __syncthreads();                         // -W visible to all waves
 
-        if (vact) {
+        if (SEG && vact && !wo) {
+            // ------------ U = Ut - W S0^T alone (a segment-map run writes no
+            // outputs); the same contraction order as below
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                bf16x8 sh[VB], sl[VB];
+#pragma unroll
+                for (int vb = 0; vb < VB; ++vb) {
+                    uint2 h0, l0, h1, l1;
+                    split4(st[2 * ks][vb], h0, l0);
+                    split4(st[2 * ks + 1][vb], h1, l1);
+                    sh[vb] = as_bf16x8(cat(h0, h1));
+                    sl[vb] = as_bf16x8(cat(l0, l1));
+                }
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) {
+                    const bf16x8 aw = frag_perm(sm.vt_w[0], SK, 16 * tb + l16, 32 * ks, q4);
+#pragma unroll
+                    for (int vb = 0; vb < VB; ++vb) {
+                        u[tb][vb] = mfma(aw, sh[vb], u[tb][vb]);
+                        u[tb][vb] = mfma(aw, sl[vb], u[tb][vb]);
+                    }
+                }
+            }
+        }
+        if (vact && (!SEG || wo)) {
             // ------------ U = Ut - W S0^T and, transposed, O1^T = S0 Q^T.  The
             // state's hi/lo fragments (permuted k-slots) are the B operand of the
             // first and, holding the same values, the A operand of the second.
@@ -812,7 +900,7 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
                     ch[ks][vb] = as_bf16x8(cat(h0, h1));
                     cl[ks][vb] = as_bf16x8(cat(l0, l1));
                 }
-            if (c0 + CH < t1) fetch(c0 + CH, min(CH, t1 - c0 - CH));   // next chunk, in flight
+            if (c0 + CH < a1) fetch(c0 + CH, min(CH, a1 - c0 - CH));   // next chunk, in flight
             const float egl = sm.egl;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
@@ -836,18 +924,18 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
                 }
             }
         }
-        if (!vact && c0 + CH < t1) fetch(c0 + CH, min(CH, t1 - c0 - CH));
+        if (!vact && c0 + CH < a1) fetch(c0 + CH, min(CH, a1 - c0 - CH));
         __syncthreads();                         // LDS is rewritten by the next chunk
     }
 
-    // ---- final state back to the slot
-    if (vact) {
+    // ---- final state back to the slot (or to the segment workspace)
+    if (vact && (!SEG || fin)) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int vb = 0; vb < VB; ++vb) {
                 const int v = 16 * (wave * VB + vb) + l16;
-                *reinterpret_cast<float4*>(S + static_cast<size_t>(v) * D + 16 * kb + 4 * q4) =
+                *reinterpret_cast<float4*>(fin + static_cast<size_t>(v) * D + 16 * kb + 4 * q4) =
                     make_float4(st[kb][vb][0], st[kb][vb][1], st[kb][vb][2], st[kb][vb][3]);
             }
     }
@@ -858,28 +946,47 @@ template <int D, typename IT, typename OT>
 hipError_t run_prefill(const void* q, const void* k, const void* v, const GateArgs& ga,
                        const int32_t* cu, int32_t n_seqs, const int32_t* slot,
                        float* rec, void* out, const gdn_dims& d, int32_t sqk, int32_t sv,
-                       float scale, int32_t flags, const int32_t* err, hipStream_t st) {
-    dim3 grid(d.num_v_heads, n_seqs);
+                       float scale, int32_t flags, const SegArgs& sg, int32_t nz,
+                       const int32_t* err, hipStream_t st) {
+    dim3 grid(d.num_v_heads, n_seqs, nz);
     const int32_t ns = (flags & GDN_FLAG_PREFILL_NS3) ? 3 : (flags & GDN_FLAG_PREFILL_NS4) ? 4 : 0;
-    if (ns > 0)
-        return launch(prefill_kernel<D, IT, OT, true>, grid, dim3(PF_NT), 0, st,
-                      static_cast<const IT*>(q), static_cast<const IT*>(k),
-                      static_cast<const IT*>(v), ga, cu, slot, rec, static_cast<OT*>(out),
-                      d.num_k_heads, d.num_v_heads, sqk, sv, scale, flags, ns, err);
-    return launch(prefill_kernel<D, IT, OT, false>, grid, dim3(PF_NT), 0, st,
-                  static_cast<const IT*>(q), static_cast<const IT*>(k),
-                  static_cast<const IT*>(v), ga, cu, slot, rec, static_cast<OT*>(out),
-                  d.num_k_heads, d.num_v_heads, sqk, sv, scale, flags, 0, err);
+    auto go = [&](auto kernel, int32_t nsr) {
+        return launch(kernel, grid, dim3(PF_NT), 0, st, static_cast<const IT*>(q),
+                      static_cast<const IT*>(k), static_cast<const IT*>(v), ga, cu, slot, rec,
+                      static_cast<OT*>(out), d.num_k_heads, d.num_v_heads, sqk, sv, scale, flags,
+                      nsr, sg, err);
+    };
+    if (sg.pass != 0)
+        return ns > 0 ? go(prefill_kernel<D, IT, OT, true, true>, ns)
+                      : go(prefill_kernel<D, IT, OT, false, true>, 0);
+    return ns > 0 ? go(prefill_kernel<D, IT, OT, true, false>, ns)
+                  : go(prefill_kernel<D, IT, OT, false, false>, 0);
 }
 
 template <int D, typename IT>
 hipError_t pick_out(gdn_dtype out_dt, const void* q, const void* k, const void* v, const GateArgs& ga,
                     const int32_t* cu, int32_t n_seqs, const int32_t* slot,
                     float* rec, void* out, const gdn_dims& d, int32_t sqk, int32_t sv, float scale,
-                    int32_t flags, const int32_t* err, hipStream_t st) {
+                    int32_t flags, const SegArgs& sg, int32_t nz, const int32_t* err,
+                    hipStream_t st) {
     return out_dt == GDN_BF16
-        ? run_prefill<D, IT, bf16_t>(q, k, v, ga, cu, n_seqs, slot, rec, out, d, sqk, sv, scale, flags, err, st)
-        : run_prefill<D, IT, float>(q, k, v, ga, cu, n_seqs, slot, rec, out, d, sqk, sv, scale, flags, err, st);
+        ? run_prefill<D, IT, bf16_t>(q, k, v, ga, cu, n_seqs, slot, rec, out, d, sqk, sv, scale, flags, sg, nz, err, st)
+        : run_prefill<D, IT, float>(q, k, v, ga, cu, n_seqs, slot, rec, out, d, sqk, sv, scale, flags, sg, nz, err, st);
+}
+
+hipError_t prefill_pass(const void* q, const void* k, const void* v, gdn_dtype in_dt,
+                        const GateArgs& ga, const int32_t* cu, int32_t n_seqs,
+                        const int32_t* slot, float* rec, void* out, gdn_dtype out_dt,
+                        const gdn_dims& d, int32_t sqk, int32_t sv, float scale, int32_t flags,
+                        const SegArgs& sg, int32_t nz, const int32_t* err, hipStream_t st) {
+    const int D = d.head_k_dim;
+    if (in_dt == GDN_F32) {
+        if (D == 32) return pick_out<32, float>(out_dt, q, k, v, ga, cu, n_seqs, slot, rec, out, d, sqk, sv, scale, flags, sg, nz, err, st);
+        return pick_out<64, float>(out_dt, q, k, v, ga, cu, n_seqs, slot, rec, out, d, sqk, sv, scale, flags, sg, nz, err, st);
+    }
+    if (D == 32) return pick_out<32, bf16_t>(out_dt, q, k, v, ga, cu, n_seqs, slot, rec, out, d, sqk, sv, scale, flags, sg, nz, err, st);
+    if (D == 64) return pick_out<64, bf16_t>(out_dt, q, k, v, ga, cu, n_seqs, slot, rec, out, d, sqk, sv, scale, flags, sg, nz, err, st);
+    return pick_out<128, bf16_t>(out_dt, q, k, v, ga, cu, n_seqs, slot, rec, out, d, sqk, sv, scale, flags, sg, nz, err, st);
 }
 }  // namespace
 
@@ -898,14 +1005,134 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, gdn_dtype
                           const int32_t* err, hipStream_t st) {
     if (n_seqs == 0) return hipSuccess;
     if (!prefill_supported(d, in_dt)) return hipErrorInvalidValue;
-    const int D = d.head_k_dim;
-    if (in_dt == GDN_F32) {
-        if (D == 32) return pick_out<32, float>(out_dt, q, k, v, ga, cu, n_seqs, slot, rec, out, d, sqk, sv, scale, flags, err, st);
-        return pick_out<64, float>(out_dt, q, k, v, ga, cu, n_seqs, slot, rec, out, d, sqk, sv, scale, flags, err, st);
+    return prefill_pass(q, k, v, in_dt, ga, cu, n_seqs, slot, rec, out, out_dt, d, sqk, sv,
+                        scale, flags, SegArgs{nullptr, 0, 0}, 1, err, st);
+}
+
+// ---------------------------------------------------------------------------
+// Segment-parallel prefill
+
+// Start states of segments 2.. of each sequence: start[j + 1] = start[j] P_j + B_j
+// (row v of a state depends only on row v of the previous one, so a workgroup
+// owns 16 state rows of one (sequence, value head); the sum over the inner
+// index runs in ascending order with fused multiply-adds, fp32).  P_j is staged
+// in LDS each step; the 16 rows stay in LDS between steps.
+template <int D>
+__global__ __launch_bounds__(256) void prefill_seg_scan_kernel(
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ slot, int32_t HV, int32_t seg_len,
+    float* __restrict__ ws, const int32_t* __restrict__ err_flag) {
+    constexpr int CPT = D / 16;                  // columns per thread
+    __shared__ float ps[D * D];
+    __shared__ float rows[16 * D];
+    if (call_rejected(err_flag)) return;
+    const int hv = blockIdx.x, n = blockIdx.y, rb = blockIdx.z;
+    const int32_t t0 = cu[n], t1 = cu[n + 1];
+    if (slot[n] <= 0 || t1 <= t0) return;
+    const int32_t nseg = (t1 - t0 + seg_len - 1) / seg_len;
+    if (nseg < 3) return;
+    const int64_t id0 = n + t0 / seg_len;
+    auto wsm = [&](int64_t id, int kind) {
+        return ws + ((id * 3 + kind) * HV + hv) * static_cast<size_t>(D) * D;
+    };
+    const int tid = threadIdx.x;
+    const int r = tid >> 4;                      // row within the block
+    const int c0 = (tid & 15) * CPT;             // first column
+    const int v = 16 * rb + r;
+    {
+        const float* s1 = wsm(id0 + 1, 0);
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) rows[r * D + c0 + c] = s1[static_cast<size_t>(v) * D + c0 + c];
     }
-    if (D == 32) return pick_out<32, bf16_t>(out_dt, q, k, v, ga, cu, n_seqs, slot, rec, out, d, sqk, sv, scale, flags, err, st);
-    if (D == 64) return pick_out<64, bf16_t>(out_dt, q, k, v, ga, cu, n_seqs, slot, rec, out, d, sqk, sv, scale, flags, err, st);
-    return pick_out<128, bf16_t>(out_dt, q, k, v, ga, cu, n_seqs, slot, rec, out, d, sqk, sv, scale, flags, err, st);
+    for (int j = 1; j <= nseg - 2; ++j) {
+        const float4* p = reinterpret_cast<const float4*>(wsm(id0 + j, 1));
+        __syncthreads();                         // previous step's reads of ps are done
+        for (int i = tid; i < D * D / 4; i += 256) reinterpret_cast<float4*>(ps)[i] = p[i];
+        const float* b = wsm(id0 + j, 2) + static_cast<size_t>(v) * D + c0;
+        float acc[CPT];
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) acc[c] = b[c];
+        __syncthreads();
+        for (int i = 0; i < D; ++i) {
+            const float x = rows[r * D + i];
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) acc[c] = fmaf(x, ps[i * D + c0 + c], acc[c]);
+        }
+        __syncthreads();                         // every read of rows is done
+        float* dst = wsm(id0 + j + 1, 0) + static_cast<size_t>(v) * D + c0;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            rows[r * D + c0 + c] = acc[c];
+            dst[c] = acc[c];
+        }
+    }
+}
+
+int64_t prefill_segment_ids(int32_t n_seqs, int32_t total_tokens, int32_t seg_len) {
+    return static_cast<int64_t>(n_seqs) + total_tokens / seg_len + 1;
+}
+
+size_t prefill_segmented_workspace(const gdn_dims& d, int32_t n_seqs, int32_t total_tokens,
+                                   int32_t seg_len) {
+    if (seg_len <= 0) return 0;
+    const size_t mat = static_cast<size_t>(d.head_k_dim) * d.head_v_dim * sizeof(float);
+    return static_cast<size_t>(prefill_segment_ids(n_seqs, total_tokens, seg_len)) * 3 *
+           static_cast<size_t>(d.num_v_heads) * mat;
+}
+
+// Model (per-chunk workgroup time as the unit, one workgroup per CU, equal
+// sequence lengths): whole sequences take c = chunks per sequence; with m
+// segments of c/m chunks, pass 1 runs G (2m - 3) workgroups and pass 2 G (m - 1),
+// G = sequences x value heads, each in ceil(count / CUs) rounds, plus the
+// scan's m - 2 steps at about a quarter chunk each.  The plain call segments
+// only where the model gains at least 15%.
+int32_t prefill_auto_segment_len(const gdn_dims& d, int32_t n_seqs, int32_t total_tokens) {
+    if (n_seqs <= 0 || total_tokens <= 0) return 0;
+    const int64_t groups = static_cast<int64_t>(n_seqs) * d.num_v_heads;
+    const int64_t cus = cu_count();
+    if (groups * 2 > cus) return 0;              // the chip is at least half busy already
+    const int64_t chunks = (total_tokens / n_seqs + 63) / 64;
+    if (chunks < 8) return 0;
+    double best = static_cast<double>(chunks);
+    int32_t best_len = 0;
+    for (int64_t m = 3; m <= 64; ++m) {
+        const int64_t per = (chunks + m - 1) / m;          // chunks per segment
+        const int64_t mm = (chunks + per - 1) / per;        // segments actually used
+        if (mm < 3) continue;
+        const int64_t r1 = (groups * (2 * mm - 3) + cus - 1) / cus;
+        const int64_t r2 = (groups * (mm - 1) + cus - 1) / cus;
+        const double t = static_cast<double>(per) * (r1 + r2) + 0.25 * (mm - 2);
+        if (t < best * 0.999) { best = t; best_len = static_cast<int32_t>(per * 64); }
+    }
+    return (best <= 0.85 * chunks) ? best_len : 0;
+}
+
+hipError_t launch_prefill_segmented(const void* q, const void* k, const void* v, gdn_dtype in_dt,
+                                    const GateArgs& ga, const int32_t* cu, int32_t n_seqs,
+                                    int32_t total_tokens, const int32_t* slot, float* rec,
+                                    void* out, gdn_dtype out_dt, const gdn_dims& d,
+                                    int32_t sqk, int32_t sv, float scale, int32_t flags,
+                                    int32_t seg_len, float* ws, const int32_t* err,
+                                    hipStream_t st) {
+    if (n_seqs == 0) return hipSuccess;
+    if (!prefill_supported(d, in_dt) || seg_len <= 0 || seg_len % CH != 0)
+        return hipErrorInvalidValue;
+    // segments of the longest possible sequence (all tokens in one)
+    const int32_t smax = total_tokens > 0 ? (total_tokens + seg_len - 1) / seg_len : 1;
+    const int32_t nz1 = smax >= 2 ? 2 * (smax - 1) : 1;
+    if (nz1 > 65535) return hipErrorInvalidValue;
+    hipError_t e = prefill_pass(q, k, v, in_dt, ga, cu, n_seqs, slot, rec, out, out_dt, d, sqk,
+                                sv, scale, flags, SegArgs{ws, seg_len, 1}, nz1, err, st);
+    if (e != hipSuccess || smax < 2) return e;
+    if (smax >= 3) {
+        const int D = d.head_k_dim;
+        const dim3 grid(d.num_v_heads, n_seqs, D / 16);
+        if (D == 32) e = launch(prefill_seg_scan_kernel<32>, grid, dim3(256), 0, st, cu, slot, d.num_v_heads, seg_len, ws, err);
+        else if (D == 64) e = launch(prefill_seg_scan_kernel<64>, grid, dim3(256), 0, st, cu, slot, d.num_v_heads, seg_len, ws, err);
+        else e = launch(prefill_seg_scan_kernel<128>, grid, dim3(256), 0, st, cu, slot, d.num_v_heads, seg_len, ws, err);
+        if (e != hipSuccess) return e;
+    }
+    return prefill_pass(q, k, v, in_dt, ga, cu, n_seqs, slot, rec, out, out_dt, d, sqk, sv,
+                        scale, flags, SegArgs{ws, seg_len, 2}, smax - 1, err, st);
 }
 
 }  // namespace gdn

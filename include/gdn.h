@@ -84,7 +84,9 @@ enum {
     GDN_FLAG_STEP_FUSED = 8,  /* gdn_decode_step: force the one-kernel path      */
     GDN_FLAG_STEP_SPLIT = 16, /* gdn_decode_step: force conv kernel + recurrence  */
     GDN_FLAG_PREFILL_NS3 = 32, /* prefill A/B variant: diagonal KK^T blocks by   */
-    GDN_FLAG_PREFILL_NS4 = 64  /* 3 or 4 bf16 Newton-Schulz rounds (see below)   */
+    GDN_FLAG_PREFILL_NS4 = 64, /* 3 or 4 bf16 Newton-Schulz rounds (see below)   */
+    GDN_FLAG_PREFILL_SEQUENTIAL = 128 /* prefill: never split sequences into      */
+                                      /* segments (see gdn_prefill_chunked)       */
 };
 
 enum {                      /* flags of gdn_gated_rmsnorm                         */
@@ -230,9 +232,12 @@ gdn_status gdn_decode_recurrent(const void* qkv, gdn_dtype qkv_dt,
                                 int32_t* err_flag, void* stream);
 
 /*
- * gdn_prefill_workspace_size -- bytes of device workspace gdn_prefill_chunked
- * needs for n_seqs sequences and total_tokens tokens.  Returns 0 for
- * unsupported dims.
+ * gdn_prefill_workspace_size -- bytes of device workspace with which
+ * gdn_prefill_chunked(_gated) runs the segment-parallel schedule (see
+ * gdn_prefill_segmented) for n_seqs sequences and total_tokens tokens on the
+ * current device; 0 when those sizes run whole sequences (the chip is already
+ * busy with one workgroup per (sequence, value head), or the sequences are
+ * short) and for unsupported dims.
  */
 size_t gdn_prefill_workspace_size(const gdn_dims* dims, int32_t n_seqs, int32_t total_tokens);
 
@@ -258,7 +263,16 @@ size_t gdn_prefill_workspace_size(const gdn_dims* dims, int32_t n_seqs, int32_t 
  *                by 3 or 4 Newton-Schulz rounds with bf16 intermediates, as [P4]
  *                "Numerical root cause and fix" describes, instead of the default
  *                exact fp32 forward substitution
- *   workspace    >= gdn_prefill_workspace_size(...) bytes of device memory
+ *                or GDN_FLAG_PREFILL_SEQUENTIAL
+ *   workspace    device memory, 16-byte aligned, or NULL.  With at least
+ *                gdn_prefill_workspace_size(...) bytes (and that size > 0,
+ *                and no GDN_FLAG_PREFILL_SEQUENTIAL) the call runs the
+ *                segment-parallel schedule of gdn_prefill_segmented with the
+ *                segment length the library picks for these sizes; otherwise
+ *                each (sequence, value head) is walked by one workgroup from
+ *                start to end.  The two schedules agree to rounding, not
+ *                bitwise: whole-sequence runs are bitwise independent of how a
+ *                sequence is split into calls along the 64-token grid.
  */
 gdn_status gdn_prefill_chunked(const void* q, const void* k, const void* v, gdn_dtype in_dt,
                                const float* g, const float* beta,
@@ -269,6 +283,46 @@ gdn_status gdn_prefill_chunked(const void* q, const void* k, const void* v, gdn_
                                const gdn_dims* dims, float scale, int32_t flags,
                                void* workspace, size_t workspace_bytes,
                                int32_t* err_flag, void* stream);
+
+/*
+ * gdn_prefill_segmented -- gdn_prefill_chunked with the sequences cut into
+ * segments of seg_len tokens (a positive multiple of 64, so the segments are
+ * runs of whole 64-token chunks) that are processed in parallel.  A segment
+ * maps its start state affinely: S_end = S_start P + B, where P is the
+ * segment's run from the identity with v = 0 and B its run from the zero state
+ * (the token update multiplies the state on the right by
+ * exp(g)(I - beta k k^T) and adds beta v k^T; [P1] "Notes" and "Deliberately
+ * not in this PR" mention a context-parallel prefill path without describing
+ * it; this is a one-GPU form of such a split).  Three launches:
+ * segment 0 from the slot's state together with the P and B runs of the
+ * middle segments; a scan of the start states in fp32; segments 1.. again
+ * from their start states, writing outputs and, for the last, the slot.
+ * The cost is about 2.4x the chunk work of a middle segment, for a critical
+ * path of about two segments instead of the whole sequence.
+ *
+ *   g, beta, gate  either g and beta (gate NULL) or gate (g, beta NULL; as in
+ *                  gdn_prefill_chunked_gated); GDN_ERR_FLAGS if both
+ *   seg_len        tokens per segment: GDN_ERR_DIMS unless a positive multiple
+ *                  of 64 (and at most 32768 segments of total_tokens)
+ *   workspace      >= gdn_prefill_segmented_workspace_size(dims, n_seqs,
+ *                  total_tokens, seg_len) bytes of device memory, 16-byte
+ *                  aligned: three dv x dk fp32 matrices per (segment id, value
+ *                  head), (n_seqs + total_tokens / seg_len + 1) segment ids
+ *                  (GDN_ERR_WORKSPACE if NULL or smaller, with tokens to run)
+ * Every other argument, flag (GDN_FLAG_PREFILL_SEQUENTIAL excepted:
+ * GDN_ERR_FLAGS) and error is as for gdn_prefill_chunked.
+ */
+size_t gdn_prefill_segmented_workspace_size(const gdn_dims* dims, int32_t n_seqs,
+                                            int32_t total_tokens, int32_t seg_len);
+gdn_status gdn_prefill_segmented(const void* q, const void* k, const void* v, gdn_dtype in_dt,
+                                 const float* g, const float* beta, const gdn_gate_inputs* gate,
+                                 const int32_t* cu_seqlens, int32_t n_seqs, int32_t total_tokens,
+                                 const int32_t* slot_idx,
+                                 float* rec_state, int32_t num_slots,
+                                 void* out, gdn_dtype out_dt,
+                                 const gdn_dims* dims, float scale, int32_t flags,
+                                 int32_t seg_len, void* workspace, size_t workspace_bytes,
+                                 int32_t* err_flag, void* stream);
 
 /*
  * gdn_decode_step_gated / gdn_prefill_chunked_gated -- gdn_decode_step and

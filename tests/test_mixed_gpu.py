@@ -160,8 +160,9 @@ def test_split_post_conv_prefill_on_grid_is_bitwise():
     dims = gdn.make_dims(H, HV, DK, DK, 4)
     rs_w = p["rec_state"].clone()
     out_w = torch.empty(300, HV, DK, dtype=torch.bfloat16, device="cuda")
+    seq = gdn.FLAG_QK_L2NORM | gdn.FLAG_PREFILL_SEQUENTIAL
     gdn.gdn_prefill_chunked(p["q"], p["k"], p["v"], p["g"], p["beta"], p["cu_seqlens"],
-                            p["slot_idx"], rs_w, out_w, dims, SCALE)
+                            p["slot_idx"], rs_w, out_w, dims, SCALE, flags=seq)
     rs_s = p["rec_state"].clone()
     out_s = torch.empty_like(out_w)
     for a, e in ((0, 64), (64, 192), (192, 300)):
@@ -169,7 +170,7 @@ def test_split_post_conv_prefill_on_grid_is_bitwise():
         gdn.gdn_prefill_chunked(p["q"][a:e].contiguous(), p["k"][a:e].contiguous(),
                                 p["v"][a:e].contiguous(), p["g"][a:e].contiguous(),
                                 p["beta"][a:e].contiguous(), gi.cu_from_lengths([e - a]).cuda(),
-                                p["slot_idx"], rs_s, o, dims, SCALE)
+                                p["slot_idx"], rs_s, o, dims, SCALE, flags=seq)
         out_s[a:e] = o
     torch.cuda.synchronize()
     assert torch.equal(out_s, out_w)
