@@ -32,6 +32,8 @@
 // 16 + 4q + s - 4 (s >= 4), which is exactly what two vertically adjacent
 // accumulator tiles hold in one lane.  With permuted slots the state, U and
 // (cK . U) feed MFMA B operands straight from accumulator registers.
+#include <type_traits>
+
 #include "gate.hpp"
 #include "gdn_device.hpp"
 #include "gdn_internal.hpp"
@@ -226,11 +228,10 @@ struct PrefillSmem {
     static constexpr int SK = D + PADB;         // row stride of K, Q, W (bf16)
     static constexpr int ST = CH + PADB;        // row stride of K^T, V^T, coefficient arrays
     static constexpr int SF = CH + PADF;        // row stride of fp32 64x64 arrays
-    static constexpr int VW = (D * ST > CH * SK) ? D * ST : CH * SK;
     bf16_t k[NP][CH * SK];                      // K   [t][k]
     bf16_t q[NP][CH * SK];                      // Q   [t][k]
     bf16_t kt[NP][D * ST];                      // K^T [k][t]
-    bf16_t vt_w[NP][VW];                        // V^T [v][t]; later -W [t][k] in plane 0
+    bf16_t vt[NP][D * ST];                      // V^T [v][t]
     float g[CH * SF];                           // A, then T in place (lower, unit diag, zero upper),
                                                 // except T's block [32:64][0:32], which is in xs
     struct {
@@ -274,7 +275,6 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
     constexpr int KB = D / 16;                   // 16-row key blocks of the state
     constexpr int KS = D / 32;                   // 32-wide k-steps over the head dim
     constexpr int VB = (D / 16 / NW > 0) ? D / 16 / NW : 1;   // 16-wide value blocks per wave
-    constexpr int WB = (KB / NW > 0) ? KB / NW : 1;           // 16-wide key blocks of W per wave
     constexpr int CG = PF_NT / 32;               // 8-column groups per load pass
     constexpr int CP = (D / (8 * CG) > 0) ? D / (8 * CG) : 1; // load passes
     constexpr int WPE = SPL ? 2 : 1;             // uint4 words per 8 input elements
@@ -296,7 +296,6 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
     const int32_t s = slot[n];
     const bool norm = (flags & GDN_FLAG_QK_L2NORM) != 0;
     const bool vact = wave * VB * 16 < D;        // this wave owns value columns
-    const bool wact = wave * WB < KB;            // this wave owns W columns
 
     if (s <= 0) {                                // inactive: zero outputs, state untouched
         if (SEG && (sg.pass == 2 || blockIdx.z != 0)) return;
@@ -461,7 +460,7 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
                     *reinterpret_cast<uint4*>(&sm.q[pl][ta * SK + k0]) = qw[0][pl];
                     *reinterpret_cast<uint4*>(&sm.q[pl][(ta + 1) * SK + k0]) = qw[1][pl];
                     store_pairs_t(sm.kt[pl], ST, k0, ta, kw[0][pl], kw[1][pl]);
-                    store_pairs_t(sm.vt_w[pl], ST, k0, ta, vw[0][pl], vw[1][pl]);
+                    store_pairs_t(sm.vt[pl], ST, k0, ta, vw[0][pl], vw[1][pl]);
                 }
             }
         }
@@ -564,21 +563,101 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
         }
         __syncthreads();
 
+        // ---------------- state products that need only S0 and the staged
+        // chunk: Z = K S0^T (so that W S0^T = cW Z, with no W formed) and,
+        // transposed, O1^T = S0 Q^T, scaled by e^gamma_t rq_t.  The state's
+        // hi/lo fragments (permuted k-slots) are the B operand of the first
+        // and, holding the same values, the A operand of the second.  They run
+        // on the waves the block inverse below leaves idle.
+        f32x4 z[4][VB];                          // Z tiles (t-block, v-block)
+        f32x4 o[VB][4];                          // O^T tiles (v-block, t-block)
+        auto early = [&](auto DZ, auto DO) {
+            constexpr bool dz = decltype(DZ)::value, doo = decltype(DO)::value;
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+                for (int vb = 0; vb < VB; ++vb) {
+                    if (dz) z[tb][vb] = f32x4{0, 0, 0, 0};
+                    if (doo) o[vb][tb] = f32x4{0, 0, 0, 0};
+                }
+            if (!vact) return;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                bf16x8 sh[VB], sl[VB];
+#pragma unroll
+                for (int vb = 0; vb < VB; ++vb) {
+                    uint2 h0, l0, h1, l1;
+                    split4(st[2 * ks][vb], h0, l0);
+                    split4(st[2 * ks + 1][vb], h1, l1);
+                    sh[vb] = as_bf16x8(cat(h0, h1));
+                    sl[vb] = as_bf16x8(cat(l0, l1));
+                }
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) {
+                    if constexpr (dz) {
+                        const bf16x8 ak = frag_perm(sm.k[0], SK, 16 * tb + l16, 32 * ks, q4);
+#pragma unroll
+                        for (int vb = 0; vb < VB; ++vb) {
+                            z[tb][vb] = mfma(ak, sh[vb], z[tb][vb]);
+                            z[tb][vb] = mfma(ak, sl[vb], z[tb][vb]);
+                        }
+                        if constexpr (SPL) {
+                            const bf16x8 akl = frag_perm(sm.k[NP - 1], SK, 16 * tb + l16, 32 * ks, q4);
+#pragma unroll
+                            for (int vb = 0; vb < VB; ++vb) z[tb][vb] = mfma(akl, sh[vb], z[tb][vb]);
+                        }
+                    }
+                    if (doo && (!SEG || wo)) {
+                        const bf16x8 bq = frag_perm(sm.q[0], SK, 16 * tb + l16, 32 * ks, q4);
+#pragma unroll
+                        for (int vb = 0; vb < VB; ++vb) {
+                            o[vb][tb] = mfma(sh[vb], bq, o[vb][tb]);
+                            o[vb][tb] = mfma(sl[vb], bq, o[vb][tb]);
+                        }
+                        if constexpr (SPL) {
+                            const bf16x8 bql = frag_perm(sm.q[NP - 1], SK, 16 * tb + l16, 32 * ks, q4);
+#pragma unroll
+                            for (int vb = 0; vb < VB; ++vb) o[vb][tb] = mfma(sh[vb], bql, o[vb][tb]);
+                        }
+                    }
+                }
+            }
+            if (doo && (!SEG || wo)) {
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) {
+                    const float e = sm.eg[16 * tb + l16];
+#pragma unroll
+                    for (int vb = 0; vb < VB; ++vb) {
+                        o[vb][tb][0] *= e; o[vb][tb][1] *= e; o[vb][tb][2] *= e; o[vb][tb][3] *= e;
+                    }
+                }
+            }
+        };
+        using T_ = std::true_type;
+        using F_ = std::false_type;
+
         // ---------------- T = (I + A)^-1.  Diagonal 16x16 blocks by forward
-        // substitution (wave 0: lane = 16 block + column c).  Lane c holds column
+        // substitution (wave WF: lane = 16 block + column c).  Lane c holds column
         // c of each row of the block; row r's entry A[r][j] reaches every lane of
         // the block by a DPP row broadcast from lane j.  Right-looking order: once
         // T[j][c] is final, every later row r adds A[r][j] T[j][c], so each row
         // still accumulates its terms in ascending j.  The upper triangle of
-        // sm.g is zero from the epilogue above and stays zero.
+        // sm.g is zero from the epilogue above and stays zero.  The other waves
+        // run `early` meanwhile; WF runs its Z part during the 16 -> 32 merge and
+        // its O1 part during the 32 -> 64 merge.
         // With ns_rounds > 0 the blocks are instead inverted by Newton-Schulz with
         // bf16 intermediates (an A/B variant reproducing vLLM PR #53864,
-        // "Numerical root cause and fix"): waves 0-3, one block each.
+        // "Numerical root cause and fix"): waves 0-3, one block each, and then
+        // every wave runs `early`.
+        constexpr int WF = NW - 1;               // forward-substitution wave
+        constexpr int WM = NW - 3;               // merge waves WM, WM + 1
         if constexpr (NSV) {
             if (wave < 4) ns_block_inverse(&sm.g[(16 * wave) * SF + 16 * wave], SF,
                                            reinterpret_cast<bf16_t*>(sm.xs) + 512 * wave, ns_rounds,
                                            l16, q4);
-        } else if (wave == 0) {
+            __syncthreads();
+            early(T_{}, T_{});
+        } else if (wave == WF) {
             const int b = lane >> 4;
             const int c = lane & 15;
             float* blk = &sm.g[(16 * b) * SF + 16 * b];
@@ -594,14 +673,17 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
             }
 #pragma unroll
             for (int r = 0; r < 16; ++r) blk[r * SF + c] = tc[r];
+        } else {
+            early(T_{}, T_{});
         }
         __syncthreads();
-        // merge 16 -> 32 for block pairs p = (0,1), (2,3) on fp32 MFMA (wave p):
+        // merge 16 -> 32 for block pairs p = (0,1), (2,3) on fp32 MFMA (wave WM + p):
         // X = A21 T11 goes through the LDS scratch and straight back into the same
         // wave (LDS is in order within a wave; the fence keeps the compiler from
         // reordering), then T21 = -T22 X.  Operands are loaded before the MFMAs.
-        if (wave < 2) {
-            const int b0 = 32 * wave, b1 = b0 + 16;
+        if (wave == WM || wave == WM + 1) {
+            const int pw = wave - WM;
+            const int b0 = 32 * pw, b1 = b0 + 16;
             float a[4], bb[4];
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
@@ -612,27 +694,29 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) x = mfma4(a[kk], bb[kk], x);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sm.xs[(16 * wave + 4 * q4 + r) * 36 + l16] = x[r];
+            for (int r = 0; r < 4; ++r) sm.xs[(16 * pw + 4 * q4 + r) * 36 + l16] = x[r];
             __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
                 a[kk] = sm.g[(b1 + l16) * SF + b1 + 4 * kk + q4];
-                bb[kk] = sm.xs[(16 * wave + 4 * kk + q4) * 36 + l16];
+                bb[kk] = sm.xs[(16 * pw + 4 * kk + q4) * 36 + l16];
             }
             f32x4 t = f32x4{0, 0, 0, 0};
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) t = mfma4(a[kk], bb[kk], t);
 #pragma unroll
             for (int r = 0; r < 4; ++r) sm.g[(b1 + 4 * q4 + r) * SF + b0 + l16] = -t[r];
+        } else if (!NSV && wave == WF) {
+            early(T_{}, F_{});
         }
         __syncthreads();
-        // merge 32 -> 64 (wave tj < 2: output column block tj of the lower-left
-        // 32x32 block, both row blocks ti): X[:, tj] = A[32:64][0:32] T11[:, tj],
-        // then T21[:, tj] = -T22 X[:, tj], the same wave-local LDS round trip;
-        // T21 is left in xs.  T11's block (0, 1) and T22's block (0, 1) are zero:
-        // skipped.
-        if (wave < 2) {
-            const int tj = wave;
+        // merge 32 -> 64 (wave WM + tj, tj < 2: output column block tj of the
+        // lower-left 32x32 block, both row blocks ti): X[:, tj] = A[32:64][0:32]
+        // T11[:, tj], then T21[:, tj] = -T22 X[:, tj], the same wave-local LDS
+        // round trip; T21 is left in xs.  T11's block (0, 1) and T22's block
+        // (0, 1) are zero: skipped.
+        if (wave == WM || wave == WM + 1) {
+            const int tj = wave - WM;
             const int k0 = 4 * tj;                 // T11[:, tj] is zero above row 16 tj
             float a[2][8], bb[8];
 #pragma unroll
@@ -673,6 +757,8 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
             for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) sm.xs[(16 * ti + 4 * q4 + r) * 36 + 16 * tj + l16] = -t[ti][r];
+        } else if (!NSV && wave == WF) {
+            early(F_{}, T_{});
         }
         __syncthreads();
 
@@ -701,8 +787,11 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
         }
         __syncthreads();
 
-        // ---------------- Ut = cU V (wave's value columns) and W = cW K
-        // (split coefficients x raw planes: hh + lh (+ hl for split inputs))
+        // ---------------- U = cU V - cW Z (wave's value columns): Ut = cU V with
+        // the split coefficients on the raw V planes (hh + lh (+ hl for split
+        // inputs)), then cW (split) times -Z (split, permuted t-slots from the
+        // accumulators: hh + hl + lh).  Both coefficient matrices are lower
+        // triangular: blocks above the diagonal are zero and skipped.
         f32x4 u[4][VB];                          // U tiles (t-block, v-block): rows t, cols v
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb)
@@ -713,127 +802,50 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
             for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
+                    if (32 * ks > 16 * tb + 15) continue;          // strictly above the diagonal
                     const bf16x8 ah = frag_std(sm.pc.c + 2 * CH * ST, ST, 16 * tb + l16, 32 * ks, q4);
                     const bf16x8 al = frag_std(sm.pc.c + 3 * CH * ST, ST, 16 * tb + l16, 32 * ks, q4);
 #pragma unroll
                     for (int vb = 0; vb < VB; ++vb) {
                         const int vr = 16 * (wave * VB + vb) + l16;
-                        const bf16x8 bv = frag_std(sm.vt_w[0], ST, vr, 32 * ks, q4);
+                        const bf16x8 bv = frag_std(sm.vt[0], ST, vr, 32 * ks, q4);
                         u[tb][vb] = mfma(ah, bv, u[tb][vb]);
                         u[tb][vb] = mfma(al, bv, u[tb][vb]);
                         if constexpr (SPL)
-                            u[tb][vb] = mfma(ah, frag_std(sm.vt_w[NP - 1], ST, vr, 32 * ks, q4), u[tb][vb]);
+                            u[tb][vb] = mfma(ah, frag_std(sm.vt[NP - 1], ST, vr, 32 * ks, q4), u[tb][vb]);
                     }
                 }
-        }
-        f32x4 w[4][WB];
+            bf16x8 zh[2][VB], zl[2][VB];
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
+            for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int kb = 0; kb < WB; ++kb) w[tb][kb] = f32x4{0, 0, 0, 0};
-        if (wact) {
+                for (int vb = 0; vb < VB; ++vb) {
+                    f32x4 n0 = z[2 * ks][vb], n1 = z[2 * ks + 1][vb];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) { n0[r] = -n0[r]; n1[r] = -n1[r]; }
+                    uint2 h0, l0, h1, l1;
+                    split4(n0, h0, l0);
+                    split4(n1, h1, l1);
+                    zh[ks][vb] = as_bf16x8(cat(h0, h1));
+                    zl[ks][vb] = as_bf16x8(cat(l0, l1));
+                }
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
-                    const bf16x8 ah = frag_std(sm.pc.c + 0 * CH * ST, ST, 16 * tb + l16, 32 * ks, q4);
-                    const bf16x8 al = frag_std(sm.pc.c + 1 * CH * ST, ST, 16 * tb + l16, 32 * ks, q4);
-#pragma unroll
-                    for (int kb = 0; kb < WB; ++kb) {
-                        const int kr = 16 * (wave * WB + kb) + l16;
-                        const bf16x8 bk = frag_std(sm.kt[0], ST, kr, 32 * ks, q4);
-                        w[tb][kb] = mfma(ah, bk, w[tb][kb]);
-                        w[tb][kb] = mfma(al, bk, w[tb][kb]);
-                        if constexpr (SPL)
-                            w[tb][kb] = mfma(ah, frag_std(sm.kt[NP - 1], ST, kr, 32 * ks, q4), w[tb][kb]);
-                    }
-                }
-        }
-        __syncthreads();                         // V^T is dead: its plane 0 takes -W
-        if (wact) {
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-                for (int kb = 0; kb < WB; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        sm.vt_w[0][(16 * tb + 4 * q4 + r) * SK + 16 * (wave * WB + kb) + l16] = f32_to_bf16(-w[tb][kb][r]);
-        }
-        __syncthreads();                         // -W visible to all waves
-
-        if (SEG && vact && !wo) {
-            // ------------ U = Ut - W S0^T alone (a segment-map run writes no
-            // outputs); the same contraction order as below
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                bf16x8 sh[VB], sl[VB];
-#pragma unroll
-                for (int vb = 0; vb < VB; ++vb) {
-                    uint2 h0, l0, h1, l1;
-                    split4(st[2 * ks][vb], h0, l0);
-                    split4(st[2 * ks + 1][vb], h1, l1);
-                    sh[vb] = as_bf16x8(cat(h0, h1));
-                    sl[vb] = as_bf16x8(cat(l0, l1));
-                }
-#pragma unroll
-                for (int tb = 0; tb < 4; ++tb) {
-                    const bf16x8 aw = frag_perm(sm.vt_w[0], SK, 16 * tb + l16, 32 * ks, q4);
+                    if (32 * ks > 16 * tb + 15) continue;
+                    const bf16x8 wh = frag_perm(sm.pc.c + 0 * CH * ST, ST, 16 * tb + l16, 32 * ks, q4);
+                    const bf16x8 wl = frag_perm(sm.pc.c + 1 * CH * ST, ST, 16 * tb + l16, 32 * ks, q4);
 #pragma unroll
                     for (int vb = 0; vb < VB; ++vb) {
-                        u[tb][vb] = mfma(aw, sh[vb], u[tb][vb]);
-                        u[tb][vb] = mfma(aw, sl[vb], u[tb][vb]);
+                        u[tb][vb] = mfma(wh, zh[ks][vb], u[tb][vb]);
+                        u[tb][vb] = mfma(wh, zl[ks][vb], u[tb][vb]);
+                        u[tb][vb] = mfma(wl, zh[ks][vb], u[tb][vb]);
                     }
                 }
-            }
         }
+
         if (vact && (!SEG || wo)) {
-            // ------------ U = Ut - W S0^T and, transposed, O1^T = S0 Q^T.  The
-            // state's hi/lo fragments (permuted k-slots) are the B operand of the
-            // first and, holding the same values, the A operand of the second.
-            f32x4 o[VB][4];                      // O^T tiles (v-block, t-block)
-#pragma unroll
-            for (int vb = 0; vb < VB; ++vb)
-#pragma unroll
-                for (int tb = 0; tb < 4; ++tb) o[vb][tb] = f32x4{0, 0, 0, 0};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                bf16x8 sh[VB], sl[VB];
-#pragma unroll
-                for (int vb = 0; vb < VB; ++vb) {
-                    uint2 h0, l0, h1, l1;
-                    split4(st[2 * ks][vb], h0, l0);
-                    split4(st[2 * ks + 1][vb], h1, l1);
-                    sh[vb] = as_bf16x8(cat(h0, h1));
-                    sl[vb] = as_bf16x8(cat(l0, l1));
-                }
-#pragma unroll
-                for (int tb = 0; tb < 4; ++tb) {
-                    const bf16x8 aw = frag_perm(sm.vt_w[0], SK, 16 * tb + l16, 32 * ks, q4);
-                    const bf16x8 bq = frag_perm(sm.q[0], SK, 16 * tb + l16, 32 * ks, q4);
-#pragma unroll
-                    for (int vb = 0; vb < VB; ++vb) {
-                        u[tb][vb] = mfma(aw, sh[vb], u[tb][vb]);
-                        u[tb][vb] = mfma(aw, sl[vb], u[tb][vb]);
-                        o[vb][tb] = mfma(sh[vb], bq, o[vb][tb]);
-                        o[vb][tb] = mfma(sl[vb], bq, o[vb][tb]);
-                    }
-                    if constexpr (SPL) {
-                        const bf16x8 bql = frag_perm(sm.q[NP - 1], SK, 16 * tb + l16, 32 * ks, q4);
-#pragma unroll
-                        for (int vb = 0; vb < VB; ++vb) o[vb][tb] = mfma(sh[vb], bql, o[vb][tb]);
-                    }
-                }
-            }
-            // O1^T columns (tokens) scaled by e^gamma_t rq_t
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                const float e = sm.eg[16 * tb + l16];
-#pragma unroll
-                for (int vb = 0; vb < VB; ++vb) {
-                    o[vb][tb][0] *= e; o[vb][tb][1] *= e; o[vb][tb][2] *= e; o[vb][tb][3] *= e;
-                }
-            }
-
             // ------------ O^T += U^T (M o P)^T  (U split: A operand, permuted t-slots)
             bf16x8 uh[2][VB], ul[2][VB];
 #pragma unroll
