@@ -119,11 +119,19 @@ __device__ __forceinline__ float row_bcast(float x, int j) {
 __device__ __forceinline__ bf16x8 frag_std(const bf16_t* base, int stride, int row, int c0, int q) {
     return as_bf16x8(*reinterpret_cast<const uint4*>(base + row * stride + c0 + 8 * q));
 }
-// Permuted-slot fragment: 4 bf16 at c0 + 4q and 4 bf16 at c0 + 16 + 4q.
+// Arrays read with permuted k-slots are stored with each 32-element block
+// reordered: element 4b + s (b < 8, s < 4) of a block sits at position 8b + s
+// for b < 4 and at 8(b - 4) + 4 + s otherwise, so the eight elements a lane's
+// permuted slots name (c0 + 4q .. + 3 and c0 + 16 + 4q .. + 3) are contiguous
+// at c0 + 8q: one 16-byte read with an immediate offset.  A product of two
+// such arrays along their permuted dimension (K K^T, Q K^T) is unchanged.
+__host__ __device__ constexpr int pperm(int e) {
+    return (e & ~31) + (((e & 31) >> 2) < 4 ? 8 * ((e & 31) >> 2) : 8 * (((e & 31) >> 2) - 4) + 4) + (e & 3);
+}
+// Permuted-slot fragment (from an array in pperm order): the elements
+// c0 + 4q .. + 3 and c0 + 16 + 4q .. + 3 of row `row`.
 __device__ __forceinline__ bf16x8 frag_perm(const bf16_t* base, int stride, int row, int c0, int q) {
-    const uint2 a = *reinterpret_cast<const uint2*>(base + row * stride + c0 + 4 * q);
-    const uint2 b = *reinterpret_cast<const uint2*>(base + row * stride + c0 + 16 + 4 * q);
-    return as_bf16x8(cat(a, b));
+    return as_bf16x8(*reinterpret_cast<const uint4*>(base + row * stride + c0 + 8 * q));
 }
 
 // Eight fp32 values (two uint4 of bits) into packed bf16 hi and lo words.
@@ -142,7 +150,8 @@ __device__ __forceinline__ void split8(const uint4& a, const uint4& b, uint4& hi
 }
 
 // Store the 32-bit (t, t+1) pairs of two token rows' 8 columns into a
-// transposed [col][t] array at column c0, token t = ta (even).
+// transposed [col][t] array at column c0, token position ta (even; the pair
+// stays adjacent under pperm).
 __device__ __forceinline__ void store_pairs_t(bf16_t* arr, int stride, int c0, int ta, const uint4& ra,
                                               const uint4& rb) {
     const uint32_t* a32 = reinterpret_cast<const uint32_t*>(&ra);
@@ -455,11 +464,16 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
                 }
 #pragma unroll
                 for (int pl = 0; pl < NP; ++pl) {
-                    *reinterpret_cast<uint4*>(&sm.k[pl][ta * SK + k0]) = kw[0][pl];
-                    *reinterpret_cast<uint4*>(&sm.k[pl][(ta + 1) * SK + k0]) = kw[1][pl];
-                    *reinterpret_cast<uint4*>(&sm.q[pl][ta * SK + k0]) = qw[0][pl];
-                    *reinterpret_cast<uint4*>(&sm.q[pl][(ta + 1) * SK + k0]) = qw[1][pl];
-                    store_pairs_t(sm.kt[pl], ST, k0, ta, kw[0][pl], kw[1][pl]);
+                    // K and Q rows in pperm order along k; K^T in pperm order along t
+                    const int p0 = pperm(k0), p1 = pperm(k0 + 4);
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        *reinterpret_cast<uint2*>(&sm.k[pl][(ta + e) * SK + p0]) = make_uint2(kw[e][pl].x, kw[e][pl].y);
+                        *reinterpret_cast<uint2*>(&sm.k[pl][(ta + e) * SK + p1]) = make_uint2(kw[e][pl].z, kw[e][pl].w);
+                        *reinterpret_cast<uint2*>(&sm.q[pl][(ta + e) * SK + p0]) = make_uint2(qw[e][pl].x, qw[e][pl].y);
+                        *reinterpret_cast<uint2*>(&sm.q[pl][(ta + e) * SK + p1]) = make_uint2(qw[e][pl].z, qw[e][pl].w);
+                    }
+                    store_pairs_t(sm.kt[pl], ST, k0, pperm(ta), kw[0][pl], kw[1][pl]);
                     store_pairs_t(sm.vt[pl], ST, k0, ta, vw[0][pl], vw[1][pl]);
                 }
             }
@@ -557,8 +571,8 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
                 *reinterpret_cast<float4*>(&sm.g[i * SF + c]) = make_float4(a[0], a[1], a[2], a[3]);
                 uint2 h2, l2;
                 split4(mp, h2, l2);
-                *reinterpret_cast<uint2*>(&sm.mp[i * ST + c]) = h2;
-                *reinterpret_cast<uint2*>(&sm.mp[CH * ST + i * ST + c]) = l2;
+                *reinterpret_cast<uint2*>(&sm.mp[i * ST + pperm(c)]) = h2;         // pperm order
+                *reinterpret_cast<uint2*>(&sm.mp[CH * ST + i * ST + pperm(c)]) = l2;
             }
         }
         __syncthreads();
@@ -581,8 +595,25 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
                     if (doo) o[vb][tb] = f32x4{0, 0, 0, 0};
                 }
             if (!vact) return;
+            // per k-step: every fragment load first, then the state split (VALU
+            // work that covers the loads' latency), then the MFMAs; the
+            // scheduling barriers keep the compiler from sinking each load
+            // next to its first use
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
+                bf16x8 ak[4], akl[4], bq[4], bql[4];
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) {
+                    if constexpr (dz) {
+                        ak[tb] = frag_perm(sm.k[0], SK, 16 * tb + l16, 32 * ks, q4);
+                        if constexpr (SPL) akl[tb] = frag_perm(sm.k[NP - 1], SK, 16 * tb + l16, 32 * ks, q4);
+                    }
+                    if (doo && (!SEG || wo)) {
+                        bq[tb] = frag_perm(sm.q[0], SK, 16 * tb + l16, 32 * ks, q4);
+                        if constexpr (SPL) bql[tb] = frag_perm(sm.q[NP - 1], SK, 16 * tb + l16, 32 * ks, q4);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
                 bf16x8 sh[VB], sl[VB];
 #pragma unroll
                 for (int vb = 0; vb < VB; ++vb) {
@@ -592,32 +623,29 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
                     sh[vb] = as_bf16x8(cat(h0, h1));
                     sl[vb] = as_bf16x8(cat(l0, l1));
                 }
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb) {
                     if constexpr (dz) {
-                        const bf16x8 ak = frag_perm(sm.k[0], SK, 16 * tb + l16, 32 * ks, q4);
 #pragma unroll
                         for (int vb = 0; vb < VB; ++vb) {
-                            z[tb][vb] = mfma(ak, sh[vb], z[tb][vb]);
-                            z[tb][vb] = mfma(ak, sl[vb], z[tb][vb]);
+                            z[tb][vb] = mfma(ak[tb], sh[vb], z[tb][vb]);
+                            z[tb][vb] = mfma(ak[tb], sl[vb], z[tb][vb]);
                         }
                         if constexpr (SPL) {
-                            const bf16x8 akl = frag_perm(sm.k[NP - 1], SK, 16 * tb + l16, 32 * ks, q4);
 #pragma unroll
-                            for (int vb = 0; vb < VB; ++vb) z[tb][vb] = mfma(akl, sh[vb], z[tb][vb]);
+                            for (int vb = 0; vb < VB; ++vb) z[tb][vb] = mfma(akl[tb], sh[vb], z[tb][vb]);
                         }
                     }
                     if (doo && (!SEG || wo)) {
-                        const bf16x8 bq = frag_perm(sm.q[0], SK, 16 * tb + l16, 32 * ks, q4);
 #pragma unroll
                         for (int vb = 0; vb < VB; ++vb) {
-                            o[vb][tb] = mfma(sh[vb], bq, o[vb][tb]);
-                            o[vb][tb] = mfma(sl[vb], bq, o[vb][tb]);
+                            o[vb][tb] = mfma(sh[vb], bq[tb], o[vb][tb]);
+                            o[vb][tb] = mfma(sl[vb], bq[tb], o[vb][tb]);
                         }
                         if constexpr (SPL) {
-                            const bf16x8 bql = frag_perm(sm.q[NP - 1], SK, 16 * tb + l16, 32 * ks, q4);
 #pragma unroll
-                            for (int vb = 0; vb < VB; ++vb) o[vb][tb] = mfma(sh[vb], bql, o[vb][tb]);
+                            for (int vb = 0; vb < VB; ++vb) o[vb][tb] = mfma(sh[vb], bql[tb], o[vb][tb]);
                         }
                     }
                 }
@@ -780,8 +808,11 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
                 split4(u, h2, l2); uh[2 * j] = h2.x; uh[2 * j + 1] = h2.y; ul[2 * j] = l2.x; ul[2 * j + 1] = l2.y;
             }
             bf16_t* base = sm.pc.c + r * ST + cb;
-            *reinterpret_cast<uint4*>(base + 0 * CH * ST) = make_uint4(wh[0], wh[1], wh[2], wh[3]);
-            *reinterpret_cast<uint4*>(base + 1 * CH * ST) = make_uint4(wl[0], wl[1], wl[2], wl[3]);
+            bf16_t* wbase = sm.pc.c + r * ST;            // cW planes in pperm order
+            *reinterpret_cast<uint2*>(wbase + 0 * CH * ST + pperm(cb)) = make_uint2(wh[0], wh[1]);
+            *reinterpret_cast<uint2*>(wbase + 0 * CH * ST + pperm(cb + 4)) = make_uint2(wh[2], wh[3]);
+            *reinterpret_cast<uint2*>(wbase + 1 * CH * ST + pperm(cb)) = make_uint2(wl[0], wl[1]);
+            *reinterpret_cast<uint2*>(wbase + 1 * CH * ST + pperm(cb + 4)) = make_uint2(wl[2], wl[3]);
             *reinterpret_cast<uint4*>(base + 2 * CH * ST) = make_uint4(uh[0], uh[1], uh[2], uh[3]);
             *reinterpret_cast<uint4*>(base + 3 * CH * ST) = make_uint4(ul[0], ul[1], ul[2], ul[3]);
         }
