@@ -1059,7 +1059,8 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, gdn_dtype
 // (row v of a state depends only on row v of the previous one, so a workgroup
 // owns 16 state rows of one (sequence, value head); the sum over the inner
 // index runs in ascending order with fused multiply-adds, fp32).  P_j is staged
-// in LDS each step; the 16 rows stay in LDS between steps.
+// in LDS each step from registers loaded during the previous step; the 16 rows
+// stay in LDS between steps.
 template <int D>
 __global__ __launch_bounds__(256) void prefill_seg_scan_kernel(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ slot, int32_t HV, int32_t seg_len,
@@ -1081,20 +1082,39 @@ __global__ __launch_bounds__(256) void prefill_seg_scan_kernel(
     const int r = tid >> 4;                      // row within the block
     const int c0 = (tid & 15) * CPT;             // first column
     const int v = 16 * rb + r;
+    constexpr int PL = D * D / 4 / 256;          // float4 of P per thread
+    f32x4 pre[PL];
+    float bn[CPT];                               // the next step's B row part
+    {
+        const f32x4* p = reinterpret_cast<const f32x4*>(wsm(id0 + 1, 1));
+#pragma unroll
+        for (int k = 0; k < PL; ++k) pre[k] = p[tid + 256 * k];
+        const float* b = wsm(id0 + 1, 2) + static_cast<size_t>(v) * D + c0;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) bn[c] = b[c];
+    }
     {
         const float* s1 = wsm(id0 + 1, 0);
 #pragma unroll
         for (int c = 0; c < CPT; ++c) rows[r * D + c0 + c] = s1[static_cast<size_t>(v) * D + c0 + c];
     }
     for (int j = 1; j <= nseg - 2; ++j) {
-        const float4* p = reinterpret_cast<const float4*>(wsm(id0 + j, 1));
         __syncthreads();                         // previous step's reads of ps are done
-        for (int i = tid; i < D * D / 4; i += 256) reinterpret_cast<float4*>(ps)[i] = p[i];
-        const float* b = wsm(id0 + j, 2) + static_cast<size_t>(v) * D + c0;
+#pragma unroll
+        for (int k = 0; k < PL; ++k) reinterpret_cast<f32x4*>(ps)[tid + 256 * k] = pre[k];
         float acc[CPT];
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) acc[c] = b[c];
+        for (int c = 0; c < CPT; ++c) acc[c] = bn[c];
         __syncthreads();
+        {                                        // the next step's P and B (the last step reloads its own)
+            const int jn = j + 1 <= nseg - 2 ? j + 1 : j;
+            const f32x4* p = reinterpret_cast<const f32x4*>(wsm(id0 + jn, 1));
+#pragma unroll
+            for (int k = 0; k < PL; ++k) pre[k] = p[tid + 256 * k];
+            const float* b = wsm(id0 + jn, 2) + static_cast<size_t>(v) * D + c0;
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) bn[c] = b[c];
+        }
         for (int i = 0; i < D; ++i) {
             const float x = rows[r * D + i];
 #pragma unroll
