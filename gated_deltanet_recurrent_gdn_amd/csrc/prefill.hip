@@ -260,10 +260,10 @@ constexpr int PF_NT = 64 * PF_NW;        // threads per workgroup
 // Which part of each sequence a launch walks.  Pass 0: whole sequences.
 // Segment passes (segments of seg_len tokens, a multiple of CH; blockIdx.z
 // picks the segment): pass 1 runs segment 0 from the slot's state (z = 0) and
-// each middle segment j from the zero state (z = 2j, its B) and from the
-// identity with v = 0 (z = 2j + 1, its P), the last two without outputs;
-// pass 2 reruns segment j = z + 1 from its composed start state.  ws holds
-// the D x D fp32 matrices [segment id][start, P, B][value head].
+// each middle segment j (z = j) as a pair of runs in one workgroup, from the
+// zero state (its B) and from the identity with v = 0 (its P), both without
+// outputs; pass 2 reruns segment j = z + 1 from its composed start state.  ws
+// holds the D x D fp32 matrices [segment id][start, P, B][value head].
 struct SegArgs {
     float* ws;
     int32_t seg_len;
@@ -319,14 +319,18 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
     float* S = rec + (static_cast<size_t>(s) * HV + hv) * static_cast<size_t>(D) * D;
 
     // The tokens [a0, a1) this workgroup walks, where its start state comes
-    // from (0: the slot, 1: zero, 2: identity, 3: `init`), whether it writes
-    // outputs and reads v, and where its end state goes (nullptr: dropped).
-    // Whole-sequence launches (SEG false) compile none of the segment logic.
+    // from (0: the slot, 1: zero, 3: `init`), whether it writes outputs, and
+    // where its end state goes (nullptr: dropped).  A paired workgroup (pb)
+    // also carries a second state from the identity with v = 0 (a middle
+    // segment's P run beside its B run, sharing every intra-chunk step) and
+    // writes it to fin2.  Whole-sequence launches (SEG false) compile none of
+    // the segment logic.
     int32_t a0 = t0, a1 = t1;
     int init_mode = 0;
     const float* init = S;
     float* fin = S;
-    bool wo = true, vzero = false;
+    float* fin2 = nullptr;
+    bool wo = true, pb = false;
     if constexpr (SEG) {
         const int32_t seg = sg.seg_len;
         const int32_t nseg = (t1 - t0 + seg - 1) / seg;
@@ -336,11 +340,10 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
         };
         const int z = blockIdx.z;
         if (sg.pass == 1) {
-            const int j = z >> 1;
+            const int j = z;
             if (nseg <= 1) {
                 if (z != 0) return;              // one segment: the whole run, as pass 0
             } else if (j == 0) {
-                if (z != 0) return;
                 a1 = t0 + seg;
                 fin = wsm(id0 + 1, 0);           // start state of segment 1
             } else {
@@ -348,8 +351,10 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
                 a0 = t0 + j * seg;
                 a1 = a0 + seg;
                 wo = false;
-                if (z & 1) { init_mode = 2; vzero = true; fin = wsm(id0 + j, 1); }
-                else       { init_mode = 1; fin = wsm(id0 + j, 2); }
+                pb = true;
+                init_mode = 1;
+                fin = wsm(id0 + j, 2);           // B: the run from zero
+                fin2 = wsm(id0 + j, 1);          // P: the run from the identity, v = 0
             }
         } else {
             const int j = z + 1;
@@ -364,20 +369,24 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
 
     // ---- state S0^T [k][v] in accumulator layout: tile (kb, vb) lane holds
     //      S0^T[16 kb + 4 q4 + r][16 (wave VB + vb) + l16] = S[v][k..k+3]
-    f32x4 st[KB][VB];
+    f32x4 st[KB][VB], st2[KB][VB];           // st2: the paired P run's state
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int vb = 0; vb < VB; ++vb) {
             st[kb][vb] = f32x4{0, 0, 0, 0};
+            st2[kb][vb] = f32x4{0, 0, 0, 0};
             if (vact) {
                 const int v = 16 * (wave * VB + vb) + l16;
                 if (!SEG || init_mode == 0 || init_mode == 3) {
                     const float4 x = *reinterpret_cast<const float4*>(init + static_cast<size_t>(v) * D + 16 * kb + 4 * q4);
                     st[kb][vb] = f32x4{x.x, x.y, x.z, x.w};
-                } else if (init_mode == 2) {
+                }
+                if constexpr (SEG) {
+                    if (pb) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) st[kb][vb][r] = (16 * kb + 4 * q4 + r == v) ? 1.0f : 0.0f;
+                        for (int r = 0; r < 4; ++r) st2[kb][vb][r] = (16 * kb + 4 * q4 + r == v) ? 1.0f : 0.0f;
+                    }
                 }
             }
         }
@@ -404,7 +413,7 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
     auto fetch = [&](int32_t c, int Lc) {
         const rsrc_t rk_ = make_rsrc(kg + static_cast<size_t>(c) * sqk, Lc * row_kq);
         const rsrc_t rq_ = make_rsrc(qg + static_cast<size_t>(c) * sqk, Lc * row_kq);
-        const rsrc_t rv_ = make_rsrc(vg + static_cast<size_t>(c) * sv, vzero ? 0u : Lc * row_v);
+        const rsrc_t rv_ = make_rsrc(vg + static_cast<size_t>(c) * sv, Lc * row_v);
 #pragma unroll
         for (int pass = 0; pass < CP; ++pass) {
             const int k0 = 8 * (cg + CG * pass);
@@ -444,6 +453,19 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
 
     for (int32_t c0 = a0; c0 < a1; c0 += CH) {
         const int L = min(CH, a1 - c0);
+        // Segment launches: the lane coordinates re-derived each chunk from an
+        // opaque copy of the thread index, so the compiler recomputes the
+        // chunk's LDS addresses inside the loop instead of holding them in
+        // registers across it (the registers the paired P/B runs need).
+        // Whole-sequence launches keep the hoisted addresses (faster there).
+        int tid_o = static_cast<int>(threadIdx.x);
+        if constexpr (SEG) asm volatile("" : "+v"(tid_o));
+        const int tid = tid_o;
+        const int lane = tid & 63;
+        const int q4 = lane >> 4;
+        const int l16 = lane & 15;
+        const int tp = tid & 31;
+        const int ta = 2 * tp;
 
         // ---------------- stage the fetched chunk into LDS (planes hi [, lo])
 #pragma unroll
@@ -604,7 +626,7 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
                 bf16x8 ak[4], akl[4], bq[4], bql[4];
 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb) {
-                    if constexpr (dz) {
+                    if (dz || (SEG && doo && pb)) {
                         ak[tb] = frag_perm(sm.k[0], SK, 16 * tb + l16, 32 * ks, q4);
                         if constexpr (SPL) akl[tb] = frag_perm(sm.k[NP - 1], SK, 16 * tb + l16, 32 * ks, q4);
                     }
@@ -624,6 +646,25 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
                     sl[vb] = as_bf16x8(cat(l0, l1));
                 }
                 __builtin_amdgcn_sched_barrier(0);
+                if constexpr (SEG && doo) {
+                    // paired P run: its Z (from st2) accumulates in the O tiles,
+                    // which a run without outputs does not use
+                    if (pb) {
+#pragma unroll
+                        for (int vb = 0; vb < VB; ++vb) {
+                            uint2 h0, l0, h1, l1;
+                            split4(st2[2 * ks][vb], h0, l0);
+                            split4(st2[2 * ks + 1][vb], h1, l1);
+                            const bf16x8 s2h = as_bf16x8(cat(h0, h1)), s2l = as_bf16x8(cat(l0, l1));
+#pragma unroll
+                            for (int tb = 0; tb < 4; ++tb) {
+                                o[vb][tb] = mfma(ak[tb], s2h, o[vb][tb]);
+                                o[vb][tb] = mfma(ak[tb], s2l, o[vb][tb]);
+                                if constexpr (SPL) o[vb][tb] = mfma(akl[tb], s2h, o[vb][tb]);
+                            }
+                        }
+                    }
+                }
 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb) {
                     if constexpr (dz) {
@@ -824,10 +865,11 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
         // accumulators: hh + hl + lh).  Both coefficient matrices are lower
         // triangular: blocks above the diagonal are zero and skipped.
         f32x4 u[4][VB];                          // U tiles (t-block, v-block): rows t, cols v
+        f32x4 u2[4][VB];                         // the paired P run's U (= -cW Z2; its v is 0)
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-            for (int vb = 0; vb < VB; ++vb) u[tb][vb] = f32x4{0, 0, 0, 0};
+            for (int vb = 0; vb < VB; ++vb) { u[tb][vb] = f32x4{0, 0, 0, 0}; u2[tb][vb] = f32x4{0, 0, 0, 0}; }
         if (vact) {
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb)
@@ -874,6 +916,37 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
                         u[tb][vb] = mfma(wl, zh[ks][vb], u[tb][vb]);
                     }
                 }
+            if constexpr (SEG) {
+                if (pb) {                        // U2 = -cW Z2, Z2 held in the O tiles
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                        for (int vb = 0; vb < VB; ++vb) {
+                            f32x4 n0 = o[vb][2 * ks], n1 = o[vb][2 * ks + 1];
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) { n0[r] = -n0[r]; n1[r] = -n1[r]; }
+                            uint2 h0, l0, h1, l1;
+                            split4(n0, h0, l0);
+                            split4(n1, h1, l1);
+                            zh[ks][vb] = as_bf16x8(cat(h0, h1));
+                            zl[ks][vb] = as_bf16x8(cat(l0, l1));
+                        }
+#pragma unroll
+                    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+                        for (int ks = 0; ks < 2; ++ks) {
+                            if (32 * ks > 16 * tb + 15) continue;
+                            const bf16x8 wh = frag_perm(sm.pc.c + 0 * CH * ST, ST, 16 * tb + l16, 32 * ks, q4);
+                            const bf16x8 wl = frag_perm(sm.pc.c + 1 * CH * ST, ST, 16 * tb + l16, 32 * ks, q4);
+#pragma unroll
+                            for (int vb = 0; vb < VB; ++vb) {
+                                u2[tb][vb] = mfma(wh, zh[ks][vb], u2[tb][vb]);
+                                u2[tb][vb] = mfma(wh, zl[ks][vb], u2[tb][vb]);
+                                u2[tb][vb] = mfma(wl, zh[ks][vb], u2[tb][vb]);
+                            }
+                        }
+                }
+            }
         }
 
         if (vact && (!SEG || wo)) {
@@ -943,6 +1016,27 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
                     ch[ks][vb] = as_bf16x8(cat(h0, h1));
                     cl[ks][vb] = as_bf16x8(cat(l0, l1));
                 }
+            bf16x8 c2h[2][VB], c2l[2][VB];       // the paired P run's cK . U2
+            if constexpr (SEG) {
+                if (pb) {
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                        for (int vb = 0; vb < VB; ++vb) {
+                            f32x4 a = u2[2 * ks][vb], b = u2[2 * ks + 1][vb];
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                a[r] *= sm.ck[32 * ks + 4 * q4 + r];
+                                b[r] *= sm.ck[32 * ks + 16 + 4 * q4 + r];
+                            }
+                            uint2 h0, l0, h1, l1;
+                            split4(a, h0, l0);
+                            split4(b, h1, l1);
+                            c2h[ks][vb] = as_bf16x8(cat(h0, h1));
+                            c2l[ks][vb] = as_bf16x8(cat(l0, l1));
+                        }
+                }
+            }
             if (c0 + CH < a1) fetch(c0 + CH, min(CH, a1 - c0 - CH));   // next chunk, in flight
             const float egl = sm.egl;
 #pragma unroll
@@ -964,6 +1058,19 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
                         if constexpr (SPL) acc = mfma(akl[ks], ch[ks][vb], acc);
                     }
                     st[kb][vb] = acc;
+                    if constexpr (SEG) {
+                        if (pb) {
+                            f32x4 acc2 = st2[kb][vb];
+                            acc2[0] *= egl; acc2[1] *= egl; acc2[2] *= egl; acc2[3] *= egl;
+#pragma unroll
+                            for (int ks = 0; ks < 2; ++ks) {
+                                acc2 = mfma(ak[ks], c2h[ks][vb], acc2);
+                                acc2 = mfma(ak[ks], c2l[ks][vb], acc2);
+                                if constexpr (SPL) acc2 = mfma(akl[ks], c2h[ks][vb], acc2);
+                            }
+                            st2[kb][vb] = acc2;
+                        }
+                    }
                 }
             }
         }
@@ -971,7 +1078,20 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
         __syncthreads();                         // LDS is rewritten by the next chunk
     }
 
-    // ---- final state back to the slot (or to the segment workspace)
+    // ---- the paired P run's end state, then the final state back to the slot
+    //      (or to the segment workspace)
+    if constexpr (SEG) {
+        if (vact && pb) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int vb = 0; vb < VB; ++vb) {
+                    const int v = 16 * (wave * VB + vb) + l16;
+                    *reinterpret_cast<float4*>(fin2 + static_cast<size_t>(v) * D + 16 * kb + 4 * q4) =
+                        make_float4(st2[kb][vb][0], st2[kb][vb][1], st2[kb][vb][2], st2[kb][vb][3]);
+                }
+        }
+    }
     if (vact && (!SEG || fin)) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
@@ -1144,10 +1264,11 @@ size_t prefill_segmented_workspace(const gdn_dims& d, int32_t n_seqs, int32_t to
 
 // Model (per-chunk workgroup time as the unit, one workgroup per CU, equal
 // sequence lengths): whole sequences take c = chunks per sequence; with m
-// segments of c/m chunks, pass 1 runs G (2m - 3) workgroups and pass 2 G (m - 1),
-// G = sequences x value heads, each in ceil(count / CUs) rounds, plus the
-// scan's m - 2 steps at about a quarter chunk each.  The plain call segments
-// only where the model gains at least 15%.
+// segments of c/m chunks, pass 1 runs G (m - 1) workgroups (segment 0 and the
+// paired P/B runs, which take about 1.3 chunk-times per chunk) and pass 2
+// G (m - 1), G = sequences x value heads, each in ceil(count / CUs) rounds,
+// plus the scan's m - 2 steps at about a quarter chunk each.  The plain call
+// segments only where the model gains at least 15%.
 int32_t prefill_auto_segment_len(const gdn_dims& d, int32_t n_seqs, int32_t total_tokens) {
     if (n_seqs <= 0 || total_tokens <= 0) return 0;
     const int64_t groups = static_cast<int64_t>(n_seqs) * d.num_v_heads;
@@ -1161,9 +1282,9 @@ int32_t prefill_auto_segment_len(const gdn_dims& d, int32_t n_seqs, int32_t tota
         const int64_t per = (chunks + m - 1) / m;          // chunks per segment
         const int64_t mm = (chunks + per - 1) / per;        // segments actually used
         if (mm < 3) continue;
-        const int64_t r1 = (groups * (2 * mm - 3) + cus - 1) / cus;
+        const int64_t r1 = (groups * (mm - 1) + cus - 1) / cus;
         const int64_t r2 = (groups * (mm - 1) + cus - 1) / cus;
-        const double t = static_cast<double>(per) * (r1 + r2) + 0.25 * (mm - 2);
+        const double t = static_cast<double>(per) * (1.3 * r1 + r2) + 0.25 * (mm - 2);
         if (t < best * 0.999) { best = t; best_len = static_cast<int32_t>(per * 64); }
     }
     return (best <= 0.85 * chunks) ? best_len : 0;
@@ -1181,7 +1302,7 @@ hipError_t launch_prefill_segmented(const void* q, const void* k, const void* v,
         return hipErrorInvalidValue;
     // segments of the longest possible sequence (all tokens in one)
     const int32_t smax = total_tokens > 0 ? (total_tokens + seg_len - 1) / seg_len : 1;
-    const int32_t nz1 = smax >= 2 ? 2 * (smax - 1) : 1;
+    const int32_t nz1 = smax >= 2 ? smax - 1 : 1;   // segment 0 and the paired middle segments
     if (nz1 > 65535) return hipErrorInvalidValue;
     hipError_t e = prefill_pass(q, k, v, in_dt, ga, cu, n_seqs, slot, rec, out, out_dt, d, sqk,
                                 sv, scale, flags, SegArgs{ws, seg_len, 1}, nz1, err, st);
