@@ -319,14 +319,13 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
     float* S = rec + (static_cast<size_t>(s) * HV + hv) * static_cast<size_t>(D) * D;
 
     // The tokens [a0, a1) this workgroup walks, where its start state comes
-    // from (0: the slot, 1: zero, 3: `init`), whether it writes outputs, and
+    // from (`init`; nullptr: the zero state), whether it writes outputs, and
     // where its end state goes (nullptr: dropped).  A paired workgroup (pb)
     // also carries a second state from the identity with v = 0 (a middle
     // segment's P run beside its B run, sharing every intra-chunk step) and
     // writes it to fin2.  Whole-sequence launches (SEG false) compile none of
     // the segment logic.
     int32_t a0 = t0, a1 = t1;
-    int init_mode = 0;
     const float* init = S;
     float* fin = S;
     float* fin2 = nullptr;
@@ -352,7 +351,7 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
                 a1 = a0 + seg;
                 wo = false;
                 pb = true;
-                init_mode = 1;
+                init = nullptr;
                 fin = wsm(id0 + j, 2);           // B: the run from zero
                 fin2 = wsm(id0 + j, 1);          // P: the run from the identity, v = 0
             }
@@ -361,7 +360,6 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
             if (nseg <= 1 || j > nseg - 1) return;
             a0 = t0 + j * seg;
             a1 = min(a0 + seg, t1);
-            init_mode = 3;
             init = wsm(id0 + j, 0);
             fin = (j == nseg - 1) ? S : nullptr;
         }
@@ -378,7 +376,7 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
             st2[kb][vb] = f32x4{0, 0, 0, 0};
             if (vact) {
                 const int v = 16 * (wave * VB + vb) + l16;
-                if (!SEG || init_mode == 0 || init_mode == 3) {
+                if (!SEG || init) {
                     const float4 x = *reinterpret_cast<const float4*>(init + static_cast<size_t>(v) * D + 16 * kb + 4 * q4);
                     st[kb][vb] = f32x4{x.x, x.y, x.z, x.w};
                 }
@@ -410,6 +408,12 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
     const uint32_t off_v = static_cast<uint32_t>(hv * D) * sizeof(IT);
     const uint32_t row_kq = static_cast<uint32_t>(sqk) * sizeof(IT);
     const uint32_t row_v = static_cast<uint32_t>(sv) * sizeof(IT);
+    // gate sources, resolved once: g, beta fp32 or a, b (bf16 or fp32)
+    const bool ghalf = ga.a != nullptr && ga.ab_bf16;
+    const uint32_t ges = ghalf ? 2 : 4;
+    const uint32_t grow = static_cast<uint32_t>(HV) * ges;
+    const char* gsrc0 = static_cast<const char*>(ga.a ? ga.a : static_cast<const void*>(ga.g));
+    const char* gsrc1 = static_cast<const char*>(ga.a ? ga.b : static_cast<const void*>(ga.beta));
     auto fetch = [&](int32_t c, int Lc) {
         const rsrc_t rk_ = make_rsrc(kg + static_cast<size_t>(c) * sqk, Lc * row_kq);
         const rsrc_t rq_ = make_rsrc(qg + static_cast<size_t>(c) * sqk, Lc * row_kq);
@@ -433,15 +437,11 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
         }
         // the chunk's raw gate values (g and beta, or a and b for fused gating);
         // used by wave 0 at the loop top
-        const bool half = ga.a != nullptr && ga.ab_bf16;
-        const uint32_t es = half ? 2 : 4;
-        const char* s0 = static_cast<const char*>(ga.a ? ga.a : static_cast<const void*>(ga.g));
-        const char* s1 = static_cast<const char*>(ga.a ? ga.b : static_cast<const void*>(ga.beta));
-        const rsrc_t r0 = make_rsrc(s0 + static_cast<size_t>(c) * HV * es, Lc * HV * es);
-        const rsrc_t r1 = make_rsrc(s1 + static_cast<size_t>(c) * HV * es, Lc * HV * es);
-        const uint32_t ob = static_cast<uint32_t>(min(tid, CH) * HV + hv) * es;
+        const rsrc_t r0 = make_rsrc(gsrc0 + static_cast<size_t>(c) * grow, Lc * grow);
+        const rsrc_t r1 = make_rsrc(gsrc1 + static_cast<size_t>(c) * grow, Lc * grow);
+        const uint32_t ob = static_cast<uint32_t>(min(tid, CH) * HV + hv) * ges;
         // raw bits only: converting here would wait for every load issued above
-        if (half) {
+        if (ghalf) {
             pg = buf_ld2(r0, ob);
             pbeta = buf_ld2(r1, ob);
         } else {
@@ -502,7 +502,7 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
         }
         if (wave == 0) {                         // gate, then the cumulative log-decay:
             float gt, bv;                        // fixed-order DPP wave scan
-            const bool half = ga.a != nullptr && ga.ab_bf16;
+            const bool half = ghalf;
             gate_finish(ga, gh, half ? bf16_to_f32(static_cast<bf16_t>(pg)) : __uint_as_float(pg),
                         half ? bf16_to_f32(static_cast<bf16_t>(pbeta)) : __uint_as_float(pbeta), gt, bv);
             if (lane >= L) { gt = 0.0f; bv = 0.0f; }   // rows past the chunk (raw values read as 0)
