@@ -229,13 +229,21 @@ __global__ __launch_bounds__(256) void decode_rec_kernel(
 // order, so this kernel and the conv kernel + decode_rec_kernel pair give
 // bitwise-identical results.  The first pass's state loads are issued right
 // after the conv's own loads, so that they are in flight during the conv.
+//
+// DB (double-buffered passes): the second pass's loads also go out before the
+// conv, and each pass's loads go out as soon as the pass two back has stored,
+// so one pass computes while the next one streams in.  The extra 16 state
+// registers fit under the 128-register cap of 1024-thread groups only with q
+// re-read from LDS in each row (and scaled there), which costs about 1.5% when
+// many groups queue per CU; with one or two groups per CU the step is a short
+// latency chain per CU, and there double-buffering saves 15% (batch 16).
 // ---------------------------------------------------------------------------
 // Threads per fused-step workgroup: a pass streams NT / 8 state rows.
 #ifndef GDN_STEP_NT
 #define GDN_STEP_NT 1024
 #endif
 
-template <int DK, typename XT, typename CT, typename WT, typename OT>
+template <int DK, bool DB, typename XT, typename CT, typename WT, typename OT>
 __global__ __launch_bounds__(GDN_STEP_NT) void decode_step_kernel(
     const XT* __restrict__ x, const GateArgs ga,
     const int32_t* __restrict__ slot, CT* __restrict__ cs, const WT* __restrict__ w,
@@ -274,7 +282,7 @@ __global__ __launch_bounds__(GDN_STEP_NT) void decode_step_kernel(
                     St[i] = state_ld(Sg + static_cast<size_t>(r0 + rl) * DK + 32 * i + 4 * sub);
             }
         };
-        float4 S[NV];
+        float4 S[NV], S2[NV];
 
         // conv of the group's channels into LDS (and the in-place roll).  With
         // one 4-channel unit per thread, the unit's loads go out first and the
@@ -305,6 +313,7 @@ __global__ __launch_bounds__(GDN_STEP_NT) void decode_step_kernel(
             conv4_load<XT, CT, WT>(xb + c, csb + static_cast<size_t>(c) * (CONV_W - 1), w + c * CONV_W,
                                    bias ? bias + c : nullptr, in);
             fetch(S, 0);
+            if constexpr (DB) fetch(S2, RP);
             if (mine) {
                 float y[4];
                 conv4_finish<XT, CT, WT>(in, csb + static_cast<size_t>(c) * (CONV_W - 1), silu_on, y);
@@ -320,6 +329,7 @@ __global__ __launch_bounds__(GDN_STEP_NT) void decode_step_kernel(
                 *reinterpret_cast<float4*>(&ys[lc]) = make_float4(y[0], y[1], y[2], y[3]);
             }
             fetch(S, 0);
+            if constexpr (DB) fetch(S2, RP);
         }
         if (gate_lane) {
             float gv, bv;
@@ -364,7 +374,7 @@ __global__ __launch_bounds__(GDN_STEP_NT) void decode_step_kernel(
         }
 
         // the passes: pass 0's rows are already in S
-        auto pass = [&](int r0) {
+        auto pass = [&](float4 (&S)[NV], int r0) {
             const int r = r0 + rl;
             if (r >= R) return;               // the 8 lanes of a row share the test
             const int gi = r / dv;            // this row's value head within the group
@@ -381,22 +391,38 @@ __global__ __launch_bounds__(GDN_STEP_NT) void decode_step_kernel(
             u = sum8(u);
             const float delta = bt * (vr - u);
             float o = 0.f;
+            int qo = 4 * sub;
+            if constexpr (DB) asm volatile("" : "+v"(qo));   // no reuse across rows
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
                 S[i].x = fmaf(delta, kf[i].x, S[i].x); S[i].y = fmaf(delta, kf[i].y, S[i].y);
                 S[i].z = fmaf(delta, kf[i].z, S[i].z); S[i].w = fmaf(delta, kf[i].w, S[i].w);
-                o = fmaf(S[i].x, qf[i].x, o); o = fmaf(S[i].y, qf[i].y, o);
-                o = fmaf(S[i].z, qf[i].z, o); o = fmaf(S[i].w, qf[i].w, o);
+                float4 qv = qf[i];
+                if constexpr (DB) {
+                    qv = *reinterpret_cast<const float4*>(&ys[32 * i + qo]);
+                    qv.x *= qmul; qv.y *= qmul; qv.z *= qmul; qv.w *= qmul;
+                }
+                o = fmaf(S[i].x, qv.x, o); o = fmaf(S[i].y, qv.y, o);
+                o = fmaf(S[i].z, qv.z, o); o = fmaf(S[i].w, qv.w, o);
             }
             o = sum8(o);
 #pragma unroll
             for (int i = 0; i < NV; ++i) state_st(Sg + static_cast<size_t>(r) * DK + 32 * i + 4 * sub, S[i]);
             if (sub == 0) elem<OT>::st(ob + r, o);
         };
-        pass(0);
-        for (int r0 = RP; r0 < R; r0 += RP) {
-            fetch(S, r0);
-            pass(r0);
+        if constexpr (DB) {
+            for (int r0 = 0; r0 < R; r0 += 2 * RP) {
+                pass(S, r0);
+                fetch(S, r0 + 2 * RP);
+                pass(S2, r0 + RP);
+                fetch(S2, r0 + 3 * RP);
+            }
+        } else {
+            pass(S, 0);
+            for (int r0 = RP; r0 < R; r0 += RP) {
+                fetch(S, r0);
+                pass(S, r0);
+            }
         }
         __syncthreads();                      // ys is rewritten by the next group
     }
@@ -474,9 +500,17 @@ hipError_t pick_dk(const RecArgs& a) {
 }
 }  // namespace
 
-// Workgroups per CU in the fused step's persistent grid.
+// Workgroups per CU in the fused step's grid (a group-strided loop beyond it).
+// Measured at batch 256: one workgroup per group (4096) 206 us; one or two
+// resident per CU looping over groups 211 us.
 #ifndef GDN_STEP_WG_PER_CU
 #define GDN_STEP_WG_PER_CU GDN_DECODE_WG_PER_CU
+#endif
+// Double-buffered passes up to this many groups per CU (see decode_step_kernel).
+// Measured: batch 32 (2 groups per CU) 30.1 us vs 30.5 single-buffered; batch
+// 64 56.7 vs 55.7; batch 256 206.7 vs 203.6.
+#ifndef GDN_STEP_DB_MAX_GROUPS_PER_CU
+#define GDN_STEP_DB_MAX_GROUPS_PER_CU 2
 #endif
 
 namespace {
@@ -493,7 +527,13 @@ hipError_t run_step(const StepArgs& a) {
     const int64_t groups = static_cast<int64_t>(a.batch) * a.d->num_k_heads;
     const int64_t resident = static_cast<int64_t>(cu_count()) * GDN_STEP_WG_PER_CU;
     const int grid = static_cast<int>(groups < resident ? groups : resident);
-    return launch(decode_step_kernel<DK, XT, CT, WT, OT>, dim3(grid), dim3(GDN_STEP_NT), lds, a.st,
+    // dk > 128 keeps single buffering: its 32 state registers per pass would
+    // not fit twice
+    const bool db = DK <= 128 &&
+                    groups <= static_cast<int64_t>(cu_count()) * GDN_STEP_DB_MAX_GROUPS_PER_CU;
+    auto kern = db ? decode_step_kernel<DK, (DK <= 128), XT, CT, WT, OT>
+                   : decode_step_kernel<DK, false, XT, CT, WT, OT>;
+    return launch(kern, dim3(grid), dim3(GDN_STEP_NT), lds, a.st,
                   static_cast<const XT*>(a.x), a.gate, a.slot, static_cast<CT*>(a.cs),
                   static_cast<const WT*>(a.w), static_cast<const WT*>(a.bias), a.rec,
                   static_cast<OT*>(a.out), a.d->num_k_heads, a.d->num_v_heads,
@@ -518,14 +558,15 @@ hipError_t step_x(gdn_dtype xt, gdn_dtype c, gdn_dtype wt, gdn_dtype o, const St
 }
 }  // namespace
 
-// The fused step is chosen from this many (row, key head) groups per CU on.
-// Measured (graph replay, H = 16, HV = 32, d = 128, 256 CUs, 1024-thread
-// groups): batch 256 fused 203.3 us vs 206.1 us for the conv + recurrence
-// pair; batch 16 17.5 vs 17.9; batch 32 and 64 within 2%; below one group per
-// CU the pair's 32-row items spread the few rows over more CUs (batch 1: 7.0
-// vs 9.3 us, batch 4: 9.3 vs 10.4).
-#ifndef GDN_DECODE_FUSED_MIN_GROUPS_PER_CU
-#define GDN_DECODE_FUSED_MIN_GROUPS_PER_CU 1
+// The fused step is chosen while each (row, key head) group has at most this
+// many CUs to itself.  Measured (graph replay, H = 16, HV = 32, d = 128, 256
+// CUs, 1024-thread groups), fused vs the conv + recurrence pair: batch 256
+// 203.6 vs 206.5 us; batch 32 30.1 vs 30.0; batch 16 15.1 vs 17.9; batch 12
+// 12.8 vs 15.4; batch 8 12.1 vs 12.0; batch 4 8.95 vs 9.1; below that the
+// pair's 32-row recurrence items spread the few rows over more CUs (batch 2:
+// 8.7 vs 7.4, batch 1: 8.5 vs 7.0).
+#ifndef GDN_DECODE_FUSED_MAX_CUS_PER_GROUP
+#define GDN_DECODE_FUSED_MAX_CUS_PER_GROUP 4
 #endif
 
 bool decode_step_fused_fits(const gdn_dims& d) {
@@ -538,8 +579,8 @@ bool decode_step_use_fused(const gdn_dims& d, int32_t batch) {
     // dk > 128 stays on the pair: the 1024-thread fused kernel (128 VGPRs)
     // spills its per-row registers there
     return decode_step_fused_fits(d) && d.head_k_dim <= 128 &&
-           static_cast<int64_t>(batch) * d.num_k_heads >=
-               static_cast<int64_t>(GDN_DECODE_FUSED_MIN_GROUPS_PER_CU) * cu_count();
+           static_cast<int64_t>(batch) * d.num_k_heads * GDN_DECODE_FUSED_MAX_CUS_PER_GROUP >=
+               static_cast<int64_t>(cu_count());
 }
 
 hipError_t launch_decode_step_fused(const void* x, gdn_dtype x_dt, const GateArgs& gate,

@@ -65,9 +65,9 @@ hipError_t launch_decode_rec(const void* y, gdn_dtype y_dt, const GateArgs& gate
                              int32_t flags, const int32_t* err_flag, hipStream_t stream);
 
 // Fused decode step (conv + SiLU + norms + recurrence in one kernel, one
-// workgroup per (row, key head) group, activations in LDS).  Chosen when the
-// batch has at least one group per CU and a group's activations fit in LDS;
-// its results equal those of the conv + recurrence pair bitwise.
+// workgroup per (row, key head) group, activations in LDS).  Chosen when
+// dk <= 128, there is at least one group per 4 CUs and a group's activations
+// fit in LDS; its results equal those of the conv + recurrence pair bitwise.
 bool decode_step_fused_fits(const gdn_dims& d);
 bool decode_step_use_fused(const gdn_dims& d, int32_t batch);
 hipError_t launch_decode_step_fused(const void* x, gdn_dtype x_dt, const GateArgs& gate,

@@ -192,11 +192,11 @@ size_t gdn_decode_workspace_size(const gdn_dims* dims, int32_t batch);
  * kernel (one workgroup per (row, key head) group: conv of q_h, k_h and the
  * value heads sharing h into LDS, then their recurrence) and a conv kernel
  * writing the fp32 activations to the workspace followed by the recurrence
- * kernel.  By default the fused kernel runs when batch * num_k_heads is at
- * least the number of compute units and (2 dk + (HV / H) (dv + 2)) * 4 bytes
- * fit in 64 KiB of LDS; the STEP flags force a path (GDN_ERR_DIMS if the fused
- * kernel is forced where the group does not fit, GDN_ERR_FLAGS if both are
- * set).
+ * kernel.  By default the fused kernel runs when head_k_dim <= 128, when
+ * 4 * batch * num_k_heads is at least the number of compute units and when
+ * (2 dk + (HV / H) (dv + 2)) * 4 bytes fit in 64 KiB of LDS; the STEP flags
+ * force a path (GDN_ERR_DIMS if the fused kernel is forced where the group
+ * does not fit, GDN_ERR_FLAGS if both are set).
  */
 gdn_status gdn_decode_step(const void* mixed_qkv, gdn_dtype x_dt,
                            const float* g, const float* beta,

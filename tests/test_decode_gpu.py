@@ -151,10 +151,21 @@ _PATH_CASES = [
 _DT = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 
+def _batch_for(regime, H):
+    """Batch at which the fused step runs double-buffered ("few": at most two
+    (row, key head) groups per CU) or single-buffered ("many": more)."""
+    if regime == "few":
+        return 11
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return max(11, (2 * cus) // H + 5)
+
+
+@pytest.mark.parametrize("regime", ["few", "many"])
 @pytest.mark.parametrize("case", _PATH_CASES, ids=lambda c: "-".join(map(str, c[:8])))
-def test_fused_equals_split_bitwise(case):
+def test_fused_equals_split_bitwise(case, regime):
     H, HV, dk, dv, xd, cd, wd, od, bias, flags = case
-    d = gi.decode_inputs(11, 24, H=H, HV=HV, dk=dk, dv=dv, seed=40 + dk + dv, conv_bias=bias)
+    B = _batch_for(regime, H)
+    d = gi.decode_inputs(B, B + 13, H=H, HV=HV, dk=dk, dv=dv, seed=40 + dk + dv, conv_bias=bias)
     d["mixed_qkv"] = d["mixed_qkv"].to(_DT[xd])
     d["conv_state"] = d["conv_state"].to(_DT[cd])
     d["conv_weight"] = d["conv_weight"].to(_DT[wd])
