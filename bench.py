@@ -17,8 +17,9 @@ second at batch 256 (GB/s); the batch-16 decode rate and the prefill tokens/s
 ride along in "extra".  "roofline" reports the headline step's kernel (at
 batch 256 the step is one fused conv + recurrence kernel) timed alone with HIP
 events over eager launches; the conv + recurrence pair that the step uses below
-one (row, key head) group per CU is timed alongside.  "cpu_baseline" is the
-fp64 oracle on a bounded sample of the same workload.
+one (row, key head) group per 4 CUs is timed alongside.  "cpu_baseline" is the
+fp64 oracle on a bounded sample of the same workload, run over independent
+rows on the host's threads (at most 16); the one-thread figure is in "extra".
 """
 import argparse
 import json
@@ -301,14 +302,54 @@ def time_loop(torch, fn, steps, warmup):
     return [s.elapsed_time(e) for s, e in zip(starts, ends)]
 
 
-def cpu_baseline(budget_s):
-    """The fp64 oracle, as it stands, on decode rows of the batch-256 workload
-    (same shapes and distributions), repeated until the budget is spent."""
-    import numpy as np
+def host_threads():
+    """Host threads for the oracle's all-cores leg: the CPUs this process may
+    run on, at most 16 (one GPU's share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def run_oracle_threads(n_threads, budget_s, make_unit):
+    """Run independent oracle units on n_threads threads for budget_s seconds.
+
+    make_unit(i) builds thread i's own inputs and caches (untimed) and returns
+    (work, units): work() makes one oracle call covering `units` rows or
+    tokens.  The oracle is C called through ctypes, which releases the GIL, so
+    the threads run in parallel; nothing is shared between them.  Returns
+    (units done, wall seconds)."""
+    import threading
+    works = [make_unit(i) for i in range(n_threads)]
+    done = [0] * n_threads
+    start = threading.Barrier(n_threads + 1)
+    deadline = [0.0]
+
+    def body(i):
+        work, units = works[i]
+        start.wait()
+        while time.perf_counter() < deadline[0]:
+            work()
+            done[i] += units
+
+    threads = [threading.Thread(target=body, args=(i,)) for i in range(n_threads)]
+    for t in threads:
+        t.start()
+    t0 = time.perf_counter()
+    deadline[0] = t0 + budget_s
+    start.wait()
+    for t in threads:
+        t.join()
+    return sum(done), time.perf_counter() - t0
+
+
+def decode_oracle_unit(B, seed):
+    """One thread's decode sample: B rows of the batch-256 workload's shapes and
+    distributions, with the thread's own fp64 caches."""
     import gdn_inputs as gi
     import oracle
-    B = 64
-    d = gi.decode_inputs(B, B + 1, seed=2)
+    d = gi.decode_inputs(B, B + 1, seed=seed)
     x = d["mixed_qkv"].double().numpy()
     g = d["g"].double().numpy()
     b = d["beta"].double().numpy()
@@ -316,36 +357,54 @@ def cpu_baseline(budget_s):
     cs = d["conv_state"].double().numpy().copy()
     rs = d["rec_state"].double().numpy().copy()
     w = d["conv_weight"].double().numpy()
-    rows = 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < budget_s:
+
+    def work():
         oracle.decode_step(x, g, b, slots, cs, w, rs, H, HV, DK, DV, DK ** -0.5)
-        rows += B
-    dt = time.perf_counter() - t0
-    gbs = rows * decode_bytes_per_seq() / dt / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{rows} decode rows ({rows // B} steps of batch {B}, same shapes "
-                      f"and distributions as the batch-256 workload) in {dt:.1f} s, "
-                      "single-threaded fp64 C"}
+    return work, B
 
 
-def cpu_baseline_prefill(budget_s):
-    """The fp64 oracle prefill on the first 512 tokens of the prefill workload's
-    first sequence (all 32 value heads), repeated until the budget is spent."""
+def prefill_oracle_unit(seed):
+    """One thread's prefill sample: a 512-token sequence of the prefill
+    workload's shapes and distributions (all 32 value heads), own fp64 state."""
     import gdn_inputs as gi
     import oracle
-    p = gi.prefill_inputs([512], 2, seed=3)
+    p = gi.prefill_inputs([512], 2, seed=seed)
     args = [p[k].double().numpy() for k in ("q", "k", "v", "g", "beta")]
     rec = p["rec_state"].double().numpy().copy()
-    toks = 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < budget_s:
-        oracle.prefill(*args, p["cu_seqlens"].numpy(), p["slot_idx"].numpy(), rec, DK ** -0.5)
-        toks += 512
-    dt = time.perf_counter() - t0
-    return {"value": round(toks / dt, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{toks} prefill tokens (512-token sequence, H=16 HV=32 d=128) in "
-                      f"{dt:.1f} s, single-threaded fp64 C, token by token"}
+    cu, sl = p["cu_seqlens"].numpy(), p["slot_idx"].numpy()
+
+    def work():
+        oracle.prefill(*args, cu, sl, rec, DK ** -0.5)
+    return work, 512
+
+
+def cpu_baseline(budget_s, n_threads):
+    """The fp64 oracle, as it stands, on decode rows of the batch-256 workload
+    (same shapes and distributions): on n_threads threads over independent row
+    samples (the reported figure) and on one thread.  Each leg runs for about
+    budget_s seconds of wall time."""
+    rows, dt = run_oracle_threads(n_threads, budget_s,
+                                  lambda i: decode_oracle_unit(16, 2 + 100 * i))
+    gbs = rows * decode_bytes_per_seq() / dt / 1e9
+    rows1, dt1 = run_oracle_threads(1, budget_s, lambda i: decode_oracle_unit(64, 2))
+    gbs1 = rows1 * decode_bytes_per_seq() / dt1 / 1e9
+    main = {"value": round(gbs, 4), "unit": "GB/s", "cores": n_threads, "kind": "oracle",
+            "sample": f"{rows} decode rows (batch-16 steps on {n_threads} threads, each with "
+                      f"its own rows and caches; shapes and distributions of the batch-256 "
+                      f"workload) in {dt:.1f} s, fp64 C"}
+    one = {"value": round(gbs1, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": f"{rows1} decode rows (steps of batch 64) in {dt1:.1f} s, "
+                     "single-threaded fp64 C"}
+    return main, one
+
+
+def cpu_baseline_prefill(budget_s, n_threads):
+    """The fp64 oracle prefill on 512-token sequences of the prefill workload's
+    shapes (all 32 value heads), one independent sequence per thread."""
+    toks, dt = run_oracle_threads(n_threads, budget_s, lambda i: prefill_oracle_unit(3 + 100 * i))
+    return {"value": round(toks / dt, 2), "unit": "tokens/s", "cores": n_threads, "kind": "oracle",
+            "sample": f"{toks} prefill tokens (512-token sequences, H=16 HV=32 d=128, one per "
+                      f"thread on {n_threads} threads) in {dt:.1f} s, fp64 C, token by token"}
 
 
 def gi_stress(T):
@@ -509,8 +568,9 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(args.cpu_seconds)
-        extra["cpu_baseline_prefill"] = cpu_baseline_prefill(max(4.0, args.cpu_seconds / 2))
+        nth = host_threads()
+        cpu, extra["cpu_baseline_1thread"] = cpu_baseline(args.cpu_seconds / 2, nth)
+        extra["cpu_baseline_prefill"] = cpu_baseline_prefill(max(4.0, args.cpu_seconds / 3), nth)
 
     traffic = measured_traffic()
 
