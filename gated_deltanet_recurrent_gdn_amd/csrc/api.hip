@@ -89,8 +89,9 @@ gdn_status gdn_conv_update(const void* x, gdn_dtype x_dt, const int32_t* cu_seql
                                        err_flag, s));
     const int32_t* ef = (flags & GDN_FLAG_VALIDATE) ? err_flag : nullptr;
     if (cu_seqlens)
-        GDN_TRY_LAUNCH(launch_conv_varlen(x, x_dt, cu_seqlens, n_seqs, slot_idx, conv_state, cs_dt,
-                                          weight, bias, w_dt, out, out_dt, dim, flags, ef, s));
+        GDN_TRY_LAUNCH(launch_conv_varlen(x, x_dt, cu_seqlens, n_seqs, total_tokens, slot_idx,
+                                          conv_state, cs_dt, weight, bias, w_dt, out, out_dt, dim,
+                                          flags, ef, s));
     else
         GDN_TRY_LAUNCH(launch_conv_decode(x, x_dt, slot_idx, n_seqs, conv_state, cs_dt, weight,
                                           bias, w_dt, out, out_dt, dim, flags, ef, s));
@@ -432,8 +433,8 @@ gdn_status gdn_mixed_step(const void* x, gdn_dtype x_dt, const float* g, const f
     uint16_t* yp = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) +
                                            round256(static_cast<size_t>(n_dec) * D * sizeof(float)));
     const int32_t* sp = slot_idx + n_dec;
-    GDN_TRY_LAUNCH(launch_conv_varlen(xp, x_dt, cu_seqlens, n_pre, sp, conv_state, cs_dt,
-                                      conv_weight, conv_bias, w_dt, yp, GDN_BF16, D,
+    GDN_TRY_LAUNCH(launch_conv_varlen(xp, x_dt, cu_seqlens, n_pre, total_pre, sp, conv_state,
+                                      cs_dt, conv_weight, conv_bias, w_dt, yp, GDN_BF16, D,
                                       flags & GDN_FLAG_SILU, ef, s));
     GateArgs gp = ga;
     gp.g = ga.g + static_cast<size_t>(n_dec) * HV;

@@ -47,10 +47,154 @@ __global__ __launch_bounds__(256) void conv_decode_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Varlen: grid = (ceil(D / 64), n_seqs), 256 threads = 64 channels x 4 token
-// lanes; token lane tg handles tokens tg, tg+4, ...  The old state is read
-// into registers by every thread before a barrier; after it, token lane 0
-// alone writes the rolled state.
+// Varlen, token-parallel (the path for dim % 4 == 0 and 16-byte aligned
+// tensors).  grid = (ceil(T / 64), ceil(D / 256)); a thread owns 4 channels
+// and 16 consecutive tokens of the concatenated token rows (a wave: 256
+// channels of the same 16 tokens, so each token row is read as one contiguous
+// 512- or 1024-byte span).  All 19 inputs of the thread's window are loaded
+// before any arithmetic; the sequence of each token comes from a binary search
+// of cu_seqlens (and a walk across the sequence starts inside the tile), and a
+// token among the first W-1 of its sequence takes the missing taps from the
+// cached state of its slot.  The cache is not written here: conv_roll_kernel,
+// launched after this kernel on the same stream, rolls it, so no thread can
+// read a rolled tap.  Arithmetic per channel: bias, then taps 0..W-1 with
+// fmaf, then SiLU -- the order of every other conv path, bitwise.
+// ---------------------------------------------------------------------------
+constexpr int CONV_TT = 16;                 // tokens per thread
+
+template <typename XT, typename CT, typename WT, typename OT>
+__global__ __launch_bounds__(256) void conv_varlen_tok_kernel(
+    const XT* __restrict__ x, const int32_t* __restrict__ cu, int32_t n_seqs, int32_t T,
+    const int32_t* __restrict__ slot, const CT* __restrict__ cs, const WT* __restrict__ w,
+    const WT* __restrict__ bias, OT* __restrict__ out, int32_t D, int32_t flags,
+    const int32_t* __restrict__ err_flag) {
+    static_assert(CONV_W == 4, "four taps");
+    typedef typename V4<XT>::raw XR;
+    typedef typename V4<WT>::raw WR;
+    if (call_rejected(err_flag)) return;
+    const int c = 4 * (static_cast<int>(blockIdx.y) * 64 + static_cast<int>(threadIdx.x & 63));
+    const int t0 = static_cast<int>(blockIdx.x) * (4 * CONV_TT) + static_cast<int>(threadIdx.x >> 6) * CONV_TT;
+    if (c >= D || t0 >= T || n_seqs <= 0) return;
+
+    // the window's inputs first (rows clamped into [0, T); unused ones are ignored)
+    XR xv[CONV_TT + CONV_W - 1];
+#pragma unroll
+    for (int i = 0; i < CONV_TT + CONV_W - 1; ++i) {
+        const int p = min(max(t0 - (CONV_W - 1) + i, 0), T - 1);
+        xv[i] = ld_nt<XR>(reinterpret_cast<const XR*>(x + static_cast<size_t>(p) * D + c));
+    }
+    WR wr[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wr[j] = reinterpret_cast<const WR*>(w + static_cast<size_t>(c) * CONV_W)[j];
+    const WR br = bias ? *reinterpret_cast<const WR*>(bias + c) : V4<WT>::make(0.f, 0.f, 0.f, 0.f);
+
+    // the sequence n with cu[n] <= t0 < cu[n + 1]
+    int lo = 0, hi = n_seqs;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (cu[mid] <= t0) lo = mid; else hi = mid;
+    }
+    int n = lo;
+    int st = cu[n], en = cu[n + 1];
+    int32_t s = slot[n];
+    const bool silu_on = (flags & GDN_FLAG_SILU) != 0;
+
+#pragma unroll
+    for (int i = 0; i < CONV_TT; ++i) {
+        const int t = t0 + i;
+        if (t >= T) break;
+        while (t >= en && n + 1 < n_seqs) {       // sequence starts inside the tile
+            ++n;
+            st = en;
+            en = cu[n + 1];
+            s = slot[n];
+        }
+        if (t < st || t >= en) continue;          // outside every sequence: nothing to write
+        typename V4<OT>::raw* o = reinterpret_cast<typename V4<OT>::raw*>(out + static_cast<size_t>(t) * D + c);
+        if (s <= 0) {                             // inactive sequence: zeros, cache untouched
+            *o = V4<OT>::make(0.f, 0.f, 0.f, 0.f);
+            continue;
+        }
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = V4<WT>::get(br, e);
+#pragma unroll
+        for (int j = 0; j < CONV_W; ++j) {
+            const int p = t - (CONV_W - 1) + j;
+            if (p >= st) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    y[e] = fmaf(vget<WT, 4>(wr, 4 * e + j), V4<XT>::get(xv[i + j], e), y[e]);
+            } else {                              // tap m of the cached state
+                const CT* sp = cs + (static_cast<size_t>(s) * D + c) * (CONV_W - 1) + (p - st + CONV_W - 1);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    y[e] = fmaf(vget<WT, 4>(wr, 4 * e + j), elem<CT>::ld(sp + (CONV_W - 1) * e), y[e]);
+            }
+        }
+        if (silu_on) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = silu(y[e]);
+        }
+        *o = V4<OT>::make(y[0], y[1], y[2], y[3]);
+    }
+}
+
+// Roll of the conv cache after conv_varlen_tok_kernel: the new state of an
+// active sequence of length L > 0 is the last W-1 entries of [state | tokens],
+// copied as raw bits (a token is rounded to the cache dtype when the dtypes
+// differ).  grid = (ceil(D / 1024), n_seqs); a thread owns 4 channels.
+template <typename XT, typename CT>
+__global__ __launch_bounds__(256) void conv_roll_kernel(
+    const XT* __restrict__ x, const int32_t* __restrict__ cu, const int32_t* __restrict__ slot,
+    CT* __restrict__ cs, int32_t D, const int32_t* __restrict__ err_flag) {
+    typedef typename V4<XT>::raw XR;
+    typedef typename V4<CT>::raw CR;
+    if (call_rejected(err_flag)) return;
+    const int c = 4 * (static_cast<int>(blockIdx.x) * 256 + static_cast<int>(threadIdx.x));
+    const int n = blockIdx.y;
+    if (c >= D) return;
+    const int st = cu[n];
+    const int L = cu[n + 1] - st;
+    const int32_t s = slot[n];
+    if (s <= 0 || L <= 0) return;
+    CR* sp = reinterpret_cast<CR*>(cs + (static_cast<size_t>(s) * D + c) * (CONV_W - 1));
+    CR raw[CONV_W - 1];
+    if (L < CONV_W - 1) {
+#pragma unroll
+        for (int j = 0; j < CONV_W - 1; ++j) raw[j] = sp[j];
+    }
+    uint32_t nb[4 * (CONV_W - 1)];
+#pragma unroll
+    for (int m = 0; m < CONV_W - 1; ++m) {
+        const int q = L - (CONV_W - 1) + m;       // position of new tap m within the tokens
+        if (q >= 0) {
+            const XR xin = *reinterpret_cast<const XR*>(x + static_cast<size_t>(st + q) * D + c);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                nb[(CONV_W - 1) * e + m] = std::is_same<XT, CT>::value ? V4<XT>::bits(xin, e)
+                                                                       : V4<CT>::to_bits(V4<XT>::get(xin, e));
+        } else {                                  // old tap q + W-1 (constant indices)
+#pragma unroll
+            for (int k = 0; k < CONV_W - 1; ++k) {
+                if (q + (CONV_W - 1) == k) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        nb[(CONV_W - 1) * e + m] = vbits<CT, CONV_W - 1>(raw, (CONV_W - 1) * e + k);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < CONV_W - 1; ++j)
+        st_nt<CR>(sp + j, V4<CT>::make_bits(nb[4 * j], nb[4 * j + 1], nb[4 * j + 2], nb[4 * j + 3]));
+}
+
+// ---------------------------------------------------------------------------
+// Varlen, general (any dim, any alignment): grid = (ceil(D / 64), n_seqs), 256
+// threads = 64 channels x 4 token lanes; token lane tg handles tokens tg,
+// tg+4, ...  The old state is read into registers by every thread before a
+// barrier; after it, token lane 0 alone writes the rolled state.
 // ---------------------------------------------------------------------------
 template <typename XT, typename CT, typename WT, typename OT>
 __global__ __launch_bounds__(256) void conv_varlen_kernel(
@@ -139,11 +283,29 @@ struct DecodeK {
                       static_cast<OT*>(out), D, flags, err);
     }
 };
+bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
 template <typename XT, typename CT, typename WT, typename OT>
 struct VarlenK {
-    static hipError_t run(const void* x, const int32_t* cu, int32_t n_seqs, const int32_t* slot,
-                          void* cs, const void* w, const void* bias, void* out, int32_t D,
-                          int32_t flags, const int32_t* err, hipStream_t st) {
+    static hipError_t run(const void* x, const int32_t* cu, int32_t n_seqs, int32_t T,
+                          const int32_t* slot, void* cs, const void* w, const void* bias,
+                          void* out, int32_t D, int32_t flags, const int32_t* err, hipStream_t st) {
+        const bool vec = D % 4 == 0 && a16(x) && a16(out) && a16(cs) && a16(w) && (!bias || a16(bias)) &&
+                         (static_cast<size_t>(D) * sizeof(XT)) % 8 == 0;
+        if (vec) {
+            if (T > 0) {
+                dim3 grid((T + 4 * CONV_TT - 1) / (4 * CONV_TT), (D / 4 + 63) / 64);
+                const hipError_t e = launch(conv_varlen_tok_kernel<XT, CT, WT, OT>, grid, dim3(256), 0, st,
+                                            static_cast<const XT*>(x), cu, n_seqs, T, slot,
+                                            static_cast<const CT*>(cs), static_cast<const WT*>(w),
+                                            static_cast<const WT*>(bias), static_cast<OT*>(out), D,
+                                            flags, err);
+                if (e != hipSuccess) return e;
+            }
+            dim3 rgrid((D / 4 + 255) / 256, n_seqs);
+            return launch(conv_roll_kernel<XT, CT>, rgrid, dim3(256), 0, st,
+                          static_cast<const XT*>(x), cu, slot, static_cast<CT*>(cs), D, err);
+        }
         dim3 grid((D + 63) / 64, n_seqs);
         return launch(conv_varlen_kernel<XT, CT, WT, OT>, grid, dim3(256), 0, st,
                       static_cast<const XT*>(x), cu, slot, static_cast<CT*>(cs),
@@ -187,13 +349,14 @@ hipError_t launch_conv_decode(const void* x, gdn_dtype x_dt, const int32_t* slot
 }
 
 hipError_t launch_conv_varlen(const void* x, gdn_dtype x_dt, const int32_t* cu_seqlens,
-                              int32_t n_seqs, const int32_t* slot_idx, void* conv_state,
-                              gdn_dtype cs_dt, const void* weight, const void* bias,
-                              gdn_dtype w_dt, void* out, gdn_dtype out_dt, int32_t dim,
-                              int32_t flags, const int32_t* err_flag, hipStream_t stream) {
+                              int32_t n_seqs, int32_t total_tokens, const int32_t* slot_idx,
+                              void* conv_state, gdn_dtype cs_dt, const void* weight,
+                              const void* bias, gdn_dtype w_dt, void* out, gdn_dtype out_dt,
+                              int32_t dim, int32_t flags, const int32_t* err_flag,
+                              hipStream_t stream) {
     if (n_seqs == 0) return hipSuccess;
-    return pick_all<VarlenK>(x_dt, cs_dt, w_dt, out_dt, x, cu_seqlens, n_seqs, slot_idx,
-                             conv_state, weight, bias, out, dim, flags, err_flag, stream);
+    return pick_all<VarlenK>(x_dt, cs_dt, w_dt, out_dt, x, cu_seqlens, n_seqs, total_tokens,
+                             slot_idx, conv_state, weight, bias, out, dim, flags, err_flag, stream);
 }
 
 }  // namespace gdn

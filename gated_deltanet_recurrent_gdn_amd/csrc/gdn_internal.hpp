@@ -53,10 +53,11 @@ hipError_t launch_conv_decode(const void* x, gdn_dtype x_dt, const int32_t* slot
 
 // Conv update over token runs described by cu_seqlens.
 hipError_t launch_conv_varlen(const void* x, gdn_dtype x_dt, const int32_t* cu_seqlens,
-                              int32_t n_seqs, const int32_t* slot_idx, void* conv_state,
-                              gdn_dtype cs_dt, const void* weight, const void* bias,
-                              gdn_dtype w_dt, void* out, gdn_dtype out_dt, int32_t dim,
-                              int32_t flags, const int32_t* err_flag, hipStream_t stream);
+                              int32_t n_seqs, int32_t total_tokens, const int32_t* slot_idx,
+                              void* conv_state, gdn_dtype cs_dt, const void* weight,
+                              const void* bias, gdn_dtype w_dt, void* out, gdn_dtype out_dt,
+                              int32_t dim, int32_t flags, const int32_t* err_flag,
+                              hipStream_t stream);
 
 // Gated delta-rule decode update from the post-conv activations y [B, D].
 hipError_t launch_decode_rec(const void* y, gdn_dtype y_dt, const GateArgs& gate,

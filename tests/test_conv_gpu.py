@@ -63,10 +63,11 @@ def test_conv_decode_form(x_dt, cs_dt, w_dt, bias, silu):
 @pytest.mark.parametrize("x_dt,cs_dt,w_dt", [("bf16", "bf16", "bf16"), ("f32", "f32", "f32"),
                                              ("f32", "bf16", "f32")])
 @pytest.mark.parametrize("out_dt", ["f32", "bf16"])
-def test_conv_varlen_form(x_dt, cs_dt, w_dt, out_dt):
+@pytest.mark.parametrize("dim", [264, 262])   # token-parallel kernel; general kernel (dim % 4 != 0)
+def test_conv_varlen_form(x_dt, cs_dt, w_dt, out_dt, dim):
     lengths = [1, 2, 3, 0, 17, 64, 5, 200]
     cu = gi.cu_from_lengths(lengths)
-    T, dim, ns = int(cu[-1]), 264, 12
+    T, ns = int(cu[-1]), 12
     x, cs, w, b = _case(T, dim, ns, x_dt, cs_dt, w_dt, True, seed=32)
     slots = torch.tensor([4, 8, 0, 2, 11, 1, 6, 9], dtype=torch.int32)
     cs_g = cs.cuda()
@@ -106,6 +107,54 @@ def test_conv_varlen_equals_token_by_token():
         o = torch.empty(len(rows), dim, device="cuda")
         gdn.gdn_conv_update(x[idx].contiguous().cuda(), slots[rows].cuda(), cs_b, w.cuda(), o)
         out_b[idx.cuda()] = o
+    torch.cuda.synchronize()
+    assert torch.equal(out_a, out_b)
+    assert torch.equal(cs_a, cs_b)
+
+
+@pytest.mark.parametrize("x_dt,cs_dt", [("bf16", "bf16"), ("f32", "bf16")])
+def test_conv_varlen_many_short_sequences(x_dt, cs_dt):
+    """Sequences of 0..20 tokens starting anywhere inside the 16-token tiles of
+    the token-parallel kernel (several sequence starts per tile), some inactive."""
+    gen = torch.Generator().manual_seed(35)
+    n = 120
+    lengths = torch.randint(0, 21, (n,), generator=gen).tolist()
+    cu = gi.cu_from_lengths(lengths)
+    T, dim, ns = int(cu[-1]), 256, n + 7
+    x, cs, w, b = _case(T, dim, ns, x_dt, cs_dt, "bf16", True, seed=36)
+    slots = (torch.randperm(ns - 1, generator=gen)[:n] + 1).to(torch.int32)
+    slots[::9] = 0                                         # inactive sequences
+    cs_g = cs.cuda()
+    out = torch.full((T, dim), float("nan"), device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    gdn.gdn_conv_update(x.cuda(), slots.cuda(), cs_g, w.cuda(), out, bias=b.cuda(),
+                        cu_seqlens=cu.cuda(), flags=gdn.FLAG_SILU | gdn.FLAG_VALIDATE,
+                        err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    cs_o = f64(cs).copy()
+    ref = oracle.conv_update(f64(x), slots.numpy(), cs_o, f64(w), bias=f64(b),
+                             cu_seqlens=cu.numpy(), flags=oracle.FLAG_SILU)
+    assert rel_err(f64(out), ref) <= 1e-5
+    assert torch.equal(cs_g.cpu(), _expected_cache(cs, cs_o, cs.dtype))
+
+
+def test_conv_varlen_paths_agree_bitwise():
+    """The token-parallel kernel (16-byte aligned tensors) and the general one
+    (taken for a misaligned output view) give identical outputs and caches."""
+    lengths = [3, 1, 0, 70, 2, 33]
+    cu = gi.cu_from_lengths(lengths)
+    T, dim, ns = int(cu[-1]), 256, 9
+    x, cs, w, b = _case(T, dim, ns, "bf16", "bf16", "bf16", True, seed=37)
+    slots = torch.tensor([3, 1, 5, 8, 0, 2], dtype=torch.int32)
+    cs_a, cs_b = cs.cuda(), cs.cuda()
+    out_a = torch.empty(T, dim, device="cuda")
+    gdn.gdn_conv_update(x.cuda(), slots.cuda(), cs_a, w.cuda(), out_a, bias=b.cuda(),
+                        cu_seqlens=cu.cuda(), flags=gdn.FLAG_SILU)
+    buf = torch.empty(T * dim + 1, device="cuda")
+    out_b = buf[1:].view(T, dim)                           # 4-byte aligned only
+    gdn.gdn_conv_update(x.cuda(), slots.cuda(), cs_b, w.cuda(), out_b, bias=b.cuda(),
+                        cu_seqlens=cu.cuda(), flags=gdn.FLAG_SILU)
     torch.cuda.synchronize()
     assert torch.equal(out_a, out_b)
     assert torch.equal(cs_a, cs_b)
