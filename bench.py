@@ -220,16 +220,23 @@ class MixedSetup:
         self.cu = gi.cu_from_lengths(self.lengths).to(dev)
         self.out = torch.empty(256 + T, HV, DV, device=dev)
         dims = big.dims
-        self.ws = torch.empty(big.gdn.gdn_mixed_workspace_size(dims, 256, T), dtype=torch.uint8,
-                              device=dev)
+        # the minimal workspace runs each prefill sequence whole; with the
+        # prefill's segment states as well it may take the segment-parallel schedule
+        base = big.gdn.gdn_mixed_workspace_size(dims, 256, T)
+        self.ws_min = torch.empty(base, dtype=torch.uint8, device=dev)
+        self.ws = torch.empty(base + big.gdn.gdn_prefill_workspace_size(dims, 2, T),
+                              dtype=torch.uint8, device=dev)
         self.T = T
 
-    def step(self):
+    def step(self, ws=None):
         b = self.big
         d = b.d
         self.gdn.gdn_mixed_step(self.x, self.g, self.beta, 256, self.cu, self.slots,
                                 d["conv_state"], d["conv_weight"], d["rec_state"], self.out,
-                                b.dims, b.scale, workspace=self.ws)
+                                b.dims, b.scale, workspace=self.ws if ws is None else ws)
+
+    def step_whole(self):
+        self.step(self.ws_min)
 
 
 class PrefillSetup:
@@ -488,6 +495,7 @@ def main():
     # a mixed step: the batch-256 decode rows plus two 1024-token prefills
     mixed = MixedSetup(big, seed=9, dev="cuda")
     ms_mixed = time_loop(torch, mixed.step, args.steps, args.warmup)
+    ms_mixed_whole = time_loop(torch, mixed.step_whole, args.steps, args.warmup)
     # the same batch-256 step and prefill with the gating fused in (raw a, b)
     big.use_gating(seed=7)
     pre.use_gating(seed=8)
@@ -549,8 +557,12 @@ def main():
         "gated_rmsnorm_note": ("gdn_gated_rmsnorm on the prefill output: "
                                f"{pre.T * HV} rows of {DV}, bf16 x, z, out, fp32 weight"),
         "mixed_step_ms_mean": round(mean(ms_mixed), 4),
+        "mixed_step_whole_prefill_ms_mean": round(mean(ms_mixed_whole), 4),
         "mixed_step_note": ("gdn_mixed_step, eager: the 256 decode rows of the batch-256 "
-                            "workload plus two 1024-token prefill sequences (pre-conv input)"),
+                            "workload plus two 1024-token prefill sequences (pre-conv input); "
+                            "the workspace holds the prefill's segment states, so the prefill "
+                            "part may run segment-parallel; *_whole_prefill: the minimal "
+                            "workspace, one run per sequence"),
         "decode_rec_kernel_b256_ms_mean": round(rec_ms, 5),
         "decode_rec_kernel_b256_GBps": round(rec_gbs, 2),
         "decode_rec_kernel_b256_pct_hbm_peak": round(100 * rec_gbs / HBM_PEAK_GBS, 2),

@@ -381,7 +381,8 @@ gdn_status gdn_mixed_step(const void* x, gdn_dtype x_dt, const float* g, const f
                           gdn_dtype out_dt, const gdn_dims* dims, float scale, int32_t flags,
                           void* workspace, size_t workspace_bytes, int32_t* err_flag,
                           void* stream) {
-    if (gdn_status st = check_flags(flags, KNOWN_FLAGS | GDN_FLAG_STEP_FUSED | GDN_FLAG_STEP_SPLIT,
+    if (gdn_status st = check_flags(flags, KNOWN_FLAGS | GDN_FLAG_STEP_FUSED | GDN_FLAG_STEP_SPLIT |
+                                               GDN_FLAG_PREFILL_SEQUENTIAL,
                                     err_flag))
         return st;
     if ((flags & GDN_FLAG_STEP_FUSED) && (flags & GDN_FLAG_STEP_SPLIT)) return GDN_ERR_FLAGS;
@@ -441,9 +442,22 @@ gdn_status gdn_mixed_step(const void* x, gdn_dtype x_dt, const float* g, const f
     gp.beta = ga.beta + static_cast<size_t>(n_dec) * HV;
     const int32_t Hdk = dims->num_k_heads * dims->head_k_dim;
     void* op = static_cast<char*>(out) + static_cast<size_t>(n_dec) * HV * dv * eso;
-    GDN_TRY_LAUNCH(launch_prefill(yp, yp + Hdk, yp + 2 * Hdk, GDN_BF16, gp, cu_seqlens, n_pre, sp,
-                                  rec_state, op, out_dt, *dims, D, D, scale,
-                                  flags & (GDN_FLAG_QK_L2NORM), ef, s));
+    // the segment-parallel schedule that gdn_prefill_chunked would pick, when
+    // the workspace holds its segment states past the activations
+    const size_t base = gdn_mixed_workspace_size(dims, n_dec, total_pre);
+    int32_t seg = (flags & GDN_FLAG_PREFILL_SEQUENTIAL) ? 0 : prefill_auto_segment_len(*dims, n_pre, total_pre);
+    if (seg > 0 && workspace_bytes - base < prefill_segmented_workspace(*dims, n_pre, total_pre, seg))
+        seg = 0;
+    if (seg > 0)
+        GDN_TRY_LAUNCH(launch_prefill_segmented(yp, yp + Hdk, yp + 2 * Hdk, GDN_BF16, gp, cu_seqlens,
+                                                n_pre, total_pre, sp, rec_state, op, out_dt, *dims,
+                                                D, D, scale, flags & (GDN_FLAG_QK_L2NORM), seg,
+                                                reinterpret_cast<float*>(static_cast<char*>(workspace) + base),
+                                                ef, s));
+    else
+        GDN_TRY_LAUNCH(launch_prefill(yp, yp + Hdk, yp + 2 * Hdk, GDN_BF16, gp, cu_seqlens, n_pre, sp,
+                                      rec_state, op, out_dt, *dims, D, D, scale,
+                                      flags & (GDN_FLAG_QK_L2NORM), ef, s));
     return GDN_OK;
 }
 

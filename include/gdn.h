@@ -374,9 +374,13 @@ size_t gdn_mixed_workspace_size(const gdn_dims* dims, int32_t n_dec, int32_t tot
  * so every decode row's output, recurrent state and conv state are bitwise
  * independent of what else the step holds.  The prefill tokens go through
  * the varlen conv (SiLU per flags) into bf16 activations -- the serving path's
- * convention -- and then the chunked prefill.  A sequence prefilled over
- * several calls equals one whole prefill bitwise when every non-final call
- * covers a multiple of 64 of its tokens (the chunk grid then coincides).
+ * convention -- and then the chunked prefill: as one run per (sequence, value
+ * head), or, when the workspace also holds the segment states, on the
+ * segment-parallel schedule that gdn_prefill_chunked would pick (see
+ * gdn_prefill_workspace_size).  With one run per sequence (the minimal
+ * workspace, or GDN_FLAG_PREFILL_SEQUENTIAL) a sequence prefilled over several
+ * calls equals one whole prefill bitwise when every non-final call covers a
+ * multiple of 64 of its tokens (the chunk grid then coincides).
  *
  *   x            [n_dec + total_pre, D], x_dt: the n_dec decode rows, then the
  *                prefill tokens (pre-conv mixed q | k | v)
@@ -393,9 +397,14 @@ size_t gdn_mixed_workspace_size(const gdn_dims* dims, int32_t n_dec, int32_t tot
  *                the same conv cache and recurrent cache)
  *   out          [n_dec + total_pre, HV, dv], out_dt
  *   flags        GDN_FLAG_SILU | GDN_FLAG_QK_L2NORM | GDN_FLAG_VALIDATE (one
- *                validation over all slot indices and cu_seqlens), and the
- *                decode rows' GDN_FLAG_STEP_FUSED / GDN_FLAG_STEP_SPLIT
- *   workspace    >= gdn_mixed_workspace_size(dims, n_dec, total_pre) bytes
+ *                validation over all slot indices and cu_seqlens), the
+ *                decode rows' GDN_FLAG_STEP_FUSED / GDN_FLAG_STEP_SPLIT, and
+ *                GDN_FLAG_PREFILL_SEQUENTIAL (one run per sequence always)
+ *   workspace    >= gdn_mixed_workspace_size(dims, n_dec, total_pre) bytes;
+ *                with gdn_mixed_workspace_size(dims, n_dec, total_pre) +
+ *                gdn_prefill_workspace_size(dims, n_pre, total_pre) bytes the
+ *                prefill part may take the segment-parallel schedule (its
+ *                segment states live past the activations)
  * The prefill part needs dk == dv <= 128 (GDN_ERR_DIMS otherwise, when
  * n_pre > 0).
  */

@@ -46,15 +46,24 @@ def _rows(n, seed):
     return x, g, beta
 
 
-def _mixed(x, g, beta, n_dec, lengths, slots, caches, flags=gdn.DEFAULT_DECODE_FLAGS):
-    """Run one mixed step on GPU copies of the caches; returns (out, cs, rs)."""
+def _mixed(x, g, beta, n_dec, lengths, slots, caches, flags=gdn.DEFAULT_DECODE_FLAGS,
+           segment_states=False):
+    """Run one mixed step on GPU copies of the caches; returns (out, cs, rs).
+    segment_states: give the step room for the prefill's segment states."""
     cs, w, b, rs = (c.cuda() for c in caches)
     cs, rs = cs.clone(), rs.clone()
     cu = gi.cu_from_lengths(lengths).cuda() if lengths else None
     dims = gdn.make_dims(H, HV, DK, DK, 4)
     out = torch.full((x.shape[0], HV, DK), float("nan"), device="cuda")
+    ws = None
+    if segment_states:
+        T = sum(lengths)
+        extra = gdn.gdn_prefill_workspace_size(dims, len(lengths), T)
+        assert extra > 0, "these sizes should take the segment-parallel schedule"
+        ws = torch.empty(gdn.gdn_mixed_workspace_size(dims, n_dec, T) + extra,
+                         dtype=torch.uint8, device="cuda")
     gdn.gdn_mixed_step(x.cuda(), g.cuda(), beta.cuda(), n_dec, cu, slots.cuda(), cs, w, rs, out,
-                       dims, SCALE, conv_bias=b, flags=flags)
+                       dims, SCALE, conv_bias=b, flags=flags, workspace=ws)
     torch.cuda.synchronize()
     return out, cs, rs
 
@@ -97,6 +106,36 @@ def test_mixed_step_matches_oracle():
     c = [n_dec + t for t in gi.cu_from_lengths(lengths).tolist()]
     assert torch.all(out[c[4]:c[5]] == 0)                 # inactive prefill sequence
     assert torch.all(out[1] == 0)                         # inactive decode row
+
+
+def test_mixed_step_segmented_prefill():
+    """With room for the segment states, the prefill part of a mixed step runs
+    segment-parallel (two 1024-token sequences of 16 chunks over 16 (sequence,
+    value head) runs) and still meets the prefill bar against the oracle; the
+    decode rows stay bitwise those of the minimal-workspace step, and the
+    prefill rows differ from the whole-run schedule only by rounding."""
+    n_dec, lengths = 3, [1024, 1024]
+    caches = _caches(12, seed=75)
+    x, g, beta = _rows(n_dec + sum(lengths), seed=76)
+    # slow decay on the prefill rows, so that a segment's start state still
+    # matters at its end (with g ~ U[-1, 0] it fades by ~e^-32 over 64 tokens,
+    # and both schedules give the same bits)
+    g[n_dec:] *= 0.02
+    slots = torch.tensor([2, 0, 7, 5, 9], dtype=torch.int32)
+    out, cs, rs = _mixed(x, g, beta, n_dec, lengths, slots, caches, segment_states=True)
+    out_w, cs_w, rs_w = _mixed(x, g, beta, n_dec, lengths, slots, caches)
+    o_dec, o_pre, cs_ref, rs_ref = _oracle_mixed(x, g, beta, n_dec, lengths, slots, caches)
+    assert torch.equal(out[:n_dec], out_w[:n_dec])
+    assert rel_err(f64(out[n_dec:]), o_pre) <= PREFILL_TOL
+    assert not torch.equal(out[n_dec:], out_w[n_dec:]), "the segment-parallel schedule did not run"
+    for i, s in enumerate(slots.tolist()):
+        if s <= 0:
+            continue
+        tol = DECODE_TOL if i < n_dec else PREFILL_TOL
+        assert rel_err(f64(rs[s]), rs_ref[s]) <= tol, (i, s)
+        assert np.array_equal(f64(cs[s]), cs_ref[s]), f"conv roll of slot {s}"
+        if i < n_dec:
+            assert torch.equal(rs[s], rs_w[s]) and torch.equal(cs[s], cs_w[s])
 
 
 @pytest.mark.parametrize("path", [None, "fused", "split"])
