@@ -422,8 +422,8 @@ def gi_stress(T):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the GDN core has "
-              "no cross-GPU step in this build.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the GDN core "
+              "implements no cross-GPU step.", file=sys.stderr)
         sys.exit(2)
     import torch
     import gated_deltanet_recurrent_gdn_amd as gdn

@@ -4,13 +4,15 @@
 // mismatch mechanisms": the conv state is [num_blocks, dim, W-1]; the window
 // is the state followed by the new token(s); the fp32 accumulator starts from
 // the bias and adds the taps in order; the state is rolled to the last W-1
-// raw inputs (compared bitwise there); SiLU is optional.  This build keeps the
-// exact bf16 x bf16 products (exact in fp32) instead of rounding each product
-// to bf16, and computes SiLU with IEEE division and the device expf.
+// raw inputs (compared bitwise there); SiLU is optional.  The products are
+// kept exact (bf16 x bf16 is exact in fp32) rather than rounded to bf16 one by
+// one, and SiLU uses IEEE division and the device expf.
 //
-// Ownership: each (sequence, channel) is read and rolled by exactly one
-// workgroup, and inside it by one thread, after every read of the old state
-// by that workgroup -- no cross-workgroup race on the in-place roll.
+// The in-place roll never races a read of the old state: in the decode form
+// and the general varlen kernel one thread reads and then rolls each
+// (sequence, channel) (the varlen one after a barrier that follows every read
+// of its workgroup); the token-parallel varlen kernel only reads the cache,
+// and a separate kernel, next on the stream, rolls it.
 #include <type_traits>
 
 #include "conv_io.hpp"
