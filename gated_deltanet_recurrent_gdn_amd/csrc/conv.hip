@@ -92,6 +92,18 @@ __global__ __launch_bounds__(256) void conv_varlen_tok_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) wr[j] = reinterpret_cast<const WR*>(w + static_cast<size_t>(c) * CONV_W)[j];
     const WR br = bias ? *reinterpret_cast<const WR*>(bias + c) : V4<WT>::make(0.f, 0.f, 0.f, 0.f);
+    // widened once: each input feeds up to W tokens, each weight every token
+    float wf[4][CONV_W], bf[4], xf[CONV_TT + CONV_W - 1][4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        bf[e] = V4<WT>::get(br, e);
+#pragma unroll
+        for (int j = 0; j < CONV_W; ++j) wf[e][j] = vget<WT, 4>(wr, 4 * e + j);
+    }
+#pragma unroll
+    for (int i = 0; i < CONV_TT + CONV_W - 1; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xf[i][e] = V4<XT>::get(xv[i], e);
 
     // the sequence n with cu[n] <= t0 < cu[n + 1]
     int lo = 0, hi = n_seqs;
@@ -122,19 +134,24 @@ __global__ __launch_bounds__(256) void conv_varlen_tok_kernel(
         }
         float y[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = V4<WT>::get(br, e);
+        for (int e = 0; e < 4; ++e) y[e] = bf[e];
+        if (t - (CONV_W - 1) >= st) {             // the whole window is in the sequence
 #pragma unroll
-        for (int j = 0; j < CONV_W; ++j) {
-            const int p = t - (CONV_W - 1) + j;
-            if (p >= st) {
+            for (int j = 0; j < CONV_W; ++j)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    y[e] = fmaf(vget<WT, 4>(wr, 4 * e + j), V4<XT>::get(xv[i + j], e), y[e]);
-            } else {                              // tap m of the cached state
-                const CT* sp = cs + (static_cast<size_t>(s) * D + c) * (CONV_W - 1) + (p - st + CONV_W - 1);
+                for (int e = 0; e < 4; ++e) y[e] = fmaf(wf[e][j], xf[i + j][e], y[e]);
+        } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    y[e] = fmaf(vget<WT, 4>(wr, 4 * e + j), elem<CT>::ld(sp + (CONV_W - 1) * e), y[e]);
+            for (int j = 0; j < CONV_W; ++j) {
+                const int p = t - (CONV_W - 1) + j;
+                if (p >= st) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) y[e] = fmaf(wf[e][j], xf[i + j][e], y[e]);
+                } else {                          // tap m of the cached state
+                    const CT* sp = cs + (static_cast<size_t>(s) * D + c) * (CONV_W - 1) + (p - st + CONV_W - 1);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) y[e] = fmaf(wf[e][j], elem<CT>::ld(sp + (CONV_W - 1) * e), y[e]);
+                }
             }
         }
         if (silu_on) {
