@@ -470,6 +470,20 @@ def main():
     ms_norm = time_loop(torch, lambda: gdn.gdn_gated_rmsnorm(pre.out, wn, yn, z=zn),
                         args.steps, args.warmup)
     norm_bytes = pre.T * HV * DV * 2 * 3 + DV * 4
+    del zn, yn
+    # the varlen conv (gdn_conv_update with cu_seqlens) over the prefill
+    # workload's token rows: pre-conv mixed q | k | v bf16 [T, 8192] -> bf16
+    # activations, SiLU on, rolling the 8 sequences' conv slots
+    cgen = torch.Generator().manual_seed(11)
+    cx = torch.randn(pre.T, D, generator=cgen).to(torch.bfloat16).to(dev)
+    ccs = torch.randn(16, D, W - 1, generator=cgen).to(torch.bfloat16).to(dev)
+    cw = (torch.rand(D, W, generator=cgen) - 0.5).to(torch.bfloat16).to(dev)
+    cy = torch.empty(pre.T, D, dtype=torch.bfloat16, device=dev)
+    ms_conv = time_loop(torch, lambda: gdn.gdn_conv_update(cx, pre.p["slot_idx"], ccs, cw, cy,
+                                                           cu_seqlens=pre.p["cu_seqlens"]),
+                        args.steps, args.warmup)
+    conv_bytes = pre.T * D * 2 * 2 + 2 * 8 * D * (W - 1) * 2 + D * W * 2
+    del cx, ccs, cw, cy
     # the prefill with the Newton-Schulz (4 bf16 rounds) block-inverse variant
     ms_pre_ns4 = time_loop(torch, lambda: gdn.gdn_prefill_chunked(
         pre.p["q"], pre.p["k"], pre.p["v"], pre.p["g"], pre.p["beta"], pre.p["cu_seqlens"],
@@ -552,6 +566,11 @@ def main():
                                   "H=16 HV=32 d=128): gdn_prefill_chunked with "
                                   "GDN_FLAG_PREFILL_SEQUENTIAL vs the segment-parallel schedule "
                                   "it picks with its workspace"),
+        "conv_varlen_ms_mean": round(mean(ms_conv), 4),
+        "conv_varlen_GBps": round(conv_bytes / (mean(ms_conv) * 1e-3) / 1e9, 1),
+        "conv_varlen_note": ("gdn_conv_update with cu_seqlens over the prefill workload's "
+                             f"{pre.T} token rows: bf16 [T, {D}] in and out, SiLU, 8 conv "
+                             "slots rolled (conv + roll kernels)"),
         "gated_rmsnorm_ms_mean": round(mean(ms_norm), 4),
         "gated_rmsnorm_GBps": round(norm_bytes / (mean(ms_norm) * 1e-3) / 1e9, 1),
         "gated_rmsnorm_note": ("gdn_gated_rmsnorm on the prefill output: "
