@@ -292,7 +292,18 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
     __shared__ Sm sm;
 
     if (call_rejected(err_flag)) return;
-    const int hv = blockIdx.x;
+    // Value heads to workgroups so that the G = HV / H heads sharing a key head
+    // get workgroup ids 8 apart (workgroups go to the 8 XCDs round-robin by
+    // id, and each XCD has its own L2): they then read that key head's q and k
+    // through one L2.  Needs HV % 8 == 0 and H % 8 == 0; identity otherwise.
+    int hv = blockIdx.x;
+    {
+        const int G = HV / H;
+        if (HV % 8 == 0 && H % 8 == 0) {
+            const int a = hv >> 3, b = hv & 7;
+            hv = G * (8 * (a / G) + b) + a % G;
+        }
+    }
     const int n = blockIdx.y;
     const int h = hv / (HV / H);
     const int tid = threadIdx.x;
