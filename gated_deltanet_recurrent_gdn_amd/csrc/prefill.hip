@@ -1186,19 +1186,25 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, gdn_dtype
 // ---------------------------------------------------------------------------
 // Segment-parallel prefill
 
-// Start states of segments 2.. of each sequence: start[j + 1] = start[j] P_j + B_j
-// (row v of a state depends only on row v of the previous one, so a workgroup
-// owns 16 state rows of one (sequence, value head); the sum over the inner
-// index runs in ascending order with fused multiply-adds, fp32).  P_j is staged
-// in LDS each step from registers loaded during the previous step; the 16 rows
-// stay in LDS between steps.
+// Start states of segments 2.. of each sequence: start[j + 1] = start[j] P_j + B_j.
+// Row v of a state depends only on row v of the previous one, so a workgroup
+// owns 16 state rows of one (sequence, value head).  Each step is a 16 x D by
+// D x D product on fp32 MFMA (v_mfma_f32_16x16x4f32: fp32 products and sums),
+// accumulated onto B_j's rows: wave w computes the 16-column tiles
+// w TPW .. w TPW + TPW - 1; lane group q of a wave takes the inner indices
+// KT q + t (t = 0 .. KT - 1), so a lane's row fragment is one contiguous run of
+// the LDS row buffer, and the wave's columns of P_j come from global memory
+// straight into registers in the operand layout -- P_{j+1}'s (and B_{j+1}'s)
+// during step j.
 template <int D>
 __global__ __launch_bounds__(256) void prefill_seg_scan_kernel(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ slot, int32_t HV, int32_t seg_len,
     float* __restrict__ ws, const int32_t* __restrict__ err_flag) {
-    constexpr int CPT = D / 16;                  // columns per thread
-    __shared__ float ps[D * D];
-    __shared__ float rows[16 * D];
+    constexpr int NTL = D / 16;                  // 16-column tiles
+    constexpr int TPW = NTL >= 4 ? NTL / 4 : 1;  // tiles per wave
+    constexpr int KT = D / 4;                    // inner steps per lane group
+    constexpr int RS = D + 4;                    // LDS row stride (floats): 2-way at most
+    __shared__ float rows[16 * RS];
     if (call_rejected(err_flag)) return;
     const int hv = blockIdx.x, n = blockIdx.y, rb = blockIdx.z;
     const int32_t t0 = cu[n], t1 = cu[n + 1];
@@ -1210,53 +1216,69 @@ __global__ __launch_bounds__(256) void prefill_seg_scan_kernel(
         return ws + ((id * 3 + kind) * HV + hv) * static_cast<size_t>(D) * D;
     };
     const int tid = threadIdx.x;
-    const int r = tid >> 4;                      // row within the block
-    const int c0 = (tid & 15) * CPT;             // first column
-    const int v = 16 * rb + r;
-    constexpr int PL = D * D / 4 / 256;          // float4 of P per thread
-    f32x4 pre[PL];
-    float bn[CPT];                               // the next step's B row part
+    const int wave = tid >> 6, lane = tid & 63;
+    const int q = lane >> 4, l16 = lane & 15;
+    const bool active = wave * TPW < NTL;        // D = 32: two waves hold the two tiles
+    const int v0 = 16 * rb;                      // first state row of the block
+
+    // start[1]'s rows into LDS
     {
-        const f32x4* p = reinterpret_cast<const f32x4*>(wsm(id0 + 1, 1));
-#pragma unroll
-        for (int k = 0; k < PL; ++k) pre[k] = p[tid + 256 * k];
-        const float* b = wsm(id0 + 1, 2) + static_cast<size_t>(v) * D + c0;
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) bn[c] = b[c];
+        const float* s1 = wsm(id0 + 1, 0) + static_cast<size_t>(v0) * D;
+        for (int i = tid; i < 16 * D; i += 256) rows[(i / D) * RS + i % D] = s1[i];
     }
-    {
-        const float* s1 = wsm(id0 + 1, 0);
+    // P_j in the B-operand layout: pc[tt][t] = P_j[KT q + t][16 (wave TPW + tt) + l16];
+    // B_j in the accumulator layout: bc[tt][r] = B_j[v0 + 4 q + r][16 (wave TPW + tt) + l16]
+    float pc[TPW][KT], pn[TPW][KT];
+    f32x4 bc[TPW], bn[TPW];
+    auto load_pb = [&](int j, float (&pp)[TPW][KT], f32x4 (&bb)[TPW]) {
+        const float* P = wsm(id0 + j, 1);
+        const float* Bm = wsm(id0 + j, 2);
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) rows[r * D + c0 + c] = s1[static_cast<size_t>(v) * D + c0 + c];
-    }
+        for (int tt = 0; tt < TPW; ++tt) {
+            const int col = 16 * (wave * TPW + tt) + l16;
+#pragma unroll
+            for (int t = 0; t < KT; ++t) pp[tt][t] = P[static_cast<size_t>(KT * q + t) * D + col];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) bb[tt][r] = Bm[static_cast<size_t>(v0 + 4 * q + r) * D + col];
+        }
+    };
+    if (active) load_pb(1, pc, bc);
     for (int j = 1; j <= nseg - 2; ++j) {
-        __syncthreads();                         // previous step's reads of ps are done
+        __syncthreads();                         // rows holds start[j]
+        if (active && j + 1 <= nseg - 2) load_pb(j + 1, pn, bn);
+        f32x4 acc[TPW];
+        if (active) {
+            float a[KT];
 #pragma unroll
-        for (int k = 0; k < PL; ++k) reinterpret_cast<f32x4*>(ps)[tid + 256 * k] = pre[k];
-        float acc[CPT];
+            for (int t = 0; t < KT; t += 4) {
+                const f32x4 v = *reinterpret_cast<const f32x4*>(&rows[l16 * RS + KT * q + t]);
+                a[t] = v[0]; a[t + 1] = v[1]; a[t + 2] = v[2]; a[t + 3] = v[3];
+            }
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) acc[c] = bn[c];
-        __syncthreads();
-        {                                        // the next step's P and B (the last step reloads its own)
-            const int jn = j + 1 <= nseg - 2 ? j + 1 : j;
-            const f32x4* p = reinterpret_cast<const f32x4*>(wsm(id0 + jn, 1));
+            for (int tt = 0; tt < TPW; ++tt) acc[tt] = bc[tt];
 #pragma unroll
-            for (int k = 0; k < PL; ++k) pre[k] = p[tid + 256 * k];
-            const float* b = wsm(id0 + jn, 2) + static_cast<size_t>(v) * D + c0;
+            for (int t = 0; t < KT; ++t)
 #pragma unroll
-            for (int c = 0; c < CPT; ++c) bn[c] = b[c];
+                for (int tt = 0; tt < TPW; ++tt) acc[tt] = mfma4(a[t], pc[tt][t], acc[tt]);
         }
-        for (int i = 0; i < D; ++i) {
-            const float x = rows[r * D + i];
+        __syncthreads();                         // every read of start[j] is done
+        if (active) {
+            float* dst = wsm(id0 + j + 1, 0);
 #pragma unroll
-            for (int c = 0; c < CPT; ++c) acc[c] = fmaf(x, ps[i * D + c0 + c], acc[c]);
-        }
-        __syncthreads();                         // every read of rows is done
-        float* dst = wsm(id0 + j + 1, 0) + static_cast<size_t>(v) * D + c0;
+            for (int tt = 0; tt < TPW; ++tt) {
+                const int col = 16 * (wave * TPW + tt) + l16;
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-            rows[r * D + c0 + c] = acc[c];
-            dst[c] = acc[c];
+                for (int r = 0; r < 4; ++r) {
+                    rows[(4 * q + r) * RS + col] = acc[tt][r];
+                    dst[static_cast<size_t>(v0 + 4 * q + r) * D + col] = acc[tt][r];
+                }
+            }
+#pragma unroll
+            for (int tt = 0; tt < TPW; ++tt) {
+                bc[tt] = bn[tt];
+#pragma unroll
+                for (int t = 0; t < KT; ++t) pc[tt][t] = pn[tt][t];
+            }
         }
     }
 }
