@@ -234,3 +234,46 @@ def test_mixed_validation_covers_both_parts():
     assert int(err.item()) & gdn.EFLAG_SLOT_REPEAT
     assert torch.isnan(out).all()
     assert torch.equal(cs, cs0) and torch.equal(rs, rs0)
+
+
+def test_mixed_step_graph_replay_matches_eager():
+    """A captured HIP graph of a mixed step on the segment-parallel schedule
+    (varlen conv + roll, both segment passes and the scan, the decode rows)
+    reproduces three consecutive eager steps bitwise on every replay, with eager
+    work between replays: every call only enqueues kernels."""
+    n_dec, lengths = 5, [300, 700]
+    dims = gdn.make_dims(H, HV, DK, DK, 4)
+    T = sum(lengths)
+    caches = [c.cuda() for c in _caches(16, seed=77)]
+    x, g, beta = (t.cuda() for t in _rows(n_dec + T, seed=78))
+    slots = torch.tensor([3, 0, 9, 12, 1, 5, 7], dtype=torch.int32).cuda()
+    cu = gi.cu_from_lengths(lengths).cuda()
+    extra = gdn.gdn_prefill_workspace_size(dims, len(lengths), T)
+    assert extra > 0, "these sizes should take the segment-parallel schedule"
+    ws = torch.empty(gdn.gdn_mixed_workspace_size(dims, n_dec, T) + extra, dtype=torch.uint8,
+                     device="cuda")
+
+    def step(cs, rs, out):
+        gdn.gdn_mixed_step(x, g, beta, n_dec, cu, slots, cs, caches[1], rs, out, dims, SCALE,
+                           conv_bias=caches[2], workspace=ws)
+
+    cs_e, rs_e = caches[0].clone(), caches[3].clone()
+    ref = []
+    for _ in range(3):
+        o = torch.empty(n_dec + T, HV, DK, device="cuda")
+        step(cs_e, rs_e, o)
+        ref.append(o)
+    torch.cuda.synchronize()
+    cs_g, rs_g = caches[0].clone(), caches[3].clone()
+    out = torch.empty(n_dec + T, HV, DK, device="cuda")
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(cs_g, rs_g, out)
+    torch.cuda.synchronize()
+    for i in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref[i]), f"replay {i} output"
+        _ = torch.randn(1024, 1024, device="cuda").sum().item()   # eager work between
+    assert torch.equal(rs_g, rs_e)
+    assert torch.equal(cs_g, cs_e)
