@@ -232,11 +232,12 @@ __global__ __launch_bounds__(256) void decode_rec_kernel(
 //
 // DB (double-buffered passes): the second pass's loads also go out before the
 // conv, and each pass's loads go out as soon as the pass two back has stored,
-// so one pass computes while the next one streams in.  The extra 16 state
-// registers fit under the 128-register cap of 1024-thread groups only with q
-// re-read from LDS in each row (and scaled there), which costs about 1.5% when
-// many groups queue per CU; with one or two groups per CU the step is a short
-// latency chain per CU, and there double-buffering saves 15% (batch 16).
+// so one pass computes while the next one streams in.  q is re-read from LDS
+// in each row (and scaled there) to keep the 16 extra state registers well
+// under the 128-register cap of 1024-thread groups (111-113 VGPRs; 127 with q in
+// registers, measured no faster).  With one or two groups per CU the step is a
+// short latency chain per CU, and there double-buffering saves 15% (batch 16);
+// with many groups queued per CU it costs 1.5-2% (batch 256), q placement aside.
 // ---------------------------------------------------------------------------
 // Threads per fused-step workgroup: a pass streams NT / 8 state rows.
 #ifndef GDN_STEP_NT
