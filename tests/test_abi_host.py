@@ -200,6 +200,13 @@ def test_mixed_step_decode_only_dims_ok_without_prefill(lib):
                   ws=None) == OK
 
 
+def test_mixed_step_accepts_sequential_prefill_flag(lib):
+    # GDN_FLAG_PREFILL_SEQUENTIAL (128) keeps the prefill part on whole runs; the
+    # Newton-Schulz A/B flags stay prefill-call only
+    assert _mixed(lib, flags=3 | 128, n_dec=0, n_pre=0, total=0, cu=None, ws=None) == OK
+    assert _mixed(lib, flags=3 | 32) == ERR_FLAGS
+
+
 def test_mixed_workspace_size(lib):
     d = _dims()
     D = 2 * 16 * 128 + 32 * 128
