@@ -75,19 +75,24 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_step_kernel_b256_traffic.t
 DECODE_SRC = os.path.join(ROOT, "gated_deltanet_recurrent_gdn_amd", "csrc", "decode.hip")
 
 
-def measured_traffic():
-    """HBM bytes per launch of the fused step kernel at batch 256 from the
-    committed counter runs (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None
-    when decode.hip has changed since those counters were taken."""
+PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_kernel_varlen_traffic.txt")
+PREFILL_SRC = os.path.join(ROOT, "gated_deltanet_recurrent_gdn_amd", "csrc", "prefill.hip")
+
+
+def measured_traffic(path=TRAFFIC_FILE, src_path=DECODE_SRC, key="decode_hip_sha256"):
+    """HBM bytes per launch from a committed counter summary (FETCH_SIZE +
+    WRITE_SIZE, copy-calibrated) -- by default the fused step kernel at batch
+    256 -- or None when the kernel's source has changed since those counters
+    were taken."""
     import hashlib
     try:
         kv = {}
-        for line in open(TRAFFIC_FILE):
+        for line in open(path):
             if "=" in line and not line.lstrip().startswith("#"):
                 k, v = line.split("=", 1)
                 kv[k.strip()] = v.strip()
-        src = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
-        if kv.get("decode_hip_sha256") != src:
+        src = hashlib.sha256(open(src_path, "rb").read()).hexdigest()
+        if kv.get(key) != src:
             return None
         return int(kv["fetch_bytes_per_launch"]) + int(kv["write_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
@@ -554,6 +559,15 @@ def main():
         "prefill_tokens": pre.T, "prefill_lengths": pre.lengths,
         "prefill_ms_mean": round(pre_ms, 4), "prefill_ms_min": round(min(ms_pre), 4),
         "prefill_tokens_per_s": round(pre_tps, 1),
+        "prefill_roofline": {
+            "bound": "mfma", "kernel": "prefill_kernel",
+            "achieved": round(pre_tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(pre_tflops / BF16_PEAK_TFLOPS, 4),
+            "hbm_frac": round(pre_bytes / (pre_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(PREFILL_TRAFFIC_FILE, PREFILL_SRC, "prefill_hip_sha256"),
+            "algorithmic_flops_per_launch": pre_flops, "algorithmic_bytes_per_launch": pre_bytes,
+            "note": ("one launch per call (whole runs: the chip is full); event-timed eager calls; "
+                     "bound in practice by the sequential chunk chain of the longest sequence")},
         "prefill_TFLOPs": round(pre_tflops, 2),
         "prefill_pct_mfma_peak": round(100 * pre_tflops / BF16_PEAK_TFLOPS, 2),
         "prefill_algorithmic_flops": pre_flops, "prefill_algorithmic_bytes": pre_bytes,
