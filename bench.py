@@ -324,6 +324,17 @@ def host_threads():
     return max(1, min(16, n))
 
 
+def host_cpu_model():
+    """The host CPU's model name (first /proc/cpuinfo entry), or "unknown"."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def run_oracle_threads(n_threads, budget_s, make_unit):
     """Run independent oracle units on n_threads threads for budget_s seconds.
 
@@ -403,7 +414,7 @@ def cpu_baseline(budget_s, n_threads):
     main = {"value": round(gbs, 4), "unit": "GB/s", "cores": n_threads, "kind": "oracle",
             "sample": f"{rows} decode rows (batch-16 steps on {n_threads} threads, each with "
                       f"its own rows and caches; shapes and distributions of the batch-256 "
-                      f"workload) in {dt:.1f} s, fp64 C"}
+                      f"workload) in {dt:.1f} s, fp64 C, host CPU {host_cpu_model()}"}
     one = {"value": round(gbs1, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
            "sample": f"{rows1} decode rows (steps of batch 64) in {dt1:.1f} s, "
                      "single-threaded fp64 C"}
