@@ -366,7 +366,10 @@ def gdn_mixed_step(x, g, beta, n_dec, cu_seqlens, slot_idx, conv_state, conv_wei
     """One step with ``n_dec`` decode rows followed by prefill sequences
     (gdn.h: gdn_mixed_step).  ``x`` [n_dec + T, D] pre-conv, ``cu_seqlens``
     [n_pre + 1] over the T prefill tokens (or None), ``slot_idx`` [n_dec + n_pre],
-    ``out`` [n_dec + T, HV, dv].  Caches updated in place."""
+    ``out`` [n_dec + T, HV, dv].  Caches updated in place.  Without a
+    ``workspace`` the minimal one is allocated (whole prefill runs); a workspace
+    of gdn_mixed_workspace_size + gdn_prefill_workspace_size bytes lets the
+    prefill part take the segment-parallel schedule."""
     lib = load_library()
     rows = x.shape[0]
     HV, dk, dv = dims.num_v_heads, dims.head_k_dim, dims.head_v_dim
