@@ -44,7 +44,15 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 constexpr int CH = 64;          // chunk length (tokens)
-constexpr int PADB = 8;         // bf16 row padding (16 bytes) against LDS bank conflicts
+// bf16 row padding.  The MFMA fragment reads are 16-byte ds_read_b128 with lane l
+// on row l % 16 and 16-byte column block l / 16; the LDS serves them 16 lanes a
+// cycle over 64 banks, and a one-wave probe found them conflict-free when the
+// row stride in 4-byte words is 8 mod 16 (2-way at 4 mod 16).  The transposed
+// and coefficient arrays take that stride (PADT); K and Q keep 4 mod 16 (PADK),
+// because their 8-byte row stores of token pairs conflict 4-way at 4 mod 16
+// but 8-way at 8 mod 16, which measured slower overall.
+constexpr int PADK = 8;
+constexpr int PADT = 16;
 constexpr int PADF = 4;         // fp32 row padding
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
@@ -149,6 +157,14 @@ __device__ __forceinline__ void split8(const uint4& a, const uint4& b, uint4& hi
     lo = make_uint4(l[0], l[1], l[2], l[3]);
 }
 
+// One 8-byte LDS store, kept whole (ds_write_b64).  A store through a uint2
+// can reach the backend as two 32-bit halves (ds_write2_b32), which took more
+// than twice the cycles of ds_write_b64 on the same strided addresses.
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void lds_st8(bf16_t* p, uint32_t a, uint32_t b) {
+    *reinterpret_cast<u32x2_t*>(p) = u32x2_t{a, b};
+}
+
 // Store the 32-bit (t, t+1) pairs of two token rows' 8 columns into a
 // transposed [col][t] array at column c0, token position ta (even; the pair
 // stays adjacent under pperm).
@@ -234,8 +250,10 @@ __device__ __forceinline__ void ns_block_inverse(float* blk, int sf, bf16_t* scr
 template <int D, bool SPL>
 struct PrefillSmem {
     static constexpr int NP = SPL ? 2 : 1;
-    static constexpr int SK = D + PADB;         // row stride of K, Q, W (bf16)
-    static constexpr int ST = CH + PADB;        // row stride of K^T, V^T, coefficient arrays
+    static constexpr int SK = D + PADK;         // row stride of K, Q, W (bf16)
+    // row stride of K^T, V^T, coefficient arrays (PADT, except where it would
+    // not fit the 160 KB of LDS: hi/lo planes at D = 64)
+    static constexpr int ST = CH + ((SPL && D == 64) ? 8 : PADT);
     static constexpr int SF = CH + PADF;        // row stride of fp32 64x64 arrays
     bf16_t k[NP][CH * SK];                      // K   [t][k]
     bf16_t q[NP][CH * SK];                      // Q   [t][k]
@@ -401,8 +419,9 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
         }
 
     // Chunk loads.  Thread (tp, cg) moves token rows 2tp, 2tp+1 at columns
-    // 8 (cg + CG pass); K^T / V^T receive 32-bit (t, t+1) pairs, so the 64 lanes
-    // of a wave store to 64 distinct banks.  The next chunk's loads are issued
+    // 8 (cg + CG pass); K^T / V^T receive 32-bit (t, t+1) pairs, so the 32 lanes
+    // of a half-wave (one cg) store 32 consecutive words: no bank conflict, as
+    // the LDS takes 32-bit stores 32 lanes a cycle over 32 banks.  The next chunk's loads are issued
     // during the current chunk's state update and staged at the loop top.
     const int tp = tid & 31;
     const int cg = tid >> 5;                     // 0..CG-1
@@ -501,10 +520,10 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
                     const int p0 = pperm(k0), p1 = pperm(k0 + 4);
 #pragma unroll
                     for (int e = 0; e < 2; ++e) {
-                        *reinterpret_cast<uint2*>(&sm.k[pl][(ta + e) * SK + p0]) = make_uint2(kw[e][pl].x, kw[e][pl].y);
-                        *reinterpret_cast<uint2*>(&sm.k[pl][(ta + e) * SK + p1]) = make_uint2(kw[e][pl].z, kw[e][pl].w);
-                        *reinterpret_cast<uint2*>(&sm.q[pl][(ta + e) * SK + p0]) = make_uint2(qw[e][pl].x, qw[e][pl].y);
-                        *reinterpret_cast<uint2*>(&sm.q[pl][(ta + e) * SK + p1]) = make_uint2(qw[e][pl].z, qw[e][pl].w);
+                        lds_st8(&sm.k[pl][(ta + e) * SK + p0], kw[e][pl].x, kw[e][pl].y);
+                        lds_st8(&sm.k[pl][(ta + e) * SK + p1], kw[e][pl].z, kw[e][pl].w);
+                        lds_st8(&sm.q[pl][(ta + e) * SK + p0], qw[e][pl].x, qw[e][pl].y);
+                        lds_st8(&sm.q[pl][(ta + e) * SK + p1], qw[e][pl].z, qw[e][pl].w);
                     }
                     store_pairs_t(sm.kt[pl], ST, k0, pperm(ta), kw[0][pl], kw[1][pl]);
                     store_pairs_t(sm.vt[pl], ST, k0, ta, vw[0][pl], vw[1][pl]);
@@ -604,8 +623,8 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
                 *reinterpret_cast<float4*>(&sm.g[i * SF + c]) = make_float4(a[0], a[1], a[2], a[3]);
                 uint2 h2, l2;
                 split4(mp, h2, l2);
-                *reinterpret_cast<uint2*>(&sm.mp[i * ST + pperm(c)]) = h2;         // pperm order
-                *reinterpret_cast<uint2*>(&sm.mp[CH * ST + i * ST + pperm(c)]) = l2;
+                lds_st8(&sm.mp[i * ST + pperm(c)], h2.x, h2.y);                   // pperm order
+                lds_st8(&sm.mp[CH * ST + i * ST + pperm(c)], l2.x, l2.y);
             }
         }
         __syncthreads();
@@ -861,10 +880,10 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
             }
             bf16_t* base = sm.pc.c + r * ST + cb;
             bf16_t* wbase = sm.pc.c + r * ST;            // cW planes in pperm order
-            *reinterpret_cast<uint2*>(wbase + 0 * CH * ST + pperm(cb)) = make_uint2(wh[0], wh[1]);
-            *reinterpret_cast<uint2*>(wbase + 0 * CH * ST + pperm(cb + 4)) = make_uint2(wh[2], wh[3]);
-            *reinterpret_cast<uint2*>(wbase + 1 * CH * ST + pperm(cb)) = make_uint2(wl[0], wl[1]);
-            *reinterpret_cast<uint2*>(wbase + 1 * CH * ST + pperm(cb + 4)) = make_uint2(wl[2], wl[3]);
+            lds_st8(wbase + 0 * CH * ST + pperm(cb), wh[0], wh[1]);
+            lds_st8(wbase + 0 * CH * ST + pperm(cb + 4), wh[2], wh[3]);
+            lds_st8(wbase + 1 * CH * ST + pperm(cb), wl[0], wl[1]);
+            lds_st8(wbase + 1 * CH * ST + pperm(cb + 4), wl[2], wl[3]);
             *reinterpret_cast<uint4*>(base + 2 * CH * ST) = make_uint4(uh[0], uh[1], uh[2], uh[3]);
             *reinterpret_cast<uint4*>(base + 3 * CH * ST) = make_uint4(ul[0], ul[1], ul[2], ul[3]);
         }
