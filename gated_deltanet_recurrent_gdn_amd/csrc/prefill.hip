@@ -47,12 +47,19 @@ constexpr int CH = 64;          // chunk length (tokens)
 // bf16 row padding.  The MFMA fragment reads are 16-byte ds_read_b128 with lane l
 // on row l % 16 and 16-byte column block l / 16; the LDS serves them 16 lanes a
 // cycle over 64 banks, and a one-wave probe found them conflict-free when the
-// row stride in 4-byte words is 8 mod 16 (2-way at 4 mod 16).  The transposed
-// and coefficient arrays take that stride (PADT); K and Q keep 4 mod 16 (PADK),
-// because their 8-byte row stores of token pairs conflict 4-way at 4 mod 16
-// but 8-way at 8 mod 16, which measured slower overall.
-constexpr int PADK = 8;
+// row stride in 4-byte words is 8 mod 16 (2-way at 4 mod 16).  Every bf16
+// operand array takes such a stride.  K and Q are also swizzled (kq_swz).
+constexpr int PADK = 16;
 constexpr int PADT = 16;
+
+// K and Q swizzle: row r's 16-byte units are XOR-permuted within each 64-byte
+// group by (r / 4) % 4.  A lane's 8-byte row stores of token pairs 2tp, 2tp+1
+// then spread over 8 bank pairs instead of 2 (2-way instead of 8-way at the
+// 8 mod 16 stride), and the fragment reads stay conflict-free: for a read
+// group (lanes 0-3, 12-15, 20-27 or the rest of a half-wave) the 16 (row,
+// block) pairs still land on 16 distinct 16-byte bank slots.  Element index e
+// of row r sits at e ^ kq_swz(r).
+__host__ __device__ constexpr int kq_swz(int r) { return ((r >> 2) & 3) << 3; }
 constexpr int PADF = 4;         // fp32 row padding
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
@@ -123,6 +130,12 @@ __device__ __forceinline__ float row_bcast(float x, int j) {
 #undef GDN_RB
 }
 
+// K/Q fragment (either slot order): the 8 bf16 at row `row`, columns
+// (c0 + 8q) ^ kq_swz(row); row % 16 is the lane's l16, so the caller passes
+// sw = kq_swz(l16) (c0 is a multiple of 32, so the XOR stays in the block).
+__device__ __forceinline__ bf16x8 frag_kq(const bf16_t* base, int stride, int row, int c0, int q, int sw) {
+    return as_bf16x8(*reinterpret_cast<const uint4*>(base + row * stride + c0 + ((8 * q) ^ sw)));
+}
 // Standard-slot fragment: 8 consecutive bf16 at row `row`, column c0 + 8q.
 __device__ __forceinline__ bf16x8 frag_std(const bf16_t* base, int stride, int row, int c0, int q) {
     return as_bf16x8(*reinterpret_cast<const uint4*>(base + row * stride + c0 + 8 * q));
@@ -494,6 +507,7 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
         const int lane = tid & 63;
         const int q4 = lane >> 4;
         const int l16 = lane & 15;
+        const int swl = kq_swz(l16);             // K/Q swizzle of the lane's fragment rows
         const int tp = tid & 31;
         const int ta = 2 * tp;
 
@@ -516,14 +530,15 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
                 }
 #pragma unroll
                 for (int pl = 0; pl < NP; ++pl) {
-                    // K and Q rows in pperm order along k; K^T in pperm order along t
-                    const int p0 = pperm(k0), p1 = pperm(k0 + 4);
+                    // K and Q rows in pperm order along k (swizzled: rows ta, ta + 1
+                    // share kq_swz); K^T in pperm order along t
+                    const int p0 = pperm(k0), p1 = pperm(k0 + 4), swt = kq_swz(ta);
 #pragma unroll
                     for (int e = 0; e < 2; ++e) {
-                        lds_st8(&sm.k[pl][(ta + e) * SK + p0], kw[e][pl].x, kw[e][pl].y);
-                        lds_st8(&sm.k[pl][(ta + e) * SK + p1], kw[e][pl].z, kw[e][pl].w);
-                        lds_st8(&sm.q[pl][(ta + e) * SK + p0], qw[e][pl].x, qw[e][pl].y);
-                        lds_st8(&sm.q[pl][(ta + e) * SK + p1], qw[e][pl].z, qw[e][pl].w);
+                        lds_st8(&sm.k[pl][(ta + e) * SK + (p0 ^ swt)], kw[e][pl].x, kw[e][pl].y);
+                        lds_st8(&sm.k[pl][(ta + e) * SK + (p1 ^ swt)], kw[e][pl].z, kw[e][pl].w);
+                        lds_st8(&sm.q[pl][(ta + e) * SK + (p0 ^ swt)], qw[e][pl].x, qw[e][pl].y);
+                        lds_st8(&sm.q[pl][(ta + e) * SK + (p1 ^ swt)], qw[e][pl].z, qw[e][pl].w);
                     }
                     store_pairs_t(sm.kt[pl], ST, k0, pperm(ta), kw[0][pl], kw[1][pl]);
                     store_pairs_t(sm.vt[pl], ST, k0, ta, vw[0][pl], vw[1][pl]);
@@ -565,18 +580,18 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
             for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
                 for (int pa = 0; pa < NP; ++pa) {
-                    const bf16x8 ak = frag_std(sm.k[pa], SK, 16 * tb + l16, 32 * ks, q4);
-                    const bf16x8 aq = frag_std(sm.q[pa], SK, 16 * tb + l16, 32 * ks, q4);
+                    const bf16x8 ak = frag_kq(sm.k[pa], SK, 16 * tb + l16, 32 * ks, q4, swl);
+                    const bf16x8 aq = frag_kq(sm.q[pa], SK, 16 * tb + l16, 32 * ks, q4, swl);
 #pragma unroll
                     for (int pb = 0; pb < NP - pa; ++pb) {
 #pragma unroll
                         for (int j = 0; j < 2; ++j) {
-                            const bf16x8 bk = frag_std(sm.k[pb], SK, 16 * (2 * jh + j) + l16, 32 * ks, q4);
+                            const bf16x8 bk = frag_kq(sm.k[pb], SK, 16 * (2 * jh + j) + l16, 32 * ks, q4, swl);
                             accg[j] = mfma(bk, ak, accg[j]);
                             accp[j] = mfma(bk, aq, accp[j]);
                         }
                         if (diag)
-                            accq = mfma(frag_std(sm.q[pb], SK, 16 * tb + l16, 32 * ks, q4), aq, accq);
+                            accq = mfma(frag_kq(sm.q[pb], SK, 16 * tb + l16, 32 * ks, q4, swl), aq, accq);
                     }
                 }
             }
@@ -657,12 +672,12 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb) {
                     if (dz || (SEG && doo && pb)) {
-                        ak[tb] = frag_perm(sm.k[0], SK, 16 * tb + l16, 32 * ks, q4);
-                        if constexpr (SPL) akl[tb] = frag_perm(sm.k[NP - 1], SK, 16 * tb + l16, 32 * ks, q4);
+                        ak[tb] = frag_kq(sm.k[0], SK, 16 * tb + l16, 32 * ks, q4, swl);
+                        if constexpr (SPL) akl[tb] = frag_kq(sm.k[NP - 1], SK, 16 * tb + l16, 32 * ks, q4, swl);
                     }
                     if (doo && (!SEG || wo)) {
-                        bq[tb] = frag_perm(sm.q[0], SK, 16 * tb + l16, 32 * ks, q4);
-                        if constexpr (SPL) bql[tb] = frag_perm(sm.q[NP - 1], SK, 16 * tb + l16, 32 * ks, q4);
+                        bq[tb] = frag_kq(sm.q[0], SK, 16 * tb + l16, 32 * ks, q4, swl);
+                        if constexpr (SPL) bql[tb] = frag_kq(sm.q[NP - 1], SK, 16 * tb + l16, 32 * ks, q4, swl);
                     }
                 }
                 __builtin_amdgcn_sched_barrier(0);
