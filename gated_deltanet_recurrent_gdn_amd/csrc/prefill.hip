@@ -508,6 +508,9 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
         const int q4 = lane >> 4;
         const int l16 = lane & 15;
         const int swl = kq_swz(l16);             // K/Q swizzle of the lane's fragment rows
+        // M o P-hat takes the same swizzle at the 8 mod 16 word stride (its 8-byte
+        // row stores: 4-way -> 2-way; reads stay conflict-free), not at 4 mod 16
+        const int swm = (ST % 32 == 16) ? swl : 0;
         const int tp = tid & 31;
         const int ta = 2 * tp;
 
@@ -638,8 +641,10 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
                 *reinterpret_cast<float4*>(&sm.g[i * SF + c]) = make_float4(a[0], a[1], a[2], a[3]);
                 uint2 h2, l2;
                 split4(mp, h2, l2);
-                lds_st8(&sm.mp[i * ST + pperm(c)], h2.x, h2.y);                   // pperm order
-                lds_st8(&sm.mp[CH * ST + i * ST + pperm(c)], l2.x, l2.y);
+                // pperm order, swizzled like K and Q where the stride suits it
+                // (row i = 16 tb + l16: the lane's swl)
+                lds_st8(&sm.mp[i * ST + (pperm(c) ^ swm)], h2.x, h2.y);
+                lds_st8(&sm.mp[CH * ST + i * ST + (pperm(c) ^ swm)], l2.x, l2.y);
             }
         }
         __syncthreads();
@@ -1012,8 +1017,8 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
                     if (32 * ks > 16 * tb + 15) continue;          // strictly above the diagonal
-                    const bf16x8 mh = frag_perm(sm.mp, ST, 16 * tb + l16, 32 * ks, q4);
-                    const bf16x8 ml = frag_perm(sm.mp + CH * ST, ST, 16 * tb + l16, 32 * ks, q4);
+                    const bf16x8 mh = frag_kq(sm.mp, ST, 16 * tb + l16, 32 * ks, q4, swm);
+                    const bf16x8 ml = frag_kq(sm.mp + CH * ST, ST, 16 * tb + l16, 32 * ks, q4, swm);
 #pragma unroll
                     for (int vb = 0; vb < VB; ++vb) {
                         o[vb][tb] = mfma(uh[ks][vb], mh, o[vb][tb]);
