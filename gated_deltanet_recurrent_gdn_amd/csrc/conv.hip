@@ -50,7 +50,12 @@ __global__ __launch_bounds__(256) void conv_decode_kernel(
 
 // ---------------------------------------------------------------------------
 // Varlen, token-parallel (the path for dim % 4 == 0 and 16-byte aligned
-// tensors).  grid = (ceil(T / (4 CONV_TT)), ceil(D / 256)); a thread owns 4
+// tensors).  One-dimensional grid of ceil(T / (4 CONV_TT)) token tiles times
+// ceil(D / 256) channel blocks, channel block fastest: consecutive workgroups
+// read consecutive 512- or 1024-byte pieces of the same token rows (7-9% faster
+// than token tiles fastest, whose neighbours read pieces a row apart), and with
+// a multiple of 8 channel blocks a channel block stays on one XCD for every
+// tile, so a tile's W-1 halo rows are in that XCD's L2.  A thread owns 4
 // channels and CONV_TT consecutive tokens of the concatenated token rows (a
 // wave: 256 channels of the same tokens, so each token row is read as one
 // contiguous 512- or 1024-byte span).  All CONV_TT + 3 inputs of the thread's
@@ -77,8 +82,11 @@ __global__ __launch_bounds__(256) void conv_varlen_tok_kernel(
     typedef typename V4<XT>::raw XR;
     typedef typename V4<WT>::raw WR;
     if (call_rejected(err_flag)) return;
-    const int c = 4 * (static_cast<int>(blockIdx.y) * 64 + static_cast<int>(threadIdx.x & 63));
-    const int t0 = static_cast<int>(blockIdx.x) * (4 * CONV_TT) + static_cast<int>(threadIdx.x >> 6) * CONV_TT;
+    const int ncb = (D / 4 + 63) / 64;            // 256-channel blocks per token tile
+    const int cbk = static_cast<int>(blockIdx.x % static_cast<unsigned>(ncb));
+    const int tile = static_cast<int>(blockIdx.x / static_cast<unsigned>(ncb));
+    const int c = 4 * (cbk * 64 + static_cast<int>(threadIdx.x & 63));
+    const int t0 = tile * (4 * CONV_TT) + static_cast<int>(threadIdx.x >> 6) * CONV_TT;
     if (c >= D || t0 >= T || n_seqs <= 0) return;
 
     // the window's inputs first (rows clamped into [0, T); unused ones are
@@ -318,7 +326,10 @@ struct VarlenK {
                          (static_cast<size_t>(D) * sizeof(XT)) % 8 == 0;
         if (vec) {
             if (T > 0) {
-                dim3 grid((T + 4 * CONV_TT - 1) / (4 * CONV_TT), (D / 4 + 63) / 64);
+                const size_t nblk = static_cast<size_t>((T + 4 * CONV_TT - 1) / (4 * CONV_TT)) *
+                                    static_cast<size_t>((D / 4 + 63) / 64);
+                if (nblk > 0x7fffffffu) return hipErrorInvalidValue;
+                dim3 grid(static_cast<unsigned>(nblk));
                 const hipError_t e = launch(conv_varlen_tok_kernel<XT, CT, WT, OT>, grid, dim3(256), 0, st,
                                             static_cast<const XT*>(x), cu, n_seqs, T, slot,
                                             static_cast<const CT*>(cs), static_cast<const WT*>(w),
