@@ -5,6 +5,8 @@
 // no synchronisation, no global mutable state.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "gdn.h"
 #include "gdn_internal.hpp"
 
@@ -373,6 +375,36 @@ size_t gdn_mixed_workspace_size(const gdn_dims* dims, int32_t n_dec, int32_t tot
            round256(static_cast<size_t>(total_pre) * D * sizeof(uint16_t));
 }
 
+// Side stream of the mixed step, one per device, created on first use outside
+// a stream capture and kept until the process ends (default priority).
+struct SideStream {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+    std::mutex mu;
+};
+static SideStream* side_stream_for(hipStream_t caller) {
+    static std::mutex tab_mu;
+    static SideStream* tab[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    std::lock_guard<std::mutex> lk(tab_mu);
+    if (tab[dev]) return tab[dev];
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(caller, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone) return nullptr;
+    auto* p = new SideStream();
+    if (hipStreamCreateWithFlags(&p->s, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&p->fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&p->join, hipEventDisableTiming) != hipSuccess) {
+        if (p->join) (void)hipEventDestroy(p->join);
+        if (p->fork) (void)hipEventDestroy(p->fork);
+        if (p->s) (void)hipStreamDestroy(p->s);
+        delete p;
+        return nullptr;
+    }
+    tab[dev] = p;
+    return p;
+}
+
 gdn_status gdn_mixed_step(const void* x, gdn_dtype x_dt, const float* g, const float* beta,
                           int32_t n_dec, const int32_t* cu_seqlens, int32_t n_pre,
                           int32_t total_pre, const int32_t* slot_idx, void* conv_state,
@@ -420,45 +452,68 @@ gdn_status gdn_mixed_step(const void* x, gdn_dtype x_dt, const float* g, const f
     const size_t eso = (out_dt == GDN_BF16) ? 2 : 4;
 
     // decode rows: exactly the decode-only step's kernels (rows 0 .. n_dec-1)
-    if (gdn_status st = decode_step_launch(x, x_dt, ga, slot_idx, n_dec, conv_state, cs_dt,
-                                           conv_weight, conv_bias, w_dt, rec_state, out, out_dt,
-                                           dims, scale, flags, workspace, ef, s))
-        return st;
-    if (n_pre == 0 || total_pre == 0) {
-        // sequences without tokens leave their state untouched: nothing to launch
-        return GDN_OK;
-    }
+    auto decode_part = [&](hipStream_t ds) -> gdn_status {
+        return decode_step_launch(x, x_dt, ga, slot_idx, n_dec, conv_state, cs_dt, conv_weight, conv_bias,
+                                  w_dt, rec_state, out, out_dt, dims, scale, flags, workspace, ef, ds);
+    };
     // prefill tokens (rows n_dec ..): varlen conv into bf16 activations, then
     // the chunked prefill reading q, k, v as slices of those rows
-    const char* xp = static_cast<const char*>(x) + static_cast<size_t>(n_dec) * D * esx;
-    uint16_t* yp = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) +
-                                           round256(static_cast<size_t>(n_dec) * D * sizeof(float)));
-    const int32_t* sp = slot_idx + n_dec;
-    GDN_TRY_LAUNCH(launch_conv_varlen(xp, x_dt, cu_seqlens, n_pre, total_pre, sp, conv_state,
-                                      cs_dt, conv_weight, conv_bias, w_dt, yp, GDN_BF16, D,
-                                      flags & GDN_FLAG_SILU, ef, s));
-    GateArgs gp = ga;
-    gp.g = ga.g + static_cast<size_t>(n_dec) * HV;
-    gp.beta = ga.beta + static_cast<size_t>(n_dec) * HV;
-    const int32_t Hdk = dims->num_k_heads * dims->head_k_dim;
-    void* op = static_cast<char*>(out) + static_cast<size_t>(n_dec) * HV * dv * eso;
-    // the segment-parallel schedule that gdn_prefill_chunked would pick, when
-    // the workspace holds its segment states past the activations
-    const size_t base = gdn_mixed_workspace_size(dims, n_dec, total_pre);
-    int32_t seg = (flags & GDN_FLAG_PREFILL_SEQUENTIAL) ? 0 : prefill_auto_segment_len(*dims, n_pre, total_pre);
-    if (seg > 0 && workspace_bytes - base < prefill_segmented_workspace(*dims, n_pre, total_pre, seg))
-        seg = 0;
-    if (seg > 0)
-        GDN_TRY_LAUNCH(launch_prefill_segmented(yp, yp + Hdk, yp + 2 * Hdk, GDN_BF16, gp, cu_seqlens,
-                                                n_pre, total_pre, sp, rec_state, op, out_dt, *dims,
-                                                D, D, scale, flags & (GDN_FLAG_QK_L2NORM), seg,
-                                                reinterpret_cast<float*>(static_cast<char*>(workspace) + base),
-                                                ef, s));
-    else
-        GDN_TRY_LAUNCH(launch_prefill(yp, yp + Hdk, yp + 2 * Hdk, GDN_BF16, gp, cu_seqlens, n_pre, sp,
-                                      rec_state, op, out_dt, *dims, D, D, scale,
-                                      flags & (GDN_FLAG_QK_L2NORM), ef, s));
-    return GDN_OK;
+    auto prefill_part = [&](hipStream_t ps, bool beside_decode) -> gdn_status {
+        const char* xp = static_cast<const char*>(x) + static_cast<size_t>(n_dec) * D * esx;
+        uint16_t* yp = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) +
+                                               round256(static_cast<size_t>(n_dec) * D * sizeof(float)));
+        const int32_t* sp = slot_idx + n_dec;
+        GDN_TRY_LAUNCH(launch_conv_varlen(xp, x_dt, cu_seqlens, n_pre, total_pre, sp, conv_state,
+                                          cs_dt, conv_weight, conv_bias, w_dt, yp, GDN_BF16, D,
+                                          flags & GDN_FLAG_SILU, ef, ps));
+        GateArgs gp = ga;
+        gp.g = ga.g + static_cast<size_t>(n_dec) * HV;
+        gp.beta = ga.beta + static_cast<size_t>(n_dec) * HV;
+        const int32_t Hdk = dims->num_k_heads * dims->head_k_dim;
+        void* op = static_cast<char*>(out) + static_cast<size_t>(n_dec) * HV * dv * eso;
+        // the segment-parallel schedule that gdn_prefill_chunked would pick, when
+        // the workspace holds its segment states past the activations -- but not
+        // beside decode rows: there the CUs it would fill are the decode's, and
+        // whole runs overlapped with the decode measured faster
+        const size_t base = gdn_mixed_workspace_size(dims, n_dec, total_pre);
+        int32_t seg = ((flags & GDN_FLAG_PREFILL_SEQUENTIAL) || beside_decode)
+                          ? 0 : prefill_auto_segment_len(*dims, n_pre, total_pre);
+        if (seg > 0 && workspace_bytes - base < prefill_segmented_workspace(*dims, n_pre, total_pre, seg))
+            seg = 0;
+        if (seg > 0)
+            GDN_TRY_LAUNCH(launch_prefill_segmented(yp, yp + Hdk, yp + 2 * Hdk, GDN_BF16, gp, cu_seqlens,
+                                                    n_pre, total_pre, sp, rec_state, op, out_dt, *dims,
+                                                    D, D, scale, flags & (GDN_FLAG_QK_L2NORM), seg,
+                                                    reinterpret_cast<float*>(static_cast<char*>(workspace) + base),
+                                                    ef, ps));
+        else
+            GDN_TRY_LAUNCH(launch_prefill(yp, yp + Hdk, yp + 2 * Hdk, GDN_BF16, gp, cu_seqlens, n_pre, sp,
+                                          rec_state, op, out_dt, *dims, D, D, scale,
+                                          flags & (GDN_FLAG_QK_L2NORM), ef, ps));
+        return GDN_OK;
+    };
+    // sequences without tokens leave their state untouched: nothing to launch
+    const bool has_pre = n_pre > 0 && total_pre > 0;
+    SideStream* side = (has_pre && n_dec > 0) ? side_stream_for(s) : nullptr;
+    if (!side) {
+        if (gdn_status st = decode_part(s)) return st;
+        return has_pre ? prefill_part(s, false) : GDN_OK;
+    }
+    // The two parts touch disjoint rows, slots and workspace regions, and a CU
+    // cannot hold a workgroup of each, so the prefill runs on the library's
+    // side stream (forked from and joined back into the caller's stream by
+    // events) and takes CUs as the decode's workgroups retire.  The lock keeps
+    // another host thread's fork/join off the same events meanwhile.
+    std::lock_guard<std::mutex> lk(side->mu);
+    if (hipEventRecord(side->fork, s) != hipSuccess || hipStreamWaitEvent(side->s, side->fork, 0) != hipSuccess)
+        return GDN_ERR_LAUNCH;
+    const gdn_status sp_st = prefill_part(side->s, true);
+    const gdn_status sd_st = decode_part(s);
+    const bool joined = hipEventRecord(side->join, side->s) == hipSuccess &&
+                        hipStreamWaitEvent(s, side->join, 0) == hipSuccess;
+    if (sp_st != GDN_OK) return sp_st;
+    if (sd_st != GDN_OK) return sd_st;
+    return joined ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
 gdn_status gdn_gated_rmsnorm(const void* x, gdn_dtype x_dt, const void* z, const void* weight,

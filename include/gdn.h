@@ -375,9 +375,16 @@ size_t gdn_mixed_workspace_size(const gdn_dims* dims, int32_t n_dec, int32_t tot
  * independent of what else the step holds.  The prefill tokens go through
  * the varlen conv (SiLU per flags) into bf16 activations -- the serving path's
  * convention -- and then the chunked prefill: as one run per (sequence, value
- * head), or, when the workspace also holds the segment states, on the
- * segment-parallel schedule that gdn_prefill_chunked would pick (see
- * gdn_prefill_workspace_size).  With one run per sequence (the minimal
+ * head), or, when the step has no decode rows and the workspace also holds
+ * the segment states, on the segment-parallel schedule that
+ * gdn_prefill_chunked would pick (see gdn_prefill_workspace_size).  When the
+ * step holds both parts, the prefill part runs on a stream the library owns
+ * (one per device, created on the first such call made outside a stream
+ * capture; until then, and if it cannot be created, both parts run in order on
+ * `stream`), forked from and joined back into `stream` by events, so it
+ * overlaps the decode rows: the call is ordered on `stream` as a whole and is
+ * capturable, and the two parts share no memory because active slots are
+ * distinct across both.  With one run per sequence (the minimal
  * workspace, or GDN_FLAG_PREFILL_SEQUENTIAL) a sequence prefilled over several
  * calls equals one whole prefill bitwise when every non-final call covers a
  * multiple of 64 of its tokens (the chunk grid then coincides).

@@ -108,26 +108,32 @@ def test_mixed_step_matches_oracle():
     assert torch.all(out[1] == 0)                         # inactive decode row
 
 
-def test_mixed_step_segmented_prefill():
-    """With room for the segment states, the prefill part of a mixed step runs
-    segment-parallel (two 1024-token sequences of 16 chunks over 16 (sequence,
-    value head) runs) and still meets the prefill bar against the oracle; the
-    decode rows stay bitwise those of the minimal-workspace step, and the
-    prefill rows differ from the whole-run schedule only by rounding."""
-    n_dec, lengths = 3, [1024, 1024]
+@pytest.mark.parametrize("n_dec", [0, 3])
+def test_mixed_step_segmented_prefill(n_dec):
+    """With room for the segment states and no decode rows, the prefill part
+    of a mixed step runs segment-parallel (two 1024-token sequences of 16
+    chunks over 16 (sequence, value head) runs), meets the prefill bar against
+    the oracle and differs from the whole-run schedule only by rounding.
+    Beside decode rows it runs whole (overlapped with the decode on a second
+    stream), bitwise equal to the minimal-workspace step; the decode rows are
+    bitwise those of the minimal-workspace step either way."""
+    lengths = [1024, 1024]
     caches = _caches(12, seed=75)
     x, g, beta = _rows(n_dec + sum(lengths), seed=76)
     # slow decay on the prefill rows, so that a segment's start state still
     # matters at its end (with g ~ U[-1, 0] it fades by ~e^-32 over 64 tokens,
     # and both schedules give the same bits)
     g[n_dec:] *= 0.02
-    slots = torch.tensor([2, 0, 7, 5, 9], dtype=torch.int32)
+    slots = torch.tensor([2, 0, 7, 5, 9][3 - n_dec:], dtype=torch.int32)
     out, cs, rs = _mixed(x, g, beta, n_dec, lengths, slots, caches, segment_states=True)
     out_w, cs_w, rs_w = _mixed(x, g, beta, n_dec, lengths, slots, caches)
     o_dec, o_pre, cs_ref, rs_ref = _oracle_mixed(x, g, beta, n_dec, lengths, slots, caches)
     assert torch.equal(out[:n_dec], out_w[:n_dec])
     assert rel_err(f64(out[n_dec:]), o_pre) <= PREFILL_TOL
-    assert not torch.equal(out[n_dec:], out_w[n_dec:]), "the segment-parallel schedule did not run"
+    if n_dec == 0:
+        assert not torch.equal(out[n_dec:], out_w[n_dec:]), "the segment-parallel schedule did not run"
+    else:
+        assert torch.equal(out[n_dec:], out_w[n_dec:]), "beside decode rows the prefill runs whole"
     for i, s in enumerate(slots.tolist()):
         if s <= 0:
             continue
