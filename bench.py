@@ -604,9 +604,9 @@ def main():
         "mixed_step_whole_prefill_ms_mean": round(mean(ms_mixed_whole), 4),
         "mixed_step_note": ("gdn_mixed_step, eager: the 256 decode rows of the batch-256 "
                             "workload plus two 1024-token prefill sequences (pre-conv input); "
-                            "the workspace holds the prefill's segment states, so the prefill "
-                            "part may run segment-parallel; *_whole_prefill: the minimal "
-                            "workspace, one run per sequence"),
+                            "the prefill part runs on the library's side stream, overlapped "
+                            "with the decode rows, as whole runs; *_whole_prefill: the same "
+                            "step given the minimal workspace"),
         "decode_rec_kernel_b256_ms_mean": round(rec_ms, 5),
         "decode_rec_kernel_b256_GBps": round(rec_gbs, 2),
         "decode_rec_kernel_b256_pct_hbm_peak": round(100 * rec_gbs / HBM_PEAK_GBS, 2),
