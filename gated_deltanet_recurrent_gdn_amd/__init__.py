@@ -12,5 +12,5 @@ from ._abi import (  # noqa: F401
     gdn_mixed_workspace_size,
     gdn_prefill_chunked, gdn_prefill_chunked_gated, gdn_prefill_segmented,
     gdn_prefill_segmented_workspace_size, gdn_prefill_workspace_size, gdn_strerror,
-    load_library, make_dims,
+    load_library, make_dims, MixedStreams,
 )

@@ -99,7 +99,7 @@ def load_library(path: str = None):
     lib.gdn_mixed_workspace_size.argtypes = [D, i32, i32]
     lib.gdn_mixed_workspace_size.restype = sz
     lib.gdn_mixed_step.argtypes = [P, i32, P, P, i32, P, i32, i32, P, P, i32, P, P, i32, P, i32,
-                                   P, i32, D, f32, i32, P, sz, P, P]
+                                   P, i32, D, f32, i32, P, sz, P, P, P, P, P]
     lib.gdn_gated_rmsnorm.argtypes = [P, i32, P, P, i32, ctypes.c_int64, i32, f32, i32, P, i32, P]
     lib.gdn_strerror.argtypes = [i32]
     lib.gdn_strerror.restype = ctypes.c_char_p
@@ -360,16 +360,38 @@ def gdn_mixed_workspace_size(dims: gdn_dims, n_dec: int, total_pre: int) -> int:
                                                         int(total_pre)))
 
 
+class MixedStreams:
+    """The caller-owned second stream and fork / join events with which
+    gdn_mixed_step overlaps its prefill part with its decode rows.  Plain torch
+    objects; the library only records and waits on them.  Use one instance per
+    host thread."""
+
+    def __init__(self, device=None):
+        self.stream = torch.cuda.Stream(device=device)
+        self.fork = torch.cuda.Event()
+        self.join = torch.cuda.Event()
+        # torch creates an event's HIP handle on its first record
+        cur = torch.cuda.current_stream(device)
+        self.fork.record(cur)
+        self.join.record(cur)
+
+    def handles(self):
+        return (ctypes.c_void_p(self.stream.cuda_stream), ctypes.c_void_p(self.fork.cuda_event),
+                ctypes.c_void_p(self.join.cuda_event))
+
+
 def gdn_mixed_step(x, g, beta, n_dec, cu_seqlens, slot_idx, conv_state, conv_weight, rec_state,
                    out, dims: gdn_dims, scale, conv_bias=None, flags=DEFAULT_DECODE_FLAGS,
-                   workspace=None, err_flag=None, stream=None):
+                   workspace=None, err_flag=None, stream=None, streams: MixedStreams = None):
     """One step with ``n_dec`` decode rows followed by prefill sequences
     (gdn.h: gdn_mixed_step).  ``x`` [n_dec + T, D] pre-conv, ``cu_seqlens``
     [n_pre + 1] over the T prefill tokens (or None), ``slot_idx`` [n_dec + n_pre],
     ``out`` [n_dec + T, HV, dv].  Caches updated in place.  Without a
     ``workspace`` the minimal one is allocated (whole prefill runs); a workspace
     of gdn_mixed_workspace_size + gdn_prefill_workspace_size bytes lets the
-    prefill part take the segment-parallel schedule."""
+    prefill part of a step without decode rows take the segment-parallel
+    schedule.  ``streams`` (a MixedStreams) overlaps the prefill part with the
+    decode rows on its second stream; without it both run in order."""
     lib = load_library()
     rows = x.shape[0]
     HV, dk, dv = dims.num_v_heads, dims.head_k_dim, dims.head_v_dim
@@ -399,7 +421,7 @@ def gdn_mixed_step(x, g, beta, n_dec, cu_seqlens, slot_idx, conv_state, conv_wei
         _p(conv_state), _dt(conv_state), _p(conv_weight), _p(conv_bias), _dt(conv_weight),
         _p(rec_state), ns, _p(out), _dt(out), ctypes.byref(dims), float(scale), flags,
         _p(workspace), workspace.numel() * workspace.element_size(), _p(err_flag),
-        _stream(stream)))
+        _stream(stream), *(streams.handles() if streams is not None else (None, None, None))))
     return out
 
 

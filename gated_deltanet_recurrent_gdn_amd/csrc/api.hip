@@ -1,11 +1,10 @@
 // api.hip -- the extern "C" entry points of libgdn.so (declared in gdn.h).
 //
 // Host-side only: validate what can be checked without reading device memory,
-// then enqueue the kernels on the caller's stream and return.  No allocation,
-// no synchronisation, no global mutable state.
+// then enqueue the kernels on the caller's stream(s) and return.  No
+// allocation, no synchronisation, no global mutable state: every stream and
+// event a call uses is the caller's.
 #include <hip/hip_runtime.h>
-
-#include <mutex>
 
 #include "gdn.h"
 #include "gdn_internal.hpp"
@@ -70,7 +69,7 @@ gdn_status gdn_conv_update(const void* x, gdn_dtype x_dt, const int32_t* cu_seql
                            void* conv_state, gdn_dtype cs_dt, int32_t num_slots,
                            const void* weight, const void* bias, gdn_dtype w_dt, void* out,
                            gdn_dtype out_dt, int32_t dim, int32_t width, int32_t flags,
-                           int32_t* err_flag, void* stream) {
+                           int32_t* err_flag, hipStream_t stream) {
     if (gdn_status st = check_flags(flags, GDN_FLAG_SILU | GDN_FLAG_VALIDATE, err_flag)) return st;
     if (n_seqs < 0 || total_tokens < 0 || num_slots < 1 || dim <= 0 || width != 4)
         return GDN_ERR_DIMS;
@@ -85,7 +84,7 @@ gdn_status gdn_conv_update(const void* x, gdn_dtype x_dt, const int32_t* cu_seql
         (!aligned16(x) || !aligned16(out) || !aligned16(conv_state) || !aligned16(weight) ||
          (bias && !aligned16(bias))))
         return GDN_ERR_ALIGN;
-    auto s = static_cast<hipStream_t>(stream);
+    const hipStream_t s = stream;
     if (flags & GDN_FLAG_VALIDATE)
         GDN_TRY_LAUNCH(launch_validate(slot_idx, n_seqs, num_slots, cu_seqlens, n_seqs, total_tokens,
                                        err_flag, s));
@@ -160,7 +159,7 @@ gdn_status decode_step_impl(const void* mixed_qkv, gdn_dtype x_dt, const float* 
                             gdn_dtype w_dt, float* rec_state, int32_t num_slots, void* out,
                             gdn_dtype out_dt, const gdn_dims* dims, float scale, int32_t flags,
                             void* workspace, size_t workspace_bytes, int32_t* err_flag,
-                            void* stream) {
+                            hipStream_t stream) {
     if (gdn_status st = check_flags(flags, KNOWN_FLAGS | GDN_FLAG_STEP_FUSED | GDN_FLAG_STEP_SPLIT,
                                     err_flag))
         return st;
@@ -182,7 +181,7 @@ gdn_status decode_step_impl(const void* mixed_qkv, gdn_dtype x_dt, const float* 
             return GDN_ERR_ALIGN;
         if (workspace_bytes < gdn_decode_workspace_size(dims, batch)) return GDN_ERR_WORKSPACE;
     }
-    auto s = static_cast<hipStream_t>(stream);
+    const hipStream_t s = stream;
     if (flags & GDN_FLAG_VALIDATE)
         GDN_TRY_LAUNCH(launch_validate(slot_idx, batch, num_slots, nullptr, 0, 0, err_flag, s));
     const int32_t* ef = (flags & GDN_FLAG_VALIDATE) ? err_flag : nullptr;
@@ -197,7 +196,7 @@ gdn_status prefill_impl(const void* q, const void* k, const void* v, gdn_dtype i
                         const int32_t* slot_idx, float* rec_state, int32_t num_slots, void* out,
                         gdn_dtype out_dt, const gdn_dims* dims, float scale, int32_t flags,
                         int32_t seg_len, void* workspace, size_t workspace_bytes,
-                        int32_t* err_flag, void* stream) {
+                        int32_t* err_flag, hipStream_t stream) {
     if (gdn_status st = check_flags(flags, GDN_FLAG_QK_L2NORM | GDN_FLAG_VALIDATE |
                                                GDN_FLAG_PREFILL_NS3 | GDN_FLAG_PREFILL_NS4 |
                                                GDN_FLAG_PREFILL_SEQUENTIAL,
@@ -235,7 +234,7 @@ gdn_status prefill_impl(const void* q, const void* k, const void* v, gdn_dtype i
     } else {
         return GDN_ERR_DIMS;
     }
-    auto s = static_cast<hipStream_t>(stream);
+    const hipStream_t s = stream;
     if (flags & GDN_FLAG_VALIDATE)
         GDN_TRY_LAUNCH(launch_validate(slot_idx, n_seqs, num_slots, cu_seqlens, n_seqs, total_tokens,
                                        err_flag, s));
@@ -263,7 +262,7 @@ gdn_status gdn_decode_step(const void* mixed_qkv, gdn_dtype x_dt, const float* g
                            const void* conv_bias, gdn_dtype w_dt, float* rec_state,
                            int32_t num_slots, void* out, gdn_dtype out_dt, const gdn_dims* dims,
                            float scale, int32_t flags, void* workspace, size_t workspace_bytes,
-                           int32_t* err_flag, void* stream) {
+                           int32_t* err_flag, hipStream_t stream) {
     return decode_step_impl(mixed_qkv, x_dt, g, beta, nullptr, slot_idx, batch, conv_state,
                             cs_dt, conv_weight, conv_bias, w_dt, rec_state, num_slots, out,
                             out_dt, dims, scale, flags, workspace, workspace_bytes, err_flag,
@@ -277,7 +276,7 @@ gdn_status gdn_decode_step_gated(const void* mixed_qkv, gdn_dtype x_dt,
                                  float* rec_state, int32_t num_slots, void* out, gdn_dtype out_dt,
                                  const gdn_dims* dims, float scale, int32_t flags,
                                  void* workspace, size_t workspace_bytes, int32_t* err_flag,
-                                 void* stream) {
+                                 hipStream_t stream) {
     if (!gate) return GDN_ERR_NULL;
     return decode_step_impl(mixed_qkv, x_dt, nullptr, nullptr, gate, slot_idx, batch,
                             conv_state, cs_dt, conv_weight, conv_bias, w_dt, rec_state,
@@ -289,7 +288,7 @@ gdn_status gdn_decode_recurrent(const void* qkv, gdn_dtype qkv_dt, const float* 
                                 const float* beta, const int32_t* slot_idx, int32_t batch,
                                 float* rec_state, int32_t num_slots, void* out, gdn_dtype out_dt,
                                 const gdn_dims* dims, float scale, int32_t flags,
-                                int32_t* err_flag, void* stream) {
+                                int32_t* err_flag, hipStream_t stream) {
     if (gdn_status st = check_flags(flags, GDN_FLAG_QK_L2NORM | GDN_FLAG_VALIDATE, err_flag))
         return st;
     if (gdn_status st = check_dims(dims)) return st;
@@ -302,7 +301,7 @@ gdn_status gdn_decode_recurrent(const void* qkv, gdn_dtype qkv_dt, const float* 
         if (!qkv || !slot_idx || !rec_state || !out) return GDN_ERR_NULL;
         if (!aligned16(rec_state) || !aligned16(qkv)) return GDN_ERR_ALIGN;
     }
-    auto s = static_cast<hipStream_t>(stream);
+    const hipStream_t s = stream;
     if (flags & GDN_FLAG_VALIDATE)
         GDN_TRY_LAUNCH(launch_validate(slot_idx, batch, num_slots, nullptr, 0, 0, err_flag, s));
     const int32_t* ef = (flags & GDN_FLAG_VALIDATE) ? err_flag : nullptr;
@@ -334,7 +333,7 @@ gdn_status gdn_prefill_segmented(const void* q, const void* k, const void* v, gd
                                  const int32_t* slot_idx, float* rec_state, int32_t num_slots,
                                  void* out, gdn_dtype out_dt, const gdn_dims* dims, float scale,
                                  int32_t flags, int32_t seg_len, void* workspace,
-                                 size_t workspace_bytes, int32_t* err_flag, void* stream) {
+                                 size_t workspace_bytes, int32_t* err_flag, hipStream_t stream) {
     if (seg_len <= 0) return GDN_ERR_DIMS;
     if (gate && (g || beta)) return GDN_ERR_FLAGS;
     return prefill_impl(q, k, v, in_dt, gate ? nullptr : g, gate ? nullptr : beta, gate,
@@ -348,7 +347,7 @@ gdn_status gdn_prefill_chunked(const void* q, const void* k, const void* v, gdn_
                                int32_t n_seqs, int32_t total_tokens, const int32_t* slot_idx,
                                float* rec_state, int32_t num_slots, void* out, gdn_dtype out_dt,
                                const gdn_dims* dims, float scale, int32_t flags, void* workspace,
-                               size_t workspace_bytes, int32_t* err_flag, void* stream) {
+                               size_t workspace_bytes, int32_t* err_flag, hipStream_t stream) {
     return prefill_impl(q, k, v, in_dt, g, beta, nullptr, cu_seqlens, n_seqs, total_tokens,
                         slot_idx, rec_state, num_slots, out, out_dt, dims, scale, flags, -1,
                         workspace, workspace_bytes, err_flag, stream);
@@ -361,7 +360,7 @@ gdn_status gdn_prefill_chunked_gated(const void* q, const void* k, const void* v
                                      float* rec_state, int32_t num_slots, void* out,
                                      gdn_dtype out_dt, const gdn_dims* dims, float scale,
                                      int32_t flags, void* workspace, size_t workspace_bytes,
-                                     int32_t* err_flag, void* stream) {
+                                     int32_t* err_flag, hipStream_t stream) {
     if (!gate) return GDN_ERR_NULL;
     return prefill_impl(q, k, v, in_dt, nullptr, nullptr, gate, cu_seqlens, n_seqs,
                         total_tokens, slot_idx, rec_state, num_slots, out, out_dt, dims, scale,
@@ -375,36 +374,6 @@ size_t gdn_mixed_workspace_size(const gdn_dims* dims, int32_t n_dec, int32_t tot
            round256(static_cast<size_t>(total_pre) * D * sizeof(uint16_t));
 }
 
-// Side stream of the mixed step, one per device, created on first use outside
-// a stream capture and kept until the process ends (default priority).
-struct SideStream {
-    hipStream_t s = nullptr;
-    hipEvent_t fork = nullptr, join = nullptr;
-    std::mutex mu;
-};
-static SideStream* side_stream_for(hipStream_t caller) {
-    static std::mutex tab_mu;
-    static SideStream* tab[64] = {};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-    std::lock_guard<std::mutex> lk(tab_mu);
-    if (tab[dev]) return tab[dev];
-    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(caller, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone) return nullptr;
-    auto* p = new SideStream();
-    if (hipStreamCreateWithFlags(&p->s, hipStreamNonBlocking) != hipSuccess ||
-        hipEventCreateWithFlags(&p->fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&p->join, hipEventDisableTiming) != hipSuccess) {
-        if (p->join) (void)hipEventDestroy(p->join);
-        if (p->fork) (void)hipEventDestroy(p->fork);
-        if (p->s) (void)hipStreamDestroy(p->s);
-        delete p;
-        return nullptr;
-    }
-    tab[dev] = p;
-    return p;
-}
-
 gdn_status gdn_mixed_step(const void* x, gdn_dtype x_dt, const float* g, const float* beta,
                           int32_t n_dec, const int32_t* cu_seqlens, int32_t n_pre,
                           int32_t total_pre, const int32_t* slot_idx, void* conv_state,
@@ -412,7 +381,8 @@ gdn_status gdn_mixed_step(const void* x, gdn_dtype x_dt, const float* g, const f
                           gdn_dtype w_dt, float* rec_state, int32_t num_slots, void* out,
                           gdn_dtype out_dt, const gdn_dims* dims, float scale, int32_t flags,
                           void* workspace, size_t workspace_bytes, int32_t* err_flag,
-                          void* stream) {
+                          hipStream_t stream, hipStream_t prefill_stream, hipEvent_t fork_event,
+                          hipEvent_t join_event) {
     if (gdn_status st = check_flags(flags, KNOWN_FLAGS | GDN_FLAG_STEP_FUSED | GDN_FLAG_STEP_SPLIT |
                                                GDN_FLAG_PREFILL_SEQUENTIAL,
                                     err_flag))
@@ -441,7 +411,8 @@ gdn_status gdn_mixed_step(const void* x, gdn_dtype x_dt, const float* g, const f
         return GDN_ERR_ALIGN;
     if (rows > 0 && workspace_bytes < gdn_mixed_workspace_size(dims, n_dec, total_pre))
         return GDN_ERR_WORKSPACE;
-    auto s = static_cast<hipStream_t>(stream);
+    if (prefill_stream && (!fork_event || !join_event)) return GDN_ERR_NULL;
+    const hipStream_t s = stream;
     if (flags & GDN_FLAG_VALIDATE)
         GDN_TRY_LAUNCH(launch_validate(slot_idx, n_dec + n_pre, num_slots, n_pre > 0 ? cu_seqlens : nullptr,
                                        n_pre, total_pre, err_flag, s));
@@ -474,7 +445,8 @@ gdn_status gdn_mixed_step(const void* x, gdn_dtype x_dt, const float* g, const f
         // the segment-parallel schedule that gdn_prefill_chunked would pick, when
         // the workspace holds its segment states past the activations -- but not
         // beside decode rows: there the CUs it would fill are the decode's, and
-        // whole runs overlapped with the decode measured faster
+        // whole runs overlapped with the decode measured faster.  The choice
+        // depends on the call's arguments only (never on the streams given).
         const size_t base = gdn_mixed_workspace_size(dims, n_dec, total_pre);
         int32_t seg = ((flags & GDN_FLAG_PREFILL_SEQUENTIAL) || beside_decode)
                           ? 0 : prefill_auto_segment_len(*dims, n_pre, total_pre);
@@ -494,23 +466,24 @@ gdn_status gdn_mixed_step(const void* x, gdn_dtype x_dt, const float* g, const f
     };
     // sequences without tokens leave their state untouched: nothing to launch
     const bool has_pre = n_pre > 0 && total_pre > 0;
-    SideStream* side = (has_pre && n_dec > 0) ? side_stream_for(s) : nullptr;
-    if (!side) {
+    const bool beside = has_pre && n_dec > 0;
+    if (!beside || !prefill_stream) {
         if (gdn_status st = decode_part(s)) return st;
-        return has_pre ? prefill_part(s, false) : GDN_OK;
+        return has_pre ? prefill_part(s, beside) : GDN_OK;
     }
     // The two parts touch disjoint rows, slots and workspace regions, and a CU
-    // cannot hold a workgroup of each, so the prefill runs on the library's
-    // side stream (forked from and joined back into the caller's stream by
-    // events) and takes CUs as the decode's workgroups retire.  The lock keeps
-    // another host thread's fork/join off the same events meanwhile.
-    std::lock_guard<std::mutex> lk(side->mu);
-    if (hipEventRecord(side->fork, s) != hipSuccess || hipStreamWaitEvent(side->s, side->fork, 0) != hipSuccess)
+    // cannot hold a workgroup of each, so the prefill runs on the caller's
+    // prefill_stream (forked from `stream` after the validation and joined
+    // back into it by the caller's events) and takes CUs as the decode's
+    // workgroups retire.  The join is enqueued even after a failed launch, so
+    // `stream` stays ordered after everything this call enqueued.
+    if (hipEventRecord(fork_event, s) != hipSuccess ||
+        hipStreamWaitEvent(prefill_stream, fork_event, 0) != hipSuccess)
         return GDN_ERR_LAUNCH;
-    const gdn_status sp_st = prefill_part(side->s, true);
-    const gdn_status sd_st = decode_part(s);
-    const bool joined = hipEventRecord(side->join, side->s) == hipSuccess &&
-                        hipStreamWaitEvent(s, side->join, 0) == hipSuccess;
+    const gdn_status sp_st = prefill_part(prefill_stream, true);
+    const gdn_status sd_st = sp_st == GDN_OK ? decode_part(s) : GDN_OK;
+    const bool joined = hipEventRecord(join_event, prefill_stream) == hipSuccess &&
+                        hipStreamWaitEvent(s, join_event, 0) == hipSuccess;
     if (sp_st != GDN_OK) return sp_st;
     if (sd_st != GDN_OK) return sd_st;
     return joined ? GDN_OK : GDN_ERR_LAUNCH;
@@ -518,7 +491,7 @@ gdn_status gdn_mixed_step(const void* x, gdn_dtype x_dt, const float* g, const f
 
 gdn_status gdn_gated_rmsnorm(const void* x, gdn_dtype x_dt, const void* z, const void* weight,
                              gdn_dtype w_dt, int64_t rows, int32_t dim, float eps, int32_t flags,
-                             void* out, gdn_dtype out_dt, void* stream) {
+                             void* out, gdn_dtype out_dt, hipStream_t stream) {
     if (flags & ~(GDN_NORM_GATE_SIGMOID | GDN_NORM_ZERO_CENTRED)) return GDN_ERR_FLAGS;
     if (rows < 0 || dim < 4 || dim > 1024 || dim % 4 != 0 || !(eps >= 0.0f)) return GDN_ERR_DIMS;
     if (rows > (static_cast<int64_t>(1) << 32)) return GDN_ERR_DIMS;
@@ -527,7 +500,7 @@ gdn_status gdn_gated_rmsnorm(const void* x, gdn_dtype x_dt, const void* z, const
     if (!aligned16(x) || !aligned16(weight) || !aligned16(out) || (z && !aligned16(z)))
         return GDN_ERR_ALIGN;
     GDN_TRY_LAUNCH(launch_gated_rmsnorm(x, x_dt, z, weight, w_dt, out, out_dt, rows, dim, eps,
-                                        flags, static_cast<hipStream_t>(stream)));
+                                        flags, stream));
     return GDN_OK;
 }
 

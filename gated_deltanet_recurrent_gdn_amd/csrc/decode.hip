@@ -21,7 +21,6 @@
 // fixed-order fma chain followed by the 8-lane DPP butterfly `sum8`: the order
 // depends on nothing but dk, so results are batch-invariant and replay
 // bitwise.  No LDS is used at all.
-#include <atomic>
 
 #include "conv_io.hpp"
 #include "gate.hpp"
@@ -431,18 +430,13 @@ __global__ __launch_bounds__(GDN_STEP_NT) void decode_step_kernel(
     }
 }
 
-// Compute units of the current device, queried once per device (a relaxed
-// atomic cache: concurrent first calls store the same value).
+// Compute units of the current device, asked of the runtime on every call
+// (no cache is kept).
 int cu_count() {
-    static std::atomic<int> cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    int n = cache[dev].load(std::memory_order_relaxed);
-    if (n == 0) {
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            n = 256;
-        cache[dev].store(n, std::memory_order_relaxed);
-    }
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        return 256;
     return n;
 }
 

@@ -78,7 +78,7 @@ hipError_t launch_decode_step_fused(const void* x, gdn_dtype x_dt, const GateArg
                                     gdn_dtype out_dt, const gdn_dims& dims, float scale,
                                     int32_t flags, const int32_t* err_flag, hipStream_t stream);
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (asked of the runtime each call).
 int cu_count();
 
 // Chunked prefill: one workgroup per (sequence, value head).

@@ -32,8 +32,11 @@
  * Conventions common to every call
  *   - Every tensor is caller-owned DEVICE memory, dense, row-major (C order),
  *     at least 16-byte aligned.  The library never allocates, frees or
- *     synchronises; each call only enqueues kernels on `stream` (a
- *     hipStream_t; NULL = the default stream) and returns.
+ *     synchronises and holds no state between calls; each call only enqueues
+ *     kernels (and, in gdn_mixed_step, event records and waits) on the
+ *     caller's `stream` (NULL = the default stream) and streams, and returns.
+ *     Calls on different streams that touch disjoint slots and buffers are
+ *     independent.
  *   - Caches are updated in place.  Outputs must not alias any input.  Within
  *     one call each active slot may appear at most once ([P1] "State ABI").
  *   - Slot indices: s <= 0 marks an inactive (padded) row: its outputs are
@@ -41,7 +44,9 @@
  *     reserved null block and is never addressed ([P1] "State ABI"; [P2]).
  *   - Synchronous status (gdn_status): what the host can check without reading
  *     device memory -- null pointers, dims, dtypes, alignment, workspace size.
- *     On any status other than GDN_OK nothing was enqueued.
+ *     Those argument errors are found before anything is enqueued.
+ *     GDN_ERR_LAUNCH (the runtime refused a launch) can leave the kernels the
+ *     call launched before that one enqueued.
  *   - Device-side validation: with GDN_FLAG_VALIDATE set, a first kernel
  *     checks the slot indices (and cu_seqlens) and WRITES *err_flag (0 when
  *     clean, else GDN_EFLAG_* bits).  When any bit is set every later kernel
@@ -59,6 +64,14 @@
 
 #include <stddef.h>
 #include <stdint.h>
+
+/* HIP stream and event handles: the runtime's own opaque pointer types (the
+   same declarations as hip_runtime_api.h, repeated only when that header is
+   not already in scope). */
+#ifndef HIP_INCLUDE_HIP_HIP_RUNTIME_API_H
+typedef struct ihipStream_t* hipStream_t;
+typedef struct ihipEvent_t* hipEvent_t;
+#endif
 
 #ifdef __cplusplus
 extern "C" {
@@ -160,7 +173,7 @@ gdn_status gdn_conv_update(const void* x, gdn_dtype x_dt,
                            const void* weight, const void* bias, gdn_dtype w_dt,
                            void* out, gdn_dtype out_dt,
                            int32_t dim, int32_t width, int32_t flags,
-                           int32_t* err_flag, void* stream);
+                           int32_t* err_flag, hipStream_t stream);
 
 /*
  * gdn_decode_workspace_size -- bytes of device workspace gdn_decode_step needs
@@ -207,7 +220,7 @@ gdn_status gdn_decode_step(const void* mixed_qkv, gdn_dtype x_dt,
                            void* out, gdn_dtype out_dt,
                            const gdn_dims* dims, float scale, int32_t flags,
                            void* workspace, size_t workspace_bytes,
-                           int32_t* err_flag, void* stream);
+                           int32_t* err_flag, hipStream_t stream);
 
 /*
  * gdn_decode_recurrent -- the recurrent half of the decode step alone, on
@@ -229,7 +242,7 @@ gdn_status gdn_decode_recurrent(const void* qkv, gdn_dtype qkv_dt,
                                 float* rec_state, int32_t num_slots,
                                 void* out, gdn_dtype out_dt,
                                 const gdn_dims* dims, float scale, int32_t flags,
-                                int32_t* err_flag, void* stream);
+                                int32_t* err_flag, hipStream_t stream);
 
 /*
  * gdn_prefill_workspace_size -- bytes of device workspace with which
@@ -282,7 +295,7 @@ gdn_status gdn_prefill_chunked(const void* q, const void* k, const void* v, gdn_
                                void* out, gdn_dtype out_dt,
                                const gdn_dims* dims, float scale, int32_t flags,
                                void* workspace, size_t workspace_bytes,
-                               int32_t* err_flag, void* stream);
+                               int32_t* err_flag, hipStream_t stream);
 
 /*
  * gdn_prefill_segmented -- gdn_prefill_chunked with the sequences cut into
@@ -322,7 +335,7 @@ gdn_status gdn_prefill_segmented(const void* q, const void* k, const void* v, gd
                                  void* out, gdn_dtype out_dt,
                                  const gdn_dims* dims, float scale, int32_t flags,
                                  int32_t seg_len, void* workspace, size_t workspace_bytes,
-                                 int32_t* err_flag, void* stream);
+                                 int32_t* err_flag, hipStream_t stream);
 
 /*
  * gdn_decode_step_gated / gdn_prefill_chunked_gated -- gdn_decode_step and
@@ -342,7 +355,7 @@ gdn_status gdn_decode_step_gated(const void* mixed_qkv, gdn_dtype x_dt,
                                  void* out, gdn_dtype out_dt,
                                  const gdn_dims* dims, float scale, int32_t flags,
                                  void* workspace, size_t workspace_bytes,
-                                 int32_t* err_flag, void* stream);
+                                 int32_t* err_flag, hipStream_t stream);
 
 gdn_status gdn_prefill_chunked_gated(const void* q, const void* k, const void* v,
                                      gdn_dtype in_dt, const gdn_gate_inputs* gate,
@@ -352,7 +365,7 @@ gdn_status gdn_prefill_chunked_gated(const void* q, const void* k, const void* v
                                      void* out, gdn_dtype out_dt,
                                      const gdn_dims* dims, float scale, int32_t flags,
                                      void* workspace, size_t workspace_bytes,
-                                     int32_t* err_flag, void* stream);
+                                     int32_t* err_flag, hipStream_t stream);
 
 /*
  * gdn_mixed_workspace_size -- bytes of device workspace gdn_mixed_step needs:
@@ -377,17 +390,27 @@ size_t gdn_mixed_workspace_size(const gdn_dims* dims, int32_t n_dec, int32_t tot
  * convention -- and then the chunked prefill: as one run per (sequence, value
  * head), or, when the step has no decode rows and the workspace also holds
  * the segment states, on the segment-parallel schedule that
- * gdn_prefill_chunked would pick (see gdn_prefill_workspace_size).  When the
- * step holds both parts, the prefill part runs on a stream the library owns
- * (one per device, created on the first such call made outside a stream
- * capture; until then, and if it cannot be created, both parts run in order on
- * `stream`), forked from and joined back into `stream` by events, so it
- * overlaps the decode rows: the call is ordered on `stream` as a whole and is
- * capturable, and the two parts share no memory because active slots are
- * distinct across both.  With one run per sequence (the minimal
- * workspace, or GDN_FLAG_PREFILL_SEQUENTIAL) a sequence prefilled over several
- * calls equals one whole prefill bitwise when every non-final call covers a
+ * gdn_prefill_chunked would pick (see gdn_prefill_workspace_size).  The
+ * schedule depends on these arguments only, never on the streams.
+ * With one run per sequence (the minimal workspace, decode rows in the step,
+ * or GDN_FLAG_PREFILL_SEQUENTIAL) a sequence prefilled over several calls
+ * equals one whole prefill bitwise when every non-final call covers a
  * multiple of 64 of its tokens (the chunk grid then coincides).
+ *
+ * Streams.  With prefill_stream NULL both parts run in order on `stream`
+ * (fork_event and join_event are ignored).  With a prefill_stream and a step
+ * holding both parts, the call records fork_event on `stream` after the
+ * optional validation, makes prefill_stream wait for it, enqueues the prefill
+ * part there and the decode part on `stream`, records join_event on
+ * prefill_stream and makes `stream` wait for it: the parts overlap on the GPU
+ * (they share no memory, active slots being distinct across both), and the
+ * call is still ordered on `stream` as a whole, under stream capture too (the
+ * fork pulls prefill_stream into the capture and the join ends it there).
+ * Results are bitwise the same with or without a prefill_stream.  The streams
+ * and events belong to the caller (events created with
+ * hipEventDisableTiming are enough); one event pair must not be recorded by
+ * two calls concurrently from different host threads.
+ *
  *
  *   x            [n_dec + total_pre, D], x_dt: the n_dec decode rows, then the
  *                prefill tokens (pre-conv mixed q | k | v)
@@ -412,6 +435,12 @@ size_t gdn_mixed_workspace_size(const gdn_dims* dims, int32_t n_dec, int32_t tot
  *                gdn_prefill_workspace_size(dims, n_pre, total_pre) bytes the
  *                prefill part may take the segment-parallel schedule (its
  *                segment states live past the activations)
+ *   stream       the step's stream: validation, decode part and, without a
+ *                prefill_stream, the prefill part
+ *   prefill_stream, fork_event, join_event
+ *                the caller's second stream and two events for the
+ *                overlapped schedule above, or NULL, NULL, NULL
+ *                (GDN_ERR_NULL if prefill_stream is given without both events)
  * The prefill part needs dk == dv <= 128 (GDN_ERR_DIMS otherwise, when
  * n_pre > 0).
  */
@@ -426,7 +455,9 @@ gdn_status gdn_mixed_step(const void* x, gdn_dtype x_dt,
                           void* out, gdn_dtype out_dt,
                           const gdn_dims* dims, float scale, int32_t flags,
                           void* workspace, size_t workspace_bytes,
-                          int32_t* err_flag, void* stream);
+                          int32_t* err_flag, hipStream_t stream,
+                          hipStream_t prefill_stream, hipEvent_t fork_event,
+                          hipEvent_t join_event);
 
 /*
  * gdn_gated_rmsnorm -- the gated RMSNorm that follows the GDN core in the
@@ -448,7 +479,7 @@ gdn_status gdn_mixed_step(const void* x, gdn_dtype x_dt,
 gdn_status gdn_gated_rmsnorm(const void* x, gdn_dtype x_dt, const void* z,
                              const void* weight, gdn_dtype w_dt,
                              int64_t rows, int32_t dim, float eps, int32_t flags,
-                             void* out, gdn_dtype out_dt, void* stream);
+                             void* out, gdn_dtype out_dt, hipStream_t stream);
 
 /* gdn_strerror -- static, NUL-terminated description of a status code. */
 const char* gdn_strerror(gdn_status s);

@@ -172,10 +172,10 @@ def test_gated_calls_empty_is_ok(lib):
 
 
 def _mixed(lib, dims=None, n_dec=2, cu=FAKE, n_pre=1, total=64, flags=3, ws=FAKE,
-           ws_bytes=1 << 30, err=None):
+           ws_bytes=1 << 30, err=None, side=(None, None, None)):
     return lib.gdn_mixed_step(FAKE, 1, FAKE, FAKE, n_dec, cu, n_pre, total, FAKE, FAKE, 1, FAKE,
                               None, 1, FAKE, 8, FAKE, 0, dims or _dims(), 0.1, flags, ws,
-                              ws_bytes, err, None)
+                              ws_bytes, err, None, *side)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -188,6 +188,8 @@ def _mixed(lib, dims=None, n_dec=2, cu=FAKE, n_pre=1, total=64, flags=3, ws=FAKE
     (dict(cu=None), ERR_NULL),
     (dict(ws=None), ERR_NULL),
     (dict(ws_bytes=16), ERR_WS),
+    (dict(side=(FAKE, None, FAKE)), ERR_NULL),         # a prefill stream needs both events
+    (dict(side=(FAKE, FAKE, None)), ERR_NULL),
 ])
 def test_mixed_step_rejects(lib, kw, code):
     assert _mixed(lib, **kw) == code

@@ -47,9 +47,10 @@ def _rows(n, seed):
 
 
 def _mixed(x, g, beta, n_dec, lengths, slots, caches, flags=gdn.DEFAULT_DECODE_FLAGS,
-           segment_states=False):
+           segment_states=False, streams=None):
     """Run one mixed step on GPU copies of the caches; returns (out, cs, rs).
-    segment_states: give the step room for the prefill's segment states."""
+    segment_states: give the step room for the prefill's segment states;
+    streams: a MixedStreams for the overlapped two-stream schedule."""
     cs, w, b, rs = (c.cuda() for c in caches)
     cs, rs = cs.clone(), rs.clone()
     cu = gi.cu_from_lengths(lengths).cuda() if lengths else None
@@ -63,7 +64,7 @@ def _mixed(x, g, beta, n_dec, lengths, slots, caches, flags=gdn.DEFAULT_DECODE_F
         ws = torch.empty(gdn.gdn_mixed_workspace_size(dims, n_dec, T) + extra,
                          dtype=torch.uint8, device="cuda")
     gdn.gdn_mixed_step(x.cuda(), g.cuda(), beta.cuda(), n_dec, cu, slots.cuda(), cs, w, rs, out,
-                       dims, SCALE, conv_bias=b, flags=flags, workspace=ws)
+                       dims, SCALE, conv_bias=b, flags=flags, workspace=ws, streams=streams)
     torch.cuda.synchronize()
     return out, cs, rs
 
@@ -86,14 +87,16 @@ def _oracle_mixed(x, g, beta, n_dec, lengths, slots, caches):
     return o_dec, o_pre, cs, rs
 
 
-def test_mixed_step_matches_oracle():
+@pytest.mark.parametrize("two_streams", [False, True])
+def test_mixed_step_matches_oracle(two_streams):
     n_dec, lengths = 5, [1, 70, 0, 130, 64]
     caches = _caches(16, seed=70)
     x, g, beta = _rows(n_dec + sum(lengths), seed=71)
     slots = torch.tensor([3, 0, 9, 12, 1, 5, 7, 2, -1, 14], dtype=torch.int32)
     slots[8 + 0] = 11          # prefill seq 3 (130 tokens) active
     slots[9] = 0               # prefill seq 4 inactive (64 tokens): zero output
-    out, cs, rs = _mixed(x, g, beta, n_dec, lengths, slots, caches)
+    out, cs, rs = _mixed(x, g, beta, n_dec, lengths, slots, caches,
+                         streams=gdn.MixedStreams() if two_streams else None)
     o_dec, o_pre, cs_ref, rs_ref = _oracle_mixed(x, g, beta, n_dec, lengths, slots, caches)
     assert rel_err(f64(out[:n_dec]), o_dec) <= DECODE_TOL
     assert rel_err(f64(out[n_dec:]), o_pre) <= PREFILL_TOL
@@ -108,15 +111,15 @@ def test_mixed_step_matches_oracle():
     assert torch.all(out[1] == 0)                         # inactive decode row
 
 
-@pytest.mark.parametrize("n_dec", [0, 3])
-def test_mixed_step_segmented_prefill(n_dec):
+@pytest.mark.parametrize("n_dec,two_streams", [(0, False), (3, False), (3, True)])
+def test_mixed_step_segmented_prefill(n_dec, two_streams):
     """With room for the segment states and no decode rows, the prefill part
     of a mixed step runs segment-parallel (two 1024-token sequences of 16
     chunks over 16 (sequence, value head) runs), meets the prefill bar against
     the oracle and differs from the whole-run schedule only by rounding.
-    Beside decode rows it runs whole (overlapped with the decode on a second
-    stream), bitwise equal to the minimal-workspace step; the decode rows are
-    bitwise those of the minimal-workspace step either way."""
+    Beside decode rows it runs whole whatever the workspace and the streams,
+    bitwise equal to the minimal-workspace one-stream step; the decode rows
+    are bitwise those of the minimal-workspace step either way."""
     lengths = [1024, 1024]
     caches = _caches(12, seed=75)
     x, g, beta = _rows(n_dec + sum(lengths), seed=76)
@@ -125,7 +128,8 @@ def test_mixed_step_segmented_prefill(n_dec):
     # and both schedules give the same bits)
     g[n_dec:] *= 0.02
     slots = torch.tensor([2, 0, 7, 5, 9][3 - n_dec:], dtype=torch.int32)
-    out, cs, rs = _mixed(x, g, beta, n_dec, lengths, slots, caches, segment_states=True)
+    out, cs, rs = _mixed(x, g, beta, n_dec, lengths, slots, caches, segment_states=True,
+                         streams=gdn.MixedStreams() if two_streams else None)
     out_w, cs_w, rs_w = _mixed(x, g, beta, n_dec, lengths, slots, caches)
     o_dec, o_pre, cs_ref, rs_ref = _oracle_mixed(x, g, beta, n_dec, lengths, slots, caches)
     assert torch.equal(out[:n_dec], out_w[:n_dec])
@@ -242,17 +246,17 @@ def test_mixed_validation_covers_both_parts():
     assert torch.equal(cs, cs0) and torch.equal(rs, rs0)
 
 
-def test_mixed_step_graph_replay_matches_eager():
-    """A captured HIP graph of a mixed step on the segment-parallel schedule
-    (varlen conv + roll, both segment passes and the scan, the decode rows)
-    reproduces three consecutive eager steps bitwise on every replay, with eager
-    work between replays: every call only enqueues kernels."""
-    n_dec, lengths = 5, [300, 700]
+def _graph_vs_eager(n_dec, lengths, streams, capture_first):
+    """Capture one mixed step in a HIP graph and compare three replays with
+    three consecutive eager steps, bitwise, with eager work between replays.
+    capture_first: the capture is this process's first mixed step with these
+    arguments (the schedule must not depend on what ran before)."""
     dims = gdn.make_dims(H, HV, DK, DK, 4)
     T = sum(lengths)
     caches = [c.cuda() for c in _caches(16, seed=77)]
     x, g, beta = (t.cuda() for t in _rows(n_dec + T, seed=78))
-    slots = torch.tensor([3, 0, 9, 12, 1, 5, 7], dtype=torch.int32).cuda()
+    g[n_dec:] *= 0.02                 # slow decay: the segment schedule differs from whole runs
+    slots = torch.tensor([3, 0, 9, 12, 1, 5, 7][5 - n_dec:], dtype=torch.int32).cuda()
     cu = gi.cu_from_lengths(lengths).cuda()
     extra = gdn.gdn_prefill_workspace_size(dims, len(lengths), T)
     assert extra > 0, "these sizes should take the segment-parallel schedule"
@@ -261,21 +265,28 @@ def test_mixed_step_graph_replay_matches_eager():
 
     def step(cs, rs, out):
         gdn.gdn_mixed_step(x, g, beta, n_dec, cu, slots, cs, caches[1], rs, out, dims, SCALE,
-                           conv_bias=caches[2], workspace=ws)
+                           conv_bias=caches[2], workspace=ws, streams=streams)
 
-    cs_e, rs_e = caches[0].clone(), caches[3].clone()
-    ref = []
-    for _ in range(3):
-        o = torch.empty(n_dec + T, HV, DK, device="cuda")
-        step(cs_e, rs_e, o)
-        ref.append(o)
-    torch.cuda.synchronize()
+    def eager():
+        cs_e, rs_e = caches[0].clone(), caches[3].clone()
+        ref = []
+        for _ in range(3):
+            o = torch.empty(n_dec + T, HV, DK, device="cuda")
+            step(cs_e, rs_e, o)
+            ref.append(o)
+        torch.cuda.synchronize()
+        return ref, cs_e, rs_e
+
+    if not capture_first:
+        ref, cs_e, rs_e = eager()
     cs_g, rs_g = caches[0].clone(), caches[3].clone()
     out = torch.empty(n_dec + T, HV, DK, device="cuda")
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         step(cs_g, rs_g, out)
     torch.cuda.synchronize()
+    if capture_first:
+        ref, cs_e, rs_e = eager()
     for i in range(3):
         graph.replay()
         torch.cuda.synchronize()
@@ -283,3 +294,31 @@ def test_mixed_step_graph_replay_matches_eager():
         _ = torch.randn(1024, 1024, device="cuda").sum().item()   # eager work between
     assert torch.equal(rs_g, rs_e)
     assert torch.equal(cs_g, cs_e)
+    return ref
+
+
+@pytest.mark.parametrize("two_streams", [False, True])
+@pytest.mark.parametrize("capture_first", [False, True])
+def test_mixed_step_graph_replay_matches_eager(two_streams, capture_first):
+    """A captured HIP graph of a mixed step with decode rows (varlen conv +
+    roll, whole prefill runs, the decode rows; on one stream, or forked onto
+    a second stream and joined back by events inside the capture) reproduces
+    three consecutive eager steps bitwise on every replay, whether the capture
+    or the eager steps come first: every call only enqueues work, and the
+    schedule depends on the arguments alone."""
+    _graph_vs_eager(5, [300, 700], gdn.MixedStreams() if two_streams else None, capture_first)
+
+
+def test_mixed_step_graph_replay_segmented():
+    """The same for a step without decode rows on the segment-parallel
+    schedule (both segment passes and the scan in the graph); the outputs
+    differ from the whole-run schedule by rounding, which shows the schedule
+    that was captured."""
+    ref = _graph_vs_eager(0, [1024, 1024], None, capture_first=True)
+    lengths = [1024, 1024]
+    x, g, beta = _rows(sum(lengths), seed=78)
+    g *= 0.02
+    slots = torch.tensor([3, 0, 9, 12, 1, 5, 7][5:], dtype=torch.int32)
+    caches = _caches(16, seed=77)
+    out_w, _, _ = _mixed(x, g, beta, 0, lengths, slots, caches)
+    assert not torch.equal(ref[0], out_w), "the segment-parallel schedule was not captured"
