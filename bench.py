@@ -167,7 +167,8 @@ class DecodeSetup:
                             err_flag=self.err if validate else None)
 
     def capture(self, validate=False):
-        """One HIP graph holding one step per slot set (replayed as a unit)."""
+        """One HIP graph holding one step per disjoint slot set, in order
+        (replayed as a unit)."""
         torch = self.torch
         self.i = 0
         side = torch.cuda.Stream()
@@ -225,42 +226,61 @@ class MixedSetup:
         self.cu = gi.cu_from_lengths(self.lengths).to(dev)
         self.out = torch.empty(256 + T, HV, DV, device=dev)
         dims = big.dims
-        # the minimal workspace runs each prefill sequence whole; with the
-        # prefill's segment states as well it may take the segment-parallel schedule
-        base = big.gdn.gdn_mixed_workspace_size(dims, 256, T)
-        self.ws_min = torch.empty(base, dtype=torch.uint8, device=dev)
-        self.ws = torch.empty(base + big.gdn.gdn_prefill_workspace_size(dims, 2, T),
+        # beside decode rows the prefill part runs whole sequences: the
+        # minimal workspace is all the step uses
+        self.ws = torch.empty(big.gdn.gdn_mixed_workspace_size(dims, 256, T),
                               dtype=torch.uint8, device=dev)
         self.T = T
 
-    def step(self, ws=None):
+        self.streams = big.gdn.MixedStreams()
+
+    def step(self, overlap=True):
+        """One mixed step; overlap: the prefill part on the caller-owned second
+        stream (forked and joined by events), else both parts in order."""
         b = self.big
         d = b.d
         self.gdn.gdn_mixed_step(self.x, self.g, self.beta, 256, self.cu, self.slots,
                                 d["conv_state"], d["conv_weight"], d["rec_state"], self.out,
-                                b.dims, b.scale, workspace=self.ws if ws is None else ws)
+                                b.dims, b.scale, workspace=self.ws,
+                                streams=self.streams if overlap else None)
 
-    def step_whole(self):
-        self.step(self.ws_min)
+    def step_serial(self):
+        self.step(overlap=False)
 
 
 class PrefillSetup:
-    """The varlen prefill workload: 8 sequences, lengths uniform in [512, 8192]."""
+    """The varlen prefill workload: 8 sequences, lengths uniform in [512, 8192]
+    (drawn with the workload's seed).  `copies` input sets of those lengths
+    (the first with the workload's seed, the others with their own), each with
+    its own states, slots and output, are rotated call to call so that no call
+    finds the previous call's inputs in the 256 MB Infinity Cache."""
 
-    def __init__(self, seed, dev):
+    def __init__(self, seed, dev, copies=3):
         import torch
         import gdn_inputs as gi
         import gated_deltanet_recurrent_gdn_amd as gdn
         self.torch, self.gdn = torch, gdn
         gen = torch.Generator().manual_seed(seed)
         self.lengths = gi.seqlens_uniform(8, 512, 8192, gen)
-        p = gi.prefill_inputs(self.lengths, 16, seed=seed)
-        self.p = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in p.items()}
+        self.sets = []
+        for c in range(copies):
+            p = gi.prefill_inputs(self.lengths, 16, seed=seed + 1000 * c)
+            self.sets.append({k: (v.to(dev) if isinstance(v, torch.Tensor) else v)
+                              for k, v in p.items()})
+        self.p = self.sets[0]
         self.T = int(sum(self.lengths))
         self.dims = gdn.make_dims(H, HV, DK, DV, W)
-        self.out = torch.empty(self.T, HV, DV, dtype=torch.bfloat16, device=dev)
+        self.outs = [torch.empty(self.T, HV, DV, dtype=torch.bfloat16, device=dev)
+                     for _ in range(copies)]
+        self.out = self.outs[0]
         self.err = torch.zeros(1, dtype=torch.int32, device=dev)
         self.gate = None
+        self.i = 0
+
+    def rotate(self):
+        """Move to the next input set (and its output buffer)."""
+        self.i = (self.i + 1) % len(self.sets)
+        self.p, self.out = self.sets[self.i], self.outs[self.i]
 
     def use_gating(self, seed):
         import gdn_inputs as gi
@@ -270,6 +290,7 @@ class PrefillSetup:
 
     def step(self, validate=False):
         gdn = self.gdn
+        self.rotate()
         p = self.p
         flags = gdn.FLAG_QK_L2NORM | (gdn.FLAG_VALIDATE if validate else 0)
         if self.gate is not None:
@@ -283,12 +304,13 @@ class PrefillSetup:
                                 flags=flags, err_flag=self.err if validate else None)
 
 
-def time_graph(torch, graph, per_replay, steps, warmup):
-    """Replay a captured graph of `per_replay` steps; per-step ms for each replay."""
+def time_graph(torch, graph, per_replay, steps, warmup, min_replays=5):
+    """Replay a captured graph of `per_replay` steps (at least `steps` steps and
+    `min_replays` replays); per-step ms for each replay."""
     for _ in range(max(1, warmup // per_replay)):
         graph.replay()
     torch.cuda.synchronize()
-    n = max(1, -(-steps // per_replay))
+    n = max(min_replays, -(-steps // per_replay))
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
     for i in range(n):
@@ -314,14 +336,20 @@ def time_loop(torch, fn, steps, warmup):
     return [s.elapsed_time(e) for s, e in zip(starts, ends)]
 
 
+def host_cpu_counts():
+    """(CPUs this process may run on, CPUs the OS reports)."""
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except AttributeError:
+        aff = os.cpu_count() or 1
+    return aff, os.cpu_count() or aff
+
+
 def host_threads():
     """Host threads for the oracle's all-cores leg: the CPUs this process may
-    run on, at most 16 (one GPU's share of the host)."""
-    try:
-        n = len(os.sched_getaffinity(0))
-    except AttributeError:
-        n = os.cpu_count() or 1
-    return max(1, min(16, n))
+    run on, at most 16 -- one GPU's share of the host, the share a one-GPU job
+    is granted on the GPU hosts here, whatever the OS reports in total."""
+    return max(1, min(16, host_cpu_counts()[0]))
 
 
 def host_cpu_model():
@@ -411,10 +439,14 @@ def cpu_baseline(budget_s, n_threads):
     gbs = rows * decode_bytes_per_seq() / dt / 1e9
     rows1, dt1 = run_oracle_threads(1, budget_s, lambda i: decode_oracle_unit(64, 2))
     gbs1 = rows1 * decode_bytes_per_seq() / dt1 / 1e9
+    aff, ncpu = host_cpu_counts()
     main = {"value": round(gbs, 4), "unit": "GB/s", "cores": n_threads, "kind": "oracle",
             "sample": f"{rows} decode rows (batch-16 steps on {n_threads} threads, each with "
                       f"its own rows and caches; shapes and distributions of the batch-256 "
-                      f"workload) in {dt:.1f} s, fp64 C, host CPU {host_cpu_model()}"}
+                      f"workload) in {dt:.1f} s, fp64 C; host CPU '{host_cpu_model()}', "
+                      f"nproc {aff} (affinity), {ncpu} CPUs reported by the OS; threads "
+                      f"capped at 16, one GPU's share of the host",
+            "nproc": aff, "os_cpus": ncpu, "cpu_model": host_cpu_model()}
     one = {"value": round(gbs1, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
            "sample": f"{rows1} decode rows (steps of batch 64) in {dt1:.1f} s, "
                      "single-threaded fp64 C"}
@@ -447,8 +479,13 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    big = DecodeSetup(256, 2048, seed=2, dev="cuda")
+    # decode buckets: batch 1, 2, 4, 8, 16 from a 256-slot cache (seed 1) and
+    # batch 256, 1024 from a 2048-slot cache (seed 2); each bucket has its own cache
+    buckets = {b: DecodeSetup(b, 256, seed=1, dev="cuda") for b in (1, 2, 4, 8)}
     small = DecodeSetup(16, 256, seed=1, dev="cuda")
+    buckets[16] = small
+    big = DecodeSetup(256, 2048, seed=2, dev="cuda")
+    buckets[256] = big
     pre = PrefillSetup(seed=3, dev="cuda")
     torch.cuda.synchronize()
 
@@ -460,16 +497,31 @@ def main():
     torch.cuda.synchronize()
     del cal_src, cal_dst
 
+    bucket_ms, bucket_sets = {}, {}
     if args.eager:
         r_big = r_small = 1
         ms_big = time_loop(torch, lambda: big.step(args.validate), args.steps, args.warmup)
         ms_small = time_loop(torch, lambda: small.step(args.validate), args.steps, args.warmup)
     else:
-        # decode buckets: graph replay of one step per disjoint slot set
-        g_big, r_big = big.capture(args.validate)
-        g_small, r_small = small.capture(args.validate)
-        ms_big = time_graph(torch, g_big, r_big, args.steps, args.warmup)
-        ms_small = time_graph(torch, g_small, r_small, args.steps, args.warmup)
+        # decode buckets: graph replay of one step per disjoint slot set, at
+        # least 5 replays per bucket (mean / min / max / spread over replays)
+        for b in (1, 2, 4, 8, 16, 256):
+            gph, nsets = buckets[b].capture(args.validate)
+            bucket_ms[b] = time_graph(torch, gph, nsets, args.steps, args.warmup)
+            bucket_sets[b] = nsets
+            del gph
+        ms_big, r_big = bucket_ms[256], bucket_sets[256]
+        ms_small, r_small = bucket_ms[16], bucket_sets[16]
+        for b in (1, 2, 4, 8):
+            del buckets[b]
+        # batch 1024 (one slot set of the 2048-slot cache: 4 GiB of state per
+        # step, far past the Infinity Cache)
+        huge = DecodeSetup(1024, 2048, seed=2, dev="cuda")
+        gph, nsets = huge.capture(args.validate)
+        bucket_ms[1024] = time_graph(torch, gph, nsets, args.steps, args.warmup)
+        bucket_sets[1024] = nsets
+        del gph, huge
+        torch.cuda.synchronize()
     # prefill, eager (one call is milliseconds)
     ms_pre = time_loop(torch, lambda: pre.step(args.validate), args.steps, args.warmup)
     # the headline step's kernel alone (the fused step at batch 256), eager
@@ -522,10 +574,15 @@ def main():
                             max(1, args.warmup // 2))
     ms_long_seg = time_loop(torch, lambda: long_prefill(0), lsteps, max(1, args.warmup // 2))
     del lp, lp_out, lp_ws
-    # a mixed step: the batch-256 decode rows plus two 1024-token prefills
+    # a mixed step: the batch-256 decode rows plus two 1024-token prefills, with
+    # the prefill part overlapped on a second stream and in order on one,
+    # alternating so both see the same conditions
     mixed = MixedSetup(big, seed=9, dev="cuda")
-    ms_mixed = time_loop(torch, mixed.step, args.steps, args.warmup)
-    ms_mixed_whole = time_loop(torch, mixed.step_whole, args.steps, args.warmup)
+    ms_mixed, ms_mixed_serial = [], []
+    for _ in range(3):
+        ms_mixed += time_loop(torch, mixed.step, max(2, args.steps // 3), args.warmup)
+        ms_mixed_serial += time_loop(torch, mixed.step_serial, max(2, args.steps // 3),
+                                     args.warmup)
     # the same batch-256 step and prefill with the gating fused in (raw a, b)
     big.use_gating(seed=7)
     pre.use_gating(seed=8)
@@ -601,12 +658,13 @@ def main():
         "gated_rmsnorm_note": ("gdn_gated_rmsnorm on the prefill output: "
                                f"{pre.T * HV} rows of {DV}, bf16 x, z, out, fp32 weight"),
         "mixed_step_ms_mean": round(mean(ms_mixed), 4),
-        "mixed_step_whole_prefill_ms_mean": round(mean(ms_mixed_whole), 4),
+        "mixed_step_serial_ms_mean": round(mean(ms_mixed_serial), 4),
         "mixed_step_note": ("gdn_mixed_step, eager: the 256 decode rows of the batch-256 "
-                            "workload plus two 1024-token prefill sequences (pre-conv input); "
-                            "the prefill part runs on the library's side stream, overlapped "
-                            "with the decode rows, as whole runs; *_whole_prefill: the same "
-                            "step given the minimal workspace"),
+                            "workload plus two 1024-token prefill sequences (pre-conv input), "
+                            "prefill as whole runs; mixed_step: the prefill part on a "
+                            "caller-owned second stream (fork / join events), overlapped with "
+                            "the decode rows; *_serial: both parts in order on one stream; "
+                            "the two alternate in the same run"),
         "decode_rec_kernel_b256_ms_mean": round(rec_ms, 5),
         "decode_rec_kernel_b256_GBps": round(rec_gbs, 2),
         "decode_rec_kernel_b256_pct_hbm_peak": round(100 * rec_gbs / HBM_PEAK_GBS, 2),
@@ -619,6 +677,26 @@ def main():
                        "g and beta computed in-kernel from bf16 a, b and fp32 A_log, dt_bias"),
         "validate": bool(args.validate),
     }
+
+    if bucket_ms:
+        # per bucket, as the graph-replay table of the GB10 decode post does:
+        # mean / min / max per step over the replays, spread = (max - min) / mean
+        tab = {}
+        for b, ms in sorted(bucket_ms.items()):
+            by = b * decode_bytes_per_seq() + conv_weight_bytes()
+            m = mean(ms)
+            tab[str(b)] = {"ms_mean": round(m, 5), "ms_min": round(min(ms), 5),
+                           "ms_max": round(max(ms), 5),
+                           "spread": round((max(ms) - min(ms)) / m, 4),
+                           "bytes_per_step": by, "GBps": round(by / (m * 1e-3) / 1e9, 1),
+                           "pct_hbm_peak": round(100 * by / (m * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                           "slot_sets": bucket_sets[b], "replays": len(ms)}
+        extra["decode_buckets"] = tab
+        extra["decode_buckets_note"] = (
+            "gdn_decode_step per bucket, HIP graph replay of one step per disjoint slot set "
+            "(every set of the cache: batch 1..16 over a 256-slot cache, 256 and 1024 over a "
+            "2048-slot cache), per-step time of each replay; bytes = 4325636 per row + the "
+            "65536-byte conv weight")
 
     total_ms = mean(ms_big) + mean(ms_small) + pre_ms
 

@@ -262,7 +262,13 @@ size_t gdn_prefill_workspace_size(const gdn_dims* dims, int32_t n_seqs, int32_t 
  * forward substitution ([P4] "Numerical root cause and fix"), and the state is
  * carried from chunk to chunk.
  *
- *   q, k         [total_tokens, H, dk]; v [total_tokens, HV, dv]; in_dt
+ *   q, k         [total_tokens, H, dk]; v [total_tokens, HV, dv]; in_dt:
+ *                GDN_BF16 at dk = dv in {32, 64, 128}; GDN_F32 only at 32 and
+ *                64 (GDN_ERR_DTYPE at 128).  fp32 inputs are carried as bf16
+ *                hi + lo planes in LDS, and at 128 the doubled K, Q, K^T and
+ *                V^T planes alone (8 x 64 x 128 x 2 bytes = 128 KiB) leave too
+ *                little of the 160 KiB of LDS for the chunk's work arrays;
+ *                round fp32 inputs to bf16 first at that size.
  *   g, beta      [total_tokens, HV] fp32
  *   cu_seqlens   [n_seqs + 1] int32; slot_idx [n_seqs] int32 (<= 0 inactive:
  *                zero outputs, state untouched)

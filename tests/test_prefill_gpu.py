@@ -115,6 +115,36 @@ def test_prefill_varlen_full_size(varlen_workload):
     print(f"varlen T={p['q'].shape[0]}: out {eo:.2e} state {es:.2e}")
 
 
+@pytest.mark.parametrize("n_seqs", [1, 5, 257])
+def test_prefill_many_sequences(n_seqs):
+    """vLLM PR #53864, "Test Plan": num_seqs 1, 5 and 257 at the Qwen3-Next-like
+    heads (H=16, HV=32, d=128) with short ragged lengths, one sequence inactive
+    when there are several; 257 sequences are 8224 workgroups, many rounds of
+    the 256 CUs.  Sampled value heads against the oracle, every output and
+    state finite, the inactive sequence's rows zero and its slot untouched."""
+    gen = torch.Generator().manual_seed(100 + n_seqs)
+    lengths = [97] if n_seqs == 1 else gi.seqlens_uniform(n_seqs, 1, 160, gen)
+    p = gi.prefill_inputs(lengths, n_seqs + 1, seed=200 + n_seqs)
+    dead = None
+    if n_seqs > 1:
+        dead = n_seqs // 2
+        p["slot_idx"][dead] = 0
+    g = to_dev(p)
+    before = g["rec_state"].clone()
+    out = run_prefill_gpu(g, 128 ** -0.5)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    assert torch.isfinite(g["rec_state"]).all()
+    if dead is not None:
+        cu = p["cu_seqlens"].tolist()
+        assert torch.all(out[cu[dead]:cu[dead + 1]] == 0)
+        used = set(p["slot_idx"].tolist())
+        free = [s for s in range(n_seqs + 1) if s not in used]
+        assert torch.equal(before[free], g["rec_state"][free])
+    eo, es = check_heads(p, g, out, [0, 21, 31], 128 ** -0.5)
+    print(f"{n_seqs} sequences, T={sum(lengths)}: out {eo:.2e} state {es:.2e}")
+
+
 @pytest.mark.parametrize("T,heads", [(64, list(range(32))), (16384, [0, 17, 30])])
 def test_prefill_correlated_keys(T, heads):
     p = gi.stress_prefill_inputs(T)
