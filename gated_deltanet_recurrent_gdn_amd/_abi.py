@@ -29,7 +29,7 @@ _STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_DIMS", 3: "GDN_ERR_DTYPE"
            4: "GDN_ERR_ALIGN", 5: "GDN_ERR_WORKSPACE", 6: "GDN_ERR_LAUNCH", 7: "GDN_ERR_FLAGS"}
 
 EXPORTED = ["gdn_conv_update", "gdn_decode_workspace_size", "gdn_decode_step",
-            "gdn_decode_step_gated", "gdn_decode_recurrent",
+            "gdn_decode_step_gated", "gdn_decode_step_noalloc", "gdn_decode_recurrent",
             "gdn_prefill_workspace_size", "gdn_prefill_chunked", "gdn_prefill_chunked_gated",
             "gdn_prefill_segmented_workspace_size", "gdn_prefill_segmented",
             "gdn_mixed_workspace_size", "gdn_mixed_step", "gdn_gated_rmsnorm", "gdn_strerror"]
@@ -81,6 +81,8 @@ def load_library(path: str = None):
     lib.gdn_decode_workspace_size.restype = sz
     lib.gdn_decode_step.argtypes = [P, i32, P, P, P, i32, P, i32, P, P, i32, P, i32, P, i32,
                                     D, f32, i32, P, sz, P, P]
+    lib.gdn_decode_step_noalloc.argtypes = [P, i32, P, P, P, i32, P, i32, P, P, i32, P, i32, P,
+                                            i32, D, f32, i32, P, P]
     lib.gdn_decode_recurrent.argtypes = [P, i32, P, P, P, i32, P, i32, P, i32, D, f32, i32,
                                          P, P]
     lib.gdn_prefill_workspace_size.argtypes = [D, i32, i32]
@@ -103,7 +105,8 @@ def load_library(path: str = None):
     lib.gdn_gated_rmsnorm.argtypes = [P, i32, P, P, i32, ctypes.c_int64, i32, f32, i32, P, i32, P]
     lib.gdn_strerror.argtypes = [i32]
     lib.gdn_strerror.restype = ctypes.c_char_p
-    for f in (lib.gdn_conv_update, lib.gdn_decode_step, lib.gdn_decode_recurrent,
+    for f in (lib.gdn_conv_update, lib.gdn_decode_step, lib.gdn_decode_step_noalloc,
+              lib.gdn_decode_recurrent,
               lib.gdn_prefill_chunked, lib.gdn_decode_step_gated, lib.gdn_prefill_chunked_gated,
               lib.gdn_mixed_step, lib.gdn_gated_rmsnorm, lib.gdn_prefill_segmented):
         f.restype = ctypes.c_int
@@ -215,13 +218,18 @@ def _decode_step(fn, mixed_qkv, gb, gate, slot_idx, conv_state, conv_weight, rec
         raise ValueError("rec_state must be [num_slots, HV, dv, dk]")
     if tuple(conv_state.shape) != (ns, D, dims.conv_width - 1):
         raise ValueError("conv_state must be [num_slots, D, W-1] with the rec_state slot count")
+    args = (_p(slot_idx), B, _p(conv_state), _dt(conv_state), _p(conv_weight), _p(conv_bias),
+            _dt(conv_weight), _p(rec_state), ns, _p(out), _dt(out), ctypes.byref(dims),
+            float(scale), flags)
+    if fn == "gdn_decode_step_noalloc":          # no workspace: the library's scratch
+        _check(fn, lib.gdn_decode_step_noalloc(_p(mixed_qkv), _dt(mixed_qkv), _p(gb[0]),
+                                               _p(gb[1]), *args, _p(err_flag), _stream(stream)))
+        return out
     need = gdn_decode_workspace_size(dims, B)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=mixed_qkv.device)
     _dev(workspace, "workspace")
-    rest = (_p(slot_idx), B, _p(conv_state), _dt(conv_state), _p(conv_weight), _p(conv_bias),
-            _dt(conv_weight), _p(rec_state), ns, _p(out), _dt(out), ctypes.byref(dims),
-            float(scale), flags, _p(workspace), workspace.numel() * workspace.element_size(),
+    rest = (*args, _p(workspace), workspace.numel() * workspace.element_size(),
             _p(err_flag), _stream(stream))
     if gate is None:
         status = lib.gdn_decode_step(_p(mixed_qkv), _dt(mixed_qkv), _p(gb[0]), _p(gb[1]), *rest)
@@ -240,6 +248,17 @@ def gdn_decode_step(mixed_qkv, g, beta, slot_idx, conv_state, conv_weight, rec_s
     return _decode_step("gdn_decode_step", mixed_qkv, (g, beta), None, slot_idx, conv_state,
                         conv_weight, rec_state, out, dims, scale, conv_bias, flags, workspace,
                         err_flag, stream)
+
+
+def gdn_decode_step_noalloc(mixed_qkv, g, beta, slot_idx, conv_state, conv_weight, rec_state,
+                            out, dims: gdn_dims, scale, conv_bias=None,
+                            flags=DEFAULT_DECODE_FLAGS, err_flag=None, stream=None):
+    """gdn_decode_step without a workspace (gdn.h: gdn_decode_step_noalloc):
+    nothing is allocated, here or in the library; the conv + recurrence path
+    uses the library's per-device scratch array."""
+    return _decode_step("gdn_decode_step_noalloc", mixed_qkv, (g, beta), None, slot_idx,
+                        conv_state, conv_weight, rec_state, out, dims, scale, conv_bias, flags,
+                        None, err_flag, stream)
 
 
 def gdn_decode_step_gated(mixed_qkv, gate: GateInputs, slot_idx, conv_state, conv_weight,

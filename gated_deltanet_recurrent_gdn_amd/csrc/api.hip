@@ -6,10 +6,15 @@
 // event a call uses is the caller's.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "gdn.h"
 #include "gdn_internal.hpp"
 
 using namespace gdn;
+
+// gdn_decode_step_noalloc's scratch (see noalloc_scratch below).
+static __device__ __align__(256) unsigned char scratch[GDN_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -124,6 +129,26 @@ gdn_status gate_args(const float* g, const float* beta, const gdn_gate_inputs* g
     return GDN_OK;
 }
 
+// Scratch of gdn_decode_step_noalloc: the conv + recurrence pair's fp32
+// activations live here instead of in a caller workspace.  The array is part
+// of the code object, so each device holds its own copy at its own address
+// from module load until the process ends; host code must never pass the
+// array's name to a kernel (on the host it is only a stand-in for the symbol):
+// the device address comes from hipGetSymbolAddress, looked up on the first
+// call on each device, with that device current, and kept per device.
+std::atomic<void*> scratch_addr[64];
+
+void* noalloc_scratch() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    void* p = scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        scratch_addr[dev].store(p, std::memory_order_release);   // concurrent first calls agree
+    }
+    return p;
+}
+
 // The decode step's kernels for `batch` rows (after the checks and the
 // optional validation): the fused kernel or the conv + recurrence pair.
 gdn_status decode_step_launch(const void* mixed_qkv, gdn_dtype x_dt, const GateArgs& ga,
@@ -159,7 +184,7 @@ gdn_status decode_step_impl(const void* mixed_qkv, gdn_dtype x_dt, const float* 
                             gdn_dtype w_dt, float* rec_state, int32_t num_slots, void* out,
                             gdn_dtype out_dt, const gdn_dims* dims, float scale, int32_t flags,
                             void* workspace, size_t workspace_bytes, int32_t* err_flag,
-                            hipStream_t stream) {
+                            hipStream_t stream, bool use_scratch = false) {
     if (gdn_status st = check_flags(flags, KNOWN_FLAGS | GDN_FLAG_STEP_FUSED | GDN_FLAG_STEP_SPLIT,
                                     err_flag))
         return st;
@@ -174,12 +199,24 @@ gdn_status decode_step_impl(const void* mixed_qkv, gdn_dtype x_dt, const float* 
     if (gdn_status st = gate_args(g, beta, gate, batch > 0, ga)) return st;
     if (batch > 0) {
         if (!mixed_qkv || !slot_idx || !conv_state || !conv_weight || !rec_state || !out ||
-            !workspace)
+            (!workspace && !use_scratch))
             return GDN_ERR_NULL;
         if (!aligned16(rec_state) || !aligned16(workspace) || !aligned16(mixed_qkv) ||
             !aligned16(conv_state) || !aligned16(conv_weight) || (conv_bias && !aligned16(conv_bias)))
             return GDN_ERR_ALIGN;
-        if (workspace_bytes < gdn_decode_workspace_size(dims, batch)) return GDN_ERR_WORKSPACE;
+        if (use_scratch) {
+            // the library's scratch array stands in for the workspace; it is
+            // needed only when the call takes the conv + recurrence pair (the
+            // fused kernel keeps the activations in LDS)
+            const bool fused = (flags & GDN_FLAG_STEP_FUSED) ||
+                               (!(flags & GDN_FLAG_STEP_SPLIT) && decode_step_use_fused(*dims, batch));
+            if (!fused && gdn_decode_workspace_size(dims, batch) > GDN_NOALLOC_SCRATCH_BYTES)
+                return GDN_ERR_WORKSPACE;
+            workspace = noalloc_scratch();
+            if (!workspace) return GDN_ERR_LAUNCH;
+        } else if (workspace_bytes < gdn_decode_workspace_size(dims, batch)) {
+            return GDN_ERR_WORKSPACE;
+        }
     }
     const hipStream_t s = stream;
     if (flags & GDN_FLAG_VALIDATE)
@@ -282,6 +319,18 @@ gdn_status gdn_decode_step_gated(const void* mixed_qkv, gdn_dtype x_dt,
                             conv_state, cs_dt, conv_weight, conv_bias, w_dt, rec_state,
                             num_slots, out, out_dt, dims, scale, flags, workspace,
                             workspace_bytes, err_flag, stream);
+}
+
+gdn_status gdn_decode_step_noalloc(const void* mixed_qkv, gdn_dtype x_dt, const float* g,
+                                   const float* beta, const int32_t* slot_idx, int32_t batch,
+                                   void* conv_state, gdn_dtype cs_dt, const void* conv_weight,
+                                   const void* conv_bias, gdn_dtype w_dt, float* rec_state,
+                                   int32_t num_slots, void* out, gdn_dtype out_dt,
+                                   const gdn_dims* dims, float scale, int32_t flags,
+                                   int32_t* err_flag, hipStream_t stream) {
+    return decode_step_impl(mixed_qkv, x_dt, g, beta, nullptr, slot_idx, batch, conv_state,
+                            cs_dt, conv_weight, conv_bias, w_dt, rec_state, num_slots, out,
+                            out_dt, dims, scale, flags, nullptr, 0, err_flag, stream, true);
 }
 
 gdn_status gdn_decode_recurrent(const void* qkv, gdn_dtype qkv_dt, const float* g,

@@ -223,6 +223,32 @@ gdn_status gdn_decode_step(const void* mixed_qkv, gdn_dtype x_dt,
                            int32_t* err_flag, hipStream_t stream);
 
 /*
+ * gdn_decode_step_noalloc -- gdn_decode_step for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same arguments without the workspace, the same
+ * kernels and bitwise the same results.  Where the call takes the conv +
+ * recurrence pair, the fp32 activations (batch * D * 4 bytes) go to a scratch
+ * array of GDN_NOALLOC_SCRATCH_BYTES that the library holds in device memory,
+ * one per device, until the process ends; GDN_ERR_WORKSPACE if they would not
+ * fit (at D = 8192: more than 512 rows on that path).  The fused kernel needs
+ * no scratch.  The call allocates nothing; its first call on a device looks
+ * up the array's device address (GDN_ERR_LAUNCH if the runtime cannot) and
+ * keeps it for that device.  Every call on a device shares that device's
+ * array, so calls that can overlap on one device (different streams, or
+ * threads) race on it: order them, or use gdn_decode_step.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES (16u << 20)
+gdn_status gdn_decode_step_noalloc(const void* mixed_qkv, gdn_dtype x_dt,
+                                   const float* g, const float* beta,
+                                   const int32_t* slot_idx, int32_t batch,
+                                   void* conv_state, gdn_dtype cs_dt,
+                                   const void* conv_weight, const void* conv_bias, gdn_dtype w_dt,
+                                   float* rec_state, int32_t num_slots,
+                                   void* out, gdn_dtype out_dt,
+                                   const gdn_dims* dims, float scale, int32_t flags,
+                                   int32_t* err_flag, hipStream_t stream);
+
+/*
  * gdn_decode_recurrent -- the recurrent half of the decode step alone, on
  * post-conv activations (the split of [P1] "Which provider this aligns to":
  * conv update, then the packed recurrent decode on mixed q|k|v):
