@@ -7,6 +7,8 @@
 //   U  = Ut - W S0^T                     (row r: beta_r times the delta of token r)
 //   O  = diag(e^gamma) Q S0^T + (M o P) U, P = Q K^T, M[r,i] = exp(gamma_r - gamma_i), i <= r
 //   S1 = e^{gamma_L} S0 + U^T diag(exp(gamma_L - gamma)) K
+// The kernel forms U as cU (V - diag(e^gamma) K S0^T) with cU = T diag(beta):
+// W and Ut share the factor T diag(beta), so one coefficient matrix serves.
 // which equals the token-by-token recurrence S_t = exp(g_t) S (I - b k k^T) +
 // b v k^T exactly in exact arithmetic.  The 64-token chunk and the inverse of
 // the lower-triangular KK^T matrix through its 16x16 diagonal blocks follow
@@ -275,11 +277,11 @@ struct PrefillSmem {
     float g[CH * SF];                           // A, then T in place (lower, unit diag, zero upper),
                                                 // except T's block [32:64][0:32], which is in xs
     struct {
-        bf16_t c[4 * CH * ST];                  // cW hi, cW lo, cU hi, cU lo   [t][t']
+        bf16_t c[2 * CH * ST];                  // cU hi, cU lo [t][t'], pperm order along t'
     } pc;
     float xs[32 * 36];                          // merge scratch X; finally T[32:64][0:32]
     bf16_t mp[2 * CH * ST];                     // (M o P) hi, lo   [t][t']
-    float gam[CH], beta[CH], rk[CH], rq[CH], eg[CH], ck[CH], cwc[CH];
+    float gam[CH], beta[CH], rk[CH], rq[CH], eg[CH], ck[CH], cy[CH];
     float egl;
 };
 
@@ -618,7 +620,7 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
                 const float et = expf(gv);
                 sm.eg[tid] = et * sm.rq[tid];
                 sm.ck[tid] = (tid < L) ? expf(gl - gv) * sm.rk[tid] : 0.0f;
-                sm.cwc[tid] = sm.beta[tid] * et * sm.rk[tid];
+                sm.cy[tid] = et * sm.rk[tid];
                 if (tid == 0) sm.egl = expf(gl);
             }
             const float gi = sm.gam[i];
@@ -650,7 +652,7 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
         __syncthreads();
 
         // ---------------- state products that need only S0 and the staged
-        // chunk: Z = K S0^T (so that W S0^T = cW Z, with no W formed) and,
+        // chunk: Z = K S0^T (so that U = cU (V - diag(cy) Z), with no W formed) and,
         // transposed, O1^T = S0 Q^T, scaled by e^gamma_t rq_t.  The state's
         // hi/lo fragments (permuted k-slots) are the B operand of the first
         // and, holding the same values, the A operand of the second.  They run
@@ -881,120 +883,104 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
         }
         __syncthreads();
 
-        // ---------------- coefficients cW = T diag(cwc), cU = T diag(beta), split
+        // ---------------- coefficients cU = T diag(beta), split into hi/lo and
+        // stored in pperm order along t' (it meets Y in permuted t-slots)
         // (thread: row r, 8 columns; T's upper triangle is exactly zero)
         {
             const int r = tid >> 3, cb = 8 * (tid & 7);
-            uint32_t wh[4], wl[4], uh[4], ul[4];
+            uint32_t uh[4], ul[4];
             const float* trow = (r >= 32 && cb < 32) ? &sm.xs[(r - 32) * 36 + cb] : &sm.g[r * SF + cb];
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const float4 t = *reinterpret_cast<const float4*>(trow + 4 * j);
-                const float4 cw = *reinterpret_cast<const float4*>(&sm.cwc[cb + 4 * j]);
                 const float4 bt = *reinterpret_cast<const float4*>(&sm.beta[cb + 4 * j]);
-                const f32x4 w = {t.x * cw.x, t.y * cw.y, t.z * cw.z, t.w * cw.w};
                 const f32x4 u = {t.x * bt.x, t.y * bt.y, t.z * bt.z, t.w * bt.w};
                 uint2 h2, l2;
-                split4(w, h2, l2); wh[2 * j] = h2.x; wh[2 * j + 1] = h2.y; wl[2 * j] = l2.x; wl[2 * j + 1] = l2.y;
                 split4(u, h2, l2); uh[2 * j] = h2.x; uh[2 * j + 1] = h2.y; ul[2 * j] = l2.x; ul[2 * j + 1] = l2.y;
             }
-            bf16_t* base = sm.pc.c + r * ST + cb;
-            bf16_t* wbase = sm.pc.c + r * ST;            // cW planes in pperm order
-            lds_st8(wbase + 0 * CH * ST + pperm(cb), wh[0], wh[1]);
-            lds_st8(wbase + 0 * CH * ST + pperm(cb + 4), wh[2], wh[3]);
-            lds_st8(wbase + 1 * CH * ST + pperm(cb), wl[0], wl[1]);
-            lds_st8(wbase + 1 * CH * ST + pperm(cb + 4), wl[2], wl[3]);
-            *reinterpret_cast<uint4*>(base + 2 * CH * ST) = make_uint4(uh[0], uh[1], uh[2], uh[3]);
-            *reinterpret_cast<uint4*>(base + 3 * CH * ST) = make_uint4(ul[0], ul[1], ul[2], ul[3]);
+            bf16_t* ubase = sm.pc.c + r * ST;
+            lds_st8(ubase + 0 * CH * ST + pperm(cb), uh[0], uh[1]);
+            lds_st8(ubase + 0 * CH * ST + pperm(cb + 4), uh[2], uh[3]);
+            lds_st8(ubase + 1 * CH * ST + pperm(cb), ul[0], ul[1]);
+            lds_st8(ubase + 1 * CH * ST + pperm(cb + 4), ul[2], ul[3]);
         }
         __syncthreads();
 
-        // ---------------- U = cU V - cW Z (wave's value columns): Ut = cU V with
-        // the split coefficients on the raw V planes (hh + lh (+ hl for split
-        // inputs)), then cW (split) times -Z (split, permuted t-slots from the
-        // accumulators: hh + hl + lh).  Both coefficient matrices are lower
-        // triangular: blocks above the diagonal are zero and skipped.
+        // ---------------- U = cU Y with Y = V - diag(cy) Z, cy = e^gamma rk: the
+        // same U as Ut - W S0^T (W = cU diag(cy) K, so W S0^T = cU diag(cy) Z),
+        // with one coefficient matrix.  Y is formed in fp32 from the Z
+        // accumulators and V (read from V^T, four consecutive tokens of one
+        // value column per lane: the accumulator layout), split into hi/lo and
+        // fed as permuted t-slots; cU (split) is lower triangular, so blocks
+        // above the diagonal are skipped (hh + hl + lh).
         f32x4 u[4][VB];                          // U tiles (t-block, v-block): rows t, cols v
-        f32x4 u2[4][VB];                         // the paired P run's U (= -cW Z2; its v is 0)
+        f32x4 u2[4][VB];                         // the paired P run's U (= cU Y2, Y2 = -diag(cy) Z2)
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
             for (int vb = 0; vb < VB; ++vb) { u[tb][vb] = f32x4{0, 0, 0, 0}; u2[tb][vb] = f32x4{0, 0, 0, 0}; }
         if (vact) {
+            bf16x8 yh[2][VB], yl[2][VB];
+            auto make_y = [&](const f32x4 (&zz)[4][VB], bool with_v) {
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    if (32 * ks > 16 * tb + 15) continue;          // strictly above the diagonal
-                    const bf16x8 ah = frag_std(sm.pc.c + 2 * CH * ST, ST, 16 * tb + l16, 32 * ks, q4);
-                    const bf16x8 al = frag_std(sm.pc.c + 3 * CH * ST, ST, 16 * tb + l16, 32 * ks, q4);
+                for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
                     for (int vb = 0; vb < VB; ++vb) {
                         const int vr = 16 * (wave * VB + vb) + l16;
-                        const bf16x8 bv = frag_std(sm.vt[0], ST, vr, 32 * ks, q4);
-                        u[tb][vb] = mfma(ah, bv, u[tb][vb]);
-                        u[tb][vb] = mfma(al, bv, u[tb][vb]);
-                        if constexpr (SPL)
-                            u[tb][vb] = mfma(ah, frag_std(sm.vt[NP - 1], ST, vr, 32 * ks, q4), u[tb][vb]);
+                        f32x4 n[2];
+#pragma unroll
+                        for (int e = 0; e < 2; ++e) {
+                            const int tb = 2 * ks + e;
+                            const int t0 = 16 * tb + 4 * q4;
+                            const float4 cyv = *reinterpret_cast<const float4*>(&sm.cy[t0]);
+                            float vv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                            if (with_v) {
+#pragma unroll
+                                for (int pl = 0; pl < NP; ++pl) {
+                                    const uint2 w = *reinterpret_cast<const uint2*>(&sm.vt[pl][vr * ST + t0]);
+                                    vv[0] += bf16lo_to_f32(w.x); vv[1] += bf16hi_to_f32(w.x);
+                                    vv[2] += bf16lo_to_f32(w.y); vv[3] += bf16hi_to_f32(w.y);
+                                }
+                            }
+                            n[e][0] = vv[0] - cyv.x * zz[tb][vb][0];
+                            n[e][1] = vv[1] - cyv.y * zz[tb][vb][1];
+                            n[e][2] = vv[2] - cyv.z * zz[tb][vb][2];
+                            n[e][3] = vv[3] - cyv.w * zz[tb][vb][3];
+                        }
+                        uint2 h0, l0, h1, l1;
+                        split4(n[0], h0, l0);
+                        split4(n[1], h1, l1);
+                        yh[ks][vb] = as_bf16x8(cat(h0, h1));
+                        yl[ks][vb] = as_bf16x8(cat(l0, l1));
                     }
-                }
-            bf16x8 zh[2][VB], zl[2][VB];
+            };
+            auto mul_cu = [&](f32x4 (&acc)[4][VB]) {
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
+                for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-                for (int vb = 0; vb < VB; ++vb) {
-                    f32x4 n0 = z[2 * ks][vb], n1 = z[2 * ks + 1][vb];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) { n0[r] = -n0[r]; n1[r] = -n1[r]; }
-                    uint2 h0, l0, h1, l1;
-                    split4(n0, h0, l0);
-                    split4(n1, h1, l1);
-                    zh[ks][vb] = as_bf16x8(cat(h0, h1));
-                    zl[ks][vb] = as_bf16x8(cat(l0, l1));
-                }
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    if (32 * ks > 16 * tb + 15) continue;
-                    const bf16x8 wh = frag_perm(sm.pc.c + 0 * CH * ST, ST, 16 * tb + l16, 32 * ks, q4);
-                    const bf16x8 wl = frag_perm(sm.pc.c + 1 * CH * ST, ST, 16 * tb + l16, 32 * ks, q4);
-#pragma unroll
-                    for (int vb = 0; vb < VB; ++vb) {
-                        u[tb][vb] = mfma(wh, zh[ks][vb], u[tb][vb]);
-                        u[tb][vb] = mfma(wh, zl[ks][vb], u[tb][vb]);
-                        u[tb][vb] = mfma(wl, zh[ks][vb], u[tb][vb]);
-                    }
-                }
-            if constexpr (SEG) {
-                if (pb) {                        // U2 = -cW Z2, Z2 held in the O tiles
-#pragma unroll
-                    for (int ks = 0; ks < 2; ++ks)
+                    for (int ks = 0; ks < 2; ++ks) {
+                        if (32 * ks > 16 * tb + 15) continue;          // strictly above the diagonal
+                        const bf16x8 ch = frag_perm(sm.pc.c + 0 * CH * ST, ST, 16 * tb + l16, 32 * ks, q4);
+                        const bf16x8 cl = frag_perm(sm.pc.c + 1 * CH * ST, ST, 16 * tb + l16, 32 * ks, q4);
 #pragma unroll
                         for (int vb = 0; vb < VB; ++vb) {
-                            f32x4 n0 = o[vb][2 * ks], n1 = o[vb][2 * ks + 1];
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) { n0[r] = -n0[r]; n1[r] = -n1[r]; }
-                            uint2 h0, l0, h1, l1;
-                            split4(n0, h0, l0);
-                            split4(n1, h1, l1);
-                            zh[ks][vb] = as_bf16x8(cat(h0, h1));
-                            zl[ks][vb] = as_bf16x8(cat(l0, l1));
+                            acc[tb][vb] = mfma(ch, yh[ks][vb], acc[tb][vb]);
+                            acc[tb][vb] = mfma(ch, yl[ks][vb], acc[tb][vb]);
+                            acc[tb][vb] = mfma(cl, yh[ks][vb], acc[tb][vb]);
                         }
+                    }
+            };
+            make_y(z, true);
+            mul_cu(u);
+            if constexpr (SEG) {
+                if (pb) {                        // U2 = cU Y2, Z2 held in the O tiles
+                    f32x4 z2[4][VB];
 #pragma unroll
                     for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-                        for (int ks = 0; ks < 2; ++ks) {
-                            if (32 * ks > 16 * tb + 15) continue;
-                            const bf16x8 wh = frag_perm(sm.pc.c + 0 * CH * ST, ST, 16 * tb + l16, 32 * ks, q4);
-                            const bf16x8 wl = frag_perm(sm.pc.c + 1 * CH * ST, ST, 16 * tb + l16, 32 * ks, q4);
-#pragma unroll
-                            for (int vb = 0; vb < VB; ++vb) {
-                                u2[tb][vb] = mfma(wh, zh[ks][vb], u2[tb][vb]);
-                                u2[tb][vb] = mfma(wh, zl[ks][vb], u2[tb][vb]);
-                                u2[tb][vb] = mfma(wl, zh[ks][vb], u2[tb][vb]);
-                            }
-                        }
+                        for (int vb = 0; vb < VB; ++vb) z2[tb][vb] = o[vb][tb];
+                    make_y(z2, false);
+                    mul_cu(u2);
                 }
             }
         }
