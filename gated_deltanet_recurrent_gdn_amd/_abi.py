@@ -97,7 +97,7 @@ def load_library(path: str = None):
     lib.gdn_prefill_segmented_workspace_size.argtypes = [D, i32, i32, i32]
     lib.gdn_prefill_segmented_workspace_size.restype = sz
     lib.gdn_prefill_segmented.argtypes = [P, P, P, i32, P, P, G, P, i32, i32, P, P, i32, P, i32,
-                                          D, f32, i32, i32, P, sz, P, P]
+                                          D, f32, i32, i32, i32, P, sz, P, P]
     lib.gdn_mixed_workspace_size.argtypes = [D, i32, i32]
     lib.gdn_mixed_workspace_size.restype = sz
     lib.gdn_mixed_step.argtypes = [P, i32, P, P, i32, P, i32, i32, P, P, i32, P, P, i32, P, i32,
@@ -303,7 +303,7 @@ def gdn_prefill_segmented_workspace_size(dims: gdn_dims, n_seqs: int, total_toke
 
 
 def _prefill(fn, q, k, v, gb, gate, cu_seqlens, slot_idx, rec_state, out, dims, scale, flags,
-             workspace, err_flag, stream, seg_len=None):
+             workspace, err_flag, stream, seg_len=None, head_len=0):
     lib = load_library()
     T = q.shape[0]
     H, HV, dk, dv = dims.num_k_heads, dims.num_v_heads, dims.head_k_dim, dims.head_v_dim
@@ -329,7 +329,8 @@ def _prefill(fn, q, k, v, gb, gate, cu_seqlens, slot_idx, rec_state, out, dims, 
             _p(q), _p(k), _p(v), _dt(q), _p(gb[0]) if gate is None else None,
             _p(gb[1]) if gate is None else None, None if gs is None else ctypes.byref(gs),
             _p(cu_seqlens), n, T, _p(slot_idx), _p(rec_state), rec_state.shape[0], _p(out),
-            _dt(out), ctypes.byref(dims), float(scale), flags, int(seg_len), _p(workspace),
+            _dt(out), ctypes.byref(dims), float(scale), flags, int(seg_len), int(head_len),
+            _p(workspace),
             workspace.numel() * workspace.element_size(), _p(err_flag), _stream(stream))
         _check(fn, status)
         return out
@@ -364,14 +365,16 @@ def gdn_prefill_chunked_gated(q, k, v, gate: GateInputs, cu_seqlens, slot_idx, r
 
 def gdn_prefill_segmented(q, k, v, g, beta, cu_seqlens, slot_idx, rec_state, out,
                           dims: gdn_dims, scale, seg_len: int, flags=DEFAULT_PREFILL_FLAGS,
-                          gate: GateInputs = None, workspace=None, err_flag=None, stream=None):
-    """Segment-parallel prefill with seg_len-token segments (gdn.h:
-    gdn_prefill_segmented); with ``gate`` given, g and beta must be None."""
+                          gate: GateInputs = None, workspace=None, err_flag=None, stream=None,
+                          head_len: int = 0):
+    """Segment-parallel prefill (gdn.h: gdn_prefill_segmented): segment 0 of
+    head_len tokens (0: seg_len), then seg_len-token segments; with ``gate``
+    given, g and beta must be None."""
     if gate is not None and (g is not None or beta is not None):
         raise ValueError("pass either g and beta or gate")
     return _prefill("gdn_prefill_segmented", q, k, v, (g, beta), gate, cu_seqlens, slot_idx,
                     rec_state, out, dims, scale, flags, workspace, err_flag, stream,
-                    seg_len=seg_len)
+                    seg_len=seg_len, head_len=head_len)
 
 
 def gdn_mixed_workspace_size(dims: gdn_dims, n_dec: int, total_pre: int) -> int:

@@ -232,8 +232,8 @@ gdn_status prefill_impl(const void* q, const void* k, const void* v, gdn_dtype i
                         const int32_t* cu_seqlens, int32_t n_seqs, int32_t total_tokens,
                         const int32_t* slot_idx, float* rec_state, int32_t num_slots, void* out,
                         gdn_dtype out_dt, const gdn_dims* dims, float scale, int32_t flags,
-                        int32_t seg_len, void* workspace, size_t workspace_bytes,
-                        int32_t* err_flag, hipStream_t stream) {
+                        int32_t seg_len, int32_t head_len, void* workspace,
+                        size_t workspace_bytes, int32_t* err_flag, hipStream_t stream) {
     if (gdn_status st = check_flags(flags, GDN_FLAG_QK_L2NORM | GDN_FLAG_VALIDATE |
                                                GDN_FLAG_PREFILL_NS3 | GDN_FLAG_PREFILL_NS4 |
                                                GDN_FLAG_PREFILL_SEQUENTIAL,
@@ -251,8 +251,12 @@ gdn_status prefill_impl(const void* q, const void* k, const void* v, gdn_dtype i
     if (total_tokens > 0 && (!q || !k || !v || !out)) return GDN_ERR_NULL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(rec_state))
         return GDN_ERR_ALIGN;
-    if (seg_len > 0) {                           // explicit segment length
+    PrefillSchedule sch{0, 0, true};
+    if (seg_len > 0) {                           // explicit segment lengths
         if (seg_len % 64 != 0) return GDN_ERR_DIMS;
+        if (head_len == 0) head_len = seg_len;
+        if (head_len < seg_len || head_len % 64 != 0) return GDN_ERR_DIMS;
+        sch = PrefillSchedule{seg_len, head_len, true};
         if (flags & GDN_FLAG_PREFILL_SEQUENTIAL) return GDN_ERR_FLAGS;
         if ((total_tokens + seg_len - 1) / seg_len > 32768) return GDN_ERR_DIMS;
         if (n_seqs > 0 && total_tokens > 0) {
@@ -262,12 +266,11 @@ gdn_status prefill_impl(const void* q, const void* k, const void* v, gdn_dtype i
             if (!aligned16(workspace)) return GDN_ERR_ALIGN;
         }
     } else if (seg_len < 0) {                    // the plain call: segments when they pay
-        seg_len = (flags & GDN_FLAG_PREFILL_SEQUENTIAL)
-            ? 0 : prefill_auto_segment_len(*dims, n_seqs, total_tokens);
-        if (seg_len > 0 &&
+        if (!(flags & GDN_FLAG_PREFILL_SEQUENTIAL)) sch = prefill_auto_schedule(*dims, n_seqs, total_tokens);
+        if (sch.seg_len > 0 &&
             (!workspace || !aligned16(workspace) ||
-             workspace_bytes < prefill_segmented_workspace(*dims, n_seqs, total_tokens, seg_len)))
-            seg_len = 0;
+             workspace_bytes < prefill_segmented_workspace(*dims, n_seqs, total_tokens, sch.seg_len)))
+            sch = PrefillSchedule{0, 0, true};
     } else {
         return GDN_ERR_DIMS;
     }
@@ -278,10 +281,10 @@ gdn_status prefill_impl(const void* q, const void* k, const void* v, gdn_dtype i
     const int32_t* ef = (flags & GDN_FLAG_VALIDATE) ? err_flag : nullptr;
     const int32_t sqk = dims->num_k_heads * dims->head_k_dim;
     const int32_t sv = dims->num_v_heads * dims->head_v_dim;
-    if (seg_len > 0 && n_seqs > 0 && total_tokens > 0)
+    if (sch.seg_len > 0 && n_seqs > 0 && total_tokens > 0)
         GDN_TRY_LAUNCH(launch_prefill_segmented(q, k, v, in_dt, ga, cu_seqlens, n_seqs,
                                                 total_tokens, slot_idx, rec_state, out, out_dt,
-                                                *dims, sqk, sv, scale, flags, seg_len,
+                                                *dims, sqk, sv, scale, flags, sch,
                                                 static_cast<float*>(workspace), ef, s));
     else
         GDN_TRY_LAUNCH(launch_prefill(q, k, v, in_dt, ga, cu_seqlens, n_seqs, slot_idx,
@@ -365,7 +368,7 @@ size_t gdn_prefill_workspace_size(const gdn_dims* dims, int32_t n_seqs, int32_t 
     if (check_dims(dims) != GDN_OK || n_seqs <= 0 || total_tokens <= 0) return 0;
     if (dims->head_k_dim != dims->head_v_dim || dims->head_k_dim > 128) return 0;
     return prefill_segmented_workspace(*dims, n_seqs, total_tokens,
-                                       prefill_auto_segment_len(*dims, n_seqs, total_tokens));
+                                       prefill_auto_schedule(*dims, n_seqs, total_tokens).seg_len);
 }
 
 size_t gdn_prefill_segmented_workspace_size(const gdn_dims* dims, int32_t n_seqs,
@@ -381,14 +384,15 @@ gdn_status gdn_prefill_segmented(const void* q, const void* k, const void* v, gd
                                  const int32_t* cu_seqlens, int32_t n_seqs, int32_t total_tokens,
                                  const int32_t* slot_idx, float* rec_state, int32_t num_slots,
                                  void* out, gdn_dtype out_dt, const gdn_dims* dims, float scale,
-                                 int32_t flags, int32_t seg_len, void* workspace,
-                                 size_t workspace_bytes, int32_t* err_flag, hipStream_t stream) {
-    if (seg_len <= 0) return GDN_ERR_DIMS;
+                                 int32_t flags, int32_t seg_len, int32_t head_len,
+                                 void* workspace, size_t workspace_bytes, int32_t* err_flag,
+                                 hipStream_t stream) {
+    if (seg_len <= 0 || head_len < 0) return GDN_ERR_DIMS;
     if (gate && (g || beta)) return GDN_ERR_FLAGS;
     return prefill_impl(q, k, v, in_dt, gate ? nullptr : g, gate ? nullptr : beta, gate,
                         cu_seqlens, n_seqs, total_tokens, slot_idx, rec_state, num_slots, out,
-                        out_dt, dims, scale, flags, seg_len, workspace, workspace_bytes,
-                        err_flag, stream);
+                        out_dt, dims, scale, flags, seg_len, head_len, workspace,
+                        workspace_bytes, err_flag, stream);
 }
 
 gdn_status gdn_prefill_chunked(const void* q, const void* k, const void* v, gdn_dtype in_dt,
@@ -398,7 +402,7 @@ gdn_status gdn_prefill_chunked(const void* q, const void* k, const void* v, gdn_
                                const gdn_dims* dims, float scale, int32_t flags, void* workspace,
                                size_t workspace_bytes, int32_t* err_flag, hipStream_t stream) {
     return prefill_impl(q, k, v, in_dt, g, beta, nullptr, cu_seqlens, n_seqs, total_tokens,
-                        slot_idx, rec_state, num_slots, out, out_dt, dims, scale, flags, -1,
+                        slot_idx, rec_state, num_slots, out, out_dt, dims, scale, flags, -1, 0,
                         workspace, workspace_bytes, err_flag, stream);
 }
 
@@ -413,7 +417,7 @@ gdn_status gdn_prefill_chunked_gated(const void* q, const void* k, const void* v
     if (!gate) return GDN_ERR_NULL;
     return prefill_impl(q, k, v, in_dt, nullptr, nullptr, gate, cu_seqlens, n_seqs,
                         total_tokens, slot_idx, rec_state, num_slots, out, out_dt, dims, scale,
-                        flags, -1, workspace, workspace_bytes, err_flag, stream);
+                        flags, -1, 0, workspace, workspace_bytes, err_flag, stream);
 }
 
 size_t gdn_mixed_workspace_size(const gdn_dims* dims, int32_t n_dec, int32_t total_pre) {
@@ -497,14 +501,16 @@ gdn_status gdn_mixed_step(const void* x, gdn_dtype x_dt, const float* g, const f
         // whole runs overlapped with the decode measured faster.  The choice
         // depends on the call's arguments only (never on the streams given).
         const size_t base = gdn_mixed_workspace_size(dims, n_dec, total_pre);
-        int32_t seg = ((flags & GDN_FLAG_PREFILL_SEQUENTIAL) || beside_decode)
-                          ? 0 : prefill_auto_segment_len(*dims, n_pre, total_pre);
-        if (seg > 0 && workspace_bytes - base < prefill_segmented_workspace(*dims, n_pre, total_pre, seg))
-            seg = 0;
-        if (seg > 0)
+        PrefillSchedule sch{0, 0, true};
+        if (!(flags & GDN_FLAG_PREFILL_SEQUENTIAL) && !beside_decode)
+            sch = prefill_auto_schedule(*dims, n_pre, total_pre);
+        if (sch.seg_len > 0 &&
+            workspace_bytes - base < prefill_segmented_workspace(*dims, n_pre, total_pre, sch.seg_len))
+            sch = PrefillSchedule{0, 0, true};
+        if (sch.seg_len > 0)
             GDN_TRY_LAUNCH(launch_prefill_segmented(yp, yp + Hdk, yp + 2 * Hdk, GDN_BF16, gp, cu_seqlens,
                                                     n_pre, total_pre, sp, rec_state, op, out_dt, *dims,
-                                                    D, D, scale, flags & (GDN_FLAG_QK_L2NORM), seg,
+                                                    D, D, scale, flags & (GDN_FLAG_QK_L2NORM), sch,
                                                     reinterpret_cast<float*>(static_cast<char*>(workspace) + base),
                                                     ef, ps));
         else

@@ -91,29 +91,36 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, gdn_dtype
                           const gdn_dims& d, int32_t sqk, int32_t sv, float scale, int32_t flags,
                           const int32_t* err, hipStream_t st);
 
-// Segment-parallel prefill.  A sequence is cut into segments of seg_len
-// tokens (a multiple of the 64-token chunk, so the chunks are those of the
-// whole-sequence run).  A segment maps its start state affinely,
-// S_end = S_start P + B, with P the segment's run from the identity with v = 0
-// and B its run from the zero state.  Pass 1 runs, in parallel, segment 0 from
-// the slot's state (outputs written, end state kept) and every middle
-// segment's P and B runs (no outputs); a scan composes the start states; pass
-// 2 reruns segments 1.. from their start states with outputs, the last one
-// writing the slot.  The workspace holds three D x D fp32 matrices (start
-// state, P, B) per (segment id, value head); the segment id of segment j of
-// sequence n is n + cu[n] / seg_len + j, below n_seqs + total / seg_len + 1.
+// Segment-parallel prefill.  Segment 0 of a sequence is its first `head`
+// tokens, segments 1.. the following runs of seg_len tokens (head >= seg_len,
+// both multiples of the 64-token chunk, so the chunks are those of the
+// whole-sequence run; head == seg_len gives equal segments).  A segment maps
+// its start state affinely, S_end = S_start P + B, with P the segment's run
+// from the identity with v = 0 and B its run from the zero state.  Pass 1
+// runs, in parallel, segment 0 from the slot's state (outputs written, end
+// state kept) and every middle segment's P and B runs (no outputs); a scan
+// composes the start states; pass 2 reruns segments 1.. from their start
+// states with outputs, the last one writing the slot.  The workspace holds
+// three D x D fp32 matrices (start state, P, B) per (segment id, value head);
+// the segment id of segment j of sequence n is n + cu[n] / seg_len + j, below
+// n_seqs + total / seg_len + 1.
+struct PrefillSchedule {
+    int32_t seg_len;     // 0: whole sequences
+    int32_t head;        // tokens of segment 0 (>= seg_len)
+    bool paired;         // pass 1: a middle segment's P and B runs in one workgroup
+};
 int64_t prefill_segment_ids(int32_t n_seqs, int32_t total_tokens, int32_t seg_len);
 size_t prefill_segmented_workspace(const gdn_dims& d, int32_t n_seqs, int32_t total_tokens,
                                    int32_t seg_len);
-// Segment length the plain prefill call uses for these sizes (0: whole
+// Schedule the plain prefill call uses for these sizes (seg_len 0: whole
 // sequences), from a model of its workgroup rounds on the current device.
-int32_t prefill_auto_segment_len(const gdn_dims& d, int32_t n_seqs, int32_t total_tokens);
+PrefillSchedule prefill_auto_schedule(const gdn_dims& d, int32_t n_seqs, int32_t total_tokens);
 hipError_t launch_prefill_segmented(const void* q, const void* k, const void* v, gdn_dtype in_dt,
                                     const GateArgs& gate, const int32_t* cu, int32_t n_seqs,
                                     int32_t total_tokens, const int32_t* slot, float* rec,
                                     void* out, gdn_dtype out_dt, const gdn_dims& d,
                                     int32_t sqk, int32_t sv, float scale, int32_t flags,
-                                    int32_t seg_len, float* ws, const int32_t* err,
+                                    PrefillSchedule sch, float* ws, const int32_t* err,
                                     hipStream_t st);
 
 // Gated RMSNorm over rows of `dim` values (z has x's dtype; NULL = no gate).

@@ -291,19 +291,40 @@ constexpr int PF_NW = 8;                 // waves per workgroup
 constexpr int PF_NT = 64 * PF_NW;        // threads per workgroup
 
 // Which part of each sequence a launch walks.  Pass 0: whole sequences.
-// Segment passes (segments of seg_len tokens, a multiple of CH; blockIdx.z
-// picks the segment): pass 1 runs segment 0 from the slot's state (z = 0) and
-// each middle segment j (z = j) as a pair of runs in one workgroup, from the
-// zero state (its B) and from the identity with v = 0 (its P), both without
-// outputs; pass 2 reruns segment j = z + 1 from its composed start state.  ws
-// holds the D x D fp32 matrices [segment id][start, P, B][value head].
+// Segment passes (blockIdx.z picks the segment): segment 0 of a sequence is
+// its first `head` tokens and segments 1.. are the following runs of seg_len
+// tokens (head >= seg_len, both multiples of CH; a sequence of at most head
+// tokens is one segment).  Pass 1 runs segment 0 from the slot's state (z = 0)
+// and, for each middle segment j, its run from the zero state (its B) and its
+// run from the identity with v = 0 (its P), both without outputs: paired in
+// one workgroup (z = j; the P run's state is a second register array), or as
+// two workgroups (z = 2j - 1 the B run, z = 2j the P run; one state, so the
+// kernel keeps the registers of a whole-sequence run).  Pass 2 reruns segment
+// j = z + 1 from its composed start state.  ws holds the D x D fp32 matrices
+// [segment id][start, P, B][value head].
 struct SegArgs {
     float* ws;
     int32_t seg_len;
     int32_t pass;
+    int32_t head;
+    int32_t pair;        // pass 1: P and B runs paired in one workgroup
+    // Segment map (written by prefill_seg_map_kernel), so that the grid
+    // carries a bound on the real workgroup count instead of every sequence
+    // times the longest.  Pass 1: blockIdx.y < n_seqs is sequence blockIdx.y's
+    // segment 0 (all of them dispatched first, so that no P/B run takes a CU
+    // before every segment 0 has one); y = n_seqs + i indexes the P/B runs,
+    // sequence n owning i in [map[n], map[n + 1]) with z = 1 + i - map[n].
+    // Pass 2: sequence n owns y in [map[n], map[n + 1]), z = y - map[n].
+    const int32_t* map;
+    int32_t n_seqs;
 };
 
-template <int D, typename IT, typename OT, bool NSV, bool SEG>
+// Segments of a sequence of L tokens (head >= seg >= 1).
+__host__ __device__ inline int32_t seg_count(int32_t L, int32_t head, int32_t seg) {
+    return L <= head ? 1 : 1 + (L - head + seg - 1) / seg;
+}
+
+template <int D, typename IT, typename OT, bool NSV, bool SEG, bool PAIR>
 __global__ __launch_bounds__(PF_NT) void prefill_kernel(
     const IT* __restrict__ qg, const IT* __restrict__ kg, const IT* __restrict__ vg,
     const GateArgs ga, const int32_t* __restrict__ cu,
@@ -311,6 +332,7 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
     int32_t HV, int32_t sqk, int32_t sv, float scale, int32_t flags, int32_t ns_rounds,
     const SegArgs sg, const int32_t* __restrict__ err_flag) {
     constexpr bool SPL = sizeof(IT) == 4;        // fp32 inputs: hi/lo planes
+    constexpr bool PAIRED = SEG && PAIR;         // P and B runs share a workgroup
     constexpr int NP = SPL ? 2 : 1;
     static_assert(D == 32 || D == 64 || D == 128, "head dim");
     constexpr int NW = PF_NW;                    // waves
@@ -337,7 +359,27 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
             hv = G * (8 * (a / G) + b) + a % G;
         }
     }
-    const int n = blockIdx.y;
+    // the sequence and the segment index within its pass: from the grid, or,
+    // for segment passes, from the segment map (binary search)
+    int n = blockIdx.y;
+    int zseg = blockIdx.z;
+    if constexpr (SEG) {
+        int g = blockIdx.y;
+        if (sg.pass == 1 && g < sg.n_seqs) {
+            zseg = 0;                            // segment 0 of sequence g
+        } else {
+            const int base = sg.pass == 1 ? 1 : 0;
+            if (sg.pass == 1) g -= sg.n_seqs;
+            if (g >= sg.map[sg.n_seqs]) return;
+            int lo = 0, hi = sg.n_seqs;
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (sg.map[mid] <= g) lo = mid; else hi = mid;
+            }
+            n = lo;
+            zseg = base + g - sg.map[lo];
+        }
+    }
     const int h = hv / (HV / H);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -351,7 +393,7 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
     const bool vact = wave * VB * 16 < D;        // this wave owns value columns
 
     if (s <= 0) {                                // inactive: zero outputs, state untouched
-        if (SEG && (sg.pass == 2 || blockIdx.z != 0)) return;
+        if (SEG && (sg.pass == 2 || zseg != 0)) return;
         for (int64_t i = tid; i < static_cast<int64_t>(t1 - t0) * D; i += PF_NT) {
             const int64_t t = t0 + i / D;
             elem<OT>::st(out + (t * HV + hv) * D + i % D, 0.0f);
@@ -373,36 +415,51 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
     const float* init = S;
     float* fin = S;
     float* fin2 = nullptr;
-    bool wo = true, pb = false;
+    bool wo = true, pb = false, ident = false, use_v = true;
     if constexpr (SEG) {
         const int32_t seg = sg.seg_len;
-        const int32_t nseg = (t1 - t0 + seg - 1) / seg;
+        const int32_t nseg = seg_count(t1 - t0, sg.head, seg);
         const int64_t id0 = n + t0 / seg;        // segment id of the sequence's first segment
+        auto seg_start = [&](int j) { return j == 0 ? t0 : t0 + sg.head + (j - 1) * seg; };
         auto wsm = [&](int64_t id, int kind) {
             return sg.ws + ((id * 3 + kind) * HV + hv) * static_cast<size_t>(D) * D;
         };
-        const int z = blockIdx.z;
+        const int z = zseg;
         if (sg.pass == 1) {
             const int j = z;
             if (nseg <= 1) {
                 if (z != 0) return;              // one segment: the whole run, as pass 0
             } else if (j == 0) {
-                a1 = t0 + seg;
+                a1 = t0 + sg.head;
                 fin = wsm(id0 + 1, 0);           // start state of segment 1
-            } else {
+            } else if constexpr (PAIR) {
                 if (j > nseg - 2) return;
-                a0 = t0 + j * seg;
+                a0 = seg_start(j);
                 a1 = a0 + seg;
                 wo = false;
                 pb = true;
                 init = nullptr;
                 fin = wsm(id0 + j, 2);           // B: the run from zero
                 fin2 = wsm(id0 + j, 1);          // P: the run from the identity, v = 0
+            } else {
+                const int jj = (z + 1) / 2;      // z = 2 jj - 1: B run, z = 2 jj: P run
+                if (jj > nseg - 2) return;
+                a0 = seg_start(jj);
+                a1 = a0 + seg;
+                wo = false;
+                init = nullptr;
+                if (z & 1) {
+                    fin = wsm(id0 + jj, 2);      // B: the run from zero
+                } else {
+                    fin = wsm(id0 + jj, 1);      // P: the run from the identity, v = 0
+                    ident = true;
+                    use_v = false;
+                }
             }
         } else {
             const int j = z + 1;
             if (nseg <= 1 || j > nseg - 1) return;
-            a0 = t0 + j * seg;
+            a0 = seg_start(j);
             a1 = min(a0 + seg, t1);
             init = wsm(id0 + j, 0);
             fin = (j == nseg - 1) ? S : nullptr;
@@ -424,7 +481,13 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
                     const float4 x = *reinterpret_cast<const float4*>(init + static_cast<size_t>(v) * D + 16 * kb + 4 * q4);
                     st[kb][vb] = f32x4{x.x, x.y, x.z, x.w};
                 }
-                if constexpr (SEG) {
+                if constexpr (SEG && !PAIR) {
+                    if (ident) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) st[kb][vb][r] = (16 * kb + 4 * q4 + r == v) ? 1.0f : 0.0f;
+                    }
+                }
+                if constexpr (PAIRED) {
                     if (pb) {
 #pragma unroll
                         for (int r = 0; r < 4; ++r) st2[kb][vb][r] = (16 * kb + 4 * q4 + r == v) ? 1.0f : 0.0f;
@@ -504,7 +567,7 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
         // registers across it (the registers the paired P/B runs need).
         // Whole-sequence launches keep the hoisted addresses (faster there).
         int tid_o = static_cast<int>(threadIdx.x);
-        if constexpr (SEG) asm volatile("" : "+v"(tid_o));
+        if constexpr (PAIRED) asm volatile("" : "+v"(tid_o));
         const int tid = tid_o;
         const int lane = tid & 63;
         const int q4 = lane >> 4;
@@ -678,7 +741,7 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
                 bf16x8 ak[4], akl[4], bq[4], bql[4];
 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb) {
-                    if (dz || (SEG && doo && pb)) {
+                    if (dz || (PAIRED && doo && pb)) {
                         ak[tb] = frag_kq(sm.k[0], SK, 16 * tb + l16, 32 * ks, q4, swl);
                         if constexpr (SPL) akl[tb] = frag_kq(sm.k[NP - 1], SK, 16 * tb + l16, 32 * ks, q4, swl);
                     }
@@ -698,7 +761,7 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
                     sl[vb] = as_bf16x8(cat(l0, l1));
                 }
                 __builtin_amdgcn_sched_barrier(0);
-                if constexpr (SEG && doo) {
+                if constexpr (PAIRED && doo) {
                     // paired P run: its Z (from st2) accumulates in the O tiles,
                     // which a run without outputs does not use
                     if (pb) {
@@ -970,9 +1033,9 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
                         }
                     }
             };
-            make_y(z, true);
+            make_y(z, use_v);
             mul_cu(u);
-            if constexpr (SEG) {
+            if constexpr (PAIRED) {
                 if (pb) {                        // U2 = cU Y2, Z2 held in the O tiles
                     f32x4 z2[4][VB];
 #pragma unroll
@@ -1053,7 +1116,7 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
                     cl[ks][vb] = as_bf16x8(cat(l0, l1));
                 }
             bf16x8 c2h[2][VB], c2l[2][VB];       // the paired P run's cK . U2
-            if constexpr (SEG) {
+            if constexpr (PAIRED) {
                 if (pb) {
 #pragma unroll
                     for (int ks = 0; ks < 2; ++ks)
@@ -1094,7 +1157,7 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
                         if constexpr (SPL) acc = mfma(akl[ks], ch[ks][vb], acc);
                     }
                     st[kb][vb] = acc;
-                    if constexpr (SEG) {
+                    if constexpr (PAIRED) {
                         if (pb) {
                             f32x4 acc2 = st2[kb][vb];
                             acc2[0] *= egl; acc2[1] *= egl; acc2[2] *= egl; acc2[3] *= egl;
@@ -1116,7 +1179,7 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
 
     // ---- the paired P run's end state, then the final state back to the slot
     //      (or to the segment workspace)
-    if constexpr (SEG) {
+    if constexpr (PAIRED) {
         if (vact && pb) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
@@ -1155,11 +1218,16 @@ hipError_t run_prefill(const void* q, const void* k, const void* v, const GateAr
                       static_cast<OT*>(out), d.num_k_heads, d.num_v_heads, sqk, sv, scale, flags,
                       nsr, sg, err);
     };
+    // pass 2 never pairs runs: it takes the unpaired kernel, whose registers
+    // are those of a whole-sequence run
+    if (sg.pass == 1 && sg.pair)
+        return ns > 0 ? go(prefill_kernel<D, IT, OT, true, true, true>, ns)
+                      : go(prefill_kernel<D, IT, OT, false, true, true>, 0);
     if (sg.pass != 0)
-        return ns > 0 ? go(prefill_kernel<D, IT, OT, true, true>, ns)
-                      : go(prefill_kernel<D, IT, OT, false, true>, 0);
-    return ns > 0 ? go(prefill_kernel<D, IT, OT, true, false>, ns)
-                  : go(prefill_kernel<D, IT, OT, false, false>, 0);
+        return ns > 0 ? go(prefill_kernel<D, IT, OT, true, true, false>, ns)
+                      : go(prefill_kernel<D, IT, OT, false, true, false>, 0);
+    return ns > 0 ? go(prefill_kernel<D, IT, OT, true, false, false>, ns)
+                  : go(prefill_kernel<D, IT, OT, false, false, false>, 0);
 }
 
 template <int D, typename IT>
@@ -1205,7 +1273,7 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, gdn_dtype
     if (n_seqs == 0) return hipSuccess;
     if (!prefill_supported(d, in_dt)) return hipErrorInvalidValue;
     return prefill_pass(q, k, v, in_dt, ga, cu, n_seqs, slot, rec, out, out_dt, d, sqk, sv,
-                        scale, flags, SegArgs{nullptr, 0, 0}, 1, err, st);
+                        scale, flags, SegArgs{nullptr, 0, 0, 0, 0, nullptr, 0}, 1, err, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -1224,7 +1292,7 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, gdn_dtype
 template <int D>
 __global__ __launch_bounds__(256) void prefill_seg_scan_kernel(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ slot, int32_t HV, int32_t seg_len,
-    float* __restrict__ ws, const int32_t* __restrict__ err_flag) {
+    int32_t head, float* __restrict__ ws, const int32_t* __restrict__ err_flag) {
     constexpr int NTL = D / 16;                  // 16-column tiles
     constexpr int TPW = NTL >= 4 ? NTL / 4 : 1;  // tiles per wave
     constexpr int KT = D / 4;                    // inner steps per lane group
@@ -1234,7 +1302,7 @@ __global__ __launch_bounds__(256) void prefill_seg_scan_kernel(
     const int hv = blockIdx.x, n = blockIdx.y, rb = blockIdx.z;
     const int32_t t0 = cu[n], t1 = cu[n + 1];
     if (slot[n] <= 0 || t1 <= t0) return;
-    const int32_t nseg = (t1 - t0 + seg_len - 1) / seg_len;
+    const int32_t nseg = seg_count(t1 - t0, head, seg_len);
     if (nseg < 3) return;
     const int64_t id0 = n + t0 / seg_len;
     auto wsm = [&](int64_t id, int kind) {
@@ -1312,28 +1380,106 @@ int64_t prefill_segment_ids(int32_t n_seqs, int32_t total_tokens, int32_t seg_le
     return static_cast<int64_t>(n_seqs) + total_tokens / seg_len + 1;
 }
 
-size_t prefill_segmented_workspace(const gdn_dims& d, int32_t n_seqs, int32_t total_tokens,
-                                   int32_t seg_len) {
-    if (seg_len <= 0) return 0;
+// Bytes of the segment matrices; the two segment maps ([n_seqs + 1] int32
+// each) follow them.
+static size_t seg_matrix_bytes(const gdn_dims& d, int32_t n_seqs, int32_t total_tokens,
+                               int32_t seg_len) {
     const size_t mat = static_cast<size_t>(d.head_k_dim) * d.head_v_dim * sizeof(float);
     return static_cast<size_t>(prefill_segment_ids(n_seqs, total_tokens, seg_len)) * 3 *
            static_cast<size_t>(d.num_v_heads) * mat;
 }
 
-// Model (per-chunk workgroup time as the unit, one workgroup per CU, equal
-// sequence lengths): whole sequences take c = chunks per sequence; with m
-// segments of c/m chunks, pass 1 runs G (m - 1) workgroups (segment 0 and the
-// paired P/B runs, which take about 1.3 chunk-times per chunk) and pass 2
-// G (m - 1), G = sequences x value heads, each in ceil(count / CUs) rounds,
-// plus the scan's m - 2 steps at about a quarter chunk each.  The plain call
-// segments only where the model gains at least 15%.
-int32_t prefill_auto_segment_len(const gdn_dims& d, int32_t n_seqs, int32_t total_tokens) {
-    if (n_seqs <= 0 || total_tokens <= 0) return 0;
+size_t prefill_segmented_workspace(const gdn_dims& d, int32_t n_seqs, int32_t total_tokens,
+                                   int32_t seg_len) {
+    if (seg_len <= 0) return 0;
+    return seg_matrix_bytes(d, n_seqs, total_tokens, seg_len) +
+           ((2 * (static_cast<size_t>(n_seqs) + 1) * sizeof(int32_t) + 255) & ~static_cast<size_t>(255));
+}
+
+// Segment maps of the two passes: map1[n] / map2[n] = the workgroups of pass
+// 1 (P/B runs only: segment 0 of every sequence has a grid row of its own) /
+// pass 2 that sequences 0 .. n-1 own.  Pass 1: a sequence of nseg segments
+// owns its nseg - 2 middle segments' runs (one workgroup each when paired, two
+// otherwise); pass 2 its nseg - 1 reruns.  One workgroup: each thread counts a contiguous range of sequences,
+// then the partial sums are scanned in LDS (fixed order).
+__global__ __launch_bounds__(1024) void prefill_seg_map_kernel(
+    const int32_t* __restrict__ cu, int32_t n_seqs, int32_t head, int32_t seg, int32_t pair,
+    int32_t* __restrict__ map1, int32_t* __restrict__ map2, const int32_t* __restrict__ err_flag) {
+    __shared__ int32_t s1[1024], s2[1024];
+    if (call_rejected(err_flag)) return;
+    const int t = threadIdx.x;
+    const int per = (n_seqs + 1023) / 1024;
+    const int b0 = min(t * per, n_seqs), b1 = min(b0 + per, n_seqs);
+    auto counts = [&](int n, int32_t& c1, int32_t& c2) {
+        const int32_t L = cu[n + 1] - cu[n];
+        const int32_t m = L > 0 ? seg_count(L, head, seg) : 1;
+        c1 = m > 2 ? (pair ? 1 : 2) * (m - 2) : 0;
+        c2 = m - 1;
+    };
+    int32_t a1 = 0, a2 = 0;
+    for (int n = b0; n < b1; ++n) {
+        int32_t c1, c2;
+        counts(n, c1, c2);
+        a1 += c1;
+        a2 += c2;
+    }
+    s1[t] = a1;
+    s2[t] = a2;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {     // inclusive scan (Hillis-Steele)
+        const int32_t v1 = t >= off ? s1[t - off] : 0;
+        const int32_t v2 = t >= off ? s2[t - off] : 0;
+        __syncthreads();
+        s1[t] += v1;
+        s2[t] += v2;
+        __syncthreads();
+    }
+    int32_t r1 = t > 0 ? s1[t - 1] : 0, r2 = t > 0 ? s2[t - 1] : 0;
+    for (int n = b0; n < b1; ++n) {
+        map1[n] = r1;
+        map2[n] = r2;
+        int32_t c1, c2;
+        counts(n, c1, c2);
+        r1 += c1;
+        r2 += c2;
+    }
+    if (t == 1023) {
+        map1[n_seqs] = s1[1023];
+        map2[n_seqs] = s2[1023];
+    }
+}
+
+// The schedule the plain prefill call takes for these sizes on the current
+// device (seg_len 0: whole sequences).  Units of the model are chunk-times of
+// one workgroup per CU.
+//  * Few (sequence, value head) runs (G = n_seqs HV at most half the CUs):
+//    equal segments.  Whole sequences take c chunk-times (c = chunks per
+//    sequence); with m segments of c / m chunks, pass 1 runs G (m - 1)
+//    workgroups (segment 0 and the paired P/B runs, about 1.3 chunk-times per
+//    chunk) and pass 2 G (m - 1), each in ceil(count / CUs) rounds, plus the
+//    scan's m - 2 steps at about a quarter chunk each; the call segments where
+//    that gains at least 15%.
+//  * A busy chip: a head of the chunks a CU carries when the work is spread
+//    evenly (C = ceil(chunks x HV / CUs), chunks estimated as total / 64 plus
+//    half a chunk per sequence) and tail segments of about C / 4 chunks.  A
+//    sequence no longer than the head is one segment and runs whole in pass 1,
+//    so equal lengths keep whole runs; the tails of longer sequences get their
+//    P/B runs (as separate workgroups, which keep the registers of a whole run,
+//    on the CUs that shorter sequences free during pass 1), and reruns about
+//    C / 4 chunks long in pass 2.
+PrefillSchedule prefill_auto_schedule(const gdn_dims& d, int32_t n_seqs, int32_t total_tokens) {
+    if (n_seqs <= 0 || total_tokens <= 0) return PrefillSchedule{0, 0, true};
     const int64_t groups = static_cast<int64_t>(n_seqs) * d.num_v_heads;
     const int64_t cus = cu_count();
-    if (groups * 2 > cus) return 0;              // the chip is at least half busy already
+    if (groups * 2 > cus) {
+        const int64_t chunks = (static_cast<int64_t>(total_tokens) + 63) / 64 + (n_seqs + 1) / 2;
+        const int64_t bal = (chunks * d.num_v_heads + cus - 1) / cus;
+        if (bal < 8) return PrefillSchedule{0, 0, true};
+        const int64_t tail = (bal + 3) / 4;
+        return PrefillSchedule{static_cast<int32_t>(64 * tail), static_cast<int32_t>(64 * bal), false};
+    }
     const int64_t chunks = (total_tokens / n_seqs + 63) / 64;
-    if (chunks < 8) return 0;
+    if (chunks < 8) return PrefillSchedule{0, 0, true};
     double best = static_cast<double>(chunks);
     int32_t best_len = 0;
     for (int64_t m = 3; m <= 64; ++m) {
@@ -1345,7 +1491,7 @@ int32_t prefill_auto_segment_len(const gdn_dims& d, int32_t n_seqs, int32_t tota
         const double t = static_cast<double>(per) * (1.3 * r1 + r2) + 0.25 * (mm - 2);
         if (t < best * 0.999) { best = t; best_len = static_cast<int32_t>(per * 64); }
     }
-    return (best <= 0.85 * chunks) ? best_len : 0;
+    return (best <= 0.85 * chunks) ? PrefillSchedule{best_len, best_len, true} : PrefillSchedule{0, 0, true};
 }
 
 hipError_t launch_prefill_segmented(const void* q, const void* k, const void* v, gdn_dtype in_dt,
@@ -1353,28 +1499,44 @@ hipError_t launch_prefill_segmented(const void* q, const void* k, const void* v,
                                     int32_t total_tokens, const int32_t* slot, float* rec,
                                     void* out, gdn_dtype out_dt, const gdn_dims& d,
                                     int32_t sqk, int32_t sv, float scale, int32_t flags,
-                                    int32_t seg_len, float* ws, const int32_t* err,
+                                    PrefillSchedule sch, float* ws, const int32_t* err,
                                     hipStream_t st) {
     if (n_seqs == 0) return hipSuccess;
-    if (!prefill_supported(d, in_dt) || seg_len <= 0 || seg_len % CH != 0)
+    const int32_t seg_len = sch.seg_len, head = sch.head, pair = sch.paired ? 1 : 0;
+    if (!prefill_supported(d, in_dt) || seg_len <= 0 || seg_len % CH != 0 || head < seg_len ||
+        head % CH != 0)
         return hipErrorInvalidValue;
-    // segments of the longest possible sequence (all tokens in one)
-    const int32_t smax = total_tokens > 0 ? (total_tokens + seg_len - 1) / seg_len : 1;
-    const int32_t nz1 = smax >= 2 ? smax - 1 : 1;   // segment 0 and the paired middle segments
-    if (nz1 > 65535) return hipErrorInvalidValue;
-    hipError_t e = prefill_pass(q, k, v, in_dt, ga, cu, n_seqs, slot, rec, out, out_dt, d, sqk,
-                                sv, scale, flags, SegArgs{ws, seg_len, 1}, nz1, err, st);
-    if (e != hipSuccess || smax < 2) return e;
-    if (smax >= 3) {
+    // bounds on the workgroups of each pass over all sequences: a sequence of
+    // L > head tokens has nseg - 1 = ceil((L - head) / seg_len) <= L / seg_len + 1
+    // segments past the first
+    const int64_t rest = static_cast<int64_t>(total_tokens) / seg_len + n_seqs;
+    const int64_t g1 = n_seqs + (pair ? 1 : 2) * rest;
+    const int64_t g2 = rest;
+    if (g1 > 65535) return hipErrorInvalidValue;
+    int32_t* map1 = reinterpret_cast<int32_t*>(
+        reinterpret_cast<char*>(ws) + seg_matrix_bytes(d, n_seqs, total_tokens, seg_len));
+    int32_t* map2 = map1 + (n_seqs + 1);
+    hipError_t e = launch(prefill_seg_map_kernel, dim3(1), dim3(1024), 0, st, cu, n_seqs, head,
+                          seg_len, pair, map1, map2, err);
+    if (e != hipSuccess) return e;
+    // the pass kernels take the sequence count as the grid's y extent for
+    // whole runs; segment passes index the map with blockIdx.y instead
+    e = prefill_pass(q, k, v, in_dt, ga, cu, static_cast<int32_t>(g1), slot, rec, out, out_dt, d,
+                     sqk, sv, scale, flags, SegArgs{ws, seg_len, 1, head, pair, map1, n_seqs}, 1,
+                     err, st);
+    if (e != hipSuccess) return e;
+    {
         const int D = d.head_k_dim;
         const dim3 grid(d.num_v_heads, n_seqs, D / 16);
-        if (D == 32) e = launch(prefill_seg_scan_kernel<32>, grid, dim3(256), 0, st, cu, slot, d.num_v_heads, seg_len, ws, err);
-        else if (D == 64) e = launch(prefill_seg_scan_kernel<64>, grid, dim3(256), 0, st, cu, slot, d.num_v_heads, seg_len, ws, err);
-        else e = launch(prefill_seg_scan_kernel<128>, grid, dim3(256), 0, st, cu, slot, d.num_v_heads, seg_len, ws, err);
+        if (D == 32) e = launch(prefill_seg_scan_kernel<32>, grid, dim3(256), 0, st, cu, slot, d.num_v_heads, seg_len, head, ws, err);
+        else if (D == 64) e = launch(prefill_seg_scan_kernel<64>, grid, dim3(256), 0, st, cu, slot, d.num_v_heads, seg_len, head, ws, err);
+        else e = launch(prefill_seg_scan_kernel<128>, grid, dim3(256), 0, st, cu, slot, d.num_v_heads, seg_len, head, ws, err);
         if (e != hipSuccess) return e;
     }
-    return prefill_pass(q, k, v, in_dt, ga, cu, n_seqs, slot, rec, out, out_dt, d, sqk, sv,
-                        scale, flags, SegArgs{ws, seg_len, 2}, smax - 1, err, st);
+    if (g2 <= 0) return hipSuccess;
+    return prefill_pass(q, k, v, in_dt, ga, cu, static_cast<int32_t>(g2), slot, rec, out, out_dt,
+                        d, sqk, sv, scale, flags, SegArgs{ws, seg_len, 2, head, 0, map2, n_seqs},
+                        1, err, st);
 }
 
 }  // namespace gdn

@@ -274,9 +274,15 @@ gdn_status gdn_decode_recurrent(const void* qkv, gdn_dtype qkv_dt,
  * gdn_prefill_workspace_size -- bytes of device workspace with which
  * gdn_prefill_chunked(_gated) runs the segment-parallel schedule (see
  * gdn_prefill_segmented) for n_seqs sequences and total_tokens tokens on the
- * current device; 0 when those sizes run whole sequences (the chip is already
- * busy with one workgroup per (sequence, value head), or the sequences are
- * short) and for unsupported dims.
+ * current device; 0 when those sizes run whole sequences (the sequences are
+ * short) and for unsupported dims.  The schedule depends on the sizes only:
+ *   - few (sequence, value head) runs (n_seqs * HV at most half the compute
+ *     units): equal segments, where a model of the workgroup rounds gains;
+ *   - a busy chip: segment 0 of each sequence is a head of the chunks a
+ *     compute unit carries when the work is spread evenly, and the tokens past
+ *     it form segments of about a quarter of that; sequences no longer than
+ *     the head run whole, so equal lengths keep whole runs, while the tails of
+ *     longer ones run in parallel on the units shorter ones free.
  */
 size_t gdn_prefill_workspace_size(const gdn_dims* dims, int32_t n_seqs, int32_t total_tokens);
 
@@ -331,8 +337,11 @@ gdn_status gdn_prefill_chunked(const void* q, const void* k, const void* v, gdn_
 
 /*
  * gdn_prefill_segmented -- gdn_prefill_chunked with the sequences cut into
- * segments of seg_len tokens (a positive multiple of 64, so the segments are
- * runs of whole 64-token chunks) that are processed in parallel.  A segment
+ * segments that are processed in parallel: segment 0 is the first head_len
+ * tokens of the sequence and segments 1.. the following runs of seg_len
+ * tokens (both multiples of 64, so the segments are runs of whole 64-token
+ * chunks; head_len 0 means seg_len; a sequence of at most head_len tokens is
+ * one segment and runs whole).  A segment
  * maps its start state affinely: S_end = S_start P + B, where P is the
  * segment's run from the identity with v = 0 and B its run from the zero state
  * (the token update multiplies the state on the right by
@@ -349,6 +358,8 @@ gdn_status gdn_prefill_chunked(const void* q, const void* k, const void* v, gdn_
  *                  gdn_prefill_chunked_gated); GDN_ERR_FLAGS if both
  *   seg_len        tokens per segment: GDN_ERR_DIMS unless a positive multiple
  *                  of 64 (and at most 32768 segments of total_tokens)
+ *   head_len       tokens of segment 0: 0 (= seg_len) or a multiple of 64 of
+ *                  at least seg_len (GDN_ERR_DIMS otherwise)
  *   workspace      >= gdn_prefill_segmented_workspace_size(dims, n_seqs,
  *                  total_tokens, seg_len) bytes of device memory, 16-byte
  *                  aligned: three dv x dk fp32 matrices per (segment id, value
@@ -366,7 +377,8 @@ gdn_status gdn_prefill_segmented(const void* q, const void* k, const void* v, gd
                                  float* rec_state, int32_t num_slots,
                                  void* out, gdn_dtype out_dt,
                                  const gdn_dims* dims, float scale, int32_t flags,
-                                 int32_t seg_len, void* workspace, size_t workspace_bytes,
+                                 int32_t seg_len, int32_t head_len,
+                                 void* workspace, size_t workspace_bytes,
                                  int32_t* err_flag, hipStream_t stream);
 
 /*

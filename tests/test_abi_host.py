@@ -240,10 +240,10 @@ def test_prefill_rejects_both_newton_schulz_variants(lib):
 
 
 def _segmented(lib, seg_len=128, flags=2, g=FAKE, beta=FAKE, gate=None, ws=FAKE,
-               ws_bytes=1 << 34, total=256):
+               ws_bytes=1 << 34, total=256, head=0):
     return lib.gdn_prefill_segmented(FAKE, FAKE, FAKE, 1, g, beta, gate, FAKE, 1, total, FAKE,
-                                     FAKE, 8, FAKE, 1, _dims(), 0.1, flags, seg_len, ws, ws_bytes,
-                                     None, None)
+                                     FAKE, 8, FAKE, 1, _dims(), 0.1, flags, seg_len, head, ws,
+                                     ws_bytes, None, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -252,6 +252,9 @@ def _segmented(lib, seg_len=128, flags=2, g=FAKE, beta=FAKE, gate=None, ws=FAKE,
     (dict(ws=None), ERR_WS), (dict(ws_bytes=1024), ERR_WS), (dict(ws=MISALIGNED), ERR_ALIGN),
     (dict(g=None), ERR_NULL), (dict(gate="both"), ERR_FLAGS),
     (dict(seg_len=64, total=64 * 32769), ERR_DIMS),   # more than 32768 segments
+    (dict(head=64), ERR_DIMS),                     # head shorter than the segments
+    (dict(head=200), ERR_DIMS),                    # head not a multiple of 64
+    (dict(head=-64), ERR_DIMS),
 ])
 def test_prefill_segmented_rejects(lib, kw, code):
     if kw.get("gate") == "both":
@@ -262,20 +265,25 @@ def test_prefill_segmented_rejects(lib, kw, code):
 def test_prefill_segmented_empty_is_ok(lib):
     # no sequences and no tokens: nothing to run, so no workspace is needed
     assert lib.gdn_prefill_segmented(None, None, None, 1, None, None, None, None, 0, 0, None,
-                                     None, 8, None, 1, _dims(), 0.1, 2, 128, None, 0, None,
+                                     None, 8, None, 1, _dims(), 0.1, 2, 128, 0, None, 0, None,
                                      None) == OK
 
 
 def test_prefill_workspace_sizes(lib):
     d = gdn.make_dims(16, 32, 128, 128, 4)
     mats = 3 * 32 * 128 * 128 * 4                 # start state, P, B per value head
-    assert gdn.gdn_prefill_segmented_workspace_size(d, 1, 16384, 2048) == (1 + 8 + 1) * mats
-    assert gdn.gdn_prefill_segmented_workspace_size(d, 8, 24674, 2048) == (8 + 12 + 1) * mats
+    maps = 256                                    # the two segment maps, rounded up
+    assert gdn.gdn_prefill_segmented_workspace_size(d, 1, 16384, 2048) == (1 + 8 + 1) * mats + maps
+    assert gdn.gdn_prefill_segmented_workspace_size(d, 8, 24674, 2048) == (8 + 12 + 1) * mats + maps
     assert gdn.gdn_prefill_segmented_workspace_size(d, 1, 16384, 100) == 0
     assert gdn.gdn_prefill_segmented_workspace_size(gdn.make_dims(16, 32, 256, 256, 4), 1, 64, 64) == 0
-    # eight sequences x 32 value heads fill a 256-CU chip: whole-sequence runs
-    assert gdn.gdn_prefill_workspace_size(d, 8, 24674) == 0
+    # eight sequences x 32 value heads fill a 256-CU chip (the host fallback
+    # count without a GPU): a head of ceil((386 + 4) x 32 / 256) = 49 chunks and
+    # tail segments of 13 chunks (832 tokens), 8 + 24674 // 832 + 1 segment ids
+    assert gdn.gdn_prefill_workspace_size(d, 8, 24674) == (8 + 29 + 1) * mats + maps
+    # a busy chip with short sequences keeps whole runs (head under 8 chunks)
+    assert gdn.gdn_prefill_workspace_size(d, 8, 1600) == 0
     # one long sequence leaves most of the chip idle: the call asks for segments
     ws = gdn.gdn_prefill_workspace_size(d, 1, 16384)
-    assert ws > 0 and ws % mats == 0
+    assert ws > 0 and (ws - maps) % mats == 0
     assert gdn.gdn_prefill_workspace_size(d, 1, 256) == 0     # too short to pay

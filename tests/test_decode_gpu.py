@@ -5,7 +5,8 @@ Bars: o and the fp32 state at max|err| / max|ref| <= 1e-5; the conv cache roll
 and every untouched slot bit-exact.  Shapes: the tiny fp32 case (H=2, HV=4,
 d=32), the Qwen3-Next-like buckets B = 1..16 over a 256-slot cache, and the
 large batches B = 256 / 1024 over a 2048-slot cache (sampled rows checked
-against the oracle one by one; every row checked for the slot contract).
+against the oracle one by one; every row checked for the slot contract; at
+B = 256 every row is also checked against the oracle).
 """
 import math
 
@@ -119,6 +120,23 @@ def test_decode_large_batch_sampled(large_cache, B, path):
     rows = sorted(rng.choice(B, 48, replace=False).tolist())
     _check_rows(d, g, out, rows, 128 ** -0.5)
     assert torch.isfinite(out).all()
+    assert _untouched(d["rec_state"], g["rec_state"], d["slot_idx"].tolist())
+    del g
+    torch.cuda.empty_cache()
+
+
+def test_decode_batch256_every_row(large_cache):
+    """The batch-256 workload (seed 2, 2048-slot cache): every row's output,
+    recurrent state and conv roll against the oracle (checked 64 rows at a
+    time), on the library's default path."""
+    B = 256
+    d = {k: (v[:B] if k in ("mixed_qkv", "g", "beta", "slot_idx") else v)
+         for k, v in large_cache.items()}
+    g = to_dev(d)
+    out = run_decode_gpu(g, 128 ** -0.5)
+    torch.cuda.synchronize()
+    for r0 in range(0, B, 64):
+        _check_rows(d, g, out, list(range(r0, r0 + 64)), 128 ** -0.5)
     assert _untouched(d["rec_state"], g["rec_state"], d["slot_idx"].tolist())
     del g
     torch.cuda.empty_cache()

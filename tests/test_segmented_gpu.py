@@ -35,14 +35,14 @@ def _dims(p):
 
 
 def run_segmented(g, scale, seg_len, out_dtype=torch.bfloat16, flags=gdn.FLAG_QK_L2NORM,
-                  err_flag=None, gate=None):
+                  err_flag=None, gate=None, head_len=0):
     dm = g["dims"]
     T = g["q"].shape[0]
     out = torch.full((T, dm["HV"], dm["dv"]), float("nan"), dtype=out_dtype, device="cuda")
     gdn.gdn_prefill_segmented(g["q"], g["k"], g["v"], None if gate else g["g"],
                               None if gate else g["beta"], g["cu_seqlens"], g["slot_idx"],
                               g["rec_state"], out, _dims(g), scale, seg_len, flags=flags,
-                              gate=gate, err_flag=err_flag)
+                              gate=gate, err_flag=err_flag, head_len=head_len)
     return out
 
 
@@ -70,6 +70,64 @@ def test_segmented_matches_oracle(seg_len, d, in_dtype):
     assert torch.isfinite(out).all()
     eo, es = check_heads(p, g, out, list(range(4)), d ** -0.5)
     print(f"segmented seg={seg_len} d={d} in={in_dtype}: out {eo:.2e} state {es:.2e}")
+
+
+@pytest.mark.parametrize("seg_len,head_len", [(64, 128), (64, 192), (128, 256), (64, 384)])
+def test_head_and_tail_segments_match_oracle(seg_len, head_len):
+    """Segment 0 longer than the rest: sequences no longer than the head run
+    whole, longer ones get tail segments (zero to five of them here, so the
+    scan runs zero to three steps).  A slow decay keeps each segment's start
+    state visible at its end, so the composition matters."""
+    p = gi.prefill_inputs(LENGTHS, 16, H=2, HV=4, dk=64, dv=64, seed=23, state_std=0.1,
+                          g_mode="softplus")
+    p["g"] *= 0.02
+    g = to_dev(p)
+    out = run_segmented(g, 64 ** -0.5, seg_len, out_dtype=torch.float32, head_len=head_len)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    eo, es = check_heads(p, g, out, list(range(4)), 64 ** -0.5)
+    print(f"head {head_len} seg {seg_len}: out {eo:.2e} state {es:.2e}")
+
+
+def test_head_covering_every_sequence_is_the_whole_run_bitwise():
+    """With every sequence no longer than the head, each is one segment: the
+    first pass is the whole-sequence run, bitwise."""
+    p = gi.prefill_inputs(LENGTHS, 16, H=2, HV=4, dk=64, dv=64, seed=24, g_mode="softplus")
+    ga, gb = to_dev(p), to_dev(p)
+    oa = run_segmented(ga, 0.125, 64, head_len=384)
+    ob = run_whole(gb, 0.125)
+    torch.cuda.synchronize()
+    assert torch.equal(oa, ob)
+    assert torch.equal(ga["rec_state"], gb["rec_state"])
+
+
+def test_busy_chip_tail_schedule_matches_oracle():
+    """The plain call's own schedule on a busy chip (8 sequences x 32 value
+    heads, skewed lengths, its workspace given): a head of the balanced
+    per-unit chunk count, tails of the longer sequences in parallel.  Against
+    the oracle on sampled heads with a slow decay (so the tails' composed start
+    states matter), and within the bar of whole-sequence runs."""
+    lengths = [1800, 200, 1700, 150, 2300, 100, 1300, 2200]
+    p = gi.prefill_inputs(lengths, 10, seed=25)
+    p["g"] *= 0.02
+    dims = gdn.make_dims(16, 32, 128, 128, 4)
+    T = sum(lengths)
+    ws_bytes = gdn.gdn_prefill_workspace_size(dims, len(lengths), T)
+    if ws_bytes == 0:
+        pytest.skip("this device runs the workload whole (fewer than 512 CUs busy is assumed)")
+    ga, gb = to_dev(p), to_dev(p)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    oa = torch.full((T, 32, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    gdn.gdn_prefill_chunked(ga["q"], ga["k"], ga["v"], ga["g"], ga["beta"], ga["cu_seqlens"],
+                            ga["slot_idx"], ga["rec_state"], oa, dims, 128 ** -0.5,
+                            flags=gdn.FLAG_QK_L2NORM, workspace=ws)
+    ob = run_whole(gb, 128 ** -0.5)
+    torch.cuda.synchronize()
+    assert torch.isfinite(oa).all()
+    assert not torch.equal(oa, ob), "the tail schedule did not run"
+    assert rel_err(f64(oa), f64(ob)) <= PREFILL_TOL
+    eo, es = check_heads(p, ga, oa, [0, 19, 31], 128 ** -0.5)
+    print(f"busy-chip tail schedule: out {eo:.2e} state {es:.2e}")
 
 
 def test_segmented_d128_matches_oracle_and_whole_runs():
