@@ -75,15 +75,18 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_step_kernel_b256_traffic.t
 DECODE_SRC = os.path.join(ROOT, "gated_deltanet_recurrent_gdn_amd", "csrc", "decode.hip")
 
 
-PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_kernel_varlen_traffic.txt")
+PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_call_varlen_traffic.txt")
 PREFILL_SRC = os.path.join(ROOT, "gated_deltanet_recurrent_gdn_amd", "csrc", "prefill.hip")
+CONV_COUNTER_FILE = os.path.join(ROOT, "profiles", "conv_varlen_tok_kernel_valu.txt")
+CONV_SRC = os.path.join(ROOT, "gated_deltanet_recurrent_gdn_amd", "csrc", "conv.hip")
+# vector ALU issue peak: 256 CUs x 4 SIMDs, one wave64 instruction per SIMD every
+# 4 cycles (16 lanes wide), 2.4 GHz
+VALU_PEAK_WAVE_INSTS = 256 * 2.4e9
 
 
-def measured_traffic(path=TRAFFIC_FILE, src_path=DECODE_SRC, key="decode_hip_sha256"):
-    """HBM bytes per launch from a committed counter summary (FETCH_SIZE +
-    WRITE_SIZE, copy-calibrated) -- by default the fused step kernel at batch
-    256 -- or None when the kernel's source has changed since those counters
-    were taken."""
+def counter_summary(path, src_path, key):
+    """The key = value lines of a committed counter summary, or None when the
+    kernel's source has changed since those counters were taken."""
     import hashlib
     try:
         kv = {}
@@ -92,11 +95,37 @@ def measured_traffic(path=TRAFFIC_FILE, src_path=DECODE_SRC, key="decode_hip_sha
                 k, v = line.split("=", 1)
                 kv[k.strip()] = v.strip()
         src = hashlib.sha256(open(src_path, "rb").read()).hexdigest()
-        if kv.get(key) != src:
-            return None
-        return int(kv["fetch_bytes_per_launch"]) + int(kv["write_bytes_per_launch"])
-    except (OSError, KeyError, ValueError):
+        return kv if kv.get(key) == src else None
+    except OSError:
         return None
+
+
+def measured_traffic(path=TRAFFIC_FILE, src_path=DECODE_SRC, key="decode_hip_sha256"):
+    """HBM bytes per launch from a committed counter summary (FETCH_SIZE +
+    WRITE_SIZE, copy-calibrated) -- by default the fused step kernel at batch
+    256 -- or None when the kernel's source has changed since those counters
+    were taken."""
+    kv = counter_summary(path, src_path, key)
+    try:
+        return int(kv["fetch_bytes_per_launch"]) + int(kv["write_bytes_per_launch"])
+    except (TypeError, KeyError, ValueError):
+        return None
+
+
+def conv_roofline(ms):
+    """The varlen conv against the vector ALU issue peak: wave64 VALU
+    instructions per call from the committed counter summary (SQ_INSTS_VALU of
+    conv_varlen_tok_kernel) over the call's live mean time (which also holds the
+    small roll kernel), or None when conv.hip has changed since."""
+    kv = counter_summary(CONV_COUNTER_FILE, CONV_SRC, "conv_hip_sha256")
+    if kv is None:
+        return None
+    insts = float(kv["valu_wave_insts_per_launch"])
+    rate = insts / (ms * 1e-3)
+    return {"bound": "alu", "kernel": "conv_varlen_tok_kernel",
+            "achieved": round(rate / 1e9, 1), "peak": round(VALU_PEAK_WAVE_INSTS / 1e9, 1),
+            "unit": "G wave64 VALU instructions/s", "frac": round(rate / VALU_PEAK_WAVE_INSTS, 4),
+            "traffic": int(kv["fetch_bytes_per_launch"]) + int(kv["write_bytes_per_launch"])}
 
 
 def parse():
@@ -276,6 +305,11 @@ class PrefillSetup:
         self.err = torch.zeros(1, dtype=torch.int32, device=dev)
         self.gate = None
         self.i = 0
+        # the workspace with which the call takes the schedule it picks for
+        # these sizes (on a busy chip: heads plus tail segments)
+        self.ws = torch.empty(max(1, gdn.gdn_prefill_workspace_size(self.dims, 8, self.T)),
+                              dtype=torch.uint8, device=dev)
+        self.whole = False
 
     def rotate(self):
         """Move to the next input set (and its output buffer)."""
@@ -293,15 +327,26 @@ class PrefillSetup:
         self.rotate()
         p = self.p
         flags = gdn.FLAG_QK_L2NORM | (gdn.FLAG_VALIDATE if validate else 0)
+        if self.whole:
+            flags |= gdn.FLAG_PREFILL_SEQUENTIAL
         if self.gate is not None:
             gdn.gdn_prefill_chunked_gated(p["q"], p["k"], p["v"], self.gate, p["cu_seqlens"],
                                           p["slot_idx"], p["rec_state"], self.out, self.dims,
-                                          DK ** -0.5, flags=flags,
+                                          DK ** -0.5, flags=flags, workspace=self.ws,
                                           err_flag=self.err if validate else None)
             return
         gdn.gdn_prefill_chunked(p["q"], p["k"], p["v"], p["g"], p["beta"], p["cu_seqlens"],
                                 p["slot_idx"], p["rec_state"], self.out, self.dims, DK ** -0.5,
-                                flags=flags, err_flag=self.err if validate else None)
+                                flags=flags, workspace=self.ws,
+                                err_flag=self.err if validate else None)
+
+    def step_whole(self):
+        """The same call with GDN_FLAG_PREFILL_SEQUENTIAL: one run per (sequence, value head)."""
+        self.whole = True
+        try:
+            self.step()
+        finally:
+            self.whole = False
 
 
 def time_graph(torch, graph, per_replay, steps, warmup, min_replays=5):
@@ -522,8 +567,12 @@ def main():
         bucket_sets[1024] = nsets
         del gph, huge
         torch.cuda.synchronize()
-    # prefill, eager (one call is milliseconds)
-    ms_pre = time_loop(torch, lambda: pre.step(args.validate), args.steps, args.warmup)
+    # prefill, eager (one call is milliseconds): the call's own schedule, and
+    # whole runs alternating with it
+    ms_pre, ms_pre_whole = [], []
+    for _ in range(2):
+        ms_pre += time_loop(torch, lambda: pre.step(args.validate), max(2, args.steps // 2), args.warmup)
+        ms_pre_whole += time_loop(torch, pre.step_whole, max(2, args.steps // 2), args.warmup)
     # the headline step's kernel alone (the fused step at batch 256), eager
     # launches bracketed by events on the stream they run on
     ms_step_k = time_loop(torch, big.step, args.steps, args.warmup)
@@ -628,14 +677,22 @@ def main():
         "prefill_ms_mean": round(pre_ms, 4), "prefill_ms_min": round(min(ms_pre), 4),
         "prefill_tokens_per_s": round(pre_tps, 1),
         "prefill_roofline": {
-            "bound": "mfma", "kernel": "prefill_kernel",
+            "bound": "mfma",
+            "kernel": "gdn_prefill_chunked call (prefill_seg_map_kernel, prefill_kernel pass 1, "
+                      "prefill_seg_scan_kernel, prefill_kernel pass 2)",
             "achieved": round(pre_tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(pre_tflops / BF16_PEAK_TFLOPS, 4),
             "hbm_frac": round(pre_bytes / (pre_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(PREFILL_TRAFFIC_FILE, PREFILL_SRC, "prefill_hip_sha256"),
             "algorithmic_flops_per_launch": pre_flops, "algorithmic_bytes_per_launch": pre_bytes,
-            "note": ("one launch per call (whole runs: the chip is full); event-timed eager calls; "
-                     "bound in practice by the sequential chunk chain of the longest sequence")},
+            "note": ("the whole call, event-timed eager calls: on this busy chip the call's own "
+                     "schedule is a segment map, pass 1 (each sequence's first 49 chunks, the "
+                     "balanced per-CU share, and the P/B runs of longer sequences' tails on CUs "
+                     "that short sequences free), a scan and pass 2 (the tails); bound by the "
+                     "sequential chunk chain of the longest head and tail")},
+        "prefill_whole_ms_mean": round(mean(ms_pre_whole), 4),
+        "prefill_whole_note": "the same workload as one run per (sequence, value head), "
+                              "GDN_FLAG_PREFILL_SEQUENTIAL, alternating with the timed calls",
         "prefill_TFLOPs": round(pre_tflops, 2),
         "prefill_pct_mfma_peak": round(100 * pre_tflops / BF16_PEAK_TFLOPS, 2),
         "prefill_algorithmic_flops": pre_flops, "prefill_algorithmic_bytes": pre_bytes,
@@ -649,6 +706,7 @@ def main():
                                   "GDN_FLAG_PREFILL_SEQUENTIAL vs the segment-parallel schedule "
                                   "it picks with its workspace"),
         "conv_varlen_ms_mean": round(mean(ms_conv), 4),
+        "conv_varlen_roofline": conv_roofline(mean(ms_conv)),
         "conv_varlen_GBps": round(conv_bytes / (mean(ms_conv) * 1e-3) / 1e9, 1),
         "conv_varlen_note": ("gdn_conv_update with cu_seqlens over the prefill workload's "
                              f"{pre.T} token rows: bf16 [T, {D}] in and out, SiLU, 8 conv "
