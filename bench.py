@@ -15,9 +15,10 @@ state written in a recent step.
 Prints ONE JSON line.  `value` is the decode step's algorithmic HBM bytes per
 second at batch 256 (GB/s); the batch-16 decode rate and the prefill tokens/s
 ride along in "extra".  "roofline" reports the headline step's kernel (at
-batch 256 the step is one fused conv + recurrence kernel) timed alone with HIP
-events over eager launches; the conv + recurrence pair that the step uses below
-one (row, key head) group per 4 CUs is timed alongside.  "cpu_baseline" is the
+batch 256 the step is one fused conv + recurrence kernel) timed alone: blocks of
+back-to-back eager launches, one HIP event pair on their stream per block, the
+block time divided by its launches; the split path's recurrence kernel is timed
+the same way alongside.  "cpu_baseline" is the
 fp64 oracle on a bounded sample of the same workload, run over independent
 rows on the host's threads (at most 16); the one-thread figure is in "extra".
 """
@@ -84,23 +85,35 @@ CONV_SRC = os.path.join(ROOT, "gated_deltanet_recurrent_gdn_amd", "csrc", "conv.
 VALU_PEAK_WAVE_INSTS = 256 * 2.4e9
 
 
+def sources_sha256(src_path):
+    """sha256 over a kernel's source file followed by every header it can
+    include (the package's csrc/*.hpp, then include/*.h, each set in name
+    order): a change to any of them invalidates counters taken before it."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    pkg = os.path.join(ROOT, "gated_deltanet_recurrent_gdn_amd", "csrc")
+    for f in [src_path] + sorted(glob.glob(os.path.join(pkg, "*.hpp"))) + \
+            sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))):
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
 def counter_summary(path, src_path, key):
     """The key = value lines of a committed counter summary, or None when the
-    kernel's source has changed since those counters were taken."""
-    import hashlib
+    kernel's sources have changed since those counters were taken."""
     try:
         kv = {}
         for line in open(path):
             if "=" in line and not line.lstrip().startswith("#"):
                 k, v = line.split("=", 1)
                 kv[k.strip()] = v.strip()
-        src = hashlib.sha256(open(src_path, "rb").read()).hexdigest()
-        return kv if kv.get(key) == src else None
+        return kv if kv.get(key) == sources_sha256(src_path) else None
     except OSError:
         return None
 
 
-def measured_traffic(path=TRAFFIC_FILE, src_path=DECODE_SRC, key="decode_hip_sha256"):
+def measured_traffic(path=TRAFFIC_FILE, src_path=DECODE_SRC, key="decode_sources_sha256"):
     """HBM bytes per launch from a committed counter summary (FETCH_SIZE +
     WRITE_SIZE, copy-calibrated) -- by default the fused step kernel at batch
     256 -- or None when the kernel's source has changed since those counters
@@ -112,20 +125,23 @@ def measured_traffic(path=TRAFFIC_FILE, src_path=DECODE_SRC, key="decode_hip_sha
         return None
 
 
-def conv_roofline(ms):
-    """The varlen conv against the vector ALU issue peak: wave64 VALU
-    instructions per call from the committed counter summary (SQ_INSTS_VALU of
-    conv_varlen_tok_kernel) over the call's live mean time (which also holds the
-    small roll kernel), or None when conv.hip has changed since."""
-    kv = counter_summary(CONV_COUNTER_FILE, CONV_SRC, "conv_hip_sha256")
-    if kv is None:
-        return None
-    insts = float(kv["valu_wave_insts_per_launch"])
-    rate = insts / (ms * 1e-3)
-    return {"bound": "alu", "kernel": "conv_varlen_tok_kernel",
-            "achieved": round(rate / 1e9, 1), "peak": round(VALU_PEAK_WAVE_INSTS / 1e9, 1),
-            "unit": "G wave64 VALU instructions/s", "frac": round(rate / VALU_PEAK_WAVE_INSTS, 4),
-            "traffic": int(kv["fetch_bytes_per_launch"]) + int(kv["write_bytes_per_launch"])}
+def conv_roofline(ms, alg_bytes):
+    """The varlen conv call (token kernel + roll kernel) against HBM: algorithmic
+    bytes over the call's live mean time; traffic and the token kernel's vector
+    ALU issue rate come from the committed counter summary (SQ_INSTS_VALU over
+    the same live time, against 256 CUs x one wave64 instruction per cycle) and
+    are None once the conv sources have changed since those counters."""
+    gbs = alg_bytes / (ms * 1e-3) / 1e9
+    kv = counter_summary(CONV_COUNTER_FILE, CONV_SRC, "conv_sources_sha256")
+    out = {"bound": "hbm", "kernel": "conv_varlen_tok_kernel + conv_roll_kernel",
+           "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": alg_bytes,
+           "traffic": None, "valu_issue_frac": None}
+    if kv is not None:
+        out["traffic"] = int(kv["fetch_bytes_per_launch"]) + int(kv["write_bytes_per_launch"])
+        out["valu_issue_frac"] = round(float(kv["valu_wave_insts_per_launch"]) / (ms * 1e-3) /
+                                       VALU_PEAK_WAVE_INSTS, 4)
+    return out
 
 
 def parse():
@@ -381,6 +397,26 @@ def time_loop(torch, fn, steps, warmup):
     return [s.elapsed_time(e) for s, e in zip(starts, ends)]
 
 
+def time_block(torch, fn, steps, warmup, rounds=3):
+    """Average launch duration over a block of back-to-back launches: one event
+    pair on the current stream around `steps` launches, divided by `steps`
+    (so per-launch event packets do not add to each kernel); returns one mean
+    per round."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(rounds):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(steps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        out.append(s.elapsed_time(e) / steps)
+    return out
+
+
 def host_cpu_counts():
     """(CPUs this process may run on, CPUs the OS reports)."""
     try:
@@ -573,12 +609,12 @@ def main():
     for _ in range(2):
         ms_pre += time_loop(torch, lambda: pre.step(args.validate), max(2, args.steps // 2), args.warmup)
         ms_pre_whole += time_loop(torch, pre.step_whole, max(2, args.steps // 2), args.warmup)
-    # the headline step's kernel alone (the fused step at batch 256), eager
-    # launches bracketed by events on the stream they run on
-    ms_step_k = time_loop(torch, big.step, args.steps, args.warmup)
+    # the headline step's kernel alone (the fused step at batch 256): eager
+    # launches back to back, one event pair on their stream around each block
+    ms_step_k = time_block(torch, big.step, args.steps, args.warmup)
     # the split path's recurrence kernel alone (post-conv activations in)
     big.prepare_rec()
-    ms_rec = time_loop(torch, big.rec_step, args.steps, args.warmup)
+    ms_rec = time_block(torch, big.rec_step, args.steps, args.warmup)
     torch.cuda.synchronize()
     # gated RMSNorm epilogue on the prefill output (o [T, HV, dv] bf16, z bf16, w fp32)
     zn = torch.randn(pre.T, HV, DV, device=dev).to(torch.bfloat16)
@@ -683,7 +719,7 @@ def main():
             "achieved": round(pre_tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(pre_tflops / BF16_PEAK_TFLOPS, 4),
             "hbm_frac": round(pre_bytes / (pre_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(PREFILL_TRAFFIC_FILE, PREFILL_SRC, "prefill_hip_sha256"),
+            "traffic": measured_traffic(PREFILL_TRAFFIC_FILE, PREFILL_SRC, "prefill_sources_sha256"),
             "algorithmic_flops_per_launch": pre_flops, "algorithmic_bytes_per_launch": pre_bytes,
             "note": ("the whole call, event-timed eager calls: on this busy chip the call's own "
                      "schedule is a segment map, pass 1 (each sequence's first 49 chunks, the "
@@ -706,7 +742,7 @@ def main():
                                   "GDN_FLAG_PREFILL_SEQUENTIAL vs the segment-parallel schedule "
                                   "it picks with its workspace"),
         "conv_varlen_ms_mean": round(mean(ms_conv), 4),
-        "conv_varlen_roofline": conv_roofline(mean(ms_conv)),
+        "conv_varlen_roofline": conv_roofline(mean(ms_conv), conv_bytes),
         "conv_varlen_GBps": round(conv_bytes / (mean(ms_conv) * 1e-3) / 1e9, 1),
         "conv_varlen_note": ("gdn_conv_update with cu_seqlens over the prefill workload's "
                              f"{pre.T} token rows: bf16 [T, {D}] in and out, SiLU, 8 conv "

@@ -73,6 +73,13 @@ __device__ __forceinline__ bool call_rejected(const int32_t* err_flag) {
     return err_flag != nullptr && __builtin_nontemporal_load(err_flag) != 0;
 }
 
-__device__ __forceinline__ float silu(float y) { return y / (1.0f + expf(-y)); }
+// SiLU through the hardware base-2 exponential (__expf) and reciprocal
+// (v_rcp_f32, 1 ulp): a few fp32 ulps from the correctly rounded value, the
+// form a production conv provider uses (exp2 approximation and an approximate
+// division), against the exp and IEEE division of the golden.  Every conv path
+// calls this one function, so the paths stay bitwise equal to each other.
+__device__ __forceinline__ float silu(float y) {
+    return y * __builtin_amdgcn_rcpf(1.0f + __expf(-y));
+}
 
 }  // namespace gdn
