@@ -14,6 +14,12 @@
  *   gdn_mixed_step       one step holding decode rows and prefill sequences,
  *                        the decode rows computed exactly as in a decode-only
  *                        step
+ *   gdn_prefill_segmented
+ *                        the chunked prefill on an explicit segment-parallel
+ *                        schedule (the plain call picks one by itself)
+ *   gdn_gated_rmsnorm    the gated RMSNorm epilogue after the core
+ *   gdn_decode_step_noalloc
+ *                        gdn_decode_step for callers that cannot allocate
  *
  * Sources (pages, by title and section):
  *   [P1] RL-Kernel PR #469 "C6: GDN decode-step goldens and recurrent/conv
@@ -32,7 +38,9 @@
  * Conventions common to every call
  *   - Every tensor is caller-owned DEVICE memory, dense, row-major (C order),
  *     at least 16-byte aligned.  The library never allocates, frees or
- *     synchronises and holds no state between calls; each call only enqueues
+ *     synchronises and holds no state between calls (the one exception is
+ *     gdn_decode_step_noalloc's per-device scratch array, declared with that
+ *     call for callers that cannot allocate); each call only enqueues
  *     kernels (and, in gdn_mixed_step, event records and waits) on the
  *     caller's `stream` (NULL = the default stream) and streams, and returns.
  *     Calls on different streams that touch disjoint slots and buffers are
