@@ -1207,6 +1207,800 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Pipelined chunk step (d = 128, bf16 inputs; whole runs and unpaired segment
+// runs).  The arithmetic of prefill_kernel term for term and in the same order
+// (so the two kernels agree bit for bit), with the eight waves split by role,
+// so that the state-independent work of one chunk runs beside the state
+// products of another:
+//   state waves 0-3 (one per SIMD) own 32 value columns each of S0^T and do
+//     Z = K S0^T, O1^T = S0 Q^T, Y, U = cU Y, O and the state update of chunk c;
+//   coefficient waves 4-7 invert chunk c's (I + A) (forward substitution on
+//     wave 7, merges on waves 5 and 6), form its cU, and then build chunk
+//     c + 1's gate scan, G = K K^T, P = Q K^T, norms, A and M o P-hat while the
+//     state waves finish chunk c.
+// One chunk step is seven barrier-separated sub-steps.  The two roles run as
+// two loops over the same chunks with the same seven barriers per chunk, so
+// every barrier is met by all eight waves:
+//   A1  state: Z                        coef: forward substitution (wave 7);
+//                                             eg/ck/cy(c) (wave 4); loads of chunk
+//                                             c+1 (waves 4-6); M o P-hat(c) rows (5, 6)
+//   A2  state: Y = V - cy Z             coef: stage K^T(c); loads (wave 7);
+//                                             merge 16 -> 32 (waves 5, 6)
+//   A3  state: O1, scaled               coef: merge 32 -> 64 (waves 5, 6);
+//                                             M o P-hat(c) rows (waves 4, 7)
+//   A4  all: cU(c) (rows 0-31 on the state waves, 32-63 on the coefficient waves)
+//   B1  state: U = cU Y                 coef: stage K, Q, V^T(c+1); gate scan(c+1)
+//   B2  state: O (stored)               coef: G, P, norms(c+1)
+//   B3  state: cK . U, the state update coef: A(c+1)
+// Each coefficient wave keeps its G and P tiles of chunk c+1 in registers from
+// B2 to the next chunk's M o P-hat step, so that work lands where the wave has
+// slack.  The waves on the critical path of their sub-step (substitution,
+// merges) raise their issue priority over the state wave sharing their SIMD.
+// The chunk loads go out on waves with nothing else to do in that sub-step:
+// a burst of them stalls the issuing wave for much of the memory latency.
+// LDS ownership follows from that order: K and Q (c) are read in A1-A3 and
+// replaced in B1; V^T(c) is read in A2 and replaced in B1; K^T(c) is read in
+// B3 and replaced in A2; A / T live in g and xs from B3 to A4; cU is written
+// in A4 and read in B1; M o P-hat is read in B2 and written in B3.  The per-token
+// coefficients the state waves use (e^gamma r_q, c_K, e^gamma r_k, e^gamma_L)
+// are double-buffered by chunk parity.
+struct PipeSmem {
+    static constexpr int D = 128;
+    static constexpr int SK = D + PADK;         // row stride of K, Q (bf16)
+    static constexpr int ST = CH + PADT;        // row stride of K^T, V^T, cU, M o P-hat
+    static constexpr int SF = CH + PADF;        // row stride of the fp32 64x64 array
+    bf16_t k[CH * SK];                          // K   [t][k]
+    bf16_t q[CH * SK];                          // Q   [t][k]
+    bf16_t kt[D * ST];                          // K^T [k][t]
+    bf16_t vt[D * ST];                          // V^T [v][t]
+    float g[CH * SF];                           // A, then T in place (block [32:64][0:32] in xs)
+    bf16_t cu[2 * CH * ST];                     // cU hi, lo [t][t'], pperm order along t'
+    float xs[32 * 36];                          // merge scratch X; finally T[32:64][0:32]
+    bf16_t mp[2 * CH * ST];                     // (M o P) hi, lo [t][t']
+    float gam[CH], beta[CH], rk[CH], rq[CH];
+    float eg[2][CH], ck[2][CH], cy[2][CH];
+    float egl[2];
+};
+
+template <typename OT, bool SEG>
+__global__ __launch_bounds__(PF_NT) void prefill_pipe_kernel(
+    const bf16_t* __restrict__ qg, const bf16_t* __restrict__ kg, const bf16_t* __restrict__ vg,
+    const GateArgs ga, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ slot, float* __restrict__ rec, OT* __restrict__ out, int32_t H,
+    int32_t HV, int32_t sqk, int32_t sv, float scale, int32_t flags,
+    const SegArgs sg, const int32_t* __restrict__ err_flag) {
+    constexpr int D = 128;
+    constexpr int KB = D / 16;                   // 16-row key blocks of the state
+    constexpr int KS = D / 32;                   // 32-wide k-steps over the head dim
+    constexpr int VB = 2;                        // 16-wide value blocks per state wave
+    constexpr int SK = PipeSmem::SK, ST = PipeSmem::ST, SF = PipeSmem::SF;
+    constexpr int WF = 7;                        // forward-substitution wave
+    constexpr int WM = 5;                        // merge waves WM, WM + 1
+    constexpr int GW = 4;                        // gate-scan wave
+    __shared__ PipeSmem sm;
+
+    if (call_rejected(err_flag)) return;
+    int hv = blockIdx.x;
+    {
+        const int G = HV / H;
+        if (HV % 8 == 0 && H % 8 == 0) {
+            const int a = hv >> 3, b = hv & 7;
+            hv = G * (8 * (a / G) + b) + a % G;
+        }
+    }
+    int n = blockIdx.y;
+    int zseg = blockIdx.z;
+    if constexpr (SEG) {
+        int gy = blockIdx.y;
+        if (sg.pass == 1 && gy < sg.n_seqs) {
+            zseg = 0;
+        } else {
+            const int base = sg.pass == 1 ? 1 : 0;
+            if (sg.pass == 1) gy -= sg.n_seqs;
+            if (gy >= sg.map[sg.n_seqs]) return;
+            int lo = 0, hi = sg.n_seqs;
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (sg.map[mid] <= gy) lo = mid; else hi = mid;
+            }
+            n = lo;
+            zseg = base + gy - sg.map[lo];
+        }
+    }
+    const int h = hv / (HV / H);
+    const int tid = threadIdx.x;
+    // the wave index read from the first lane: the role branches below are
+    // then scalar branches
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool state_w = wave < 4;
+    // Lane coordinates, re-derived at every chunk from an opaque copy of the
+    // thread index, so that the compiler recomputes the chunk's LDS addresses
+    // inside the loop instead of holding them in registers across it.
+    int lane, q4, l16, tp, cg, ta, swl, swm;
+    auto set_lane = [&]() {
+        int t = static_cast<int>(threadIdx.x);
+        asm volatile("" : "+v"(t));
+        lane = t & 63;
+        q4 = lane >> 4;
+        l16 = lane & 15;
+        tp = t & 31;
+        cg = (t >> 5) & 7;                       // staging: 8 column groups, two passes
+        ta = 2 * tp;
+        swl = kq_swz(l16);
+        swm = (PipeSmem::ST % 32 == 16) ? swl : 0;
+    };
+    set_lane();
+    const int32_t t0 = cu[n];
+    const int32_t t1 = cu[n + 1];
+    const int32_t s = slot[n];
+    const bool norm = (flags & GDN_FLAG_QK_L2NORM) != 0;
+
+    if (s <= 0) {                                // inactive: zero outputs, state untouched
+        if (SEG && (sg.pass == 2 || zseg != 0)) return;
+        for (int64_t i = tid; i < static_cast<int64_t>(t1 - t0) * D; i += PF_NT) {
+            const int64_t t = t0 + i / D;
+            elem<OT>::st(out + (t * HV + hv) * D + i % D, 0.0f);
+        }
+        return;
+    }
+    if (t1 <= t0) return;                        // empty sequence: state untouched
+
+    float* S = rec + (static_cast<size_t>(s) * HV + hv) * static_cast<size_t>(D) * D;
+    // the token range, start state (nullptr: zero), outputs, end state: as in
+    // prefill_kernel's unpaired segment runs
+    int32_t a0 = t0, a1 = t1;
+    const float* init = S;
+    float* fin = S;
+    bool wo = true, ident = false, use_v = true;
+    if constexpr (SEG) {
+        const int32_t seg = sg.seg_len;
+        const int32_t nseg = seg_count(t1 - t0, sg.head, seg);
+        const int64_t id0 = n + t0 / seg;
+        auto seg_start = [&](int j) { return j == 0 ? t0 : t0 + sg.head + (j - 1) * seg; };
+        auto wsm = [&](int64_t id, int kind) {
+            return sg.ws + ((id * 3 + kind) * HV + hv) * static_cast<size_t>(D) * D;
+        };
+        const int z = zseg;
+        if (sg.pass == 1) {
+            if (nseg <= 1) {
+                if (z != 0) return;
+            } else if (z == 0) {
+                a1 = t0 + sg.head;
+                fin = wsm(id0 + 1, 0);
+            } else {
+                const int jj = (z + 1) / 2;      // z = 2 jj - 1: B run, z = 2 jj: P run
+                if (jj > nseg - 2) return;
+                a0 = seg_start(jj);
+                a1 = a0 + seg;
+                wo = false;
+                init = nullptr;
+                if (z & 1) {
+                    fin = wsm(id0 + jj, 2);
+                } else {
+                    fin = wsm(id0 + jj, 1);
+                    ident = true;
+                    use_v = false;
+                }
+            }
+        } else {
+            const int j = z + 1;
+            if (nseg <= 1 || j > nseg - 1) return;
+            a0 = seg_start(j);
+            a1 = min(a0 + seg, t1);
+            init = wsm(id0 + j, 0);
+            fin = (j == nseg - 1) ? S : nullptr;
+        }
+    }
+
+    // ---- state S0^T [k][v] (state waves): tile (kb, vb) lane holds
+    //      S0^T[16 kb + 4 q4 + r][32 wave + 16 vb + l16]
+    f32x4 st[KB][VB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int vb = 0; vb < VB; ++vb) {
+            st[kb][vb] = f32x4{0, 0, 0, 0};
+            if (state_w) {
+                const int v = 16 * (wave * VB + vb) + l16;
+                if (!SEG || init) {
+                    const float4 x = *reinterpret_cast<const float4*>(init + static_cast<size_t>(v) * D + 16 * kb + 4 * q4);
+                    st[kb][vb] = f32x4{x.x, x.y, x.z, x.w};
+                }
+                if constexpr (SEG) {
+                    if (ident) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) st[kb][vb][r] = (16 * kb + 4 * q4 + r == v) ? 1.0f : 0.0f;
+                    }
+                }
+            }
+        }
+
+    // Chunk loads (coefficient waves): thread (tp, cg) moves token rows 2tp,
+    // 2tp+1 at columns 8 (cg + 8 pass), through buffer descriptors over the
+    // chunk's rows (rows past its length read as zero), issued two sub-steps
+    // before they are staged; the state waves hold no chunk registers.
+    uint4 pk[2][2], pq[2][2], pv[2][2];          // [pass][row]: K of chunk c; Q, V of c + 1
+    uint4 pk2[2][2];                             // K of chunk c + 1 (K^T(c) is staged from pk)
+    uint32_t pbeta = 0, pg = 0;
+    const GateHead gh = gate_head(ga, hv);
+    const uint32_t off_kq = static_cast<uint32_t>(h * D) * sizeof(bf16_t);
+    const uint32_t off_v = static_cast<uint32_t>(hv * D) * sizeof(bf16_t);
+    const uint32_t row_kq = static_cast<uint32_t>(sqk) * sizeof(bf16_t);
+    const uint32_t row_v = static_cast<uint32_t>(sv) * sizeof(bf16_t);
+    const bool ghalf = ga.a != nullptr && ga.ab_bf16;
+    const uint32_t ges = ghalf ? 2 : 4;
+    const uint32_t grow = static_cast<uint32_t>(HV) * ges;
+    const char* gsrc0 = static_cast<const char*>(ga.a ? ga.a : static_cast<const void*>(ga.g));
+    const char* gsrc1 = static_cast<const char*>(ga.a ? ga.b : static_cast<const void*>(ga.beta));
+    auto fetch = [&](int32_t c, int Lc) {
+        const rsrc_t rk_ = make_rsrc(kg + static_cast<size_t>(c) * sqk, Lc * row_kq);
+        const rsrc_t rq_ = make_rsrc(qg + static_cast<size_t>(c) * sqk, Lc * row_kq);
+        const rsrc_t rv_ = make_rsrc(vg + static_cast<size_t>(c) * sv, Lc * row_v);
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+            const uint32_t kk = static_cast<uint32_t>(8 * (cg + 8 * pass)) * sizeof(bf16_t);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const uint32_t t = ta + e;
+                pk2[pass][e] = buf_ld16(rk_, t * row_kq + off_kq + kk);
+                pq[pass][e] = buf_ld16(rq_, t * row_kq + off_kq + kk);
+                pv[pass][e] = buf_ld16(rv_, t * row_v + off_v + kk);
+            }
+        }
+        if (wave == GW) {                        // the gate-scan wave: token = lane
+            const rsrc_t r0 = make_rsrc(gsrc0 + static_cast<size_t>(c) * grow, Lc * grow);
+            const rsrc_t r1 = make_rsrc(gsrc1 + static_cast<size_t>(c) * grow, Lc * grow);
+            const uint32_t ob = static_cast<uint32_t>(lane * HV + hv) * ges;
+            if (ghalf) {
+                pg = buf_ld2(r0, ob);
+                pbeta = buf_ld2(r1, ob);
+            } else {
+                pg = __builtin_amdgcn_raw_buffer_load_b32(r0, ob, 0, 0);
+                pbeta = __builtin_amdgcn_raw_buffer_load_b32(r1, ob, 0, 0);
+            }
+        }
+    };
+    // K, Q rows (pperm order along k, swizzled) and V^T from the fetched registers
+    auto stage_kqv = [&]() {
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+            const int k0 = 8 * (cg + 8 * pass);
+            const int p0 = pperm(k0), p1 = pperm(k0 + 4), swt = kq_swz(ta);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                lds_st8(&sm.k[(ta + e) * SK + (p0 ^ swt)], pk2[pass][e].x, pk2[pass][e].y);
+                lds_st8(&sm.k[(ta + e) * SK + (p1 ^ swt)], pk2[pass][e].z, pk2[pass][e].w);
+                lds_st8(&sm.q[(ta + e) * SK + (p0 ^ swt)], pq[pass][e].x, pq[pass][e].y);
+                lds_st8(&sm.q[(ta + e) * SK + (p1 ^ swt)], pq[pass][e].z, pq[pass][e].w);
+            }
+            store_pairs_t(sm.vt, ST, k0, ta, pv[pass][0], pv[pass][1]);
+        }
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) pk[pass][e] = pk2[pass][e];
+    };
+    auto stage_kt = [&]() {
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass)
+            store_pairs_t(sm.kt, ST, 8 * (cg + 8 * pass), pperm(ta), pk[pass][0], pk[pass][1]);
+    };
+    // cU = T diag(beta), hi/lo, pperm order along t' (thread t < 512: row t / 8,
+    // eight columns)
+    auto cu_part = [&](int t) {
+        const int r = t >> 3, cb = 8 * (t & 7);
+        uint32_t uh[4], ul[4];
+        const float* trow = (r >= 32 && cb < 32) ? &sm.xs[(r - 32) * 36 + cb] : &sm.g[r * SF + cb];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const float4 tv = *reinterpret_cast<const float4*>(trow + 4 * j);
+            const float4 bt = *reinterpret_cast<const float4*>(&sm.beta[cb + 4 * j]);
+            const f32x4 u = {tv.x * bt.x, tv.y * bt.y, tv.z * bt.z, tv.w * bt.w};
+            uint2 h2, l2;
+            split4(u, h2, l2);
+            uh[2 * j] = h2.x; uh[2 * j + 1] = h2.y; ul[2 * j] = l2.x; ul[2 * j + 1] = l2.y;
+        }
+        bf16_t* ubase = sm.cu + r * ST;
+        lds_st8(ubase + 0 * CH * ST + pperm(cb), uh[0], uh[1]);
+        lds_st8(ubase + 0 * CH * ST + pperm(cb + 4), uh[2], uh[3]);
+        lds_st8(ubase + 1 * CH * ST + pperm(cb), ul[0], ul[1]);
+        lds_st8(ubase + 1 * CH * ST + pperm(cb + 4), ul[2], ul[3]);
+    };
+    // gate, then the cumulative log-decay: fixed-order DPP wave scan (wave GW)
+    auto gate_scan = [&](int L) {
+        float gt, bv;
+        gate_finish(ga, gh, ghalf ? bf16_to_f32(static_cast<bf16_t>(pg)) : __uint_as_float(pg),
+                    ghalf ? bf16_to_f32(static_cast<bf16_t>(pbeta)) : __uint_as_float(pbeta), gt, bv);
+        if (lane >= L) { gt = 0.0f; bv = 0.0f; }
+        sm.beta[lane] = bv;
+        gt += dpp_scan_step<0x111, 0xF>(gt);
+        gt += dpp_scan_step<0x112, 0xF>(gt);
+        gt += dpp_scan_step<0x114, 0xF>(gt);
+        gt += dpp_scan_step<0x118, 0xF>(gt);
+        gt += dpp_scan_step<0x142, 0xA>(gt);
+        gt += dpp_scan_step<0x143, 0xC>(gt);
+        sm.gam[lane] = gt;
+    };
+    // coefficient waves: G = K K^T and P = Q K^T tiles of row block tb = wave - 4
+    // (key block as the A operand, so a lane holds row i and four consecutive
+    // columns), and the diagonal block of Q Q^T; the norms from the diagonals
+    const int tb_c = wave & 3;
+    f32x4 accg[4], accp[4], accq;
+    auto gram = [&]() {
+        accq = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { accg[j] = f32x4{0, 0, 0, 0}; accp[j] = f32x4{0, 0, 0, 0}; }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 ak = frag_kq(sm.k, SK, 16 * tb_c + l16, 32 * ks, q4, swl);
+            const bf16x8 aq = frag_kq(sm.q, SK, 16 * tb_c + l16, 32 * ks, q4, swl);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bf16x8 bk = frag_kq(sm.k, SK, 16 * j + l16, 32 * ks, q4, swl);
+                accg[j] = mfma(bk, ak, accg[j]);
+                accp[j] = mfma(bk, aq, accp[j]);
+            }
+            accq = mfma(frag_kq(sm.q, SK, 16 * tb_c + l16, 32 * ks, q4, swl), aq, accq);
+        }
+        const int i = 16 * tb_c + l16;
+        const int r0 = l16 - 4 * q4;
+        if (r0 >= 0 && r0 < 4) {
+            const f32x4 gd = accg[tb_c];
+            float dk = gd[0], dq = accq[0];
+#pragma unroll
+            for (int r = 1; r < 4; ++r)
+                if (r == r0) { dk = gd[r]; dq = accq[r]; }
+            sm.rk[i] = norm ? 1.0f / sqrtf(dk + 1e-6f) : 1.0f;
+            sm.rq[i] = norm ? scale / sqrtf(dq + 1e-6f) : scale;
+        }
+    };
+    // the chunk's per-token coefficients (one wave, token = lane; parity pc);
+    // decays use the hardware base-2 exponential, as in prefill_kernel
+    auto coefs = [&](int L, int pc) {
+        const float gl = sm.gam[L - 1];
+        const float gv = sm.gam[lane];
+        const float et = __expf(gv);
+        sm.eg[pc][lane] = et * sm.rq[lane];
+        sm.ck[pc][lane] = (lane < L) ? __expf(gl - gv) * sm.rk[lane] : 0.0f;
+        sm.cy[pc][lane] = et * sm.rk[lane];
+        if (lane == 0) sm.egl[pc] = __expf(gl);
+    };
+    // A (fp32 into g) and, separately, M o P-hat (hi/lo into mp) from this
+    // wave's G and P tiles: row i = 16 tb + l16, columns c .. c + 3
+    auto epi_a = [&]() {
+        const int i = 16 * tb_c + l16;
+        const float gi = sm.gam[i];
+        const float brk = sm.beta[i] * sm.rk[i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = 16 * j + 4 * q4;
+            const float4 gc = *reinterpret_cast<const float4*>(&sm.gam[c]);
+            const float4 rkc = *reinterpret_cast<const float4*>(&sm.rk[c]);
+            const float gcs[4] = {gc.x, gc.y, gc.z, gc.w};
+            const float rks[4] = {rkc.x, rkc.y, rkc.z, rkc.w};
+            f32x4 a;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float dec = (c + r <= i) ? __expf(gi - gcs[r]) : 0.0f;
+                a[r] = (c + r < i) ? (brk * rks[r]) * (dec * accg[j][r]) : 0.0f;
+            }
+            *reinterpret_cast<float4*>(&sm.g[i * SF + c]) = make_float4(a[0], a[1], a[2], a[3]);
+        }
+    };
+    auto epi_mp = [&]() {
+        const int i = 16 * tb_c + l16;
+        const float gi = sm.gam[i];
+        const float rqi = sm.rq[i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = 16 * j + 4 * q4;
+            const float4 gc = *reinterpret_cast<const float4*>(&sm.gam[c]);
+            const float4 rkc = *reinterpret_cast<const float4*>(&sm.rk[c]);
+            const float gcs[4] = {gc.x, gc.y, gc.z, gc.w};
+            const float rks[4] = {rkc.x, rkc.y, rkc.z, rkc.w};
+            f32x4 mp;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float dec = (c + r <= i) ? __expf(gi - gcs[r]) : 0.0f;
+                mp[r] = (rqi * rks[r]) * (dec * accp[j][r]);
+            }
+            uint2 h2, l2;
+            split4(mp, h2, l2);
+            lds_st8(&sm.mp[i * ST + (pperm(c) ^ swm)], h2.x, h2.y);
+            lds_st8(&sm.mp[CH * ST + i * ST + (pperm(c) ^ swm)], l2.x, l2.y);
+        }
+    };
+
+    // ---- the first chunk's staging and coefficient work
+    {
+        const int L0 = min(CH, a1 - a0);
+        if (!state_w) {
+            fetch(a0, L0);
+            stage_kqv();
+            if (wave == GW) gate_scan(L0);
+        }
+        __syncthreads();
+        if (!state_w) gram();
+        __syncthreads();
+        if (!state_w) epi_a();
+        __syncthreads();
+    }
+
+    // The two roles run as two loops over the same chunks, each with the same
+    // seven barriers per chunk (so every barrier is met by all eight waves),
+    // which keeps each role's registers out of the other's code.
+    if (state_w) {
+        int p = 0;                               // parity of chunk c
+        for (int32_t c0 = a0; c0 < a1; c0 += CH) {
+            const int L = min(CH, a1 - c0);
+            const bool nxt = c0 + CH < a1;
+            const int Ln = nxt ? min(CH, a1 - c0 - CH) : 0;
+            set_lane();
+            f32x4 z[4][VB];                      // Z tiles (t-block, v-block)
+            f32x4 o[VB][4];                      // O^T tiles (v-block, t-block)
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+                for (int vb = 0; vb < VB; ++vb) { z[tb][vb] = f32x4{0, 0, 0, 0}; o[vb][tb] = f32x4{0, 0, 0, 0}; }
+            // one k-step of Z = K S0^T (doz) or O1^T = S0 Q^T (doo): every
+            // fragment load first, then the state split (VALU work that covers
+            // the loads' latency), then the MFMAs
+            auto early = [&](int ks, bool doz, bool doo) {
+                bf16x8 ak[4], bq[4];
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) {
+                    if (doz) ak[tb] = frag_kq(sm.k, SK, 16 * tb + l16, 32 * ks, q4, swl);
+                    if (doo) bq[tb] = frag_kq(sm.q, SK, 16 * tb + l16, 32 * ks, q4, swl);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                bf16x8 sh[VB], sl[VB];
+#pragma unroll
+                for (int vb = 0; vb < VB; ++vb) {
+                    uint2 h0, l0, h1, l1;
+                    split4(st[2 * ks][vb], h0, l0);
+                    split4(st[2 * ks + 1][vb], h1, l1);
+                    sh[vb] = as_bf16x8(cat(h0, h1));
+                    sl[vb] = as_bf16x8(cat(l0, l1));
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) {
+                    if (doz) {
+#pragma unroll
+                        for (int vb = 0; vb < VB; ++vb) {
+                            z[tb][vb] = mfma(ak[tb], sh[vb], z[tb][vb]);
+                            z[tb][vb] = mfma(ak[tb], sl[vb], z[tb][vb]);
+                        }
+                    }
+                    if (doo) {
+#pragma unroll
+                        for (int vb = 0; vb < VB; ++vb) {
+                            o[vb][tb] = mfma(sh[vb], bq[tb], o[vb][tb]);
+                            o[vb][tb] = mfma(sl[vb], bq[tb], o[vb][tb]);
+                        }
+                    }
+                }
+            };
+
+            // ---- A1: Z = K S0^T
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) early(ks, true, false);
+            __syncthreads();
+            // ---- A2: Y = V - diag(cy) Z in fp32 (V from V^T: four consecutive
+            // tokens of one value column per lane, the accumulator layout), split
+            // hi/lo
+            bf16x8 yh[2][VB], yl[2][VB];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int vb = 0; vb < VB; ++vb) {
+                    const int vr = 16 * (wave * VB + vb) + l16;
+                    f32x4 nn[2];
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const int tb = 2 * ks + e;
+                        const int tt = 16 * tb + 4 * q4;
+                        const float4 cyv = *reinterpret_cast<const float4*>(&sm.cy[p][tt]);
+                        float vv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                        if (use_v) {
+                            const uint2 w = *reinterpret_cast<const uint2*>(&sm.vt[vr * ST + tt]);
+                            vv[0] += bf16lo_to_f32(w.x); vv[1] += bf16hi_to_f32(w.x);
+                            vv[2] += bf16lo_to_f32(w.y); vv[3] += bf16hi_to_f32(w.y);
+                        }
+                        nn[e][0] = vv[0] - cyv.x * z[tb][vb][0];
+                        nn[e][1] = vv[1] - cyv.y * z[tb][vb][1];
+                        nn[e][2] = vv[2] - cyv.z * z[tb][vb][2];
+                        nn[e][3] = vv[3] - cyv.w * z[tb][vb][3];
+                    }
+                    uint2 h0, l0, h1, l1;
+                    split4(nn[0], h0, l0);
+                    split4(nn[1], h1, l1);
+                    yh[ks][vb] = as_bf16x8(cat(h0, h1));
+                    yl[ks][vb] = as_bf16x8(cat(l0, l1));
+                }
+            __syncthreads();
+            // ---- A3: O1^T = S0 Q^T, scaled by e^gamma_t r_q
+            if (wo) {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) early(ks, false, true);
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) {
+                    const float e = sm.eg[p][16 * tb + l16];
+#pragma unroll
+                    for (int vb = 0; vb < VB; ++vb) {
+                        o[vb][tb][0] *= e; o[vb][tb][1] *= e; o[vb][tb][2] *= e; o[vb][tb][3] *= e;
+                    }
+                }
+            }
+            __syncthreads();
+            // ---- A4: rows 0-31 of cU
+            cu_part(tid);
+            __syncthreads();
+            // ---- B1: U = cU Y (cU lower triangular: blocks above the diagonal
+            // skipped)
+            f32x4 u[4][VB];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+                for (int vb = 0; vb < VB; ++vb) u[tb][vb] = f32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    if (32 * ks > 16 * tb + 15) continue;
+                    const bf16x8 ch = frag_perm(sm.cu + 0 * CH * ST, ST, 16 * tb + l16, 32 * ks, q4);
+                    const bf16x8 cl = frag_perm(sm.cu + 1 * CH * ST, ST, 16 * tb + l16, 32 * ks, q4);
+#pragma unroll
+                    for (int vb = 0; vb < VB; ++vb) {
+                        u[tb][vb] = mfma(ch, yh[ks][vb], u[tb][vb]);
+                        u[tb][vb] = mfma(ch, yl[ks][vb], u[tb][vb]);
+                        u[tb][vb] = mfma(cl, yh[ks][vb], u[tb][vb]);
+                    }
+                }
+            __syncthreads();
+            // ---- B2: O^T += U^T (M o P)^T (U split: A operand, permuted
+            // t-slots), stored; cK . U split; state rows 0-63
+            if (wo) {
+                bf16x8 uh[2][VB], ul[2][VB];
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int vb = 0; vb < VB; ++vb) {
+                        uint2 h0, l0, h1, l1;
+                        split4(u[2 * ks][vb], h0, l0);
+                        split4(u[2 * ks + 1][vb], h1, l1);
+                        uh[ks][vb] = as_bf16x8(cat(h0, h1));
+                        ul[ks][vb] = as_bf16x8(cat(l0, l1));
+                    }
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks) {
+                        if (32 * ks > 16 * tb + 15) continue;
+                        const bf16x8 mh = frag_kq(sm.mp, ST, 16 * tb + l16, 32 * ks, q4, swm);
+                        const bf16x8 ml = frag_kq(sm.mp + CH * ST, ST, 16 * tb + l16, 32 * ks, q4, swm);
+#pragma unroll
+                        for (int vb = 0; vb < VB; ++vb) {
+                            o[vb][tb] = mfma(uh[ks][vb], mh, o[vb][tb]);
+                            o[vb][tb] = mfma(ul[ks][vb], mh, o[vb][tb]);
+                            o[vb][tb] = mfma(uh[ks][vb], ml, o[vb][tb]);
+                        }
+                    }
+                // lane holds O[t = 16 tb + l16][v = 16 (wave VB + vb) + 4 q4 .. + 3];
+                // rows t >= L fall outside the descriptor's range and are dropped
+                const uint32_t row_o = static_cast<uint32_t>(HV * D) * sizeof(OT);
+                const rsrc_t ro = make_rsrc(out + static_cast<size_t>(c0) * HV * D, L * row_o);
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+                    for (int vb = 0; vb < VB; ++vb) {
+                        const uint32_t off = static_cast<uint32_t>(16 * tb + l16) * row_o +
+                            static_cast<uint32_t>(hv * D + 16 * (wave * VB + vb) + 4 * q4) * sizeof(OT);
+                        if constexpr (sizeof(OT) == 4) {
+                            buf_st16(ro, off, __float_as_uint(o[vb][tb][0]), __float_as_uint(o[vb][tb][1]),
+                                     __float_as_uint(o[vb][tb][2]), __float_as_uint(o[vb][tb][3]));
+                        } else {
+                            buf_st8(ro, off, pack_bf16x2(o[vb][tb][0], o[vb][tb][1]),
+                                    pack_bf16x2(o[vb][tb][2], o[vb][tb][3]));
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+            // ---- B3: cK . U split; the state update
+            bf16x8 chk[2][VB], clk[2][VB];       // cK . U, split
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int vb = 0; vb < VB; ++vb) {
+                    f32x4 a = u[2 * ks][vb], b = u[2 * ks + 1][vb];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        a[r] *= sm.ck[p][32 * ks + 4 * q4 + r];
+                        b[r] *= sm.ck[p][32 * ks + 16 + 4 * q4 + r];
+                    }
+                    uint2 h0, l0, h1, l1;
+                    split4(a, h0, l0);
+                    split4(b, h1, l1);
+                    chk[ks][vb] = as_bf16x8(cat(h0, h1));
+                    clk[ks][vb] = as_bf16x8(cat(l0, l1));
+                }
+            // S0^T <- e^{gamma_L} S0^T + K^T (cK . U), key blocks kb0 .. kb0 + 3
+            auto update = [&](int kb0) {
+                const float egl = sm.egl[p];
+#pragma unroll
+                for (int kb = kb0; kb < kb0 + 4; ++kb) {
+                    bf16x8 ak[2];
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks) ak[ks] = frag_perm(sm.kt, ST, 16 * kb + l16, 32 * ks, q4);
+#pragma unroll
+                    for (int vb = 0; vb < VB; ++vb) {
+                        f32x4 acc = st[kb][vb];
+                        acc[0] *= egl; acc[1] *= egl; acc[2] *= egl; acc[3] *= egl;
+#pragma unroll
+                        for (int ks = 0; ks < 2; ++ks) {
+                            acc = mfma(ak[ks], chk[ks][vb], acc);
+                            acc = mfma(ak[ks], clk[ks][vb], acc);
+                        }
+                        st[kb][vb] = acc;
+                    }
+                }
+            };
+            update(0);
+            update(4);
+            __syncthreads();
+            p ^= 1;
+        }
+    } else {
+        for (int32_t c0 = a0; c0 < a1; c0 += CH) {
+            const bool nxt = c0 + CH < a1;
+            const int Ln = nxt ? min(CH, a1 - c0 - CH) : 0;
+            const int L = min(CH, a1 - c0);
+            const int pc = ((c0 - a0) / CH) & 1;         // parity of chunk c
+            set_lane();
+            // ---- A1: K^T(c); forward substitution of the four diagonal 16x16
+            // blocks of chunk c (wave WF: lane = 16 block + column c).  Lane c
+            // holds column c of each row of the block; row r's entry A[r][j]
+            // reaches every lane of the block by a DPP row broadcast from lane
+            // j.  Right-looking order: once T[j][c] is final, every later row r
+            // adds A[r][j] T[j][c], so each row still accumulates its terms in
+            // ascending j.
+            if (wave == GW) coefs(L, pc);
+            if (wave != WF && nxt) fetch(c0 + CH, Ln);
+            if (wave == WF) {
+                __builtin_amdgcn_s_setprio(2);
+                const int b = lane >> 4;
+                const int c = lane & 15;
+                float* blk = &sm.g[(16 * b) * SF + 16 * b];
+                float ar[16], acc[16], tc[16];
+#pragma unroll
+                for (int r = 1; r < 16; ++r) { ar[r] = blk[r * SF + c]; acc[r] = 0.0f; }
+                tc[0] = (c == 0) ? 1.0f : 0.0f;
+#pragma unroll
+                for (int j = 0; j < 15; ++j) {
+#pragma unroll
+                    for (int r = j + 1; r < 16; ++r) acc[r] = fmaf(row_bcast(ar[r], j), tc[j], acc[r]);
+                    tc[j + 1] = (j + 1 > c) ? -acc[j + 1] : ((j + 1 == c) ? 1.0f : 0.0f);
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) blk[r * SF + c] = tc[r];
+                __builtin_amdgcn_s_setprio(0);
+            } else if (wave == WM || wave == WM + 1) {
+                epi_mp();                        // M o P-hat(c), rows of this wave
+            }
+            __syncthreads();
+            // ---- A2: K^T(c); merge 16 -> 32 for block pairs (0,1), (2,3) on
+            // fp32 MFMA (wave WM + pair): X = A21 T11 through the LDS scratch and
+            // straight back into the same wave, then T21 = -T22 X
+            stage_kt();
+            if (wave == WF && nxt) fetch(c0 + CH, Ln);
+            if (wave == WM || wave == WM + 1) {
+                __builtin_amdgcn_s_setprio(2);
+                const int pw = wave - WM;
+                const int b0 = 32 * pw, b1 = b0 + 16;
+                float a[4], bb[4];
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    a[kk] = sm.g[(b1 + l16) * SF + b0 + 4 * kk + q4];
+                    bb[kk] = sm.g[(b0 + 4 * kk + q4) * SF + b0 + l16];
+                }
+                f32x4 x = f32x4{0, 0, 0, 0};
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) x = mfma4(a[kk], bb[kk], x);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sm.xs[(16 * pw + 4 * q4 + r) * 36 + l16] = x[r];
+                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    a[kk] = sm.g[(b1 + l16) * SF + b1 + 4 * kk + q4];
+                    bb[kk] = sm.xs[(16 * pw + 4 * kk + q4) * 36 + l16];
+                }
+                f32x4 t = f32x4{0, 0, 0, 0};
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) t = mfma4(a[kk], bb[kk], t);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sm.g[(b1 + 4 * q4 + r) * SF + b0 + l16] = -t[r];
+            }
+            __syncthreads();
+            // ---- A3: merge 32 -> 64 (wave WM + tj: output column block tj of
+            // the lower-left 32x32 block; T21 is left in xs); M o P-hat(c) rows
+            // of waves 4 and 7
+            if (wave == WM || wave == WM + 1) {
+                const int tj = wave - WM;
+                const int k0 = 4 * tj;
+                float a[2][8], bb[8];
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk) {
+                    if (kk < k0) continue;
+                    bb[kk] = sm.g[(4 * kk + q4) * SF + 16 * tj + l16];
+#pragma unroll
+                    for (int ti = 0; ti < 2; ++ti) a[ti][kk] = sm.g[(32 + 16 * ti + l16) * SF + 4 * kk + q4];
+                }
+                f32x4 x[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk) {
+                    if (kk < k0) continue;
+#pragma unroll
+                    for (int ti = 0; ti < 2; ++ti) x[ti] = mfma4(a[ti][kk], bb[kk], x[ti]);
+                }
+#pragma unroll
+                for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sm.xs[(16 * ti + 4 * q4 + r) * 36 + 16 * tj + l16] = x[ti][r];
+                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk) {
+                    bb[kk] = sm.xs[(4 * kk + q4) * 36 + 16 * tj + l16];
+#pragma unroll
+                    for (int ti = 0; ti < 2; ++ti) a[ti][kk] = sm.g[(32 + 16 * ti + l16) * SF + 32 + 4 * kk + q4];
+                }
+                f32x4 t[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk) {
+                    t[1] = mfma4(a[1][kk], bb[kk], t[1]);
+                    if (kk < 4) t[0] = mfma4(a[0][kk], bb[kk], t[0]);
+                }
+#pragma unroll
+                for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sm.xs[(16 * ti + 4 * q4 + r) * 36 + 16 * tj + l16] = -t[ti][r];
+                __builtin_amdgcn_s_setprio(0);
+            } else {
+                epi_mp();
+            }
+            __syncthreads();
+            // ---- A4: rows 32-63 of cU
+            cu_part(tid);
+            __syncthreads();
+            // ---- B1: K, Q, V^T(c + 1); gate scan(c + 1)
+            if (nxt) {
+                stage_kqv();
+                if (wave == GW) gate_scan(Ln);
+            }
+            __syncthreads();
+            // ---- B2: G, P, norms(c + 1)
+            if (nxt) gram();
+            __syncthreads();
+            // ---- B3: A, M o P-hat, coefficients(c + 1)
+            if (nxt) epi_a();
+            __syncthreads();
+        }
+    }
+
+    // ---- the final state back to the slot (or the segment's matrix)
+    if (state_w && (!SEG || fin)) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int vb = 0; vb < VB; ++vb) {
+                const int v = 16 * (wave * VB + vb) + l16;
+                *reinterpret_cast<float4*>(fin + static_cast<size_t>(v) * D + 16 * kb + 4 * q4) =
+                    make_float4(st[kb][vb][0], st[kb][vb][1], st[kb][vb][2], st[kb][vb][3]);
+            }
+    }
+}
+
 namespace {
 template <int D, typename IT, typename OT>
 hipError_t run_prefill(const void* q, const void* k, const void* v, const GateArgs& ga,
@@ -1222,6 +2016,20 @@ hipError_t run_prefill(const void* q, const void* k, const void* v, const GateAr
                       static_cast<OT*>(out), d.num_k_heads, d.num_v_heads, sqk, sv, scale, flags,
                       nsr, sg, err);
     };
+    // d = 128 with bf16 inputs: the pipelined chunk step, for whole runs and
+    // unpaired segment runs (the Newton-Schulz variant and paired P/B runs keep
+    // prefill_kernel; both compute the same values bit for bit)
+    if constexpr (D == 128 && std::is_same<IT, bf16_t>::value) {
+        if (ns == 0 && !(sg.pass == 1 && sg.pair)) {
+            auto go2 = [&](auto kernel) {
+                return launch(kernel, grid, dim3(PF_NT), 0, st, static_cast<const bf16_t*>(q),
+                              static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), ga, cu,
+                              slot, rec, static_cast<OT*>(out), d.num_k_heads, d.num_v_heads, sqk,
+                              sv, scale, flags, sg, err);
+            };
+            return sg.pass != 0 ? go2(prefill_pipe_kernel<OT, true>) : go2(prefill_pipe_kernel<OT, false>);
+        }
+    }
     // pass 2 never pairs runs: it takes the unpaired kernel, whose registers
     // are those of a whole-sequence run
     if (sg.pass == 1 && sg.pair)
