@@ -121,13 +121,15 @@ __device__ __forceinline__ float dpp_scan_step(float x) {
 }
 
 // Broadcast lane j of each 16-lane row to the whole row (DPP row_newbcast,
-// controls 0x150 + j on CDNA); j must fold to a constant.
+// controls 0x150 + j on CDNA); j must fold to a constant.  Every lane of the
+// row is written, so no old value is needed: one v_mov_b32_dpp, no zeroing
+// move in front of it.
 __device__ __forceinline__ float row_bcast(float x, int j) {
-#define GDN_RB(J) case J: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + J, 0xF, 0xF, false))
+#define GDN_RB(J) case J: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x150 + J, 0xF, 0xF, false))
     switch (j) {
         GDN_RB(0); GDN_RB(1); GDN_RB(2); GDN_RB(3); GDN_RB(4); GDN_RB(5); GDN_RB(6); GDN_RB(7);
         GDN_RB(8); GDN_RB(9); GDN_RB(10); GDN_RB(11); GDN_RB(12); GDN_RB(13); GDN_RB(14);
-        default: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + 15, 0xF, 0xF, false));
+        default: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x150 + 15, 0xF, 0xF, false));
     }
 #undef GDN_RB
 }
@@ -1683,7 +1685,8 @@ __global__ __launch_bounds__(PF_NT) void prefill_pipe_kernel(
                 }
             };
 
-            // ---- A1: Z = K S0^T
+            // ---- A1: Z = K S0^T (O1 runs in A3, where the state waves have no
+            // other work; beside Z here it measured the same)
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) early(ks, true, false);
             __syncthreads();
