@@ -20,6 +20,7 @@ FLAG_SILU, FLAG_QK_L2NORM, FLAG_VALIDATE = 1, 2, 4
 FLAG_STEP_FUSED, FLAG_STEP_SPLIT = 8, 16
 FLAG_PREFILL_NS3, FLAG_PREFILL_NS4 = 32, 64
 FLAG_PREFILL_SEQUENTIAL = 128
+FLAG_PREFILL_SINGLE_ROLE = 256
 NORM_GATE_SIGMOID, NORM_ZERO_CENTRED = 1, 2
 EFLAG_SLOT_RANGE, EFLAG_SLOT_REPEAT, EFLAG_SEQLENS = 1, 2, 4
 DEFAULT_DECODE_FLAGS = FLAG_SILU | FLAG_QK_L2NORM

@@ -236,7 +236,8 @@ gdn_status prefill_impl(const void* q, const void* k, const void* v, gdn_dtype i
                         size_t workspace_bytes, int32_t* err_flag, hipStream_t stream) {
     if (gdn_status st = check_flags(flags, GDN_FLAG_QK_L2NORM | GDN_FLAG_VALIDATE |
                                                GDN_FLAG_PREFILL_NS3 | GDN_FLAG_PREFILL_NS4 |
-                                               GDN_FLAG_PREFILL_SEQUENTIAL,
+                                               GDN_FLAG_PREFILL_SEQUENTIAL |
+                                               GDN_FLAG_PREFILL_SINGLE_ROLE,
                                     err_flag))
         return st;
     if ((flags & GDN_FLAG_PREFILL_NS3) && (flags & GDN_FLAG_PREFILL_NS4)) return GDN_ERR_FLAGS;
@@ -437,7 +438,8 @@ gdn_status gdn_mixed_step(const void* x, gdn_dtype x_dt, const float* g, const f
                           hipStream_t stream, hipStream_t prefill_stream, hipEvent_t fork_event,
                           hipEvent_t join_event) {
     if (gdn_status st = check_flags(flags, KNOWN_FLAGS | GDN_FLAG_STEP_FUSED | GDN_FLAG_STEP_SPLIT |
-                                               GDN_FLAG_PREFILL_SEQUENTIAL,
+                                               GDN_FLAG_PREFILL_SEQUENTIAL |
+                                               GDN_FLAG_PREFILL_SINGLE_ROLE,
                                     err_flag))
         return st;
     if ((flags & GDN_FLAG_STEP_FUSED) && (flags & GDN_FLAG_STEP_SPLIT)) return GDN_ERR_FLAGS;
@@ -510,13 +512,13 @@ gdn_status gdn_mixed_step(const void* x, gdn_dtype x_dt, const float* g, const f
         if (sch.seg_len > 0)
             GDN_TRY_LAUNCH(launch_prefill_segmented(yp, yp + Hdk, yp + 2 * Hdk, GDN_BF16, gp, cu_seqlens,
                                                     n_pre, total_pre, sp, rec_state, op, out_dt, *dims,
-                                                    D, D, scale, flags & (GDN_FLAG_QK_L2NORM), sch,
+                                                    D, D, scale, flags & (GDN_FLAG_QK_L2NORM | GDN_FLAG_PREFILL_SINGLE_ROLE), sch,
                                                     reinterpret_cast<float*>(static_cast<char*>(workspace) + base),
                                                     ef, ps));
         else
             GDN_TRY_LAUNCH(launch_prefill(yp, yp + Hdk, yp + 2 * Hdk, GDN_BF16, gp, cu_seqlens, n_pre, sp,
                                           rec_state, op, out_dt, *dims, D, D, scale,
-                                          flags & (GDN_FLAG_QK_L2NORM), ef, ps));
+                                          flags & (GDN_FLAG_QK_L2NORM | GDN_FLAG_PREFILL_SINGLE_ROLE), ef, ps));
         return GDN_OK;
     };
     // sequences without tokens leave their state untouched: nothing to launch

@@ -2021,9 +2021,10 @@ hipError_t run_prefill(const void* q, const void* k, const void* v, const GateAr
     };
     // d = 128 with bf16 inputs: the pipelined chunk step, for whole runs and
     // unpaired segment runs (the Newton-Schulz variant and paired P/B runs keep
-    // prefill_kernel; both compute the same values bit for bit)
+    // prefill_kernel, and so does a call that asks for the single-role step;
+    // both compute the same values bit for bit)
     if constexpr (D == 128 && std::is_same<IT, bf16_t>::value) {
-        if (ns == 0 && !(sg.pass == 1 && sg.pair)) {
+        if (ns == 0 && !(sg.pass == 1 && sg.pair) && !(flags & GDN_FLAG_PREFILL_SINGLE_ROLE)) {
             auto go2 = [&](auto kernel) {
                 return launch(kernel, grid, dim3(PF_NT), 0, st, static_cast<const bf16_t*>(q),
                               static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), ga, cu,

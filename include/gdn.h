@@ -106,8 +106,10 @@ enum {
     GDN_FLAG_STEP_SPLIT = 16, /* gdn_decode_step: force conv kernel + recurrence  */
     GDN_FLAG_PREFILL_NS3 = 32, /* prefill A/B variant: diagonal KK^T blocks by   */
     GDN_FLAG_PREFILL_NS4 = 64, /* 3 or 4 bf16 Newton-Schulz rounds (see below)   */
-    GDN_FLAG_PREFILL_SEQUENTIAL = 128 /* prefill: never split sequences into      */
-                                      /* segments (see gdn_prefill_chunked)       */
+    GDN_FLAG_PREFILL_SEQUENTIAL = 128, /* prefill: never split sequences into     */
+                                       /* segments (see gdn_prefill_chunked)      */
+    GDN_FLAG_PREFILL_SINGLE_ROLE = 256 /* prefill: run the chunk step on the      */
+                                       /* single-role kernel (see below)          */
 };
 
 enum {                      /* flags of gdn_gated_rmsnorm                         */
@@ -322,7 +324,13 @@ size_t gdn_prefill_workspace_size(const gdn_dims* dims, int32_t n_seqs, int32_t 
  *                by 3 or 4 Newton-Schulz rounds with bf16 intermediates, as [P4]
  *                "Numerical root cause and fix" describes, instead of the default
  *                exact fp32 forward substitution
- *                or GDN_FLAG_PREFILL_SEQUENTIAL
+ *                or GDN_FLAG_PREFILL_SEQUENTIAL, and GDN_FLAG_PREFILL_SINGLE_ROLE:
+ *                at dk = dv = 128 with bf16 inputs the chunk step normally runs
+ *                on a kernel whose waves split into two roles (half carry the
+ *                state and produce outputs, half build the next chunk's
+ *                coefficients ahead of them); this flag runs it on the
+ *                single-role kernel instead, which computes the same values
+ *                bit for bit (an A/B switch for tests and timing)
  *   workspace    device memory, 16-byte aligned, or NULL.  With at least
  *                gdn_prefill_workspace_size(...) bytes (and that size > 0,
  *                and no GDN_FLAG_PREFILL_SEQUENTIAL) the call runs the
@@ -482,6 +490,7 @@ size_t gdn_mixed_workspace_size(const gdn_dims* dims, int32_t n_dec, int32_t tot
  *                validation over all slot indices and cu_seqlens), the
  *                decode rows' GDN_FLAG_STEP_FUSED / GDN_FLAG_STEP_SPLIT, and
  *                GDN_FLAG_PREFILL_SEQUENTIAL (one run per sequence always)
+ *                and GDN_FLAG_PREFILL_SINGLE_ROLE (as for gdn_prefill_chunked)
  *   workspace    >= gdn_mixed_workspace_size(dims, n_dec, total_pre) bytes;
  *                with gdn_mixed_workspace_size(dims, n_dec, total_pre) +
  *                gdn_prefill_workspace_size(dims, n_pre, total_pre) bytes the

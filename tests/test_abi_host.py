@@ -209,6 +209,27 @@ def test_mixed_step_accepts_sequential_prefill_flag(lib):
     assert _mixed(lib, flags=3 | 32) == ERR_FLAGS
 
 
+def test_single_role_prefill_flag(lib):
+    # GDN_FLAG_PREFILL_SINGLE_ROLE (256) picks the prefill's chunk-step kernel:
+    # prefill calls and the mixed step take it, the decode calls do not
+    chunked = (None, None, None, 1, None, None, None, 0, 0, None, None, 8, None, 1, _dims(), 0.1)
+    assert lib.gdn_prefill_chunked(*chunked, 2 | 256, None, 0, None, None) == OK
+    assert lib.gdn_prefill_chunked(*chunked, 2 | 512, None, 0, None, None) == ERR_FLAGS
+    assert lib.gdn_prefill_segmented(None, None, None, 1, None, None, None, None, 0, 0, None,
+                                     None, 8, None, 1, _dims(), 0.1, 2 | 256, 128, 0, None, 0,
+                                     None, None) == OK
+    assert _mixed(lib, flags=3 | 256, n_dec=0, n_pre=0, total=0, cu=None, ws=None) == OK
+    assert _decode(lib, flags=3 | 256) == ERR_FLAGS
+
+
+def test_header_flag_values_match_binding():
+    text = open(HEADER).read()
+    vals = dict(re.findall(r"\b(GDN_FLAG_[A-Z0-9_]+)\s*=\s*(\d+)", text))
+    for name, v in vals.items():
+        assert getattr(_abi, name[4:]) == int(v), name
+    assert len(vals) == 9
+
+
 def test_mixed_workspace_size(lib):
     d = _dims()
     D = 2 * 16 * 128 + 32 * 128

@@ -278,3 +278,87 @@ def test_newton_schulz_variants_agree_on_random_keys():
         torch.cuda.synchronize()
         eo, es = _errs(p, g, out, [0, 9, 31])
         assert eo <= PREFILL_TOL and es <= PREFILL_TOL, (fl, eo, es)
+
+
+# ---------------------------------------------------------------------------
+# At dk = dv = 128 with bf16 inputs the chunk step runs on the two-role kernel
+# (state waves and coefficient waves); GDN_FLAG_PREFILL_SINGLE_ROLE runs it on
+# the single-role kernel.  Both take the same arithmetic in the same order, so
+# every output and state must match bit for bit, on every schedule.
+def _ab_call(p, flags, out_dtype=torch.bfloat16, gate=None, ws=None, seg=None):
+    g = to_dev(p)
+    dm = p["dims"]
+    dims = gdn.make_dims(dm["H"], dm["HV"], dm["dk"], dm["dv"], 4)
+    T = p["q"].shape[0]
+    out = torch.full((T, dm["HV"], dm["dv"]), float("nan"), dtype=out_dtype, device="cuda")
+    if seg is not None:
+        seg_len, head_len = seg
+        wsb = gdn.gdn_prefill_segmented_workspace_size(dims, len(p["slot_idx"]), T, seg_len)
+        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+        gdn.gdn_prefill_segmented(g["q"], g["k"], g["v"], None if gate else g["g"],
+                                  None if gate else g["beta"], g["cu_seqlens"], g["slot_idx"],
+                                  g["rec_state"], out, dims, 128 ** -0.5, seg_len, flags=flags,
+                                  gate=gate, workspace=ws, head_len=head_len)
+    elif gate is not None:
+        gdn.gdn_prefill_chunked_gated(g["q"], g["k"], g["v"], gate, g["cu_seqlens"],
+                                      g["slot_idx"], g["rec_state"], out, dims, 128 ** -0.5,
+                                      flags=flags, workspace=ws)
+    else:
+        gdn.gdn_prefill_chunked(g["q"], g["k"], g["v"], g["g"], g["beta"], g["cu_seqlens"],
+                                g["slot_idx"], g["rec_state"], out, dims, 128 ** -0.5,
+                                flags=flags, workspace=ws)
+    return out, g["rec_state"]
+
+
+def _ab_equal(p, flags=gdn.FLAG_QK_L2NORM, **kw):
+    oa, sa = _ab_call(p, flags, **kw)
+    ob, sb = _ab_call(p, flags | gdn.FLAG_PREFILL_SINGLE_ROLE, **kw)
+    torch.cuda.synchronize()
+    assert torch.isfinite(oa).all() and torch.isfinite(sa).all()
+    assert torch.equal(oa, ob), "outputs differ between the two chunk-step kernels"
+    assert torch.equal(sa, sb), "states differ between the two chunk-step kernels"
+    return oa
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_pipelined_step_equals_single_role_ragged(out_dtype):
+    """Whole runs: lengths around the 16- and 64-token boundaries, an empty
+    and an inactive sequence, random start states."""
+    lengths = [1, 15, 16, 17, 63, 64, 65, 130, 0, 200, 777]
+    p = gi.prefill_inputs(lengths, 14, H=2, HV=4, dk=128, dv=128, seed=61, state_std=0.1)
+    p["slot_idx"][3] = 0
+    out = _ab_equal(p, gdn.FLAG_QK_L2NORM | gdn.FLAG_PREFILL_SEQUENTIAL, out_dtype=out_dtype)
+    cu = p["cu_seqlens"].tolist()
+    assert torch.all(out[cu[3]:cu[4]] == 0)
+
+
+def test_pipelined_step_equals_single_role_norm_off_and_gated():
+    p = gi.prefill_inputs([70, 64, 5, 300], 6, H=2, HV=4, dk=128, dv=128, seed=62,
+                          qk_normalised=True)
+    _ab_equal(p, 0)
+    T = p["q"].shape[0]
+    gt = gi.gating_inputs(T, 4, seed=63)
+    gate = gdn.GateInputs(gt["a"].cuda(), gt["b"].cuda(), gt["A_log"].cuda(),
+                          gt["dt_bias"].cuda())
+    _ab_equal(p, gate=gate)
+
+
+@pytest.mark.parametrize("seg", [(128, 0), (128, 256), (256, 512)])
+def test_pipelined_step_equals_single_role_segmented(seg):
+    """Segment runs (pass 1 paired and unpaired, pass 2), ragged tails."""
+    p = gi.prefill_inputs([900, 70, 1500, 333], 6, H=2, HV=4, dk=128, dv=128, seed=64,
+                          state_std=0.1)
+    p["g"] *= 0.05
+    _ab_equal(p, seg=seg)
+
+
+def test_pipelined_step_equals_single_role_auto_schedules():
+    """The plain call's own schedules at H=16, HV=32: the busy-chip head/tail
+    schedule with its workspace, and the whole-run schedule without one."""
+    lengths = [1800, 200, 1700, 150, 2300, 100, 1300, 2200]
+    p = gi.prefill_inputs(lengths, 10, seed=65)
+    dims = gdn.make_dims(16, 32, 128, 128, 4)
+    wsb = gdn.gdn_prefill_workspace_size(dims, len(lengths), sum(lengths))
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda") if wsb else None
+    _ab_equal(p, ws=ws)
+    _ab_equal(p)
