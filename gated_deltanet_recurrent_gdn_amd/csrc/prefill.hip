@@ -120,19 +120,88 @@ __device__ __forceinline__ float dpp_scan_step(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xF, false));
 }
 
-// Broadcast lane j of each 16-lane row to the whole row (DPP row_newbcast,
-// controls 0x150 + j on CDNA); j must fold to a constant.  Every lane of the
-// row is written, so no old value is needed: one v_mov_b32_dpp, no zeroing
-// move in front of it.
-__device__ __forceinline__ float row_bcast(float x, int j) {
-#define GDN_RB(J) case J: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x150 + J, 0xF, 0xF, false))
-    switch (j) {
-        GDN_RB(0); GDN_RB(1); GDN_RB(2); GDN_RB(3); GDN_RB(4); GDN_RB(5); GDN_RB(6); GDN_RB(7);
-        GDN_RB(8); GDN_RB(9); GDN_RB(10); GDN_RB(11); GDN_RB(12); GDN_RB(13); GDN_RB(14);
-        default: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x150 + 15, 0xF, 0xF, false));
-    }
-#undef GDN_RB
+// T = (I + A)^-1 for the four unit lower triangular 16x16 diagonal blocks
+// of a chunk, one block per 16-lane row of the wave, by exact fp32 forward
+// substitution in place (blk: the block's top-left element, row stride ld; the
+// strictly lower part holds A, lane c of the row owns column c).
+// Right-looking order: once T[j][c] is final every later row r adds
+// A[r][j] T[j][c], so each row still accumulates its terms in ascending j.
+// The accumulators start at -1 on the diagonal and hold -T, so the negated
+// accumulator is the multiplier with no select per step (for j < c the term
+// is A[r][j] * (-0), which leaves every accumulator's value as it was).
+// Each term is one v_fmac_f32_dpp: the DPP row broadcast row_newbcast:j hands
+// A[r][j] from lane j to the whole row inside the multiply-add (the compiler
+// keeps a separate DPP move in front of each fma).  A VGPR a VALU instruction
+// wrote may be read through DPP only two wait states later; A comes from LDS
+// loads, and the s_nop at the top of every step covers any copy the compiler
+// might place in front of the block.
+#define GDN_FS_FMAC(R, J) "v_fmac_f32_dpp %[c" #R "], %[a" #R "], -%[c" #J "] row_newbcast:" #J \
+                          " row_mask:0xf bank_mask:0xf\n\t"
+#define GDN_FS_ROWS1(J) GDN_FS_FMAC(1, J) GDN_FS_ROWS2(J)
+#define GDN_FS_ROWS2(J) GDN_FS_FMAC(2, J) GDN_FS_ROWS3(J)
+#define GDN_FS_ROWS3(J) GDN_FS_FMAC(3, J) GDN_FS_ROWS4(J)
+#define GDN_FS_ROWS4(J) GDN_FS_FMAC(4, J) GDN_FS_ROWS5(J)
+#define GDN_FS_ROWS5(J) GDN_FS_FMAC(5, J) GDN_FS_ROWS6(J)
+#define GDN_FS_ROWS6(J) GDN_FS_FMAC(6, J) GDN_FS_ROWS7(J)
+#define GDN_FS_ROWS7(J) GDN_FS_FMAC(7, J) GDN_FS_ROWS8(J)
+#define GDN_FS_ROWS8(J) GDN_FS_FMAC(8, J) GDN_FS_ROWS9(J)
+#define GDN_FS_ROWS9(J) GDN_FS_FMAC(9, J) GDN_FS_ROWS10(J)
+#define GDN_FS_ROWS10(J) GDN_FS_FMAC(10, J) GDN_FS_ROWS11(J)
+#define GDN_FS_ROWS11(J) GDN_FS_FMAC(11, J) GDN_FS_ROWS12(J)
+#define GDN_FS_ROWS12(J) GDN_FS_FMAC(12, J) GDN_FS_ROWS13(J)
+#define GDN_FS_ROWS13(J) GDN_FS_FMAC(13, J) GDN_FS_ROWS14(J)
+#define GDN_FS_ROWS14(J) GDN_FS_FMAC(14, J) GDN_FS_ROWS15(J)
+#define GDN_FS_ROWS15(J) GDN_FS_FMAC(15, J)
+#define GDN_FS_OUT [c0] "+v"(acc[0]), [c1] "+v"(acc[1]), [c2] "+v"(acc[2]), [c3] "+v"(acc[3]), \
+                   [c4] "+v"(acc[4]), [c5] "+v"(acc[5]), [c6] "+v"(acc[6]), [c7] "+v"(acc[7]), \
+                   [c8] "+v"(acc[8]), [c9] "+v"(acc[9]), [c10] "+v"(acc[10]), [c11] "+v"(acc[11]), \
+                   [c12] "+v"(acc[12]), [c13] "+v"(acc[13]), [c14] "+v"(acc[14]), [c15] "+v"(acc[15])
+#define GDN_FS_IN [a1] "v"(ar[1]), [a2] "v"(ar[2]), [a3] "v"(ar[3]), [a4] "v"(ar[4]), [a5] "v"(ar[5]), \
+                  [a6] "v"(ar[6]), [a7] "v"(ar[7]), [a8] "v"(ar[8]), [a9] "v"(ar[9]), [a10] "v"(ar[10]), \
+                  [a11] "v"(ar[11]), [a12] "v"(ar[12]), [a13] "v"(ar[13]), [a14] "v"(ar[14]), \
+                  [a15] "v"(ar[15])
+__device__ __forceinline__ void fwd_subst16(float* blk, int ld, int c) {
+    float ar[16], acc[16];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) ar[r] = blk[r * ld + c];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = (r == c) ? -1.0f : 0.0f;
+    asm volatile("s_nop 1\n\t" GDN_FS_ROWS1(0) : GDN_FS_OUT : GDN_FS_IN);
+    asm volatile("s_nop 1\n\t" GDN_FS_ROWS2(1) : GDN_FS_OUT : GDN_FS_IN);
+    asm volatile("s_nop 1\n\t" GDN_FS_ROWS3(2) : GDN_FS_OUT : GDN_FS_IN);
+    asm volatile("s_nop 1\n\t" GDN_FS_ROWS4(3) : GDN_FS_OUT : GDN_FS_IN);
+    asm volatile("s_nop 1\n\t" GDN_FS_ROWS5(4) : GDN_FS_OUT : GDN_FS_IN);
+    asm volatile("s_nop 1\n\t" GDN_FS_ROWS6(5) : GDN_FS_OUT : GDN_FS_IN);
+    asm volatile("s_nop 1\n\t" GDN_FS_ROWS7(6) : GDN_FS_OUT : GDN_FS_IN);
+    asm volatile("s_nop 1\n\t" GDN_FS_ROWS8(7) : GDN_FS_OUT : GDN_FS_IN);
+    asm volatile("s_nop 1\n\t" GDN_FS_ROWS9(8) : GDN_FS_OUT : GDN_FS_IN);
+    asm volatile("s_nop 1\n\t" GDN_FS_ROWS10(9) : GDN_FS_OUT : GDN_FS_IN);
+    asm volatile("s_nop 1\n\t" GDN_FS_ROWS11(10) : GDN_FS_OUT : GDN_FS_IN);
+    asm volatile("s_nop 1\n\t" GDN_FS_ROWS12(11) : GDN_FS_OUT : GDN_FS_IN);
+    asm volatile("s_nop 1\n\t" GDN_FS_ROWS13(12) : GDN_FS_OUT : GDN_FS_IN);
+    asm volatile("s_nop 1\n\t" GDN_FS_ROWS14(13) : GDN_FS_OUT : GDN_FS_IN);
+    asm volatile("s_nop 1\n\t" GDN_FS_ROWS15(14) : GDN_FS_OUT : GDN_FS_IN);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) blk[r * ld + c] = (r < c) ? 0.0f : -acc[r];
 }
+#undef GDN_FS_FMAC
+#undef GDN_FS_ROWS1
+ #undef GDN_FS_ROWS2
+ #undef GDN_FS_ROWS3
+ #undef GDN_FS_ROWS4
+ #undef GDN_FS_ROWS5
+ #undef GDN_FS_ROWS6
+ #undef GDN_FS_ROWS7
+ #undef GDN_FS_ROWS8
+ #undef GDN_FS_ROWS9
+ #undef GDN_FS_ROWS10
+ #undef GDN_FS_ROWS11
+ #undef GDN_FS_ROWS12
+ #undef GDN_FS_ROWS13
+ #undef GDN_FS_ROWS14
+ #undef GDN_FS_ROWS15
+#undef GDN_FS_OUT
+#undef GDN_FS_IN
 
 // K/Q fragment (either slot order): the 8 bf16 at row `row`, columns
 // (c0 + 8q) ^ kq_swz(row); row % 16 is the lane's l16, so the caller passes
@@ -849,20 +918,7 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
             early(T_{}, T_{});
         } else if (wave == WF) {
             const int b = lane >> 4;
-            const int c = lane & 15;
-            float* blk = &sm.g[(16 * b) * SF + 16 * b];
-            float ar[16], acc[16], tc[16];
-#pragma unroll
-            for (int r = 1; r < 16; ++r) { ar[r] = blk[r * SF + c]; acc[r] = 0.0f; }
-            tc[0] = (c == 0) ? 1.0f : 0.0f;
-#pragma unroll
-            for (int j = 0; j < 15; ++j) {
-#pragma unroll
-                for (int r = j + 1; r < 16; ++r) acc[r] = fmaf(row_bcast(ar[r], j), tc[j], acc[r]);
-                tc[j + 1] = (j + 1 > c) ? -acc[j + 1] : ((j + 1 == c) ? 1.0f : 0.0f);
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) blk[r * SF + c] = tc[r];
+            fwd_subst16(&sm.g[(16 * b) * SF + 16 * b], SF, lane & 15);
         } else {
             early(T_{}, T_{});
         }
@@ -1242,20 +1298,24 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
 // The chunk loads go out on waves with nothing else to do in that sub-step:
 // a burst of them stalls the issuing wave for much of the memory latency.
 // LDS ownership follows from that order: K and Q (c) are read in A1-A3 and
-// replaced in B1; V^T(c) is read in A2 and replaced in B1; K^T(c) is read in
+// replaced in B1; V(c) is read in A2 and replaced in B1; K^T(c) is read in
 // B3 and replaced in A2; A / T live in g and xs from B3 to A4; cU is written
 // in A4 and read in B1; M o P-hat is read in B2 and written in B3.  The per-token
 // coefficients the state waves use (e^gamma r_q, c_K, e^gamma r_k, e^gamma_L)
 // are double-buffered by chunk parity.
-struct PipeSmem {
+struct alignas(16) PipeSmem {
     static constexpr int D = 128;
     static constexpr int SK = D + PADK;         // row stride of K, Q (bf16)
-    static constexpr int ST = CH + PADT;        // row stride of K^T, V^T, cU, M o P-hat
+    static constexpr int ST = CH + PADT;        // row stride of K^T, cU, M o P-hat
+    // row stride of V (bf16): 16-byte rows for its staging stores, and rows
+    // four apart 16 banks apart, so that the value-column reads (16 columns x
+    // rows t, t + 4, t + 8, t + 12 per instruction) are conflict-free
+    static constexpr int SV = D + 8;
     static constexpr int SF = CH + PADF;        // row stride of the fp32 64x64 array
     bf16_t k[CH * SK];                          // K   [t][k]
     bf16_t q[CH * SK];                          // Q   [t][k]
     bf16_t kt[D * ST];                          // K^T [k][t]
-    bf16_t vt[D * ST];                          // V^T [v][t]
+    bf16_t v[CH * SV];                          // V   [t][v]
     float g[CH * SF];                           // A, then T in place (block [32:64][0:32] in xs)
     bf16_t cu[2 * CH * ST];                     // cU hi, lo [t][t'], pperm order along t'
     float xs[32 * 36];                          // merge scratch X; finally T[32:64][0:32]
@@ -1418,12 +1478,17 @@ __global__ __launch_bounds__(PF_NT) void prefill_pipe_kernel(
             }
         }
 
-    // Chunk loads (coefficient waves): thread (tp, cg) moves token rows 2tp,
-    // 2tp+1 at columns 8 (cg + 8 pass), through buffer descriptors over the
-    // chunk's rows (rows past its length read as zero), issued two sub-steps
-    // before they are staged; the state waves hold no chunk registers.
-    uint4 pk[2][2], pq[2][2], pv[2][2];          // [pass][row]: K of chunk c; Q, V of c + 1
-    uint4 pk2[2][2];                             // K of chunk c + 1 (K^T(c) is staged from pk)
+    // Chunk loads (coefficient waves), through buffer descriptors over the
+    // chunk's rows (rows past its length read as zero), issued one or two
+    // sub-steps before they are staged; the state waves hold no chunk
+    // registers.  Load i of coefficient wave cw reads rows 16 cw + 4 i .. + 3
+    // of K, Q and V, 16 bytes per lane, so that every load covers four whole
+    // 256-byte rows (eight cache lines, each read once); all three are staged
+    // row-major.  (A token-pair mapping, thread (tp, cg) on rows 2tp, 2tp+1 at
+    // columns 8 (cg + 8 pass), touched 32 rows for 32 bytes each per load, and
+    // issuing the loads stalled the coefficient waves for much of their
+    // sub-step.)
+    uint4 pk2[4], pq[4], pv[4];                  // K, Q, V of chunk c + 1 [load]
     uint32_t pbeta = 0, pg = 0;
     const GateHead gh = gate_head(ga, hv);
     const uint32_t off_kq = static_cast<uint32_t>(h * D) * sizeof(bf16_t);
@@ -1440,15 +1505,12 @@ __global__ __launch_bounds__(PF_NT) void prefill_pipe_kernel(
         const rsrc_t rq_ = make_rsrc(qg + static_cast<size_t>(c) * sqk, Lc * row_kq);
         const rsrc_t rv_ = make_rsrc(vg + static_cast<size_t>(c) * sv, Lc * row_v);
 #pragma unroll
-        for (int pass = 0; pass < 2; ++pass) {
-            const uint32_t kk = static_cast<uint32_t>(8 * (cg + 8 * pass)) * sizeof(bf16_t);
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const uint32_t t = ta + e;
-                pk2[pass][e] = buf_ld16(rk_, t * row_kq + off_kq + kk);
-                pq[pass][e] = buf_ld16(rq_, t * row_kq + off_kq + kk);
-                pv[pass][e] = buf_ld16(rv_, t * row_v + off_v + kk);
-            }
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t tr = static_cast<uint32_t>(16 * (wave & 3) + 4 * i + (lane >> 4));
+            const uint32_t kc = off_kq + static_cast<uint32_t>(16 * (lane & 15));
+            pk2[i] = buf_ld16(rk_, tr * row_kq + kc);
+            pq[i] = buf_ld16(rq_, tr * row_kq + kc);
+            pv[i] = buf_ld16(rv_, tr * row_v + off_v + static_cast<uint32_t>(16 * (lane & 15)));
         }
         if (wave == GW) {                        // the gate-scan wave: token = lane
             const rsrc_t r0 = make_rsrc(gsrc0 + static_cast<size_t>(c) * grow, Lc * grow);
@@ -1463,30 +1525,37 @@ __global__ __launch_bounds__(PF_NT) void prefill_pipe_kernel(
             }
         }
     };
-    // K, Q rows (pperm order along k, swizzled) and V^T from the fetched registers
+    // K, Q rows (pperm order along k, swizzled) and V rows from the fetched registers
     auto stage_kqv = [&]() {
+        const int k0 = 8 * (lane & 15);
+        const int p0 = pperm(k0), p1 = pperm(k0 + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * (wave & 3) + 4 * i + (lane >> 4);
+            const int swt = kq_swz(row);
+            lds_st8(&sm.k[row * SK + (p0 ^ swt)], pk2[i].x, pk2[i].y);
+            lds_st8(&sm.k[row * SK + (p1 ^ swt)], pk2[i].z, pk2[i].w);
+            lds_st8(&sm.q[row * SK + (p0 ^ swt)], pq[i].x, pq[i].y);
+            lds_st8(&sm.q[row * SK + (p1 ^ swt)], pq[i].z, pq[i].w);
+            *reinterpret_cast<uint4*>(&sm.v[row * PipeSmem::SV + 8 * (lane & 15)]) = pv[i];
+        }
+    };
+    // K^T(c) from the K(c) rows in LDS: thread (tp, cg) reads rows 2tp, 2tp+1
+    // at columns 8 (cg + 8 pass) and stores their 32-bit token pairs
+    auto stage_kt = [&]() {
 #pragma unroll
         for (int pass = 0; pass < 2; ++pass) {
             const int k0 = 8 * (cg + 8 * pass);
-            const int p0 = pperm(k0), p1 = pperm(k0 + 4), swt = kq_swz(ta);
+            const int swt = kq_swz(ta);
+            uint4 kw[2];
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
-                lds_st8(&sm.k[(ta + e) * SK + (p0 ^ swt)], pk2[pass][e].x, pk2[pass][e].y);
-                lds_st8(&sm.k[(ta + e) * SK + (p1 ^ swt)], pk2[pass][e].z, pk2[pass][e].w);
-                lds_st8(&sm.q[(ta + e) * SK + (p0 ^ swt)], pq[pass][e].x, pq[pass][e].y);
-                lds_st8(&sm.q[(ta + e) * SK + (p1 ^ swt)], pq[pass][e].z, pq[pass][e].w);
+                const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(&sm.k[(ta + e) * SK + (pperm(k0) ^ swt)]);
+                const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(&sm.k[(ta + e) * SK + (pperm(k0 + 4) ^ swt)]);
+                kw[e] = uint4{lo[0], lo[1], hi[0], hi[1]};
             }
-            store_pairs_t(sm.vt, ST, k0, ta, pv[pass][0], pv[pass][1]);
+            store_pairs_t(sm.kt, ST, k0, pperm(ta), kw[0], kw[1]);
         }
-#pragma unroll
-        for (int pass = 0; pass < 2; ++pass)
-#pragma unroll
-            for (int e = 0; e < 2; ++e) pk[pass][e] = pk2[pass][e];
-    };
-    auto stage_kt = [&]() {
-#pragma unroll
-        for (int pass = 0; pass < 2; ++pass)
-            store_pairs_t(sm.kt, ST, 8 * (cg + 8 * pass), pperm(ta), pk[pass][0], pk[pass][1]);
     };
     // cU = T diag(beta), hi/lo, pperm order along t' (thread t < 512: row t / 8,
     // eight columns)
@@ -1690,9 +1759,8 @@ __global__ __launch_bounds__(PF_NT) void prefill_pipe_kernel(
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) early(ks, true, false);
             __syncthreads();
-            // ---- A2: Y = V - diag(cy) Z in fp32 (V from V^T: four consecutive
-            // tokens of one value column per lane, the accumulator layout), split
-            // hi/lo
+            // ---- A2: Y = V - diag(cy) Z in fp32 (four consecutive tokens of
+            // one value column per lane, the accumulator layout), split hi/lo
             bf16x8 yh[2][VB], yl[2][VB];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
@@ -1707,9 +1775,8 @@ __global__ __launch_bounds__(PF_NT) void prefill_pipe_kernel(
                         const float4 cyv = *reinterpret_cast<const float4*>(&sm.cy[p][tt]);
                         float vv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
                         if (use_v) {
-                            const uint2 w = *reinterpret_cast<const uint2*>(&sm.vt[vr * ST + tt]);
-                            vv[0] += bf16lo_to_f32(w.x); vv[1] += bf16hi_to_f32(w.x);
-                            vv[2] += bf16lo_to_f32(w.y); vv[3] += bf16hi_to_f32(w.y);
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) vv[r] += bf16_to_f32(sm.v[(tt + r) * PipeSmem::SV + vr]);
                         }
                         nn[e][0] = vv[0] - cyv.x * z[tb][vb][0];
                         nn[e][1] = vv[1] - cyv.y * z[tb][vb][1];
@@ -1874,20 +1941,7 @@ __global__ __launch_bounds__(PF_NT) void prefill_pipe_kernel(
             if (wave == WF) {
                 __builtin_amdgcn_s_setprio(2);
                 const int b = lane >> 4;
-                const int c = lane & 15;
-                float* blk = &sm.g[(16 * b) * SF + 16 * b];
-                float ar[16], acc[16], tc[16];
-#pragma unroll
-                for (int r = 1; r < 16; ++r) { ar[r] = blk[r * SF + c]; acc[r] = 0.0f; }
-                tc[0] = (c == 0) ? 1.0f : 0.0f;
-#pragma unroll
-                for (int j = 0; j < 15; ++j) {
-#pragma unroll
-                    for (int r = j + 1; r < 16; ++r) acc[r] = fmaf(row_bcast(ar[r], j), tc[j], acc[r]);
-                    tc[j + 1] = (j + 1 > c) ? -acc[j + 1] : ((j + 1 == c) ? 1.0f : 0.0f);
-                }
-#pragma unroll
-                for (int r = 0; r < 16; ++r) blk[r * SF + c] = tc[r];
+                fwd_subst16(&sm.g[(16 * b) * SF + 16 * b], SF, lane & 15);
                 __builtin_amdgcn_s_setprio(0);
             } else if (wave == WM || wave == WM + 1) {
                 epi_mp();                        // M o P-hat(c), rows of this wave
