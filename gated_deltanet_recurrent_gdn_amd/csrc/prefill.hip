@@ -1631,29 +1631,42 @@ __global__ __launch_bounds__(PF_NT) void prefill_pipe_kernel(
     auto coefs = [&](int L, int pc) {
         const float gl = sm.gam[L - 1];
         const float gv = sm.gam[lane];
+        const float rql = sm.rq[lane], rkl = sm.rk[lane];
+        asm volatile("" :: "v"(rkl));            // (no read inside the masked select)
         const float et = __expf(gv);
-        sm.eg[pc][lane] = et * sm.rq[lane];
-        sm.ck[pc][lane] = (lane < L) ? __expf(gl - gv) * sm.rk[lane] : 0.0f;
-        sm.cy[pc][lane] = et * sm.rk[lane];
+        const float ck = __expf(gl - gv) * rkl;
+        sm.eg[pc][lane] = et * rql;
+        sm.ck[pc][lane] = (lane < L) ? ck : 0.0f;
+        sm.cy[pc][lane] = et * rkl;
         if (lane == 0) sm.egl[pc] = __expf(gl);
     };
     // A (fp32 into g) and, separately, M o P-hat (hi/lo into mp) from this
     // wave's G and P tiles: row i = 16 tb + l16, columns c .. c + 3
+    // Both read every operand from LDS first and evaluate the decay
+    // exponentials unconditionally (a masked one may overflow; the select drops
+    // it), so the reads overlap and no lane mask splits the code; for A the
+    // decay's own mask (c <= i) is implied by A's (c < i).
     auto epi_a = [&]() {
         const int i = 16 * tb_c + l16;
+        float4 gc[4], rkc[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            gc[j] = *reinterpret_cast<const float4*>(&sm.gam[16 * j + 4 * q4]);
+            rkc[j] = *reinterpret_cast<const float4*>(&sm.rk[16 * j + 4 * q4]);
+        }
+        // (keeps the compiler from sinking a read into a masked branch)
+        asm volatile("" :: "v"(gc[0].x), "v"(rkc[0].x));
         const float gi = sm.gam[i];
         const float brk = sm.beta[i] * sm.rk[i];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int c = 16 * j + 4 * q4;
-            const float4 gc = *reinterpret_cast<const float4*>(&sm.gam[c]);
-            const float4 rkc = *reinterpret_cast<const float4*>(&sm.rk[c]);
-            const float gcs[4] = {gc.x, gc.y, gc.z, gc.w};
-            const float rks[4] = {rkc.x, rkc.y, rkc.z, rkc.w};
+            const float gcs[4] = {gc[j].x, gc[j].y, gc[j].z, gc[j].w};
+            const float rks[4] = {rkc[j].x, rkc[j].y, rkc[j].z, rkc[j].w};
             f32x4 a;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float dec = (c + r <= i) ? __expf(gi - gcs[r]) : 0.0f;
+                const float dec = __expf(gi - gcs[r]);
                 a[r] = (c + r < i) ? (brk * rks[r]) * (dec * accg[j][r]) : 0.0f;
             }
             *reinterpret_cast<float4*>(&sm.g[i * SF + c]) = make_float4(a[0], a[1], a[2], a[3]);
@@ -1661,19 +1674,25 @@ __global__ __launch_bounds__(PF_NT) void prefill_pipe_kernel(
     };
     auto epi_mp = [&]() {
         const int i = 16 * tb_c + l16;
+        float4 gc[4], rkc[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            gc[j] = *reinterpret_cast<const float4*>(&sm.gam[16 * j + 4 * q4]);
+            rkc[j] = *reinterpret_cast<const float4*>(&sm.rk[16 * j + 4 * q4]);
+        }
+        asm volatile("" :: "v"(gc[0].x), "v"(rkc[0].x));
         const float gi = sm.gam[i];
         const float rqi = sm.rq[i];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int c = 16 * j + 4 * q4;
-            const float4 gc = *reinterpret_cast<const float4*>(&sm.gam[c]);
-            const float4 rkc = *reinterpret_cast<const float4*>(&sm.rk[c]);
-            const float gcs[4] = {gc.x, gc.y, gc.z, gc.w};
-            const float rks[4] = {rkc.x, rkc.y, rkc.z, rkc.w};
+            const float gcs[4] = {gc[j].x, gc[j].y, gc[j].z, gc[j].w};
+            const float rks[4] = {rkc[j].x, rkc[j].y, rkc[j].z, rkc[j].w};
             f32x4 mp;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float dec = (c + r <= i) ? __expf(gi - gcs[r]) : 0.0f;
+                const float ev = __expf(gi - gcs[r]);
+                const float dec = (c + r <= i) ? ev : 0.0f;
                 mp[r] = (rqi * rks[r]) * (dec * accp[j][r]);
             }
             uint2 h2, l2;
