@@ -1277,32 +1277,34 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
 //     wave 7, merges on waves 5 and 6), form its cU, and then build chunk
 //     c + 1's gate scan, G = K K^T, P = Q K^T, norms, A and M o P-hat while the
 //     state waves finish chunk c.
-// One chunk step is seven barrier-separated sub-steps.  The two roles run as
-// two loops over the same chunks with the same seven barriers per chunk, so
+// One chunk step is six barrier-separated sub-steps.  The two roles run as
+// two loops over the same chunks with the same six barriers per chunk, so
 // every barrier is met by all eight waves:
 //   A1  state: Z                        coef: forward substitution (wave 7);
 //                                             eg/ck/cy(c) (wave 4); loads of chunk
 //                                             c+1 (waves 4-6); M o P-hat(c) rows (5, 6)
 //   A2  state: Y = V - cy Z             coef: stage K^T(c); loads (wave 7);
 //                                             merge 16 -> 32 (waves 5, 6)
-//   A3  state: O1, scaled               coef: merge 32 -> 64 (waves 5, 6);
+//   A3  state: O1, scaled; cU(c) of the coef: merge 32 -> 64 and the cU(c) of
+//       diagonal 32x32 blocks                 that block (waves 5, 6);
 //                                             M o P-hat(c) rows (waves 4, 7)
-//   A4  all: cU(c) (rows 0-31 on the state waves, 32-63 on the coefficient waves)
-//   B1  state: U = cU Y                 coef: stage K, Q, V^T(c+1); gate scan(c+1)
+//   B1  state: U = cU Y                 coef: stage K, Q, V(c+1); gate scan(c+1)
 //   B2  state: O (stored)               coef: G, P, norms(c+1)
-//   B3  state: cK . U, the state update coef: A(c+1)
-// Each coefficient wave keeps its G and P tiles of chunk c+1 in registers from
-// B2 to the next chunk's M o P-hat step, so that work lands where the wave has
-// slack.  The waves on the critical path of their sub-step (substitution,
-// merges) raise their issue priority over the state wave sharing their SIMD.
-// The chunk loads go out on waves with nothing else to do in that sub-step:
-// a burst of them stalls the issuing wave for much of the memory latency.
+//   B3  state: cK . U, the state update coef: A(c+1), and the masked decays
+//                                             its M o P-hat reuses
+// Each coefficient wave keeps its G and P tiles of chunk c+1 and the decays in
+// registers from B2/B3 to the next chunk's M o P-hat step, so that work lands
+// where the wave has slack.  The waves on the critical path of their sub-step
+// (substitution, merges) raise their issue priority over the state wave
+// sharing their SIMD.  The chunk loads go out on waves with little else to do
+// in that sub-step.
 // LDS ownership follows from that order: K and Q (c) are read in A1-A3 and
 // replaced in B1; V(c) is read in A2 and replaced in B1; K^T(c) is read in
-// B3 and replaced in A2; A / T live in g and xs from B3 to A4; cU is written
-// in A4 and read in B1; M o P-hat is read in B2 and written in B3.  The per-token
-// coefficients the state waves use (e^gamma r_q, c_K, e^gamma r_k, e^gamma_L)
-// are double-buffered by chunk parity.
+// B3 and replaced in A2; A / T live in g (and the merge scratch xs) from B3 to
+// A3; cU is written in A3 and read in B1; M o P-hat is written in A1 and A3
+// and read in B2.  The per-token coefficients the state waves use
+// (e^gamma r_q, c_K, e^gamma r_k, e^gamma_L) are double-buffered by chunk
+// parity.
 struct alignas(16) PipeSmem {
     static constexpr int D = 128;
     static constexpr int SK = D + PADK;         // row stride of K, Q (bf16)
@@ -1557,12 +1559,16 @@ __global__ __launch_bounds__(PF_NT) void prefill_pipe_kernel(
             store_pairs_t(sm.kt, ST, k0, pperm(ta), kw[0], kw[1]);
         }
     };
-    // cU = T diag(beta), hi/lo, pperm order along t' (thread t < 512: row t / 8,
-    // eight columns)
+    // cU = T diag(beta), hi/lo, pperm order along t', for the blocks of T in
+    // g: rows 0-31 x columns 0-31 and rows 32-63 x columns 32-63 (state thread
+    // t < 256: row r, eight columns from cb).  The block rows 32-63 x columns
+    // 0-31 comes from the 32 -> 64 merge's registers, and rows 0-31 x columns
+    // 32-63 (zero) is never read.
     auto cu_part = [&](int t) {
-        const int r = t >> 3, cb = 8 * (t & 7);
+        const int r = (t < 128) ? (t >> 2) : 32 + ((t - 128) >> 2);
+        const int cb = (t < 128) ? 8 * (t & 3) : 32 + 8 * (t & 3);
         uint32_t uh[4], ul[4];
-        const float* trow = (r >= 32 && cb < 32) ? &sm.xs[(r - 32) * 36 + cb] : &sm.g[r * SF + cb];
+        const float* trow = &sm.g[r * SF + cb];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const float4 tv = *reinterpret_cast<const float4*>(trow + 4 * j);
@@ -1598,6 +1604,7 @@ __global__ __launch_bounds__(PF_NT) void prefill_pipe_kernel(
     // columns), and the diagonal block of Q Q^T; the norms from the diagonals
     const int tb_c = wave & 3;
     f32x4 accg[4], accp[4], accq;
+    float dmp[4][4];                             // masked decays of the row block, epi_a -> epi_mp
     auto gram = [&]() {
         accq = f32x4{0, 0, 0, 0};
 #pragma unroll
@@ -1642,10 +1649,12 @@ __global__ __launch_bounds__(PF_NT) void prefill_pipe_kernel(
     };
     // A (fp32 into g) and, separately, M o P-hat (hi/lo into mp) from this
     // wave's G and P tiles: row i = 16 tb + l16, columns c .. c + 3
-    // Both read every operand from LDS first and evaluate the decay
+    // epi_a reads every operand from LDS first and evaluates the decay
     // exponentials unconditionally (a masked one may overflow; the select drops
     // it), so the reads overlap and no lane mask splits the code; for A the
-    // decay's own mask (c <= i) is implied by A's (c < i).
+    // decay's own mask (c <= i) is implied by A's (c < i).  It keeps the masked
+    // decays of its row block in registers for that block's M o P-hat (the same
+    // chunk, one or two sub-steps later).
     auto epi_a = [&]() {
         const int i = 16 * tb_c + l16;
         float4 gc[4], rkc[4];
@@ -1668,33 +1677,24 @@ __global__ __launch_bounds__(PF_NT) void prefill_pipe_kernel(
             for (int r = 0; r < 4; ++r) {
                 const float dec = __expf(gi - gcs[r]);
                 a[r] = (c + r < i) ? (brk * rks[r]) * (dec * accg[j][r]) : 0.0f;
+                dmp[j][r] = (c + r <= i) ? dec : 0.0f;
             }
             *reinterpret_cast<float4*>(&sm.g[i * SF + c]) = make_float4(a[0], a[1], a[2], a[3]);
         }
     };
     auto epi_mp = [&]() {
         const int i = 16 * tb_c + l16;
-        float4 gc[4], rkc[4];
+        float4 rkc[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            gc[j] = *reinterpret_cast<const float4*>(&sm.gam[16 * j + 4 * q4]);
-            rkc[j] = *reinterpret_cast<const float4*>(&sm.rk[16 * j + 4 * q4]);
-        }
-        asm volatile("" :: "v"(gc[0].x), "v"(rkc[0].x));
-        const float gi = sm.gam[i];
+        for (int j = 0; j < 4; ++j) rkc[j] = *reinterpret_cast<const float4*>(&sm.rk[16 * j + 4 * q4]);
         const float rqi = sm.rq[i];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int c = 16 * j + 4 * q4;
-            const float gcs[4] = {gc[j].x, gc[j].y, gc[j].z, gc[j].w};
             const float rks[4] = {rkc[j].x, rkc[j].y, rkc[j].z, rkc[j].w};
             f32x4 mp;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float ev = __expf(gi - gcs[r]);
-                const float dec = (c + r <= i) ? ev : 0.0f;
-                mp[r] = (rqi * rks[r]) * (dec * accp[j][r]);
-            }
+            for (int r = 0; r < 4; ++r) mp[r] = (rqi * rks[r]) * (dmp[j][r] * accp[j][r]);
             uint2 h2, l2;
             split4(mp, h2, l2);
             lds_st8(&sm.mp[i * ST + (pperm(c) ^ swm)], h2.x, h2.y);
@@ -1822,8 +1822,7 @@ __global__ __launch_bounds__(PF_NT) void prefill_pipe_kernel(
                     }
                 }
             }
-            __syncthreads();
-            // ---- A4: rows 0-31 of cU
+            // cU(c) outside the 32 -> 64 merge's block
             cu_part(tid);
             __syncthreads();
             // ---- B1: U = cU Y (cU lower triangular: blocks above the diagonal
@@ -2000,8 +1999,8 @@ __global__ __launch_bounds__(PF_NT) void prefill_pipe_kernel(
             }
             __syncthreads();
             // ---- A3: merge 32 -> 64 (wave WM + tj: output column block tj of
-            // the lower-left 32x32 block; T21 is left in xs); M o P-hat(c) rows
-            // of waves 4 and 7
+            // the lower-left 32x32 block T21, whose cU block goes straight from
+            // the accumulators to cU); M o P-hat(c) rows of waves 4 and 7
             if (wave == WM || wave == WM + 1) {
                 const int tj = wave - WM;
                 const int k0 = 4 * tj;
@@ -2037,17 +2036,30 @@ __global__ __launch_bounds__(PF_NT) void prefill_pipe_kernel(
                     t[1] = mfma4(a[1][kk], bb[kk], t[1]);
                     if (kk < 4) t[0] = mfma4(a[0][kk], bb[kk], t[0]);
                 }
+                // cU = T21 diag(beta) (lane: rows 32 + 16 ti + 4 q4 + r, column
+                // 16 tj + l16), hi/lo, one bf16 per store
+                const float bc = sm.beta[16 * tj + l16];
+                const int pcol = pperm(16 * tj + l16);
 #pragma unroll
-                for (int ti = 0; ti < 2; ++ti)
+                for (int ti = 0; ti < 2; ++ti) {
+                    f32x4 u;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) sm.xs[(16 * ti + 4 * q4 + r) * 36 + 16 * tj + l16] = -t[ti][r];
+                    for (int r = 0; r < 4; ++r) u[r] = -t[ti][r] * bc;
+                    uint2 h2, l2;
+                    split4(u, h2, l2);
+                    const uint32_t hv[4] = {h2.x, h2.x >> 16, h2.y, h2.y >> 16};
+                    const uint32_t lv[4] = {l2.x, l2.x >> 16, l2.y, l2.y >> 16};
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        bf16_t* dst = sm.cu + (32 + 16 * ti + 4 * q4 + r) * ST + pcol;
+                        dst[0] = static_cast<bf16_t>(hv[r]);
+                        dst[CH * ST] = static_cast<bf16_t>(lv[r]);
+                    }
+                }
                 __builtin_amdgcn_s_setprio(0);
             } else {
                 epi_mp();
             }
-            __syncthreads();
-            // ---- A4: rows 32-63 of cU
-            cu_part(tid);
             __syncthreads();
             // ---- B1: K, Q, V^T(c + 1); gate scan(c + 1)
             if (nxt) {
