@@ -2001,21 +2001,22 @@ __global__ __launch_bounds__(PF_NT) void prefill_pipe_kernel(
             // ---- A3: merge 32 -> 64 (wave WM + tj: output column block tj of
             // the lower-left 32x32 block T21, whose cU block goes straight from
             // the accumulators to cU); M o P-hat(c) rows of waves 4 and 7
-            if (wave == WM || wave == WM + 1) {
-                const int tj = wave - WM;
-                const int k0 = 4 * tj;
+            // (the column block is a compile-time constant in each wave's copy,
+            // so the triangular k-ranges unroll with every operand read issued
+            // up front)
+            auto merge2 = [&](auto tjc) {
+                constexpr int tj = decltype(tjc)::value;
+                constexpr int k0 = 4 * tj;
                 float a[2][8], bb[8];
 #pragma unroll
-                for (int kk = 0; kk < 8; ++kk) {
-                    if (kk < k0) continue;
+                for (int kk = k0; kk < 8; ++kk) {
                     bb[kk] = sm.g[(4 * kk + q4) * SF + 16 * tj + l16];
 #pragma unroll
                     for (int ti = 0; ti < 2; ++ti) a[ti][kk] = sm.g[(32 + 16 * ti + l16) * SF + 4 * kk + q4];
                 }
                 f32x4 x[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
 #pragma unroll
-                for (int kk = 0; kk < 8; ++kk) {
-                    if (kk < k0) continue;
+                for (int kk = k0; kk < 8; ++kk) {
 #pragma unroll
                     for (int ti = 0; ti < 2; ++ti) x[ti] = mfma4(a[ti][kk], bb[kk], x[ti]);
                 }
@@ -2056,6 +2057,12 @@ __global__ __launch_bounds__(PF_NT) void prefill_pipe_kernel(
                         dst[CH * ST] = static_cast<bf16_t>(lv[r]);
                     }
                 }
+            };
+            if (wave == WM) {
+                merge2(std::integral_constant<int, 0>{});
+                __builtin_amdgcn_s_setprio(0);
+            } else if (wave == WM + 1) {
+                merge2(std::integral_constant<int, 1>{});
                 __builtin_amdgcn_s_setprio(0);
             } else {
                 epi_mp();
