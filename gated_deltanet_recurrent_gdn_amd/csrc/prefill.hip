@@ -1283,22 +1283,25 @@ __global__ __launch_bounds__(PF_NT) void prefill_kernel(
 //   A1  state: Z                        coef: forward substitution (wave 7);
 //                                             eg/ck/cy(c) (wave 4); loads of chunk
 //                                             c+1 (waves 4-6); M o P-hat(c) rows (5, 6)
-//   A2  state: Y = V - cy Z             coef: stage K^T(c); loads (wave 7);
-//                                             merge 16 -> 32 (waves 5, 6)
-//   A3  state: O1, scaled; cU(c) of the coef: merge 32 -> 64 and the cU(c) of
-//       diagonal 32x32 blocks                 that block (waves 5, 6);
+//   A2  state: O1, scaled (its MFMAs    coef: stage K^T(c); loads (wave 7);
+//       overlap Y's vector work);             merge 16 -> 32 (waves 5, 6)
+//       Y = V - cy Z
+//   A3  state: cU(c) of the diagonal    coef: merge 32 -> 64 and the cU(c) of
+//       32x32 blocks                          that block (waves 5, 6);
 //                                             M o P-hat(c) rows (waves 4, 7)
 //   B1  state: U = cU Y                 coef: stage K, Q, V(c+1); gate scan(c+1)
 //   B2  state: O (stored)               coef: G, P, norms(c+1)
 //   B3  state: cK . U, the state update coef: A(c+1), and the masked decays
 //                                             its M o P-hat reuses
+// (O1 sits beside Y rather than beside the 32 -> 64 merge: the two waves of a
+// SIMD then do not both issue MFMAs in the same sub-step.)
 // Each coefficient wave keeps its G and P tiles of chunk c+1 and the decays in
 // registers from B2/B3 to the next chunk's M o P-hat step, so that work lands
 // where the wave has slack.  The waves on the critical path of their sub-step
 // (substitution, merges) raise their issue priority over the state wave
 // sharing their SIMD.  The chunk loads go out on waves with little else to do
 // in that sub-step.
-// LDS ownership follows from that order: K and Q (c) are read in A1-A3 and
+// LDS ownership follows from that order: K and Q (c) are read in A1-A2 and
 // replaced in B1; V(c) is read in A2 and replaced in B1; K^T(c) is read in
 // B3 and replaced in A2; A / T live in g (and the merge scratch xs) from B3 to
 // A3; cU is written in A3 and read in B1; M o P-hat is written in A1 and A3
@@ -1505,7 +1508,9 @@ __global__ __launch_bounds__(PF_NT) void prefill_pipe_kernel(
     auto fetch = [&](int32_t c, int Lc) {
         const rsrc_t rk_ = make_rsrc(kg + static_cast<size_t>(c) * sqk, Lc * row_kq);
         const rsrc_t rq_ = make_rsrc(qg + static_cast<size_t>(c) * sqk, Lc * row_kq);
-        const rsrc_t rv_ = make_rsrc(vg + static_cast<size_t>(c) * sv, Lc * row_v);
+        // (runs that take no values, the segment transition runs, get an empty
+        // range: V reads as zero)
+        const rsrc_t rv_ = make_rsrc(vg + static_cast<size_t>(c) * sv, use_v ? Lc * row_v : 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const uint32_t tr = static_cast<uint32_t>(16 * (wave & 3) + 4 * i + (lane >> 4));
@@ -1778,7 +1783,19 @@ __global__ __launch_bounds__(PF_NT) void prefill_pipe_kernel(
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) early(ks, true, false);
             __syncthreads();
-            // ---- A2: Y = V - diag(cy) Z in fp32 (four consecutive tokens of
+            // ---- A2: O1^T = S0 Q^T, scaled by e^gamma_t r_q (also in runs
+            // that store no outputs, so that it interleaves with Y)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) early(ks, false, true);
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                const float e = sm.eg[p][16 * tb + l16];
+#pragma unroll
+                for (int vb = 0; vb < VB; ++vb) {
+                    o[vb][tb][0] *= e; o[vb][tb][1] *= e; o[vb][tb][2] *= e; o[vb][tb][3] *= e;
+                }
+            }
+            // Y = V - diag(cy) Z in fp32 (four consecutive tokens of
             // one value column per lane, the accumulator layout), split hi/lo
             bf16x8 yh[2][VB], yl[2][VB];
 #pragma unroll
@@ -1793,10 +1810,8 @@ __global__ __launch_bounds__(PF_NT) void prefill_pipe_kernel(
                         const int tt = 16 * tb + 4 * q4;
                         const float4 cyv = *reinterpret_cast<const float4*>(&sm.cy[p][tt]);
                         float vv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-                        if (use_v) {
 #pragma unroll
-                            for (int r = 0; r < 4; ++r) vv[r] += bf16_to_f32(sm.v[(tt + r) * PipeSmem::SV + vr]);
-                        }
+                        for (int r = 0; r < 4; ++r) vv[r] += bf16_to_f32(sm.v[(tt + r) * PipeSmem::SV + vr]);
                         nn[e][0] = vv[0] - cyv.x * z[tb][vb][0];
                         nn[e][1] = vv[1] - cyv.y * z[tb][vb][1];
                         nn[e][2] = vv[2] - cyv.z * z[tb][vb][2];
@@ -1809,19 +1824,7 @@ __global__ __launch_bounds__(PF_NT) void prefill_pipe_kernel(
                     yl[ks][vb] = as_bf16x8(cat(l0, l1));
                 }
             __syncthreads();
-            // ---- A3: O1^T = S0 Q^T, scaled by e^gamma_t r_q
-            if (wo) {
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) early(ks, false, true);
-#pragma unroll
-                for (int tb = 0; tb < 4; ++tb) {
-                    const float e = sm.eg[p][16 * tb + l16];
-#pragma unroll
-                    for (int vb = 0; vb < VB; ++vb) {
-                        o[vb][tb][0] *= e; o[vb][tb][1] *= e; o[vb][tb][2] *= e; o[vb][tb][3] *= e;
-                    }
-                }
-            }
+            // ---- A3
             // cU(c) outside the 32 -> 64 merge's block
             cu_part(tid);
             __syncthreads();
