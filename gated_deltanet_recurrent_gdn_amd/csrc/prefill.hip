@@ -1328,6 +1328,10 @@ struct alignas(16) PipeSmem {
     float gam[CH], beta[CH], rk[CH], rq[CH];
     float eg[2][CH], ck[2][CH], cy[2][CH];
     float egl[2];
+    // bf16 output tile of the chunk [t][v] (row stride SO): written by the state
+    // waves in B2 from their accumulators, stored as whole 256-byte rows in B3
+    static constexpr int SO = D + 8;
+    bf16_t ob[CH * SO];
 };
 
 template <typename OT, bool SEG>
@@ -1878,28 +1882,48 @@ __global__ __launch_bounds__(PF_NT) void prefill_pipe_kernel(
                             o[vb][tb] = mfma(uh[ks][vb], ml, o[vb][tb]);
                         }
                     }
-                // lane holds O[t = 16 tb + l16][v = 16 (wave VB + vb) + 4 q4 .. + 3];
-                // rows t >= L fall outside the descriptor's range and are dropped
-                const uint32_t row_o = static_cast<uint32_t>(HV * D) * sizeof(OT);
-                const rsrc_t ro = make_rsrc(out + static_cast<size_t>(c0) * HV * D, L * row_o);
+                // lane holds O[t = 16 tb + l16][v = 16 (wave VB + vb) + 4 q4 .. + 3].
+                // fp32 outputs go straight out (64 bytes of a row per lane group;
+                // rows t >= L fall outside the descriptor's range and are
+                // dropped); bf16 outputs go to the LDS tile, stored in B3 as
+                // whole rows (a direct store wrote 32 bytes of each of 16 rows,
+                // and at full load those partial lines cost ~1.3 us per chunk)
 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb) {
 #pragma unroll
                     for (int vb = 0; vb < VB; ++vb) {
-                        const uint32_t off = static_cast<uint32_t>(16 * tb + l16) * row_o +
-                            static_cast<uint32_t>(hv * D + 16 * (wave * VB + vb) + 4 * q4) * sizeof(OT);
                         if constexpr (sizeof(OT) == 4) {
+                            const uint32_t row_o = static_cast<uint32_t>(HV * D) * sizeof(OT);
+                            const rsrc_t ro = make_rsrc(out + static_cast<size_t>(c0) * HV * D, L * row_o);
+                            const uint32_t off = static_cast<uint32_t>(16 * tb + l16) * row_o +
+                                static_cast<uint32_t>(hv * D + 16 * (wave * VB + vb) + 4 * q4) * sizeof(OT);
                             buf_st16(ro, off, __float_as_uint(o[vb][tb][0]), __float_as_uint(o[vb][tb][1]),
                                      __float_as_uint(o[vb][tb][2]), __float_as_uint(o[vb][tb][3]));
                         } else {
-                            buf_st8(ro, off, pack_bf16x2(o[vb][tb][0], o[vb][tb][1]),
+                            lds_st8(&sm.ob[(16 * tb + l16) * PipeSmem::SO + 16 * (wave * VB + vb) + 4 * q4],
+                                    pack_bf16x2(o[vb][tb][0], o[vb][tb][1]),
                                     pack_bf16x2(o[vb][tb][2], o[vb][tb][3]));
                         }
                     }
                 }
             }
             __syncthreads();
-            // ---- B3: cK . U split; the state update
+            // ---- B3: the bf16 output tile as whole rows (wave w: rows 16 w ..
+            // 16 w + 15, four per store); cK . U split; the state update
+            if constexpr (sizeof(OT) == 2) {
+                if (wo) {
+                    const uint32_t row_o = static_cast<uint32_t>(HV * D) * sizeof(OT);
+                    const rsrc_t ro = make_rsrc(out + static_cast<size_t>(c0) * HV * D, L * row_o);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = 16 * wave + 4 * i + (lane >> 4);
+                        const uint4 w = *reinterpret_cast<const uint4*>(&sm.ob[row * PipeSmem::SO + 8 * (lane & 15)]);
+                        buf_st16(ro, static_cast<uint32_t>(row) * row_o +
+                                         static_cast<uint32_t>(hv * D + 8 * (lane & 15)) * sizeof(OT),
+                                 w.x, w.y, w.z, w.w);
+                    }
+                }
+            }
             bf16x8 chk[2][VB], clk[2][VB];       // cK . U, split
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
