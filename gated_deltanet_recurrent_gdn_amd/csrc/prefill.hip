@@ -108,6 +108,11 @@ __device__ __forceinline__ void buf_st16(rsrc_t r, uint32_t off, uint32_t a, uin
     typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
     __builtin_amdgcn_raw_buffer_store_b128(u32x4{a, b, c, d}, r, off, 0, 0);
 }
+// The same with the nontemporal hint (cache policy bit NT)
+__device__ __forceinline__ void buf_st16_nt(rsrc_t r, uint32_t off, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{a, b, c, d}, r, off, 0, 2);
+}
 __device__ __forceinline__ void buf_st8(rsrc_t r, uint32_t off, uint32_t a, uint32_t b) {
     typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
     __builtin_amdgcn_raw_buffer_store_b64(u32x2{a, b}, r, off, 0, 0);
@@ -1918,9 +1923,10 @@ __global__ __launch_bounds__(PF_NT) void prefill_pipe_kernel(
                     for (int i = 0; i < 4; ++i) {
                         const int row = 16 * wave + 4 * i + (lane >> 4);
                         const uint4 w = *reinterpret_cast<const uint4*>(&sm.ob[row * PipeSmem::SO + 8 * (lane & 15)]);
-                        buf_st16(ro, static_cast<uint32_t>(row) * row_o +
-                                         static_cast<uint32_t>(hv * D + 8 * (lane & 15)) * sizeof(OT),
-                                 w.x, w.y, w.z, w.w);
+                        // (nontemporal: the outputs are not read again here)
+                        buf_st16_nt(ro, static_cast<uint32_t>(row) * row_o +
+                                            static_cast<uint32_t>(hv * D + 8 * (lane & 15)) * sizeof(OT),
+                                    w.x, w.y, w.z, w.w);
                     }
                 }
             }
