@@ -632,9 +632,11 @@ def main():
     ccs = torch.randn(16, D, W - 1, generator=cgen).to(torch.bfloat16).to(dev)
     cw = (torch.rand(D, W, generator=cgen) - 0.5).to(torch.bfloat16).to(dev)
     cy = torch.empty(pre.T, D, dtype=torch.bfloat16, device=dev)
-    ms_conv = time_loop(torch, lambda: gdn.gdn_conv_update(cx, pre.p["slot_idx"], ccs, cw, cy,
-                                                           cu_seqlens=pre.p["cu_seqlens"]),
-                        args.steps, args.warmup)
+    # block timing (one event pair around the steps' back-to-back calls), so the
+    # per-call figure holds no event packets between the ~140 us calls
+    ms_conv = time_block(torch, lambda: gdn.gdn_conv_update(cx, pre.p["slot_idx"], ccs, cw, cy,
+                                                            cu_seqlens=pre.p["cu_seqlens"]),
+                         args.steps, args.warmup)
     conv_bytes = pre.T * D * 2 * 2 + 2 * 8 * D * (W - 1) * 2 + D * W * 2
     del cx, ccs, cw, cy
     # the prefill with the Newton-Schulz (4 bf16 rounds) block-inverse variant

@@ -6,7 +6,8 @@
 // the bias and adds the taps in order; the state is rolled to the last W-1
 // raw inputs (compared bitwise there); SiLU is optional.  The products are
 // kept exact (bf16 x bf16 is exact in fp32) rather than rounded to bf16 one by
-// one, and SiLU uses IEEE division and the device expf.
+// one.  SiLU is the hardware form x * rcp(1 + 2^(-x log2 e)) (the production
+// provider's kind), a few fp32 ulps from the golden's exp with IEEE division.
 //
 // The in-place roll never races a read of the old state: in the decode form
 // and the general varlen kernel one thread reads and then rolls each
@@ -67,10 +68,12 @@ __global__ __launch_bounds__(256) void conv_decode_kernel(
 // read a rolled tap.  Arithmetic per channel: bias, then taps 0..W-1 with
 // fmaf, then SiLU -- the order of every other conv path, bitwise.
 // ---------------------------------------------------------------------------
-// Tokens per thread.  Measured (eager, conv + roll, dim 8192, bf16): 24,674
-// tokens over 8 sequences 249-263 us at 8 against 272-286 at 4, 284-306 at 16
-// and 297-306 at 32; 2 x 1024 tokens 45 us at 8 against 47 at 16.
-constexpr int CONV_TT = 8;
+// Tokens per thread.  Measured (eager, conv + roll, dim 8192, bf16, with the
+// sequence search and window branches on the scalar unit): 24,674 tokens over
+// 8 sequences 141-143 us at 4 against 146-148 at 8, 153 at 16 and 163-167 at
+// 2; 200 x 17 tokens 35 us at 4 and 8, 37 at 2.  (Before the scalar control
+// flow, when the VALU was the limit, 8 was the best.)
+constexpr int CONV_TT = 4;
 
 template <typename XT, typename CT, typename WT, typename OT>
 __global__ __launch_bounds__(256) void conv_varlen_tok_kernel(
@@ -86,7 +89,11 @@ __global__ __launch_bounds__(256) void conv_varlen_tok_kernel(
     const int cbk = static_cast<int>(blockIdx.x % static_cast<unsigned>(ncb));
     const int tile = static_cast<int>(blockIdx.x / static_cast<unsigned>(ncb));
     const int c = 4 * (cbk * 64 + static_cast<int>(threadIdx.x & 63));
-    const int t0 = tile * (4 * CONV_TT) + static_cast<int>(threadIdx.x >> 6) * CONV_TT;
+    // t0 is the same for the whole wave; saying so puts the sequence search,
+    // the cu_seqlens / slot reads and every per-token branch below on the scalar
+    // unit (as vector compares with exec masking they cost 16% of the call:
+    // 24,674 tokens 167-174 -> 146-148 us at 8 tokens per thread)
+    const int t0 = __builtin_amdgcn_readfirstlane(tile * (4 * CONV_TT) + static_cast<int>(threadIdx.x >> 6) * CONV_TT);
     if (c >= D || t0 >= T || n_seqs <= 0) return;
 
     // the window's inputs first (rows clamped into [0, T); unused ones are
