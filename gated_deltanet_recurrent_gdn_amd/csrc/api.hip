@@ -257,9 +257,13 @@ gdn_status prefill_impl(const void* q, const void* k, const void* v, gdn_dtype i
         if (seg_len % 64 != 0) return GDN_ERR_DIMS;
         if (head_len == 0) head_len = seg_len;
         if (head_len < seg_len || head_len % 64 != 0) return GDN_ERR_DIMS;
-        sch = PrefillSchedule{seg_len, head_len, true};
+        // at head dim 128 a middle segment's P and B runs are workgroups of
+        // their own on the pipelined step (faster than the paired single-role
+        // workgroup there); at 32 and 64 they share one
+        sch = PrefillSchedule{seg_len, head_len, dims->head_k_dim < 128};
         if (flags & GDN_FLAG_PREFILL_SEQUENTIAL) return GDN_ERR_FLAGS;
         if ((total_tokens + seg_len - 1) / seg_len > 32768) return GDN_ERR_DIMS;
+        if (!prefill_seg_grid_fits(n_seqs, total_tokens, sch)) return GDN_ERR_DIMS;
         if (n_seqs > 0 && total_tokens > 0) {
             if (!workspace) return GDN_ERR_WORKSPACE;
             if (workspace_bytes < prefill_segmented_workspace(*dims, n_seqs, total_tokens, seg_len))

@@ -112,6 +112,9 @@ struct PrefillSchedule {
 int64_t prefill_segment_ids(int32_t n_seqs, int32_t total_tokens, int32_t seg_len);
 size_t prefill_segmented_workspace(const gdn_dims& d, int32_t n_seqs, int32_t total_tokens,
                                    int32_t seg_len);
+// Whether the two segment passes' grids (bounded from the sizes alone) stay
+// within the 65535 workgroups of a grid's y extent.
+bool prefill_seg_grid_fits(int32_t n_seqs, int32_t total_tokens, PrefillSchedule sch);
 // Schedule the plain prefill call uses for these sizes (seg_len 0: whole
 // sequences), from a model of its workgroup rounds on the current device.
 PrefillSchedule prefill_auto_schedule(const gdn_dims& d, int32_t n_seqs, int32_t total_tokens);

@@ -2390,16 +2390,42 @@ __global__ __launch_bounds__(1024) void prefill_seg_map_kernel(
     }
 }
 
+// Bounds on the workgroups of each pass over all sequences: a sequence of
+// L > head tokens has nseg - 1 = ceil((L - head) / seg_len) <= L / seg_len + 1
+// segments past the first; pass 1 holds every segment 0 and the middle
+// segments' P/B runs (one workgroup each when paired, two otherwise), pass 2
+// the reruns.
+static int64_t seg_rest(int32_t n_seqs, int32_t total_tokens, int32_t seg_len) {
+    return static_cast<int64_t>(total_tokens) / seg_len + n_seqs;
+}
+static int64_t seg_grid1(int32_t n_seqs, int32_t total_tokens, const PrefillSchedule& sch) {
+    return n_seqs + (sch.paired ? 1 : 2) * seg_rest(n_seqs, total_tokens, sch.seg_len);
+}
+bool prefill_seg_grid_fits(int32_t n_seqs, int32_t total_tokens, PrefillSchedule sch) {
+    return sch.seg_len <= 0 || seg_grid1(n_seqs, total_tokens, sch) <= 65535;
+}
+
 // The schedule the plain prefill call takes for these sizes on the current
 // device (seg_len 0: whole sequences).  Units of the model are chunk-times of
-// one workgroup per CU.
-//  * Few (sequence, value head) runs (G = n_seqs HV at most half the CUs):
-//    equal segments.  Whole sequences take c chunk-times (c = chunks per
-//    sequence); with m segments of c / m chunks, pass 1 runs G (m - 1)
-//    workgroups (segment 0 and the paired P/B runs, about 1.3 chunk-times per
-//    chunk) and pass 2 G (m - 1), each in ceil(count / CUs) rounds, plus the
-//    scan's m - 2 steps at about a quarter chunk each; the call segments where
-//    that gains at least 15%.
+// one workgroup per CU; c = chunks per sequence (average), whole sequences
+// take c.
+//  * Few (sequence, value head) runs (G = n_seqs HV at most half the CUs), head
+//    dim 128 (the pipelined step, whose P and B runs are separate workgroups):
+//    a head of h chunks and m tails of s chunks.  Pass 1 runs segment 0 (G
+//    workgroups, h chunks) and the P and B runs of the m - 1 middle tails
+//    (2 G (m - 1) workgroups of s chunks) on the CUs segment 0 leaves free, in
+//    r = ceil(2 G (m - 1) / (CUs - G)) rounds; pass 2 reruns the m tails in
+//    ceil(G m / CUs) rounds.  With s = ceil(c / (r + m)) and h = c - m s the
+//    head lasts about as long as the P/B rounds; the model charges
+//    max(h, r s) + ceil(G m / CUs) s, plus about half a chunk per scan step and
+//    two for the extra launches, and the call segments where that is at most
+//    0.85 c.  (One 16,384-token sequence: head 48, tails 26 chunks.)
+//  * Few runs at head dims 32 and 64 (prefill_kernel, P and B runs paired in
+//    one workgroup, about 1.3 chunk-times per chunk): equal segments; with m
+//    segments of c / m chunks, pass 1 runs G (m - 1) workgroups and pass 2
+//    G (m - 1), each in ceil(count / CUs) rounds, plus the scan's m - 2 steps
+//    at about a quarter chunk each; the call segments where that gains at
+//    least 15%.
 //  * A busy chip: a head of the chunks a CU carries when the work is spread
 //    evenly (C = ceil(chunks x HV / CUs), chunks estimated as total / 64 plus
 //    half a chunk per sequence) and tail segments of about C / 4 chunks.  A
@@ -2408,7 +2434,7 @@ __global__ __launch_bounds__(1024) void prefill_seg_map_kernel(
 //    P/B runs (as separate workgroups, which keep the registers of a whole run,
 //    on the CUs that shorter sequences free during pass 1), and reruns about
 //    C / 4 chunks long in pass 2.
-PrefillSchedule prefill_auto_schedule(const gdn_dims& d, int32_t n_seqs, int32_t total_tokens) {
+static PrefillSchedule auto_schedule_model(const gdn_dims& d, int32_t n_seqs, int32_t total_tokens) {
     if (n_seqs <= 0 || total_tokens <= 0) return PrefillSchedule{0, 0, true};
     const int64_t groups = static_cast<int64_t>(n_seqs) * d.num_v_heads;
     const int64_t cus = cu_count();
@@ -2421,6 +2447,21 @@ PrefillSchedule prefill_auto_schedule(const gdn_dims& d, int32_t n_seqs, int32_t
     }
     const int64_t chunks = (total_tokens / n_seqs + 63) / 64;
     if (chunks < 8) return PrefillSchedule{0, 0, true};
+    if (d.head_k_dim == 128) {
+        double best = static_cast<double>(chunks);
+        int64_t best_s = 0, best_h = 0;
+        for (int64_t m = 2; m <= 64; ++m) {                    // tails after the head
+            const int64_t r = (2 * groups * (m - 1) + (cus - groups) - 1) / (cus - groups);
+            const int64_t s = (chunks + r + m - 1) / (r + m);
+            const int64_t h = std::max(s, chunks - m * s);
+            const int64_t r2 = (groups * m + cus - 1) / cus;
+            const double t = static_cast<double>(std::max(h, r * s) + r2 * s) + 0.55 * static_cast<double>(m - 1) + 2.0;
+            if (t < best * 0.999) { best = t; best_s = s; best_h = h; }
+        }
+        return (best_s > 0 && best <= 0.85 * static_cast<double>(chunks))
+            ? PrefillSchedule{static_cast<int32_t>(64 * best_s), static_cast<int32_t>(64 * best_h), false}
+            : PrefillSchedule{0, 0, true};
+    }
     double best = static_cast<double>(chunks);
     int32_t best_len = 0;
     for (int64_t m = 3; m <= 64; ++m) {
@@ -2435,6 +2476,12 @@ PrefillSchedule prefill_auto_schedule(const gdn_dims& d, int32_t n_seqs, int32_t
     return (best <= 0.85 * chunks) ? PrefillSchedule{best_len, best_len, true} : PrefillSchedule{0, 0, true};
 }
 
+PrefillSchedule prefill_auto_schedule(const gdn_dims& d, int32_t n_seqs, int32_t total_tokens) {
+    const PrefillSchedule sch = auto_schedule_model(d, n_seqs, total_tokens);
+    // many thousands of sequences could overflow a segment pass's grid: whole runs then
+    return prefill_seg_grid_fits(n_seqs, total_tokens, sch) ? sch : PrefillSchedule{0, 0, true};
+}
+
 hipError_t launch_prefill_segmented(const void* q, const void* k, const void* v, gdn_dtype in_dt,
                                     const GateArgs& ga, const int32_t* cu, int32_t n_seqs,
                                     int32_t total_tokens, const int32_t* slot, float* rec,
@@ -2447,12 +2494,8 @@ hipError_t launch_prefill_segmented(const void* q, const void* k, const void* v,
     if (!prefill_supported(d, in_dt) || seg_len <= 0 || seg_len % CH != 0 || head < seg_len ||
         head % CH != 0)
         return hipErrorInvalidValue;
-    // bounds on the workgroups of each pass over all sequences: a sequence of
-    // L > head tokens has nseg - 1 = ceil((L - head) / seg_len) <= L / seg_len + 1
-    // segments past the first
-    const int64_t rest = static_cast<int64_t>(total_tokens) / seg_len + n_seqs;
-    const int64_t g1 = n_seqs + (pair ? 1 : 2) * rest;
-    const int64_t g2 = rest;
+    const int64_t g1 = seg_grid1(n_seqs, total_tokens, sch);
+    const int64_t g2 = seg_rest(n_seqs, total_tokens, seg_len);
     if (g1 > 65535) return hipErrorInvalidValue;
     int32_t* map1 = reinterpret_cast<int32_t*>(
         reinterpret_cast<char*>(ws) + seg_matrix_bytes(d, n_seqs, total_tokens, seg_len));

@@ -335,7 +335,9 @@ size_t gdn_prefill_workspace_size(const gdn_dims* dims, int32_t n_seqs, int32_t 
  *                gdn_prefill_workspace_size(...) bytes (and that size > 0,
  *                and no GDN_FLAG_PREFILL_SEQUENTIAL) the call runs the
  *                segment-parallel schedule of gdn_prefill_segmented with the
- *                segment length the library picks for these sizes; otherwise
+ *                head and segment lengths the library picks for these sizes
+ *                (from n_seqs, total_tokens, the head dims and the device's CU
+ *                count alone); otherwise
  *                each (sequence, value head) is walked by one workgroup from
  *                start to end.  The two schedules agree to rounding, not
  *                bitwise: whole-sequence runs are bitwise independent of how a
@@ -367,13 +369,17 @@ gdn_status gdn_prefill_chunked(const void* q, const void* k, const void* v, gdn_
  * segment 0 from the slot's state together with the P and B runs of the
  * middle segments; a scan of the start states in fp32; segments 1.. again
  * from their start states, writing outputs and, for the last, the slot.
- * The cost is about 2.4x the chunk work of a middle segment, for a critical
- * path of about two segments instead of the whole sequence.
+ * A middle segment costs its P run, its B run and its rerun (at dk = 128 the
+ * P and B runs are workgroups of their own; at 32 and 64 they share one), for
+ * a critical path of about the head plus one segment instead of the whole
+ * sequence.
  *
  *   g, beta, gate  either g and beta (gate NULL) or gate (g, beta NULL; as in
  *                  gdn_prefill_chunked_gated); GDN_ERR_FLAGS if both
  *   seg_len        tokens per segment: GDN_ERR_DIMS unless a positive multiple
- *                  of 64 (and at most 32768 segments of total_tokens)
+ *                  of 64, at most 32768 segments of total_tokens, and the first
+ *                  pass's workgroup rows, n_seqs + (2 at dk = 128, else 1) x
+ *                  (total_tokens / seg_len + n_seqs), at most 65535
  *   head_len       tokens of segment 0: 0 (= seg_len) or a multiple of 64 of
  *                  at least seg_len (GDN_ERR_DIMS otherwise)
  *   workspace      >= gdn_prefill_segmented_workspace_size(dims, n_seqs,

@@ -273,6 +273,9 @@ def _segmented(lib, seg_len=128, flags=2, g=FAKE, beta=FAKE, gate=None, ws=FAKE,
     (dict(ws=None), ERR_WS), (dict(ws_bytes=1024), ERR_WS), (dict(ws=MISALIGNED), ERR_ALIGN),
     (dict(g=None), ERR_NULL), (dict(gate="both"), ERR_FLAGS),
     (dict(seg_len=64, total=64 * 32769), ERR_DIMS),   # more than 32768 segments
+    # 32768 segments of one sequence at dk = 128: the first pass's separate P
+    # and B runs would need 1 + 2 x 32769 grid rows, past 65535
+    (dict(seg_len=64, total=64 * 32768), ERR_DIMS),
     (dict(head=64), ERR_DIMS),                     # head shorter than the segments
     (dict(head=200), ERR_DIMS),                    # head not a multiple of 64
     (dict(head=-64), ERR_DIMS),
@@ -304,7 +307,14 @@ def test_prefill_workspace_sizes(lib):
     assert gdn.gdn_prefill_workspace_size(d, 8, 24674) == (8 + 29 + 1) * mats + maps
     # a busy chip with short sequences keeps whole runs (head under 8 chunks)
     assert gdn.gdn_prefill_workspace_size(d, 8, 1600) == 0
-    # one long sequence leaves most of the chip idle: the call asks for segments
-    ws = gdn.gdn_prefill_workspace_size(d, 1, 16384)
-    assert ws > 0 and (ws - maps) % mats == 0
+    # one long sequence leaves most of the chip idle: the call asks for segments.
+    # The model (head h, m tails of s chunks, separate P/B runs at dk = 128):
+    # m = 8 tails need 2 x 32 x 7 = 448 P/B runs, two rounds on the 224 CUs
+    # segment 0 leaves, so s = ceil(256 / (2 + 8)) = 26 chunks (1664 tokens)
+    # and h = 256 - 8 x 26 = 48: 1 + 16384 // 1664 + 1 segment ids
+    assert gdn.gdn_prefill_workspace_size(d, 1, 16384) == (1 + 9 + 1) * mats + maps
     assert gdn.gdn_prefill_workspace_size(d, 1, 256) == 0     # too short to pay
+    assert gdn.gdn_prefill_workspace_size(d, 1, 512) == 0     # 8 chunks: the launches eat the gain
+    # 30000 sequences on a busy chip: the segment passes' grids would pass
+    # 65535 rows, so the call keeps whole runs
+    assert gdn.gdn_prefill_workspace_size(d, 30000, 30000 * 600) == 0

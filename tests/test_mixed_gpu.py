@@ -306,7 +306,7 @@ def test_mixed_step_graph_replay_matches_eager(two_streams, capture_first):
     three consecutive eager steps bitwise on every replay, whether the capture
     or the eager steps come first: every call only enqueues work, and the
     schedule depends on the arguments alone."""
-    _graph_vs_eager(5, [300, 700], gdn.MixedStreams() if two_streams else None, capture_first)
+    _graph_vs_eager(5, [700, 1300], gdn.MixedStreams() if two_streams else None, capture_first)
 
 
 def test_mixed_step_graph_replay_segmented():
