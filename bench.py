@@ -716,8 +716,8 @@ def main():
         "prefill_tokens_per_s": round(pre_tps, 1),
         "prefill_roofline": {
             "bound": "mfma",
-            "kernel": "gdn_prefill_chunked call (prefill_seg_map_kernel, prefill_kernel pass 1, "
-                      "prefill_seg_scan_kernel, prefill_kernel pass 2)",
+            "kernel": "gdn_prefill_chunked call (prefill_seg_map_kernel, prefill_pipe_kernel "
+                      "pass 1, prefill_seg_scan_kernel, prefill_pipe_kernel pass 2)",
             "achieved": round(pre_tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(pre_tflops / BF16_PEAK_TFLOPS, 4),
             "hbm_frac": round(pre_bytes / (pre_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
