@@ -14,11 +14,13 @@ state written in a recent step.
 
 Prints ONE JSON line.  `value` is the decode step's algorithmic HBM bytes per
 second at batch 256 (GB/s); the batch-16 decode rate and the prefill tokens/s
-ride along in "extra".  "roofline" reports the headline step's kernel (at
-batch 256 the step is one fused conv + recurrence kernel) timed alone: blocks of
-back-to-back eager launches, one HIP event pair on their stream per block, the
-block time divided by its launches; the split path's recurrence kernel is timed
-the same way alongside.  "cpu_baseline" is the
+ride along in "extra".  "roofline" reports the headline step's dominant kernel
+timed alone: at batch 256 the step is the conv kernel followed by the
+recurrence kernel (the library's choice for that batch; the fused one-kernel
+step serves one or two (row, key head) groups per CU), and the recurrence kernel
+carries ~92% of its time.  Timing: blocks of back-to-back eager launches, one
+HIP event pair on their stream per block, the block time divided by its
+launches; the whole step and the fused kernel are timed the same way alongside.  "cpu_baseline" is the
 fp64 oracle on a bounded sample of the same workload, run over independent
 rows on the host's threads (at most 16); the one-thread figure is in "extra".
 """
@@ -73,6 +75,7 @@ def prefill_bytes(total_tokens, n_seqs, in_bytes=2, out_bytes=2):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_step_kernel_b256_traffic.txt")
+REC_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_rec_kernel_b256_traffic.txt")
 DECODE_SRC = os.path.join(ROOT, "gated_deltanet_recurrent_gdn_amd", "csrc", "decode.hip")
 
 
@@ -186,6 +189,7 @@ class DecodeSetup:
         self.scale = DK ** -0.5
         self.i = 0
         self.gate = None
+        self.extra_flags = 0                                 # e.g. force a step path
 
     def use_gating(self, seed):
         """Switch the step to the fused-gating call (raw a, b projections in bf16)."""
@@ -199,7 +203,8 @@ class DecodeSetup:
         d = self.d
         slots = self.slot_sets[self.i % len(self.slot_sets)]
         self.i += 1
-        flags = gdn.DEFAULT_DECODE_FLAGS | (gdn.FLAG_VALIDATE if validate else 0)
+        flags = (gdn.DEFAULT_DECODE_FLAGS | (gdn.FLAG_VALIDATE if validate else 0) |
+                 self.extra_flags)
         if self.gate is not None:
             gdn.gdn_decode_step_gated(d["mixed_qkv"], self.gate, slots, d["conv_state"],
                                       d["conv_weight"], d["rec_state"], self.out, self.dims,
@@ -609,9 +614,12 @@ def main():
     for _ in range(2):
         ms_pre += time_loop(torch, lambda: pre.step(args.validate), max(2, args.steps // 2), args.warmup)
         ms_pre_whole += time_loop(torch, pre.step_whole, max(2, args.steps // 2), args.warmup)
-    # the headline step's kernel alone (the fused step at batch 256): eager
-    # launches back to back, one event pair on their stream around each block
+    # the headline step alone (eager launches back to back, one event pair on
+    # their stream around each block), and the fused step kernel forced
     ms_step_k = time_block(torch, big.step, args.steps, args.warmup)
+    big.extra_flags = gdn.FLAG_STEP_FUSED
+    ms_fused_k = time_block(torch, big.step, args.steps, args.warmup)
+    big.extra_flags = 0
     # the split path's recurrence kernel alone (post-conv activations in)
     big.prepare_rec()
     ms_rec = time_block(torch, big.rec_step, args.steps, args.warmup)
@@ -694,6 +702,9 @@ def main():
     rec_gbs = rec_bytes / (rec_ms * 1e-3) / 1e9
     stepk_ms = mean(ms_step_k)
     stepk_gbs = step_bytes_big / (stepk_ms * 1e-3) / 1e9
+    fusedk_ms = mean(ms_fused_k)
+    fusedk_gbs = step_bytes_big / (fusedk_ms * 1e-3) / 1e9
+    big_fused = gdn.gdn_decode_step_fused(big.dims, 256) == 1
     pre_ms = mean(ms_pre)
     pre_flops = prefill_flops(pre.lengths)
     pre_bytes = prefill_bytes(pre.T, len(pre.lengths))
@@ -761,11 +772,20 @@ def main():
                             "caller-owned second stream (fork / join events), overlapped with "
                             "the decode rows; *_serial: both parts in order on one stream; "
                             "the two alternate in the same run"),
+        "decode_step_b256_block_ms_mean": round(stepk_ms, 5),
+        "decode_step_b256_block_GBps": round(stepk_gbs, 2),
+        "decode_step_b256_path": "fused kernel" if big_fused else "conv kernel + recurrence kernel",
+        "decode_fused_kernel_b256_ms_mean": round(fusedk_ms, 5),
+        "decode_fused_kernel_b256_GBps": round(fusedk_gbs, 2),
+        "decode_fused_kernel_b256_pct_hbm_peak": round(100 * fusedk_gbs / HBM_PEAK_GBS, 2),
+        "decode_fused_kernel_note": ("gdn_decode_step at batch 256 with GDN_FLAG_STEP_FUSED (the "
+                                     "one-kernel step, bitwise the same results), eager blocks"),
         "decode_rec_kernel_b256_ms_mean": round(rec_ms, 5),
         "decode_rec_kernel_b256_GBps": round(rec_gbs, 2),
         "decode_rec_kernel_b256_pct_hbm_peak": round(100 * rec_gbs / HBM_PEAK_GBS, 2),
         "decode_rec_kernel_note": ("gdn_decode_recurrent alone at batch 256 (fp32 post-conv "
-                                   "activations in): the recurrence of the split path"),
+                                   "activations in): the recurrence kernel of the conv + "
+                                   "recurrence path"),
         "decode_b256_gated_ms_mean": round(mean(ms_big_g), 5),
         "decode_b256_gated_GBps": round(step_bytes_big_gated / (mean(ms_big_g) * 1e-3) / 1e9, 2),
         "prefill_gated_ms_mean": round(mean(ms_pre_g), 4),
@@ -802,7 +822,22 @@ def main():
         cpu, extra["cpu_baseline_1thread"] = cpu_baseline(args.cpu_seconds / 2, nth)
         extra["cpu_baseline_prefill"] = cpu_baseline_prefill(max(4.0, args.cpu_seconds / 3), nth)
 
-    traffic = measured_traffic()
+    if big_fused:
+        roof = {"bound": "hbm", "kernel": "decode_step_kernel",
+                "achieved": round(stepk_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(stepk_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                "avg_launch_ms": round(stepk_ms, 5),
+                "algorithmic_bytes_per_launch": step_bytes_big}
+    else:
+        roof = {"bound": "hbm", "kernel": "decode_rec_kernel",
+                "achieved": round(rec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(rec_gbs / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(REC_TRAFFIC_FILE),
+                "avg_launch_ms": round(rec_ms, 5),
+                "algorithmic_bytes_per_launch": rec_bytes,
+                "note": ("the dominant kernel of the batch-256 step (conv_decode_kernel, then "
+                         "decode_rec_kernel on the fp32 activations); algorithmic bytes: state "
+                         "read + write, activations, g, beta, slot, output")}
 
     line = {
         "metric": "GDN decode HBM GB/s (% peak) at batch 16/256; prefill tokens/s (% MFMA)",
@@ -822,11 +857,7 @@ def main():
                                "step also runs decode batch 16 and the 8-sequence varlen "
                                "prefill (see extra)",
                    "global_batch": 256, "seq_len": 1, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "hbm", "kernel": "decode_step_kernel",
-                     "achieved": round(stepk_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(stepk_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "avg_launch_ms": round(stepk_ms, 5),
-                     "algorithmic_bytes_per_launch": step_bytes_big},
+        "roofline": roof,
         "cpu_baseline": cpu,
         "extra": extra,
     }

@@ -9,7 +9,8 @@ from ._abi import (  # noqa: F401
     FLAG_PREFILL_NS3, FLAG_PREFILL_NS4, FLAG_PREFILL_SEQUENTIAL, FLAG_PREFILL_SINGLE_ROLE,
     FLAG_VALIDATE, GDN_BF16, GDN_F32, NORM_GATE_SIGMOID, NORM_ZERO_CENTRED, gdn_gated_rmsnorm,
     GateInputs, GDNError, gdn_conv_update, gdn_decode_recurrent, gdn_decode_step,
-    gdn_decode_step_gated, gdn_decode_step_noalloc, gdn_decode_workspace_size, gdn_dims, gdn_gate_inputs, gdn_mixed_step,
+    gdn_decode_step_fused, gdn_decode_step_gated, gdn_decode_step_noalloc, gdn_decode_workspace_size,
+    gdn_dims, gdn_gate_inputs, gdn_mixed_step,
     gdn_mixed_workspace_size,
     gdn_prefill_chunked, gdn_prefill_chunked_gated, gdn_prefill_segmented,
     gdn_prefill_segmented_workspace_size, gdn_prefill_workspace_size, gdn_strerror,

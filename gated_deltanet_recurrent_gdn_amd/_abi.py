@@ -29,7 +29,7 @@ DEFAULT_PREFILL_FLAGS = FLAG_QK_L2NORM
 _STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_DIMS", 3: "GDN_ERR_DTYPE",
            4: "GDN_ERR_ALIGN", 5: "GDN_ERR_WORKSPACE", 6: "GDN_ERR_LAUNCH", 7: "GDN_ERR_FLAGS"}
 
-EXPORTED = ["gdn_conv_update", "gdn_decode_workspace_size", "gdn_decode_step",
+EXPORTED = ["gdn_conv_update", "gdn_decode_workspace_size", "gdn_decode_step", "gdn_decode_step_fused",
             "gdn_decode_step_gated", "gdn_decode_step_noalloc", "gdn_decode_recurrent",
             "gdn_prefill_workspace_size", "gdn_prefill_chunked", "gdn_prefill_chunked_gated",
             "gdn_prefill_segmented_workspace_size", "gdn_prefill_segmented",
@@ -80,6 +80,8 @@ def load_library(path: str = None):
                                     i32, i32, i32, P, P]
     lib.gdn_decode_workspace_size.argtypes = [D, i32]
     lib.gdn_decode_workspace_size.restype = sz
+    lib.gdn_decode_step_fused.argtypes = [D, i32]
+    lib.gdn_decode_step_fused.restype = i32
     lib.gdn_decode_step.argtypes = [P, i32, P, P, P, i32, P, i32, P, P, i32, P, i32, P, i32,
                                     D, f32, i32, P, sz, P, P]
     lib.gdn_decode_step_noalloc.argtypes = [P, i32, P, P, P, i32, P, i32, P, P, i32, P, i32, P,
@@ -198,6 +200,12 @@ def gdn_conv_update(x, slot_idx, conv_state, weight, out, bias=None, cu_seqlens=
 
 def gdn_decode_workspace_size(dims: gdn_dims, batch: int) -> int:
     return int(load_library().gdn_decode_workspace_size(ctypes.byref(dims), int(batch)))
+
+
+def gdn_decode_step_fused(dims: gdn_dims, batch: int) -> int:
+    """1 if gdn_decode_step takes the fused kernel for `batch` rows on this
+    device, 0 for the conv + recurrence pair, -1 for invalid arguments."""
+    return int(load_library().gdn_decode_step_fused(ctypes.byref(dims), int(batch)))
 
 
 def _decode_step(fn, mixed_qkv, gb, gate, slot_idx, conv_state, conv_weight, rec_state, out,

@@ -40,10 +40,16 @@ template <> __device__ __forceinline__ float4 load4<bf16_t>(const bf16_t* p) {
                        __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
 }
 
-// Workgroups resident per CU in the persistent grid, and whether the state
-// stream uses nontemporal loads/stores (it is read once and written once).
+// Workgroups per CU in the recurrence kernel's grid (an item-strided loop
+// beyond it), and whether the state stream uses nontemporal loads/stores (it
+// is read once and written once).  One workgroup per 32-row item up to batch
+// 1024 at HV = 32: the hardware then starts an item's loads as soon as a
+// workgroup slot frees, which a loop over items inside a resident workgroup
+// does not (batch 256, 32768 items: 16 per CU, eight items per workgroup,
+// 191.8 us; 64 per CU 181.2 us; 128, one item each, 174.9 us = 6.2 TB/s;
+// batch 1024: 807 / 784 / 764 us, and the whole step 785 us at 512).
 #ifndef GDN_DECODE_WG_PER_CU
-#define GDN_DECODE_WG_PER_CU 16
+#define GDN_DECODE_WG_PER_CU 512
 #endif
 #ifndef GDN_DECODE_NT
 #define GDN_DECODE_NT 1
@@ -208,7 +214,8 @@ __global__ __launch_bounds__(256) void decode_rec_kernel(
     int32_t flags, const int32_t* __restrict__ err_flag) {
     constexpr int NV = DK / 32;               // float4 per lane per row
     if (call_rejected(err_flag)) return;
-    // persistent grid: workgroup-uniform loop over (row, value head, tile) items
+    // one (row, value head, tile) item per workgroup up to the grid's cap, a
+    // workgroup-uniform loop over items beyond it
     for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
         const int per_row = HV * tiles_per_head;
         const int b = item / per_row;
@@ -499,9 +506,10 @@ hipError_t pick_dk(const RecArgs& a) {
 
 // Workgroups per CU in the fused step's grid (a group-strided loop beyond it).
 // Measured at batch 256: one workgroup per group (4096) 206 us; one or two
-// resident per CU looping over groups 211 us.
+// resident per CU looping over groups 211 us; at batch 1024 (16384 groups) a
+// 4096 grid looping over four groups each 823 us, one per group 793 us.
 #ifndef GDN_STEP_WG_PER_CU
-#define GDN_STEP_WG_PER_CU GDN_DECODE_WG_PER_CU
+#define GDN_STEP_WG_PER_CU 256
 #endif
 // Double-buffered passes up to this many groups per CU (see decode_step_kernel).
 // Measured: batch 32 (2 groups per CU) 30.1 us vs 30.5 single-buffered; batch
@@ -555,15 +563,24 @@ hipError_t step_x(gdn_dtype xt, gdn_dtype c, gdn_dtype wt, gdn_dtype o, const St
 }
 }  // namespace
 
-// The fused step is chosen while each (row, key head) group has at most this
-// many CUs to itself.  Measured (graph replay, H = 16, HV = 32, d = 128, 256
-// CUs, 1024-thread groups), fused vs the conv + recurrence pair: batch 256
-// 203.6 vs 206.5 us; batch 32 30.1 vs 30.0; batch 16 15.1 vs 17.9; batch 12
-// 12.8 vs 15.4; batch 8 12.1 vs 12.0; batch 4 8.95 vs 9.1; below that the
-// pair's 32-row recurrence items spread the few rows over more CUs (batch 2:
-// 8.7 vs 7.4, batch 1: 8.5 vs 7.0).
+// The fused step is chosen while each (row, key head) group has at most
+// GDN_DECODE_FUSED_MAX_CUS_PER_GROUP CUs to itself and there are at most
+// GDN_DECODE_FUSED_MAX_GROUPS_PER_CU groups per CU.  Measured (graph replay per
+// step, H = 16, HV = 32, d = 128, 256 CUs, 1024-thread groups, the recurrence
+// kernel with one workgroup per item), fused vs the conv + recurrence pair:
+// batch 1024 811.4 vs 797.6 us; 256 204.8 vs 193.1; 128 103.7 vs 97.8; 64 56.2
+// vs 54.0; 32 30.1 vs 29.7; 16 14.5 vs 17.2; 8 11.1 vs 11.3; 4 7.8 vs 7.7.
+// With one or two groups per CU the fused kernel's double-buffered passes hide
+// its latency chain; past that, the pair's small recurrence items (no barrier,
+// several workgroups per CU) stream the state faster than one 1024-thread
+// group per CU, the conv kernel and the activations' round trip included.
+// Below a quarter group per CU the pair's items also spread the few rows over
+// more CUs (batch 2: 8.7 vs 7.4 us, batch 1: 8.5 vs 7.0).
 #ifndef GDN_DECODE_FUSED_MAX_CUS_PER_GROUP
 #define GDN_DECODE_FUSED_MAX_CUS_PER_GROUP 4
+#endif
+#ifndef GDN_DECODE_FUSED_MAX_GROUPS_PER_CU
+#define GDN_DECODE_FUSED_MAX_GROUPS_PER_CU 1
 #endif
 
 bool decode_step_fused_fits(const gdn_dims& d) {
@@ -575,9 +592,11 @@ bool decode_step_fused_fits(const gdn_dims& d) {
 bool decode_step_use_fused(const gdn_dims& d, int32_t batch) {
     // dk > 128 stays on the pair: the 1024-thread fused kernel (128 VGPRs)
     // spills its per-row registers there
+    const int64_t groups = static_cast<int64_t>(batch) * d.num_k_heads;
+    const int64_t cus = cu_count();
     return decode_step_fused_fits(d) && d.head_k_dim <= 128 &&
-           static_cast<int64_t>(batch) * d.num_k_heads * GDN_DECODE_FUSED_MAX_CUS_PER_GROUP >=
-               static_cast<int64_t>(cu_count());
+           groups * GDN_DECODE_FUSED_MAX_CUS_PER_GROUP >= cus &&
+           groups <= cus * GDN_DECODE_FUSED_MAX_GROUPS_PER_CU;
 }
 
 hipError_t launch_decode_step_fused(const void* x, gdn_dtype x_dt, const GateArgs& gate,

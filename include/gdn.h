@@ -216,8 +216,12 @@ size_t gdn_decode_workspace_size(const gdn_dims* dims, int32_t batch);
  * value heads sharing h into LDS, then their recurrence) and a conv kernel
  * writing the fp32 activations to the workspace followed by the recurrence
  * kernel.  By default the fused kernel runs when head_k_dim <= 128, when
- * 4 * batch * num_k_heads is at least the number of compute units and when
- * (2 dk + (HV / H) (dv + 2)) * 4 bytes fit in 64 KiB of LDS; the STEP flags
+ * batch * num_k_heads is between a quarter of the number of compute units
+ * and that number (one or two groups per compute unit at most: there its
+ * double-buffered passes hide its latency chain; with more groups the pair's
+ * small recurrence items stream the state faster) and when
+ * (2 dk + (HV / H) (dv + 2)) * 4 bytes fit in 64 KiB of LDS
+ * (gdn_decode_step_fused reports the choice); the STEP flags
  * force a path (GDN_ERR_DIMS if the fused kernel is forced where the group
  * does not fit, GDN_ERR_FLAGS if both are set).
  */
@@ -233,15 +237,27 @@ gdn_status gdn_decode_step(const void* mixed_qkv, gdn_dtype x_dt,
                            int32_t* err_flag, hipStream_t stream);
 
 /*
+ * gdn_decode_step_fused -- the path gdn_decode_step, gdn_decode_step_gated and
+ * the decode rows of gdn_mixed_step take for `batch` rows without a STEP flag
+ * on the current device: 1 = the fused kernel, 0 = the conv kernel followed by
+ * the recurrence kernel (the rule above: dims, batch and the device's compute
+ * unit count alone; both paths give the same bits).  -1 for invalid dims or a
+ * batch outside [0, 65535].  Enqueues nothing.
+ */
+int32_t gdn_decode_step_fused(const gdn_dims* dims, int32_t batch);
+
+/*
  * gdn_decode_step_noalloc -- gdn_decode_step for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc): the same arguments without the workspace, the same
  * kernels and bitwise the same results.  Where the call takes the conv +
  * recurrence pair, the fp32 activations (batch * D * 4 bytes) go to a scratch
  * array of GDN_NOALLOC_SCRATCH_BYTES that the library holds in device memory,
- * one per device, until the process ends; GDN_ERR_WORKSPACE if they would not
- * fit (at D = 8192: more than 512 rows on that path).  The fused kernel needs
- * no scratch.  The call allocates nothing; its first call on a device looks
+ * one per device, until the process ends.  Where they would not fit (at
+ * D = 8192: more than 512 rows) the call takes the fused kernel instead,
+ * which needs no scratch and gives the same bits; GDN_ERR_WORKSPACE if
+ * GDN_FLAG_STEP_SPLIT forces the pair there (or the fused kernel's group does
+ * not fit its LDS).  The call allocates nothing; its first call on a device looks
  * up the array's device address (GDN_ERR_LAUNCH if the runtime cannot) and
  * keeps it for that device.  Every call on a device shares that device's
  * array, so calls that can overlap on one device (different streams, or
@@ -449,9 +465,12 @@ size_t gdn_mixed_workspace_size(const gdn_dims* dims, int32_t n_dec, int32_t tot
  * composition; the proposed fix routes them through the decode kernel and
  * aligns non-final chunked-prefill calls to the 64-token grid).
  *
- * The decode rows run exactly the kernels of gdn_decode_step for n_dec rows,
- * so every decode row's output, recurrent state and conv state are bitwise
- * independent of what else the step holds.  The prefill tokens go through
+ * The decode rows run gdn_decode_step's kernels for n_dec rows (beside a
+ * prefill part on prefill_stream, the fused kernel where it fits, which lets
+ * the prefill's workgroups take compute units as the decode's groups retire;
+ * both of that call's paths give the same bits), so every decode row's output,
+ * recurrent state and conv state are bitwise independent of what else the
+ * step holds and of the streams.  The prefill tokens go through
  * the varlen conv (SiLU per flags) into bf16 activations -- the serving path's
  * convention -- and then the chunked prefill: as one run per (sequence, value
  * head), or, when the step has no decode rows and the workspace also holds

@@ -34,6 +34,18 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, n), n
 
 
+def test_decode_step_path_query(lib):
+    # without a GPU the CU count is the 256 fallback: the fused kernel for
+    # 64 .. 256 (row, key head) groups, the conv + recurrence pair outside
+    d = gdn.make_dims(16, 32, 128, 128, 4)
+    assert [gdn.gdn_decode_step_fused(d, b) for b in (1, 2, 3, 4, 8, 16, 17, 32, 256, 1024)] == \
+        [0, 0, 0, 1, 1, 1, 0, 0, 0, 0]
+    assert gdn.gdn_decode_step_fused(d, 0) == 0
+    assert gdn.gdn_decode_step_fused(gdn.make_dims(16, 32, 256, 256, 4), 8) == 0   # dk > 128
+    assert gdn.gdn_decode_step_fused(gdn.make_dims(16, 30, 128, 128, 4), 8) == -1  # HV % H
+    assert gdn.gdn_decode_step_fused(d, -1) == -1 and gdn.gdn_decode_step_fused(d, 65536) == -1
+
+
 def test_strerror(lib):
     for code in range(8):
         assert gdn.gdn_strerror(code)

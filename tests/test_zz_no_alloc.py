@@ -68,3 +68,17 @@ def test_noalloc_equals_decode_step(path):
         assert torch.equal(o_na, o_ws), (path, batch)
         assert torch.equal(rs_na, rs_ws), (path, batch)
         assert torch.equal(cs_na, cs_ws), (path, batch)
+
+
+@pytest.mark.gpu
+def test_noalloc_past_the_scratch_takes_the_fused_kernel():
+    """520 rows need 16.25 MiB of activations on the conv + recurrence pair,
+    past the scratch: the default noalloc call then takes the fused kernel,
+    while gdn_decode_step takes the pair for that batch -- the same bits."""
+    dims = gdn.make_dims(H, HV, DK, DK, 4)
+    assert gdn.gdn_decode_step_fused(dims, 520) == 0       # the plain call: the pair
+    (o_ws, cs_ws, rs_ws), (o_na, cs_na, rs_na) = _pair(520, 13, gdn.DEFAULT_DECODE_FLAGS)
+    assert not torch.isnan(o_na).any()
+    assert torch.equal(o_na, o_ws)
+    assert torch.equal(rs_na, rs_ws)
+    assert torch.equal(cs_na, cs_ws)
